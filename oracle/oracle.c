@@ -1,0 +1,580 @@
+/*
+ * oracle.c -- plain serial CPU oracle for the lossless entropy-coded bf16
+ * weight container.
+ *
+ * TEST INFRASTRUCTURE ONLY: used by the tests, the smoke entry point and the
+ * benchmark's CPU-baseline leg, never by the product library.  It shares no
+ * code, header or table with the HIP path.
+ *
+ * Sources followed (cited by page title and part of the page):
+ *  [DF11]  "70% Size, 100% Accuracy: Lossless LLM Compression for Efficient
+ *          GPU Inference via Dynamic-Length Float" (DFloat11), abstract:
+ *          the low entropy of the bf16 representation is removed by entropy
+ *          coding that gives shorter codes to more frequent values; outputs
+ *          are bit-for-bit identical; decoding uses lightweight auxiliary
+ *          variables (per-thread bit offsets, per-block output positions).
+ *  [L2-7B] "From a Lossless (~1.5:1) Compression Algorithm for Llama2 7B
+ *          Weights to Variable Precision, Variable Range, Compressed Numeric
+ *          Data Types for CNNs and LLMs", abstract: lossless ~1.5:1 coding
+ *          of bf16 weights.
+ *  [LW]    LazyWeights review page, analogy and verified facts: Huffman
+ *          coding, shorter labels for the common values, decoded bit-exact.
+ *  [HUFF]  "Huff-LLM: End-to-End Lossless Compression for Efficient LLM
+ *          Inference", abstract: weights stay Huffman-compressed end to end.
+ *  Textbook material the pages rely on but do not spell out:
+ *    Huffman's construction (D. A. Huffman, 1952); package-merge for an
+ *    optimal length-limited code (Larmore & Hirschberg, 1990); canonical
+ *    code assignment as in RFC 1951 section 3.2.2.
+ *
+ * Readings where the pages are silent (each also listed in the design doc):
+ *  - split: e = bits 14..7 of the bf16 word, sm = bit 15 then bits 6..0;
+ *  - codes are canonical, at most max_code_len (<= 24) bits, written
+ *    MSB-first into bytes in ascending address order;
+ *  - one present symbol gets the 1-bit code "0";
+ *  - the stream is cut into 64-bit chunks; gap[c] is the offset of the first
+ *    codeword that starts at or after bit 64c (stream end if none);
+ *  - chunks are grouped G at a time; group_start[g] is the index of the first
+ *    element whose codeword starts at or after bit 64*G*g (n if none), plus a
+ *    final entry equal to n.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Container v1 layout, as restated for the oracle (little-endian fields).  */
+/* ------------------------------------------------------------------------ */
+#define HDR_BYTES       256u
+#define ALIGN           256u
+#define MAX_LEN_LIMIT   24u
+#define CHUNK_BITS      64u
+
+#define F_MAGIC          0   /* "WCBF"                                      */
+#define F_VERSION        4   /* u16, 1                                      */
+#define F_FLAGS          6   /* u16, 0                                      */
+#define F_MAXLEN         8   /* u8                                          */
+#define F_CHUNKBITS      9   /* u8, 64                                      */
+#define F_RES0          10   /* u16, 0                                      */
+#define F_G             12   /* u32 chunks per group                        */
+#define F_NTENS         16   /* u32                                         */
+#define F_RES1          20   /* u32, 0                                      */
+#define F_N             24   /* u64 elements                                */
+#define F_SBITS         32   /* u64 stream bits                             */
+#define F_NCHUNKS       40   /* u64                                         */
+#define F_NGROUPS       48   /* u64                                         */
+#define F_OFF_LEN       56   /* u64: u8 code_len[256]                       */
+#define F_OFF_TENS      64   /* u64: {u64 offset, u64 numel}[n_tensors]     */
+#define F_OFF_GS        72   /* u64: u64 group_start[n_groups + 1]          */
+#define F_OFF_GAP       80   /* u64: u8 gap[n_chunks]                       */
+#define F_OFF_STREAM    88   /* u64: stream bytes                           */
+#define F_STREAM_BYTES  96   /* u64: 8 * n_chunks + 16 (zero padded)        */
+#define F_OFF_SM       104   /* u64: u8 sm[n]                               */
+#define F_TOTAL        112   /* u64: whole container size                   */
+
+static uint64_t rd(const uint8_t* p, int nbytes) {
+    uint64_t v = 0;
+    for (int i = nbytes - 1; i >= 0; --i) v = (v << 8) | p[i];
+    return v;
+}
+static void wr(uint8_t* p, uint64_t v, int nbytes) {
+    for (int i = 0; i < nbytes; ++i) { p[i] = (uint8_t)(v & 0xFF); v >>= 8; }
+}
+static uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+static uint64_t ceil_div(uint64_t x, uint64_t a) { return (x + a - 1) / a; }
+
+/* ------------------------------------------------------------------------ */
+/* Planes [DF11 abstract; L2-7B abstract]                                   */
+/* ------------------------------------------------------------------------ */
+void orc_split_planes(const uint16_t* w, uint64_t n, uint8_t* exp_out, uint8_t* sm_out) {
+    for (uint64_t i = 0; i < n; ++i) {
+        uint16_t b = w[i];
+        exp_out[i] = (uint8_t)((b >> 7) & 0xFF);
+        sm_out[i] = (uint8_t)(((b >> 8) & 0x80) | (b & 0x7F));
+    }
+}
+
+void orc_join_planes(const uint8_t* exp_in, const uint8_t* sm_in, uint64_t n, uint16_t* w_out) {
+    for (uint64_t i = 0; i < n; ++i) {
+        uint16_t e = exp_in[i], s = sm_in[i];
+        w_out[i] = (uint16_t)(((s & 0x80) << 8) | (e << 7) | (s & 0x7F));
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Huffman's construction, unrestricted depth [LW analogy; DF11 abstract]   */
+/* ------------------------------------------------------------------------ */
+int orc_heap_huffman(const uint64_t counts[256], uint8_t lens[256]) {
+    /* nodes 0..255 are leaves, 256.. are merged trees */
+    uint64_t weight[512];
+    int minsym[512], parent[512], alive[512];
+    int n_nodes = 256, n_alive = 0;
+    for (int s = 0; s < 256; ++s) {
+        lens[s] = 0;
+        weight[s] = counts[s];
+        minsym[s] = s;
+        parent[s] = -1;
+        alive[s] = counts[s] > 0;
+        n_alive += alive[s];
+    }
+    if (n_alive == 0) return ORC_OK;
+    if (n_alive == 1) {
+        for (int s = 0; s < 256; ++s) if (alive[s]) lens[s] = 1;
+        return ORC_OK;
+    }
+    while (n_alive > 1) {
+        /* pick the two lightest live trees; ties go to the smaller symbol */
+        int a = -1, b = -1;
+        for (int i = 0; i < n_nodes; ++i) {
+            if (!alive[i]) continue;
+            if (a < 0 || weight[i] < weight[a] || (weight[i] == weight[a] && minsym[i] < minsym[a])) {
+                b = a;
+                a = i;
+            } else if (b < 0 || weight[i] < weight[b] || (weight[i] == weight[b] && minsym[i] < minsym[b])) {
+                b = i;
+            }
+        }
+        int p = n_nodes++;
+        weight[p] = weight[a] + weight[b];
+        minsym[p] = minsym[a] < minsym[b] ? minsym[a] : minsym[b];
+        parent[p] = -1;
+        alive[p] = 1;
+        alive[a] = alive[b] = 0;
+        parent[a] = parent[b] = p;
+        n_alive -= 1;
+    }
+    for (int s = 0; s < 256; ++s) {
+        if (counts[s] == 0) continue;
+        int d = 0;
+        for (int v = s; parent[v] >= 0; v = parent[v]) ++d;
+        lens[s] = (uint8_t)d;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Package-merge (Larmore & Hirschberg): optimal code with lengths <= L.    */
+/* Each item carries how many times every present symbol occurs in it; the  */
+/* final length of a symbol is its number of occurrences among the first    */
+/* 2m-2 items of the last list.                                             */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    uint64_t w;
+    uint8_t cnt[256];   /* indexed by rank among present symbols */
+} pm_item;
+
+int orc_package_merge(const uint64_t counts[256], uint32_t max_len, uint8_t lens[256]) {
+    int sym[256], m = 0;
+    for (int s = 0; s < 256; ++s) { lens[s] = 0; if (counts[s]) sym[m++] = s; }
+    if (max_len < 1 || max_len > 32) return ORC_E_ARG;
+    if (m == 0) return ORC_OK;
+    if (m == 1) { lens[sym[0]] = 1; return ORC_OK; }
+    if (max_len < 31 && ((uint64_t)1 << max_len) < (uint64_t)m) return ORC_E_ARG;
+
+    /* present symbols sorted by (count, symbol): insertion sort, m <= 256 */
+    for (int i = 1; i < m; ++i) {
+        int s = sym[i], j = i - 1;
+        while (j >= 0 && (counts[sym[j]] > counts[s] || (counts[sym[j]] == counts[s] && sym[j] > s))) {
+            sym[j + 1] = sym[j];
+            --j;
+        }
+        sym[j + 1] = s;
+    }
+    pm_item* leaves = (pm_item*)calloc((size_t)m, sizeof(pm_item));
+    pm_item* list = (pm_item*)calloc((size_t)2 * m, sizeof(pm_item));
+    pm_item* next = (pm_item*)calloc((size_t)2 * m, sizeof(pm_item));
+    pm_item* pk = (pm_item*)calloc((size_t)m, sizeof(pm_item));
+    if (!leaves || !list || !next || !pk) {
+        free(leaves); free(list); free(next); free(pk);
+        return ORC_E_NOMEM;
+    }
+    for (int k = 0; k < m; ++k) { leaves[k].w = counts[sym[k]]; leaves[k].cnt[k] = 1; }
+    memcpy(list, leaves, (size_t)m * sizeof(pm_item));
+    int size = m;
+    /* lists for depths L-1 down to 1: package pairs, then merge with leaves */
+    for (uint32_t level = 1; level < max_len; ++level) {
+        int np = size / 2;
+        for (int j = 0; j < np; ++j) {
+            pk[j].w = list[2 * j].w + list[2 * j + 1].w;
+            for (int k = 0; k < m; ++k) pk[j].cnt[k] = (uint8_t)(list[2 * j].cnt[k] + list[2 * j + 1].cnt[k]);
+        }
+        int a = 0, b = 0, o = 0;
+        while (a < m || b < np) {
+            if (b >= np || (a < m && leaves[a].w <= pk[b].w)) next[o++] = leaves[a++];
+            else next[o++] = pk[b++];
+        }
+        pm_item* t = list; list = next; next = t;
+        size = o;
+    }
+    int take = 2 * m - 2;
+    for (int j = 0; j < take; ++j)
+        for (int k = 0; k < m; ++k) lens[sym[k]] = (uint8_t)(lens[sym[k]] + list[j].cnt[k]);
+    free(leaves); free(list); free(next); free(pk);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Canonical codes (RFC 1951 section 3.2.2 convention)                      */
+/* ------------------------------------------------------------------------ */
+int orc_canonical_codes(const uint8_t lens[256], uint32_t codes[256]) {
+    int order[256], m = 0;
+    for (int s = 0; s < 256; ++s) { codes[s] = 0; if (lens[s]) order[m++] = s; }
+    /* sort by (length, symbol) */
+    for (int i = 1; i < m; ++i) {
+        int s = order[i], j = i - 1;
+        while (j >= 0 && (lens[order[j]] > lens[s] || (lens[order[j]] == lens[s] && order[j] > s))) {
+            order[j + 1] = order[j];
+            --j;
+        }
+        order[j + 1] = s;
+    }
+    uint64_t code = 0;
+    int prev_len = 0;
+    for (int i = 0; i < m; ++i) {
+        int s = order[i], L = lens[s];
+        if (L > 32) return ORC_E_LENGTHS;
+        if (i > 0) code = (code + 1) << (L - prev_len);
+        else code = 0;
+        if (code >> L) return ORC_E_KRAFT;   /* ran out of codes: over-subscribed */
+        codes[s] = (uint32_t)code;
+        prev_len = L;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Writer (serial).  Container layout as in the header comment.             */
+/* ------------------------------------------------------------------------ */
+int orc_encode(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
+               uint32_t max_code_len, uint32_t G, uint8_t** blob, uint64_t* blob_bytes) {
+    if (!blob || !blob_bytes || (n && !w)) return ORC_E_ARG;
+    if (max_code_len < 1 || max_code_len > MAX_LEN_LIMIT || G < 1) return ORC_E_ARG;
+    uint64_t one_numel = n;
+    if (!numels) { numels = &one_numel; n_tensors = 1; }
+    uint64_t sum = 0;
+    for (uint32_t t = 0; t < n_tensors; ++t) sum += numels[t];
+    if (sum != n) return ORC_E_ARG;
+
+    uint8_t* e = (uint8_t*)malloc(n ? n : 1);
+    uint8_t* sm = (uint8_t*)malloc(n ? n : 1);
+    if (!e || !sm) { free(e); free(sm); return ORC_E_NOMEM; }
+    orc_split_planes(w, n, e, sm);
+
+    uint64_t hist[256] = {0};
+    for (uint64_t i = 0; i < n; ++i) hist[e[i]]++;
+    uint8_t lens[256];
+    uint32_t codes[256];
+    int st = orc_package_merge(hist, max_code_len, lens);
+    if (st == ORC_OK) st = orc_canonical_codes(lens, codes);
+    if (st != ORC_OK) { free(e); free(sm); return st; }
+
+    uint64_t bits = 0;
+    for (int s = 0; s < 256; ++s) bits += hist[s] * lens[s];
+    uint64_t n_chunks = ceil_div(bits, CHUNK_BITS);
+    uint64_t n_groups = ceil_div(n_chunks, G);
+    uint64_t stream_bytes = 8 * n_chunks + 16;
+
+    uint64_t off_len = HDR_BYTES;
+    uint64_t off_tens = round_up(off_len + 256, ALIGN);
+    uint64_t off_gs = round_up(off_tens + 16ull * n_tensors, ALIGN);
+    uint64_t off_gap = round_up(off_gs + 8 * (n_groups + 1), ALIGN);
+    uint64_t off_stream = round_up(off_gap + n_chunks, ALIGN);
+    uint64_t off_sm = round_up(off_stream + stream_bytes, ALIGN);
+    uint64_t total = round_up(off_sm + n, ALIGN);
+
+    uint8_t* b = (uint8_t*)calloc(total, 1);
+    if (!b) { free(e); free(sm); return ORC_E_NOMEM; }
+
+    uint8_t* stream = b + off_stream;
+    uint8_t* gap = b + off_gap;
+    uint8_t* gs = b + off_gs;
+    uint64_t pos = 0, next_chunk = 0, next_group = 0;
+    for (uint64_t i = 0; i < n; ++i) {
+        /* auxiliary variables [DF11 abstract (ii)] for every chunk / group
+         * whose first codeword start is this one */
+        while (next_chunk < n_chunks && CHUNK_BITS * next_chunk <= pos) {
+            gap[next_chunk] = (uint8_t)(pos - CHUNK_BITS * next_chunk);
+            ++next_chunk;
+        }
+        while (next_group < n_groups && CHUNK_BITS * G * next_group <= pos) {
+            wr(gs + 8 * next_group, i, 8);
+            ++next_group;
+        }
+        int L = lens[e[i]];
+        uint32_t c = codes[e[i]];
+        for (int k = L - 1; k >= 0; --k) {
+            if ((c >> k) & 1u) stream[pos >> 3] |= (uint8_t)(0x80u >> (pos & 7));
+            ++pos;
+        }
+    }
+    while (next_chunk < n_chunks) { gap[next_chunk] = (uint8_t)(bits - CHUNK_BITS * next_chunk); ++next_chunk; }
+    while (next_group < n_groups) { wr(gs + 8 * next_group, n, 8); ++next_group; }
+    wr(gs + 8 * n_groups, n, 8);
+
+    memcpy(b + off_len, lens, 256);
+    uint64_t acc = 0;
+    for (uint32_t t = 0; t < n_tensors; ++t) {
+        wr(b + off_tens + 16ull * t, acc, 8);
+        wr(b + off_tens + 16ull * t + 8, numels[t], 8);
+        acc += numels[t];
+    }
+    if (n) memcpy(b + off_sm, sm, n);
+
+    memcpy(b + F_MAGIC, "WCBF", 4);
+    wr(b + F_VERSION, 1, 2);
+    wr(b + F_FLAGS, 0, 2);
+    wr(b + F_MAXLEN, max_code_len, 1);
+    wr(b + F_CHUNKBITS, CHUNK_BITS, 1);
+    wr(b + F_G, G, 4);
+    wr(b + F_NTENS, n_tensors, 4);
+    wr(b + F_N, n, 8);
+    wr(b + F_SBITS, bits, 8);
+    wr(b + F_NCHUNKS, n_chunks, 8);
+    wr(b + F_NGROUPS, n_groups, 8);
+    wr(b + F_OFF_LEN, off_len, 8);
+    wr(b + F_OFF_TENS, off_tens, 8);
+    wr(b + F_OFF_GS, off_gs, 8);
+    wr(b + F_OFF_GAP, off_gap, 8);
+    wr(b + F_OFF_STREAM, off_stream, 8);
+    wr(b + F_STREAM_BYTES, stream_bytes, 8);
+    wr(b + F_OFF_SM, off_sm, 8);
+    wr(b + F_TOTAL, total, 8);
+
+    free(e);
+    free(sm);
+    *blob = b;
+    *blob_bytes = total;
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Reader                                                                   */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    uint32_t max_len, G, n_tensors;
+    uint64_t n, stream_bits, n_chunks, n_groups;
+    uint64_t off_len, off_tens, off_gs, off_gap, off_stream, stream_bytes, off_sm, total;
+} hdr_t;
+
+static int parse_header(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
+    if (!blob || bytes < HDR_BYTES) return ORC_E_TRUNC;
+    if (memcmp(blob + F_MAGIC, "WCBF", 4) != 0) return ORC_E_MAGIC;
+    if (rd(blob + F_VERSION, 2) != 1 || rd(blob + F_FLAGS, 2) != 0) return ORC_E_MAGIC;
+    if (rd(blob + F_CHUNKBITS, 1) != CHUNK_BITS) return ORC_E_MAGIC;
+    if (rd(blob + F_RES0, 2) != 0 || rd(blob + F_RES1, 4) != 0) return ORC_E_MAGIC;
+    for (uint32_t k = 120; k < HDR_BYTES; ++k) if (blob[k]) return ORC_E_MAGIC;
+    h->max_len = (uint32_t)rd(blob + F_MAXLEN, 1);
+    h->G = (uint32_t)rd(blob + F_G, 4);
+    h->n_tensors = (uint32_t)rd(blob + F_NTENS, 4);
+    h->n = rd(blob + F_N, 8);
+    h->stream_bits = rd(blob + F_SBITS, 8);
+    h->n_chunks = rd(blob + F_NCHUNKS, 8);
+    h->n_groups = rd(blob + F_NGROUPS, 8);
+    h->off_len = rd(blob + F_OFF_LEN, 8);
+    h->off_tens = rd(blob + F_OFF_TENS, 8);
+    h->off_gs = rd(blob + F_OFF_GS, 8);
+    h->off_gap = rd(blob + F_OFF_GAP, 8);
+    h->off_stream = rd(blob + F_OFF_STREAM, 8);
+    h->stream_bytes = rd(blob + F_STREAM_BYTES, 8);
+    h->off_sm = rd(blob + F_OFF_SM, 8);
+    h->total = rd(blob + F_TOTAL, 8);
+    if (h->max_len < 1 || h->max_len > MAX_LEN_LIMIT || h->G < 1) return ORC_E_MAGIC;
+    /* derived sizes (guard the multiplications against absurd values first) */
+    if (h->n > ((uint64_t)1 << 48) || h->stream_bits > ((uint64_t)1 << 56)) return ORC_E_SIZES;
+    if (h->n_chunks != ceil_div(h->stream_bits, CHUNK_BITS)) return ORC_E_SIZES;
+    if (h->n_groups != ceil_div(h->n_chunks, h->G)) return ORC_E_SIZES;
+    if (h->stream_bytes != 8 * h->n_chunks + 16) return ORC_E_SIZES;
+    if (h->stream_bits > h->n * (uint64_t)h->max_len || h->stream_bits < h->n) return ORC_E_SIZES;
+    /* sections: aligned, in order, inside the blob */
+    const uint64_t offs[6] = {h->off_len, h->off_tens, h->off_gs, h->off_gap, h->off_stream, h->off_sm};
+    const uint64_t lens[6] = {256, 16ull * h->n_tensors, 8 * (h->n_groups + 1), h->n_chunks,
+                              h->stream_bytes, h->n};
+    uint64_t lo = HDR_BYTES;
+    for (int k = 0; k < 6; ++k) {
+        if (offs[k] % ALIGN || offs[k] < lo) return ORC_E_TRUNC;
+        lo = offs[k] + lens[k];
+    }
+    if (h->total < lo || h->total > bytes) return ORC_E_TRUNC;
+    return ORC_OK;
+}
+
+int orc_header(const uint8_t* blob, uint64_t blob_bytes, orc_report* rep) {
+    hdr_t h;
+    int st = parse_header(blob, blob_bytes, &h);
+    if (st != ORC_OK) return st;
+    if (rep) {
+        memset(rep, 0, sizeof(*rep));
+        rep->n_elems = h.n;
+        rep->stream_bits = h.stream_bits;
+        rep->n_chunks = h.n_chunks;
+        rep->n_groups = h.n_groups;
+        rep->n_tensors = h.n_tensors;
+        rep->chunks_per_group = h.G;
+        rep->max_code_len = h.max_len;
+    }
+    return ORC_OK;
+}
+
+/* explicit binary trie of the canonical code */
+typedef struct {
+    int child[2];
+    int sym;      /* -1 for an inner node */
+} trie_node;
+
+int orc_decode(const uint8_t* blob, uint64_t bytes, uint16_t* out, uint64_t out_cap, orc_report* rep) {
+    hdr_t h;
+    int st = parse_header(blob, bytes, &h);
+    if (st != ORC_OK) return st;
+    if (h.n > out_cap || (h.n && !out)) return ORC_E_OUTSIZE;
+
+    /* tensor table must be a partition of [0, n) in order */
+    {
+        uint64_t acc = 0;
+        for (uint32_t t = 0; t < h.n_tensors; ++t) {
+            uint64_t off = rd(blob + h.off_tens + 16ull * t, 8);
+            uint64_t num = rd(blob + h.off_tens + 16ull * t + 8, 8);
+            if (off != acc || num > h.n - acc) return ORC_E_TENSORS;
+            acc += num;
+        }
+        if (acc != h.n) return ORC_E_TENSORS;
+    }
+
+    /* code lengths and Kraft's sum, exactly, in units of 2^-24 */
+    const uint8_t* lens = blob + h.off_len;
+    uint64_t kraft = 0;
+    uint32_t m = 0, longest = 0;
+    for (int s = 0; s < 256; ++s) {
+        if (!lens[s]) continue;
+        if (lens[s] > h.max_len) return ORC_E_LENGTHS;
+        kraft += (uint64_t)1 << (MAX_LEN_LIMIT - lens[s]);
+        ++m;
+        if (lens[s] > longest) longest = lens[s];
+    }
+    if (m >= 2 && kraft != ((uint64_t)1 << MAX_LEN_LIMIT)) return ORC_E_KRAFT;
+    if (m == 1 && longest != 1) return ORC_E_KRAFT;
+    if (m == 0 && h.n != 0) return ORC_E_KRAFT;
+
+    uint32_t codes[256];
+    st = orc_canonical_codes(lens, codes);
+    if (st != ORC_OK) return st;
+
+    /* build the trie one code bit at a time, rejecting prefix conflicts */
+    int cap_nodes = 256 * (MAX_LEN_LIMIT + 1) + 1;
+    trie_node* T = (trie_node*)malloc((size_t)cap_nodes * sizeof(trie_node));
+    if (!T) return ORC_E_NOMEM;
+    int n_nodes = 1;
+    T[0].child[0] = T[0].child[1] = -1;
+    T[0].sym = -1;
+    for (int s = 0; s < 256 && st == ORC_OK; ++s) {
+        int L = lens[s];
+        if (!L) continue;
+        int node = 0;
+        for (int k = L - 1; k >= 0; --k) {
+            if (T[node].sym >= 0) { st = ORC_E_PREFIX; break; }
+            int bit = (int)((codes[s] >> k) & 1u);
+            int nxt = T[node].child[bit];
+            if (k == 0) {
+                if (nxt >= 0) { st = ORC_E_PREFIX; break; }
+                nxt = n_nodes++;
+                T[nxt].child[0] = T[nxt].child[1] = -1;
+                T[nxt].sym = s;
+                T[node].child[bit] = nxt;
+            } else {
+                if (nxt < 0) {
+                    nxt = n_nodes++;
+                    T[nxt].child[0] = T[nxt].child[1] = -1;
+                    T[nxt].sym = -1;
+                    T[node].child[bit] = nxt;
+                }
+                node = nxt;
+            }
+        }
+    }
+    if (st != ORC_OK) { free(T); return st; }
+
+    /* serial bit-by-bit decode; re-derive the auxiliary variables from the
+     * codeword starts actually observed and compare with the stored ones */
+    const uint8_t* stream = blob + h.off_stream;
+    const uint8_t* gap = blob + h.off_gap;
+    const uint8_t* gs = blob + h.off_gs;
+    const uint8_t* sm = blob + h.off_sm;
+    uint64_t hist[256] = {0};
+    uint64_t pos = 0, next_chunk = 0, next_group = 0;
+    for (uint64_t i = 0; i < h.n && st == ORC_OK; ++i) {
+        while (next_chunk < h.n_chunks && CHUNK_BITS * next_chunk <= pos) {
+            uint64_t want = pos - CHUNK_BITS * next_chunk;
+            if (want >= CHUNK_BITS || gap[next_chunk] != want) { st = ORC_E_GAP; break; }
+            ++next_chunk;
+        }
+        while (st == ORC_OK && next_group < h.n_groups && CHUNK_BITS * h.G * next_group <= pos) {
+            if (rd(gs + 8 * next_group, 8) != i) { st = ORC_E_GROUP; break; }
+            ++next_group;
+        }
+        if (st != ORC_OK) break;
+        int node = 0;
+        for (;;) {
+            if (pos >= h.stream_bits) { st = ORC_E_STREAM; break; }
+            int bit = (stream[pos >> 3] >> (7 - (pos & 7))) & 1;
+            ++pos;
+            node = T[node].child[bit];
+            if (node < 0) { st = ORC_E_STREAM; break; }
+            if (T[node].sym >= 0) break;
+        }
+        if (st != ORC_OK) break;
+        uint8_t e = (uint8_t)T[node].sym;
+        hist[e]++;
+        uint16_t s = sm[i];
+        out[i] = (uint16_t)(((s & 0x80) << 8) | ((uint16_t)e << 7) | (s & 0x7F));
+    }
+    free(T);
+    if (st != ORC_OK) return st;
+    if (pos != h.stream_bits) return ORC_E_STREAM;
+    while (next_chunk < h.n_chunks) {
+        uint64_t want = h.stream_bits - CHUNK_BITS * next_chunk;
+        if (want >= CHUNK_BITS || gap[next_chunk] != want) return ORC_E_GAP;
+        ++next_chunk;
+    }
+    while (next_group < h.n_groups) {
+        if (rd(gs + 8 * next_group, 8) != h.n) return ORC_E_GROUP;
+        ++next_group;
+    }
+    if (rd(gs + 8 * h.n_groups, 8) != h.n) return ORC_E_GROUP;
+
+    /* every bit after stream_bits, up to the end of the section, is zero */
+    for (uint64_t p = h.stream_bits; p < 8 * h.stream_bytes; ++p) {
+        if ((p & 7) == 0 && p + 8 <= 8 * h.stream_bytes) {
+            if (stream[p >> 3]) return ORC_E_PADDING;
+            p += 7;
+            continue;
+        }
+        if ((stream[p >> 3] >> (7 - (p & 7))) & 1) return ORC_E_PADDING;
+    }
+
+    if (rep) {
+        memset(rep, 0, sizeof(*rep));
+        rep->n_elems = h.n;
+        rep->stream_bits = h.stream_bits;
+        rep->n_chunks = h.n_chunks;
+        rep->n_groups = h.n_groups;
+        rep->n_tensors = h.n_tensors;
+        rep->chunks_per_group = h.G;
+        rep->max_code_len = h.max_len;
+        rep->n_symbols = m;
+        rep->longest_code = longest;
+        rep->kraft_num = kraft;
+        double H = 0.0, Lsum = 0.0;
+        for (int s = 0; s < 256; ++s) {
+            rep->hist[s] = hist[s];
+            if (!hist[s]) continue;
+            double p = (double)hist[s] / (double)h.n;
+            H -= p * log2(p);
+            Lsum += (double)hist[s] * (double)lens[s];
+        }
+        rep->entropy_bits = H;
+        rep->mean_code_bits = h.n ? Lsum / (double)h.n : 0.0;
+    }
+    return ORC_OK;
+}
+
+void orc_free(void* p) { free(p); }

@@ -1,0 +1,65 @@
+"""Read-only numpy view of a container's sections, for tests.
+
+Restates the container v1 layout (256-byte header of little-endian fields,
+then 256-byte-aligned sections code_len, tensors, group_start, gap, stream,
+sm) so that tests can inspect what an encoder wrote.  It decodes nothing.
+"""
+from __future__ import annotations
+
+import struct
+
+import numpy as np
+
+HEADER_FIELDS = {
+    "max_code_len": (8, "<B"), "chunk_bits": (9, "<B"), "chunks_per_group": (12, "<I"),
+    "n_tensors": (16, "<I"), "n_elems": (24, "<Q"), "stream_bits": (32, "<Q"), "n_chunks": (40, "<Q"),
+    "n_groups": (48, "<Q"), "off_len": (56, "<Q"), "off_tens": (64, "<Q"), "off_gs": (72, "<Q"),
+    "off_gap": (80, "<Q"), "off_stream": (88, "<Q"), "stream_bytes": (96, "<Q"), "off_sm": (104, "<Q"),
+    "total": (112, "<Q"),
+}
+
+
+def header(blob: np.ndarray) -> dict:
+    raw = bytes(blob[:256])
+    h = {k: struct.unpack_from(fmt, raw, off)[0] for k, (off, fmt) in HEADER_FIELDS.items()}
+    h["magic"] = raw[:4]
+    h["version"] = struct.unpack_from("<H", raw, 4)[0]
+    return h
+
+
+def sections(blob: np.ndarray) -> dict:
+    h = header(blob)
+    n, nc, ng, nt = h["n_elems"], h["n_chunks"], h["n_groups"], h["n_tensors"]
+    s = dict(h)
+    s["code_len"] = blob[h["off_len"]:h["off_len"] + 256]
+    s["tensors"] = blob[h["off_tens"]:h["off_tens"] + 16 * nt].view(np.uint64).reshape(nt, 2)
+    s["group_start"] = blob[h["off_gs"]:h["off_gs"] + 8 * (ng + 1)].view(np.uint64)
+    s["gap"] = blob[h["off_gap"]:h["off_gap"] + nc]
+    s["stream"] = blob[h["off_stream"]:h["off_stream"] + h["stream_bytes"]]
+    s["sm"] = blob[h["off_sm"]:h["off_sm"] + n]
+    return s
+
+
+def expected_metadata(exps: np.ndarray, code_len: np.ndarray, chunks_per_group: int):
+    """Auxiliary variables recomputed from first principles with numpy.
+
+    Codeword i starts at the sum of the lengths before it.  gap[c] is the
+    offset of the first start at or after bit 64c (stream end if none);
+    group_start[g] is the index of the first element starting at or after
+    bit 64*G*g (n if none), followed by n.
+    """
+    lens = code_len.astype(np.int64)[exps.astype(np.int64)]
+    n = exps.size
+    starts = np.zeros(n, np.int64)
+    if n:
+        starts[1:] = np.cumsum(lens)[:-1]
+    total = int(lens.sum())
+    n_chunks = -(-total // 64)
+    n_groups = -(-n_chunks // chunks_per_group)
+    starts_s = np.append(starts, total)          # stream end acts as a sentinel start
+    c_bits = 64 * np.arange(n_chunks, dtype=np.int64)
+    gap = starts_s[np.searchsorted(starts_s, c_bits, side="left")] - c_bits
+    g_bits = 64 * chunks_per_group * np.arange(n_groups, dtype=np.int64)
+    gs = np.searchsorted(starts, g_bits, side="left")
+    gs = np.append(gs, n).astype(np.uint64)
+    return total, gap, gs
