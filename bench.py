@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark: block-level decode of entropy-coded bf16 weights on one MI355X.
+
+One step = one call of wc_decode_async: a single kernel launch that decodes
+every tensor of an 8B-shape transformer block (q, k, v, o, gate, up, down and
+two RMSNorm vectors; 218,112,000 bf16 with one shared codebook) from its
+container in HBM into bf16 in HBM.  Inputs are resident in HBM before the
+timed region; several (container, output) copies are rotated so that no step
+reads what the previous one left in the 256 MB Infinity Cache.
+
+Prints one JSON line:
+  value     decompressed bf16 GB/s = 2 * n_elems * steps / elapsed
+  roofline  algorithmic bytes of the decode kernel (container bytes it must
+            read + 2 B per element written) / its average launch duration
+            (HIP events on the launch stream), against 8 TB/s HBM3E peak;
+            `traffic` = HBM bytes from rocprofv3 FETCH_SIZE/WRITE_SIZE runs
+            recorded under profiles/ (null if the kernel source changed since)
+  cpu_baseline  the CPU oracle's serial decode of the same container on one
+            host core (reported baseline, not a target)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decompressed bf16 GB/s and % of HBM roofline (1 MI355X), bit-exact"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "lossless_entropy_coded_amd", "csrc", "decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_block_8b_traffic.json")
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if still valid."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_sha() or rec.get("workload") != workload:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="block_8b",
+                    help="synthetic workload (default: block_8b, the 8B-shape transformer block)")
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain 1 GiB device copy instead (for scaling HBM counters)")
+    return ap.parse_args()
+
+
+def aligned_device_copy(torch, blob, align=256):
+    owner = torch.empty(blob.size + align, dtype=torch.uint8, device="cuda")
+    off = (-owner.data_ptr()) % align
+    view = owner[off:off + blob.size]
+    view.copy_(torch.from_numpy(blob))
+    return owner, view
+
+
+def copy_calibration(args):
+    import torch
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_step": nbytes, "bytes_written_per_step": nbytes,
+                      "steps": args.steps, "GBps_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (decode is per-GPU and needs no collectives); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args)
+        return
+
+    from lossless_entropy_coded_amd import wc
+    from lossless_entropy_coded_amd.synth import make_workload, workload_spec
+
+    t_gen = time.perf_counter()
+    wl = make_workload(args.workload)
+    blob = wc.encode_host(wl.tensors())
+    t_gen = time.perf_counter() - t_gen
+    n = wl.n
+    plan = wc.Plan(blob, device=0)
+    st = plan.stats()
+    stream_bits = st["stream_bits"]
+    n_chunks = -(-stream_bits // 64)
+    alg_read = n + -(-stream_bits // 8) + n_chunks + 8 * (st["n_groups"] + 1)
+    alg_bytes = alg_read + 2 * n
+
+    per_copy = blob.size + 2 * n
+    copies = max(2, min(64, math.ceil((1 << 30) / per_copy)))
+    blobs, outs, owners = [], [], []
+    for _ in range(copies):
+        own, view = aligned_device_copy(torch, blob)
+        owners.append(own)
+        blobs.append(view)
+        outs.append(torch.empty(n, dtype=torch.int16, device="cuda"))
+    ref = torch.from_numpy(wl.bits.view(np.int16)).cuda()
+
+    stream = torch.cuda.current_stream()
+    wc.decode_async(plan, blobs[0], outs[0], stream)
+    torch.cuda.synchronize()
+    if not torch.equal(outs[0], ref):
+        print("bench.py: decode is NOT bit-exact", file=sys.stderr)
+        sys.exit(3)
+
+    for k in range(args.warmup):
+        wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for k in range(args.steps):
+        starts[k].record(stream)
+        wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
+        ends[k].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kernel_avg_ms = sum(kernel_ms) / len(kernel_ms)
+    bit_exact = all(torch.equal(outs[k % copies], ref) for k in range(min(copies, args.steps)))
+    if not bit_exact:
+        print("bench.py: timed outputs are NOT bit-exact", file=sys.stderr)
+        sys.exit(3)
+
+    ms_per_step = total_ms / args.steps
+    value = 2.0 * n / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / (kernel_avg_ms * 1e-3) / 1e9
+
+    cpu = None
+    if args.cpu_baseline == "on":
+        import oracle
+        t = time.perf_counter()
+        dec = oracle.decode(blob)
+        t = time.perf_counter() - t
+        assert np.array_equal(dec, wl.bits)
+        cpu = {"value": 2.0 * n / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"the whole {args.workload} container ({n} elements), serial bit-by-bit trie decode "
+                         f"with every container check, {t:.2f} s on one host core"}
+
+    desc = workload_spec(args.workload)[0]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic: seeded bf16 weights, transformer-block shapes and distributions",
+        "config": {
+            "workload": f"{args.workload}: {desc}",
+            "n_elems": n,
+            "n_tensors": len(wl.numels),
+            "container_bytes": int(blob.size),
+            "compression_ratio": round(2.0 * n / blob.size, 4),
+            "mean_code_bits": round(stream_bits / n, 4),
+            "launches_per_step": 1,
+            "lut_bits": st["lut_bits"],
+            "grid": st["grid"],
+            "lds_bytes": st["lds_bytes"],
+            "rotating_copies": copies,
+            "bit_exact": bit_exact,
+            "host_prep_s": round(t_gen, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic(args.workload),
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "kernel_avg_ms": round(kernel_avg_ms, 5),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    plan.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * wc.h -- C ABI of libwc: lossless entropy-coded bf16 weights, decoded on
+ * demand on an MI355X (gfx950).
+ *
+ * The method (pages: "70% Size, 100% Accuracy: Lossless LLM Compression for
+ * Efficient GPU Inference via Dynamic-Length Float" (DFloat11), abstract;
+ * "From a Lossless (~1.5:1) Compression Algorithm for Llama2 7B Weights ...",
+ * abstract; "Huff-LLM: End-to-End Lossless Compression for Efficient LLM
+ * Inference", abstract):
+ *   each bf16 weight is split into its 8-bit exponent, which is Huffman-coded
+ *   from the exponent histogram, and a raw byte holding sign and mantissa.
+ *   Weights are prepared once on the host, stay compressed in memory, and are
+ *   decoded on demand to bit-identical bf16 before compute kernels read them.
+ *   One decode call handles a whole transformer block (DFloat11 abstract,
+ *   design point (iii)); the kernel uses compact decode tables in on-chip
+ *   memory (point (i)) and a two-phase count / scan / decode scheme driven by
+ *   small per-chunk and per-group auxiliary variables (point (ii)).
+ *
+ * Container v1 (all fields little-endian; every section 256-byte aligned):
+ *   header (256 B): "WCBF", u16 version=1, u16 flags=0, u8 max_code_len,
+ *     u8 chunk_bits=64, u16 0, u32 chunks_per_group, u32 n_tensors, u32 0,
+ *     u64 n_elems, u64 stream_bits, u64 n_chunks, u64 n_groups,
+ *     u64 offsets of code_len / tensors / group_start / gap / stream,
+ *     u64 stream_bytes, u64 offset of sm, u64 total_bytes; rest zero.
+ *   code_len    u8[256]   canonical Huffman code length per exponent value
+ *                         (0 = absent), at most max_code_len (<= 24);
+ *   tensors     {u64 elem_offset, u64 numel}[n_tensors], a partition of
+ *                         [0, n_elems) in order;
+ *   group_start u64[n_groups+1]: index of the first element whose codeword
+ *                         starts at or after bit 64*G*g; last entry n_elems;
+ *   gap         u8[n_chunks]: bit offset, inside 64-bit chunk c, of the first
+ *                         codeword starting at or after bit 64c (or of the
+ *                         stream end);
+ *   stream      exponent codes, MSB-first, n_chunks*8 + 16 bytes, zero padded;
+ *   sm          u8[n_elems]: sign bit << 7 | 7 mantissa bits.
+ *
+ * Status codes: 0 on success, a negative WC_ERR_* value otherwise.  No C++
+ * exception ever crosses this interface.
+ */
+#ifndef WC_H
+#define WC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define WC_OK                    0
+#define WC_ERR_INVALID_ARG      -1   /* NULL pointer, misaligned pointer, bad option          */
+#define WC_ERR_NOMEM            -2   /* host or device allocation failed                      */
+#define WC_ERR_HIP              -3   /* a HIP runtime call or kernel launch failed             */
+#define WC_ERR_UNSUPPORTED      -4   /* valid container this build cannot decode (e.g. G)     */
+#define WC_ERR_BAD_MAGIC        -10  /* magic, version, flags or a fixed field is wrong       */
+#define WC_ERR_TRUNCATED        -11  /* blob shorter than the header or total_bytes           */
+#define WC_ERR_SECTION_BOUNDS   -12  /* a section is misaligned, out of order or outside blob */
+#define WC_ERR_CODE_LENGTHS     -13  /* a code length > max_code_len, or no symbols for n > 0 */
+#define WC_ERR_KRAFT            -14  /* code lengths do not form a complete prefix code       */
+#define WC_ERR_GAP              -15  /* a per-chunk gap is out of range                        */
+#define WC_ERR_GROUP_START      -16  /* group starts not monotone, too far apart, or != n     */
+#define WC_ERR_STREAM_BITS      -17  /* stream_bits / n_chunks / n_groups / stream_bytes wrong */
+#define WC_ERR_TENSOR_TABLE     -18  /* tensor table is not an in-order partition of [0, n)   */
+
+/* ---- host encoder ------------------------------------------------------ */
+typedef struct {
+    uint32_t max_code_len;      /* 1..24; 0 selects the default 24                      */
+    uint32_t chunk_bytes;       /* must be 8 (or 0 for the default)                     */
+    uint32_t chunks_per_group;  /* G >= 1; 0 selects the default 256.  The GPU decoder  */
+                                /* of this build accepts only G = 256.                  */
+    uint32_t n_threads;         /* host threads for encoding; 0 = all hardware threads  */
+} wc_encode_opts;
+
+/*
+ * wc_encode_host -- offline preparation of one container from n_tensors bf16
+ * tensors (the weight-preparation step of the pages: the LazyWeights review,
+ * practical implications, needs nothing beyond preparing the weights; Huff-LLM
+ * abstract keeps them compressed everywhere).
+ *   tensors[k]  host pointer to numels[k] bf16 bit patterns (uint16), k < n_tensors;
+ *               may be NULL only when numels[k] == 0.
+ *   opts        NULL for defaults.
+ *   *blob       receives a library-allocated host buffer of *blob_bytes bytes,
+ *               256-byte aligned; release it with wc_free_host.
+ * All tensors share one codebook (block-level decode).  The sum of numels
+ * must be below 2^40.  Returns WC_ERR_INVALID_ARG for bad arguments,
+ * WC_ERR_NOMEM if the buffer cannot be allocated.
+ */
+int wc_encode_host(const uint16_t* const* tensors, const uint64_t* numels, uint32_t n_tensors,
+                   const wc_encode_opts* opts, uint8_t** blob, uint64_t* blob_bytes);
+
+/* Release a buffer returned by wc_encode_host (NULL is ignored). */
+void wc_free_host(uint8_t* blob);
+
+/* ---- planning ------------------------------------------------------------ */
+typedef struct wc_plan_s wc_plan_t;   /* opaque, immutable after creation */
+
+/*
+ * wc_plan -- validate a container held in host memory and prepare decoding on
+ * HIP device hip_device: parses and checks every section (each failure has
+ * its own WC_ERR_* code), builds the decode tables for the container's
+ * codebook on that device (a small plan-owned device buffer, freed by
+ * wc_plan_destroy) and chooses the launch configuration.  The host blob is
+ * read only during this call.  The device copy of the same bytes that is
+ * later passed to wc_decode_async is owned by the caller.
+ */
+int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_device, wc_plan_t** plan);
+
+/*
+ * wc_plan_info -- element count, tensor count and, if the arrays are not
+ * NULL, each tensor's element offset and size (arrays of n_tensors entries;
+ * call once with NULL arrays to learn n_tensors).  Any output may be NULL.
+ */
+int wc_plan_info(const wc_plan_t* plan, uint64_t* n_elems, uint32_t* n_tensors,
+                 uint64_t* tensor_offsets, uint64_t* tensor_numels);
+
+/*
+ * wc_plan_stats -- container statistics: total container bytes, stream bits,
+ * number of groups, the decode-table index width used by the kernel, the
+ * launch grid (workgroups) and the dynamic LDS bytes per workgroup.
+ */
+int wc_plan_stats(const wc_plan_t* plan, uint64_t* container_bytes, uint64_t* stream_bits,
+                  uint64_t* n_groups, uint32_t* lut_bits, uint32_t* grid, uint32_t* lds_bytes);
+
+/*
+ * wc_decode_async -- decode every tensor of the container in ONE kernel launch
+ * on `stream` (a hipStream_t; NULL = the device's null stream).
+ *   blob_dev  device pointer to the same bytes given to wc_plan, 256-byte aligned;
+ *   out_dev   device pointer to n_elems bf16 words (caller-owned), 16-byte
+ *             aligned; tensor k is out_dev[tensor_offsets[k] ...].
+ * The call returns after the launch; completion is observed by synchronising
+ * the stream.  Only launch errors are reported (WC_ERR_HIP); the kernel never
+ * writes outside out_dev[0, n_elems), even for a corrupted bit stream.
+ * n_elems == 0 is a no-op.  A plan may be used on several streams at once.
+ * The current device must be the plan's device.
+ */
+int wc_decode_async(const wc_plan_t* plan, const void* blob_dev, uint16_t* out_dev, void* stream);
+
+/* Destroy a plan and its device tables (NULL is ignored).  Pending decodes
+ * that use the plan must have completed. */
+void wc_plan_destroy(wc_plan_t* plan);
+
+/* Static, human-readable text for a status code. */
+const char* wc_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WC_H */

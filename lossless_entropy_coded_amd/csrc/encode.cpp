@@ -1,0 +1,288 @@
+// encode.cpp -- host-side container writer of libwc (offline weight preparation).
+//
+// Steps (pages: DFloat11 abstract -- entropy coding of the bf16 representation
+// by symbol frequency; LazyWeights review -- Huffman codes, shorter for common
+// values; "From a Lossless (~1.5:1) Compression Algorithm for Llama2 7B
+// Weights ...", abstract -- lossless coding of bf16 weights):
+//   1. split every bf16 word into its exponent byte and its sign+mantissa byte;
+//   2. histogram the exponents over all tensors of the block (one codebook);
+//   3. optimal code lengths limited to max_code_len (package-merge);
+//   4. canonical codes;
+//   5. pack the codes MSB-first in parallel over element ranges, recording for
+//      every 64-bit chunk the offset of its first codeword and for every group
+//      of G chunks the index of its first element (the auxiliary variables of
+//      the DFloat11 abstract, design point (ii)).
+#include <algorithm>
+#include <array>
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "format.h"
+#include "../../include/wc.h"
+
+namespace wc {
+namespace {
+
+inline uint8_t exponent_of(uint16_t b) { return (uint8_t)(b >> 7); }   // bits 14..7 (bit 15 shifted out)
+inline uint8_t sign_mantissa_of(uint16_t b) { return (uint8_t)(((b >> 8) & 0x80u) | (b & 0x7Fu)); }
+
+// ---------------------------------------------------------------------------
+// Optimal length-limited code: package-merge over a node pool.  A node is a
+// leaf (one symbol) or a package of two nodes of the next-deeper list; the
+// length of a symbol is the number of times its leaf is reached from the
+// first 2m-2 nodes of the shallowest list.
+// ---------------------------------------------------------------------------
+struct PMNode {
+    uint64_t weight;
+    int32_t left, right;   // -1 for a leaf
+    int32_t symbol;        // leaf symbol
+};
+
+int limited_code_lengths(const uint64_t hist[256], uint32_t max_len, uint8_t len[256]) {
+    std::memset(len, 0, 256);
+    std::vector<int> present;
+    for (int s = 0; s < 256; ++s)
+        if (hist[s]) present.push_back(s);
+    const int m = (int)present.size();
+    if (m == 0) return WC_OK;
+    if (m == 1) { len[present[0]] = 1; return WC_OK; }
+    if ((uint64_t)m > (1ull << max_len)) return WC_ERR_INVALID_ARG;
+    std::stable_sort(present.begin(), present.end(),
+                     [&](int a, int b) { return hist[a] < hist[b]; });
+    std::vector<PMNode> pool;
+    pool.reserve((size_t)2 * m * (max_len + 1));
+    std::vector<int32_t> leaves(m);
+    for (int k = 0; k < m; ++k) {
+        leaves[k] = (int32_t)pool.size();
+        pool.push_back({hist[present[k]], -1, -1, present[k]});
+    }
+    std::vector<int32_t> cur = leaves, merged;
+    for (uint32_t depth = max_len; depth > 1; --depth) {
+        merged.clear();
+        size_t li = 0, pi = 0, npk = cur.size() / 2;
+        while (li < leaves.size() || pi < npk) {
+            bool take_leaf;
+            if (pi >= npk) take_leaf = true;
+            else if (li >= leaves.size()) take_leaf = false;
+            else {
+                uint64_t pw = pool[cur[2 * pi]].weight + pool[cur[2 * pi + 1]].weight;
+                take_leaf = pool[leaves[li]].weight <= pw;
+            }
+            if (take_leaf) {
+                merged.push_back(leaves[li++]);
+            } else {
+                int32_t a = cur[2 * pi], b = cur[2 * pi + 1];
+                merged.push_back((int32_t)pool.size());
+                pool.push_back({pool[a].weight + pool[b].weight, a, b, -1});
+                ++pi;
+            }
+        }
+        cur.swap(merged);
+    }
+    std::vector<int32_t> stack;
+    for (int j = 0; j < 2 * m - 2; ++j) {
+        stack.push_back(cur[j]);
+        while (!stack.empty()) {
+            int32_t v = stack.back();
+            stack.pop_back();
+            if (pool[v].left < 0) ++len[pool[v].symbol];
+            else { stack.push_back(pool[v].left); stack.push_back(pool[v].right); }
+        }
+    }
+    return WC_OK;
+}
+
+// Canonical code assignment by per-length counters (shorter codes are
+// numerically smaller; equal lengths follow symbol order).
+void canonical_codes(const uint8_t len[256], uint32_t code[256]) {
+    uint32_t count[kMaxCodeLen + 2] = {0}, next[kMaxCodeLen + 2] = {0};
+    for (int s = 0; s < 256; ++s)
+        if (len[s]) ++count[len[s]];
+    uint32_t c = 0;
+    for (uint32_t L = 1; L <= kMaxCodeLen; ++L) {
+        c = (c + count[L - 1]) << 1;
+        next[L] = c;
+    }
+    for (int s = 0; s < 256; ++s) code[s] = len[s] ? next[len[s]]++ : 0;
+}
+
+// Global element index space over several tensors.
+struct Source {
+    std::vector<const uint16_t*> ptr;
+    std::vector<uint64_t> begin;   // global index of each tensor's first element
+    std::vector<uint64_t> size;
+
+    template <typename F>
+    void for_range(uint64_t i0, uint64_t i1, F&& f) const {   // f(global_index, const uint16_t* p, count)
+        size_t t = std::upper_bound(begin.begin(), begin.end(), i0) - begin.begin() - 1;
+        uint64_t i = i0;
+        while (i < i1) {
+            while (i >= begin[t] + size[t]) ++t;
+            uint64_t k = std::min(i1, begin[t] + size[t]) - i;
+            f(i, ptr[t] + (i - begin[t]), k);
+            i += k;
+        }
+    }
+    uint16_t at(uint64_t i) const {
+        size_t t = std::upper_bound(begin.begin(), begin.end(), i) - begin.begin() - 1;
+        while (size[t] == 0 || i >= begin[t] + size[t]) ++t;
+        return ptr[t][i - begin[t]];
+    }
+};
+
+template <typename F>
+void parallel_for(unsigned nthreads, F&& f) {
+    if (nthreads <= 1) { f(0u); return; }
+    std::vector<std::thread> th;
+    th.reserve(nthreads);
+    for (unsigned t = 0; t < nthreads; ++t) th.emplace_back([&f, t] { f(t); });
+    for (auto& x : th) x.join();
+}
+
+}  // namespace
+}  // namespace wc
+
+extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* numels, uint32_t n_tensors,
+                              const wc_encode_opts* opts, uint8_t** blob, uint64_t* blob_bytes) {
+    using namespace wc;
+    if (!blob || !blob_bytes) return WC_ERR_INVALID_ARG;
+    *blob = nullptr;
+    *blob_bytes = 0;
+    if (n_tensors && (!tensors || !numels)) return WC_ERR_INVALID_ARG;
+    uint32_t max_len = kMaxCodeLen, group = kDefaultGroup, nthreads = 0;
+    if (opts) {
+        if (opts->max_code_len) max_len = opts->max_code_len;
+        if (opts->chunk_bytes && opts->chunk_bytes != 8) return WC_ERR_INVALID_ARG;
+        if (opts->chunks_per_group) group = opts->chunks_per_group;
+        nthreads = opts->n_threads;
+    }
+    if (max_len < 1 || max_len > kMaxCodeLen || group < 1 || group > (1u << 20)) return WC_ERR_INVALID_ARG;
+
+    Source src;
+    uint64_t n = 0;
+    for (uint32_t k = 0; k < n_tensors; ++k) {
+        if (numels[k] && !tensors[k]) return WC_ERR_INVALID_ARG;
+        if (numels[k] > (1ull << 40) || n + numels[k] > (1ull << 40)) return WC_ERR_INVALID_ARG;
+        src.ptr.push_back(tensors[k]);
+        src.begin.push_back(n);
+        src.size.push_back(numels[k]);
+        n += numels[k];
+    }
+    if (nthreads == 0) nthreads = std::max(1u, std::thread::hardware_concurrency());
+    nthreads = (unsigned)std::min<uint64_t>(nthreads, std::max<uint64_t>(1, n / 65536));
+    nthreads = std::min(nthreads, 64u);
+    std::vector<uint64_t> r0(nthreads + 1);
+    for (unsigned t = 0; t <= nthreads; ++t) r0[t] = n * t / nthreads;
+
+    // 1-2. exponent histogram
+    std::vector<std::array<uint64_t, 256>> hist_t(nthreads);
+    parallel_for(nthreads, [&](unsigned t) {
+        auto& h = hist_t[t];
+        h.fill(0);
+        src.for_range(r0[t], r0[t + 1], [&](uint64_t, const uint16_t* p, uint64_t k) {
+            for (uint64_t j = 0; j < k; ++j) ++h[exponent_of(p[j])];
+        });
+    });
+    uint64_t hist[256] = {0};
+    for (auto& h : hist_t)
+        for (int s = 0; s < 256; ++s) hist[s] += h[s];
+
+    // 3-4. code lengths and canonical codes
+    uint8_t len[256];
+    uint32_t code[256];
+    int st = limited_code_lengths(hist, max_len, len);
+    if (st != WC_OK) return st;
+    canonical_codes(len, code);
+
+    // bit offset of every thread's first codeword
+    std::vector<uint64_t> tbits(nthreads + 1, 0);
+    for (unsigned t = 0; t < nthreads; ++t) {
+        uint64_t b = 0;
+        for (int s = 0; s < 256; ++s) b += hist_t[t][s] * len[s];
+        tbits[t + 1] = tbits[t] + b;
+    }
+    const uint64_t stream_bits = tbits[nthreads];
+    Header h = layout(n, stream_bits, n_tensors, max_len, group);
+
+    uint8_t* out = (uint8_t*)std::aligned_alloc(kAlign, h.total_bytes);
+    if (!out) return WC_ERR_NOMEM;
+    {   // zero everything but the sm plane (written in full below)
+        const uint64_t zero_end = h.off_sm;
+        parallel_for(nthreads, [&](unsigned t) {
+            uint64_t a = zero_end * t / nthreads, b = zero_end * (t + 1) / nthreads;
+            std::memset(out + a, 0, b - a);
+        });
+        std::memset(out + h.off_sm + n, 0, h.total_bytes - h.off_sm - n);
+    }
+    write_header(out, h);
+    std::memcpy(out + h.off_code_len, len, 256);
+    for (uint32_t k = 0; k < n_tensors; ++k) {
+        store_le<uint64_t>(out + h.off_tensors + 16ull * k, src.begin[k]);
+        store_le<uint64_t>(out + h.off_tensors + 16ull * k + 8, src.size[k]);
+    }
+    uint8_t* stream = out + h.off_stream;
+    uint8_t* gap = out + h.off_gap;
+    uint8_t* gstart = out + h.off_group_start;
+    uint8_t* sm = out + h.off_sm;
+    const uint64_t group_bits = (uint64_t)kChunkBits * group;
+
+    // 5. pack, plane split and auxiliary variables, per element range
+    parallel_for(nthreads, [&](unsigned t) {
+        const uint64_t i0 = r0[t], i1 = r0[t + 1];
+        if (i0 == i1) return;
+        uint64_t pos = tbits[t];                                     // start bit of element i0
+        uint64_t prev = i0 ? pos - len[exponent_of(src.at(i0 - 1))] : 0;
+        bool first_elem = (i0 == 0);
+        uint64_t wbyte = pos >> 3;                                   // next byte to write
+        uint32_t acc = 0;
+        int nacc = (int)(pos & 7);                                   // leading bits belong to the previous range
+        bool shared_head = nacc != 0;
+        auto put = [&](uint8_t v) {
+            if (shared_head) {
+                __atomic_fetch_or(stream + wbyte, v, __ATOMIC_RELAXED);
+                shared_head = false;
+            } else {
+                stream[wbyte] = v;
+            }
+            ++wbyte;
+        };
+        src.for_range(i0, i1, [&](uint64_t gi, const uint16_t* p, uint64_t k) {
+            for (uint64_t j = 0; j < k; ++j) {
+                const uint16_t b = p[j];
+                const uint8_t e = exponent_of(b);
+                const uint64_t i = gi + j;
+                sm[i] = sign_mantissa_of(b);
+                if (first_elem || (prev >> 6) != (pos >> 6)) gap[pos >> 6] = (uint8_t)(pos & 63);
+                if (first_elem || prev / group_bits != pos / group_bits)
+                    store_le<uint64_t>(gstart + 8 * (pos / group_bits), i);
+                first_elem = false;
+                const int L = len[e];
+                acc = (acc << L) | code[e];
+                nacc += L;
+                while (nacc >= 8) {
+                    nacc -= 8;
+                    put((uint8_t)(acc >> nacc));
+                }
+                acc &= (1u << nacc) - 1u;
+                prev = pos;
+                pos += L;
+            }
+        });
+        if (nacc) __atomic_fetch_or(stream + wbyte, (uint8_t)(acc << (8 - nacc)), __ATOMIC_RELAXED);
+        if (t + 1 == nthreads) {
+            // chunks / groups after the last codeword start point at the stream end / n
+            for (uint64_t c = (prev >> 6) + 1; c < h.n_chunks; ++c) gap[c] = (uint8_t)(stream_bits - 64 * c);
+            for (uint64_t g = prev / group_bits + 1; g <= h.n_groups; ++g) store_le<uint64_t>(gstart + 8 * g, n);
+        }
+    });
+    store_le<uint64_t>(gstart + 8 * h.n_groups, n);
+
+    *blob = out;
+    *blob_bytes = h.total_bytes;
+    return WC_OK;
+}
+
+extern "C" void wc_free_host(uint8_t* blob) { std::free(blob); }

@@ -1,0 +1,297 @@
+// plan.cpp -- container validation, decode planning and the decode entry point
+// of libwc.
+//
+// wc_plan checks every field and section of a container before any kernel
+// sees it, so that the decode kernel can trust the auxiliary variables it
+// reads (DFloat11 page, abstract, design point (ii)): group starts are
+// monotone and end at n, gaps are shorter than the longest code, and the code
+// lengths form a complete prefix code.  It then builds the compact decode
+// tables on the device (design point (i)) and sizes one persistent launch
+// that covers a whole multi-tensor container (design point (iii)).
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "format.h"
+#include "kernels.h"
+#include "../../include/wc.h"
+
+struct wc_plan_s {
+    int device = 0;
+    wc::Header h;
+    std::vector<uint64_t> tensor_offsets, tensor_numels;
+    uint64_t max_group_elems = 0;
+    uint32_t lut_bits = 12;
+    uint32_t grid = 0;
+    uint32_t lds_bytes = 0;
+    uint32_t ebuf_bytes = 0;
+    uint32_t* d_tables = nullptr;
+};
+
+namespace {
+
+using wc::Header;
+using wc::HeaderOffsets;
+using wc::load_le;
+
+int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<uint64_t>& toff,
+                       std::vector<uint64_t>& tnum, uint64_t& max_group_elems) {
+    using O = HeaderOffsets;
+    if (bytes < wc::kHeaderBytes) return WC_ERR_TRUNCATED;
+    if (load_le<uint32_t>(b + O::magic) != wc::kMagic || load_le<uint16_t>(b + O::version) != wc::kVersion ||
+        load_le<uint16_t>(b + O::flags) != 0 || b[O::chunk_bits] != wc::kChunkBits ||
+        load_le<uint16_t>(b + O::reserved0) != 0 || load_le<uint32_t>(b + O::reserved1) != 0)
+        return WC_ERR_BAD_MAGIC;
+    for (uint32_t k = O::reserved_tail; k < wc::kHeaderBytes; ++k)
+        if (b[k]) return WC_ERR_BAD_MAGIC;
+    h.max_code_len = b[O::max_code_len];
+    h.chunks_per_group = load_le<uint32_t>(b + O::chunks_per_group);
+    h.n_tensors = load_le<uint32_t>(b + O::n_tensors);
+    h.n_elems = load_le<uint64_t>(b + O::n_elems);
+    h.stream_bits = load_le<uint64_t>(b + O::stream_bits);
+    h.n_chunks = load_le<uint64_t>(b + O::n_chunks);
+    h.n_groups = load_le<uint64_t>(b + O::n_groups);
+    h.off_code_len = load_le<uint64_t>(b + O::off_code_len);
+    h.off_tensors = load_le<uint64_t>(b + O::off_tensors);
+    h.off_group_start = load_le<uint64_t>(b + O::off_group_start);
+    h.off_gap = load_le<uint64_t>(b + O::off_gap);
+    h.off_stream = load_le<uint64_t>(b + O::off_stream);
+    h.stream_bytes = load_le<uint64_t>(b + O::stream_bytes);
+    h.off_sm = load_le<uint64_t>(b + O::off_sm);
+    h.total_bytes = load_le<uint64_t>(b + O::total_bytes);
+    if (h.max_code_len < 1 || h.max_code_len > wc::kMaxCodeLen || h.chunks_per_group < 1) return WC_ERR_BAD_MAGIC;
+    if (h.total_bytes > bytes) return WC_ERR_TRUNCATED;
+
+    // size fields
+    if (h.n_elems > (1ull << 40) || h.stream_bits > h.n_elems * (uint64_t)h.max_code_len ||
+        h.stream_bits < h.n_elems || h.n_chunks != wc::div_up(h.stream_bits, wc::kChunkBits) ||
+        h.n_groups != wc::div_up(h.n_chunks, h.chunks_per_group) ||
+        h.stream_bytes != h.n_chunks * 8 + wc::kStreamSlack)
+        return WC_ERR_STREAM_BITS;
+
+    // sections: 256-byte aligned, in order, non-overlapping, inside total_bytes
+    if (h.n_tensors > (1u << 24)) return WC_ERR_SECTION_BOUNDS;
+    const uint64_t off[6] = {h.off_code_len, h.off_tensors, h.off_group_start, h.off_gap, h.off_stream, h.off_sm};
+    const uint64_t len[6] = {256, 16ull * h.n_tensors, 8 * (h.n_groups + 1), h.n_chunks, h.stream_bytes, h.n_elems};
+    uint64_t lo = wc::kHeaderBytes;
+    for (int k = 0; k < 6; ++k) {
+        if (off[k] % wc::kAlign || off[k] < lo || off[k] > h.total_bytes || len[k] > h.total_bytes - off[k])
+            return WC_ERR_SECTION_BOUNDS;
+        lo = off[k] + len[k];
+    }
+    // the decoder reads the sign+mantissa plane in 16-byte blocks
+    if (wc::round_up(h.n_elems, 16) > h.total_bytes - h.off_sm) return WC_ERR_SECTION_BOUNDS;
+
+    // tensor table
+    toff.resize(h.n_tensors);
+    tnum.resize(h.n_tensors);
+    uint64_t acc = 0;
+    for (uint32_t t = 0; t < h.n_tensors; ++t) {
+        toff[t] = load_le<uint64_t>(b + h.off_tensors + 16ull * t);
+        tnum[t] = load_le<uint64_t>(b + h.off_tensors + 16ull * t + 8);
+        if (toff[t] != acc || tnum[t] > h.n_elems - acc) return WC_ERR_TENSOR_TABLE;
+        acc += tnum[t];
+    }
+    if (acc != h.n_elems) return WC_ERR_TENSOR_TABLE;
+
+    // code lengths: complete prefix code (Kraft sum exactly 1), or one 1-bit code
+    const uint8_t* cl = b + h.off_code_len;
+    uint64_t kraft = 0;
+    uint32_t present = 0, longest = 0;
+    for (int s = 0; s < 256; ++s) {
+        if (!cl[s]) continue;
+        if (cl[s] > h.max_code_len) return WC_ERR_CODE_LENGTHS;
+        kraft += 1ull << (wc::kMaxCodeLen - cl[s]);
+        ++present;
+        longest = std::max<uint32_t>(longest, cl[s]);
+    }
+    if (present == 0 && h.n_elems) return WC_ERR_CODE_LENGTHS;
+    if (present >= 2 && kraft != (1ull << wc::kMaxCodeLen)) return WC_ERR_KRAFT;
+    if (present == 1 && longest != 1) return WC_ERR_KRAFT;
+
+    // gaps: a codeword reaches at most max_code_len - 1 bits into the next chunk
+    const uint8_t* gap = b + h.off_gap;
+    for (uint64_t c = 0; c < h.n_chunks; ++c)
+        if (gap[c] >= h.max_code_len || 64 * c + gap[c] > h.stream_bits) return WC_ERR_GAP;
+
+    // group starts: 0, monotone, at most 64 codewords per chunk, ending at n
+    const uint8_t* gs = b + h.off_group_start;
+    const uint64_t per_group_max = 64ull * h.chunks_per_group;
+    uint64_t prev = load_le<uint64_t>(gs);
+    if (prev != 0) return WC_ERR_GROUP_START;
+    max_group_elems = 0;
+    for (uint64_t g = 1; g <= h.n_groups; ++g) {
+        uint64_t v = load_le<uint64_t>(gs + 8 * g);
+        if (v < prev || v - prev > per_group_max) return WC_ERR_GROUP_START;
+        max_group_elems = std::max(max_group_elems, v - prev);
+        prev = v;
+    }
+    if (prev != h.n_elems) return WC_ERR_GROUP_START;
+
+    // stream padding past stream_bits must be zero (so that it cannot be
+    // mistaken for codewords by a reader that ignores stream_bits)
+    const uint8_t* st = b + h.off_stream;
+    if (h.stream_bits & 7) {
+        uint8_t tail = st[h.stream_bits >> 3];
+        if (tail & (0xFFu >> (h.stream_bits & 7))) return WC_ERR_STREAM_BITS;
+    }
+    for (uint64_t k = wc::div_up(h.stream_bits, 8); k < h.stream_bytes; ++k)
+        if (st[k]) return WC_ERR_STREAM_BITS;
+    return WC_OK;
+}
+
+uint32_t env_u32(const char* name, uint32_t dflt) {
+    const char* v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    return (uint32_t)std::strtoul(v, nullptr, 10);
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) return;
+        ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+}  // namespace
+
+extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_device, wc_plan_t** out) {
+    if (!out) return WC_ERR_INVALID_ARG;
+    *out = nullptr;
+    if (!blob_host) return WC_ERR_INVALID_ARG;
+    wc_plan_t* p = new (std::nothrow) wc_plan_t;
+    if (!p) return WC_ERR_NOMEM;
+    int st = parse_and_validate(blob_host, blob_bytes, p->h, p->tensor_offsets, p->tensor_numels, p->max_group_elems);
+    if (st == WC_OK && p->h.chunks_per_group != wc::kDecodeThreads) st = WC_ERR_UNSUPPORTED;
+    if (st != WC_OK) {
+        delete p;
+        return st;
+    }
+    p->device = hip_device;
+    p->lut_bits = env_u32("WC_LUT_BITS", 12);
+    if (p->lut_bits < wc::kMinLutBits || p->lut_bits > wc::kMaxLutBits) p->lut_bits = 12;
+    p->ebuf_bytes = (uint32_t)wc::round_up(p->max_group_elems + 15, 16);
+    p->lds_bytes = wc::decode_lds_bytes(p->lut_bits, p->ebuf_bytes);
+
+    DeviceGuard guard(hip_device);
+    if (!guard.ok) {
+        delete p;
+        return WC_ERR_HIP;
+    }
+    int n_cu = 0;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, hip_device) != hipSuccess || n_cu <= 0) {
+        delete p;
+        return WC_ERR_HIP;
+    }
+    int per_cu = wc::decode_blocks_per_cu(p->lut_bits, p->lds_bytes);
+    if (per_cu <= 0) {
+        delete p;
+        return WC_ERR_UNSUPPORTED;
+    }
+    uint64_t want = (uint64_t)n_cu * (uint64_t)per_cu;
+    uint32_t forced = env_u32("WC_GRID", 0);
+    if (forced) want = forced;
+    p->grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(want, std::max<uint64_t>(p->h.n_groups, 1)));
+
+    const size_t tbytes = (size_t)wc::table_words(p->lut_bits) * 4;
+    if (hipMalloc(reinterpret_cast<void**>(&p->d_tables), tbytes) != hipSuccess) {
+        delete p;
+        return WC_ERR_NOMEM;
+    }
+    wc::CodeLens lens;
+    std::memcpy(lens.len, blob_host + p->h.off_code_len, 256);
+    if (wc::launch_build_tables(lens, p->lut_bits, p->d_tables, nullptr) != hipSuccess ||
+        hipStreamSynchronize(nullptr) != hipSuccess) {
+        (void)hipFree(p->d_tables);
+        delete p;
+        return WC_ERR_HIP;
+    }
+    *out = p;
+    return WC_OK;
+}
+
+extern "C" int wc_plan_info(const wc_plan_t* p, uint64_t* n_elems, uint32_t* n_tensors, uint64_t* tensor_offsets,
+                            uint64_t* tensor_numels) {
+    if (!p) return WC_ERR_INVALID_ARG;
+    if (n_elems) *n_elems = p->h.n_elems;
+    if (n_tensors) *n_tensors = p->h.n_tensors;
+    if (tensor_offsets) std::copy(p->tensor_offsets.begin(), p->tensor_offsets.end(), tensor_offsets);
+    if (tensor_numels) std::copy(p->tensor_numels.begin(), p->tensor_numels.end(), tensor_numels);
+    return WC_OK;
+}
+
+extern "C" int wc_plan_stats(const wc_plan_t* p, uint64_t* container_bytes, uint64_t* stream_bits, uint64_t* n_groups,
+                             uint32_t* lut_bits, uint32_t* grid, uint32_t* lds_bytes) {
+    if (!p) return WC_ERR_INVALID_ARG;
+    if (container_bytes) *container_bytes = p->h.total_bytes;
+    if (stream_bits) *stream_bits = p->h.stream_bits;
+    if (n_groups) *n_groups = p->h.n_groups;
+    if (lut_bits) *lut_bits = p->lut_bits;
+    if (grid) *grid = p->grid;
+    if (lds_bytes) *lds_bytes = p->lds_bytes;
+    return WC_OK;
+}
+
+extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_t* out_dev, void* stream) {
+    if (!p) return WC_ERR_INVALID_ARG;
+    if (p->h.n_elems == 0) return WC_OK;
+    if (!blob_dev || !out_dev) return WC_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(blob_dev) & 255u) || (reinterpret_cast<uintptr_t>(out_dev) & 15u))
+        return WC_ERR_INVALID_ARG;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return WC_ERR_HIP;
+    if (cur != p->device) return WC_ERR_INVALID_ARG;
+    const uint8_t* b = static_cast<const uint8_t*>(blob_dev);
+    wc::DecodeParams d;
+    d.stream = b + p->h.off_stream;
+    d.gap = b + p->h.off_gap;
+    d.group_start = reinterpret_cast<const uint64_t*>(b + p->h.off_group_start);
+    d.sm = b + p->h.off_sm;
+    d.out = out_dev;
+    d.tables = p->d_tables;
+    d.n_chunks = p->h.n_chunks;
+    d.stream_bits = p->h.stream_bits;
+    d.n_groups = p->h.n_groups;
+    d.ebuf_bytes = p->ebuf_bytes;
+    d.pad = 0;
+    hipError_t e = wc::launch_decode(d, p->lut_bits, p->grid, p->lds_bytes, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? WC_OK : WC_ERR_HIP;
+}
+
+extern "C" void wc_plan_destroy(wc_plan_t* p) {
+    if (!p) return;
+    if (p->d_tables) {
+        DeviceGuard guard(p->device);
+        (void)hipFree(p->d_tables);
+    }
+    delete p;
+}
+
+extern "C" const char* wc_status_str(int s) {
+    switch (s) {
+        case WC_OK: return "ok";
+        case WC_ERR_INVALID_ARG: return "invalid argument";
+        case WC_ERR_NOMEM: return "out of memory";
+        case WC_ERR_HIP: return "HIP runtime error";
+        case WC_ERR_UNSUPPORTED: return "unsupported container parameters";
+        case WC_ERR_BAD_MAGIC: return "bad magic, version or fixed header field";
+        case WC_ERR_TRUNCATED: return "container truncated";
+        case WC_ERR_SECTION_BOUNDS: return "section misaligned, out of order or out of bounds";
+        case WC_ERR_CODE_LENGTHS: return "code length out of range";
+        case WC_ERR_KRAFT: return "code lengths do not form a complete prefix code";
+        case WC_ERR_GAP: return "per-chunk gap out of range";
+        case WC_ERR_GROUP_START: return "group output starts invalid";
+        case WC_ERR_STREAM_BITS: return "stream size fields inconsistent";
+        case WC_ERR_TENSOR_TABLE: return "tensor table is not a partition of the elements";
+        default: return "unknown status";
+    }
+}

@@ -1,0 +1,200 @@
+"""Thin ctypes binding of libwc (include/wc.h).
+
+Argument marshalling only: every step of encoding, planning and decoding runs
+in the native library (host C++ and gfx950 HIP kernels).  Importing this
+module loads ``libwc.so`` from this package directory and fails loudly if it
+has not been built (``python -m lossless_entropy_coded_amd.build``); there is
+no Python or CPU fallback for any entry point.
+
+PyTorch is used only as the owner of device memory and streams: callers pass
+tensors (or raw integer device pointers) and the binding forwards
+``data_ptr()`` and ``torch.cuda.current_stream().cuda_stream``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwc.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libwc.so is not built at {LIB_PATH}; run `python -m lossless_entropy_coded_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_u8p = ctypes.POINTER(ctypes.c_uint8)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_u64p = ctypes.POINTER(ctypes.c_uint64)
+_u32p = ctypes.POINTER(ctypes.c_uint32)
+
+
+class EncodeOpts(ctypes.Structure):
+    _fields_ = [("max_code_len", ctypes.c_uint32), ("chunk_bytes", ctypes.c_uint32),
+                ("chunks_per_group", ctypes.c_uint32), ("n_threads", ctypes.c_uint32)]
+
+
+_lib.wc_encode_host.argtypes = [ctypes.POINTER(_u16p), _u64p, ctypes.c_uint32, ctypes.POINTER(EncodeOpts),
+                                ctypes.POINTER(_u8p), _u64p]
+_lib.wc_encode_host.restype = ctypes.c_int
+_lib.wc_free_host.argtypes = [_u8p]
+_lib.wc_free_host.restype = None
+_lib.wc_plan.argtypes = [_u8p, ctypes.c_uint64, ctypes.c_int, ctypes.POINTER(ctypes.c_void_p)]
+_lib.wc_plan.restype = ctypes.c_int
+_lib.wc_plan_info.argtypes = [ctypes.c_void_p, _u64p, _u32p, _u64p, _u64p]
+_lib.wc_plan_info.restype = ctypes.c_int
+_lib.wc_plan_stats.argtypes = [ctypes.c_void_p, _u64p, _u64p, _u64p, _u32p, _u32p, _u32p]
+_lib.wc_plan_stats.restype = ctypes.c_int
+_lib.wc_decode_async.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+_lib.wc_decode_async.restype = ctypes.c_int
+_lib.wc_plan_destroy.argtypes = [ctypes.c_void_p]
+_lib.wc_plan_destroy.restype = None
+_lib.wc_status_str.argtypes = [ctypes.c_int]
+_lib.wc_status_str.restype = ctypes.c_char_p
+
+# status codes (include/wc.h)
+WC_OK = 0
+WC_ERR_INVALID_ARG = -1
+WC_ERR_NOMEM = -2
+WC_ERR_HIP = -3
+WC_ERR_UNSUPPORTED = -4
+WC_ERR_BAD_MAGIC = -10
+WC_ERR_TRUNCATED = -11
+WC_ERR_SECTION_BOUNDS = -12
+WC_ERR_CODE_LENGTHS = -13
+WC_ERR_KRAFT = -14
+WC_ERR_GAP = -15
+WC_ERR_GROUP_START = -16
+WC_ERR_STREAM_BITS = -17
+WC_ERR_TENSOR_TABLE = -18
+
+EXPORTED = ("wc_encode_host", "wc_free_host", "wc_plan", "wc_plan_info", "wc_plan_stats",
+            "wc_decode_async", "wc_plan_destroy", "wc_status_str")
+
+
+class WCError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call} failed: {status_str(status)} ({status})")
+
+
+def status_str(status: int) -> str:
+    return _lib.wc_status_str(int(status)).decode()
+
+
+def _check(status: int, call: str):
+    if status != WC_OK:
+        raise WCError(status, call)
+
+
+def _as_u16(t) -> np.ndarray:
+    if hasattr(t, "numpy"):                    # torch CPU tensor (bf16/int16/uint16)
+        import torch
+        t = t.detach()
+        if t.dtype == torch.bfloat16:
+            t = t.view(torch.int16)
+        t = t.contiguous().numpy()
+    a = np.ascontiguousarray(t).reshape(-1)
+    if a.dtype != np.uint16:
+        a = a.view(np.uint16)
+    return a
+
+
+def encode_host(tensors, max_code_len: int = 24, chunks_per_group: int = 256, n_threads: int = 0) -> np.ndarray:
+    """wc_encode_host over a list of bf16 tensors (numpy uint16 or torch CPU).
+
+    Returns the container as a numpy uint8 array (a copy of the library buffer)."""
+    arrs = [_as_u16(t) for t in tensors]
+    nt = len(arrs)
+    ptrs = (_u16p * max(nt, 1))(*[a.ctypes.data_as(_u16p) for a in arrs])
+    numels = (ctypes.c_uint64 * max(nt, 1))(*[a.size for a in arrs])
+    opts = EncodeOpts(max_code_len, 8, chunks_per_group, n_threads)
+    out = _u8p()
+    nbytes = ctypes.c_uint64(0)
+    _check(_lib.wc_encode_host(ptrs, numels, nt, ctypes.byref(opts), ctypes.byref(out), ctypes.byref(nbytes)),
+           "wc_encode_host")
+    try:
+        blob = np.empty(nbytes.value, np.uint8)
+        ctypes.memmove(blob.ctypes.data, out, nbytes.value)
+    finally:
+        _lib.wc_free_host(out)
+    return blob
+
+
+class Plan:
+    """wc_plan over a host container; owns the native plan until close()."""
+
+    def __init__(self, blob_host: np.ndarray, device: int = 0):
+        self._blob = np.ascontiguousarray(blob_host, dtype=np.uint8)
+        h = ctypes.c_void_p()
+        _check(_lib.wc_plan(self._blob.ctypes.data_as(_u8p), self._blob.size, int(device), ctypes.byref(h)),
+               "wc_plan")
+        self._h = h
+        self.device = int(device)
+        n = ctypes.c_uint64(0)
+        nt = ctypes.c_uint32(0)
+        _check(_lib.wc_plan_info(self._h, ctypes.byref(n), ctypes.byref(nt), None, None), "wc_plan_info")
+        offs = (ctypes.c_uint64 * max(nt.value, 1))()
+        nums = (ctypes.c_uint64 * max(nt.value, 1))()
+        _check(_lib.wc_plan_info(self._h, None, None, offs, nums), "wc_plan_info")
+        self.n_elems = n.value
+        self.n_tensors = nt.value
+        self.tensor_offsets = [offs[i] for i in range(nt.value)]
+        self.tensor_numels = [nums[i] for i in range(nt.value)]
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise RuntimeError("plan is closed")
+        return self._h
+
+    def stats(self) -> dict:
+        cb, sb, ng = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+        lb, gr, lds = ctypes.c_uint32(), ctypes.c_uint32(), ctypes.c_uint32()
+        _check(_lib.wc_plan_stats(self.handle, ctypes.byref(cb), ctypes.byref(sb), ctypes.byref(ng),
+                                  ctypes.byref(lb), ctypes.byref(gr), ctypes.byref(lds)), "wc_plan_stats")
+        return {"container_bytes": cb.value, "stream_bits": sb.value, "n_groups": ng.value,
+                "lut_bits": lb.value, "grid": gr.value, "lds_bytes": lds.value}
+
+    def close(self):
+        if self._h is not None:
+            _lib.wc_plan_destroy(self._h)
+            self._h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _ptr(x) -> int:
+    return int(x.data_ptr()) if hasattr(x, "data_ptr") else int(x)
+
+
+def decode_async(plan: Plan, blob_dev, out_dev, stream=None) -> None:
+    """wc_decode_async: one launch decoding the whole container into out_dev.
+
+    blob_dev / out_dev: torch device tensors (or raw device pointers).  stream:
+    a torch.cuda.Stream, a raw hipStream_t integer, or None for torch's current
+    stream."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    _check(_lib.wc_decode_async(plan.handle, ctypes.c_void_p(_ptr(blob_dev)), ctypes.c_void_p(_ptr(out_dev)),
+                                ctypes.c_void_p(int(stream))), "wc_decode_async")
+
+
+def exported_symbols():
+    """Names of the C ABI entry points resolvable in the loaded library."""
+    return [name for name in EXPORTED if hasattr(_lib, name)]

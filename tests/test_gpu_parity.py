@@ -1,0 +1,226 @@
+"""GPU parity: the gfx950 decode kernel, called through the C ABI, against the
+CPU oracle and against the identity (decode(encode(W)) == W), bit-exact.
+
+Every output buffer is framed by canary guard bands that must survive every
+decode.  Expected values come only from the seeded generators, the oracle or
+closed forms, never from the GPU.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from gpu_util import GuardedOutput, gpu_decode, log, to_device_aligned
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def wc():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from lossless_entropy_coded_amd import wc as mod
+    return mod
+
+
+@pytest.fixture
+def env_knob():
+    saved = {}
+
+    def setter(name, value):
+        if name not in saved:
+            saved[name] = os.environ.get(name)
+        if value is None:
+            os.environ.pop(name, None)
+        else:
+            os.environ[name] = str(value)
+    yield setter
+    for k, v in saved.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
+
+
+def test_worked_example(wc):
+    w = np.array([0x3C80, 0x3C00, 0x3C80, 0x3B80, 0x3C80, 0x3D00, 0x3C00, 0x3C80], np.uint16)
+    log("case: worked example n=8")
+    assert np.array_equal(gpu_decode(wc, wc.encode_host([w])), w)
+
+
+@pytest.mark.parametrize("shuffle", [False, True])
+def test_all_bf16_patterns(wc, oracle_lib, shuffle):
+    w = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    if shuffle:
+        w = np.random.default_rng(99).permutation(w)
+    for writer in ("product", "oracle"):
+        blob = wc.encode_host([w]) if writer == "product" else oracle_lib.encode(w)
+        log(f"case: all 65536 patterns shuffle={shuffle} writer={writer}")
+        assert np.array_equal(gpu_decode(wc, blob), w)
+
+
+def test_tiny_and_special_sequences(wc, oracle_lib):
+    rng = np.random.default_rng(2024)
+    special = np.array([0x0000, 0x8000, 0x0001, 0x807F, 0x7F80, 0xFF80, 0x7FC1, 0xFFFF, 0x3F80, 0xBF80],
+                       np.uint16)
+    cases = [np.zeros(0, np.uint16), np.array([0x1234], np.uint16)]
+    for n in list(range(1, 40)) + [63, 64, 65, 127, 128, 129, 255, 256, 257, 1000, 4095, 4096, 4097]:
+        cases.append(special[rng.integers(0, special.size, size=n)])
+        cases.append(rng.integers(0, 65536, size=n, dtype=np.uint16))
+        cases.append(np.full(n, 0x3C00, np.uint16))
+    for i, w in enumerate(cases):
+        log(f"case: tiny #{i} n={w.size}")
+        blob = wc.encode_host([w]) if i % 2 == 0 else oracle_lib.encode(w)
+        got = gpu_decode(wc, blob)
+        assert np.array_equal(got, w), f"case {i} n={w.size}"
+
+
+def _fib_alphabet(prefix):
+    fib = [1, 1]
+    while len(fib) < 25:
+        fib.append(fib[-1] + fib[-2])
+    counts = dict(zip(range(100, 125), fib[::-1]))
+    seq = list(prefix)
+    for s in seq:
+        counts[s] -= 1
+    rng = np.random.default_rng(len(seq))
+    rest = np.concatenate([np.full(c, s, np.uint16) for s, c in counts.items()])
+    seq = np.concatenate([np.array(seq, np.uint16), rng.permutation(rest)])
+    return (seq << 7).astype(np.uint16) | rng.integers(0, 128, size=seq.size, dtype=np.uint16)
+
+
+@pytest.mark.parametrize("prefix", [[100] * 63 + [124], [100] * 64, [124] * 10, [123, 124] * 30, []])
+def test_long_codes_and_chunk_boundaries(wc, oracle_lib, prefix):
+    """Code lengths up to 24 bits (the long-code path), codewords straddling
+    chunk boundaries by up to 23 bits, both writers."""
+    w = _fib_alphabet(prefix)
+    for writer in ("product", "oracle"):
+        blob = wc.encode_host([w]) if writer == "product" else oracle_lib.encode(w)
+        log(f"case: fib alphabet prefix_len={len(prefix)} writer={writer} n={w.size}")
+        assert np.array_equal(gpu_decode(wc, blob), w)
+
+
+@pytest.mark.parametrize("lut_bits", [10, 11, 12])
+@pytest.mark.parametrize("grid", [1, 7, 0])
+def test_table_width_and_grid_invariance(wc, env_knob, lut_bits, grid):
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload("heavy_tail_14k", scale_rows=512)
+    blob = wc.encode_host(wl.tensors())
+    env_knob("WC_LUT_BITS", lut_bits)
+    env_knob("WC_GRID", grid or None)
+    log(f"case: heavy_tail rows=512 lut_bits={lut_bits} grid={grid}")
+    with wc.Plan(blob) as plan:
+        st = plan.stats()
+        assert st["lut_bits"] == lut_bits
+        if grid:
+            assert st["grid"] == grid
+        assert np.array_equal(gpu_decode(wc, blob, plan=plan), wl.bits)
+
+
+@pytest.mark.parametrize("name", ["matrix_1k", "attn_4k_zeros", "block_8b", "heavy_tail_14k", "block_70b"])
+def test_workload_full_size(wc, oracle_lib, name):
+    """Full-size workloads, one launch each, in the benchmark's launch configuration."""
+    import torch
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload(name)
+    blob = wc.encode_host(wl.tensors())
+    log(f"case: full {name} n={wl.n} container={blob.size}")
+    with wc.Plan(blob) as plan:
+        assert plan.n_elems == wl.n and plan.tensor_numels == wl.numels
+        _, dblob = to_device_aligned(blob)
+        out = GuardedOutput(wl.n)
+        wc.decode_async(plan, dblob, out.out)
+        torch.cuda.synchronize()
+        assert out.guards_intact()
+        ref = torch.from_numpy(wl.bits.view(np.int16)).cuda()
+        assert torch.equal(out.out, ref), "GPU decode differs from the input weights"
+        # every tensor view sits at its table offset
+        for off, k in zip(plan.tensor_offsets, plan.tensor_numels):
+            assert torch.equal(out.out[off:off + k], ref[off:off + k])
+        del ref
+        if wl.n <= 300_000_000:
+            got = out.host()
+            log(f"case: full {name} oracle decode")
+            assert np.array_equal(got, oracle_lib.decode(blob))
+
+
+@pytest.mark.parametrize("name,rows", [("matrix_1k", None), ("block_8b", 256), ("heavy_tail_14k", 2048)])
+def test_oracle_written_containers(wc, oracle_lib, name, rows):
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload(name, scale_rows=rows)
+    blob = oracle_lib.encode(wl.bits, numels=wl.numels)
+    log(f"case: oracle-written {name} rows={rows}")
+    assert np.array_equal(gpu_decode(wc, blob), wl.bits)
+
+
+def test_corrupted_stream_stays_in_bounds(wc):
+    """Valid metadata, garbage bit stream: output may be wrong, but nothing is
+    written outside [out, out + n)."""
+    from container_view import sections
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload("matrix_1k", scale_rows=256)
+    blob = wc.encode_host(wl.tensors())
+    s = sections(blob)
+    rng = np.random.default_rng(3)
+    nbytes = (s["stream_bits"] + 7) // 8
+    variants = []
+    for k in (1, 10, 1000):
+        b = blob.copy()
+        pos = rng.integers(0, s["stream_bits"], size=k)
+        np.bitwise_xor.at(b, s["off_stream"] + pos // 8, (0x80 >> (pos % 8)).astype(np.uint8))
+        variants.append(("flip%d" % k, b))
+    b = blob.copy()
+    b[s["off_stream"]:s["off_stream"] + nbytes - 1] = 0xFF
+    variants.append(("ones", b))
+    b = blob.copy()
+    b[s["off_stream"]:s["off_stream"] + nbytes - 1] = 0x00
+    variants.append(("zeros", b))
+    b = blob.copy()
+    b[s["off_gs"] + 8:s["off_gs"] + 16] = np.frombuffer(np.uint64(0).tobytes(), np.uint8)
+    variants.append(("empty-first-group", b))
+    for tag, b in variants:
+        log(f"case: corrupted stream {tag}")
+        got = gpu_decode(wc, b)          # asserts the guard bands
+        assert got.size == wl.n
+
+
+def test_plan_reuse_across_streams_and_repeats(wc):
+    import torch
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload("attn_4k_zeros", scale_rows=1024)
+    blob = wc.encode_host(wl.tensors())
+    ref = torch.from_numpy(wl.bits.view(np.int16)).cuda()
+    log("case: two streams, repeated decodes")
+    with wc.Plan(blob) as plan:
+        _, dblob = to_device_aligned(blob)
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        outs = [GuardedOutput(wl.n) for _ in range(6)]
+        torch.cuda.synchronize()
+        for i, o in enumerate(outs):
+            wc.decode_async(plan, dblob, o.out, stream=(s1 if i % 2 else s2))
+        torch.cuda.synchronize()
+        for o in outs:
+            assert o.guards_intact() and torch.equal(o.out, ref)
+
+
+def test_argument_checks(wc):
+    import torch
+    w = np.arange(4096, dtype=np.uint16)
+    blob = wc.encode_host([w])
+    with wc.Plan(blob) as plan:
+        _, dblob = to_device_aligned(blob)
+        out = torch.empty(w.size + 16, dtype=torch.int16, device="cuda")
+        log("case: misaligned output pointer")
+        with pytest.raises(wc.WCError) as ei:
+            wc.decode_async(plan, dblob, out.data_ptr() + 2)
+        assert ei.value.status == wc.WC_ERR_INVALID_ARG
+        with pytest.raises(wc.WCError) as ei:
+            wc.decode_async(plan, dblob.data_ptr() + 16, out)
+        assert ei.value.status == wc.WC_ERR_INVALID_ARG
+        with pytest.raises(wc.WCError):
+            wc.decode_async(plan, 0, out)
+    empty = wc.encode_host([np.zeros(0, np.uint16)])
+    with wc.Plan(empty) as plan:
+        assert plan.n_elems == 0
+        wc.decode_async(plan, 0, 0)       # n = 0 is a no-op
+        torch.cuda.synchronize()

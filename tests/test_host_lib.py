@@ -1,0 +1,197 @@
+"""Host-side tests of libwc (CPU only): exported ABI, encoder against the
+oracle, and container validation in wc_plan.
+
+wc_plan validates a container completely before it touches the GPU, so on a
+machine without a GPU a valid container gets WC_ERR_HIP (no device) while an
+invalid one gets its own specific status code.
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+
+from container_view import expected_metadata, sections
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def wc():
+    from lossless_entropy_coded_amd import wc as mod
+    return mod
+
+
+def test_exports_every_declared_symbol(wc):
+    with open(os.path.join(ROOT, "include", "wc.h")) as f:
+        text = f.read()
+    declared = set(re.findall(r"^\s*(?:int|void|const char\*)\s+(wc_[a-z_]+)\s*\(", text, re.M))
+    assert declared == set(wc.EXPORTED)
+    for name in declared:
+        assert hasattr(wc._lib, name), name
+
+
+def test_status_strings(wc):
+    codes = [wc.WC_OK, wc.WC_ERR_INVALID_ARG, wc.WC_ERR_NOMEM, wc.WC_ERR_HIP, wc.WC_ERR_UNSUPPORTED,
+             wc.WC_ERR_BAD_MAGIC, wc.WC_ERR_TRUNCATED, wc.WC_ERR_SECTION_BOUNDS, wc.WC_ERR_CODE_LENGTHS,
+             wc.WC_ERR_KRAFT, wc.WC_ERR_GAP, wc.WC_ERR_GROUP_START, wc.WC_ERR_STREAM_BITS,
+             wc.WC_ERR_TENSOR_TABLE]
+    texts = [wc.status_str(c) for c in codes]
+    assert len(set(texts)) == len(texts)
+    assert wc.status_str(-999) == "unknown status"
+
+
+@pytest.mark.parametrize("name,rows", [("matrix_1k", None), ("attn_4k_zeros", 1024), ("block_8b", 128),
+                                       ("heavy_tail_14k", 2048), ("block_70b", 32)])
+def test_encoder_roundtrip_through_oracle(wc, oracle_lib, name, rows):
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload(name, scale_rows=rows)
+    blob = wc.encode_host(wl.tensors())
+    assert blob.ctypes.data % 1 == 0 and blob.size % 256 == 0
+    out, rep = oracle_lib.decode(blob, with_report=True)
+    assert np.array_equal(out, wl.bits)
+    H, L = rep["entropy_bits"], rep["mean_code_bits"]
+    assert H <= L < H + 1
+    # same optimal total length as the oracle's own package-merge
+    counts = rep["hist"].astype(np.int64)
+    lo = oracle_lib.package_merge_lengths(counts, 24).astype(np.int64)
+    s = sections(blob)
+    assert int((counts * s["code_len"].astype(np.int64)).sum()) == int((counts * lo).sum())
+    e, _ = oracle_lib.split_planes(wl.bits)
+    total, gap, gs = expected_metadata(e, s["code_len"], 256)
+    assert np.array_equal(s["gap"].astype(np.int64), gap) and np.array_equal(s["group_start"], gs)
+
+
+@pytest.mark.parametrize("n_threads", [1, 3, 8])
+def test_encoder_thread_count_invariant(wc, n_threads):
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload("heavy_tail_14k", scale_rows=64)
+    ref = wc.encode_host(wl.tensors(), n_threads=1)
+    got = wc.encode_host(wl.tensors(), n_threads=n_threads)
+    assert np.array_equal(ref, got)
+
+
+def test_encoder_edge_inputs(wc, oracle_lib):
+    rng = np.random.default_rng(5)
+    cases = [
+        [np.zeros(0, np.uint16)],
+        [np.array([0x3C00], np.uint16)],
+        [np.full(1000, 0x3C00, np.uint16)],                          # one symbol, 1-bit code
+        [np.arange(65536, dtype=np.uint32).astype(np.uint16)],        # every pattern
+        [np.zeros(0, np.uint16), np.array([1, 2, 3], np.uint16), np.zeros(0, np.uint16)],
+        [rng.integers(0, 65536, size=k, dtype=np.uint16) for k in (1, 7, 0, 300, 65537)],
+        [np.array([0x7FC1, 0xFF80, 0x8000, 0x0000, 0x0001, 0x807F], np.uint16)],  # NaN -inf -0 +0 subnormals
+    ]
+    for tensors in cases:
+        blob = wc.encode_host(tensors, n_threads=4)
+        flat = np.concatenate(tensors) if tensors else np.zeros(0, np.uint16)
+        assert np.array_equal(oracle_lib.decode(blob), flat)
+        s = sections(blob)
+        assert s["tensors"][:, 1].tolist() == [t.size for t in tensors]
+
+
+def test_encoder_max_code_len_option(wc, oracle_lib):
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload("heavy_tail_14k", scale_rows=256)
+    for L in (9, 12, 16):
+        blob = wc.encode_host(wl.tensors(), max_code_len=L)
+        s = sections(blob)
+        assert s["code_len"].max() <= L and s["max_code_len"] == L
+        assert np.array_equal(oracle_lib.decode(blob), wl.bits)
+
+
+def test_encoder_rejects_bad_options(wc):
+    w = np.arange(10, dtype=np.uint16)
+    for kw in ({"max_code_len": 25}, {"chunks_per_group": 1 << 21}):
+        with pytest.raises(wc.WCError) as ei:
+            wc.encode_host([w], **kw)
+        assert ei.value.status == wc.WC_ERR_INVALID_ARG
+    # 9 distinct exponents cannot fit in 3-bit codes
+    w9 = (np.arange(9, dtype=np.uint16) + 100) << 7
+    with pytest.raises(wc.WCError):
+        wc.encode_host([w9], max_code_len=3)
+
+
+def test_oracle_writer_containers_validate(wc, oracle_lib):
+    """Containers written by the oracle pass every check of wc_plan."""
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload("attn_4k_zeros", scale_rows=256)
+    blob = oracle_lib.encode(wl.bits, numels=wl.numels)
+    st = _plan_status(wc, blob)
+    assert st in (wc.WC_OK, wc.WC_ERR_HIP)
+
+
+def _plan_status(wc, blob):
+    try:
+        p = wc.Plan(blob)
+    except wc.WCError as e:
+        return e.status
+    p.close()
+    return wc.WC_OK
+
+
+def _u64(v):
+    return np.frombuffer(np.uint64(v).tobytes(), np.uint8)
+
+
+def test_plan_rejects_each_fault(wc):
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload("matrix_1k", scale_rows=128)
+    blob = wc.encode_host(wl.tensors())
+    s = sections(blob)
+    ok = (wc.WC_OK, wc.WC_ERR_HIP)
+    assert _plan_status(wc, blob) in ok
+
+    def mutated(fn):
+        b = blob.copy()
+        fn(b)
+        return _plan_status(wc, b)
+
+    def setb(off, val):
+        return lambda b: b.__setitem__(slice(off, off + len(val)), val)
+
+    assert mutated(setb(0, np.frombuffer(b"XCBF", np.uint8))) == wc.WC_ERR_BAD_MAGIC
+    assert mutated(setb(4, np.array([2, 0], np.uint8))) == wc.WC_ERR_BAD_MAGIC            # version
+    assert mutated(setb(9, np.array([32], np.uint8))) == wc.WC_ERR_BAD_MAGIC              # chunk bits
+    assert mutated(setb(200, np.array([1], np.uint8))) == wc.WC_ERR_BAD_MAGIC             # reserved tail
+    assert _plan_status(wc, blob[:100]) == wc.WC_ERR_TRUNCATED
+    assert _plan_status(wc, blob[:-256]) == wc.WC_ERR_TRUNCATED
+    assert mutated(setb(72, _u64(s["off_gs"] + 8))) == wc.WC_ERR_SECTION_BOUNDS           # misaligned
+    assert mutated(setb(80, _u64(s["off_gs"]))) == wc.WC_ERR_SECTION_BOUNDS               # overlapping
+    sym = int(np.argmax(s["code_len"]))
+    assert mutated(setb(s["off_len"] + sym, np.array([25], np.uint8))) == wc.WC_ERR_CODE_LENGTHS
+    sym = int(np.argmin(np.where(s["code_len"] > 0, s["code_len"], 99)))
+    assert mutated(setb(s["off_len"] + sym, np.array([s["code_len"][sym] + 1], np.uint8))) == wc.WC_ERR_KRAFT
+    assert mutated(setb(s["off_len"], np.zeros(256, np.uint8))) == wc.WC_ERR_CODE_LENGTHS
+    assert mutated(setb(s["off_gap"] + 5, np.array([24], np.uint8))) == wc.WC_ERR_GAP
+    last = s["off_gap"] + s["n_chunks"] - 1
+    assert mutated(setb(last, np.array([23], np.uint8))) in (wc.WC_ERR_GAP, wc.WC_OK, wc.WC_ERR_HIP)
+    g1 = s["off_gs"] + 8
+    assert mutated(setb(g1, _u64(0))) in ok           # an empty group is well-formed (the data is wrong)
+    assert mutated(setb(s["off_gs"], _u64(1))) == wc.WC_ERR_GROUP_START
+    assert mutated(setb(g1, _u64(s["n_elems"] + 5))) == wc.WC_ERR_GROUP_START            # not monotone / > n
+    assert mutated(setb(g1, _u64(64 * 256 + 1))) == wc.WC_ERR_GROUP_START                # too many per group
+    assert mutated(setb(32, _u64(s["stream_bits"] + 64))) == wc.WC_ERR_STREAM_BITS           # n_chunks disagrees
+    assert mutated(setb(40, _u64(s["n_chunks"] + 1))) == wc.WC_ERR_STREAM_BITS
+    assert mutated(setb(96, _u64(s["stream_bytes"] + 8))) == wc.WC_ERR_STREAM_BITS
+    pad = s["off_stream"] + (s["stream_bits"] + 7) // 8 + 2
+    assert mutated(setb(pad, np.array([0x10], np.uint8))) == wc.WC_ERR_STREAM_BITS
+    assert mutated(setb(s["off_tens"] + 8, _u64(s["n_elems"] + 1))) == wc.WC_ERR_TENSOR_TABLE
+    assert mutated(setb(s["off_tens"], _u64(3))) == wc.WC_ERR_TENSOR_TABLE
+    # valid container with a group size this build does not decode
+    b2 = wc.encode_host(wl.tensors(), chunks_per_group=128)
+    assert _plan_status(wc, b2) == wc.WC_ERR_UNSUPPORTED
+
+
+def test_plan_rejects_random_corruption_without_crashing(wc):
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload("matrix_1k", scale_rows=32)
+    blob = wc.encode_host(wl.tensors())
+    rng = np.random.default_rng(11)
+    hdr_and_meta = sections(blob)["off_stream"]
+    for _ in range(300):
+        b = blob.copy()
+        k = int(rng.integers(0, hdr_and_meta))
+        b[k] ^= np.uint8(1 << int(rng.integers(0, 8)))
+        st = _plan_status(wc, b)
+        assert st <= 0
