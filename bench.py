@@ -201,7 +201,8 @@ def main():
             "compression_ratio": round(2.0 * n / blob.size, 4),
             "mean_code_bits": round(stream_bits / n, 4),
             "launches_per_step": 1,
-            "lut_bits": st["lut_bits"],
+            "count_bits": st["count_bits"],
+            "decode_bits": st["decode_bits"],
             "grid": st["grid"],
             "lds_bytes": st["lds_bytes"],
             "rotating_copies": copies,

@@ -114,12 +114,15 @@ int wc_plan_info(const wc_plan_t* plan, uint64_t* n_elems, uint32_t* n_tensors,
                  uint64_t* tensor_offsets, uint64_t* tensor_numels);
 
 /*
- * wc_plan_stats -- container statistics: total container bytes, stream bits,
- * number of groups, the decode-table index width used by the kernel, the
- * launch grid (workgroups) and the dynamic LDS bytes per workgroup.
+ * wc_plan_stats -- container statistics and launch configuration: total
+ * container bytes, stream bits, number of groups, the index widths of the
+ * kernel's two LDS tables (codeword-start table, multi-codeword table), the
+ * launch grid (workgroups) and the LDS bytes per workgroup.  Any output may
+ * be NULL.
  */
 int wc_plan_stats(const wc_plan_t* plan, uint64_t* container_bytes, uint64_t* stream_bits,
-                  uint64_t* n_groups, uint32_t* lut_bits, uint32_t* grid, uint32_t* lds_bytes);
+                  uint64_t* n_groups, uint32_t* count_bits, uint32_t* decode_bits, uint32_t* grid,
+                  uint32_t* lds_bytes);
 
 /*
  * wc_decode_async -- decode every tensor of the container in ONE kernel launch

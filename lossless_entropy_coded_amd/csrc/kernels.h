@@ -9,23 +9,29 @@
 namespace wc {
 
 constexpr uint32_t kDecodeThreads = 256;   // one 64-bit chunk per lane, G = 256 chunks per group
-constexpr uint32_t kMinLutBits = 10;
-constexpr uint32_t kMaxLutBits = 12;
+constexpr uint32_t kSingleBits = 12;       // width of the build-time single-codeword table
+constexpr uint32_t kEbufSlack = 2;         // bytes a lane may write past its range (then rewritten)
 
-// Decode tables, as 32-bit words, for a first-level index of K bits:
-//   [0, 2^K)            single-codeword table, one entry per K-bit window:
-//                         bits 0..4  (32 - len) & 31   (the funnel-shift amount)
-//                         bits 8..12 len
-//                         bits 16..23 symbol
-//                         bit 31      set when the window starts a code longer than K
-//   [2^K, 2^(K+1))      codeword-start table for the counting phase:
-//                         bits 0..4  (32 - adv) & 31, bits 8..12 adv,
-//                         bits 16..16+K-1 mask of codeword starts inside the window
-//                         (adv = bits covered by the codewords that fit; 0 when none fits)
+// Device decode tables, as 32-bit words, for index widths KC (counting) and KD (decoding):
+//   [0, 2^KC)              codeword-start table: for a KC-bit window,
+//                            bits 0..4   (32 - adv) & 31      (funnel-shift amount)
+//                            bits 8..15  adv = bits covered by the whole codewords in the window
+//                            bits 16..31 mask of the offsets where those codewords start
+//                          0 when the first codeword is longer than KC bits;
+//   [2^KC, 2^KC + 2^KD)    multi-codeword table: for a KD-bit window, up to three codewords
+//                            bits 0..4   (32 - nbits) & 31, bits 5..6 number of symbols (1..3),
+//                            bits 8..15, 16..23, 24..31 the symbols in stream order
+//                          0 when the first codeword is longer than KD bits;
 //   then 32 words count[L], 32 words first[L] (canonical first code of length L),
 //   32 words base[L] (rank of the first symbol of length L), 64 words holding the
-//   256 symbols sorted by (length, symbol).
-inline uint32_t table_words(uint32_t lut_bits) { return (2u << lut_bits) + 160u; }
+//   256 symbols sorted by (length, symbol) -- used for codes longer than the index.
+inline uint32_t table_words(uint32_t count_bits, uint32_t decode_bits) {
+    return (1u << count_bits) + (1u << decode_bits) + 160u;
+}
+inline bool supported_table_bits(uint32_t count_bits, uint32_t decode_bits) {
+    return (count_bits == 12 && (decode_bits == 10 || decode_bits == 11 || decode_bits == 12)) ||
+           (count_bits == 11 && decode_bits == 11) || (count_bits == 10 && decode_bits == 10);
+}
 
 struct CodeLens {
     uint8_t len[256];
@@ -41,21 +47,23 @@ struct DecodeParams {
     uint64_t n_chunks;
     uint64_t stream_bits;
     uint64_t n_groups;
+    uint64_t sm_last;        // offset of the last 16-byte block of the sm plane: round_up(n, 16) - 16
     uint32_t ebuf_bytes;
     uint32_t pad;
 };
 
-// Dynamic LDS bytes of one decode workgroup.
-uint32_t decode_lds_bytes(uint32_t lut_bits, uint32_t ebuf_bytes);
+// LDS bytes of one decode workgroup: static tables plus the dynamic staging buffer.
+uint32_t decode_lds_bytes(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes);
 
-// Resident decode workgroups per compute unit for that LDS size (0 on error).
-int decode_blocks_per_cu(uint32_t lut_bits, uint32_t lds_bytes);
+// Resident decode workgroups per compute unit for that staging size (0 on error).
+int decode_blocks_per_cu(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes);
 
-// Build the decode tables of `lens` into d_tables (table_words(lut_bits) words) on `stream`.
-hipError_t launch_build_tables(const CodeLens& lens, uint32_t lut_bits, uint32_t* d_tables, hipStream_t stream);
+// Build the decode tables of `lens` into d_tables (table_words(...) words) on `stream`.
+hipError_t launch_build_tables(const CodeLens& lens, uint32_t count_bits, uint32_t decode_bits, uint32_t* d_tables,
+                               hipStream_t stream);
 
 // One launch decoding every group of a container.
-hipError_t launch_decode(const DecodeParams& p, uint32_t lut_bits, uint32_t grid, uint32_t lds_bytes,
-                         hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t decode_bits, uint32_t grid,
+                         uint32_t ebuf_bytes, hipStream_t stream);
 
 }  // namespace wc

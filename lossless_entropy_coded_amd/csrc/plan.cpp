@@ -25,7 +25,8 @@ struct wc_plan_s {
     wc::Header h;
     std::vector<uint64_t> tensor_offsets, tensor_numels;
     uint64_t max_group_elems = 0;
-    uint32_t lut_bits = 12;
+    uint32_t count_bits = 12;    // index width of the codeword-start table
+    uint32_t decode_bits = 11;   // index width of the multi-codeword table
     uint32_t grid = 0;
     uint32_t lds_bytes = 0;
     uint32_t ebuf_bytes = 0;
@@ -177,10 +178,16 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         return st;
     }
     p->device = hip_device;
-    p->lut_bits = env_u32("WC_LUT_BITS", 12);
-    if (p->lut_bits < wc::kMinLutBits || p->lut_bits > wc::kMaxLutBits) p->lut_bits = 12;
-    p->ebuf_bytes = (uint32_t)wc::round_up(p->max_group_elems + 15, 16);
-    p->lds_bytes = wc::decode_lds_bytes(p->lut_bits, p->ebuf_bytes);
+    p->count_bits = env_u32("WC_COUNT_BITS", 12);
+    p->decode_bits = env_u32("WC_DECODE_BITS", 11);
+    if (!wc::supported_table_bits(p->count_bits, p->decode_bits)) {
+        p->count_bits = 12;
+        p->decode_bits = 11;
+    }
+    // staging buffer: the group's exponents at offset (A mod 16), plus the
+    // bytes a lane's last three-byte write may reach past the group's end
+    p->ebuf_bytes = (uint32_t)wc::round_up(p->max_group_elems + 15 + wc::kEbufSlack, 16);
+    p->lds_bytes = wc::decode_lds_bytes(p->count_bits, p->decode_bits, p->ebuf_bytes);
 
     DeviceGuard guard(hip_device);
     if (!guard.ok) {
@@ -192,7 +199,7 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         delete p;
         return WC_ERR_HIP;
     }
-    int per_cu = wc::decode_blocks_per_cu(p->lut_bits, p->lds_bytes);
+    int per_cu = wc::decode_blocks_per_cu(p->count_bits, p->decode_bits, p->ebuf_bytes);
     if (per_cu <= 0) {
         delete p;
         return WC_ERR_UNSUPPORTED;
@@ -202,14 +209,14 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
     if (forced) want = forced;
     p->grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(want, std::max<uint64_t>(p->h.n_groups, 1)));
 
-    const size_t tbytes = (size_t)wc::table_words(p->lut_bits) * 4;
+    const size_t tbytes = (size_t)wc::table_words(p->count_bits, p->decode_bits) * 4;
     if (hipMalloc(reinterpret_cast<void**>(&p->d_tables), tbytes) != hipSuccess) {
         delete p;
         return WC_ERR_NOMEM;
     }
     wc::CodeLens lens;
     std::memcpy(lens.len, blob_host + p->h.off_code_len, 256);
-    if (wc::launch_build_tables(lens, p->lut_bits, p->d_tables, nullptr) != hipSuccess ||
+    if (wc::launch_build_tables(lens, p->count_bits, p->decode_bits, p->d_tables, nullptr) != hipSuccess ||
         hipStreamSynchronize(nullptr) != hipSuccess) {
         (void)hipFree(p->d_tables);
         delete p;
@@ -230,12 +237,13 @@ extern "C" int wc_plan_info(const wc_plan_t* p, uint64_t* n_elems, uint32_t* n_t
 }
 
 extern "C" int wc_plan_stats(const wc_plan_t* p, uint64_t* container_bytes, uint64_t* stream_bits, uint64_t* n_groups,
-                             uint32_t* lut_bits, uint32_t* grid, uint32_t* lds_bytes) {
+                             uint32_t* count_bits, uint32_t* decode_bits, uint32_t* grid, uint32_t* lds_bytes) {
     if (!p) return WC_ERR_INVALID_ARG;
     if (container_bytes) *container_bytes = p->h.total_bytes;
     if (stream_bits) *stream_bits = p->h.stream_bits;
     if (n_groups) *n_groups = p->h.n_groups;
-    if (lut_bits) *lut_bits = p->lut_bits;
+    if (count_bits) *count_bits = p->count_bits;
+    if (decode_bits) *decode_bits = p->decode_bits;
     if (grid) *grid = p->grid;
     if (lds_bytes) *lds_bytes = p->lds_bytes;
     return WC_OK;
@@ -261,9 +269,11 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
     d.n_chunks = p->h.n_chunks;
     d.stream_bits = p->h.stream_bits;
     d.n_groups = p->h.n_groups;
+    d.sm_last = wc::round_up(p->h.n_elems, 16) - 16;
     d.ebuf_bytes = p->ebuf_bytes;
     d.pad = 0;
-    hipError_t e = wc::launch_decode(d, p->lut_bits, p->grid, p->lds_bytes, static_cast<hipStream_t>(stream));
+    hipError_t e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->grid, p->ebuf_bytes,
+                                     static_cast<hipStream_t>(stream));
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
 }
 

@@ -45,7 +45,7 @@ _lib.wc_plan.argtypes = [_u8p, ctypes.c_uint64, ctypes.c_int, ctypes.POINTER(cty
 _lib.wc_plan.restype = ctypes.c_int
 _lib.wc_plan_info.argtypes = [ctypes.c_void_p, _u64p, _u32p, _u64p, _u64p]
 _lib.wc_plan_info.restype = ctypes.c_int
-_lib.wc_plan_stats.argtypes = [ctypes.c_void_p, _u64p, _u64p, _u64p, _u32p, _u32p, _u32p]
+_lib.wc_plan_stats.argtypes = [ctypes.c_void_p, _u64p, _u64p, _u64p, _u32p, _u32p, _u32p, _u32p]
 _lib.wc_plan_stats.restype = ctypes.c_int
 _lib.wc_decode_async.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
 _lib.wc_decode_async.restype = ctypes.c_int
@@ -152,11 +152,12 @@ class Plan:
 
     def stats(self) -> dict:
         cb, sb, ng = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
-        lb, gr, lds = ctypes.c_uint32(), ctypes.c_uint32(), ctypes.c_uint32()
+        kc, kd, gr, lds = ctypes.c_uint32(), ctypes.c_uint32(), ctypes.c_uint32(), ctypes.c_uint32()
         _check(_lib.wc_plan_stats(self.handle, ctypes.byref(cb), ctypes.byref(sb), ctypes.byref(ng),
-                                  ctypes.byref(lb), ctypes.byref(gr), ctypes.byref(lds)), "wc_plan_stats")
+                                  ctypes.byref(kc), ctypes.byref(kd), ctypes.byref(gr), ctypes.byref(lds)),
+               "wc_plan_stats")
         return {"container_bytes": cb.value, "stream_bits": sb.value, "n_groups": ng.value,
-                "lut_bits": lb.value, "grid": gr.value, "lds_bytes": lds.value}
+                "count_bits": kc.value, "decode_bits": kd.value, "grid": gr.value, "lds_bytes": lds.value}
 
     def close(self):
         if self._h is not None:
