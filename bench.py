@@ -77,20 +77,28 @@ def aligned_device_copy(torch, blob, align=256):
 
 
 def copy_calibration(args):
+    """A plain streaming kernel of known traffic: reads 1 GiB, writes 1 GiB.
+
+    (torch's same-dtype copy_ goes to a DMA engine, which kernel counters do
+    not see; an elementwise bitwise-not is an ordinary copy-shaped kernel.)"""
     import torch
     nbytes = 1 << 30
-    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    src = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(args.warmup):
-        dst.copy_(src)
+        torch.bitwise_not(src, out=dst)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
     for _ in range(args.steps):
-        dst.copy_(src)
+        torch.bitwise_not(src, out=dst)
+    t1.record()
     torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / args.steps
-    print(json.dumps({"calibration": "device copy", "bytes_read_per_step": nbytes, "bytes_written_per_step": nbytes,
-                      "steps": args.steps, "GBps_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
+    ms = t0.elapsed_time(t1) / args.steps
+    print(json.dumps({"calibration": "copy-shaped kernel (bitwise_not)", "bytes_read_per_step": nbytes,
+                      "bytes_written_per_step": nbytes, "steps": args.steps, "ms_per_step": ms,
+                      "GBps_read_plus_write": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
 
 
 def main():
@@ -144,21 +152,19 @@ def main():
 
     for k in range(args.warmup):
         wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # HIP events on the launch stream around the K back-to-back launches; a
+    # step is exactly one launch of the decode kernel, so the average launch
+    # duration is the timed region divided by K
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for k in range(args.steps):
-        starts[k].record(stream)
         wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
-        ends[k].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    kernel_avg_ms = sum(kernel_ms) / len(kernel_ms)
+    kernel_avg_ms = total_ms / args.steps
     bit_exact = all(torch.equal(outs[k % copies], ref) for k in range(min(copies, args.steps)))
     if not bit_exact:
         print("bench.py: timed outputs are NOT bit-exact", file=sys.stderr)

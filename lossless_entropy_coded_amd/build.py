@@ -15,6 +15,9 @@ HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
     # packed-fp32 instructions stay off in every HIP build of this library
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # no unaligned LDS/global accesses: the decode kernel's byte stores must not
+    # be merged into unaligned dword LDS stores, which stall on CDNA4
+    "-Xclang", "-target-feature", "-Xclang", "-unaligned-access-mode",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

@@ -10,22 +10,26 @@
 // first output index `group_start`); (iii) a whole transformer block is
 // decoded by one launch (here: every group of a multi-tensor container).
 //
-// Work decomposition on CDNA4: one workgroup of 256 lanes (4 wave64s) owns a
-// group of 256 chunks of 64 stream bits; lane t owns chunk t of the group.
-//   phase 1  each lane counts the codewords that START in its chunk, several
+// Work decomposition on CDNA4: a workgroup of 256 lanes (4 wave64s) owns two
+// adjacent groups (512 chunks of 64 stream bits, one contiguous output range);
+// lane t owns chunks 2t and 2t+1 of that range and decodes them as two
+// independent chains, so two table lookups are in flight per lane.
+//   phase 1  each chain counts the codewords that START in its chunk, several
 //            per lookup of a codeword-start table;
 //   scan     wave64 inclusive scan with DPP row shifts and row broadcasts,
 //            then across the 4 waves through LDS -> each lane's first output;
-//   phase 2  each lane decodes its codewords again, up to three per lookup of
+//   phase 2  each chain decodes its codewords again, up to four per lookup of
 //            a multi-codeword table, and stages the exponent bytes in LDS at
-//            their final group-relative place.  A lookup always writes three
-//            bytes; the ones past the lane's range are rewritten afterwards by
-//            the lane that owns them (its first two symbols are kept aside);
-//   merge    the workgroup joins the group's sign+mantissa bytes (prefetched
-//            with 16-byte loads while the phases run) with the staged
-//            exponents in integer registers and writes bf16 with 16-byte stores.
-// Workgroups are persistent: each stages the tables once and loops over
-// groups, loading the next group's chunk while it works on the current one.
+//            their final place (four byte stores per lookup; unaligned dword
+//            LDS stores stall on CDNA4).  Bytes written past a chain's range
+//            land on the next chain's first three bytes, which that chain
+//            keeps aside and rewrites after a barrier; writes of a finished
+//            chain go to a per-lane dummy slot;
+//   merge    the workgroup joins the sign+mantissa bytes (prefetched with
+//            16-byte loads while the phases run) with the staged exponents in
+//            integer registers and writes bf16 with 16-byte stores.
+// Workgroups are persistent: each stages the tables once and loops over its
+// units, loading the next unit's chunks while it works on the current one.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -37,6 +41,8 @@ namespace {
 
 constexpr uint32_t kCodeLimit = 24;
 constexpr uint32_t kWaves = kDecodeThreads / 64;
+constexpr uint32_t kUnitChunks = kDecodeThreads * kChunksPerLane;   // chunks per workgroup unit
+constexpr uint32_t kPrefetchBlocks = 4;                            // 16-element merge blocks per lane
 
 struct LongTables {
     const uint32_t* count;
@@ -46,9 +52,9 @@ struct LongTables {
 };
 
 // Canonical decode of a codeword longer than the table index.  `win` holds at
-// least 24 valid stream bits, MSB-aligned.  Returns the length; the symbol
-// goes to *sym.  A window that matches no code (only in a corrupted stream)
-// decodes as a 24-bit codeword of the first sorted symbol.
+// least 24 valid stream bits, MSB-aligned.  Returns the length; the (rotated)
+// symbol goes to *sym.  A window that matches no code (only in a corrupted
+// stream) decodes as a 24-bit codeword of the first sorted symbol.
 __device__ __forceinline__ uint32_t decode_long(uint32_t win, uint32_t first_len, const LongTables& t,
                                                 uint32_t* sym) {
     uint32_t L = first_len;
@@ -94,85 +100,135 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// Four bf16 words from four sign+mantissa bytes `s` and four exponent bytes `e`
-// (byte k of each belongs to element k).  The bf16 word is
-// (sm & 0x80) << 8 | e << 7 | (sm & 0x7F): a byte permute builds
-// [sm_k, sign-extension of sm_k] per 16-bit half, which already holds the sign
-// at bit 15 and the mantissa at bits 6..0; a bit-field insert then puts the
-// exponent into bits 14..7.
+// Four bf16 words from four sign+mantissa bytes `s` and four rotated exponent
+// bytes `e` (byte k of each belongs to element k).  With e' = ror8(e, 1), the
+// bf16 low byte is (e' & 0x80) | (sm & 0x7F) and the high byte is
+// (sm & 0x80) | (e' & 0x7F); two bit-field inserts build all low and all high
+// bytes, two byte permutes interleave them.
 __device__ __forceinline__ void join4(uint32_t s, uint32_t e, uint32_t& lo, uint32_t& hi) {
-    const uint32_t s8 = s << 8;
-    const uint32_t x01 = __builtin_amdgcn_perm(s8, s, 0x08010A00u);   // sm0, sext0, sm1, sext1
-    const uint32_t x23 = __builtin_amdgcn_perm(s8, s, 0x09030B02u);   // sm2, sext2, sm3, sext3
-    const uint32_t e02 = __builtin_amdgcn_perm(e, e, 0x03010200u);    // e0, e2, e1, e3
-    lo = (0x7F807F80u & (e02 << 7)) | (~0x7F807F80u & x01);
-    hi = (0x7F807F80u & (e02 >> 1)) | (~0x7F807F80u & x23);
+    const uint32_t lows = (0x80808080u & e) | (~0x80808080u & s);
+    const uint32_t highs = (0x80808080u & s) | (~0x80808080u & e);
+    lo = __builtin_amdgcn_perm(highs, lows, 0x05010400u);
+    hi = __builtin_amdgcn_perm(highs, lows, 0x07030602u);
 }
 
-struct Chunk {
-    uint32_t d0, d1, d2, gap;   // raw little-endian stream words and the first-codeword offset
-    uint64_t A, B;              // group output range [A, B)
-};
-
-__device__ __forceinline__ Chunk load_chunk(const DecodeParams& p, uint64_t g, uint32_t tid) {
-    Chunk k;
-    const uint64_t c = g * kDecodeThreads + tid;
-    k.d0 = k.d1 = k.d2 = k.gap = 0;
-    if (c < p.n_chunks) {
-        const uint2 d01 = *reinterpret_cast<const uint2*>(p.stream + 8 * c);
-        k.d0 = d01.x;
-        k.d1 = d01.y;
-        k.d2 = *reinterpret_cast<const uint32_t*>(p.stream + 8 * c + 8);
-        k.gap = p.gap[c];
-    }
-    // group bounds through the vector memory path (waited on with the chunk)
-    const uint2 a = *reinterpret_cast<const uint2*>(p.group_start + g);
-    const uint2 b = *reinterpret_cast<const uint2*>(p.group_start + g + 1);
-    k.A = ((uint64_t)a.y << 32) | a.x;
-    k.B = ((uint64_t)b.y << 32) | b.x;
-    return k;
-}
-
-// A lane's chunk ready for decoding: 96 stream bits MSB-first, shifted so that
-// the first codeword starting in the chunk is at the top; `bits` is the number
-// of bits after it in which further codewords may start.  Also the group range.
-struct State {
-    uint32_t w0, w1, w2;
-    int32_t bits;
+// Raw loads for one lane of one unit: 20 stream bytes covering its two chunks
+// plus the halo, both gaps, and the unit's output range.
+struct Raw {
+    uint4 d;        // stream bytes [8a, 8a + 16)
+    uint32_t d4;    // stream bytes [8a + 16, 8a + 20)
+    uint32_t gaps;  // gap[a] | gap[a + 1] << 8 (the second byte is not used when a + 1 is past the end)
     uint64_t A, B;
 };
 
-__device__ __forceinline__ State make_state(const DecodeParams& p, const Chunk& k, uint64_t g, uint32_t tid) {
-    State s;
-    const uint64_t c = g * kDecodeThreads + tid;
-    uint32_t w0 = __builtin_bswap32(k.d0), w1 = __builtin_bswap32(k.d1), w2 = __builtin_bswap32(k.d2);
+__device__ __forceinline__ Raw load_raw(const DecodeParams& p, uint64_t u, uint32_t tid) {
+    Raw r;
+    const uint64_t a = u * kUnitChunks + kChunksPerLane * tid;
+    r.d = make_uint4(0, 0, 0, 0);
+    r.d4 = 0;
+    r.gaps = 0;
+    if (a < p.n_chunks) {
+        // a is even: the stream load is 16-byte aligned and the gap pair 2-byte
+        // aligned; gap[a + 1] lies inside the container even when a + 1 ==
+        // n_chunks (the next section follows), and is then ignored.
+        r.d = *reinterpret_cast<const uint4*>(p.stream + 8 * a);
+        r.d4 = *reinterpret_cast<const uint32_t*>(p.stream + 8 * a + 16);
+        r.gaps = *reinterpret_cast<const uint16_t*>(p.gap + a);
+    }
+    const uint64_t g0 = u * kGroupsPerBlock;
+    const uint64_t g1 = min_u64(g0 + kGroupsPerBlock, p.n_groups);
+    const uint2 x = *reinterpret_cast<const uint2*>(p.group_start + g0);
+    const uint2 y = *reinterpret_cast<const uint2*>(p.group_start + g1);
+    r.A = ((uint64_t)x.y << 32) | x.x;
+    r.B = ((uint64_t)y.y << 32) | y.x;
+    return r;
+}
+
+// A chain ready for decoding: 96 stream bits MSB-first, shifted so that the
+// first codeword starting in the chunk is at the top; `bits` counts the bits
+// after that point in which further codewords may start.
+struct Chain {
+    uint32_t w0, w1, w2;
+    int32_t bits;
+};
+
+__device__ __forceinline__ Chain make_chain(const DecodeParams& p, uint64_t c, uint32_t d0, uint32_t d1, uint32_t d2,
+                                            uint32_t gap) {
+    Chain h;
+    const uint32_t w0 = __builtin_bswap32(d0), w1 = __builtin_bswap32(d1), w2 = __builtin_bswap32(d2);
     uint32_t end = 0;
     if (c < p.n_chunks) {
         const uint64_t left = p.stream_bits - 64 * c;
         end = left < 64 ? (uint32_t)left : 64u;
+    } else {
+        gap = 0;
     }
-    const uint64_t h01 = ((uint64_t)w0 << 32 | w1) << k.gap;
-    const uint64_t h12 = ((uint64_t)w1 << 32 | w2) << k.gap;
-    s.w0 = (uint32_t)(h01 >> 32);
-    s.w1 = (uint32_t)(h12 >> 32);
-    s.w2 = w2 << k.gap;
-    s.bits = (int32_t)end - (int32_t)k.gap;
-    s.A = uniform64(k.A);
-    s.B = uniform64(k.B);
-    return s;
+    const uint64_t h01 = ((uint64_t)w0 << 32 | w1) << gap;
+    const uint64_t h12 = ((uint64_t)w1 << 32 | w2) << gap;
+    h.w0 = (uint32_t)(h01 >> 32);
+    h.w1 = (uint32_t)(h12 >> 32);
+    h.w2 = w2 << gap;
+    h.bits = (int32_t)end - (int32_t)gap;
+    return h;
+}
+
+struct Unit {
+    Chain a, b;
+    uint64_t A, B;
+};
+
+__device__ __forceinline__ Unit make_unit(const DecodeParams& p, const Raw& r, uint64_t u, uint32_t tid) {
+    Unit x;
+    const uint64_t c = u * kUnitChunks + kChunksPerLane * tid;
+    x.a = make_chain(p, c, r.d.x, r.d.y, r.d.z, r.gaps & 0xFFu);
+    x.b = make_chain(p, c + 1, r.d.z, r.d.w, r.d4, (r.gaps >> 8) & 0xFFu);
+    x.A = uniform64(r.A);
+    x.B = uniform64(r.B);
+    return x;
+}
+
+// Entry of the codeword-start table for a code longer than the index: one
+// codeword start at offset 0, covering its L bits.
+__device__ __forceinline__ uint32_t long_count_entry(uint32_t win, uint32_t first_len, const LongTables& lt) {
+    uint32_t sym;
+    const uint32_t L = decode_long(win, first_len, lt, &sym);
+    return ((32u - L) & 31u) | (L << 8) | (1u << 16);
+}
+
+// Entry of the multi-codeword table for a code longer than the index: one symbol.
+__device__ __forceinline__ uint2 long_decode_entry(uint32_t win, uint32_t first_len, const LongTables& lt) {
+    uint32_t sym;
+    const uint32_t L = decode_long(win, first_len, lt, &sym);
+    return make_uint2(((32u - L) & 31u) | (1u << 8) | (L << 16), sym);
+}
+
+// Store the (up to four) symbol bytes of entry e at q, or at the chain's
+// dummy slot once it is past its end, and advance q by the entry's symbol
+// count.  Byte stores: ds_write_b8 takes bits 7..0 of a register and the d16_hi
+// form bits 23..16, so one byte permute feeds all four.
+__device__ __forceinline__ void put4(uint8_t*& q, const uint8_t* q_end, uint8_t* dummy, const uint2& e) {
+    uint8_t* dst = q < q_end ? q : dummy;
+    const uint32_t odd = __builtin_amdgcn_perm(e.y, e.y, 0x0C030C01u);   // [s1, 0, s3, 0]
+    dst[0] = (uint8_t)e.y;
+    dst[1] = (uint8_t)odd;
+    dst[2] = (uint8_t)(e.y >> 16);
+    dst[3] = (uint8_t)(odd >> 16);
+    q += (e.x >> 8) & 0xFFu;
 }
 
 template <int KC, int KD>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) {
     __shared__ __attribute__((aligned(16))) uint32_t s_cnt[1u << KC];
-    __shared__ __attribute__((aligned(16))) uint32_t s_dec[1u << KD];
+    __shared__ __attribute__((aligned(16))) uint2 s_dec[1u << KD];
     __shared__ __attribute__((aligned(16))) uint32_t s_long[160];
     __shared__ uint32_t s_wave[kWaves];
+    __shared__ __attribute__((aligned(16))) uint8_t s_dummy[4 * kDecodeThreads];
     extern __shared__ __attribute__((aligned(16))) uint8_t ebuf[];
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & 63u;
     const uint32_t wave = tid >> 6;
+    uint8_t* const dummy = s_dummy + 4 * tid;
 
     // stage the decode tables (built once per container) into LDS
     {
@@ -180,9 +236,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
         for (uint32_t i = tid; i < (1u << KC) / 4; i += kDecodeThreads)
             reinterpret_cast<uint4*>(s_cnt)[i] = src[i];
         src += (1u << KC) / 4;
-        for (uint32_t i = tid; i < (1u << KD) / 4; i += kDecodeThreads)
+        for (uint32_t i = tid; i < (2u << KD) / 4; i += kDecodeThreads)
             reinterpret_cast<uint4*>(s_dec)[i] = src[i];
-        src += (1u << KD) / 4;
+        src += (2u << KD) / 4;
         if (tid < 40) reinterpret_cast<uint4*>(s_long)[tid] = src[tid];
     }
     LongTables lt;
@@ -192,126 +248,187 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
     lt.sorted = reinterpret_cast<const uint8_t*>(s_long + 96);
     __syncthreads();
 
-    uint64_t g = blockIdx.x;
-    if (g >= p.n_groups) return;
-    State cur = make_state(p, load_chunk(p, g, tid), g, tid);
+    uint64_t u = blockIdx.x;
+    if (u >= p.n_blocks) return;
+    Unit cur = make_unit(p, load_raw(p, u, tid), u, tid);
 
     for (;;) {
-        // no register read below waits on memory until the next group's chunk
-        // is consumed, after phase 2: the loads issued here stay in flight
+        // Nothing below waits on memory until the next unit's loads are
+        // consumed after phase 2, so the loads issued here stay in flight.
         const uint64_t A = cur.A;
         const uint64_t B = cur.B;
         const uint64_t A0 = A & ~15ull;
         const uint32_t nblk = (uint32_t)((B - A0 + 15) >> 4);
-        uint32_t w0 = cur.w0, w1 = cur.w1, w2 = cur.w2;
 
-        // sign+mantissa bytes of this lane's first two merge blocks (block indexes
-        // past the group are clamped to the plane's last block: loaded, never used)
-        const uint4 sm0 = *reinterpret_cast<const uint4*>(p.sm + min_u64(A0 + 16ull * tid, p.sm_last));
-        const uint4 sm1 = *reinterpret_cast<const uint4*>(p.sm + min_u64(A0 + 16ull * (tid + kDecodeThreads), p.sm_last));
+        // sign+mantissa bytes of this lane's first merge blocks; block indexes
+        // past the unit are clamped to its last block (an L2 hit, never used),
+        // and every address to the plane's last block
+        const uint32_t last_blk = nblk ? nblk - 1 : 0u;
+        uint4 smv[kPrefetchBlocks];
+#pragma unroll
+        for (uint32_t k = 0; k < kPrefetchBlocks; ++k)
+            smv[k] = *reinterpret_cast<const uint4*>(
+                p.sm + min_u64(A0 + 16ull * min(tid + k * kDecodeThreads, last_blk), p.sm_last));
 
-        // next group's chunk and bounds
-        const uint64_t gn = g + gridDim.x;
-        const bool more = gn < p.n_groups;
-        Chunk nxt;
-        if (more) nxt = load_chunk(p, gn, tid);
+        const uint64_t un = u + gridDim.x;
+        const bool more = un < p.n_blocks;
+        Raw nxt;
+        if (more) nxt = load_raw(p, un, tid);
 
-        // phase 1: count the codewords starting in [start, end)
-        uint32_t count = 0;
+        // phase 1: count the codewords starting in each chunk
+        uint32_t ca = 0, cb = 0;
         {
-            uint32_t a0 = w0, a1 = w1, a2 = w2;
-            int32_t r = cur.bits;
-            while (r > 0) {
-                uint32_t e = s_cnt[a0 >> (32 - KC)];
-                if (e == 0) {                                   // a code longer than KC bits (rare)
-                    uint32_t sym;
-                    const uint32_t L = decode_long(a0, KC + 1, lt, &sym);
-                    e = ((32u - L) & 31u) | (L << 8) | (1u << 16);
+            uint32_t a0 = cur.a.w0, a1 = cur.a.w1, a2 = cur.a.w2;
+            uint32_t b0 = cur.b.w0, b1 = cur.b.w1, b2 = cur.b.w2;
+            int32_t ra = cur.a.bits, rb = cur.b.bits;
+            while (ra > 0 || rb > 0) {
+                // both lookups are issued before the (rare) long-code branch
+                uint32_t ea = s_cnt[a0 >> (32 - KC)];
+                uint32_t eb = s_cnt[b0 >> (32 - KC)];
+                if ((ea == 0) | (eb == 0)) {
+                    if (ea == 0) ea = long_count_entry(a0, KC + 1, lt);
+                    if (eb == 0) eb = long_count_entry(b0, KC + 1, lt);
                 }
-                count += __popc(__builtin_amdgcn_ubfe(e, 16, (uint32_t)(r < 16 ? r : 16)));
-                r -= (int32_t)((e >> 8) & 0xFFu);
-                consume(a0, a1, a2, e);
+                ca += __popc(__builtin_amdgcn_ubfe(ea, 16, (uint32_t)min(max(ra, 0), 16)));
+                cb += __popc(__builtin_amdgcn_ubfe(eb, 16, (uint32_t)min(max(rb, 0), 16)));
+                ra -= (int32_t)((ea >> 8) & 0xFFu);
+                rb -= (int32_t)((eb >> 8) & 0xFFu);
+                consume(a0, a1, a2, ea);
+                consume(b0, b1, b2, eb);
             }
         }
 
-        // block-wide exclusive scan of the counts
+        // block-wide exclusive scan of the lane counts
+        const uint32_t count = ca + cb;
         const uint32_t incl = wave_inclusive_scan(count);
         if (lane == 63) s_wave[wave] = incl;
         __syncthreads();
         uint32_t before = 0;
 #pragma unroll
         for (uint32_t w = 0; w < kWaves; ++w) before += (w < wave) ? s_wave[w] : 0u;
-        const uint32_t pos = before + incl - count;
+        const uint32_t pos_a = before + incl - count;
+        const uint32_t pos_b = pos_a + ca;
 
-        // phase 2: decode again and stage the exponent bytes; never past the
-        // group's element range, even for a corrupted stream
-        const uint32_t n_group = (uint32_t)(B - A);
-        const uint32_t room = pos < n_group ? n_group - pos : 0u;
-        const uint32_t todo = count < room ? count : room;
-        const uint32_t o_first = (uint32_t)(A & 15u) + pos;
-        const uint32_t o_end = o_first + todo;
-        uint8_t* q = ebuf + o_first;          // LDS address of the next symbol
-        uint8_t* const q_end = ebuf + o_end;
-        auto lookup = [&]() {
-            uint32_t e = s_dec[w0 >> (32 - KD)];
-            if (e == 0) {                                       // a code longer than KD bits (rare)
-                uint32_t sym;
-                const uint32_t L = decode_long(w0, KD + 1, lt, &sym);
-                e = ((32u - L) & 31u) | (1u << 5) | (sym << 8);
+        // phase 2: decode again and stage the exponent bytes; a chain never
+        // writes past the unit's element range, even for a corrupted stream
+        const uint32_t n_unit = (uint32_t)(B - A);
+        const uint32_t base = (uint32_t)(A & 15u);
+        const uint32_t todo_a = min(ca, pos_a < n_unit ? n_unit - pos_a : 0u);
+        const uint32_t todo_b = min(cb, pos_b < n_unit ? n_unit - pos_b : 0u);
+        uint8_t* qa = ebuf + base + pos_a;
+        uint8_t* qb = ebuf + base + pos_b;
+        uint8_t* const qa_end = qa + todo_a;
+        uint8_t* const qb_end = qb + todo_b;
+        {
+            uint32_t a0 = cur.a.w0, a1 = cur.a.w1, a2 = cur.a.w2;
+            uint32_t b0 = cur.b.w0, b1 = cur.b.w1, b2 = cur.b.w2;
+            auto step_a = [&]() {
+                uint2 e = s_dec[a0 >> (32 - KD)];
+                if (e.x == 0) e = long_decode_entry(a0, KD + 1, lt);
+                put4(qa, qa_end, dummy, e);
+                consume(a0, a1, a2, e.x);
+                return e;
+            };
+            auto step_b = [&]() {
+                uint2 e = s_dec[b0 >> (32 - KD)];
+                if (e.x == 0) e = long_decode_entry(b0, KD + 1, lt);
+                put4(qb, qb_end, dummy, e);
+                consume(b0, b1, b2, e.x);
+                return e;
+            };
+            // first lookups: each chain keeps its first three symbols aside
+            uint32_t head_a, head_b, na, nb;
+            {
+                uint2 ea = s_dec[a0 >> (32 - KD)];
+                uint2 eb = s_dec[b0 >> (32 - KD)];
+                if ((ea.x == 0) | (eb.x == 0)) {
+                    if (ea.x == 0) ea = long_decode_entry(a0, KD + 1, lt);
+                    if (eb.x == 0) eb = long_decode_entry(b0, KD + 1, lt);
+                }
+                put4(qa, qa_end, dummy, ea);
+                put4(qb, qb_end, dummy, eb);
+                consume(a0, a1, a2, ea.x);
+                consume(b0, b1, b2, eb.x);
+                head_a = ea.y;
+                head_b = eb.y;
+                na = (ea.x >> 8) & 0xFFu;
+                nb = (eb.x >> 8) & 0xFFu;
             }
-            const uint32_t t = __builtin_amdgcn_alignbit(e, e, 8);   // symbols in bytes 0, 1, 2
-            q[0] = (uint8_t)t;
-            q[1] = (uint8_t)(e >> 16);
-            q[2] = (uint8_t)(t >> 16);
-            q += (e >> 5) & 3u;
-            consume(w0, w1, w2, e);
-            return e;
-        };
-        // the first two symbols are kept aside: the left neighbour's last
-        // three-byte write may land on them
-        uint32_t head = 0;
-        if (q < q_end) {
-            const uint32_t e = lookup();
-            head = (e >> 8) & 0xFFFFu;
-            if (((e >> 5) & 3u) == 1u && q < q_end) head = (head & 0xFFu) | (lookup() & 0xFF00u);
+            while (na < kHeadBytes && qa < qa_end) {   // rare: the first lookup held fewer symbols
+                const uint2 e = step_a();
+                head_a = (head_a & ((1u << (8 * na)) - 1u)) | (e.y << (8 * na));
+                na += (e.x >> 8) & 0xFFu;
+            }
+            while (nb < kHeadBytes && qb < qb_end) {
+                const uint2 e = step_b();
+                head_b = (head_b & ((1u << (8 * nb)) - 1u)) | (e.y << (8 * nb));
+                nb += (e.x >> 8) & 0xFFu;
+            }
+            while (qa < qa_end || qb < qb_end) {
+                // both lookups are issued before the (rare) long-code branch
+                uint2 ea = s_dec[a0 >> (32 - KD)];
+                uint2 eb = s_dec[b0 >> (32 - KD)];
+                if ((ea.x == 0) | (eb.x == 0)) {
+                    if (ea.x == 0) ea = long_decode_entry(a0, KD + 1, lt);
+                    if (eb.x == 0) eb = long_decode_entry(b0, KD + 1, lt);
+                }
+                put4(qa, qa_end, dummy, ea);
+                put4(qb, qb_end, dummy, eb);
+                consume(a0, a1, a2, ea.x);
+                consume(b0, b1, b2, eb.x);
+            }
+            __syncthreads();
+            uint8_t* ha = ebuf + base + pos_a;
+            uint8_t* hb = ebuf + base + pos_b;
+#pragma unroll
+            for (uint32_t k = 0; k < kHeadBytes; ++k) {
+                if (todo_a > k) ha[k] = (uint8_t)(head_a >> (8 * k));
+                if (todo_b > k) hb[k] = (uint8_t)(head_b >> (8 * k));
+            }
         }
-        while (q < q_end) lookup();
+        // consume the next unit's loads now, before the merge issues its stores
+        Unit next = cur;
+        if (more) next = make_unit(p, nxt, un, tid);
         __syncthreads();
-        if (todo >= 1) ebuf[o_first] = (uint8_t)head;
-        if (todo >= 2) ebuf[o_first + 1] = (uint8_t)(head >> 8);
-        // consume the next group's chunk now, before the merge issues its stores
-        State next = cur;
-        if (more) next = make_state(p, nxt, gn, tid);
-        __syncthreads();
+
+        // Every prefetched block is consumed here, before any store of this
+        // unit: a load still counted as pending at the next iteration (where
+        // its registers are reloaded) would make that point wait for all
+        // outstanding memory operations, the merge stores included.
+#pragma unroll
+        for (uint32_t k = 0; k < kPrefetchBlocks; ++k)
+            asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y), "v"(smv[k].z), "v"(smv[k].w));
 
         // merge: 16 elements per lane per step, 16-byte loads and stores
-        auto merge_block = [&](uint32_t b, const uint4& s4) {
-            const uint4 e4 = *reinterpret_cast<const uint4*>(ebuf + 16 * b);
+        auto merge_block = [&](uint32_t blk, const uint4& s4) {
+            const uint4 e4 = *reinterpret_cast<const uint4*>(ebuf + 16 * blk);
             uint32_t o8[8];
             join4(s4.x, e4.x, o8[0], o8[1]);
             join4(s4.y, e4.y, o8[2], o8[3]);
             join4(s4.z, e4.z, o8[4], o8[5]);
             join4(s4.w, e4.w, o8[6], o8[7]);
-            const uint64_t base = A0 + 16ull * b;
-            if (base >= A && base + 16 <= B) {
-                uint4* dst4 = reinterpret_cast<uint4*>(p.out + base);
+            const uint64_t at = A0 + 16ull * blk;
+            if (at >= A && at + 16 <= B) {
+                uint4* dst4 = reinterpret_cast<uint4*>(p.out + at);
                 dst4[0] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
                 dst4[1] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
             } else {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const uint64_t idx = base + i;
+                    const uint64_t idx = at + i;
                     if (idx >= A && idx < B) p.out[idx] = (uint16_t)(o8[i >> 1] >> (16 * (i & 1)));
                 }
             }
         };
-        if (tid < nblk) merge_block(tid, sm0);
-        if (tid + kDecodeThreads < nblk) merge_block(tid + kDecodeThreads, sm1);
-        for (uint32_t b = tid + 2 * kDecodeThreads; b < nblk; b += kDecodeThreads)
-            merge_block(b, *reinterpret_cast<const uint4*>(p.sm + A0 + 16ull * b));
+#pragma unroll
+        for (uint32_t k = 0; k < kPrefetchBlocks; ++k)
+            if (tid + k * kDecodeThreads < nblk) merge_block(tid + k * kDecodeThreads, smv[k]);
+        for (uint32_t blk = tid + kPrefetchBlocks * kDecodeThreads; blk < nblk; blk += kDecodeThreads)
+            merge_block(blk, *reinterpret_cast<const uint4*>(p.sm + A0 + 16ull * blk));
+
         if (!more) break;
-        __syncthreads();   // ebuf and s_wave are reused by the next group
-        g = gn;
+        __syncthreads();   // ebuf and s_wave are reused by the next unit
+        u = un;
         cur = next;
     }
 }
@@ -323,7 +440,7 @@ __global__ __launch_bounds__(1024) void build_tables_kernel(CodeLens lens, uint3
     static_assert(KC <= (int)kSingleBits && KD <= (int)kSingleBits, "index wider than the single table");
     __shared__ uint32_t count[32], first[32], base[32];
     __shared__ uint8_t sorted[256];
-    __shared__ uint32_t single[1u << kS];   // symbol | length << 8, or ~0 for a longer code
+    __shared__ uint32_t single[1u << kS];   // rotated symbol | length << 8, or ~0 for a longer code
     const uint32_t tid = threadIdx.x;
     if (tid == 0) {
         for (int L = 0; L < 32; ++L) count[L] = 0;
@@ -337,7 +454,7 @@ __global__ __launch_bounds__(1024) void build_tables_kernel(CodeLens lens, uint3
             first[L] = code;             // first code of length L (canonical)
             base[L] = rank;
             for (int s = 0; s < 256; ++s)
-                if (lens.len[s] == L) sorted[rank++] = (uint8_t)s;
+                if (lens.len[s] == L) sorted[rank++] = (uint8_t)((s >> 1) | ((s & 1) << 7));
         }
         first[0] = 0;
         base[0] = 0;
@@ -369,10 +486,10 @@ __global__ __launch_bounds__(1024) void build_tables_kernel(CodeLens lens, uint3
         }
         tables[w] = at ? (((32u - at) & 31u) | (at << 8) | (mask << 16)) : 0u;
     }
-    // multi-codeword table
+    // multi-codeword table: up to four whole codewords per window
     for (uint32_t w = tid; w < (1u << KD); w += blockDim.x) {
         uint32_t at = 0, n = 0, syms = 0;
-        while (n < 3) {
+        while (n < 4) {
             const uint32_t x = ((w << at) & ((1u << KD) - 1u)) << (kS - KD);
             const uint32_t s = single[x];
             if (s == 0xFFFFFFFFu) break;
@@ -382,9 +499,10 @@ __global__ __launch_bounds__(1024) void build_tables_kernel(CodeLens lens, uint3
             ++n;
             at += L;
         }
-        tables[(1u << KC) + w] = n ? (((32u - at) & 31u) | (n << 5) | (syms << 8)) : 0u;
+        tables[(1u << KC) + 2 * w] = n ? (((32u - at) & 31u) | (n << 8) | (at << 16)) : 0u;
+        tables[(1u << KC) + 2 * w + 1] = syms;
     }
-    uint32_t* tail = tables + (1u << KC) + (1u << KD);
+    uint32_t* tail = tables + (1u << KC) + (2u << KD);
     if (tid < 32) {
         tail[tid] = count[tid];
         tail[32 + tid] = first[tid];
@@ -417,17 +535,17 @@ struct Variant {
 
 template <typename F>
 auto dispatch(uint32_t kc, uint32_t kd, F&& f) {
-    if (kc == 12 && kd == 12) return f(Variant<12, 12>{});
     if (kc == 12 && kd == 11) return f(Variant<12, 11>{});
     if (kc == 12 && kd == 10) return f(Variant<12, 10>{});
     if (kc == 11 && kd == 11) return f(Variant<11, 11>{});
+    if (kc == 11 && kd == 10) return f(Variant<11, 10>{});
     return f(Variant<10, 10>{});
 }
 
 }  // namespace
 
 uint32_t decode_lds_bytes(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes) {
-    return table_words(count_bits, decode_bits) * 4u + kWaves * 4u + ebuf_bytes;
+    return table_words(count_bits, decode_bits) * 4u + kWaves * 4u + 4u * kDecodeThreads + ebuf_bytes;
 }
 
 int decode_blocks_per_cu(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes) {

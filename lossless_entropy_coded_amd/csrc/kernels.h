@@ -8,29 +8,38 @@
 
 namespace wc {
 
-constexpr uint32_t kDecodeThreads = 256;   // one 64-bit chunk per lane, G = 256 chunks per group
+constexpr uint32_t kDecodeThreads = 256;   // lanes per workgroup = chunks per group G
+constexpr uint32_t kChunksPerLane = 2;     // each lane decodes two adjacent 64-bit chunks
+constexpr uint32_t kGroupsPerBlock = kChunksPerLane;   // so a workgroup covers two adjacent groups
 constexpr uint32_t kSingleBits = 12;       // width of the build-time single-codeword table
-constexpr uint32_t kEbufSlack = 2;         // bytes a lane may write past its range (then rewritten)
+constexpr uint32_t kEbufSlack = 3;         // bytes a chain may write past its range (then rewritten)
+constexpr uint32_t kHeadBytes = 3;         // leading bytes of a chain that a left neighbour may overwrite
 
 // Device decode tables, as 32-bit words, for index widths KC (counting) and KD (decoding):
-//   [0, 2^KC)              codeword-start table: for a KC-bit window,
-//                            bits 0..4   (32 - adv) & 31      (funnel-shift amount)
-//                            bits 8..15  adv = bits covered by the whole codewords in the window
-//                            bits 16..31 mask of the offsets where those codewords start
-//                          0 when the first codeword is longer than KC bits;
-//   [2^KC, 2^KC + 2^KD)    multi-codeword table: for a KD-bit window, up to three codewords
-//                            bits 0..4   (32 - nbits) & 31, bits 5..6 number of symbols (1..3),
-//                            bits 8..15, 16..23, 24..31 the symbols in stream order
-//                          0 when the first codeword is longer than KD bits;
+//   [0, 2^KC)                codeword-start table: for a KC-bit window,
+//                              bits 0..4   (32 - adv) & 31      (funnel-shift amount)
+//                              bits 8..15  adv = bits covered by the whole codewords in the window
+//                              bits 16..31 mask of the offsets where those codewords start
+//                            0 when the first codeword is longer than KC bits;
+//   [2^KC, 2^KC + 2*2^KD)    multi-codeword table, two words per KD-bit window, up to four
+//                            whole codewords:
+//                              word 0: bits 0..4 (32 - nbits) & 31, bits 8..15 number of
+//                                      symbols n (1..4), bits 16..23 nbits
+//                              word 1: the n symbols, first in the lowest byte
+//                            word 0 is 0 when the first codeword is longer than KD bits;
 //   then 32 words count[L], 32 words first[L] (canonical first code of length L),
 //   32 words base[L] (rank of the first symbol of length L), 64 words holding the
 //   256 symbols sorted by (length, symbol) -- used for codes longer than the index.
+// Symbols in the multi-codeword and sorted tables are stored rotated right by one
+// bit, e' = (e >> 1) | (e & 1) << 7: e' & 0x7F is the exponent's part of the bf16
+// high byte and e' & 0x80 its part of the low byte.
 inline uint32_t table_words(uint32_t count_bits, uint32_t decode_bits) {
-    return (1u << count_bits) + (1u << decode_bits) + 160u;
+    return (1u << count_bits) + (2u << decode_bits) + 160u;
 }
 inline bool supported_table_bits(uint32_t count_bits, uint32_t decode_bits) {
-    return (count_bits == 12 && (decode_bits == 10 || decode_bits == 11 || decode_bits == 12)) ||
-           (count_bits == 11 && decode_bits == 11) || (count_bits == 10 && decode_bits == 10);
+    return (count_bits == 12 && (decode_bits == 11 || decode_bits == 10)) ||
+           (count_bits == 11 && (decode_bits == 11 || decode_bits == 10)) ||
+           (count_bits == 10 && decode_bits == 10);
 }
 
 struct CodeLens {
@@ -48,6 +57,7 @@ struct DecodeParams {
     uint64_t stream_bits;
     uint64_t n_groups;
     uint64_t sm_last;        // offset of the last 16-byte block of the sm plane: round_up(n, 16) - 16
+    uint64_t n_blocks;       // workgroup-sized units: ceil(n_groups / kGroupsPerBlock)
     uint32_t ebuf_bytes;
     uint32_t pad;
 };

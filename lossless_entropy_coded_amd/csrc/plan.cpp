@@ -25,8 +25,10 @@ struct wc_plan_s {
     wc::Header h;
     std::vector<uint64_t> tensor_offsets, tensor_numels;
     uint64_t max_group_elems = 0;
-    uint32_t count_bits = 12;    // index width of the codeword-start table
-    uint32_t decode_bits = 11;   // index width of the multi-codeword table
+    uint64_t max_unit_elems = 0;    // elements of kGroupsPerBlock adjacent groups (one workgroup unit)
+    uint64_t n_blocks = 0;          // workgroup units
+    uint32_t count_bits = 11;    // index width of the codeword-start table
+    uint32_t decode_bits = 10;   // index width of the multi-codeword table
     uint32_t grid = 0;
     uint32_t lds_bytes = 0;
     uint32_t ebuf_bytes = 0;
@@ -178,15 +180,27 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         return st;
     }
     p->device = hip_device;
-    p->count_bits = env_u32("WC_COUNT_BITS", 12);
-    p->decode_bits = env_u32("WC_DECODE_BITS", 11);
+    p->count_bits = env_u32("WC_COUNT_BITS", 11);
+    p->decode_bits = env_u32("WC_DECODE_BITS", 10);
     if (!wc::supported_table_bits(p->count_bits, p->decode_bits)) {
-        p->count_bits = 12;
-        p->decode_bits = 11;
+        p->count_bits = 11;
+        p->decode_bits = 10;
     }
-    // staging buffer: the group's exponents at offset (A mod 16), plus the
-    // bytes a lane's last three-byte write may reach past the group's end
-    p->ebuf_bytes = (uint32_t)wc::round_up(p->max_group_elems + 15 + wc::kEbufSlack, 16);
+    // workgroup units: kGroupsPerBlock adjacent groups, one contiguous output range
+    {
+        const uint8_t* gs = blob_host + p->h.off_group_start;
+        const uint64_t ng = p->h.n_groups;
+        p->n_blocks = wc::div_up(ng, wc::kGroupsPerBlock);
+        for (uint64_t u = 0; u < p->n_blocks; ++u) {
+            const uint64_t g0 = u * wc::kGroupsPerBlock;
+            const uint64_t g1 = std::min<uint64_t>(g0 + wc::kGroupsPerBlock, ng);
+            p->max_unit_elems = std::max(p->max_unit_elems, wc::load_le<uint64_t>(gs + 8 * g1) -
+                                                                wc::load_le<uint64_t>(gs + 8 * g0));
+        }
+    }
+    // staging buffer: the unit's exponents at offset (A mod 16), plus the
+    // bytes a chain's last three-byte write may reach past the unit's end
+    p->ebuf_bytes = (uint32_t)wc::round_up(p->max_unit_elems + 15 + wc::kEbufSlack, 16);
     p->lds_bytes = wc::decode_lds_bytes(p->count_bits, p->decode_bits, p->ebuf_bytes);
 
     DeviceGuard guard(hip_device);
@@ -207,7 +221,7 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
     uint64_t want = (uint64_t)n_cu * (uint64_t)per_cu;
     uint32_t forced = env_u32("WC_GRID", 0);
     if (forced) want = forced;
-    p->grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(want, std::max<uint64_t>(p->h.n_groups, 1)));
+    p->grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(want, std::max<uint64_t>(p->n_blocks, 1)));
 
     const size_t tbytes = (size_t)wc::table_words(p->count_bits, p->decode_bits) * 4;
     if (hipMalloc(reinterpret_cast<void**>(&p->d_tables), tbytes) != hipSuccess) {
@@ -270,6 +284,7 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
     d.stream_bits = p->h.stream_bits;
     d.n_groups = p->h.n_groups;
     d.sm_last = wc::round_up(p->h.n_elems, 16) - 16;
+    d.n_blocks = p->n_blocks;
     d.ebuf_bytes = p->ebuf_bytes;
     d.pad = 0;
     hipError_t e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->grid, p->ebuf_bytes,
