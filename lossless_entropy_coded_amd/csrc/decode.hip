@@ -25,9 +25,10 @@
 //            land on the next chain's first three bytes, which that chain
 //            keeps aside and rewrites after a barrier; writes of a finished
 //            chain go to a per-lane dummy slot;
-//   merge    the workgroup joins the sign+mantissa bytes (prefetched with
-//            16-byte loads while the phases run) with the staged exponents in
-//            integer registers and writes bf16 with 16-byte stores.
+//   merge    the workgroup joins the sign+mantissa bytes (prefetched while
+//            the phases run) with the staged exponents in integer registers,
+//            8 elements per lane and step, and writes bf16 with 16-byte stores
+//            that are contiguous across the lanes of a wave.
 // Workgroups are persistent: each stages the tables once and loops over its
 // units, loading the next unit's chunks while it works on the current one.
 #include <hip/hip_runtime.h>
@@ -42,7 +43,11 @@ namespace {
 constexpr uint32_t kCodeLimit = 24;
 constexpr uint32_t kWaves = kDecodeThreads / 64;
 constexpr uint32_t kUnitChunks = kDecodeThreads * kChunksPerLane;   // chunks per workgroup unit
-constexpr uint32_t kPrefetchBlocks = 4;                            // 16-element merge blocks per lane
+// bf16 output is written with non-temporal 16-byte stores: it is not read
+// again by this kernel and streams past the caches
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kMergeElems = 8;                                // elements per lane per merge step
+constexpr uint32_t kPrefetchBlocks = 8;                            // merge blocks per lane loaded ahead
 
 struct LongTables {
     const uint32_t* count;
@@ -118,7 +123,8 @@ struct Raw {
     uint4 d;        // stream bytes [8a, 8a + 16)
     uint32_t d4;    // stream bytes [8a + 16, 8a + 20)
     uint32_t gaps;  // gap[a] | gap[a + 1] << 8 (the second byte is not used when a + 1 is past the end)
-    uint64_t A, B;
+    uint64_t A;     // first element of the unit
+    uint32_t B;     // low 32 bits of its end (B - A < 2^32: a unit holds at most 2^15 codewords)
 };
 
 __device__ __forceinline__ Raw load_raw(const DecodeParams& p, uint64_t u, uint32_t tid) {
@@ -138,9 +144,8 @@ __device__ __forceinline__ Raw load_raw(const DecodeParams& p, uint64_t u, uint3
     const uint64_t g0 = u * kGroupsPerBlock;
     const uint64_t g1 = min_u64(g0 + kGroupsPerBlock, p.n_groups);
     const uint2 x = *reinterpret_cast<const uint2*>(p.group_start + g0);
-    const uint2 y = *reinterpret_cast<const uint2*>(p.group_start + g1);
     r.A = ((uint64_t)x.y << 32) | x.x;
-    r.B = ((uint64_t)y.y << 32) | y.x;
+    r.B = *reinterpret_cast<const uint32_t*>(p.group_start + g1);   // little-endian low word
     return r;
 }
 
@@ -174,7 +179,8 @@ __device__ __forceinline__ Chain make_chain(const DecodeParams& p, uint64_t c, u
 
 struct Unit {
     Chain a, b;
-    uint64_t A, B;
+    uint64_t A;
+    uint32_t B;
 };
 
 __device__ __forceinline__ Unit make_unit(const DecodeParams& p, const Raw& r, uint64_t u, uint32_t tid) {
@@ -183,7 +189,7 @@ __device__ __forceinline__ Unit make_unit(const DecodeParams& p, const Raw& r, u
     x.a = make_chain(p, c, r.d.x, r.d.y, r.d.z, r.gaps & 0xFFu);
     x.b = make_chain(p, c + 1, r.d.z, r.d.w, r.d4, (r.gaps >> 8) & 0xFFu);
     x.A = uniform64(r.A);
-    x.B = uniform64(r.B);
+    x.B = __builtin_amdgcn_readfirstlane(r.B);
     return x;
 }
 
@@ -255,20 +261,26 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
     for (;;) {
         // Nothing below waits on memory until the next unit's loads are
         // consumed after phase 2, so the loads issued here stay in flight.
+        // The unit's elements [A, B) are merged in blocks of 8 starting at
+        // A0 = A rounded down to 8; offsets inside the unit fit 32 bits, so
+        // every global access is a uniform base plus a 32-bit lane offset.
         const uint64_t A = cur.A;
-        const uint64_t B = cur.B;
-        const uint64_t A0 = A & ~15ull;
-        const uint32_t nblk = (uint32_t)((B - A0 + 15) >> 4);
+        const uint64_t A0 = A & ~(uint64_t)(kMergeElems - 1);
+        const uint32_t lo_rel = (uint32_t)(A - A0);
+        const uint32_t hi_rel = cur.B - (uint32_t)A0;
+        const uint32_t nblk = (hi_rel + kMergeElems - 1) / kMergeElems;
 
         // sign+mantissa bytes of this lane's first merge blocks; block indexes
-        // past the unit are clamped to its last block (an L2 hit, never used),
-        // and every address to the plane's last block
+        // past the unit are clamped to its last block (an L2 hit, never used).
+        // With nblk >= 1 every block lies inside round_up(n, 8) <= the plane's
+        // padded size; an empty unit reads the plane's last piece instead.
         const uint32_t last_blk = nblk ? nblk - 1 : 0u;
-        uint4 smv[kPrefetchBlocks];
+        const uint8_t* const smu = p.sm + min_u64(A0, p.sm_last);
+        uint16_t* const outu = p.out + A0;
+        uint2 smv[kPrefetchBlocks];
 #pragma unroll
         for (uint32_t k = 0; k < kPrefetchBlocks; ++k)
-            smv[k] = *reinterpret_cast<const uint4*>(
-                p.sm + min_u64(A0 + 16ull * min(tid + k * kDecodeThreads, last_blk), p.sm_last));
+            smv[k] = *reinterpret_cast<const uint2*>(smu + kMergeElems * min(tid + k * kDecodeThreads, last_blk));
 
         const uint64_t un = u + gridDim.x;
         const bool more = un < p.n_blocks;
@@ -311,8 +323,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
 
         // phase 2: decode again and stage the exponent bytes; a chain never
         // writes past the unit's element range, even for a corrupted stream
-        const uint32_t n_unit = (uint32_t)(B - A);
-        const uint32_t base = (uint32_t)(A & 15u);
+        const uint32_t n_unit = hi_rel - lo_rel;
+        const uint32_t base = lo_rel;
         const uint32_t todo_a = min(ca, pos_a < n_unit ? n_unit - pos_a : 0u);
         const uint32_t todo_b = min(cb, pos_b < n_unit ? n_unit - pos_b : 0u);
         uint8_t* qa = ebuf + base + pos_a;
@@ -397,34 +409,52 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
         // outstanding memory operations, the merge stores included.
 #pragma unroll
         for (uint32_t k = 0; k < kPrefetchBlocks; ++k)
-            asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y), "v"(smv[k].z), "v"(smv[k].w));
+            asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
 
-        // merge: 16 elements per lane per step, 16-byte loads and stores
-        auto merge_block = [&](uint32_t blk, const uint4& s4) {
-            const uint4 e4 = *reinterpret_cast<const uint4*>(ebuf + 16 * blk);
-            uint32_t o8[8];
-            join4(s4.x, e4.x, o8[0], o8[1]);
-            join4(s4.y, e4.y, o8[2], o8[3]);
-            join4(s4.z, e4.z, o8[4], o8[5]);
-            join4(s4.w, e4.w, o8[6], o8[7]);
-            const uint64_t at = A0 + 16ull * blk;
-            if (at >= A && at + 16 <= B) {
-                uint4* dst4 = reinterpret_cast<uint4*>(p.out + at);
-                dst4[0] = make_uint4(o8[0], o8[1], o8[2], o8[3]);
-                dst4[1] = make_uint4(o8[4], o8[5], o8[6], o8[7]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const uint64_t idx = at + i;
-                    if (idx >= A && idx < B) p.out[idx] = (uint16_t)(o8[i >> 1] >> (16 * (i & 1)));
-                }
-            }
+        // merge: 8 elements per lane per step; consecutive lanes take
+        // consecutive blocks, so each wave-wide 8-byte load and 16-byte store
+        // covers one contiguous range (whole 64-byte segments)
+        // (whole blocks only: the unit's first and last block may be shared
+        // with the neighbouring units and are written element by element below)
+        const uint32_t full_lo = (lo_rel + kMergeElems - 1) / kMergeElems;
+        const uint32_t full_hi = hi_rel / kMergeElems;
+        auto merge_block = [&](uint32_t blk, const uint2& s2) {
+            const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + kMergeElems * blk);
+            uint32_t o0, o1, o2, o3;
+            join4(s2.x, e2.x, o0, o1);
+            join4(s2.y, e2.y, o2, o3);
+            u32x4 v;
+            v.x = o0;
+            v.y = o1;
+            v.z = o2;
+            v.w = o3;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(outu + kMergeElems * blk));
         };
 #pragma unroll
-        for (uint32_t k = 0; k < kPrefetchBlocks; ++k)
-            if (tid + k * kDecodeThreads < nblk) merge_block(tid + k * kDecodeThreads, smv[k]);
-        for (uint32_t blk = tid + kPrefetchBlocks * kDecodeThreads; blk < nblk; blk += kDecodeThreads)
-            merge_block(blk, *reinterpret_cast<const uint4*>(p.sm + A0 + 16ull * blk));
+        for (uint32_t k = 0; k < kPrefetchBlocks; ++k) {
+            const uint32_t blk = tid + k * kDecodeThreads;
+            if (blk >= full_lo && blk < full_hi) merge_block(blk, smv[k]);
+        }
+        for (uint32_t blk = tid + kPrefetchBlocks * kDecodeThreads; blk < full_hi; blk += kDecodeThreads)
+            merge_block(blk, *reinterpret_cast<const uint2*>(smu + kMergeElems * blk));
+        // partial edge blocks: lane 0 takes the first, lane 1 the last
+        {
+            const uint32_t blk = tid == 0 ? 0u : nblk - 1;
+            const bool partial = tid == 0 ? full_lo > 0 : (tid == 1 && full_hi < nblk && nblk - 1 >= full_lo);
+            if (partial) {
+                const uint32_t rel = kMergeElems * blk;
+                const uint2 s2 = *reinterpret_cast<const uint2*>(smu + rel);
+                const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + rel);
+                uint32_t o[4];
+                join4(s2.x, e2.x, o[0], o[1]);
+                join4(s2.y, e2.y, o[2], o[3]);
+#pragma unroll
+                for (uint32_t i = 0; i < kMergeElems; ++i) {
+                    const uint32_t idx = rel + i;
+                    if (idx >= lo_rel && idx < hi_rel) outu[idx] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
+                }
+            }
+        }
 
         if (!more) break;
         __syncthreads();   // ebuf and s_wave are reused by the next unit

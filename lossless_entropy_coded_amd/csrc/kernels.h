@@ -56,7 +56,7 @@ struct DecodeParams {
     uint64_t n_chunks;
     uint64_t stream_bits;
     uint64_t n_groups;
-    uint64_t sm_last;        // offset of the last 16-byte block of the sm plane: round_up(n, 16) - 16
+    uint64_t sm_last;        // offset of the last 8-byte piece of the sm plane: round_up(n, 8) - 8
     uint64_t n_blocks;       // workgroup-sized units: ceil(n_groups / kGroupsPerBlock)
     uint32_t ebuf_bytes;
     uint32_t pad;

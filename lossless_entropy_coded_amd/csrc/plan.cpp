@@ -283,7 +283,7 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
     d.n_chunks = p->h.n_chunks;
     d.stream_bits = p->h.stream_bits;
     d.n_groups = p->h.n_groups;
-    d.sm_last = wc::round_up(p->h.n_elems, 16) - 16;
+    d.sm_last = wc::round_up(p->h.n_elems, 8) - 8;
     d.n_blocks = p->n_blocks;
     d.ebuf_bytes = p->ebuf_bytes;
     d.pad = 0;
