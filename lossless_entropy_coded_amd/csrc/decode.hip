@@ -46,7 +46,6 @@ constexpr uint32_t kUnitChunks = kDecodeThreads * kChunksPerLane;   // chunks pe
 // bf16 output is written with non-temporal 16-byte stores: it is not read
 // again by this kernel and streams past the caches
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-constexpr uint32_t kMergeElems = 8;                                // elements per lane per merge step
 constexpr uint32_t kPrefetchBlocks = 8;                            // merge blocks per lane loaded ahead
 
 struct LongTables {
@@ -261,11 +260,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
     for (;;) {
         // Nothing below waits on memory until the next unit's loads are
         // consumed after phase 2, so the loads issued here stay in flight.
-        // The unit's elements [A, B) are merged in blocks of 8 starting at
-        // A0 = A rounded down to 8; offsets inside the unit fit 32 bits, so
-        // every global access is a uniform base plus a 32-bit lane offset.
+        // The unit's elements [A, B) are merged in blocks of 8 counted from
+        // A0 = A rounded down to 64, so that the wave-wide accesses cover
+        // whole cache lines; offsets inside the unit fit 32 bits, so every
+        // global access is a uniform base plus a 32-bit lane offset.
         const uint64_t A = cur.A;
-        const uint64_t A0 = A & ~(uint64_t)(kMergeElems - 1);
+        const uint64_t A0 = A & ~(uint64_t)(kMergeAlign - 1);
         const uint32_t lo_rel = (uint32_t)(A - A0);
         const uint32_t hi_rel = cur.B - (uint32_t)A0;
         const uint32_t nblk = (hi_rel + kMergeElems - 1) / kMergeElems;
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
         // sign+mantissa bytes of this lane's first merge blocks; block indexes
         // past the unit are clamped to its last block (an L2 hit, never used).
         // With nblk >= 1 every block lies inside round_up(n, 8) <= the plane's
-        // padded size; an empty unit reads the plane's last piece instead.
+        // padded size; a unit with no block reads the plane's last piece.
         const uint32_t last_blk = nblk ? nblk - 1 : 0u;
         const uint8_t* const smu = p.sm + min_u64(A0, p.sm_last);
         uint16_t* const outu = p.out + A0;
@@ -414,8 +414,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
         // merge: 8 elements per lane per step; consecutive lanes take
         // consecutive blocks, so each wave-wide 8-byte load and 16-byte store
         // covers one contiguous range (whole 64-byte segments)
-        // (whole blocks only: the unit's first and last block may be shared
-        // with the neighbouring units and are written element by element below)
+        // (whole blocks inside [A, B) only: the block holding A and the one
+        // holding B may be shared with the neighbouring units and are written
+        // element by element below)
         const uint32_t full_lo = (lo_rel + kMergeElems - 1) / kMergeElems;
         const uint32_t full_hi = hi_rel / kMergeElems;
         auto merge_block = [&](uint32_t blk, const uint2& s2) {
@@ -437,10 +438,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
         }
         for (uint32_t blk = tid + kPrefetchBlocks * kDecodeThreads; blk < full_hi; blk += kDecodeThreads)
             merge_block(blk, *reinterpret_cast<const uint2*>(smu + kMergeElems * blk));
-        // partial edge blocks: lane 0 takes the first, lane 1 the last
+        // partial edge blocks: lane 0 takes the one holding A, lane 1 the one
+        // holding B unless it is the same block
         {
-            const uint32_t blk = tid == 0 ? 0u : nblk - 1;
-            const bool partial = tid == 0 ? full_lo > 0 : (tid == 1 && full_hi < nblk && nblk - 1 >= full_lo);
+            const uint32_t blk = tid == 0 ? lo_rel / kMergeElems : nblk - 1;
+            const bool partial =
+                tid == 0 ? (lo_rel % kMergeElems) != 0 : (tid == 1 && full_hi < nblk && nblk - 1 >= full_lo);
             if (partial) {
                 const uint32_t rel = kMergeElems * blk;
                 const uint2 s2 = *reinterpret_cast<const uint2*>(smu + rel);

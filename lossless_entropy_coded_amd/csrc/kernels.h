@@ -14,6 +14,9 @@ constexpr uint32_t kGroupsPerBlock = kChunksPerLane;   // so a workgroup covers 
 constexpr uint32_t kSingleBits = 12;       // width of the build-time single-codeword table
 constexpr uint32_t kEbufSlack = 3;         // bytes a chain may write past its range (then rewritten)
 constexpr uint32_t kHeadBytes = 3;         // leading bytes of a chain that a left neighbour may overwrite
+constexpr uint32_t kMergeElems = 8;        // elements per lane per merge step (one 16-byte bf16 store)
+constexpr uint32_t kMergeAlign = 64;       // a unit's merge range starts at a multiple of 64 elements
+                                           // (128 B of bf16, 64 B of sign+mantissa)
 
 // Device decode tables, as 32-bit words, for index widths KC (counting) and KD (decoding):
 //   [0, 2^KC)                codeword-start table: for a KC-bit window,

@@ -200,7 +200,10 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
     }
     // staging buffer: the unit's exponents at offset (A mod 16), plus the
     // bytes a chain's last three-byte write may reach past the unit's end
-    p->ebuf_bytes = (uint32_t)wc::round_up(p->max_unit_elems + 15 + wc::kEbufSlack, 16);
+    // staging of one unit: its exponents start at A mod kMergeAlign, a chain may
+    // write kEbufSlack bytes past the end, and the merge reads whole blocks
+    p->ebuf_bytes = (uint32_t)wc::round_up(
+        p->max_unit_elems + (wc::kMergeAlign - 1) + (wc::kMergeElems - 1) + wc::kEbufSlack, 16);
     p->lds_bytes = wc::decode_lds_bytes(p->count_bits, p->decode_bits, p->ebuf_bytes);
 
     DeviceGuard guard(hip_device);
