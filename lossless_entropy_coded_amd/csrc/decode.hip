@@ -53,6 +53,9 @@ struct LongTables {
     const uint32_t* first;
     const uint32_t* base;
     const uint8_t* sorted;
+    const uint16_t* l2;   // second level: (length << 8) | rotated symbol, or 0
+    uint32_t l2_first;    // KD-bit prefix of the first code longer than KD
+    uint32_t l2_n;        // long-code prefixes the second level covers (at most kL2Prefixes)
 };
 
 // Canonical decode of a codeword longer than the table index.  `win` holds at
@@ -192,19 +195,38 @@ __device__ __forceinline__ Unit make_unit(const DecodeParams& p, const Raw& r, u
     return x;
 }
 
+// First codeword of a window whose first codeword is longer than KD bits:
+// (length << 8) | rotated symbol.  Canonical codes longer than KD bits all
+// have KD-bit prefixes >= l2_first; the second-level table, indexed by such a
+// prefix and the kL2Bits bits after it, resolves every code of at most
+// KD + kL2Bits bits with one lookup.  Longer codes, and prefixes past the
+// table, take the length-by-length canonical search.
+template <int KD>
+__device__ __forceinline__ uint32_t long_code(uint32_t win, uint32_t first_len, const LongTables& t) {
+    const uint32_t idx = (win >> (32 - KD - kL2Bits)) - (t.l2_first << kL2Bits);
+    if (idx < (t.l2_n << kL2Bits)) {
+        const uint32_t e = t.l2[idx];
+        if (e != 0) return e;
+    }
+    uint32_t sym;
+    const uint32_t L = decode_long(win, first_len, t, &sym);
+    return (L << 8) | sym;
+}
+
 // Entry of the codeword-start table for a code longer than the index: one
 // codeword start at offset 0, covering its L bits.
+template <int KD>
 __device__ __forceinline__ uint32_t long_count_entry(uint32_t win, uint32_t first_len, const LongTables& lt) {
-    uint32_t sym;
-    const uint32_t L = decode_long(win, first_len, lt, &sym);
+    const uint32_t L = long_code<KD>(win, first_len, lt) >> 8;
     return ((32u - L) & 31u) | (L << 8) | (1u << 16);
 }
 
 // Entry of the multi-codeword table for a code longer than the index: one symbol.
+template <int KD>
 __device__ __forceinline__ uint2 long_decode_entry(uint32_t win, uint32_t first_len, const LongTables& lt) {
-    uint32_t sym;
-    const uint32_t L = decode_long(win, first_len, lt, &sym);
-    return make_uint2(((32u - L) & 31u) | (1u << 8) | (L << 16), sym);
+    const uint32_t c = long_code<KD>(win, first_len, lt);
+    const uint32_t L = c >> 8;
+    return make_uint2(((32u - L) & 31u) | (1u << 8) | (L << 16), c & 0xFFu);
 }
 
 // Store the (up to four) symbol bytes of entry e at q, or at the chain's
@@ -225,10 +247,13 @@ template <int KC, int KD>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) {
     __shared__ __attribute__((aligned(16))) uint32_t s_cnt[1u << KC];
     __shared__ __attribute__((aligned(16))) uint2 s_dec[1u << KD];
-    __shared__ __attribute__((aligned(16))) uint32_t s_long[160];
+    __shared__ __attribute__((aligned(16))) uint32_t s_long[kLongWords];
     __shared__ uint32_t s_wave[kWaves];
     __shared__ __attribute__((aligned(16))) uint8_t s_dummy[4 * kDecodeThreads];
+    // dynamic: the unit's exponent staging (ebuf_bytes), then the second-level
+    // table for the long-code prefixes this container has (l2_cap * 2^kL2Bits u16)
     extern __shared__ __attribute__((aligned(16))) uint8_t ebuf[];
+    uint16_t* const s_l2 = reinterpret_cast<uint16_t*>(ebuf + p.ebuf_bytes);
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & 63u;
@@ -244,14 +269,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
         for (uint32_t i = tid; i < (2u << KD) / 4; i += kDecodeThreads)
             reinterpret_cast<uint4*>(s_dec)[i] = src[i];
         src += (2u << KD) / 4;
-        if (tid < 40) reinterpret_cast<uint4*>(s_long)[tid] = src[tid];
+        if (tid < kLongWords / 4) reinterpret_cast<uint4*>(s_long)[tid] = src[tid];
+        src += kLongWords / 4;
+        for (uint32_t i = tid; i < (p.l2_cap << kL2Bits) / 8; i += kDecodeThreads)
+            reinterpret_cast<uint4*>(s_l2)[i] = src[i];
     }
+    __syncthreads();
     LongTables lt;
     lt.count = s_long;
     lt.first = s_long + 32;
     lt.base = s_long + 64;
     lt.sorted = reinterpret_cast<const uint8_t*>(s_long + 96);
-    __syncthreads();
+    lt.l2 = s_l2;
+    lt.l2_first = __builtin_amdgcn_readfirstlane(s_long[160]);
+    lt.l2_n = min(__builtin_amdgcn_readfirstlane(s_long[161]), p.l2_cap);
 
     uint64_t u = blockIdx.x;
     if (u >= p.n_blocks) return;
@@ -298,8 +329,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
                 uint32_t ea = s_cnt[a0 >> (32 - KC)];
                 uint32_t eb = s_cnt[b0 >> (32 - KC)];
                 if ((ea == 0) | (eb == 0)) {
-                    if (ea == 0) ea = long_count_entry(a0, KC + 1, lt);
-                    if (eb == 0) eb = long_count_entry(b0, KC + 1, lt);
+                    if (ea == 0) ea = long_count_entry<KD>(a0, KC + 1, lt);
+                    if (eb == 0) eb = long_count_entry<KD>(b0, KC + 1, lt);
                 }
                 ca += __popc(__builtin_amdgcn_ubfe(ea, 16, (uint32_t)min(max(ra, 0), 16)));
                 cb += __popc(__builtin_amdgcn_ubfe(eb, 16, (uint32_t)min(max(rb, 0), 16)));
@@ -336,14 +367,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
             uint32_t b0 = cur.b.w0, b1 = cur.b.w1, b2 = cur.b.w2;
             auto step_a = [&]() {
                 uint2 e = s_dec[a0 >> (32 - KD)];
-                if (e.x == 0) e = long_decode_entry(a0, KD + 1, lt);
+                if (e.x == 0) e = long_decode_entry<KD>(a0, KD + 1, lt);
                 put4(qa, qa_end, dummy, e);
                 consume(a0, a1, a2, e.x);
                 return e;
             };
             auto step_b = [&]() {
                 uint2 e = s_dec[b0 >> (32 - KD)];
-                if (e.x == 0) e = long_decode_entry(b0, KD + 1, lt);
+                if (e.x == 0) e = long_decode_entry<KD>(b0, KD + 1, lt);
                 put4(qb, qb_end, dummy, e);
                 consume(b0, b1, b2, e.x);
                 return e;
@@ -354,8 +385,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
                 uint2 ea = s_dec[a0 >> (32 - KD)];
                 uint2 eb = s_dec[b0 >> (32 - KD)];
                 if ((ea.x == 0) | (eb.x == 0)) {
-                    if (ea.x == 0) ea = long_decode_entry(a0, KD + 1, lt);
-                    if (eb.x == 0) eb = long_decode_entry(b0, KD + 1, lt);
+                    if (ea.x == 0) ea = long_decode_entry<KD>(a0, KD + 1, lt);
+                    if (eb.x == 0) eb = long_decode_entry<KD>(b0, KD + 1, lt);
                 }
                 put4(qa, qa_end, dummy, ea);
                 put4(qb, qb_end, dummy, eb);
@@ -381,8 +412,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
                 uint2 ea = s_dec[a0 >> (32 - KD)];
                 uint2 eb = s_dec[b0 >> (32 - KD)];
                 if ((ea.x == 0) | (eb.x == 0)) {
-                    if (ea.x == 0) ea = long_decode_entry(a0, KD + 1, lt);
-                    if (eb.x == 0) eb = long_decode_entry(b0, KD + 1, lt);
+                    if (ea.x == 0) ea = long_decode_entry<KD>(a0, KD + 1, lt);
+                    if (eb.x == 0) eb = long_decode_entry<KD>(b0, KD + 1, lt);
                 }
                 put4(qa, qa_end, dummy, ea);
                 put4(qb, qb_end, dummy, eb);
@@ -545,6 +576,26 @@ __global__ __launch_bounds__(1024) void build_tables_kernel(CodeLens lens, uint3
         tail[96 + tid] = (uint32_t)sorted[4 * tid] | ((uint32_t)sorted[4 * tid + 1] << 8) |
                          ((uint32_t)sorted[4 * tid + 2] << 16) | ((uint32_t)sorted[4 * tid + 3] << 24);
     }
+    // second level for codes longer than KD: the KD-bit windows >= F hold a
+    // longer first codeword, F = (first code of length KD + 1) / 2
+    const uint32_t F = first[KD + 1] >> 1;
+    const uint32_t np = F < (1u << KD) ? min((1u << KD) - F, kL2Prefixes) : 0u;
+    if (tid < 4) tail[160 + tid] = tid == 0 ? F : (tid == 1 ? np : 0u);
+    uint16_t* l2 = reinterpret_cast<uint16_t*>(tail + kLongWords);
+    for (uint32_t w = tid; w < (kL2Prefixes << kL2Bits); w += blockDim.x) {
+        uint32_t e = 0;
+        if (w < (np << kL2Bits)) {
+            const uint32_t win = (F << kL2Bits) + w;   // a (KD + kL2Bits)-bit window
+            for (uint32_t L = KD + 1; L <= KD + kL2Bits; ++L) {
+                const uint32_t off = (win >> (KD + kL2Bits - L)) - first[L];
+                if (off < count[L]) {
+                    e = (L << 8) | sorted[(base[L] + off) & 255u];
+                    break;
+                }
+            }
+        }
+        l2[w] = (uint16_t)e;
+    }
 }
 
 template <int KC, int KD>
@@ -577,13 +628,19 @@ auto dispatch(uint32_t kc, uint32_t kd, F&& f) {
 
 }  // namespace
 
-uint32_t decode_lds_bytes(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes) {
-    return table_words(count_bits, decode_bits) * 4u + kWaves * 4u + 4u * kDecodeThreads + ebuf_bytes;
+uint32_t decode_dyn_lds_bytes(uint32_t ebuf_bytes, uint32_t l2_cap) {
+    return ebuf_bytes + (l2_cap << kL2Bits) * 2u;
 }
 
-int decode_blocks_per_cu(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes) {
+uint32_t decode_lds_bytes(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes, uint32_t l2_cap) {
+    return ((1u << count_bits) + (2u << decode_bits) + kLongWords) * 4u + kWaves * 4u + 4u * kDecodeThreads +
+           decode_dyn_lds_bytes(ebuf_bytes, l2_cap);
+}
+
+int decode_blocks_per_cu(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes, uint32_t l2_cap) {
     if (!supported_table_bits(count_bits, decode_bits)) return 0;
-    return dispatch(count_bits, decode_bits, [&](auto v) { return decltype(v)::blocks_per_cu(ebuf_bytes); });
+    const uint32_t dyn = decode_dyn_lds_bytes(ebuf_bytes, l2_cap);
+    return dispatch(count_bits, decode_bits, [&](auto v) { return decltype(v)::blocks_per_cu(dyn); });
 }
 
 hipError_t launch_build_tables(const CodeLens& lens, uint32_t count_bits, uint32_t decode_bits, uint32_t* d_tables,
@@ -593,10 +650,10 @@ hipError_t launch_build_tables(const CodeLens& lens, uint32_t count_bits, uint32
 }
 
 hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t decode_bits, uint32_t grid,
-                         uint32_t ebuf_bytes, hipStream_t stream) {
-    if (!supported_table_bits(count_bits, decode_bits)) return hipErrorInvalidValue;
-    return dispatch(count_bits, decode_bits,
-                    [&](auto v) { return decltype(v)::launch(p, grid, ebuf_bytes, stream); });
+                         hipStream_t stream) {
+    if (!supported_table_bits(count_bits, decode_bits) || p.l2_cap > kL2Prefixes) return hipErrorInvalidValue;
+    const uint32_t dyn = decode_dyn_lds_bytes(p.ebuf_bytes, p.l2_cap);
+    return dispatch(count_bits, decode_bits, [&](auto v) { return decltype(v)::launch(p, grid, dyn, stream); });
 }
 
 }  // namespace wc

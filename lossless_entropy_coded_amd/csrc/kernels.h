@@ -32,12 +32,21 @@ constexpr uint32_t kMergeAlign = 64;       // a unit's merge range starts at a m
 //                            word 0 is 0 when the first codeword is longer than KD bits;
 //   then 32 words count[L], 32 words first[L] (canonical first code of length L),
 //   32 words base[L] (rank of the first symbol of length L), 64 words holding the
-//   256 symbols sorted by (length, symbol) -- used for codes longer than the index.
+//   256 symbols sorted by (length, symbol) -- used for codes longer than the index;
+//   then F (the KD-bit prefix of the first code longer than KD), np (the number of
+//   long-code prefixes the second level covers, at most kL2Prefixes) and two zero
+//   words; then the second level: kL2Prefixes * 2^kL2Bits u16 entries, entry
+//   (p - F) * 2^kL2Bits + b for the (KD + kL2Bits)-bit window (p, b) holding
+//   (length << 8) | rotated symbol of its first codeword, or 0 when that code is
+//   longer than KD + kL2Bits bits.
 // Symbols in the multi-codeword and sorted tables are stored rotated right by one
 // bit, e' = (e >> 1) | (e & 1) << 7: e' & 0x7F is the exponent's part of the bf16
 // high byte and e' & 0x80 its part of the low byte.
+constexpr uint32_t kLongWords = 164;       // count, first, base, sorted symbols, then F, np, 0, 0
+constexpr uint32_t kL2Bits = 8;            // second-level index: bits after the KD-bit prefix
+constexpr uint32_t kL2Prefixes = 3;        // long-code prefixes the second level covers
 inline uint32_t table_words(uint32_t count_bits, uint32_t decode_bits) {
-    return (1u << count_bits) + (2u << decode_bits) + 160u;
+    return (1u << count_bits) + (2u << decode_bits) + kLongWords + (kL2Prefixes << kL2Bits) / 2;
 }
 inline bool supported_table_bits(uint32_t count_bits, uint32_t decode_bits) {
     return (count_bits == 12 && (decode_bits == 11 || decode_bits == 10)) ||
@@ -63,20 +72,25 @@ struct DecodeParams {
     uint64_t n_blocks;       // workgroup-sized units: ceil(n_groups / kGroupsPerBlock)
     uint32_t ebuf_bytes;
     uint32_t pad;
+    uint32_t l2_cap;         // long-code prefixes staged in LDS (0 .. kL2Prefixes)
+    uint32_t pad2;
 };
 
-// LDS bytes of one decode workgroup: static tables plus the dynamic staging buffer.
-uint32_t decode_lds_bytes(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes);
+// LDS bytes of one decode workgroup: static tables plus the dynamic part (the
+// unit's exponent staging and l2_cap second-level prefixes).
+uint32_t decode_dyn_lds_bytes(uint32_t ebuf_bytes, uint32_t l2_cap);
+uint32_t decode_lds_bytes(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes, uint32_t l2_cap);
 
-// Resident decode workgroups per compute unit for that staging size (0 on error).
-int decode_blocks_per_cu(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes);
+// Resident decode workgroups per compute unit by the runtime's estimate (0 on error).
+int decode_blocks_per_cu(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes, uint32_t l2_cap);
 
 // Build the decode tables of `lens` into d_tables (table_words(...) words) on `stream`.
 hipError_t launch_build_tables(const CodeLens& lens, uint32_t count_bits, uint32_t decode_bits, uint32_t* d_tables,
                                hipStream_t stream);
 
-// One launch decoding every group of a container.
+// One launch decoding every group of a container (p.ebuf_bytes and p.l2_cap set
+// the dynamic LDS).
 hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t decode_bits, uint32_t grid,
-                         uint32_t ebuf_bytes, hipStream_t stream);
+                         hipStream_t stream);
 
 }  // namespace wc

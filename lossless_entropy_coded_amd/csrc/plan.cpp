@@ -28,10 +28,11 @@ struct wc_plan_s {
     uint64_t max_unit_elems = 0;    // elements of kGroupsPerBlock adjacent groups (one workgroup unit)
     uint64_t n_blocks = 0;          // workgroup units
     uint32_t count_bits = 11;    // index width of the codeword-start table
-    uint32_t decode_bits = 10;   // index width of the multi-codeword table
+    uint32_t decode_bits = 11;   // index width of the multi-codeword table
     uint32_t grid = 0;
     uint32_t lds_bytes = 0;
     uint32_t ebuf_bytes = 0;
+    uint32_t l2_cap = 0;         // long-code prefixes whose second-level entries are staged in LDS
     uint32_t* d_tables = nullptr;
 };
 
@@ -181,10 +182,10 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
     }
     p->device = hip_device;
     p->count_bits = env_u32("WC_COUNT_BITS", 11);
-    p->decode_bits = env_u32("WC_DECODE_BITS", 10);
+    p->decode_bits = env_u32("WC_DECODE_BITS", 11);
     if (!wc::supported_table_bits(p->count_bits, p->decode_bits)) {
         p->count_bits = 11;
-        p->decode_bits = 10;
+        p->decode_bits = 11;
     }
     // workgroup units: kGroupsPerBlock adjacent groups, one contiguous output range
     {
@@ -204,7 +205,25 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
     // write kEbufSlack bytes past the end, and the merge reads whole blocks
     p->ebuf_bytes = (uint32_t)wc::round_up(
         p->max_unit_elems + (wc::kMergeAlign - 1) + (wc::kMergeElems - 1) + wc::kEbufSlack, 16);
-    p->lds_bytes = wc::decode_lds_bytes(p->count_bits, p->decode_bits, p->ebuf_bytes);
+    // Long codes: canonical codes longer than the decode-table index all have
+    // index-bit prefixes >= F = (first code of length decode_bits + 1) / 2; the
+    // second-level table is staged for min(2^decode_bits - F, kL2Prefixes) of them.
+    {
+        const uint8_t* len = blob_host + p->h.off_code_len;
+        uint64_t count[33] = {0};
+        for (int sym = 0; sym < 256; ++sym)
+            if (len[sym] >= 1 && len[sym] <= 32) ++count[len[sym]];
+        uint64_t code = 0;
+        uint64_t first_next = 0;   // first code of length decode_bits + 1
+        for (uint32_t L = 1; L <= p->decode_bits + 1; ++L) {
+            code = (code + (L > 1 ? count[L - 1] : 0)) << 1;
+            if (L == p->decode_bits + 1) first_next = code;
+        }
+        const uint64_t F = first_next >> 1;
+        const uint64_t span = 1ull << p->decode_bits;
+        p->l2_cap = F < span ? (uint32_t)std::min<uint64_t>(span - F, wc::kL2Prefixes) : 0u;
+    }
+    p->lds_bytes = wc::decode_lds_bytes(p->count_bits, p->decode_bits, p->ebuf_bytes, p->l2_cap);
 
     DeviceGuard guard(hip_device);
     if (!guard.ok) {
@@ -216,7 +235,20 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         delete p;
         return WC_ERR_HIP;
     }
-    int per_cu = wc::decode_blocks_per_cu(p->count_bits, p->decode_bits, p->ebuf_bytes);
+    int per_cu = wc::decode_blocks_per_cu(p->count_bits, p->decode_bits, p->ebuf_bytes, p->l2_cap);
+    // The persistent grid must be co-resident.  LDS is handed out in granules of
+    // 1/128 of a compute unit's LDS (1,280 bytes of 160 KiB on gfx950), which the
+    // runtime's occupancy estimate does not round for: count the granules.
+    {
+        int lds_cu = 0;
+        if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, hip_device) !=
+                hipSuccess ||
+            lds_cu <= 0)
+            lds_cu = 160 * 1024;
+        const uint32_t granule = std::max<uint32_t>(1, (uint32_t)lds_cu / 128);
+        const uint32_t granules = (uint32_t)wc::div_up(p->lds_bytes, granule);
+        per_cu = std::min<int>(per_cu, (int)(128 / std::max<uint32_t>(granules, 1)));
+    }
     if (per_cu <= 0) {
         delete p;
         return WC_ERR_UNSUPPORTED;
@@ -290,8 +322,9 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
     d.n_blocks = p->n_blocks;
     d.ebuf_bytes = p->ebuf_bytes;
     d.pad = 0;
-    hipError_t e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->grid, p->ebuf_bytes,
-                                     static_cast<hipStream_t>(stream));
+    d.l2_cap = p->l2_cap;
+    d.pad2 = 0;
+    hipError_t e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
 }
 

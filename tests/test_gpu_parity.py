@@ -100,6 +100,40 @@ def test_long_codes_and_chunk_boundaries(wc, oracle_lib, prefix):
         assert np.array_equal(gpu_decode(wc, blob), w)
 
 
+def _many_rare_exponents(n=400_000, n_rare=200, seed=7):
+    """Eight exponents with counts n/2, n/4, ..., n/256 take code lengths 1..8;
+    200 rare exponents share the remaining 1/256 of the elements, so their
+    codes are about 15-16 bits long and spread over several 10- and 11-bit
+    code prefixes (more than a second-level table of three prefixes covers)."""
+    rng = np.random.default_rng(seed)
+    head = [120, 119, 121, 118, 122, 117, 123, 116]
+    rare = np.array([e for e in range(256) if e not in head][:n_rare], np.uint16)
+    parts = []
+    left = n
+    for i, e in enumerate(head):
+        k = n >> (i + 1)
+        parts.append(np.full(k, e, np.uint16))
+        left -= k
+    parts.append(rare[np.arange(left) % n_rare])
+    exps = rng.permutation(np.concatenate(parts))
+    sm = rng.integers(0, 256, n).astype(np.uint16)
+    return (((sm & 0x80) << 8) | (exps << 7) | (sm & 0x7F)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("bits", [(12, 11), (12, 10), (11, 11), (11, 10), (10, 10)])
+def test_many_long_code_prefixes(wc, oracle_lib, env_knob, bits):
+    """Long codes of many distinct prefixes, at every table width: some resolve
+    in one second-level lookup, others need the length-by-length search."""
+    w = _many_rare_exponents()
+    blob = wc.encode_host([w])
+    env_knob("WC_COUNT_BITS", bits[0])
+    env_knob("WC_DECODE_BITS", bits[1])
+    log(f"case: many rare exponents n={w.size} table bits={bits}")
+    with wc.Plan(blob) as plan:
+        assert (plan.stats()["count_bits"], plan.stats()["decode_bits"]) == bits
+        assert np.array_equal(gpu_decode(wc, blob, plan=plan), w)
+
+
 @pytest.mark.parametrize("bits", [(12, 11), (12, 10), (11, 11), (11, 10), (10, 10)])
 @pytest.mark.parametrize("grid", [1, 7, 0])
 def test_table_width_and_grid_invariance(wc, env_knob, bits, grid):
