@@ -16,23 +16,33 @@
  *   memory (point (i)) and a two-phase count / scan / decode scheme driven by
  *   small per-chunk and per-group auxiliary variables (point (ii)).
  *
- * Container v1 (all fields little-endian; every section 256-byte aligned):
- *   header (256 B): "WCBF", u16 version=1, u16 flags=0, u8 max_code_len,
- *     u8 chunk_bits=64, u16 0, u32 chunks_per_group, u32 n_tensors, u32 0,
- *     u64 n_elems, u64 stream_bits, u64 n_chunks, u64 n_groups,
- *     u64 offsets of code_len / tensors / group_start / gap / stream,
- *     u64 stream_bytes, u64 offset of sm, u64 total_bytes; rest zero.
+ * Container v2 (all fields little-endian; every section 256-byte aligned):
+ *   header (256 B): "WCBF", u16 version=2, u16 flags=0, u8 max_code_len,
+ *     u8 chunk_bits=64, u16 0, u32 chunks_per_group G, u32 n_tensors,
+ *     u32 group_align A, u64 n_elems, u64 stream_bits, u64 n_chunks,
+ *     u64 n_groups, u64 offsets of code_len / tensors / groups / gap / stream,
+ *     u64 stream_bytes, u64 offset of sm, u64 total_bytes, u32 group_max_elems M;
+ *     rest zero.
  *   code_len    u8[256]   canonical Huffman code length per exponent value
  *                         (0 = absent), at most max_code_len (<= 24);
  *   tensors     {u64 elem_offset, u64 numel}[n_tensors], a partition of
  *                         [0, n_elems) in order;
- *   group_start u64[n_groups+1]: index of the first element whose codeword
- *                         starts at or after bit 64*G*g; last entry n_elems;
+ *   groups      {u64 first_elem, u64 first_bit}[n_groups+1]: the elements are
+ *                         cut into blocks of A (the last may be shorter); a
+ *                         group is a run of whole blocks, as long as possible
+ *                         while its codewords touch at most G 64-bit chunks
+ *                         and it holds at most M elements (and at least one
+ *                         block); first_bit is the stream
+ *                         bit where the codeword of first_elem starts; the
+ *                         last entry is {n_elems, stream_bits};
  *   gap         u8[n_chunks]: bit offset, inside 64-bit chunk c, of the first
  *                         codeword starting at or after bit 64c (or of the
  *                         stream end);
  *   stream      exponent codes, MSB-first, n_chunks*8 + 16 bytes, zero padded;
  *   sm          u8[n_elems]: sign bit << 7 | 7 mantissa bits.
+ * Each group is one independent unit of GPU work: its output starts at a
+ * multiple of A elements, so with A = 128 every 128-byte line of the bf16
+ * output and of the sm plane belongs to one group.
  *
  * Status codes: 0 on success, a negative WC_ERR_* value otherwise.  No C++
  * exception ever crosses this interface.
@@ -58,7 +68,8 @@ extern "C" {
 #define WC_ERR_CODE_LENGTHS     -13  /* a code length > max_code_len, or no symbols for n > 0 */
 #define WC_ERR_KRAFT            -14  /* code lengths do not form a complete prefix code       */
 #define WC_ERR_GAP              -15  /* a per-chunk gap is out of range                        */
-#define WC_ERR_GROUP_START      -16  /* group starts not monotone, too far apart, or != n     */
+#define WC_ERR_GROUP_START      -16  /* group table not increasing, misaligned, too wide, or  */
+                                     /* not ending at {n_elems, stream_bits}                  */
 #define WC_ERR_STREAM_BITS      -17  /* stream_bits / n_chunks / n_groups / stream_bytes wrong */
 #define WC_ERR_TENSOR_TABLE     -18  /* tensor table is not an in-order partition of [0, n)   */
 
@@ -66,9 +77,15 @@ extern "C" {
 typedef struct {
     uint32_t max_code_len;      /* 1..24; 0 selects the default 24                      */
     uint32_t chunk_bytes;       /* must be 8 (or 0 for the default)                     */
-    uint32_t chunks_per_group;  /* G >= 1; 0 selects the default 256.  The GPU decoder  */
-                                /* of this build accepts only G = 256.                  */
+    uint32_t chunks_per_group;  /* G >= 1; 0 selects the default 128.  The GPU decoder  */
+                                /* of this build accepts only G = 128.                  */
     uint32_t n_threads;         /* host threads for encoding; 0 = all hardware threads  */
+    uint32_t group_align;       /* A >= 1 elements per block; 0 selects the default 128. */
+                                /* A * max_code_len + 63 must not exceed 64 * G.  The   */
+                                /* GPU decoder accepts multiples of 8.                  */
+    uint32_t group_max_elems;   /* M, a multiple of A: elements per group at most; 0    */
+                                /* selects the default 4096, the most the GPU decoder   */
+                                /* accepts.                                             */
 } wc_encode_opts;
 
 /*

@@ -41,12 +41,16 @@ namespace wc {
 namespace {
 
 constexpr uint32_t kCodeLimit = 24;
-constexpr uint32_t kWaves = kDecodeThreads / 64;
-constexpr uint32_t kUnitChunks = kDecodeThreads * kChunksPerLane;   // chunks per workgroup unit
 // bf16 output is written with non-temporal 16-byte stores: it is not read
 // again by this kernel and streams past the caches
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-constexpr uint32_t kPrefetchBlocks = 8;                            // merge blocks per lane loaded ahead
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 8-byte non-temporal load (data read once by this kernel)
+__device__ __forceinline__ uint2 load_nt8(const uint8_t* q) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(q));
+    return make_uint2(v.x, v.y);
+}
 
 struct LongTables {
     const uint32_t* count;
@@ -99,6 +103,14 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
     return x;
 }
 
+// Order this wave's LDS accesses across the point for the compiler; the LDS
+// itself executes one wave's accesses in issue order, so lanes then see each
+// other's earlier writes without a workgroup barrier.
+__device__ __forceinline__ void wave_lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 __device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
 __device__ __forceinline__ uint64_t uniform64(uint64_t v) {
@@ -119,79 +131,119 @@ __device__ __forceinline__ void join4(uint32_t s, uint32_t e, uint32_t& lo, uint
     hi = __builtin_amdgcn_perm(highs, lows, 0x07030602u);
 }
 
-// Raw loads for one lane of one unit: 20 stream bytes covering its two chunks
-// plus the halo, both gaps, and the unit's output range.
-struct Raw {
-    uint4 d;        // stream bytes [8a, 8a + 16)
-    uint32_t d4;    // stream bytes [8a + 16, 8a + 20)
-    uint32_t gaps;  // gap[a] | gap[a + 1] << 8 (the second byte is not used when a + 1 is past the end)
-    uint64_t A;     // first element of the unit
-    uint32_t B;     // low 32 bits of its end (B - A < 2^32: a unit holds at most 2^15 codewords)
+// One group's entry pair in the group table (the same for every lane): its
+// first element and first bit, and those of the next group.
+struct Meta {
+    uint64_t e0, p0, e1, p1;
 };
 
-__device__ __forceinline__ Raw load_raw(const DecodeParams& p, uint64_t u, uint32_t tid) {
+__device__ __forceinline__ Meta load_meta(const DecodeParams& p, uint64_t u) {
+    const uint4 x = *reinterpret_cast<const uint4*>(p.groups + 2 * u);
+    const uint4 y = *reinterpret_cast<const uint4*>(p.groups + 2 * u + 2);
+    Meta m;
+    m.e0 = ((uint64_t)x.y << 32) | x.x;
+    m.p0 = ((uint64_t)x.w << 32) | x.z;
+    m.e1 = ((uint64_t)y.y << 32) | y.x;
+    m.p1 = ((uint64_t)y.w << 32) | y.z;
+    return m;
+}
+
+__device__ __forceinline__ Meta uniform_meta(const Meta& m) {
+    Meta r;
+    r.e0 = uniform64(m.e0);
+    r.p0 = uniform64(m.p0);
+    r.e1 = uniform64(m.e1);
+    r.p1 = uniform64(m.p1);
+    return r;
+}
+
+// Raw loads of one lane for one group: the stream bytes of its two chunks
+// a = c0 + 2t and a + 1 plus the lookahead of the second (20 bytes from 8a),
+// and both gaps.  The group's chunks c0 .. c1 (c0 = p0 / 64, c1 = (p1 - 1) /
+// 64) start at any chunk, so the 20 bytes are taken from two aligned 16-byte
+// loads at 8 * (a rounded down to even) (of 16 and 12 bytes); the parity of a
+// is that of c0, the same for every lane.  Both loads stay inside the
+// container: they end at most 4 bytes past the stream section, which is
+// followed by the sm section.  Every loaded word is used: a load whose
+// register is partly dead lets that register be reused while the load is in
+// flight, which costs a wait for it.
+struct Raw {
+    uint4 q0;
+    uint3 q1;
+    uint32_t ga, gb;
+};
+
+__device__ __forceinline__ Raw load_raw(const DecodeParams& p, const Meta& m, uint32_t lane) {
     Raw r;
-    const uint64_t a = u * kUnitChunks + kChunksPerLane * tid;
-    r.d = make_uint4(0, 0, 0, 0);
-    r.d4 = 0;
-    r.gaps = 0;
-    if (a < p.n_chunks) {
-        // a is even: the stream load is 16-byte aligned and the gap pair 2-byte
-        // aligned; gap[a + 1] lies inside the container even when a + 1 ==
-        // n_chunks (the next section follows), and is then ignored.
-        r.d = *reinterpret_cast<const uint4*>(p.stream + 8 * a);
-        r.d4 = *reinterpret_cast<const uint32_t*>(p.stream + 8 * a + 16);
-        r.gaps = *reinterpret_cast<const uint16_t*>(p.gap + a);
+    const uint64_t a = (m.p0 >> 6) + kChunksPerLane * lane;
+    const uint64_t c1 = (m.p1 - 1) >> 6;
+    r.q0 = make_uint4(0, 0, 0, 0);
+    r.q1 = make_uint3(0, 0, 0);
+    r.ga = r.gb = 0;
+    if (a <= c1) {
+        const uint8_t* q = p.stream + 8 * (a & ~(uint64_t)1);
+        r.q0 = *reinterpret_cast<const uint4*>(q);
+        r.q1 = *reinterpret_cast<const uint3*>(q + 16);
+        r.ga = p.gap[a];
+        r.gb = p.gap[a + 1];   // gap[n_chunks] lies in the padding after the gap section
     }
-    const uint64_t g0 = u * kGroupsPerBlock;
-    const uint64_t g1 = min_u64(g0 + kGroupsPerBlock, p.n_groups);
-    const uint2 x = *reinterpret_cast<const uint2*>(p.group_start + g0);
-    r.A = ((uint64_t)x.y << 32) | x.x;
-    r.B = *reinterpret_cast<const uint32_t*>(p.group_start + g1);   // little-endian low word
     return r;
 }
 
 // A chain ready for decoding: 96 stream bits MSB-first, shifted so that the
-// first codeword starting in the chunk is at the top; `bits` counts the bits
-// after that point in which further codewords may start.
+// first codeword it owns is at the top; `bits` counts the bits after that
+// point in which further codewords it owns may start.
 struct Chain {
     uint32_t w0, w1, w2;
     int32_t bits;
 };
 
-__device__ __forceinline__ Chain make_chain(const DecodeParams& p, uint64_t c, uint32_t d0, uint32_t d1, uint32_t d2,
-                                            uint32_t gap) {
+// Chain of chunk c of a group whose codewords start in [p0, p1): it owns the
+// codewords starting in [max(64c, p0), min(64(c + 1), p1)).  gap is gap[c];
+// the group's first chunk starts at p0 instead.  A chunk past the group owns
+// nothing.
+__device__ __forceinline__ Chain make_chain(uint64_t c, uint64_t p0, uint64_t p1, uint32_t d0, uint32_t d1,
+                                            uint32_t d2, uint32_t gap) {
     Chain h;
     const uint32_t w0 = __builtin_bswap32(d0), w1 = __builtin_bswap32(d1), w2 = __builtin_bswap32(d2);
-    uint32_t end = 0;
-    if (c < p.n_chunks) {
-        const uint64_t left = p.stream_bits - 64 * c;
-        end = left < 64 ? (uint32_t)left : 64u;
+    const uint64_t lo = 64 * c, hi = lo + 64;
+    int32_t end = 0;
+    if (lo < p1) {
+        if (lo <= p0) gap = (uint32_t)(p0 - lo);
+        end = (int32_t)((hi < p1 ? hi : p1) - lo);
     } else {
         gap = 0;
     }
-    const uint64_t h01 = ((uint64_t)w0 << 32 | w1) << gap;
-    const uint64_t h12 = ((uint64_t)w1 << 32 | w2) << gap;
+    // shift the 96 bits left by gap (0..63): whole words first, then the rest
+    const bool far = gap >= 32;
+    const uint32_t x0 = far ? w1 : w0, x1 = far ? w2 : w1, x2 = far ? 0u : w2;
+    const uint32_t sh = gap & 31u;
+    const uint64_t h01 = ((uint64_t)x0 << 32 | x1) << sh;
+    const uint64_t h12 = ((uint64_t)x1 << 32 | x2) << sh;
     h.w0 = (uint32_t)(h01 >> 32);
     h.w1 = (uint32_t)(h12 >> 32);
-    h.w2 = w2 << gap;
-    h.bits = (int32_t)end - (int32_t)gap;
+    h.w2 = x2 << sh;
+    h.bits = end - (int32_t)gap;
     return h;
 }
 
 struct Unit {
     Chain a, b;
-    uint64_t A;
-    uint32_t B;
+    uint64_t A;    // first element of the group
+    uint32_t n;    // its elements (at most kGroupMaxElems)
 };
 
-__device__ __forceinline__ Unit make_unit(const DecodeParams& p, const Raw& r, uint64_t u, uint32_t tid) {
+__device__ __forceinline__ Unit make_unit(const Raw& r, const Meta& m, uint32_t lane) {
     Unit x;
-    const uint64_t c = u * kUnitChunks + kChunksPerLane * tid;
-    x.a = make_chain(p, c, r.d.x, r.d.y, r.d.z, r.gaps & 0xFFu);
-    x.b = make_chain(p, c + 1, r.d.z, r.d.w, r.d4, (r.gaps >> 8) & 0xFFu);
-    x.A = uniform64(r.A);
-    x.B = __builtin_amdgcn_readfirstlane(r.B);
+    const bool odd = (m.p0 >> 6) & 1;
+    const uint32_t d0 = odd ? r.q0.z : r.q0.x, d1 = odd ? r.q0.w : r.q0.y;
+    const uint32_t d2 = odd ? r.q1.x : r.q0.z, d3 = odd ? r.q1.y : r.q0.w;
+    const uint32_t d4 = odd ? r.q1.z : r.q1.x;
+    const uint64_t c = (m.p0 >> 6) + kChunksPerLane * lane;
+    x.a = make_chain(c, m.p0, m.p1, d0, d1, d2, r.ga);
+    x.b = make_chain(c + 1, m.p0, m.p1, d2, d3, d4, r.gb);
+    x.A = m.e0;
+    x.n = (uint32_t)min_u64(m.e1 - m.e0, kGroupMaxElems);   // kept 64-bit: every loaded word is used
     return x;
 }
 
@@ -243,35 +295,36 @@ __device__ __forceinline__ void put4(uint8_t*& q, const uint8_t* q_end, uint8_t*
     q += (e.x >> 8) & 0xFFu;
 }
 
-template <int KC, int KD>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) {
+template <int KC, int KD, int W>
+__global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) {
+    constexpr uint32_t kThreads = kWaveLanes * W;
     __shared__ __attribute__((aligned(16))) uint32_t s_cnt[1u << KC];
     __shared__ __attribute__((aligned(16))) uint2 s_dec[1u << KD];
     __shared__ __attribute__((aligned(16))) uint32_t s_long[kLongWords];
-    __shared__ uint32_t s_wave[kWaves];
-    __shared__ __attribute__((aligned(16))) uint8_t s_dummy[4 * kDecodeThreads];
-    // dynamic: the unit's exponent staging (ebuf_bytes), then the second-level
-    // table for the long-code prefixes this container has (l2_cap * 2^kL2Bits u16)
-    extern __shared__ __attribute__((aligned(16))) uint8_t ebuf[];
-    uint16_t* const s_l2 = reinterpret_cast<uint16_t*>(ebuf + p.ebuf_bytes);
+    __shared__ __attribute__((aligned(16))) uint8_t s_dummy[4 * kThreads];
+    // dynamic: W exponent staging buffers of ebuf_bytes (one per wave), then the
+    // second-level table for the long-code prefixes of this container
+    // (l2_cap * 2^kL2Bits u16)
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+    uint16_t* const s_l2 = reinterpret_cast<uint16_t*>(dyn + W * p.ebuf_bytes);
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & 63u;
-    const uint32_t wave = tid >> 6;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     uint8_t* const dummy = s_dummy + 4 * tid;
+    uint8_t* const ebuf = dyn + wave * p.ebuf_bytes;
 
-    // stage the decode tables (built once per container) into LDS
+    // stage the decode tables (built once per container) into LDS; this is the
+    // only point where the waves of a workgroup wait for each other
     {
         const uint4* src = reinterpret_cast<const uint4*>(p.tables);
-        for (uint32_t i = tid; i < (1u << KC) / 4; i += kDecodeThreads)
-            reinterpret_cast<uint4*>(s_cnt)[i] = src[i];
+        for (uint32_t i = tid; i < (1u << KC) / 4; i += kThreads) reinterpret_cast<uint4*>(s_cnt)[i] = src[i];
         src += (1u << KC) / 4;
-        for (uint32_t i = tid; i < (2u << KD) / 4; i += kDecodeThreads)
-            reinterpret_cast<uint4*>(s_dec)[i] = src[i];
+        for (uint32_t i = tid; i < (2u << KD) / 4; i += kThreads) reinterpret_cast<uint4*>(s_dec)[i] = src[i];
         src += (2u << KD) / 4;
         if (tid < kLongWords / 4) reinterpret_cast<uint4*>(s_long)[tid] = src[tid];
         src += kLongWords / 4;
-        for (uint32_t i = tid; i < (p.l2_cap << kL2Bits) / 8; i += kDecodeThreads)
+        for (uint32_t i = tid; i < (p.l2_cap << kL2Bits) / 8; i += kThreads)
             reinterpret_cast<uint4*>(s_l2)[i] = src[i];
     }
     __syncthreads();
@@ -284,39 +337,52 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
     lt.l2_first = __builtin_amdgcn_readfirstlane(s_long[160]);
     lt.l2_n = min(__builtin_amdgcn_readfirstlane(s_long[161]), p.l2_cap);
 
-    uint64_t u = blockIdx.x;
-    if (u >= p.n_blocks) return;
-    Unit cur = make_unit(p, load_raw(p, u, tid), u, tid);
+    // Wave w of workgroup b takes groups b*W + w, then every (grid * W)-th
+    // one after it: the groups in flight at any time form one contiguous
+    // stretch of the stream and of the output, and neighbouring groups run in
+    // the same workgroup.
+    //
+    // Pipeline of one wave, per group u: at the top, the stream and gap loads
+    // of the next group (its table entries arrived one iteration earlier),
+    // the sm loads of u and the table entries of the group after next are
+    // issued; the phases run on u from LDS only; then the next group's loads
+    // are consumed, and u is merged with eight fixed store steps.  Every
+    // iteration issues the same vector memory instructions, so each wait
+    // covers exactly the loads it needs.
+    const uint64_t stride = (uint64_t)gridDim.x * W;
+    uint64_t u = (uint64_t)blockIdx.x * W + wave;
+    if (u >= p.n_units) return;
+    const uint64_t last_u = p.n_units - 1;
+    Meta m_next;
+    Unit cur;
+    {
+        const Meta m = uniform_meta(load_meta(p, u));
+        const Raw r = load_raw(p, m, lane);
+        m_next = load_meta(p, min_u64(u + stride, last_u));
+        cur = make_unit(r, m, lane);
+        m_next = uniform_meta(m_next);
+    }
 
     for (;;) {
-        // Nothing below waits on memory until the next unit's loads are
-        // consumed after phase 2, so the loads issued here stay in flight.
-        // The unit's elements [A, B) are merged in blocks of 8 counted from
-        // A0 = A rounded down to 64, so that the wave-wide accesses cover
-        // whole cache lines; offsets inside the unit fit 32 bits, so every
-        // global access is a uniform base plus a 32-bit lane offset.
+        const uint64_t un = u + stride;
+        const bool more = un < p.n_units;
+        const Raw nxt = load_raw(p, m_next, lane);
+
+        // sign+mantissa bytes of the group (non-temporal: read once); block
+        // indexes past the group are clamped to its last block (a cache hit,
+        // never used).  Every block lies inside round_up(n, 8) <= the
+        // plane's padded size.
         const uint64_t A = cur.A;
-        const uint64_t A0 = A & ~(uint64_t)(kMergeAlign - 1);
-        const uint32_t lo_rel = (uint32_t)(A - A0);
-        const uint32_t hi_rel = cur.B - (uint32_t)A0;
-        const uint32_t nblk = (hi_rel + kMergeElems - 1) / kMergeElems;
-
-        // sign+mantissa bytes of this lane's first merge blocks; block indexes
-        // past the unit are clamped to its last block (an L2 hit, never used).
-        // With nblk >= 1 every block lies inside round_up(n, 8) <= the plane's
-        // padded size; a unit with no block reads the plane's last piece.
-        const uint32_t last_blk = nblk ? nblk - 1 : 0u;
-        const uint8_t* const smu = p.sm + min_u64(A0, p.sm_last);
-        uint16_t* const outu = p.out + A0;
-        uint2 smv[kPrefetchBlocks];
+        const uint32_t n_unit = cur.n;
+        const uint32_t last_blk = (n_unit - 1) / kMergeElems;
+        const uint8_t* const smu = p.sm + A;
+        uint16_t* const outu = p.out + A;
+        uint2 smv[kMergeSteps];
 #pragma unroll
-        for (uint32_t k = 0; k < kPrefetchBlocks; ++k)
-            smv[k] = *reinterpret_cast<const uint2*>(smu + kMergeElems * min(tid + k * kDecodeThreads, last_blk));
+        for (uint32_t k = 0; k < kMergeSteps; ++k)
+            smv[k] = load_nt8(smu + kMergeElems * min(lane + k * kWaveLanes, last_blk));
 
-        const uint64_t un = u + gridDim.x;
-        const bool more = un < p.n_blocks;
-        Raw nxt;
-        if (more) nxt = load_raw(p, un, tid);
+        const Meta m_after = load_meta(p, min_u64(un + stride, last_u));
 
         // phase 1: count the codewords starting in each chunk
         uint32_t ca = 0, cb = 0;
@@ -341,25 +407,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
             }
         }
 
-        // block-wide exclusive scan of the lane counts
+        // wave-wide exclusive scan of the lane counts: each chain's first
+        // output index inside the unit
         const uint32_t count = ca + cb;
-        const uint32_t incl = wave_inclusive_scan(count);
-        if (lane == 63) s_wave[wave] = incl;
-        __syncthreads();
-        uint32_t before = 0;
-#pragma unroll
-        for (uint32_t w = 0; w < kWaves; ++w) before += (w < wave) ? s_wave[w] : 0u;
-        const uint32_t pos_a = before + incl - count;
+        const uint32_t pos_a = wave_inclusive_scan(count) - count;
         const uint32_t pos_b = pos_a + ca;
 
         // phase 2: decode again and stage the exponent bytes; a chain never
-        // writes past the unit's element range, even for a corrupted stream
-        const uint32_t n_unit = hi_rel - lo_rel;
-        const uint32_t base = lo_rel;
+        // writes past the group's element range, even for a corrupted stream
         const uint32_t todo_a = min(ca, pos_a < n_unit ? n_unit - pos_a : 0u);
         const uint32_t todo_b = min(cb, pos_b < n_unit ? n_unit - pos_b : 0u);
-        uint8_t* qa = ebuf + base + pos_a;
-        uint8_t* qb = ebuf + base + pos_b;
+        uint8_t* qa = ebuf + pos_a;
+        uint8_t* qb = ebuf + pos_b;
         uint8_t* const qa_end = qa + todo_a;
         uint8_t* const qb_end = qb + todo_b;
         {
@@ -420,80 +479,71 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
                 consume(a0, a1, a2, ea.x);
                 consume(b0, b1, b2, eb.x);
             }
-            __syncthreads();
-            uint8_t* ha = ebuf + base + pos_a;
-            uint8_t* hb = ebuf + base + pos_b;
+            // The staging belongs to this wave alone, and the LDS executes a
+            // wave's accesses in issue order: once every lane has left the
+            // loop, the head bytes overwrite whatever a left neighbour's last
+            // four-byte store put there.
+            wave_lds_order();
+            uint8_t* ha = ebuf + pos_a;
+            uint8_t* hb = ebuf + pos_b;
 #pragma unroll
             for (uint32_t k = 0; k < kHeadBytes; ++k) {
                 if (todo_a > k) ha[k] = (uint8_t)(head_a >> (8 * k));
                 if (todo_b > k) hb[k] = (uint8_t)(head_b >> (8 * k));
             }
         }
-        // consume the next unit's loads now, before the merge issues its stores
-        Unit next = cur;
-        if (more) next = make_unit(p, nxt, un, tid);
-        __syncthreads();
-
-        // Every prefetched block is consumed here, before any store of this
-        // unit: a load still counted as pending at the next iteration (where
-        // its registers are reloaded) would make that point wait for all
-        // outstanding memory operations, the merge stores included.
+        // consume every load of this iteration now, before the merge issues
+        // its stores: the next group's chains and table entries, and the sm
+        // bytes (a load still pending at the next iteration's top would make
+        // the wait there cover the merge stores as well)
+        const Unit next = make_unit(nxt, m_next, lane);
+        m_next = uniform_meta(m_after);
+        wave_lds_order();
 #pragma unroll
-        for (uint32_t k = 0; k < kPrefetchBlocks; ++k)
+        for (uint32_t k = 0; k < kMergeSteps; ++k)
             asm volatile("" ::"v"(smv[k].x), "v"(smv[k].y));
 
         // merge: 8 elements per lane per step; consecutive lanes take
         // consecutive blocks, so each wave-wide 8-byte load and 16-byte store
-        // covers one contiguous range (whole 64-byte segments)
-        // (whole blocks inside [A, B) only: the block holding A and the one
-        // holding B may be shared with the neighbouring units and are written
-        // element by element below)
-        const uint32_t full_lo = (lo_rel + kMergeElems - 1) / kMergeElems;
-        const uint32_t full_hi = hi_rel / kMergeElems;
-        auto merge_block = [&](uint32_t blk, const uint2& s2) {
-            const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + kMergeElems * blk);
-            uint32_t o0, o1, o2, o3;
-            join4(s2.x, e2.x, o0, o1);
-            join4(s2.y, e2.y, o2, o3);
-            u32x4 v;
-            v.x = o0;
-            v.y = o1;
-            v.z = o2;
-            v.w = o3;
-            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(outu + kMergeElems * blk));
-        };
+        // covers one contiguous range of whole cache lines.  A group holds at
+        // most kMergeSteps blocks per lane.  Only the container's very last
+        // block can be partial; it is written after the loop.
+        const uint32_t full = n_unit / kMergeElems;
 #pragma unroll
-        for (uint32_t k = 0; k < kPrefetchBlocks; ++k) {
-            const uint32_t blk = tid + k * kDecodeThreads;
-            if (blk >= full_lo && blk < full_hi) merge_block(blk, smv[k]);
-        }
-        for (uint32_t blk = tid + kPrefetchBlocks * kDecodeThreads; blk < full_hi; blk += kDecodeThreads)
-            merge_block(blk, *reinterpret_cast<const uint2*>(smu + kMergeElems * blk));
-        // partial edge blocks: lane 0 takes the one holding A, lane 1 the one
-        // holding B unless it is the same block
-        {
-            const uint32_t blk = tid == 0 ? lo_rel / kMergeElems : nblk - 1;
-            const bool partial =
-                tid == 0 ? (lo_rel % kMergeElems) != 0 : (tid == 1 && full_hi < nblk && nblk - 1 >= full_lo);
-            if (partial) {
-                const uint32_t rel = kMergeElems * blk;
-                const uint2 s2 = *reinterpret_cast<const uint2*>(smu + rel);
-                const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + rel);
-                uint32_t o[4];
-                join4(s2.x, e2.x, o[0], o[1]);
-                join4(s2.y, e2.y, o[2], o[3]);
-#pragma unroll
-                for (uint32_t i = 0; i < kMergeElems; ++i) {
-                    const uint32_t idx = rel + i;
-                    if (idx >= lo_rel && idx < hi_rel) outu[idx] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
-                }
+        for (uint32_t k = 0; k < kMergeSteps; ++k) {
+            const uint32_t blk = lane + k * kWaveLanes;
+            if (blk < full) {
+                const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + kMergeElems * blk);
+                uint32_t o0, o1, o2, o3;
+                join4(smv[k].x, e2.x, o0, o1);
+                join4(smv[k].y, e2.y, o2, o3);
+                u32x4 v;
+                v.x = o0;
+                v.y = o1;
+                v.z = o2;
+                v.w = o3;
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(outu + kMergeElems * blk));
             }
         }
 
         if (!more) break;
-        __syncthreads();   // ebuf and s_wave are reused by the next unit
+        wave_lds_order();   // the staging is rewritten by the next group
         u = un;
         cur = next;
+    }
+
+    // the container's last block, when it holds fewer than 8 elements
+    const uint32_t full = cur.n / kMergeElems;
+    if (full * kMergeElems < cur.n && lane == 0) {
+        const uint32_t rel = kMergeElems * full;
+        const uint2 s2 = load_nt8(p.sm + cur.A + rel);
+        const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + rel);
+        uint32_t o[4];
+        join4(s2.x, e2.x, o[0], o[1]);
+        join4(s2.y, e2.y, o[2], o[3]);
+#pragma unroll
+        for (uint32_t i = 0; i < kMergeElems; ++i)
+            if (rel + i < cur.n) p.out[cur.A + rel + i] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
     }
 }
 
@@ -598,15 +648,15 @@ __global__ __launch_bounds__(1024) void build_tables_kernel(CodeLens lens, uint3
     }
 }
 
-template <int KC, int KD>
+template <int KC, int KD, int W>
 struct Variant {
-    static hipError_t launch(const DecodeParams& p, uint32_t grid, uint32_t ebuf, hipStream_t stream) {
-        hipLaunchKernelGGL((decode_kernel<KC, KD>), dim3(grid), dim3(kDecodeThreads), ebuf, stream, p);
+    static hipError_t launch(const DecodeParams& p, uint32_t grid, uint32_t dyn, hipStream_t stream) {
+        hipLaunchKernelGGL((decode_kernel<KC, KD, W>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
         return hipGetLastError();
     }
-    static int blocks_per_cu(uint32_t ebuf) {
+    static int blocks_per_cu(uint32_t dyn) {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<KC, KD>, kDecodeThreads, ebuf) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<KC, KD, W>, kWaveLanes * W, dyn) !=
             hipSuccess)
             return 0;
         return n;
@@ -617,43 +667,53 @@ struct Variant {
     }
 };
 
+template <int W, typename F>
+auto dispatch_bits(uint32_t kc, uint32_t kd, F&& f) {
+    if (kc == 12 && kd == 11) return f(Variant<12, 11, W>{});
+    if (kc == 12 && kd == 10) return f(Variant<12, 10, W>{});
+    if (kc == 11 && kd == 11) return f(Variant<11, 11, W>{});
+    if (kc == 11 && kd == 10) return f(Variant<11, 10, W>{});
+    return f(Variant<10, 10, W>{});
+}
+
 template <typename F>
-auto dispatch(uint32_t kc, uint32_t kd, F&& f) {
-    if (kc == 12 && kd == 11) return f(Variant<12, 11>{});
-    if (kc == 12 && kd == 10) return f(Variant<12, 10>{});
-    if (kc == 11 && kd == 11) return f(Variant<11, 11>{});
-    if (kc == 11 && kd == 10) return f(Variant<11, 10>{});
-    return f(Variant<10, 10>{});
+auto dispatch(uint32_t kc, uint32_t kd, uint32_t waves, F&& f) {
+    if (waves == 4) return dispatch_bits<4>(kc, kd, f);
+    return dispatch_bits<8>(kc, kd, f);
 }
 
 }  // namespace
 
-uint32_t decode_dyn_lds_bytes(uint32_t ebuf_bytes, uint32_t l2_cap) {
-    return ebuf_bytes + (l2_cap << kL2Bits) * 2u;
+uint32_t decode_dyn_lds_bytes(uint32_t waves, uint32_t ebuf_bytes, uint32_t l2_cap) {
+    return waves * ebuf_bytes + (l2_cap << kL2Bits) * 2u;
 }
 
-uint32_t decode_lds_bytes(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes, uint32_t l2_cap) {
-    return ((1u << count_bits) + (2u << decode_bits) + kLongWords) * 4u + kWaves * 4u + 4u * kDecodeThreads +
-           decode_dyn_lds_bytes(ebuf_bytes, l2_cap);
+uint32_t decode_lds_bytes(uint32_t count_bits, uint32_t decode_bits, uint32_t waves, uint32_t ebuf_bytes,
+                          uint32_t l2_cap) {
+    return ((1u << count_bits) + (2u << decode_bits) + kLongWords) * 4u + 4u * kWaveLanes * waves +
+           decode_dyn_lds_bytes(waves, ebuf_bytes, l2_cap);
 }
 
-int decode_blocks_per_cu(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes, uint32_t l2_cap) {
-    if (!supported_table_bits(count_bits, decode_bits)) return 0;
-    const uint32_t dyn = decode_dyn_lds_bytes(ebuf_bytes, l2_cap);
-    return dispatch(count_bits, decode_bits, [&](auto v) { return decltype(v)::blocks_per_cu(dyn); });
+int decode_blocks_per_cu(uint32_t count_bits, uint32_t decode_bits, uint32_t waves, uint32_t ebuf_bytes,
+                         uint32_t l2_cap) {
+    if (!supported_table_bits(count_bits, decode_bits) || !supported_waves(waves)) return 0;
+    const uint32_t dyn = decode_dyn_lds_bytes(waves, ebuf_bytes, l2_cap);
+    return dispatch(count_bits, decode_bits, waves, [&](auto v) { return decltype(v)::blocks_per_cu(dyn); });
 }
 
 hipError_t launch_build_tables(const CodeLens& lens, uint32_t count_bits, uint32_t decode_bits, uint32_t* d_tables,
                                hipStream_t stream) {
     if (!supported_table_bits(count_bits, decode_bits)) return hipErrorInvalidValue;
-    return dispatch(count_bits, decode_bits, [&](auto v) { return decltype(v)::build(lens, d_tables, stream); });
+    return dispatch(count_bits, decode_bits, 8, [&](auto v) { return decltype(v)::build(lens, d_tables, stream); });
 }
 
-hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t decode_bits, uint32_t grid,
-                         hipStream_t stream) {
-    if (!supported_table_bits(count_bits, decode_bits) || p.l2_cap > kL2Prefixes) return hipErrorInvalidValue;
-    const uint32_t dyn = decode_dyn_lds_bytes(p.ebuf_bytes, p.l2_cap);
-    return dispatch(count_bits, decode_bits, [&](auto v) { return decltype(v)::launch(p, grid, dyn, stream); });
+hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t decode_bits, uint32_t waves,
+                         uint32_t grid, hipStream_t stream) {
+    if (!supported_table_bits(count_bits, decode_bits) || !supported_waves(waves) || p.l2_cap > kL2Prefixes)
+        return hipErrorInvalidValue;
+    const uint32_t dyn = decode_dyn_lds_bytes(waves, p.ebuf_bytes, p.l2_cap);
+    return dispatch(count_bits, decode_bits, waves,
+                    [&](auto v) { return decltype(v)::launch(p, grid, dyn, stream); });
 }
 
 }  // namespace wc

@@ -8,10 +8,14 @@
 //   2. histogram the exponents over all tensors of the block (one codebook);
 //   3. optimal code lengths limited to max_code_len (package-merge);
 //   4. canonical codes;
-//   5. pack the codes MSB-first in parallel over element ranges, recording for
-//      every 64-bit chunk the offset of its first codeword and for every group
-//      of G chunks the index of its first element (the auxiliary variables of
-//      the DFloat11 abstract, design point (ii)).
+//   5. cut the elements into groups: runs of whole blocks of `align` elements,
+//      each run as long as its codewords touch at most G 64-bit chunks and it
+//      holds at most `max_elems` elements; every group records its first
+//      element and the stream bit where that element's codeword starts;
+//   6. pack the codes MSB-first in parallel over element ranges, recording for
+//      every 64-bit chunk the offset of its first codeword (with the group
+//      table, the auxiliary variables of the DFloat11 abstract, design point
+//      (ii)).
 #include <algorithm>
 #include <array>
 #include <atomic>
@@ -152,14 +156,22 @@ extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* nu
     *blob = nullptr;
     *blob_bytes = 0;
     if (n_tensors && (!tensors || !numels)) return WC_ERR_INVALID_ARG;
-    uint32_t max_len = kMaxCodeLen, group = kDefaultGroup, nthreads = 0;
+    uint32_t max_len = kMaxCodeLen, group = kDefaultGroup, align = kDefaultAlign, max_elems = kDefaultMaxElems;
+    uint32_t nthreads = 0;
     if (opts) {
         if (opts->max_code_len) max_len = opts->max_code_len;
         if (opts->chunk_bytes && opts->chunk_bytes != 8) return WC_ERR_INVALID_ARG;
         if (opts->chunks_per_group) group = opts->chunks_per_group;
+        if (opts->group_align) align = opts->group_align;
+        if (opts->group_max_elems) max_elems = opts->group_max_elems;
         nthreads = opts->n_threads;
     }
-    if (max_len < 1 || max_len > kMaxCodeLen || group < 1 || group > (1u << 20)) return WC_ERR_INVALID_ARG;
+    if (max_len < 1 || max_len > kMaxCodeLen || group < 1 || group > (1u << 20) || align > (1u << 20) ||
+        max_elems < align || max_elems % align)
+        return WC_ERR_INVALID_ARG;
+    // every block must fit in one group whatever its codes: align codewords of
+    // up to max_len bits, starting anywhere in a chunk, touch at most G chunks
+    if ((uint64_t)align * max_len + (kChunkBits - 1) > (uint64_t)kChunkBits * group) return WC_ERR_INVALID_ARG;
 
     Source src;
     uint64_t n = 0;
@@ -174,8 +186,10 @@ extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* nu
     if (nthreads == 0) nthreads = std::max(1u, std::thread::hardware_concurrency());
     nthreads = (unsigned)std::min<uint64_t>(nthreads, std::max<uint64_t>(1, n / 65536));
     nthreads = std::min(nthreads, 64u);
+    // element ranges of the threads, on block boundaries
+    const uint64_t n_blocks = div_up(n, align);
     std::vector<uint64_t> r0(nthreads + 1);
-    for (unsigned t = 0; t <= nthreads; ++t) r0[t] = n * t / nthreads;
+    for (unsigned t = 0; t <= nthreads; ++t) r0[t] = std::min<uint64_t>(n, n_blocks * t / nthreads * align);
 
     // 1-2. exponent histogram
     std::vector<std::array<uint64_t, 256>> hist_t(nthreads);
@@ -205,7 +219,31 @@ extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* nu
         tbits[t + 1] = tbits[t] + b;
     }
     const uint64_t stream_bits = tbits[nthreads];
-    Header h = layout(n, stream_bits, n_tensors, max_len, group);
+
+    // 5. groups: bit offset of every block, then the longest runs of blocks
+    // whose codewords touch at most G chunks, of at most max_elems elements
+    std::vector<uint64_t> block_bit(n_blocks + 1, 0);
+    parallel_for(nthreads, [&](unsigned t) {
+        uint64_t pos = tbits[t];
+        src.for_range(r0[t], r0[t + 1], [&](uint64_t gi, const uint16_t* p, uint64_t k) {
+            for (uint64_t j = 0; j < k; ++j) {
+                if ((gi + j) % align == 0) block_bit[(gi + j) / align] = pos;
+                pos += len[exponent_of(p[j])];
+            }
+        });
+    });
+    block_bit[n_blocks] = stream_bits;
+    std::vector<uint64_t> g_elem{0}, g_bit{0};
+    for (uint64_t k0 = 0; k0 < n_blocks;) {
+        uint64_t k1 = k0 + 1;
+        const uint64_t k_cap = k0 + max_elems / align;
+        while (k1 < n_blocks && k1 < k_cap && chunk_span(block_bit[k0], block_bit[k1 + 1]) <= group) ++k1;
+        g_elem.push_back(std::min<uint64_t>(k1 * align, n));
+        g_bit.push_back(block_bit[k1]);
+        k0 = k1;
+    }
+    const uint64_t n_groups = g_elem.size() - 1;
+    Header h = layout(n, stream_bits, n_tensors, max_len, group, align, max_elems, n_groups);
 
     uint8_t* out = (uint8_t*)std::aligned_alloc(kAlign, h.total_bytes);
     if (!out) return WC_ERR_NOMEM;
@@ -223,13 +261,15 @@ extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* nu
         store_le<uint64_t>(out + h.off_tensors + 16ull * k, src.begin[k]);
         store_le<uint64_t>(out + h.off_tensors + 16ull * k + 8, src.size[k]);
     }
+    for (uint64_t g = 0; g <= n_groups; ++g) {
+        store_le<uint64_t>(out + h.off_groups + kGroupEntryBytes * g, g_elem[g]);
+        store_le<uint64_t>(out + h.off_groups + kGroupEntryBytes * g + 8, g_bit[g]);
+    }
     uint8_t* stream = out + h.off_stream;
     uint8_t* gap = out + h.off_gap;
-    uint8_t* gstart = out + h.off_group_start;
     uint8_t* sm = out + h.off_sm;
-    const uint64_t group_bits = (uint64_t)kChunkBits * group;
 
-    // 5. pack, plane split and auxiliary variables, per element range
+    // 6. pack, plane split and per-chunk gaps, per element range
     parallel_for(nthreads, [&](unsigned t) {
         const uint64_t i0 = r0[t], i1 = r0[t + 1];
         if (i0 == i1) return;
@@ -253,11 +293,8 @@ extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* nu
             for (uint64_t j = 0; j < k; ++j) {
                 const uint16_t b = p[j];
                 const uint8_t e = exponent_of(b);
-                const uint64_t i = gi + j;
-                sm[i] = sign_mantissa_of(b);
+                sm[gi + j] = sign_mantissa_of(b);
                 if (first_elem || (prev >> 6) != (pos >> 6)) gap[pos >> 6] = (uint8_t)(pos & 63);
-                if (first_elem || prev / group_bits != pos / group_bits)
-                    store_le<uint64_t>(gstart + 8 * (pos / group_bits), i);
                 first_elem = false;
                 const int L = len[e];
                 acc = (acc << L) | code[e];
@@ -273,12 +310,10 @@ extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* nu
         });
         if (nacc) __atomic_fetch_or(stream + wbyte, (uint8_t)(acc << (8 - nacc)), __ATOMIC_RELAXED);
         if (t + 1 == nthreads) {
-            // chunks / groups after the last codeword start point at the stream end / n
+            // chunks after the last codeword start point at the stream end
             for (uint64_t c = (prev >> 6) + 1; c < h.n_chunks; ++c) gap[c] = (uint8_t)(stream_bits - 64 * c);
-            for (uint64_t g = prev / group_bits + 1; g <= h.n_groups; ++g) store_le<uint64_t>(gstart + 8 * g, n);
         }
     });
-    store_le<uint64_t>(gstart + 8 * h.n_groups, n);
 
     *blob = out;
     *blob_bytes = h.total_bytes;

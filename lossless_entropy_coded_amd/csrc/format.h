@@ -8,28 +8,30 @@
 namespace wc {
 
 constexpr uint32_t kMagic = 0x46424357u;   // bytes "WCBF"
-constexpr uint16_t kVersion = 1;
+constexpr uint16_t kVersion = 2;
 constexpr uint32_t kHeaderBytes = 256;
 constexpr uint32_t kAlign = 256;
 constexpr uint32_t kMaxCodeLen = 24;       // longest code the format allows
 constexpr uint32_t kChunkBits = 64;        // one 8-byte chunk per decoding lane
-constexpr uint32_t kDefaultGroup = 256;    // chunks per group = lanes per workgroup
+constexpr uint32_t kDefaultGroup = 128;    // chunks per group: one wave64 unit, two chunks per lane
+constexpr uint32_t kDefaultAlign = 128;    // elements per block: groups start at multiples of it
+constexpr uint32_t kDefaultMaxElems = 4096; // elements a group may hold at most
 constexpr uint32_t kStreamSlack = 16;      // zero bytes after the last chunk
 
 // Header field offsets (little-endian).
 struct HeaderOffsets {
     static constexpr int magic = 0, version = 4, flags = 6, max_code_len = 8, chunk_bits = 9,
-                         reserved0 = 10, chunks_per_group = 12, n_tensors = 16, reserved1 = 20,
+                         reserved0 = 10, chunks_per_group = 12, n_tensors = 16, group_align = 20,
                          n_elems = 24, stream_bits = 32, n_chunks = 40, n_groups = 48,
-                         off_code_len = 56, off_tensors = 64, off_group_start = 72, off_gap = 80,
+                         off_code_len = 56, off_tensors = 64, off_groups = 72, off_gap = 80,
                          off_stream = 88, stream_bytes = 96, off_sm = 104, total_bytes = 112,
-                         reserved_tail = 120;
+                         group_max_elems = 120, reserved_tail = 124;
 };
 
 struct Header {
-    uint32_t max_code_len = 0, chunks_per_group = 0, n_tensors = 0;
+    uint32_t max_code_len = 0, chunks_per_group = 0, n_tensors = 0, group_align = 0, group_max_elems = 0;
     uint64_t n_elems = 0, stream_bits = 0, n_chunks = 0, n_groups = 0;
-    uint64_t off_code_len = 0, off_tensors = 0, off_group_start = 0, off_gap = 0, off_stream = 0,
+    uint64_t off_code_len = 0, off_tensors = 0, off_groups = 0, off_gap = 0, off_stream = 0,
              stream_bytes = 0, off_sm = 0, total_bytes = 0;
 };
 
@@ -47,22 +49,30 @@ inline void store_le(uint8_t* p, T v) {
     std::memcpy(p, &v, sizeof(T));
 }
 
+// Bytes of one entry of the groups section: u64 first element, u64 its bit.
+constexpr uint32_t kGroupEntryBytes = 16;
+
+// Chunks touched by the stream bits [p, q), q > p.
+inline uint64_t chunk_span(uint64_t p, uint64_t q) { return (q - 1) / kChunkBits - p / kChunkBits + 1; }
+
 // Section placement for a container with the given sizes.
 inline Header layout(uint64_t n_elems, uint64_t stream_bits, uint32_t n_tensors, uint32_t max_code_len,
-                     uint32_t group) {
+                     uint32_t group, uint32_t align, uint32_t max_elems, uint64_t n_groups) {
     Header h;
     h.max_code_len = max_code_len;
     h.chunks_per_group = group;
+    h.group_align = align;
+    h.group_max_elems = max_elems;
     h.n_tensors = n_tensors;
     h.n_elems = n_elems;
     h.stream_bits = stream_bits;
     h.n_chunks = div_up(stream_bits, kChunkBits);
-    h.n_groups = div_up(h.n_chunks, group);
+    h.n_groups = n_groups;
     h.stream_bytes = h.n_chunks * 8 + kStreamSlack;
     h.off_code_len = kHeaderBytes;
     h.off_tensors = round_up(h.off_code_len + 256, kAlign);
-    h.off_group_start = round_up(h.off_tensors + 16ull * n_tensors, kAlign);
-    h.off_gap = round_up(h.off_group_start + 8 * (h.n_groups + 1), kAlign);
+    h.off_groups = round_up(h.off_tensors + 16ull * n_tensors, kAlign);
+    h.off_gap = round_up(h.off_groups + kGroupEntryBytes * (h.n_groups + 1), kAlign);
     h.off_stream = round_up(h.off_gap + h.n_chunks, kAlign);
     h.off_sm = round_up(h.off_stream + h.stream_bytes, kAlign);
     h.total_bytes = round_up(h.off_sm + n_elems, kAlign);
@@ -78,13 +88,15 @@ inline void write_header(uint8_t* p, const Header& h) {
     store_le<uint8_t>(p + O::chunk_bits, (uint8_t)kChunkBits);
     store_le<uint32_t>(p + O::chunks_per_group, h.chunks_per_group);
     store_le<uint32_t>(p + O::n_tensors, h.n_tensors);
+    store_le<uint32_t>(p + O::group_align, h.group_align);
+    store_le<uint32_t>(p + O::group_max_elems, h.group_max_elems);
     store_le<uint64_t>(p + O::n_elems, h.n_elems);
     store_le<uint64_t>(p + O::stream_bits, h.stream_bits);
     store_le<uint64_t>(p + O::n_chunks, h.n_chunks);
     store_le<uint64_t>(p + O::n_groups, h.n_groups);
     store_le<uint64_t>(p + O::off_code_len, h.off_code_len);
     store_le<uint64_t>(p + O::off_tensors, h.off_tensors);
-    store_le<uint64_t>(p + O::off_group_start, h.off_group_start);
+    store_le<uint64_t>(p + O::off_groups, h.off_groups);
     store_le<uint64_t>(p + O::off_gap, h.off_gap);
     store_le<uint64_t>(p + O::off_stream, h.off_stream);
     store_le<uint64_t>(p + O::stream_bytes, h.stream_bytes);

@@ -8,15 +8,16 @@
 
 namespace wc {
 
-constexpr uint32_t kDecodeThreads = 256;   // lanes per workgroup = chunks per group G
+constexpr uint32_t kWaveLanes = 64;        // lanes of a wavefront
 constexpr uint32_t kChunksPerLane = 2;     // each lane decodes two adjacent 64-bit chunks
-constexpr uint32_t kGroupsPerBlock = kChunksPerLane;   // so a workgroup covers two adjacent groups
+constexpr uint32_t kGroupChunks = kWaveLanes * kChunksPerLane;   // chunks per group G: one wave's unit
+constexpr uint32_t kXcds = 8;              // accelerator dies; workgroup b runs on die b mod 8
 constexpr uint32_t kSingleBits = 12;       // width of the build-time single-codeword table
 constexpr uint32_t kEbufSlack = 3;         // bytes a chain may write past its range (then rewritten)
 constexpr uint32_t kHeadBytes = 3;         // leading bytes of a chain that a left neighbour may overwrite
 constexpr uint32_t kMergeElems = 8;        // elements per lane per merge step (one 16-byte bf16 store)
-constexpr uint32_t kMergeAlign = 64;       // a unit's merge range starts at a multiple of 64 elements
-                                           // (128 B of bf16, 64 B of sign+mantissa)
+constexpr uint32_t kMergeSteps = 8;        // merge steps per lane and group
+constexpr uint32_t kGroupMaxElems = kWaveLanes * kMergeSteps * kMergeElems;   // 4096 elements per group at most
 
 // Device decode tables, as 32-bit words, for index widths KC (counting) and KD (decoding):
 //   [0, 2^KC)                codeword-start table: for a KC-bit window,
@@ -61,28 +62,28 @@ struct CodeLens {
 struct DecodeParams {
     const uint8_t* stream;
     const uint8_t* gap;
-    const uint64_t* group_start;
+    const uint64_t* groups;  // {first element, first bit} per group, n_units + 1 entries
     const uint8_t* sm;
     uint16_t* out;
     const uint32_t* tables;
-    uint64_t n_chunks;
-    uint64_t stream_bits;
-    uint64_t n_groups;
-    uint64_t sm_last;        // offset of the last 8-byte piece of the sm plane: round_up(n, 8) - 8
-    uint64_t n_blocks;       // workgroup-sized units: ceil(n_groups / kGroupsPerBlock)
-    uint32_t ebuf_bytes;
-    uint32_t pad;
+    uint64_t n_elems;
+    uint64_t n_units;        // wave units = groups
+    uint32_t ebuf_bytes;     // exponent staging bytes per wave
     uint32_t l2_cap;         // long-code prefixes staged in LDS (0 .. kL2Prefixes)
-    uint32_t pad2;
 };
 
-// LDS bytes of one decode workgroup: static tables plus the dynamic part (the
-// unit's exponent staging and l2_cap second-level prefixes).
-uint32_t decode_dyn_lds_bytes(uint32_t ebuf_bytes, uint32_t l2_cap);
-uint32_t decode_lds_bytes(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes, uint32_t l2_cap);
+// Wavefronts per decode workgroup the kernels are built for.
+inline bool supported_waves(uint32_t waves) { return waves == 4 || waves == 8; }
+
+// LDS bytes of one decode workgroup of `waves` wavefronts: static tables plus
+// the dynamic part (each wave's exponent staging and l2_cap second-level prefixes).
+uint32_t decode_dyn_lds_bytes(uint32_t waves, uint32_t ebuf_bytes, uint32_t l2_cap);
+uint32_t decode_lds_bytes(uint32_t count_bits, uint32_t decode_bits, uint32_t waves, uint32_t ebuf_bytes,
+                          uint32_t l2_cap);
 
 // Resident decode workgroups per compute unit by the runtime's estimate (0 on error).
-int decode_blocks_per_cu(uint32_t count_bits, uint32_t decode_bits, uint32_t ebuf_bytes, uint32_t l2_cap);
+int decode_blocks_per_cu(uint32_t count_bits, uint32_t decode_bits, uint32_t waves, uint32_t ebuf_bytes,
+                         uint32_t l2_cap);
 
 // Build the decode tables of `lens` into d_tables (table_words(...) words) on `stream`.
 hipError_t launch_build_tables(const CodeLens& lens, uint32_t count_bits, uint32_t decode_bits, uint32_t* d_tables,
@@ -90,7 +91,7 @@ hipError_t launch_build_tables(const CodeLens& lens, uint32_t count_bits, uint32
 
 // One launch decoding every group of a container (p.ebuf_bytes and p.l2_cap set
 // the dynamic LDS).
-hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t decode_bits, uint32_t grid,
-                         hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t decode_bits, uint32_t waves,
+                         uint32_t grid, hipStream_t stream);
 
 }  // namespace wc

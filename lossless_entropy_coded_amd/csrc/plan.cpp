@@ -24,11 +24,10 @@ struct wc_plan_s {
     int device = 0;
     wc::Header h;
     std::vector<uint64_t> tensor_offsets, tensor_numels;
-    uint64_t max_group_elems = 0;
-    uint64_t max_unit_elems = 0;    // elements of kGroupsPerBlock adjacent groups (one workgroup unit)
-    uint64_t n_blocks = 0;          // workgroup units
+    uint64_t max_group_elems = 0;   // elements of the largest group (one wave's unit)
     uint32_t count_bits = 11;    // index width of the codeword-start table
     uint32_t decode_bits = 11;   // index width of the multi-codeword table
+    uint32_t waves = 8;          // wavefronts per workgroup
     uint32_t grid = 0;
     uint32_t lds_bytes = 0;
     uint32_t ebuf_bytes = 0;
@@ -48,39 +47,44 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
     if (bytes < wc::kHeaderBytes) return WC_ERR_TRUNCATED;
     if (load_le<uint32_t>(b + O::magic) != wc::kMagic || load_le<uint16_t>(b + O::version) != wc::kVersion ||
         load_le<uint16_t>(b + O::flags) != 0 || b[O::chunk_bits] != wc::kChunkBits ||
-        load_le<uint16_t>(b + O::reserved0) != 0 || load_le<uint32_t>(b + O::reserved1) != 0)
+        load_le<uint16_t>(b + O::reserved0) != 0)
         return WC_ERR_BAD_MAGIC;
     for (uint32_t k = O::reserved_tail; k < wc::kHeaderBytes; ++k)
         if (b[k]) return WC_ERR_BAD_MAGIC;
     h.max_code_len = b[O::max_code_len];
     h.chunks_per_group = load_le<uint32_t>(b + O::chunks_per_group);
     h.n_tensors = load_le<uint32_t>(b + O::n_tensors);
+    h.group_align = load_le<uint32_t>(b + O::group_align);
+    h.group_max_elems = load_le<uint32_t>(b + O::group_max_elems);
     h.n_elems = load_le<uint64_t>(b + O::n_elems);
     h.stream_bits = load_le<uint64_t>(b + O::stream_bits);
     h.n_chunks = load_le<uint64_t>(b + O::n_chunks);
     h.n_groups = load_le<uint64_t>(b + O::n_groups);
     h.off_code_len = load_le<uint64_t>(b + O::off_code_len);
     h.off_tensors = load_le<uint64_t>(b + O::off_tensors);
-    h.off_group_start = load_le<uint64_t>(b + O::off_group_start);
+    h.off_groups = load_le<uint64_t>(b + O::off_groups);
     h.off_gap = load_le<uint64_t>(b + O::off_gap);
     h.off_stream = load_le<uint64_t>(b + O::off_stream);
     h.stream_bytes = load_le<uint64_t>(b + O::stream_bytes);
     h.off_sm = load_le<uint64_t>(b + O::off_sm);
     h.total_bytes = load_le<uint64_t>(b + O::total_bytes);
-    if (h.max_code_len < 1 || h.max_code_len > wc::kMaxCodeLen || h.chunks_per_group < 1) return WC_ERR_BAD_MAGIC;
+    if (h.max_code_len < 1 || h.max_code_len > wc::kMaxCodeLen || h.chunks_per_group < 1 || h.group_align < 1 ||
+        h.group_max_elems < h.group_align || h.group_max_elems % h.group_align)
+        return WC_ERR_BAD_MAGIC;
     if (h.total_bytes > bytes) return WC_ERR_TRUNCATED;
 
     // size fields
     if (h.n_elems > (1ull << 40) || h.stream_bits > h.n_elems * (uint64_t)h.max_code_len ||
         h.stream_bits < h.n_elems || h.n_chunks != wc::div_up(h.stream_bits, wc::kChunkBits) ||
-        h.n_groups != wc::div_up(h.n_chunks, h.chunks_per_group) ||
+        h.n_groups > h.n_elems || (h.n_groups == 0) != (h.n_elems == 0) ||
         h.stream_bytes != h.n_chunks * 8 + wc::kStreamSlack)
         return WC_ERR_STREAM_BITS;
 
     // sections: 256-byte aligned, in order, non-overlapping, inside total_bytes
     if (h.n_tensors > (1u << 24)) return WC_ERR_SECTION_BOUNDS;
-    const uint64_t off[6] = {h.off_code_len, h.off_tensors, h.off_group_start, h.off_gap, h.off_stream, h.off_sm};
-    const uint64_t len[6] = {256, 16ull * h.n_tensors, 8 * (h.n_groups + 1), h.n_chunks, h.stream_bytes, h.n_elems};
+    const uint64_t off[6] = {h.off_code_len, h.off_tensors, h.off_groups, h.off_gap, h.off_stream, h.off_sm};
+    const uint64_t len[6] = {256, 16ull * h.n_tensors, wc::kGroupEntryBytes * (h.n_groups + 1), h.n_chunks,
+                             h.stream_bytes, h.n_elems};
     uint64_t lo = wc::kHeaderBytes;
     for (int k = 0; k < 6; ++k) {
         if (off[k] % wc::kAlign || off[k] < lo || off[k] > h.total_bytes || len[k] > h.total_bytes - off[k])
@@ -122,19 +126,26 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
     for (uint64_t c = 0; c < h.n_chunks; ++c)
         if (gap[c] >= h.max_code_len || 64 * c + gap[c] > h.stream_bits) return WC_ERR_GAP;
 
-    // group starts: 0, monotone, at most 64 codewords per chunk, ending at n
-    const uint8_t* gs = b + h.off_group_start;
-    const uint64_t per_group_max = 64ull * h.chunks_per_group;
-    uint64_t prev = load_le<uint64_t>(gs);
-    if (prev != 0) return WC_ERR_GROUP_START;
+    // groups: start at {0, 0}, strictly increasing, first elements on block
+    // boundaries, at most G chunks, at most group_max_elems elements and at
+    // least one bit per element each, ending at {n, stream_bits}
+    const uint8_t* gt = b + h.off_groups;
+    if (load_le<uint64_t>(gt) != 0 || load_le<uint64_t>(gt + 8) != 0) return WC_ERR_GROUP_START;
     max_group_elems = 0;
     for (uint64_t g = 1; g <= h.n_groups; ++g) {
-        uint64_t v = load_le<uint64_t>(gs + 8 * g);
-        if (v < prev || v - prev > per_group_max) return WC_ERR_GROUP_START;
-        max_group_elems = std::max(max_group_elems, v - prev);
-        prev = v;
+        const uint64_t e0 = load_le<uint64_t>(gt + wc::kGroupEntryBytes * (g - 1));
+        const uint64_t p0 = load_le<uint64_t>(gt + wc::kGroupEntryBytes * (g - 1) + 8);
+        const uint64_t e1 = load_le<uint64_t>(gt + wc::kGroupEntryBytes * g);
+        const uint64_t p1 = load_le<uint64_t>(gt + wc::kGroupEntryBytes * g + 8);
+        if (e1 <= e0 || p1 <= p0 || e1 > h.n_elems || p1 > h.stream_bits) return WC_ERR_GROUP_START;
+        if (g < h.n_groups && e1 % h.group_align) return WC_ERR_GROUP_START;
+        if (e1 - e0 > p1 - p0 || e1 - e0 > h.group_max_elems || wc::chunk_span(p0, p1) > h.chunks_per_group)
+            return WC_ERR_GROUP_START;
+        max_group_elems = std::max(max_group_elems, e1 - e0);
     }
-    if (prev != h.n_elems) return WC_ERR_GROUP_START;
+    if (load_le<uint64_t>(gt + wc::kGroupEntryBytes * h.n_groups) != h.n_elems ||
+        load_le<uint64_t>(gt + wc::kGroupEntryBytes * h.n_groups + 8) != h.stream_bits)
+        return WC_ERR_GROUP_START;
 
     // stream padding past stream_bits must be zero (so that it cannot be
     // mistaken for codewords by a reader that ignores stream_bits)
@@ -175,7 +186,9 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
     wc_plan_t* p = new (std::nothrow) wc_plan_t;
     if (!p) return WC_ERR_NOMEM;
     int st = parse_and_validate(blob_host, blob_bytes, p->h, p->tensor_offsets, p->tensor_numels, p->max_group_elems);
-    if (st == WC_OK && p->h.chunks_per_group != wc::kDecodeThreads) st = WC_ERR_UNSUPPORTED;
+    if (st == WC_OK && (p->h.chunks_per_group != wc::kGroupChunks || p->h.group_align % wc::kMergeElems ||
+                        p->h.group_max_elems > wc::kGroupMaxElems))
+        st = WC_ERR_UNSUPPORTED;
     if (st != WC_OK) {
         delete p;
         return st;
@@ -187,24 +200,12 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         p->count_bits = 11;
         p->decode_bits = 11;
     }
-    // workgroup units: kGroupsPerBlock adjacent groups, one contiguous output range
-    {
-        const uint8_t* gs = blob_host + p->h.off_group_start;
-        const uint64_t ng = p->h.n_groups;
-        p->n_blocks = wc::div_up(ng, wc::kGroupsPerBlock);
-        for (uint64_t u = 0; u < p->n_blocks; ++u) {
-            const uint64_t g0 = u * wc::kGroupsPerBlock;
-            const uint64_t g1 = std::min<uint64_t>(g0 + wc::kGroupsPerBlock, ng);
-            p->max_unit_elems = std::max(p->max_unit_elems, wc::load_le<uint64_t>(gs + 8 * g1) -
-                                                                wc::load_le<uint64_t>(gs + 8 * g0));
-        }
-    }
-    // staging buffer: the unit's exponents at offset (A mod 16), plus the
-    // bytes a chain's last three-byte write may reach past the unit's end
-    // staging of one unit: its exponents start at A mod kMergeAlign, a chain may
-    // write kEbufSlack bytes past the end, and the merge reads whole blocks
-    p->ebuf_bytes = (uint32_t)wc::round_up(
-        p->max_unit_elems + (wc::kMergeAlign - 1) + (wc::kMergeElems - 1) + wc::kEbufSlack, 16);
+    p->waves = env_u32("WC_WAVES", 8);
+    if (!wc::supported_waves(p->waves)) p->waves = 8;
+    // each wave's staging of one group's exponents: a chain may write
+    // kEbufSlack bytes past the end, and the merge reads whole blocks
+    p->ebuf_bytes =
+        (uint32_t)wc::round_up(p->max_group_elems + (wc::kMergeElems - 1) + wc::kEbufSlack, 16);
     // Long codes: canonical codes longer than the decode-table index all have
     // index-bit prefixes >= F = (first code of length decode_bits + 1) / 2; the
     // second-level table is staged for min(2^decode_bits - F, kL2Prefixes) of them.
@@ -223,7 +224,7 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         const uint64_t span = 1ull << p->decode_bits;
         p->l2_cap = F < span ? (uint32_t)std::min<uint64_t>(span - F, wc::kL2Prefixes) : 0u;
     }
-    p->lds_bytes = wc::decode_lds_bytes(p->count_bits, p->decode_bits, p->ebuf_bytes, p->l2_cap);
+    p->lds_bytes = wc::decode_lds_bytes(p->count_bits, p->decode_bits, p->waves, p->ebuf_bytes, p->l2_cap);
 
     DeviceGuard guard(hip_device);
     if (!guard.ok) {
@@ -235,7 +236,7 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         delete p;
         return WC_ERR_HIP;
     }
-    int per_cu = wc::decode_blocks_per_cu(p->count_bits, p->decode_bits, p->ebuf_bytes, p->l2_cap);
+    int per_cu = wc::decode_blocks_per_cu(p->count_bits, p->decode_bits, p->waves, p->ebuf_bytes, p->l2_cap);
     // The persistent grid must be co-resident.  LDS is handed out in granules of
     // 1/128 of a compute unit's LDS (1,280 bytes of 160 KiB on gfx950), which the
     // runtime's occupancy estimate does not round for: count the granules.
@@ -253,10 +254,16 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         delete p;
         return WC_ERR_UNSUPPORTED;
     }
+    // One persistent workgroup per resident slot, a multiple of the die count
+    // (so that each die takes a contiguous slab of groups), and no more
+    // workgroups than there are groups to give their waves.
     uint64_t want = (uint64_t)n_cu * (uint64_t)per_cu;
     uint32_t forced = env_u32("WC_GRID", 0);
     if (forced) want = forced;
-    p->grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(want, std::max<uint64_t>(p->n_blocks, 1)));
+    const uint64_t need = std::max<uint64_t>(1, wc::div_up(p->h.n_groups, p->waves));
+    want = std::min(want, need);
+    if (want >= wc::kXcds) want -= want % wc::kXcds;
+    p->grid = (uint32_t)std::max<uint64_t>(1, want);
 
     const size_t tbytes = (size_t)wc::table_words(p->count_bits, p->decode_bits) * 4;
     if (hipMalloc(reinterpret_cast<void**>(&p->d_tables), tbytes) != hipSuccess) {
@@ -311,20 +318,16 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
     wc::DecodeParams d;
     d.stream = b + p->h.off_stream;
     d.gap = b + p->h.off_gap;
-    d.group_start = reinterpret_cast<const uint64_t*>(b + p->h.off_group_start);
+    d.groups = reinterpret_cast<const uint64_t*>(b + p->h.off_groups);
     d.sm = b + p->h.off_sm;
     d.out = out_dev;
     d.tables = p->d_tables;
-    d.n_chunks = p->h.n_chunks;
-    d.stream_bits = p->h.stream_bits;
-    d.n_groups = p->h.n_groups;
-    d.sm_last = wc::round_up(p->h.n_elems, 8) - 8;
-    d.n_blocks = p->n_blocks;
+    d.n_elems = p->h.n_elems;
+    d.n_units = p->h.n_groups;
     d.ebuf_bytes = p->ebuf_bytes;
-    d.pad = 0;
     d.l2_cap = p->l2_cap;
-    d.pad2 = 0;
-    hipError_t e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->grid, static_cast<hipStream_t>(stream));
+    hipError_t e =
+        wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, p->grid, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
 }
 

@@ -33,7 +33,8 @@ _u32p = ctypes.POINTER(ctypes.c_uint32)
 
 class EncodeOpts(ctypes.Structure):
     _fields_ = [("max_code_len", ctypes.c_uint32), ("chunk_bytes", ctypes.c_uint32),
-                ("chunks_per_group", ctypes.c_uint32), ("n_threads", ctypes.c_uint32)]
+                ("chunks_per_group", ctypes.c_uint32), ("n_threads", ctypes.c_uint32),
+                ("group_align", ctypes.c_uint32), ("group_max_elems", ctypes.c_uint32)]
 
 
 _lib.wc_encode_host.argtypes = [ctypes.POINTER(_u16p), _u64p, ctypes.c_uint32, ctypes.POINTER(EncodeOpts),
@@ -70,6 +71,15 @@ WC_ERR_GROUP_START = -16
 WC_ERR_STREAM_BITS = -17
 WC_ERR_TENSOR_TABLE = -18
 
+# Group table defaults (wc_encode_opts): G = chunks per group, the most one
+# wave64 decodes (two 64-bit chunks per lane); A = elements per block, so that
+# every group's output starts on a 256-byte boundary; M = elements per group at
+# most (eight 8-element merge steps per lane).  The GPU decoder accepts G = 128,
+# any A that is a multiple of 8 and M <= 4096.
+GROUP_CHUNKS = 128
+GROUP_ALIGN = 128
+GROUP_MAX_ELEMS = 4096
+
 EXPORTED = ("wc_encode_host", "wc_free_host", "wc_plan", "wc_plan_info", "wc_plan_stats",
             "wc_decode_async", "wc_plan_destroy", "wc_status_str")
 
@@ -102,7 +112,9 @@ def _as_u16(t) -> np.ndarray:
     return a
 
 
-def encode_host(tensors, max_code_len: int = 24, chunks_per_group: int = 256, n_threads: int = 0) -> np.ndarray:
+def encode_host(tensors, max_code_len: int = 24, chunks_per_group: int = GROUP_CHUNKS,
+                n_threads: int = 0, group_align: int = GROUP_ALIGN,
+                group_max_elems: int = GROUP_MAX_ELEMS) -> np.ndarray:
     """wc_encode_host over a list of bf16 tensors (numpy uint16 or torch CPU).
 
     Returns the container as a numpy uint8 array (a copy of the library buffer)."""
@@ -110,7 +122,7 @@ def encode_host(tensors, max_code_len: int = 24, chunks_per_group: int = 256, n_
     nt = len(arrs)
     ptrs = (_u16p * max(nt, 1))(*[a.ctypes.data_as(_u16p) for a in arrs])
     numels = (ctypes.c_uint64 * max(nt, 1))(*[a.size for a in arrs])
-    opts = EncodeOpts(max_code_len, 8, chunks_per_group, n_threads)
+    opts = EncodeOpts(max_code_len, 8, chunks_per_group, n_threads, group_align, group_max_elems)
     out = _u8p()
     nbytes = ctypes.c_uint64(0)
     _check(_lib.wc_encode_host(ptrs, numels, nt, ctypes.byref(opts), ctypes.byref(out), ctypes.byref(nbytes)),

@@ -22,7 +22,7 @@ ERRORS = {
     0: "ok", -1: "bad argument", -2: "bad magic/version/fixed field", -3: "truncated or misplaced section",
     -4: "code length out of range", -5: "Kraft sum wrong", -6: "prefix conflict",
     -7: "stream does not decode to n symbols", -8: "non-zero padding", -9: "gap mismatch",
-    -10: "group start mismatch", -11: "tensor table mismatch", -12: "size fields inconsistent",
+    -10: "group table mismatch", -11: "tensor table mismatch", -12: "size fields inconsistent",
     -13: "out of memory", -14: "output too small",
 }
 
@@ -44,6 +44,8 @@ class Report(ctypes.Structure):
         ("max_code_len", ctypes.c_uint32),
         ("n_symbols", ctypes.c_uint32),
         ("longest_code", ctypes.c_uint32),
+        ("group_align", ctypes.c_uint32),
+        ("group_max_elems", ctypes.c_uint32),
         ("reserved", ctypes.c_uint32),
         ("kraft_num", ctypes.c_uint64),
         ("entropy_bits", ctypes.c_double),
@@ -89,7 +91,7 @@ def lib():
         L.orc_package_merge.argtypes = [u64p, ctypes.c_uint32, u8p]
         L.orc_canonical_codes.argtypes = [u8p, u32p]
         L.orc_encode.argtypes = [u16p, ctypes.c_uint64, u64p, ctypes.c_uint32, ctypes.c_uint32,
-                                 ctypes.c_uint32, ctypes.POINTER(u8p), u64p]
+                                 ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(u8p), u64p]
         L.orc_decode.argtypes = [u8p, ctypes.c_uint64, u16p, ctypes.c_uint64, ctypes.POINTER(Report)]
         L.orc_header.argtypes = [u8p, ctypes.c_uint64, ctypes.POINTER(Report)]
         L.orc_free.argtypes = [ctypes.c_void_p]
@@ -155,8 +157,13 @@ def canonical_codes(lens) -> np.ndarray:
     return codes
 
 
-def encode(w: np.ndarray, numels=None, max_code_len: int = 24, chunks_per_group: int = 256) -> np.ndarray:
-    """Oracle's own serial container writer.  Returns the container bytes."""
+def encode(w: np.ndarray, numels=None, max_code_len: int = 24, chunks_per_group: int = 128,
+           group_align: int = 128, group_max_elems: int = 4096) -> np.ndarray:
+    """Oracle's own serial container writer.  Returns the container bytes.
+
+    chunks_per_group (G), group_align (A) and group_max_elems (M) set the group
+    table: groups are runs of whole A-element blocks whose codewords touch at
+    most G chunks, of at most M elements."""
     w = np.ascontiguousarray(w, dtype=np.uint16).reshape(-1)
     if numels is None:
         nump, nt = None, 1
@@ -166,7 +173,8 @@ def encode(w: np.ndarray, numels=None, max_code_len: int = 24, chunks_per_group:
     out = ctypes.POINTER(ctypes.c_uint8)()
     nbytes = ctypes.c_uint64(0)
     st = lib().orc_encode(_p(w, ctypes.c_uint16), w.size, nump, nt, int(max_code_len),
-                          int(chunks_per_group), ctypes.byref(out), ctypes.byref(nbytes))
+                          int(chunks_per_group), int(group_align), int(group_max_elems), ctypes.byref(out),
+                          ctypes.byref(nbytes))
     if st:
         raise OracleError(st, "encode")
     try:

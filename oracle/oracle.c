@@ -33,9 +33,14 @@
  *  - one present symbol gets the 1-bit code "0";
  *  - the stream is cut into 64-bit chunks; gap[c] is the offset of the first
  *    codeword that starts at or after bit 64c (stream end if none);
- *  - chunks are grouped G at a time; group_start[g] is the index of the first
- *    element whose codeword starts at or after bit 64*G*g (n if none), plus a
- *    final entry equal to n.
+ *  - the per-block output positions of the pages are a group table: the
+ *    elements are cut into blocks of A (the last block may be shorter); a
+ *    group is a run of whole blocks that is as long as possible while the
+ *    codewords of its elements touch at most G chunks and it holds at most
+ *    M elements (a group takes at least one block; M is a multiple of A);
+ *    each entry holds the group's first element and the
+ *    stream bit where that element's codeword starts, and a final entry
+ *    holds {n, stream bits}.
  */
 #include "oracle.h"
 
@@ -44,7 +49,7 @@
 #include <string.h>
 
 /* ------------------------------------------------------------------------ */
-/* Container v1 layout, as restated for the oracle (little-endian fields).  */
+/* Container v2 layout, as restated for the oracle (little-endian fields).  */
 /* ------------------------------------------------------------------------ */
 #define HDR_BYTES       256u
 #define ALIGN           256u
@@ -52,26 +57,28 @@
 #define CHUNK_BITS      64u
 
 #define F_MAGIC          0   /* "WCBF"                                      */
-#define F_VERSION        4   /* u16, 1                                      */
+#define F_VERSION        4   /* u16, 2                                      */
 #define F_FLAGS          6   /* u16, 0                                      */
 #define F_MAXLEN         8   /* u8                                          */
 #define F_CHUNKBITS      9   /* u8, 64                                      */
 #define F_RES0          10   /* u16, 0                                      */
 #define F_G             12   /* u32 chunks per group                        */
 #define F_NTENS         16   /* u32                                         */
-#define F_RES1          20   /* u32, 0                                      */
+#define F_ALIGN         20   /* u32 elements per block A                    */
 #define F_N             24   /* u64 elements                                */
 #define F_SBITS         32   /* u64 stream bits                             */
 #define F_NCHUNKS       40   /* u64                                         */
 #define F_NGROUPS       48   /* u64                                         */
 #define F_OFF_LEN       56   /* u64: u8 code_len[256]                       */
 #define F_OFF_TENS      64   /* u64: {u64 offset, u64 numel}[n_tensors]     */
-#define F_OFF_GS        72   /* u64: u64 group_start[n_groups + 1]          */
+#define F_OFF_GS        72   /* u64: {u64 elem, u64 bit}[n_groups + 1]      */
 #define F_OFF_GAP       80   /* u64: u8 gap[n_chunks]                       */
 #define F_OFF_STREAM    88   /* u64: stream bytes                           */
 #define F_STREAM_BYTES  96   /* u64: 8 * n_chunks + 16 (zero padded)        */
 #define F_OFF_SM       104   /* u64: u8 sm[n]                               */
 #define F_TOTAL        112   /* u64: whole container size                   */
+#define F_MAXG         120   /* u32 elements per group at most M            */
+#define F_TAIL         124   /* zero from here to the end of the header     */
 
 static uint64_t rd(const uint8_t* p, int nbytes) {
     uint64_t v = 0;
@@ -83,6 +90,34 @@ static void wr(uint8_t* p, uint64_t v, int nbytes) {
 }
 static uint64_t round_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 static uint64_t ceil_div(uint64_t x, uint64_t a) { return (x + a - 1) / a; }
+
+/* ------------------------------------------------------------------------ */
+/* Group table [DF11 abstract (ii): per-block output positions].            */
+/* block_bit[k] is the stream bit where block k's first codeword starts,    */
+/* k < nb, and block_bit[nb] the stream length.  Writes n_groups + 1 pairs  */
+/* into elem[] / bit[] (each of capacity nb + 1) and returns n_groups.       */
+/* ------------------------------------------------------------------------ */
+static uint64_t chunks_touched(uint64_t p, uint64_t q) {   /* chunks holding bits [p, q), q > p */
+    return (q - 1) / CHUNK_BITS - p / CHUNK_BITS + 1;
+}
+
+static uint64_t orc_groups(const uint64_t* block_bit, uint64_t nb, uint64_t n, uint32_t A, uint32_t G,
+                           uint32_t M, uint64_t* elem, uint64_t* bit) {
+    uint64_t g = 0, k = 0;
+    elem[0] = 0;
+    bit[0] = 0;
+    while (k < nb) {
+        uint64_t first = k;
+        ++k;   /* at least one block */
+        while (k < nb && (k + 1 - first) * (uint64_t)A <= M &&
+               chunks_touched(block_bit[first], block_bit[k + 1]) <= G)
+            ++k;
+        ++g;
+        elem[g] = k * (uint64_t)A < n ? k * (uint64_t)A : n;
+        bit[g] = block_bit[k];
+    }
+    return g;
+}
 
 /* ------------------------------------------------------------------------ */
 /* Planes [DF11 abstract; L2-7B abstract]                                   */
@@ -247,9 +282,9 @@ int orc_canonical_codes(const uint8_t lens[256], uint32_t codes[256]) {
 /* Writer (serial).  Container layout as in the header comment.             */
 /* ------------------------------------------------------------------------ */
 int orc_encode(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
-               uint32_t max_code_len, uint32_t G, uint8_t** blob, uint64_t* blob_bytes) {
+               uint32_t max_code_len, uint32_t G, uint32_t A, uint32_t M, uint8_t** blob, uint64_t* blob_bytes) {
     if (!blob || !blob_bytes || (n && !w)) return ORC_E_ARG;
-    if (max_code_len < 1 || max_code_len > MAX_LEN_LIMIT || G < 1) return ORC_E_ARG;
+    if (max_code_len < 1 || max_code_len > MAX_LEN_LIMIT || G < 1 || A < 1 || M < A || M % A) return ORC_E_ARG;
     uint64_t one_numel = n;
     if (!numels) { numels = &one_numel; n_tensors = 1; }
     uint64_t sum = 0;
@@ -272,34 +307,53 @@ int orc_encode(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n
     uint64_t bits = 0;
     for (int s = 0; s < 256; ++s) bits += hist[s] * lens[s];
     uint64_t n_chunks = ceil_div(bits, CHUNK_BITS);
-    uint64_t n_groups = ceil_div(n_chunks, G);
     uint64_t stream_bytes = 8 * n_chunks + 16;
+
+    /* where every block of A elements starts in the stream, then the groups */
+    uint64_t nb = ceil_div(n, A);
+    uint64_t* block_bit = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+    uint64_t* g_elem = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+    uint64_t* g_bit = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+    if (!block_bit || !g_elem || !g_bit) {
+        free(block_bit); free(g_elem); free(g_bit); free(e); free(sm);
+        return ORC_E_NOMEM;
+    }
+    {
+        uint64_t at = 0;
+        for (uint64_t i = 0; i < n; ++i) {
+            if (i % A == 0) block_bit[i / A] = at;
+            at += lens[e[i]];
+        }
+        block_bit[nb] = at;
+    }
+    uint64_t n_groups = orc_groups(block_bit, nb, n, A, G, M, g_elem, g_bit);
 
     uint64_t off_len = HDR_BYTES;
     uint64_t off_tens = round_up(off_len + 256, ALIGN);
     uint64_t off_gs = round_up(off_tens + 16ull * n_tensors, ALIGN);
-    uint64_t off_gap = round_up(off_gs + 8 * (n_groups + 1), ALIGN);
+    uint64_t off_gap = round_up(off_gs + 16 * (n_groups + 1), ALIGN);
     uint64_t off_stream = round_up(off_gap + n_chunks, ALIGN);
     uint64_t off_sm = round_up(off_stream + stream_bytes, ALIGN);
     uint64_t total = round_up(off_sm + n, ALIGN);
 
     uint8_t* b = (uint8_t*)calloc(total, 1);
-    if (!b) { free(e); free(sm); return ORC_E_NOMEM; }
+    if (!b) { free(block_bit); free(g_elem); free(g_bit); free(e); free(sm); return ORC_E_NOMEM; }
 
     uint8_t* stream = b + off_stream;
     uint8_t* gap = b + off_gap;
     uint8_t* gs = b + off_gs;
-    uint64_t pos = 0, next_chunk = 0, next_group = 0;
+    for (uint64_t g = 0; g <= n_groups; ++g) {
+        wr(gs + 16 * g, g_elem[g], 8);
+        wr(gs + 16 * g + 8, g_bit[g], 8);
+    }
+    free(block_bit); free(g_elem); free(g_bit);
+    uint64_t pos = 0, next_chunk = 0;
     for (uint64_t i = 0; i < n; ++i) {
-        /* auxiliary variables [DF11 abstract (ii)] for every chunk / group
-         * whose first codeword start is this one */
+        /* auxiliary variables [DF11 abstract (ii)] for every chunk whose first
+         * codeword start is this one */
         while (next_chunk < n_chunks && CHUNK_BITS * next_chunk <= pos) {
             gap[next_chunk] = (uint8_t)(pos - CHUNK_BITS * next_chunk);
             ++next_chunk;
-        }
-        while (next_group < n_groups && CHUNK_BITS * G * next_group <= pos) {
-            wr(gs + 8 * next_group, i, 8);
-            ++next_group;
         }
         int L = lens[e[i]];
         uint32_t c = codes[e[i]];
@@ -309,8 +363,6 @@ int orc_encode(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n
         }
     }
     while (next_chunk < n_chunks) { gap[next_chunk] = (uint8_t)(bits - CHUNK_BITS * next_chunk); ++next_chunk; }
-    while (next_group < n_groups) { wr(gs + 8 * next_group, n, 8); ++next_group; }
-    wr(gs + 8 * n_groups, n, 8);
 
     memcpy(b + off_len, lens, 256);
     uint64_t acc = 0;
@@ -322,12 +374,14 @@ int orc_encode(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n
     if (n) memcpy(b + off_sm, sm, n);
 
     memcpy(b + F_MAGIC, "WCBF", 4);
-    wr(b + F_VERSION, 1, 2);
+    wr(b + F_VERSION, 2, 2);
     wr(b + F_FLAGS, 0, 2);
     wr(b + F_MAXLEN, max_code_len, 1);
     wr(b + F_CHUNKBITS, CHUNK_BITS, 1);
     wr(b + F_G, G, 4);
     wr(b + F_NTENS, n_tensors, 4);
+    wr(b + F_ALIGN, A, 4);
+    wr(b + F_MAXG, M, 4);
     wr(b + F_N, n, 8);
     wr(b + F_SBITS, bits, 8);
     wr(b + F_NCHUNKS, n_chunks, 8);
@@ -352,7 +406,7 @@ int orc_encode(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n
 /* Reader                                                                   */
 /* ------------------------------------------------------------------------ */
 typedef struct {
-    uint32_t max_len, G, n_tensors;
+    uint32_t max_len, G, A, M, n_tensors;
     uint64_t n, stream_bits, n_chunks, n_groups;
     uint64_t off_len, off_tens, off_gs, off_gap, off_stream, stream_bytes, off_sm, total;
 } hdr_t;
@@ -360,12 +414,14 @@ typedef struct {
 static int parse_header(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
     if (!blob || bytes < HDR_BYTES) return ORC_E_TRUNC;
     if (memcmp(blob + F_MAGIC, "WCBF", 4) != 0) return ORC_E_MAGIC;
-    if (rd(blob + F_VERSION, 2) != 1 || rd(blob + F_FLAGS, 2) != 0) return ORC_E_MAGIC;
+    if (rd(blob + F_VERSION, 2) != 2 || rd(blob + F_FLAGS, 2) != 0) return ORC_E_MAGIC;
     if (rd(blob + F_CHUNKBITS, 1) != CHUNK_BITS) return ORC_E_MAGIC;
-    if (rd(blob + F_RES0, 2) != 0 || rd(blob + F_RES1, 4) != 0) return ORC_E_MAGIC;
-    for (uint32_t k = 120; k < HDR_BYTES; ++k) if (blob[k]) return ORC_E_MAGIC;
+    if (rd(blob + F_RES0, 2) != 0) return ORC_E_MAGIC;
+    for (uint32_t k = F_TAIL; k < HDR_BYTES; ++k) if (blob[k]) return ORC_E_MAGIC;
     h->max_len = (uint32_t)rd(blob + F_MAXLEN, 1);
     h->G = (uint32_t)rd(blob + F_G, 4);
+    h->A = (uint32_t)rd(blob + F_ALIGN, 4);
+    h->M = (uint32_t)rd(blob + F_MAXG, 4);
     h->n_tensors = (uint32_t)rd(blob + F_NTENS, 4);
     h->n = rd(blob + F_N, 8);
     h->stream_bits = rd(blob + F_SBITS, 8);
@@ -379,16 +435,17 @@ static int parse_header(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
     h->stream_bytes = rd(blob + F_STREAM_BYTES, 8);
     h->off_sm = rd(blob + F_OFF_SM, 8);
     h->total = rd(blob + F_TOTAL, 8);
-    if (h->max_len < 1 || h->max_len > MAX_LEN_LIMIT || h->G < 1) return ORC_E_MAGIC;
+    if (h->max_len < 1 || h->max_len > MAX_LEN_LIMIT || h->G < 1 || h->A < 1 || h->M < h->A || h->M % h->A)
+        return ORC_E_MAGIC;
     /* derived sizes (guard the multiplications against absurd values first) */
     if (h->n > ((uint64_t)1 << 48) || h->stream_bits > ((uint64_t)1 << 56)) return ORC_E_SIZES;
     if (h->n_chunks != ceil_div(h->stream_bits, CHUNK_BITS)) return ORC_E_SIZES;
-    if (h->n_groups != ceil_div(h->n_chunks, h->G)) return ORC_E_SIZES;
+    if (h->n_groups > h->n || (h->n_groups == 0) != (h->n == 0)) return ORC_E_SIZES;
     if (h->stream_bytes != 8 * h->n_chunks + 16) return ORC_E_SIZES;
     if (h->stream_bits > h->n * (uint64_t)h->max_len || h->stream_bits < h->n) return ORC_E_SIZES;
     /* sections: aligned, in order, inside the blob */
     const uint64_t offs[6] = {h->off_len, h->off_tens, h->off_gs, h->off_gap, h->off_stream, h->off_sm};
-    const uint64_t lens[6] = {256, 16ull * h->n_tensors, 8 * (h->n_groups + 1), h->n_chunks,
+    const uint64_t lens[6] = {256, 16ull * h->n_tensors, 16 * (h->n_groups + 1), h->n_chunks,
                               h->stream_bytes, h->n};
     uint64_t lo = HDR_BYTES;
     for (int k = 0; k < 6; ++k) {
@@ -411,6 +468,8 @@ int orc_header(const uint8_t* blob, uint64_t blob_bytes, orc_report* rep) {
         rep->n_groups = h.n_groups;
         rep->n_tensors = h.n_tensors;
         rep->chunks_per_group = h.G;
+        rep->group_align = h.A;
+        rep->group_max_elems = h.M;
         rep->max_code_len = h.max_len;
     }
     return ORC_OK;
@@ -500,18 +559,18 @@ int orc_decode(const uint8_t* blob, uint64_t bytes, uint16_t* out, uint64_t out_
     const uint8_t* gs = blob + h.off_gs;
     const uint8_t* sm = blob + h.off_sm;
     uint64_t hist[256] = {0};
-    uint64_t pos = 0, next_chunk = 0, next_group = 0;
+    uint64_t nb = ceil_div(h.n, h.A);
+    uint64_t* block_bit = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+    if (!block_bit) { free(T); return ORC_E_NOMEM; }
+    uint64_t pos = 0, next_chunk = 0;
     for (uint64_t i = 0; i < h.n && st == ORC_OK; ++i) {
         while (next_chunk < h.n_chunks && CHUNK_BITS * next_chunk <= pos) {
             uint64_t want = pos - CHUNK_BITS * next_chunk;
             if (want >= CHUNK_BITS || gap[next_chunk] != want) { st = ORC_E_GAP; break; }
             ++next_chunk;
         }
-        while (st == ORC_OK && next_group < h.n_groups && CHUNK_BITS * h.G * next_group <= pos) {
-            if (rd(gs + 8 * next_group, 8) != i) { st = ORC_E_GROUP; break; }
-            ++next_group;
-        }
         if (st != ORC_OK) break;
+        if (i % h.A == 0) block_bit[i / h.A] = pos;
         int node = 0;
         for (;;) {
             if (pos >= h.stream_bits) { st = ORC_E_STREAM; break; }
@@ -528,18 +587,27 @@ int orc_decode(const uint8_t* blob, uint64_t bytes, uint16_t* out, uint64_t out_
         out[i] = (uint16_t)(((s & 0x80) << 8) | ((uint16_t)e << 7) | (s & 0x7F));
     }
     free(T);
-    if (st != ORC_OK) return st;
-    if (pos != h.stream_bits) return ORC_E_STREAM;
+    if (st != ORC_OK) { free(block_bit); return st; }
+    if (pos != h.stream_bits) { free(block_bit); return ORC_E_STREAM; }
     while (next_chunk < h.n_chunks) {
         uint64_t want = h.stream_bits - CHUNK_BITS * next_chunk;
-        if (want >= CHUNK_BITS || gap[next_chunk] != want) return ORC_E_GAP;
+        if (want >= CHUNK_BITS || gap[next_chunk] != want) { free(block_bit); return ORC_E_GAP; }
         ++next_chunk;
     }
-    while (next_group < h.n_groups) {
-        if (rd(gs + 8 * next_group, 8) != h.n) return ORC_E_GROUP;
-        ++next_group;
+    /* the group table, re-derived from the observed block starts */
+    block_bit[nb] = pos;
+    {
+        uint64_t* g_elem = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+        uint64_t* g_bit = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+        if (!g_elem || !g_bit) { free(g_elem); free(g_bit); free(block_bit); return ORC_E_NOMEM; }
+        uint64_t ng = orc_groups(block_bit, nb, h.n, h.A, h.G, h.M, g_elem, g_bit);
+        if (ng != h.n_groups) st = ORC_E_GROUP;
+        for (uint64_t g = 0; st == ORC_OK && g <= ng; ++g)
+            if (rd(gs + 16 * g, 8) != g_elem[g] || rd(gs + 16 * g + 8, 8) != g_bit[g]) st = ORC_E_GROUP;
+        free(g_elem); free(g_bit);
     }
-    if (rd(gs + 8 * h.n_groups, 8) != h.n) return ORC_E_GROUP;
+    free(block_bit);
+    if (st != ORC_OK) return st;
 
     /* every bit after stream_bits, up to the end of the section, is zero */
     for (uint64_t p = h.stream_bits; p < 8 * h.stream_bytes; ++p) {
@@ -559,6 +627,8 @@ int orc_decode(const uint8_t* blob, uint64_t bytes, uint16_t* out, uint64_t out_
         rep->n_groups = h.n_groups;
         rep->n_tensors = h.n_tensors;
         rep->chunks_per_group = h.G;
+        rep->group_align = h.A;
+        rep->group_max_elems = h.M;
         rep->max_code_len = h.max_len;
         rep->n_symbols = m;
         rep->longest_code = longest;

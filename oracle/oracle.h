@@ -43,7 +43,7 @@ extern "C" {
 #define ORC_E_STREAM      -7   /* bit stream does not decode to n symbols    */
 #define ORC_E_PADDING     -8   /* non-zero padding bits after stream end     */
 #define ORC_E_GAP         -9   /* stored per-chunk gap disagrees             */
-#define ORC_E_GROUP      -10   /* stored group output start disagrees        */
+#define ORC_E_GROUP      -10   /* stored group table disagrees               */
 #define ORC_E_TENSORS    -11   /* tensor table is not a partition of [0, n)  */
 #define ORC_E_SIZES      -12   /* n_chunks / n_groups / stream_bytes wrong   */
 #define ORC_E_NOMEM      -13
@@ -60,6 +60,8 @@ typedef struct {
     uint32_t max_code_len;     /* header field                               */
     uint32_t n_symbols;        /* symbols with a non-zero code length        */
     uint32_t longest_code;     /* max code length actually assigned          */
+    uint32_t group_align;      /* elements per block of the group table      */
+    uint32_t group_max_elems;  /* elements per group at most                 */
     uint32_t reserved;
     uint64_t kraft_num;        /* sum over symbols of 2^(24 - len)           */
     double   entropy_bits;     /* H of the exponent histogram, bits/symbol   */
@@ -87,11 +89,12 @@ int orc_package_merge(const uint64_t counts[256], uint32_t max_len, uint8_t lens
 int orc_canonical_codes(const uint8_t lens[256], uint32_t codes[256]);
 
 /* Independent container writer (serial, one bit at a time).
- * w: n bf16 words; numels: n_tensors sizes summing to n (NULL -> one tensor).
+ * w: n bf16 words; numels: n_tensors sizes summing to n (NULL -> one tensor);
+ * chunks_per_group G, group_align A and group_max_elems M set the group table.
  * On success *blob is malloc'ed (free with orc_free). */
 int orc_encode(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
-               uint32_t max_code_len, uint32_t chunks_per_group,
-               uint8_t** blob, uint64_t* blob_bytes);
+               uint32_t max_code_len, uint32_t chunks_per_group, uint32_t group_align,
+               uint32_t group_max_elems, uint8_t** blob, uint64_t* blob_bytes);
 
 /* Serial bit-by-bit decoder with full container checks.
  * out must hold out_cap >= n_elems words.  rep may be NULL. */

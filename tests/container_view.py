@@ -1,8 +1,8 @@
 """Read-only numpy view of a container's sections, for tests.
 
-Restates the container v1 layout (256-byte header of little-endian fields,
-then 256-byte-aligned sections code_len, tensors, group_start, gap, stream,
-sm) so that tests can inspect what an encoder wrote.  It decodes nothing.
+Restates the container v2 layout (256-byte header of little-endian fields,
+then 256-byte-aligned sections code_len, tensors, groups, gap, stream, sm) so
+that tests can inspect what an encoder wrote.  It decodes nothing.
 """
 from __future__ import annotations
 
@@ -12,10 +12,10 @@ import numpy as np
 
 HEADER_FIELDS = {
     "max_code_len": (8, "<B"), "chunk_bits": (9, "<B"), "chunks_per_group": (12, "<I"),
-    "n_tensors": (16, "<I"), "n_elems": (24, "<Q"), "stream_bits": (32, "<Q"), "n_chunks": (40, "<Q"),
+    "n_tensors": (16, "<I"), "group_align": (20, "<I"), "n_elems": (24, "<Q"), "stream_bits": (32, "<Q"), "n_chunks": (40, "<Q"),
     "n_groups": (48, "<Q"), "off_len": (56, "<Q"), "off_tens": (64, "<Q"), "off_gs": (72, "<Q"),
     "off_gap": (80, "<Q"), "off_stream": (88, "<Q"), "stream_bytes": (96, "<Q"), "off_sm": (104, "<Q"),
-    "total": (112, "<Q"),
+    "total": (112, "<Q"), "group_max_elems": (120, "<I"),
 }
 
 
@@ -33,20 +33,25 @@ def sections(blob: np.ndarray) -> dict:
     s = dict(h)
     s["code_len"] = blob[h["off_len"]:h["off_len"] + 256]
     s["tensors"] = blob[h["off_tens"]:h["off_tens"] + 16 * nt].view(np.uint64).reshape(nt, 2)
-    s["group_start"] = blob[h["off_gs"]:h["off_gs"] + 8 * (ng + 1)].view(np.uint64)
+    s["groups"] = blob[h["off_gs"]:h["off_gs"] + 16 * (ng + 1)].view(np.uint64).reshape(ng + 1, 2)
     s["gap"] = blob[h["off_gap"]:h["off_gap"] + nc]
     s["stream"] = blob[h["off_stream"]:h["off_stream"] + h["stream_bytes"]]
     s["sm"] = blob[h["off_sm"]:h["off_sm"] + n]
     return s
 
 
-def expected_metadata(exps: np.ndarray, code_len: np.ndarray, chunks_per_group: int):
+def expected_metadata(exps: np.ndarray, code_len: np.ndarray, chunks_per_group: int, group_align: int,
+                      group_max_elems: int):
     """Auxiliary variables recomputed from first principles with numpy.
 
     Codeword i starts at the sum of the lengths before it.  gap[c] is the
-    offset of the first start at or after bit 64c (stream end if none);
-    group_start[g] is the index of the first element starting at or after
-    bit 64*G*g (n if none), followed by n.
+    offset of the first start at or after bit 64c (stream end if none).  The
+    group table cuts the elements into blocks of A = group_align; a group is a
+    run of whole blocks (at least one), as long as possible while its
+    codewords touch at most G chunks, i.e. while the run ends at a bit
+    <= 64 * (first chunk + G), and while it holds at most M = group_max_elems
+    elements; each entry is {first element, its start bit}, and the last one
+    {n, total bits}.  Returns (total, gap, groups[n_groups + 1, 2]).
     """
     lens = code_len.astype(np.int64)[exps.astype(np.int64)]
     n = exps.size
@@ -55,11 +60,18 @@ def expected_metadata(exps: np.ndarray, code_len: np.ndarray, chunks_per_group: 
         starts[1:] = np.cumsum(lens)[:-1]
     total = int(lens.sum())
     n_chunks = -(-total // 64)
-    n_groups = -(-n_chunks // chunks_per_group)
     starts_s = np.append(starts, total)          # stream end acts as a sentinel start
     c_bits = 64 * np.arange(n_chunks, dtype=np.int64)
     gap = starts_s[np.searchsorted(starts_s, c_bits, side="left")] - c_bits
-    g_bits = 64 * chunks_per_group * np.arange(n_groups, dtype=np.int64)
-    gs = np.searchsorted(starts, g_bits, side="left")
-    gs = np.append(gs, n).astype(np.uint64)
-    return total, gap, gs
+    A, G = int(group_align), int(chunks_per_group)
+    block_bit = np.append(starts[::A], total)     # start of every block, then the end
+    nb = block_bit.size - 1
+    groups = [(0, 0)]
+    k = 0
+    while k < nb:
+        limit = 64 * (int(block_bit[k]) // 64 + G)
+        end = int(np.searchsorted(block_bit, limit, side="right")) - 1   # last block end <= limit
+        end = min(max(end, k + 1), nb, k + int(group_max_elems) // A)
+        groups.append((min(end * A, n), int(block_bit[end])))
+        k = end
+    return total, gap, np.array(groups, dtype=np.uint64)

@@ -54,7 +54,7 @@ def test_all_bf16_patterns(wc, oracle_lib, shuffle):
     if shuffle:
         w = np.random.default_rng(99).permutation(w)
     for writer in ("product", "oracle"):
-        blob = wc.encode_host([w]) if writer == "product" else oracle_lib.encode(w)
+        blob = wc.encode_host([w]) if writer == "product" else oracle_lib.encode(w, chunks_per_group=wc.GROUP_CHUNKS)
         log(f"case: all 65536 patterns shuffle={shuffle} writer={writer}")
         assert np.array_equal(gpu_decode(wc, blob), w)
 
@@ -70,7 +70,7 @@ def test_tiny_and_special_sequences(wc, oracle_lib):
         cases.append(np.full(n, 0x3C00, np.uint16))
     for i, w in enumerate(cases):
         log(f"case: tiny #{i} n={w.size}")
-        blob = wc.encode_host([w]) if i % 2 == 0 else oracle_lib.encode(w)
+        blob = wc.encode_host([w]) if i % 2 == 0 else oracle_lib.encode(w, chunks_per_group=wc.GROUP_CHUNKS)
         got = gpu_decode(wc, blob)
         assert np.array_equal(got, w), f"case {i} n={w.size}"
 
@@ -95,7 +95,7 @@ def test_long_codes_and_chunk_boundaries(wc, oracle_lib, prefix):
     chunk boundaries by up to 23 bits, both writers."""
     w = _fib_alphabet(prefix)
     for writer in ("product", "oracle"):
-        blob = wc.encode_host([w]) if writer == "product" else oracle_lib.encode(w)
+        blob = wc.encode_host([w]) if writer == "product" else oracle_lib.encode(w, chunks_per_group=wc.GROUP_CHUNKS)
         log(f"case: fib alphabet prefix_len={len(prefix)} writer={writer} n={w.size}")
         assert np.array_equal(gpu_decode(wc, blob), w)
 
@@ -135,15 +135,20 @@ def test_many_long_code_prefixes(wc, oracle_lib, env_knob, bits):
 
 
 @pytest.mark.parametrize("bits", [(12, 11), (12, 10), (11, 11), (11, 10), (10, 10)])
-@pytest.mark.parametrize("grid", [1, 7, 0])
-def test_table_width_and_grid_invariance(wc, env_knob, bits, grid):
+@pytest.mark.parametrize("grid", [1, 7, 16, 0])
+@pytest.mark.parametrize("waves", [4, 8])
+def test_table_width_and_grid_invariance(wc, env_knob, bits, grid, waves):
+    """Every table width, wavefronts per workgroup and grid size (one
+    workgroup looping over every group; grids that are and are not a multiple
+    of the die count) decodes the same bits."""
     from lossless_entropy_coded_amd.synth import make_workload
     wl = make_workload("heavy_tail_14k", scale_rows=512)
     blob = wc.encode_host(wl.tensors())
     env_knob("WC_COUNT_BITS", bits[0])
     env_knob("WC_DECODE_BITS", bits[1])
     env_knob("WC_GRID", grid or None)
-    log(f"case: heavy_tail rows=512 table bits={bits} grid={grid}")
+    env_knob("WC_WAVES", waves)
+    log(f"case: heavy_tail rows=512 table bits={bits} grid={grid} waves={waves}")
     with wc.Plan(blob) as plan:
         st = plan.stats()
         assert (st["count_bits"], st["decode_bits"]) == bits
@@ -181,10 +186,28 @@ def test_workload_full_size(wc, oracle_lib, name):
 
 @pytest.mark.parametrize("name,rows", [("matrix_1k", None), ("block_8b", 256), ("heavy_tail_14k", 2048)])
 def test_oracle_written_containers(wc, oracle_lib, name, rows):
+    """Containers written by the oracle's own serial writer decode exactly."""
     from lossless_entropy_coded_amd.synth import make_workload
     wl = make_workload(name, scale_rows=rows)
-    blob = oracle_lib.encode(wl.bits, numels=wl.numels)
+    blob = oracle_lib.encode(wl.bits, numels=wl.numels, chunks_per_group=wc.GROUP_CHUNKS)
     log(f"case: oracle-written {name} rows={rows}")
+    assert np.array_equal(gpu_decode(wc, blob), wl.bits)
+
+
+@pytest.mark.parametrize("align", [8, 64, 120, 128, 256])
+@pytest.mark.parametrize("writer", ["product", "oracle"])
+def test_group_block_sizes(wc, oracle_lib, align, writer):
+    """Any block size that is a multiple of 8 decodes exactly: groups then
+    start anywhere on an 8-element boundary, not only on cache lines."""
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload("heavy_tail_14k", scale_rows=256)
+    M = wc.GROUP_MAX_ELEMS // align * align            # the largest multiple of A the decoder accepts
+    if writer == "product":
+        blob = wc.encode_host(wl.tensors(), group_align=align, group_max_elems=M)
+    else:
+        blob = oracle_lib.encode(wl.bits, numels=wl.numels, chunks_per_group=wc.GROUP_CHUNKS, group_align=align,
+                                 group_max_elems=M)
+    log(f"case: group_align={align} writer={writer}")
     assert np.array_equal(gpu_decode(wc, blob), wl.bits)
 
 
@@ -210,9 +233,14 @@ def test_corrupted_stream_stays_in_bounds(wc):
     b = blob.copy()
     b[s["off_stream"]:s["off_stream"] + nbytes - 1] = 0x00
     variants.append(("zeros", b))
-    b = blob.copy()
-    b[s["off_gs"] + 8:s["off_gs"] + 16] = np.frombuffer(np.uint64(0).tobytes(), np.uint8)
-    variants.append(("empty-first-group", b))
+    # group bit offsets that pass wc_plan's checks but are not codeword starts
+    for shift in (1, 23, 63):
+        b = blob.copy()
+        for g in range(1, int(s["n_groups"]), 3):
+            at = s["off_gs"] + 16 * g + 8
+            v = np.uint64(int(s["groups"][g, 1]) + shift)
+            b[at:at + 8] = np.frombuffer(v.tobytes(), np.uint8)
+        variants.append(("group-bits+%d" % shift, b))
     for tag, b in variants:
         log(f"case: corrupted stream {tag}")
         got = gpu_decode(wc, b)          # asserts the guard bands

@@ -58,8 +58,10 @@ def test_encoder_roundtrip_through_oracle(wc, oracle_lib, name, rows):
     s = sections(blob)
     assert int((counts * s["code_len"].astype(np.int64)).sum()) == int((counts * lo).sum())
     e, _ = oracle_lib.split_planes(wl.bits)
-    total, gap, gs = expected_metadata(e, s["code_len"], 256)
-    assert np.array_equal(s["gap"].astype(np.int64), gap) and np.array_equal(s["group_start"], gs)
+    total, gap, groups = expected_metadata(e, s["code_len"], wc.GROUP_CHUNKS, wc.GROUP_ALIGN, wc.GROUP_MAX_ELEMS)
+    assert s["chunks_per_group"] == wc.GROUP_CHUNKS and s["group_align"] == wc.GROUP_ALIGN
+    assert s["group_max_elems"] == wc.GROUP_MAX_ELEMS
+    assert np.array_equal(s["gap"].astype(np.int64), gap) and np.array_equal(s["groups"], groups)
 
 
 @pytest.mark.parametrize("n_threads", [1, 3, 8])
@@ -102,7 +104,10 @@ def test_encoder_max_code_len_option(wc, oracle_lib):
 
 def test_encoder_rejects_bad_options(wc):
     w = np.arange(10, dtype=np.uint16)
-    for kw in ({"max_code_len": 25}, {"chunks_per_group": 1 << 21}):
+    # a block of A 24-bit codes must fit in G chunks: A * 24 + 63 <= 64 * G
+    # M must be a multiple of A
+    for kw in ({"max_code_len": 25}, {"chunks_per_group": 1 << 21}, {"chunks_per_group": 48},
+               {"group_align": 342}, {"group_max_elems": 1000}, {"group_max_elems": 64}):
         with pytest.raises(wc.WCError) as ei:
             wc.encode_host([w], **kw)
         assert ei.value.status == wc.WC_ERR_INVALID_ARG
@@ -116,7 +121,7 @@ def test_oracle_writer_containers_validate(wc, oracle_lib):
     """Containers written by the oracle pass every check of wc_plan."""
     from lossless_entropy_coded_amd.synth import make_workload
     wl = make_workload("attn_4k_zeros", scale_rows=256)
-    blob = oracle_lib.encode(wl.bits, numels=wl.numels)
+    blob = oracle_lib.encode(wl.bits, numels=wl.numels, chunks_per_group=wc.GROUP_CHUNKS)
     st = _plan_status(wc, blob)
     assert st in (wc.WC_OK, wc.WC_ERR_HIP)
 
@@ -151,7 +156,7 @@ def test_plan_rejects_each_fault(wc):
         return lambda b: b.__setitem__(slice(off, off + len(val)), val)
 
     assert mutated(setb(0, np.frombuffer(b"XCBF", np.uint8))) == wc.WC_ERR_BAD_MAGIC
-    assert mutated(setb(4, np.array([2, 0], np.uint8))) == wc.WC_ERR_BAD_MAGIC            # version
+    assert mutated(setb(4, np.array([1, 0], np.uint8))) == wc.WC_ERR_BAD_MAGIC            # version
     assert mutated(setb(9, np.array([32], np.uint8))) == wc.WC_ERR_BAD_MAGIC              # chunk bits
     assert mutated(setb(200, np.array([1], np.uint8))) == wc.WC_ERR_BAD_MAGIC             # reserved tail
     assert _plan_status(wc, blob[:100]) == wc.WC_ERR_TRUNCATED
@@ -166,11 +171,23 @@ def test_plan_rejects_each_fault(wc):
     assert mutated(setb(s["off_gap"] + 5, np.array([24], np.uint8))) == wc.WC_ERR_GAP
     last = s["off_gap"] + s["n_chunks"] - 1
     assert mutated(setb(last, np.array([23], np.uint8))) in (wc.WC_ERR_GAP, wc.WC_OK, wc.WC_ERR_HIP)
-    g1 = s["off_gs"] + 8
-    assert mutated(setb(g1, _u64(0))) in ok           # an empty group is well-formed (the data is wrong)
-    assert mutated(setb(s["off_gs"], _u64(1))) == wc.WC_ERR_GROUP_START
-    assert mutated(setb(g1, _u64(s["n_elems"] + 5))) == wc.WC_ERR_GROUP_START            # not monotone / > n
-    assert mutated(setb(g1, _u64(64 * 256 + 1))) == wc.WC_ERR_GROUP_START                # too many per group
+    assert s["n_groups"] >= 3
+    e1, b1 = s["off_gs"] + 16, s["off_gs"] + 24                 # first element / bit of group 1
+    e1v, b1v = int(s["groups"][1, 0]), int(s["groups"][1, 1])
+    assert mutated(setb(s["off_gs"], _u64(1))) == wc.WC_ERR_GROUP_START                  # must start at 0
+    assert mutated(setb(s["off_gs"] + 8, _u64(1))) == wc.WC_ERR_GROUP_START              # ... at bit 0
+    assert mutated(setb(e1, _u64(0))) == wc.WC_ERR_GROUP_START                           # empty group
+    assert mutated(setb(e1, _u64(e1v + wc.GROUP_ALIGN // 2))) == wc.WC_ERR_GROUP_START   # off a block boundary
+    assert mutated(setb(e1, _u64(s["n_elems"] + 5))) == wc.WC_ERR_GROUP_START            # not monotone / > n
+    assert mutated(setb(b1, _u64(b1v + 64 * wc.GROUP_CHUNKS))) == wc.WC_ERR_GROUP_START  # too many chunks
+    assert mutated(setb(b1, _u64(e1v - 1))) == wc.WC_ERR_GROUP_START                     # < 1 bit per element
+    assert mutated(setb(120, np.array([100, 0, 0, 0], np.uint8))) == wc.WC_ERR_BAD_MAGIC  # M not a multiple of A
+    big = int(s["groups"][0, 0]) + wc.GROUP_MAX_ELEMS + wc.GROUP_ALIGN
+    if big < int(s["groups"][-1, 0]):
+        assert mutated(setb(e1, _u64(big))) == wc.WC_ERR_GROUP_START                     # more than M elements
+    # a bit offset that is not the codeword start of the element: wc_plan cannot
+    # see it; the decode is then wrong but stays in bounds (GPU tests)
+    assert mutated(setb(b1, _u64(b1v + 1))) in ok
     assert mutated(setb(32, _u64(s["stream_bits"] + 64))) == wc.WC_ERR_STREAM_BITS           # n_chunks disagrees
     assert mutated(setb(40, _u64(s["n_chunks"] + 1))) == wc.WC_ERR_STREAM_BITS
     assert mutated(setb(96, _u64(s["stream_bytes"] + 8))) == wc.WC_ERR_STREAM_BITS
@@ -178,9 +195,13 @@ def test_plan_rejects_each_fault(wc):
     assert mutated(setb(pad, np.array([0x10], np.uint8))) == wc.WC_ERR_STREAM_BITS
     assert mutated(setb(s["off_tens"] + 8, _u64(s["n_elems"] + 1))) == wc.WC_ERR_TENSOR_TABLE
     assert mutated(setb(s["off_tens"], _u64(3))) == wc.WC_ERR_TENSOR_TABLE
-    # valid container with a group size this build does not decode
-    b2 = wc.encode_host(wl.tensors(), chunks_per_group=128)
+    # valid containers with a group size or block size this build does not decode
+    b2 = wc.encode_host(wl.tensors(), chunks_per_group=2 * wc.GROUP_CHUNKS)
     assert _plan_status(wc, b2) == wc.WC_ERR_UNSUPPORTED
+    b3 = wc.encode_host(wl.tensors(), group_align=100, group_max_elems=4000)
+    assert _plan_status(wc, b3) == wc.WC_ERR_UNSUPPORTED
+    b4 = wc.encode_host(wl.tensors(), group_max_elems=2 * wc.GROUP_MAX_ELEMS)
+    assert _plan_status(wc, b4) == wc.WC_ERR_UNSUPPORTED
 
 
 def test_plan_rejects_random_corruption_without_crashing(wc):

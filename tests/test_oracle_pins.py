@@ -41,7 +41,7 @@ def test_worked_example(oracle_lib):
     assert sm.tolist() == g["sm"]
     blob = oracle_lib.encode(w)
     s = sections(blob)
-    assert s["magic"] == b"WCBF" and s["version"] == 1
+    assert s["magic"] == b"WCBF" and s["version"] == 2
     lens = {str(k): int(v) for k, v in enumerate(s["code_len"]) if v}
     assert lens == g["code_lengths"]
     codes = oracle_lib.canonical_codes(s["code_len"])
@@ -52,7 +52,7 @@ def test_worked_example(oracle_lib):
     assert [format(int(b), "02X") for b in s["stream"][:nbytes]] == g["stream_bytes_hex"]
     assert not s["stream"][nbytes:].any()
     assert s["gap"].tolist() == g["gap"]
-    assert s["group_start"].tolist() == g["group_start"]
+    assert s["groups"].tolist() == g["groups"]
     out, rep = oracle_lib.decode(blob, with_report=True)
     assert np.array_equal(out, w)
     assert rep["entropy_bits"] == pytest.approx(g["entropy_bits"], abs=1e-12)
@@ -91,12 +91,13 @@ def test_split_matches_ieee_fields(oracle_lib):
 # --------------------------------------------------------------------------
 # brute force over all 65,536 bf16 patterns: closed-form container
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("shuffle", [False, True])
-def test_all_bf16_patterns_closed_form(oracle_lib, shuffle):
+@pytest.mark.parametrize("shuffle,G,M", [(False, 128, 4096), (True, 128, 4096), (False, 256, 4096),
+                                         (False, 256, 1024)])
+def test_all_bf16_patterns_closed_form(oracle_lib, shuffle, G, M):
     w = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     if shuffle:
         w = np.random.default_rng(1234).permutation(w)
-    blob = oracle_lib.encode(w, chunks_per_group=256)
+    blob = oracle_lib.encode(w, chunks_per_group=G, group_align=128, group_max_elems=M)
     s = sections(blob)
     # every exponent value occurs exactly 256 times -> every optimal code has all lengths 8
     assert np.all(s["code_len"] == 8)
@@ -107,8 +108,12 @@ def test_all_bf16_patterns_closed_form(oracle_lib, shuffle):
     assert np.array_equal(s["stream"][:65536], exp_closed)
     assert not s["stream"][65536:].any()
     assert np.all(s["gap"] == 0)
-    G = 256
-    assert s["group_start"].tolist() == [8 * G * g for g in range(s["n_groups"])] + [65536]
+    # 8-bit codes: block k of 128 elements starts at bit 1024 k, on a chunk
+    # boundary, so each group is exactly 64 G bits = 8 G elements, unless M
+    # elements come first
+    per = min(8 * G, M)
+    assert s["n_groups"] == 65536 // per
+    assert s["groups"].tolist() == [[per * g, 8 * per * g] for g in range(s["n_groups"] + 1)]
     sign_closed = (w.astype(np.uint32) >= 32768).astype(np.uint8)
     assert np.array_equal(s["sm"], (sign_closed << 7) | (w & 0x7F).astype(np.uint8))
     out, rep = oracle_lib.decode(blob, with_report=True)
@@ -168,7 +173,7 @@ def test_single_and_empty_alphabet(oracle_lib):
     blob = oracle_lib.encode(np.zeros(0, np.uint16))
     s = sections(blob)
     assert s["n_elems"] == 0 and s["stream_bits"] == 0 and s["n_chunks"] == 0 and s["n_groups"] == 0
-    assert s["group_start"].tolist() == [0]
+    assert s["groups"].tolist() == [[0, 0]]
     assert oracle_lib.decode(blob).size == 0
     # n = 1 and a constant tensor: one symbol, code "0"
     for n in (1, 100, 64, 65):
@@ -192,8 +197,8 @@ def test_exhaustive_short_sequences(oracle_lib):
         for n in range(0, max_n + 1):
             for idx in itertools.product(range(len(vals)), repeat=n):
                 w = vals[list(idx)] if n else np.zeros(0, np.uint16)
-                for G in (1, 256):
-                    blob = oracle_lib.encode(w, chunks_per_group=G)
+                for G, A, M in ((1, 1, 1), (2, 3, 6), (128, 128, 4096)):
+                    blob = oracle_lib.encode(w, chunks_per_group=G, group_align=A, group_max_elems=M)
                     assert np.array_equal(oracle_lib.decode(blob), w)
                     n_checked += 1
     assert n_checked > 10000
@@ -229,13 +234,14 @@ def test_chunk_boundaries(oracle_lib):
     s2 = sections(oracle_lib.encode(w2, max_code_len=24))
     assert int(s2["gap"][1]) == 0
     for ww in (w, w2):
-        blob = oracle_lib.encode(ww, max_code_len=24, chunks_per_group=3)
-        s = sections(blob)
-        total, gap, gs = expected_metadata(ww >> 7, s["code_len"], 3)
-        assert s["stream_bits"] == total
-        assert np.array_equal(s["gap"].astype(np.int64), gap)
-        assert np.array_equal(s["group_start"], gs)
-        assert np.array_equal(oracle_lib.decode(blob), ww)
+        for G, A, M in ((3, 4, 8), (3, 1, 1000), (128, 128, 4096), (2, 64, 64), (128, 8, 64)):
+            blob = oracle_lib.encode(ww, max_code_len=24, chunks_per_group=G, group_align=A, group_max_elems=M)
+            s = sections(blob)
+            total, gap, groups = expected_metadata(ww >> 7, s["code_len"], G, A, M)
+            assert s["stream_bits"] == total
+            assert np.array_equal(s["gap"].astype(np.int64), gap)
+            assert np.array_equal(s["groups"], groups)
+            assert np.array_equal(oracle_lib.decode(blob), ww)
     # a stream of exactly 64*k bits (all lengths 8, n multiple of 8)
     w3 = np.repeat(np.arange(256, dtype=np.uint16) << 7, 3)[: 256 * 3]
     s3 = sections(oracle_lib.encode(w3))
@@ -316,10 +322,11 @@ def test_workload_pins(oracle_lib, name, rows):
     else:
         assert _cost(counts, s["code_len"]) >= _cost(counts, lh)
     e, sm = oracle_lib.split_planes(wl.bits)
-    total, gap, gs = expected_metadata(e, s["code_len"], s["chunks_per_group"])
+    total, gap, groups = expected_metadata(e, s["code_len"], s["chunks_per_group"], s["group_align"],
+                                           s["group_max_elems"])
     assert s["stream_bits"] == total
     assert np.array_equal(s["gap"].astype(np.int64), gap)
-    assert np.array_equal(s["group_start"], gs)
+    assert np.array_equal(s["groups"], groups)
     assert np.array_equal(s["sm"], sm)
     offs = np.concatenate([[0], np.cumsum(wl.numels)[:-1]]).astype(np.uint64)
     assert np.array_equal(s["tensors"][:, 0], offs)
@@ -349,7 +356,8 @@ def test_oracle_rejects_corruption(oracle_lib):
     sym = int(np.argmin(np.where(s["code_len"] > 0, s["code_len"], 99)))
     assert status_after(lambda b: b.__setitem__(s["off_len"] + sym, s["code_len"][sym] + 1)) == -5
     assert status_after(lambda b: b.__setitem__(s["off_gap"] + 3, (int(s["gap"][3]) + 1) % 24)) == -9
-    assert status_after(lambda b: b.__setitem__(s["off_gs"] + 8, int(blob[s["off_gs"] + 8]) ^ 1)) in (-10, -3)
+    assert status_after(lambda b: b.__setitem__(s["off_gs"] + 16, int(blob[s["off_gs"] + 16]) ^ 1)) == -10
+    assert status_after(lambda b: b.__setitem__(s["off_gs"] + 24, int(blob[s["off_gs"] + 24]) ^ 1)) == -10
     pad = s["off_stream"] + (s["stream_bits"] + 7) // 8 + 3
     assert status_after(lambda b: b.__setitem__(pad, 1)) == -8
     # a flipped stream bit either breaks the container or changes the output
