@@ -64,6 +64,9 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="untimed decode launches before the warm-up steps, for at least this much GPU time: "
+                         "the GPU's clocks take about 100 back-to-back launches (~15 ms) to reach steady state")
     ap.add_argument("--workload", default="block_8b",
                     help="synthetic workload (default: block_8b, the 8B-shape transformer block)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
@@ -156,7 +159,7 @@ def main():
     st = plan.stats()
     stream_bits = st["stream_bits"]
     n_chunks = -(-stream_bits // 64)
-    alg_read = n + -(-stream_bits // 8) + n_chunks + 8 * (st["n_groups"] + 1)
+    alg_read = n + -(-stream_bits // 8) + n_chunks + 16 * (st["n_groups"] + 1)
     alg_bytes = alg_read + 2 * n
 
     per_copy = blob.size + 2 * n
@@ -176,6 +179,18 @@ def main():
         print("bench.py: decode is NOT bit-exact", file=sys.stderr)
         sys.exit(3)
 
+    # settle: untimed launches until the GPU has run the decode for settle_ms
+    settle_launches, settled_ms = 0, 0.0
+    while settled_ms < args.settle_ms and settle_launches < 5000:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for k in range(25):
+            wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
+        b.record(stream)
+        b.synchronize()
+        settled_ms += a.elapsed_time(b)
+        settle_launches += 25
     for k in range(args.warmup):
         wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
     # HIP events on the launch stream around the K back-to-back launches; a
@@ -260,6 +275,7 @@ def main():
             "grid": st["grid"],
             "lds_bytes": st["lds_bytes"],
             "rotating_copies": copies,
+            "settle_launches": settle_launches,
             "bit_exact": bit_exact,
             "host_prep_s": round(t_gen, 2),
         },

@@ -298,10 +298,15 @@ __device__ __forceinline__ void put4(uint8_t*& q, const uint8_t* q_end, uint8_t*
 template <int KC, int KD, int W>
 __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) {
     constexpr uint32_t kThreads = kWaveLanes * W;
-    __shared__ __attribute__((aligned(16))) uint32_t s_cnt[1u << KC];
-    __shared__ __attribute__((aligned(16))) uint2 s_dec[1u << KD];
-    __shared__ __attribute__((aligned(16))) uint32_t s_long[kLongWords];
+    // decode tables, in the order of the plan's device buffer: codeword-start
+    // table, multi-codeword table, the canonical arrays for long codes
+    constexpr uint32_t kCntVec = (1u << KC) / 4, kDecVec = (2u << KD) / 4, kLongVec = kLongWords / 4;
+    constexpr uint32_t kTabVec = kCntVec + kDecVec + kLongVec;
+    __shared__ __attribute__((aligned(16))) uint4 s_tab[kTabVec];
     __shared__ __attribute__((aligned(16))) uint8_t s_dummy[4 * kThreads];
+    uint32_t* const s_cnt = reinterpret_cast<uint32_t*>(s_tab);
+    uint2* const s_dec = reinterpret_cast<uint2*>(s_tab + kCntVec);
+    uint32_t* const s_long = reinterpret_cast<uint32_t*>(s_tab + kCntVec + kDecVec);
     // dynamic: W exponent staging buffers of ebuf_bytes (one per wave), then the
     // second-level table for the long-code prefixes of this container
     // (l2_cap * 2^kL2Bits u16)
@@ -313,29 +318,6 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) 
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     uint8_t* const dummy = s_dummy + 4 * tid;
     uint8_t* const ebuf = dyn + wave * p.ebuf_bytes;
-
-    // stage the decode tables (built once per container) into LDS; this is the
-    // only point where the waves of a workgroup wait for each other
-    {
-        const uint4* src = reinterpret_cast<const uint4*>(p.tables);
-        for (uint32_t i = tid; i < (1u << KC) / 4; i += kThreads) reinterpret_cast<uint4*>(s_cnt)[i] = src[i];
-        src += (1u << KC) / 4;
-        for (uint32_t i = tid; i < (2u << KD) / 4; i += kThreads) reinterpret_cast<uint4*>(s_dec)[i] = src[i];
-        src += (2u << KD) / 4;
-        if (tid < kLongWords / 4) reinterpret_cast<uint4*>(s_long)[tid] = src[tid];
-        src += kLongWords / 4;
-        for (uint32_t i = tid; i < (p.l2_cap << kL2Bits) / 8; i += kThreads)
-            reinterpret_cast<uint4*>(s_l2)[i] = src[i];
-    }
-    __syncthreads();
-    LongTables lt;
-    lt.count = s_long;
-    lt.first = s_long + 32;
-    lt.base = s_long + 64;
-    lt.sorted = reinterpret_cast<const uint8_t*>(s_long + 96);
-    lt.l2 = s_l2;
-    lt.l2_first = __builtin_amdgcn_readfirstlane(s_long[160]);
-    lt.l2_n = min(__builtin_amdgcn_readfirstlane(s_long[161]), p.l2_cap);
 
     // Wave w of workgroup b takes groups b*W + w, then every (grid * W)-th
     // one after it: the groups in flight at any time form one contiguous
@@ -351,17 +333,48 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) 
     // covers exactly the loads it needs.
     const uint64_t stride = (uint64_t)gridDim.x * W;
     uint64_t u = (uint64_t)blockIdx.x * W + wave;
-    if (u >= p.n_units) return;
     const uint64_t last_u = p.n_units - 1;
-    Meta m_next;
-    Unit cur;
+    const bool active = u < p.n_units;
+
+    // Prologue: the first group's table entries, then every table load of the
+    // workgroup's staging, are in flight together; the first group's stream
+    // loads are issued before the tables are written to LDS.  The barrier
+    // after the staging is the only point where the waves of a workgroup wait
+    // for each other.
+    const Meta m_first = load_meta(p, min_u64(u, last_u));
+    constexpr uint32_t kFull = kTabVec / kThreads;          // staging rounds every lane takes part in
+    constexpr uint32_t kTail = kTabVec - kFull * kThreads;  // pieces of the last, partial round
+    const u32x4* const tsrc = reinterpret_cast<const u32x4*>(p.tables);
+    u32x4* const tdst = reinterpret_cast<u32x4*>(s_tab);
+    u32x4 stage[kFull];
+#pragma unroll
+    for (uint32_t k = 0; k < kFull; ++k) stage[k] = tsrc[tid + k * kThreads];
+    u32x4 stage_tail = {0, 0, 0, 0};
+    if (kTail && tid < kTail) stage_tail = tsrc[kFull * kThreads + tid];
+    const Meta m0 = uniform_meta(m_first);
+    const Raw r0 = load_raw(p, m0, lane);
+    Meta m_next = load_meta(p, min_u64(u + stride, last_u));
+#pragma unroll
+    for (uint32_t k = 0; k < kFull; ++k) tdst[tid + k * kThreads] = stage[k];
+    if (kTail && tid < kTail) tdst[kFull * kThreads + tid] = stage_tail;
     {
-        const Meta m = uniform_meta(load_meta(p, u));
-        const Raw r = load_raw(p, m, lane);
-        m_next = load_meta(p, min_u64(u + stride, last_u));
-        cur = make_unit(r, m, lane);
-        m_next = uniform_meta(m_next);
+        const uint4* src = reinterpret_cast<const uint4*>(p.tables) + kTabVec;
+        for (uint32_t i = tid; i < (p.l2_cap << kL2Bits) / 8; i += kThreads)
+            reinterpret_cast<uint4*>(s_l2)[i] = src[i];
     }
+    __syncthreads();
+    if (!active) return;
+    LongTables lt;
+    lt.count = s_long;
+    lt.first = s_long + 32;
+    lt.base = s_long + 64;
+    lt.sorted = reinterpret_cast<const uint8_t*>(s_long + 96);
+    lt.l2 = s_l2;
+    lt.l2_first = __builtin_amdgcn_readfirstlane(s_long[160]);
+    lt.l2_n = min(__builtin_amdgcn_readfirstlane(s_long[161]), p.l2_cap);
+
+    Unit cur = make_unit(r0, m0, lane);
+    m_next = uniform_meta(m_next);
 
     for (;;) {
         const uint64_t un = u + stride;

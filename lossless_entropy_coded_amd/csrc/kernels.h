@@ -11,7 +11,6 @@ namespace wc {
 constexpr uint32_t kWaveLanes = 64;        // lanes of a wavefront
 constexpr uint32_t kChunksPerLane = 2;     // each lane decodes two adjacent 64-bit chunks
 constexpr uint32_t kGroupChunks = kWaveLanes * kChunksPerLane;   // chunks per group G: one wave's unit
-constexpr uint32_t kXcds = 8;              // accelerator dies; workgroup b runs on die b mod 8
 constexpr uint32_t kSingleBits = 12;       // width of the build-time single-codeword table
 constexpr uint32_t kEbufSlack = 3;         // bytes a chain may write past its range (then rewritten)
 constexpr uint32_t kHeadBytes = 3;         // leading bytes of a chain that a left neighbour may overwrite

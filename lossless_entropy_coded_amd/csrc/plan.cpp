@@ -25,9 +25,9 @@ struct wc_plan_s {
     wc::Header h;
     std::vector<uint64_t> tensor_offsets, tensor_numels;
     uint64_t max_group_elems = 0;   // elements of the largest group (one wave's unit)
-    uint32_t count_bits = 11;    // index width of the codeword-start table
+    uint32_t count_bits = 12;    // index width of the codeword-start table
     uint32_t decode_bits = 11;   // index width of the multi-codeword table
-    uint32_t waves = 8;          // wavefronts per workgroup
+    uint32_t waves = 4;          // wavefronts per workgroup
     uint32_t grid = 0;
     uint32_t lds_bytes = 0;
     uint32_t ebuf_bytes = 0;
@@ -194,14 +194,14 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         return st;
     }
     p->device = hip_device;
-    p->count_bits = env_u32("WC_COUNT_BITS", 11);
+    p->count_bits = env_u32("WC_COUNT_BITS", 12);
     p->decode_bits = env_u32("WC_DECODE_BITS", 11);
     if (!wc::supported_table_bits(p->count_bits, p->decode_bits)) {
-        p->count_bits = 11;
+        p->count_bits = 12;
         p->decode_bits = 11;
     }
-    p->waves = env_u32("WC_WAVES", 8);
-    if (!wc::supported_waves(p->waves)) p->waves = 8;
+    p->waves = env_u32("WC_WAVES", 4);
+    if (!wc::supported_waves(p->waves)) p->waves = 4;
     // each wave's staging of one group's exponents: a chain may write
     // kEbufSlack bytes past the end, and the merge reads whole blocks
     p->ebuf_bytes =
@@ -254,16 +254,15 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         delete p;
         return WC_ERR_UNSUPPORTED;
     }
-    // One persistent workgroup per resident slot, a multiple of the die count
-    // (so that each die takes a contiguous slab of groups), and no more
-    // workgroups than there are groups to give their waves.
+    // One persistent workgroup per resident slot (all of them: the decode is
+    // bound by memory throughput, which every extra wave helps more than an
+    // even last round of groups would), and no more workgroups than there
+    // are groups to give their waves.
     uint64_t want = (uint64_t)n_cu * (uint64_t)per_cu;
     uint32_t forced = env_u32("WC_GRID", 0);
     if (forced) want = forced;
     const uint64_t need = std::max<uint64_t>(1, wc::div_up(p->h.n_groups, p->waves));
-    want = std::min(want, need);
-    if (want >= wc::kXcds) want -= want % wc::kXcds;
-    p->grid = (uint32_t)std::max<uint64_t>(1, want);
+    p->grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(want, need));
 
     const size_t tbytes = (size_t)wc::table_words(p->count_bits, p->decode_bits) * 4;
     if (hipMalloc(reinterpret_cast<void**>(&p->d_tables), tbytes) != hipSuccess) {
