@@ -6,31 +6,35 @@
 // Float", abstract): (i) the big code lookup is split into compact tables
 // that live in on-chip memory (here: LDS of each workgroup); (ii) a two-phase
 // kernel coordinates where each thread reads and writes through small
-// auxiliary variables (here: a per-chunk bit offset `gap` and a per-group
-// first output index `group_start`); (iii) a whole transformer block is
-// decoded by one launch (here: every group of a multi-tensor container).
+// auxiliary variables (here: a per-chunk bit offset `gap` and a group table
+// of first elements and their stream bits); (iii) a whole transformer block
+// is decoded by one launch (here: every group of a multi-tensor container).
 //
-// Work decomposition on CDNA4: a workgroup of 256 lanes (4 wave64s) owns two
-// adjacent groups (512 chunks of 64 stream bits, one contiguous output range);
-// lane t owns chunks 2t and 2t+1 of that range and decodes them as two
-// independent chains, so two table lookups are in flight per lane.
-//   phase 1  each chain counts the codewords that START in its chunk, several
-//            per lookup of a codeword-start table;
-//   scan     wave64 inclusive scan with DPP row shifts and row broadcasts,
-//            then across the 4 waves through LDS -> each lane's first output;
+// Work decomposition on CDNA4: one wave64 decodes one group (at most 128
+// chunks of 64 stream bits, at most 4096 elements, output starting on a
+// 128-element boundary); lane t owns the group's chunks c0 + 2t and c0 + 2t + 1
+// and decodes them as two independent chains, so two table lookups are in
+// flight per lane.  Waves never wait for each other after the table staging.
+//   phase 1  each chain counts the codewords that START in its part of the
+//            group's bits, several per lookup of a codeword-start table;
+//   scan     wave64 inclusive scan with DPP row shifts and row broadcasts ->
+//            each chain's first output inside the group;
 //   phase 2  each chain decodes its codewords again, up to four per lookup of
-//            a multi-codeword table, and stages the exponent bytes in LDS at
-//            their final place (four byte stores per lookup; unaligned dword
-//            LDS stores stall on CDNA4).  Bytes written past a chain's range
-//            land on the next chain's first three bytes, which that chain
-//            keeps aside and rewrites after a barrier; writes of a finished
-//            chain go to a per-lane dummy slot;
-//   merge    the workgroup joins the sign+mantissa bytes (prefetched while
-//            the phases run) with the staged exponents in integer registers,
-//            8 elements per lane and step, and writes bf16 with 16-byte stores
-//            that are contiguous across the lanes of a wave.
-// Workgroups are persistent: each stages the tables once and loops over its
-// units, loading the next unit's chunks while it works on the current one.
+//            a multi-codeword table, and stages the exponent bytes in the
+//            wave's LDS buffer at their final place (four byte stores per
+//            lookup; unaligned dword LDS stores stall on CDNA4).  Bytes
+//            written past a chain's range land on the next chain's first
+//            three bytes, which that chain keeps aside and rewrites once the
+//            whole wave has left the loop; writes of a finished chain go to a
+//            per-lane dummy slot;
+//   merge    the wave joins the sign+mantissa bytes (prefetched while the
+//            phases run) with the staged exponents in integer registers, 8
+//            elements per lane and step, and writes bf16 with 16-byte stores
+//            that are contiguous across the lanes: whole cache lines, none of
+//            them shared with another group.
+// Workgroups are persistent: each stages the tables once and its waves loop
+// over their groups, loading the next group's chunks while they work on the
+// current one.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
