@@ -70,6 +70,9 @@ def parse_args():
     ap.add_argument("--workload", default="block_8b",
                     help="synthetic workload (default: block_8b, the 8B-shape transformer block)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--e2e", action="store_true",
+                    help="70B-shape block end to end: decode + batch-1 GEMVs against GEMVs on resident "
+                         "uncompressed weights (prints its own JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device copy instead (for scaling HBM counters)")
     return ap.parse_args()
@@ -130,6 +133,95 @@ def copy_rate(torch, nbytes, reps=20):
     return 2 * half / (ts[len(ts) // 2] * 1e-3) / 1e9
 
 
+def _timed(torch, stream, fn, steps):
+    """Milliseconds per call of fn over `steps` back-to-back calls (HIP events on `stream`)."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for k in range(steps):
+        fn(k)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def end_to_end(args):
+    """The 70B-shape block: decode the whole block and run a batch-1 bf16 GEMV
+    over each of its 7 matrices (arm A), against the same 7 GEMVs on resident
+    uncompressed weights (arm B).  Both arms run the same GEMV kernel, so their
+    outputs must be bit-identical; that is checked on the timed outputs."""
+    import numpy as np
+    import torch
+    from lossless_entropy_coded_amd import wc
+    from lossless_entropy_coded_amd.synth import gemv_input, make_workload
+
+    name = args.workload if args.workload != "block_8b" else "block_70b"
+    wl = make_workload(name)
+    blob = wc.encode_host(wl.tensors())
+    plan = wc.Plan(blob, device=0)
+    n = wl.n
+    mats = [(k, s[0], s[1]) for k, s in enumerate(wl.shapes) if len(s) == 2]
+    copies = 2
+    owners, blobs, outs, origs = [], [], [], []
+    for _ in range(copies):
+        own, view = aligned_device_copy(torch, blob)
+        owners.append(own)
+        blobs.append(view)
+        outs.append(torch.empty(n, dtype=torch.int16, device="cuda"))
+        origs.append(torch.from_numpy(wl.bits.view(np.int16)).cuda())
+    xs = {c: torch.from_numpy(gemv_input(c).view(np.int16)).cuda() for _, _, c in mats}
+    ya = [torch.empty(r, dtype=torch.float32, device="cuda") for _, r, _ in mats]
+    yb = [torch.empty(r, dtype=torch.float32, device="cuda") for _, r, _ in mats]
+    stream = torch.cuda.current_stream()
+
+    def gemvs(src, ys):
+        for j, (k, r, c) in enumerate(mats):
+            off = plan.tensor_offsets[k]
+            wc.gemv_bf16_async(src[off:off + r * c], r, c, xs[c], ys[j], stream)
+
+    def arm_a(k):
+        wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
+        gemvs(outs[k % copies], ya)
+
+    def arm_b(k):
+        gemvs(origs[k % copies], yb)
+
+    def decode_only(k):
+        wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
+
+    _timed(torch, stream, arm_a, max(40, args.warmup))          # settle clocks, warm up both arms
+    _timed(torch, stream, arm_b, max(40, args.warmup))
+    steps = args.steps
+    ms_a = _timed(torch, stream, arm_a, steps)
+    ms_b = _timed(torch, stream, arm_b, steps)
+    ms_dec = _timed(torch, stream, decode_only, steps)
+    identical = all(torch.equal(a.view(torch.int32), b.view(torch.int32)) for a, b in zip(ya, yb))
+    exact = torch.equal(outs[(steps - 1) % copies], origs[0])
+    if not (identical and exact):
+        print("bench.py --e2e: decoded GEMV outputs differ from the uncompressed ones", file=sys.stderr)
+        sys.exit(3)
+    weight_bytes = 2 * sum(r * c for _, r, c in mats)
+    line = {
+        "metric": "end-to-end batch-1 bf16 GEMV over a 70B-shape block: decode + GEMV vs GEMV on uncompressed weights",
+        "value": round(ms_a, 4), "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": max(40, args.warmup),
+        "higher_is_better": False, "vs_baseline": None, "dtype": "bf16 in, fp32 accumulate",
+        "data": "synthetic: seeded bf16 weights (70B-block shapes, N(0, 0.015)), x ~ N(0, 1) in bf16",
+        "config": {"workload": f"{name}: decode of the whole block, then q,k,v,o,gate,up,down GEMVs "
+                               f"(x length = each matrix's in-dimension)",
+                   "n_elems": n, "container_bytes": int(blob.size), "weight_bytes": weight_bytes},
+        "arm_a_decode_plus_gemv_ms": round(ms_a, 4),
+        "arm_b_uncompressed_gemv_ms": round(ms_b, 4),
+        "decode_only_ms": round(ms_dec, 4),
+        "ratio_a_over_b": round(ms_a / ms_b, 3),
+        "gemv_weight_GBps": round(weight_bytes / (ms_b * 1e-3) / 1e9, 1),
+        "decode_roofline_frac": round((blob.size + 2 * n) / (ms_dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "outputs_bit_identical": identical,
+    }
+    print(json.dumps(line), flush=True)
+    plan.close()
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -145,6 +237,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration(args)
+        return
+    if args.e2e:
+        end_to_end(args)
         return
 
     from lossless_entropy_coded_amd import wc

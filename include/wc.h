@@ -155,6 +155,25 @@ int wc_plan_stats(const wc_plan_t* plan, uint64_t* container_bytes, uint64_t* st
  */
 int wc_decode_async(const wc_plan_t* plan, const void* blob_dev, uint16_t* out_dev, void* stream);
 
+/* ---- consumer of decoded weights ------------------------------------------ */
+/*
+ * wc_gemv_bf16_async -- y = W x for a batch-1 input: the compute kernel that
+ * reads decoded weights (the pages decode weights on demand before the
+ * inference kernels use them: DFloat11 abstract; LazyWeights review, "Truck
+ * packing").  One launch on `stream`.
+ *   W     device pointer, rows x cols bf16 bit patterns, row-major, 16-byte
+ *         aligned (a tensor view of wc_decode_async's output qualifies when
+ *         its element offset is a multiple of 8);
+ *   x     device pointer, cols bf16, 16-byte aligned;
+ *   y     device pointer, rows float32, written (caller-owned).
+ * cols must be a positive multiple of 8.  Accumulation is fp32 with fused
+ * multiply-adds in a fixed order, so y is a deterministic function of the
+ * bits of W and x.  rows == 0 is a no-op.  Returns WC_ERR_INVALID_ARG for bad
+ * sizes or alignment, WC_ERR_HIP if the launch fails.
+ */
+int wc_gemv_bf16_async(const uint16_t* W, uint32_t rows, uint32_t cols, const uint16_t* x, float* y,
+                       void* stream);
+
 /* Destroy a plan and its device tables (NULL is ignored).  Pending decodes
  * that use the plan must have completed. */
 void wc_plan_destroy(wc_plan_t* plan);

@@ -27,6 +27,7 @@ import numpy as np
 
 __all__ = [
     "f32_to_bf16_rne",
+    "gemv_input",
     "Workload",
     "WORKLOADS",
     "make_workload",
@@ -148,6 +149,15 @@ def _heavy_tail(rng, spec: TensorSpec) -> np.ndarray:
     mant = rng.integers(1, 128, size=n_sub, dtype=np.uint16)
     bits[sub_idx] = sign | mant          # exponent field 0, mantissa 1..127
     return bits
+
+
+def gemv_input(cols: int, seed: int = 4) -> np.ndarray:
+    """The batch-1 input of a GEMV over a block's matrix with `cols` columns:
+    x ~ N(0, 1) in float32, rounded to bf16 (RNE); drawn from
+    ``numpy.random.default_rng([seed, cols])`` so that every in-dimension has
+    its own fixed vector."""
+    rng = np.random.default_rng([seed, cols])
+    return f32_to_bf16_rne(rng.standard_normal(cols, dtype=np.float32))
 
 
 def make_workload(name: str, scale_rows: int | None = None) -> Workload:

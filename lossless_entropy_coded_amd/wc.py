@@ -50,6 +50,9 @@ _lib.wc_plan_stats.argtypes = [ctypes.c_void_p, _u64p, _u64p, _u64p, _u32p, _u32
 _lib.wc_plan_stats.restype = ctypes.c_int
 _lib.wc_decode_async.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
 _lib.wc_decode_async.restype = ctypes.c_int
+_lib.wc_gemv_bf16_async.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+_lib.wc_gemv_bf16_async.restype = ctypes.c_int
 _lib.wc_plan_destroy.argtypes = [ctypes.c_void_p]
 _lib.wc_plan_destroy.restype = None
 _lib.wc_status_str.argtypes = [ctypes.c_int]
@@ -81,7 +84,7 @@ GROUP_ALIGN = 128
 GROUP_MAX_ELEMS = 4096
 
 EXPORTED = ("wc_encode_host", "wc_free_host", "wc_plan", "wc_plan_info", "wc_plan_stats",
-            "wc_decode_async", "wc_plan_destroy", "wc_status_str")
+            "wc_decode_async", "wc_gemv_bf16_async", "wc_plan_destroy", "wc_status_str")
 
 
 class WCError(RuntimeError):
@@ -206,6 +209,24 @@ def decode_async(plan: Plan, blob_dev, out_dev, stream=None) -> None:
         stream = stream.cuda_stream
     _check(_lib.wc_decode_async(plan.handle, ctypes.c_void_p(_ptr(blob_dev)), ctypes.c_void_p(_ptr(out_dev)),
                                 ctypes.c_void_p(int(stream))), "wc_decode_async")
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+    if hasattr(stream, "cuda_stream"):
+        return int(stream.cuda_stream)
+    return int(stream)
+
+
+def gemv_bf16_async(W_dev, rows: int, cols: int, x_dev, y_dev, stream=None) -> None:
+    """wc_gemv_bf16_async: y = W x (bf16 W rows x cols row-major, bf16 x, fp32 y), one launch.
+
+    W_dev / x_dev / y_dev: torch device tensors (or raw device pointers)."""
+    _check(_lib.wc_gemv_bf16_async(ctypes.c_void_p(_ptr(W_dev)), int(rows), int(cols), ctypes.c_void_p(_ptr(x_dev)),
+                                   ctypes.c_void_p(_ptr(y_dev)), ctypes.c_void_p(_stream_handle(stream))),
+           "wc_gemv_bf16_async")
 
 
 def exported_symbols():

@@ -94,6 +94,8 @@ def lib():
                                  ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(u8p), u64p]
         L.orc_decode.argtypes = [u8p, ctypes.c_uint64, u16p, ctypes.c_uint64, ctypes.POINTER(Report)]
         L.orc_header.argtypes = [u8p, ctypes.c_uint64, ctypes.POINTER(Report)]
+        L.orc_gemv_bf16.argtypes = [u16p, ctypes.c_uint64, ctypes.c_uint64, u16p,
+                                    ctypes.POINTER(ctypes.c_double)]
         L.orc_free.argtypes = [ctypes.c_void_p]
         L.orc_free.restype = None
         _lib = L
@@ -182,6 +184,20 @@ def encode(w: np.ndarray, numels=None, max_code_len: int = 24, chunks_per_group:
     finally:
         lib().orc_free(out)
     return blob
+
+
+def gemv_bf16(W: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """y = W x in float64 for bf16 bit patterns W (rows x cols, uint16) and x (cols)."""
+    W = np.ascontiguousarray(W, dtype=np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.uint16).reshape(-1)
+    rows, cols = W.shape
+    assert x.size == cols
+    y = np.zeros(rows, np.float64)
+    st = lib().orc_gemv_bf16(_p(W, ctypes.c_uint16), rows, cols, _p(x, ctypes.c_uint16),
+                             _p(y, ctypes.c_double))
+    if st:
+        raise OracleError(st, "gemv_bf16")
+    return y
 
 
 def header(blob: np.ndarray) -> dict:

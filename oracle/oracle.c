@@ -647,4 +647,28 @@ int orc_decode(const uint8_t* blob, uint64_t bytes, uint16_t* out, uint64_t out_
     return ORC_OK;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Batch-1 matrix-vector product over bf16 operands, exact in double:       */
+/* the consumer of decoded weights [DF11 abstract: inference kernels read   */
+/* the decompressed weights; LW "Truck packing": unpacked right before use].*/
+/* A bf16 bit pattern b is the float32 whose bits are b << 16.  Products    */
+/* and sums are taken in double, serially, column by column.                */
+/* ------------------------------------------------------------------------ */
+static double bf16_value(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+int orc_gemv_bf16(const uint16_t* W, uint64_t rows, uint64_t cols, const uint16_t* x, double* y) {
+    if ((rows && cols && (!W || !x)) || (rows && !y)) return ORC_E_ARG;
+    for (uint64_t r = 0; r < rows; ++r) {
+        double acc = 0.0;
+        for (uint64_t c = 0; c < cols; ++c) acc += bf16_value(W[r * cols + c]) * bf16_value(x[c]);
+        y[r] = acc;
+    }
+    return ORC_OK;
+}
+
 void orc_free(void* p) { free(p); }

@@ -105,6 +105,11 @@ int orc_decode(const uint8_t* blob, uint64_t blob_bytes, uint16_t* out, uint64_t
  * ones are zeroed). */
 int orc_header(const uint8_t* blob, uint64_t blob_bytes, orc_report* rep);
 
+/* y[r] = sum over c of W[r][c] * x[c] for row-major bf16 W (rows x cols) and
+ * bf16 x, in double (each bf16 value is exact in double; the sum is serial in
+ * column order).  The consumer of decoded weights, for GEMV checks. */
+int orc_gemv_bf16(const uint16_t* W, uint64_t rows, uint64_t cols, const uint16_t* x, double* y);
+
 void orc_free(void* p);
 
 #ifdef __cplusplus

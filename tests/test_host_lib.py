@@ -25,7 +25,7 @@ def wc():
 def test_exports_every_declared_symbol(wc):
     with open(os.path.join(ROOT, "include", "wc.h")) as f:
         text = f.read()
-    declared = set(re.findall(r"^\s*(?:int|void|const char\*)\s+(wc_[a-z_]+)\s*\(", text, re.M))
+    declared = set(re.findall(r"^\s*(?:int|void|const char\*)\s+(wc_[a-z0-9_]+)\s*\(", text, re.M))
     assert declared == set(wc.EXPORTED)
     for name in declared:
         assert hasattr(wc._lib, name), name
@@ -216,3 +216,18 @@ def test_plan_rejects_random_corruption_without_crashing(wc):
         b[k] ^= np.uint8(1 << int(rng.integers(0, 8)))
         st = _plan_status(wc, b)
         assert st <= 0
+
+
+def test_gemv_argument_checks_without_device(wc):
+    """Size and alignment checks of wc_gemv_bf16_async return before any HIP call."""
+    import ctypes
+    fake = 1 << 20                                    # aligned, never dereferenced
+    call = wc._lib.wc_gemv_bf16_async
+    vp = ctypes.c_void_p
+    assert call(vp(fake), 0, 8, vp(fake), vp(fake), vp(0)) == wc.WC_OK                # rows == 0: no-op
+    assert call(vp(fake), 4, 7, vp(fake), vp(fake), vp(0)) == wc.WC_ERR_INVALID_ARG   # cols % 8
+    assert call(vp(fake), 4, 0, vp(fake), vp(fake), vp(0)) == wc.WC_ERR_INVALID_ARG
+    assert call(vp(fake + 8), 4, 8, vp(fake), vp(fake), vp(0)) == wc.WC_ERR_INVALID_ARG
+    assert call(vp(fake), 4, 8, vp(fake + 2), vp(fake), vp(0)) == wc.WC_ERR_INVALID_ARG
+    assert call(vp(fake), 4, 8, vp(fake), vp(fake + 2), vp(0)) == wc.WC_ERR_INVALID_ARG
+    assert call(vp(0), 4, 8, vp(fake), vp(fake), vp(0)) == wc.WC_ERR_INVALID_ARG

@@ -367,3 +367,39 @@ def test_oracle_rejects_corruption(oracle_lib):
         st = oracle_lib.decode_status(b)
         if st == 0:
             assert not np.array_equal(oracle_lib.decode(b), wl.bits)
+
+
+# --------------------------------------------------------------------------
+# the GEMV reference (consumer of decoded weights)
+# --------------------------------------------------------------------------
+def test_gemv_bf16_values_of_every_pattern(oracle_lib):
+    """One column, x = 1.0: y is the value of each bf16 pattern, which numpy
+    gives as the float32 with those bits in the high half."""
+    w = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(-1, 1)
+    y = oracle_lib.gemv_bf16(w, np.array([0x3F80], np.uint16))
+    with np.errstate(invalid="ignore"):        # NaN patterns widen to NaN
+        ref = (w.reshape(-1).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(y, ref, equal_nan=True)
+
+
+def test_gemv_bf16_closed_forms(oracle_lib):
+    # identity selects x; a row of ones sums x exactly (small integers)
+    x = np.array([0x3F80, 0x4000, 0x4040, 0x4080, 0xBF80, 0x0000, 0x4100, 0x4120], np.uint16)   # 1 2 3 4 -1 0 8 10
+    eye = np.where(np.eye(8, dtype=bool), np.uint16(0x3F80), np.uint16(0)).astype(np.uint16)
+    assert oracle_lib.gemv_bf16(eye, x).tolist() == [1.0, 2.0, 3.0, 4.0, -1.0, 0.0, 8.0, 10.0]
+    ones = np.full((2, 8), 0x3F80, np.uint16)
+    assert oracle_lib.gemv_bf16(ones, x).tolist() == [27.0, 27.0]
+
+
+def test_gemv_bf16_against_numpy_float64(oracle_lib):
+    from lossless_entropy_coded_amd.synth import f32_to_bf16_rne
+    rng = np.random.default_rng(17)
+    for rows, cols in ((1, 8), (7, 40), (33, 1000)):
+        w = f32_to_bf16_rne(rng.standard_normal((rows, cols), dtype=np.float32) * np.float32(0.02))
+        x = f32_to_bf16_rne(rng.standard_normal(cols, dtype=np.float32))
+        wf = (w.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        got = oracle_lib.gemv_bf16(w, x)
+        ref = wf @ xf
+        scale = np.abs(wf) @ np.abs(xf)
+        assert np.all(np.abs(got - ref) <= 4 * cols * 2.0 ** -53 * scale)
