@@ -149,8 +149,11 @@ def _timed(torch, stream, fn, steps):
 def end_to_end(args):
     """The 70B-shape block: decode the whole block and run a batch-1 bf16 GEMV
     over each of its 7 matrices (arm A), against the same 7 GEMVs on resident
-    uncompressed weights (arm B).  Both arms run the same GEMV kernel, so their
-    outputs must be bit-identical; that is checked on the timed outputs."""
+    uncompressed weights (arm B), and the fused decode -> GEMV of each matrix,
+    which never writes the decoded weights (arm C).  Arms A and B run the same
+    GEMV kernel, so their outputs must be bit-identical; arm C sums in another
+    fixed order and must agree with B within both kernels' fp32 rounding
+    bounds.  Both are checked on the timed outputs."""
     import numpy as np
     import torch
     from lossless_entropy_coded_amd import wc
@@ -173,6 +176,8 @@ def end_to_end(args):
     xs = {c: torch.from_numpy(gemv_input(c).view(np.int16)).cuda() for _, _, c in mats}
     ya = [torch.empty(r, dtype=torch.float32, device="cuda") for _, r, _ in mats]
     yb = [torch.empty(r, dtype=torch.float32, device="cuda") for _, r, _ in mats]
+    yc = [torch.empty(r, dtype=torch.float32, device="cuda") for _, r, _ in mats]
+    work = torch.empty(2 * max(plan.tensor_groups(k)[1] for k, _, _ in mats), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
     def gemvs(src, ys):
@@ -190,16 +195,32 @@ def end_to_end(args):
     def decode_only(k):
         wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
 
+    def arm_c(k):
+        for j, (t, r, c) in enumerate(mats):
+            wc.decode_gemv_async(plan, blobs[k % copies], t, c, xs[c], yc[j], work, stream)
+
     _timed(torch, stream, arm_a, max(40, args.warmup))          # settle clocks, warm up both arms
     _timed(torch, stream, arm_b, max(40, args.warmup))
+    _timed(torch, stream, arm_c, max(40, args.warmup))
     steps = args.steps
     ms_a = _timed(torch, stream, arm_a, steps)
     ms_b = _timed(torch, stream, arm_b, steps)
+    ms_c = _timed(torch, stream, arm_c, steps)
     ms_dec = _timed(torch, stream, decode_only, steps)
     identical = all(torch.equal(a.view(torch.int32), b.view(torch.int32)) for a, b in zip(ya, yb))
     exact = torch.equal(outs[(steps - 1) % copies], origs[0])
-    if not (identical and exact):
-        print("bench.py --e2e: decoded GEMV outputs differ from the uncompressed ones", file=sys.stderr)
+    # arm C against arm B: |yc - yb| <= (fused bound + GEMV bound) * 2^-24 * sum |w x|,
+    # with sum |w x| from the GEMV kernel on the magnitudes (sign bits cleared)
+    fused_ok = True
+    for j, (t, r, c) in enumerate(mats):
+        off = plan.tensor_offsets[t]
+        mag = torch.empty(r, dtype=torch.float32, device="cuda")
+        wc.gemv_bf16_async(origs[0][off:off + r * c] & 0x7FFF, r, c, xs[c] & 0x7FFF, mag, stream)
+        terms = (64 + 6 + c // wc.GROUP_ALIGN + 2) + (c // 64 + 14)
+        fused_ok &= bool(((yc[j] - yb[j]).abs() <= 1.05 * terms * 2.0 ** -24 * mag).all().item())
+    if not (identical and exact and fused_ok):
+        print(f"bench.py --e2e: outputs disagree (A==B {identical}, decode exact {exact}, "
+              f"C~B {fused_ok})", file=sys.stderr)
         sys.exit(3)
     weight_bytes = 2 * sum(r * c for _, r, c in mats)
     line = {
@@ -212,11 +233,15 @@ def end_to_end(args):
                    "n_elems": n, "container_bytes": int(blob.size), "weight_bytes": weight_bytes},
         "arm_a_decode_plus_gemv_ms": round(ms_a, 4),
         "arm_b_uncompressed_gemv_ms": round(ms_b, 4),
+        "arm_c_fused_decode_gemv_ms": round(ms_c, 4),
         "decode_only_ms": round(ms_dec, 4),
         "ratio_a_over_b": round(ms_a / ms_b, 3),
+        "ratio_c_over_b": round(ms_c / ms_b, 3),
+        "fused_GBps": round((blob.size) / (ms_c * 1e-3) / 1e9, 1),
         "gemv_weight_GBps": round(weight_bytes / (ms_b * 1e-3) / 1e9, 1),
         "decode_roofline_frac": round((blob.size + 2 * n) / (ms_dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "outputs_bit_identical": identical,
+        "fused_within_bound": fused_ok,
     }
     print(json.dumps(line), flush=True)
     plan.close()

@@ -174,6 +174,42 @@ int wc_decode_async(const wc_plan_t* plan, const void* blob_dev, uint16_t* out_d
 int wc_gemv_bf16_async(const uint16_t* W, uint32_t rows, uint32_t cols, const uint16_t* x, float* y,
                        void* stream);
 
+/*
+ * wc_decode_gemv_async -- fused decode -> matrix-vector product: y = W x for
+ * one tensor of the container seen as a row-major matrix of numel/cols rows,
+ * without writing the decoded weights to memory (the decoded block goes
+ * straight to the consumer: Huff-LLM abstract keeps weights compressed up to
+ * the compute units; the DFloat11 abstract decodes right before the
+ * matrix-vector product of batch-1 inference).  Two launches on `stream`:
+ * the decode kernel over the groups covering the tensor, each wave leaving
+ * its group's fp32 partial dot products with x (the first row the group
+ * touches and the next) in work_dev, then a kernel adding each row's
+ * partials in group order.
+ *   blob_dev  as for wc_decode_async;
+ *   tensor    index of the tensor (< n_tensors);
+ *   cols      row length: a multiple of 8, at least the container's largest
+ *             group (group_max_elems always suffices), dividing the
+ *             tensor's numel; the tensor's element offset must be a
+ *             multiple of 8;
+ *   x_dev     device pointer, cols bf16, 16-byte aligned;
+ *   y_dev     device pointer, numel/cols float32, written, 4-byte aligned;
+ *   work_dev  device scratch of 2 floats per group covering the tensor
+ *             (wc_plan_tensor_groups; 8 * n_groups bytes always suffices),
+ *             8-byte aligned, caller-owned, overwritten.
+ * Each lane accumulates with fp32 fused multiply-adds in element order, the
+ * wave's 64 lane sums are added by a fixed butterfly and the group partials
+ * in group order, so y is a deterministic function of the bits of W and x.
+ * numel == 0 is a no-op.  Returns WC_ERR_INVALID_ARG for a bad tensor index,
+ * shape or alignment, WC_ERR_HIP if a launch fails.
+ */
+int wc_decode_gemv_async(const wc_plan_t* plan, const void* blob_dev, uint32_t tensor, uint32_t cols,
+                         const uint16_t* x_dev, float* y_dev, float* work_dev, void* stream);
+
+/* wc_plan_tensor_groups -- the groups [*first_group, *first_group + *n_groups)
+ * that hold tensor `tensor`'s elements (the first may start before the
+ * tensor and the last end after it).  Either output may be NULL. */
+int wc_plan_tensor_groups(const wc_plan_t* plan, uint32_t tensor, uint64_t* first_group, uint64_t* n_groups);
+
 /* Destroy a plan and its device tables (NULL is ignored).  Pending decodes
  * that use the plan must have completed. */
 void wc_plan_destroy(wc_plan_t* plan);

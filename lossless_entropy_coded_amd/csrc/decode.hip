@@ -299,7 +299,31 @@ __device__ __forceinline__ void put4(uint8_t*& q, const uint8_t* q_end, uint8_t*
     q += (e.x >> 8) & 0xFFu;
 }
 
-template <int KC, int KD, int W>
+// acc += 8 bf16 weights (four words, element k in bits 16(k & 1).. of word
+// k / 2) times 8 bf16 inputs, in element order, fp32 fused multiply-adds
+__device__ __forceinline__ float dot8_bf16(uint32_t o0, uint32_t o1, uint32_t o2, uint32_t o3, const uint4& xv,
+                                          float acc) {
+    const uint32_t w[4] = {o0, o1, o2, o3};
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        acc = __builtin_fmaf(__uint_as_float(w[i] << 16), __uint_as_float(xw[i] << 16), acc);
+        acc = __builtin_fmaf(__uint_as_float(w[i] & 0xFFFF0000u), __uint_as_float(xw[i] & 0xFFFF0000u), acc);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (uint32_t m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, (int)m, 64);
+    return v;
+}
+
+// kDot = false: decode the groups to bf16 in p.out.  kDot = true (fused
+// decode -> matrix-vector product): the decoded weights of each group never
+// leave the chip; the wave multiplies them by x and leaves its partial dot
+// products in p.work.
+template <int KC, int KD, int W, bool kDot>
 __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) {
     constexpr uint32_t kThreads = kWaveLanes * W;
     // decode tables, in the order of the plan's device buffer: codeword-start
@@ -336,9 +360,9 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) 
     // iteration issues the same vector memory instructions, so each wait
     // covers exactly the loads it needs.
     const uint64_t stride = (uint64_t)gridDim.x * W;
-    uint64_t u = (uint64_t)blockIdx.x * W + wave;
-    const uint64_t last_u = p.n_units - 1;
-    const bool active = u < p.n_units;
+    uint64_t u = p.u_begin + (uint64_t)blockIdx.x * W + wave;
+    const uint64_t last_u = p.u_end - 1;
+    const bool active = u < p.u_end;
 
     // Prologue: the first group's table entries, then every table load of the
     // workgroup's staging, are in flight together; the first group's stream
@@ -382,7 +406,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) 
 
     for (;;) {
         const uint64_t un = u + stride;
-        const bool more = un < p.n_units;
+        const bool more = un < p.u_end;
         const Raw nxt = load_raw(p, m_next, lane);
 
         // sign+mantissa bytes of the group (non-temporal: read once); block
@@ -526,6 +550,38 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) 
         // most kMergeSteps blocks per lane.  Only the container's very last
         // block can be partial; it is written after the loop.
         const uint32_t full = n_unit / kMergeElems;
+        if constexpr (kDot) {
+            // The matrix is the elements [t_lo, t_hi) in rows of `cols`
+            // (cols >= the group size and a multiple of 8, t_lo a multiple of
+            // 8): a block of 8 lies in one row, and the group touches at most
+            // the row of its first element inside the matrix and the next.
+            const uint64_t lo = A > p.t_lo ? A : p.t_lo;
+            const uint64_t row0 = (lo - p.t_lo) / p.cols;                 // wave-uniform
+            const uint64_t row1_start = p.t_lo + (row0 + 1) * p.cols;     // first element of the next row
+            const uint64_t row0_start = row1_start - p.cols;
+            float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+            for (uint32_t k = 0; k < kMergeSteps; ++k) {
+                const uint32_t blk = lane + k * kWaveLanes;
+                const uint64_t e = A + kMergeElems * blk;
+                if (blk < full && e >= p.t_lo && e < p.t_hi) {
+                    const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + kMergeElems * blk);
+                    uint32_t o0, o1, o2, o3;
+                    join4(smv[k].x, e2.x, o0, o1);
+                    join4(smv[k].y, e2.y, o2, o3);
+                    const bool second = e >= row1_start;
+                    const uint64_t col = e - (second ? row1_start : row0_start);
+                    const uint4 xv = *reinterpret_cast<const uint4*>(p.x + col);
+                    if (second)
+                        acc1 = dot8_bf16(o0, o1, o2, o3, xv, acc1);
+                    else
+                        acc0 = dot8_bf16(o0, o1, o2, o3, xv, acc0);
+                }
+            }
+            acc0 = wave_sum(acc0);
+            acc1 = wave_sum(acc1);
+            if (lane == 0) *reinterpret_cast<float2*>(p.work + 2 * (u - p.u_begin)) = make_float2(acc0, acc1);
+        } else {
 #pragma unroll
         for (uint32_t k = 0; k < kMergeSteps; ++k) {
             const uint32_t blk = lane + k * kWaveLanes;
@@ -542,6 +598,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) 
                 __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(outu + kMergeElems * blk));
             }
         }
+        }
 
         if (!more) break;
         wave_lds_order();   // the staging is rewritten by the next group
@@ -549,9 +606,10 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) 
         cur = next;
     }
 
-    // the container's last block, when it holds fewer than 8 elements
+    // the container's last block, when it holds fewer than 8 elements (a
+    // matrix for the fused product never ends in a partial block)
     const uint32_t full = cur.n / kMergeElems;
-    if (full * kMergeElems < cur.n && lane == 0) {
+    if (!kDot && full * kMergeElems < cur.n && lane == 0) {
         const uint32_t rel = kMergeElems * full;
         const uint2 s2 = load_nt8(p.sm + cur.A + rel);
         const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + rel);
@@ -667,16 +725,21 @@ __global__ __launch_bounds__(1024) void build_tables_kernel(CodeLens lens, uint3
 
 template <int KC, int KD, int W>
 struct Variant {
-    static hipError_t launch(const DecodeParams& p, uint32_t grid, uint32_t dyn, hipStream_t stream) {
-        hipLaunchKernelGGL((decode_kernel<KC, KD, W>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
+    static hipError_t launch(const DecodeParams& p, uint32_t grid, uint32_t dyn, bool dot, hipStream_t stream) {
+        if (dot)
+            hipLaunchKernelGGL((decode_kernel<KC, KD, W, true>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
+        else
+            hipLaunchKernelGGL((decode_kernel<KC, KD, W, false>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
         return hipGetLastError();
     }
     static int blocks_per_cu(uint32_t dyn) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<KC, KD, W>, kWaveLanes * W, dyn) !=
-            hipSuccess)
+        int n = 0, m = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<KC, KD, W, false>, kWaveLanes * W, dyn) !=
+                hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, decode_kernel<KC, KD, W, true>, kWaveLanes * W, dyn) !=
+                hipSuccess)
             return 0;
-        return n;
+        return n < m ? n : m;
     }
     static hipError_t build(const CodeLens& lens, uint32_t* d_tables, hipStream_t stream) {
         hipLaunchKernelGGL((build_tables_kernel<KC, KD>), dim3(1), dim3(1024), 0, stream, lens, d_tables);
@@ -725,12 +788,42 @@ hipError_t launch_build_tables(const CodeLens& lens, uint32_t count_bits, uint32
 }
 
 hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t decode_bits, uint32_t waves,
-                         uint32_t grid, hipStream_t stream) {
+                         uint32_t grid, bool dot, hipStream_t stream) {
     if (!supported_table_bits(count_bits, decode_bits) || !supported_waves(waves) || p.l2_cap > kL2Prefixes)
         return hipErrorInvalidValue;
     const uint32_t dyn = decode_dyn_lds_bytes(waves, p.ebuf_bytes, p.l2_cap);
     return dispatch(count_bits, decode_bits, waves,
-                    [&](auto v) { return decltype(v)::launch(p, grid, dyn, stream); });
+                    [&](auto v) { return decltype(v)::launch(p, grid, dyn, dot, stream); });
+}
+
+namespace {
+
+// y[r] = the partial dot products of the groups covering row r, added in
+// group order (a fixed order, so y is reproducible).  One lane per row; the
+// first group is found by binary search over the groups' first elements.
+__global__ __launch_bounds__(256) void gemv_rows_kernel(DecodeParams p, float* __restrict__ y, uint32_t rows) {
+    const uint32_t r = blockIdx.x * 256 + threadIdx.x;
+    if (r >= rows) return;
+    const uint64_t start = p.t_lo + (uint64_t)r * p.cols, end = start + p.cols;
+    uint64_t lo = p.u_begin, hi = p.u_end;   // the last group whose first element is <= start
+    while (hi - lo > 1) {
+        const uint64_t mid = lo + (hi - lo) / 2;
+        if (p.groups[2 * mid] <= start) lo = mid; else hi = mid;
+    }
+    float sum = 0.0f;
+    for (uint64_t g = lo; g < p.u_end && p.groups[2 * g] < end; ++g) {
+        const uint64_t first = p.groups[2 * g] > p.t_lo ? p.groups[2 * g] : p.t_lo;
+        const uint64_t row0 = (first - p.t_lo) / p.cols;
+        sum += p.work[2 * (g - p.u_begin) + (row0 == r ? 0 : 1)];
+    }
+    y[r] = sum;
+}
+
+}  // namespace
+
+hipError_t launch_gemv_rows(const DecodeParams& p, float* y, uint32_t rows, hipStream_t stream) {
+    hipLaunchKernelGGL(gemv_rows_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream, p, y, rows);
+    return hipGetLastError();
 }
 
 }  // namespace wc

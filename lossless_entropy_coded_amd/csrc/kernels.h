@@ -61,14 +61,24 @@ struct CodeLens {
 struct DecodeParams {
     const uint8_t* stream;
     const uint8_t* gap;
-    const uint64_t* groups;  // {first element, first bit} per group, n_units + 1 entries
+    const uint64_t* groups;  // {first element, first bit} per group, n_groups + 1 entries
     const uint8_t* sm;
-    uint16_t* out;
+    uint16_t* out;           // decoded bf16 (decode launches)
     const uint32_t* tables;
     uint64_t n_elems;
-    uint64_t n_units;        // wave units = groups
+    uint64_t u_begin;        // groups [u_begin, u_end) are decoded, one per wave
+    uint64_t u_end;
     uint32_t ebuf_bytes;     // exponent staging bytes per wave
     uint32_t l2_cap;         // long-code prefixes staged in LDS (0 .. kL2Prefixes)
+    // fused decode -> matrix-vector launches: the matrix is the elements
+    // [t_lo, t_hi) seen as rows of `cols`; each group leaves in work[2g] and
+    // work[2g + 1] its partial dot products with x for the first row it
+    // touches and the next one
+    const uint16_t* x;
+    float* work;
+    uint64_t t_lo, t_hi;
+    uint32_t cols;
+    uint32_t pad;
 };
 
 // Wavefronts per decode workgroup the kernels are built for.
@@ -88,9 +98,13 @@ int decode_blocks_per_cu(uint32_t count_bits, uint32_t decode_bits, uint32_t wav
 hipError_t launch_build_tables(const CodeLens& lens, uint32_t count_bits, uint32_t decode_bits, uint32_t* d_tables,
                                hipStream_t stream);
 
-// One launch decoding every group of a container (p.ebuf_bytes and p.l2_cap set
-// the dynamic LDS).
+// One launch decoding groups [p.u_begin, p.u_end) (p.ebuf_bytes and p.l2_cap set
+// the dynamic LDS): to bf16 in p.out, or (dot) to partial dot products in p.work.
 hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t decode_bits, uint32_t waves,
-                         uint32_t grid, hipStream_t stream);
+                         uint32_t grid, bool dot, hipStream_t stream);
+
+// One launch adding the partial dot products of the groups that cover each
+// row of the matrix [p.t_lo, p.t_hi) into y, in group order.
+hipError_t launch_gemv_rows(const DecodeParams& p, float* y, uint32_t rows, hipStream_t stream);
 
 }  // namespace wc

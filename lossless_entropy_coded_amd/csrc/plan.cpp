@@ -24,11 +24,13 @@ struct wc_plan_s {
     int device = 0;
     wc::Header h;
     std::vector<uint64_t> tensor_offsets, tensor_numels;
+    std::vector<uint64_t> tensor_g0, tensor_g1;   // groups [g0, g1) cover tensor k's elements
     uint64_t max_group_elems = 0;   // elements of the largest group (one wave's unit)
     uint32_t count_bits = 12;    // index width of the codeword-start table
     uint32_t decode_bits = 11;   // index width of the multi-codeword table
     uint32_t waves = 4;          // wavefronts per workgroup
     uint32_t grid = 0;
+    uint32_t slots = 0;          // co-resident workgroups on the device
     uint32_t lds_bytes = 0;
     uint32_t ebuf_bytes = 0;
     uint32_t l2_cap = 0;         // long-code prefixes whose second-level entries are staged in LDS
@@ -194,6 +196,30 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         return st;
     }
     p->device = hip_device;
+    // groups covering each tensor: from the last group starting at or before
+    // its first element to the last group starting before its end
+    {
+        const uint8_t* gt = blob_host + p->h.off_groups;
+        const uint64_t ng = p->h.n_groups;
+        auto first_elem = [&](uint64_t g) { return load_le<uint64_t>(gt + wc::kGroupEntryBytes * g); };
+        auto groups_le = [&](uint64_t e) {   // number of groups whose first element is <= e
+            uint64_t lo = 0, hi = ng;
+            while (lo < hi) {
+                const uint64_t mid = lo + (hi - lo) / 2;
+                if (first_elem(mid) <= e) lo = mid + 1; else hi = mid;
+            }
+            return lo;
+        };
+        const size_t nt = p->tensor_offsets.size();
+        p->tensor_g0.assign(nt, 0);
+        p->tensor_g1.assign(nt, 0);
+        for (size_t k = 0; k < nt; ++k) {
+            if (p->tensor_numels[k] == 0) continue;
+            const uint64_t a = p->tensor_offsets[k], e = a + p->tensor_numels[k];
+            p->tensor_g0[k] = groups_le(a) - 1;
+            p->tensor_g1[k] = groups_le(e - 1);
+        }
+    }
     p->count_bits = env_u32("WC_COUNT_BITS", 12);
     p->decode_bits = env_u32("WC_DECODE_BITS", 11);
     if (!wc::supported_table_bits(p->count_bits, p->decode_bits)) {
@@ -259,6 +285,7 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
     // even last round of groups would), and no more workgroups than there
     // are groups to give their waves.
     uint64_t want = (uint64_t)n_cu * (uint64_t)per_cu;
+    p->slots = (uint32_t)want;
     uint32_t forced = env_u32("WC_GRID", 0);
     if (forced) want = forced;
     const uint64_t need = std::max<uint64_t>(1, wc::div_up(p->h.n_groups, p->waves));
@@ -322,12 +349,62 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
     d.out = out_dev;
     d.tables = p->d_tables;
     d.n_elems = p->h.n_elems;
-    d.n_units = p->h.n_groups;
+    d.u_begin = 0;
+    d.u_end = p->h.n_groups;
     d.ebuf_bytes = p->ebuf_bytes;
     d.l2_cap = p->l2_cap;
-    hipError_t e =
-        wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, p->grid, static_cast<hipStream_t>(stream));
+    hipError_t e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, p->grid, false,
+                                     static_cast<hipStream_t>(stream));
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
+}
+
+extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, uint32_t tensor, uint32_t cols,
+                                    const uint16_t* x_dev, float* y_dev, float* work_dev, void* stream) {
+    if (!p || tensor >= p->h.n_tensors || cols == 0 || cols % wc::kMergeElems) return WC_ERR_INVALID_ARG;
+    const uint64_t off = p->tensor_offsets[tensor], numel = p->tensor_numels[tensor];
+    if (numel == 0) return WC_OK;
+    if (numel % cols || off % wc::kMergeElems || cols < p->max_group_elems || numel / cols > 0xFFFFFFFFull)
+        return WC_ERR_INVALID_ARG;
+    if (!blob_dev || !x_dev || !y_dev || !work_dev) return WC_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(blob_dev) & 255u) || (reinterpret_cast<uintptr_t>(x_dev) & 15u) ||
+        (reinterpret_cast<uintptr_t>(y_dev) & 3u) || (reinterpret_cast<uintptr_t>(work_dev) & 7u))
+        return WC_ERR_INVALID_ARG;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return WC_ERR_HIP;
+    if (cur != p->device) return WC_ERR_INVALID_ARG;
+    const uint8_t* b = static_cast<const uint8_t*>(blob_dev);
+    wc::DecodeParams d;
+    d.stream = b + p->h.off_stream;
+    d.gap = b + p->h.off_gap;
+    d.groups = reinterpret_cast<const uint64_t*>(b + p->h.off_groups);
+    d.sm = b + p->h.off_sm;
+    d.out = nullptr;
+    d.tables = p->d_tables;
+    d.n_elems = p->h.n_elems;
+    d.u_begin = p->tensor_g0[tensor];
+    d.u_end = p->tensor_g1[tensor];
+    d.ebuf_bytes = p->ebuf_bytes;
+    d.l2_cap = p->l2_cap;
+    d.x = x_dev;
+    d.work = work_dev;
+    d.t_lo = off;
+    d.t_hi = off + numel;
+    d.cols = cols;
+    d.pad = 0;
+    const uint64_t need = wc::div_up(d.u_end - d.u_begin, p->waves);
+    const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(p->slots, need));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, grid, true, s);
+    if (e == hipSuccess) e = wc::launch_gemv_rows(d, y_dev, (uint32_t)(numel / cols), s);
+    return e == hipSuccess ? WC_OK : WC_ERR_HIP;
+}
+
+extern "C" int wc_plan_tensor_groups(const wc_plan_t* p, uint32_t tensor, uint64_t* first_group,
+                                     uint64_t* n_groups) {
+    if (!p || tensor >= p->h.n_tensors) return WC_ERR_INVALID_ARG;
+    if (first_group) *first_group = p->tensor_g0[tensor];
+    if (n_groups) *n_groups = p->tensor_g1[tensor] - p->tensor_g0[tensor];
+    return WC_OK;
 }
 
 extern "C" void wc_plan_destroy(wc_plan_t* p) {
