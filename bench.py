@@ -149,8 +149,8 @@ def _timed(torch, stream, fn, steps):
 def end_to_end(args):
     """The 70B-shape block: decode the whole block and run a batch-1 bf16 GEMV
     over each of its 7 matrices (arm A), against the same 7 GEMVs on resident
-    uncompressed weights (arm B), and the fused decode -> GEMV of each matrix,
-    which never writes the decoded weights (arm C).  Arms A and B run the same
+    uncompressed weights (arm B), and the fused decode -> GEMV of all 7 matrices
+    in one call, which never writes the decoded weights (arm C).  Arms A and B run the same
     GEMV kernel, so their outputs must be bit-identical; arm C sums in another
     fixed order and must agree with B within both kernels' fp32 rounding
     bounds.  Both are checked on the timed outputs."""
@@ -177,7 +177,10 @@ def end_to_end(args):
     ya = [torch.empty(r, dtype=torch.float32, device="cuda") for _, r, _ in mats]
     yb = [torch.empty(r, dtype=torch.float32, device="cuda") for _, r, _ in mats]
     yc = [torch.empty(r, dtype=torch.float32, device="cuda") for _, r, _ in mats]
-    work = torch.empty(2 * max(plan.tensor_groups(k)[1] for k, _, _ in mats), dtype=torch.float32, device="cuda")
+    ops = [(k, c, xs[c], yc[j]) for j, (k, r, c) in enumerate(mats)]
+    work_bytes = wc.decode_gemv_work_bytes(plan, ops)
+    work = torch.empty(work_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    work = work[(-work.data_ptr()) % 256 // 4:]
     stream = torch.cuda.current_stream()
 
     def gemvs(src, ys):
@@ -196,8 +199,7 @@ def end_to_end(args):
         wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
 
     def arm_c(k):
-        for j, (t, r, c) in enumerate(mats):
-            wc.decode_gemv_async(plan, blobs[k % copies], t, c, xs[c], yc[j], work, stream)
+        wc.decode_gemv_async(plan, blobs[k % copies], ops, work, work_bytes, stream)
 
     _timed(torch, stream, arm_a, max(40, args.warmup))          # settle clocks, warm up both arms
     _timed(torch, stream, arm_b, max(40, args.warmup))
@@ -216,7 +218,7 @@ def end_to_end(args):
         off = plan.tensor_offsets[t]
         mag = torch.empty(r, dtype=torch.float32, device="cuda")
         wc.gemv_bf16_async(origs[0][off:off + r * c] & 0x7FFF, r, c, xs[c] & 0x7FFF, mag, stream)
-        terms = (64 + 6 + c // wc.GROUP_ALIGN + 2) + (c // 64 + 14)
+        terms = (12 + 8 + 6 + c // wc.GROUP_ALIGN + 2) + (c // 64 + 14)
         fused_ok &= bool(((yc[j] - yb[j]).abs() <= 1.05 * terms * 2.0 ** -24 * mag).all().item())
     if not (identical and exact and fused_ok):
         print(f"bench.py --e2e: outputs disagree (A==B {identical}, decode exact {exact}, "

@@ -175,40 +175,52 @@ int wc_gemv_bf16_async(const uint16_t* W, uint32_t rows, uint32_t cols, const ui
                        void* stream);
 
 /*
- * wc_decode_gemv_async -- fused decode -> matrix-vector product: y = W x for
- * one tensor of the container seen as a row-major matrix of numel/cols rows,
- * without writing the decoded weights to memory (the decoded block goes
- * straight to the consumer: Huff-LLM abstract keeps weights compressed up to
- * the compute units; the DFloat11 abstract decodes right before the
- * matrix-vector product of batch-1 inference).  Two launches on `stream`:
- * the decode kernel over the groups covering the tensor, each wave leaving
- * its group's fp32 partial dot products with x (the first row the group
- * touches and the next) in work_dev, then a kernel adding each row's
- * partials in group order.
- *   blob_dev  as for wc_decode_async;
- *   tensor    index of the tensor (< n_tensors);
- *   cols      row length: a multiple of 8, at least the container's largest
- *             group (group_max_elems always suffices), dividing the
- *             tensor's numel; the tensor's element offset must be a
- *             multiple of 8;
- *   x_dev     device pointer, cols bf16, 16-byte aligned;
- *   y_dev     device pointer, numel/cols float32, written, 4-byte aligned;
- *   work_dev  device scratch of 2 floats per group covering the tensor
- *             (wc_plan_tensor_groups; 8 * n_groups bytes always suffices),
- *             8-byte aligned, caller-owned, overwritten.
- * Each lane accumulates with fp32 fused multiply-adds in element order, the
- * wave's 64 lane sums are added by a fixed butterfly and the group partials
- * in group order, so y is a deterministic function of the bits of W and x.
- * numel == 0 is a no-op.  Returns WC_ERR_INVALID_ARG for a bad tensor index,
- * shape or alignment, WC_ERR_HIP if a launch fails.
+ * Fused decode -> matrix-vector products: y_k = W_k x_k for consecutive
+ * tensors W_k of the container, each seen as a row-major matrix, without
+ * writing the decoded weights to memory (the decoded block goes straight to
+ * its consumer: Huff-LLM abstract keeps weights compressed up to the compute
+ * units; the DFloat11 abstract decodes right before the matrix-vector
+ * products of batch-1 inference, one transformer block at a time).
  */
-int wc_decode_gemv_async(const wc_plan_t* plan, const void* blob_dev, uint32_t tensor, uint32_t cols,
-                         const uint16_t* x_dev, float* y_dev, float* work_dev, void* stream);
+typedef struct {
+    uint32_t tensor;     /* tensor index; operand i must be tensor ops[0].tensor + i     */
+    uint32_t cols;       /* row length: a multiple of 8, below 2^31, dividing the        */
+                         /* tensor's numel (which must be below 2^32) and at least the   */
+                         /* container's largest group (group_max_elems always suffices)  */
+    const uint16_t* x;   /* device, cols bf16, 16-byte aligned                           */
+    float* y;            /* device, numel / cols float32 (written), 4-byte aligned       */
+} wc_gemv_operand;
 
-/* wc_plan_tensor_groups -- the groups [*first_group, *first_group + *n_groups)
- * that hold tensor `tensor`'s elements (the first may start before the
- * tensor and the last end after it).  Either output may be NULL. */
-int wc_plan_tensor_groups(const wc_plan_t* plan, uint32_t tensor, uint64_t* first_group, uint64_t* n_groups);
+/*
+ * wc_decode_gemv_work_bytes -- size of the device work buffer that
+ * wc_decode_gemv_async needs for these operands (0 when every tensor is
+ * empty).  Validates the operands as wc_decode_gemv_async does, except the
+ * device pointers of empty tensors, which are never used.
+ */
+int wc_decode_gemv_work_bytes(const wc_plan_t* plan, const wc_gemv_operand* ops, uint32_t n_ops,
+                              uint64_t* work_bytes);
+
+/*
+ * wc_decode_gemv_async -- two launches on `stream`: one decode kernel over
+ * the groups covering the n_ops tensors (1..16 consecutive tensors of the
+ * container, the first at an element offset that is a multiple of 8), each
+ * wave leaving its group's fp32 partial dot products with x (for the first
+ * row the group touches and the next) in work_dev, then one kernel adding
+ * each row's partials in group order into its y.
+ *   blob_dev    as for wc_decode_async;
+ *   work_dev    device scratch of at least work_bytes = wc_decode_gemv_work_bytes(...)
+ *               bytes, 256-byte aligned, caller-owned, overwritten.
+ * Each 8-element block's products are summed in element-pair order by the
+ * hardware bf16 dot instruction (each step within 3 * 2^-24 of the sum of
+ * its addends' magnitudes), blocks are added to the lane's fp32 partial in
+ * order, a fixed butterfly adds the wave's 64 lanes and the rows add group
+ * partials in group order: y is a deterministic function of the bits of W
+ * and x.  Empty tensors are skipped (their y is not touched).  Returns
+ * WC_ERR_INVALID_ARG for bad operands, sizes or alignment, WC_ERR_HIP if a
+ * launch fails.
+ */
+int wc_decode_gemv_async(const wc_plan_t* plan, const void* blob_dev, const wc_gemv_operand* ops, uint32_t n_ops,
+                         void* work_dev, uint64_t work_bytes, void* stream);
 
 /* Destroy a plan and its device tables (NULL is ignored).  Pending decodes
  * that use the plan must have completed. */

@@ -299,24 +299,72 @@ __device__ __forceinline__ void put4(uint8_t*& q, const uint8_t* q_end, uint8_t*
     q += (e.x >> 8) & 0xFFu;
 }
 
-// acc += 8 bf16 weights (four words, element k in bits 16(k & 1).. of word
-// k / 2) times 8 bf16 inputs, in element order, fp32 fused multiply-adds
-__device__ __forceinline__ float dot8_bf16(uint32_t o0, uint32_t o1, uint32_t o2, uint32_t o3, const uint4& xv,
-                                          float acc) {
-    const uint32_t w[4] = {o0, o1, o2, o3};
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        acc = __builtin_fmaf(__uint_as_float(w[i] << 16), __uint_as_float(xw[i] << 16), acc);
-        acc = __builtin_fmaf(__uint_as_float(w[i] & 0xFFFF0000u), __uint_as_float(xw[i] & 0xFFFF0000u), acc);
-    }
-    return acc;
+// Dot product of 8 bf16 weights (four words, element k in bits 16(k & 1)..
+// of word k / 2) with 8 bf16 inputs in the same layout, in element-pair
+// order with v_dot2_f32_bf16.  The instruction adds two exact products to its
+// accumulator after aligning the three addends to the largest and dropping
+// the bits below 2^-24 of it, then rounds once, so each step errs by at most
+// 3 * 2^-24 times the sum of the addends' magnitudes; subnormals are kept.
+__device__ __forceinline__ float dot8_bf16(uint32_t o0, uint32_t o1, uint32_t o2, uint32_t o3, const uint4& xv) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    float d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, o0), __builtin_bit_cast(bf16x2, xv.x), 0.0f,
+                                              false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, o1), __builtin_bit_cast(bf16x2, xv.y), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, o2), __builtin_bit_cast(bf16x2, xv.z), d, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, o3), __builtin_bit_cast(bf16x2, xv.w), d, false);
+    return d;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (uint32_t m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, (int)m, 64);
     return v;
+}
+
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t magic, uint32_t shift) {
+    const uint32_t t = __umulhi(n, magic);
+    return (t + ((n - t) >> 1)) >> shift;
+}
+
+// Where one group's elements fall among the rows of the fused product: the
+// two rows it may touch, as element offsets relative to the group's first
+// element A.  Every field is wave-uniform.
+struct DotRows {
+    uint32_t lo_rel, hi_rel;    // elements [A + lo_rel, A + hi_rel) are multiplied
+    uint32_t r1_rel;            // first element of the second row (>= hi_rel: none)
+    int32_t off0, off1;         // column = relative offset + off0 (first row) or + off1 (second row)
+    const uint16_t* x0;
+    const uint16_t* x1;
+    uint32_t row0;              // global index of the first row
+    bool starts_row0;           // the group holds the first element of row0
+    bool starts_row1;           // the group holds the first element of row0 + 1
+    bool simple;                // every element of the group is multiplied, all in row0
+};
+
+// `mat` is the matrix of the wave's previous group (0 at first): a wave's
+// groups come in increasing order, so it only moves forward.
+__device__ __forceinline__ DotRows dot_rows(const DotParams& q, uint64_t A, uint32_t n, uint32_t& mat) {
+    DotRows d;
+    const uint64_t lo = A > q.bounds[0] ? A : q.bounds[0];
+    uint32_t k = mat;
+    while (k + 1 < q.n_mats && q.bounds[k + 1] <= lo) ++k;
+    mat = k;
+    const uint32_t cols = q.cols[k];
+    const uint32_t local = div_magic((uint32_t)(lo - q.bounds[k]), q.magic[k], q.shift[k]);
+    const uint64_t r0s = q.bounds[k] + (uint64_t)local * cols, r1s = r0s + cols;
+    const uint64_t end = min_u64(q.bounds[q.n_mats], A + n);
+    d.lo_rel = (uint32_t)(lo - A);
+    d.hi_rel = (uint32_t)(end - A);
+    d.r1_rel = (uint32_t)min_u64(r1s - A, 0xFFFFFFFFull);
+    d.off0 = (int32_t)((int64_t)A - (int64_t)r0s);
+    d.off1 = (int32_t)((int64_t)A - (int64_t)r1s);
+    d.x0 = q.x[k];
+    d.x1 = (r1s == q.bounds[k + 1] && k + 1 < q.n_mats) ? q.x[k + 1] : q.x[k];
+    d.row0 = (uint32_t)q.row_base[k] + local;
+    d.starts_row0 = r0s == lo;
+    d.starts_row1 = r1s < end;
+    d.simple = d.lo_rel == 0 && d.hi_rel == n && d.r1_rel >= n;
+    return d;
 }
 
 // kDot = false: decode the groups to bf16 in p.out.  kDot = true (fused
@@ -403,6 +451,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) 
 
     Unit cur = make_unit(r0, m0, lane);
     m_next = uniform_meta(m_next);
+    uint32_t dot_mat = 0;   // fused product: matrix of the wave's current group
 
     for (;;) {
         const uint64_t un = u + stride;
@@ -422,6 +471,34 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) 
 #pragma unroll
         for (uint32_t k = 0; k < kMergeSteps; ++k)
             smv[k] = load_nt8(smu + kMergeElems * min(lane + k * kWaveLanes, last_blk));
+        // fused product: the x entries of the group's blocks, loaded with the
+        // sm bytes so that they have arrived by the merge (blocks outside the
+        // multiplied range load x0[0..7], never used)
+        DotRows dr;
+        uint4 xv[kDot ? kMergeSteps : 1];
+        if constexpr (kDot) {
+            dr = dot_rows(p.dot, A, n_unit, dot_mat);
+            const uint32_t nblk = n_unit / kMergeElems;
+            if (dr.simple) {   // most groups: one row, all multiplied
+#pragma unroll
+                for (uint32_t k = 0; k < kMergeSteps; ++k) {
+                    const uint32_t rel = kMergeElems * (lane + k * kWaveLanes);
+                    const int32_t col = lane + k * kWaveLanes < nblk ? (int32_t)rel + dr.off0 : 0;
+                    xv[k] = *reinterpret_cast<const uint4*>(dr.x0 + col);
+                }
+            } else {
+#pragma unroll
+                for (uint32_t k = 0; k < kMergeSteps; ++k) {
+                    const uint32_t blk = lane + k * kWaveLanes;
+                    const uint32_t rel = kMergeElems * blk;
+                    const bool ok = blk < nblk && rel >= dr.lo_rel && rel < dr.hi_rel;
+                    const bool second = rel >= dr.r1_rel;
+                    const uint16_t* const xp = second ? dr.x1 : dr.x0;
+                    const int32_t col = ok ? (int32_t)rel + (second ? dr.off1 : dr.off0) : 0;
+                    xv[k] = *reinterpret_cast<const uint4*>(xp + col);
+                }
+            }
+        }
 
         const Meta m_after = load_meta(p, min_u64(un + stride, last_u));
 
@@ -551,36 +628,53 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) 
         // block can be partial; it is written after the loop.
         const uint32_t full = n_unit / kMergeElems;
         if constexpr (kDot) {
-            // The matrix is the elements [t_lo, t_hi) in rows of `cols`
-            // (cols >= the group size and a multiple of 8, t_lo a multiple of
-            // 8): a block of 8 lies in one row, and the group touches at most
-            // the row of its first element inside the matrix and the next.
-            const uint64_t lo = A > p.t_lo ? A : p.t_lo;
-            const uint64_t row0 = (lo - p.t_lo) / p.cols;                 // wave-uniform
-            const uint64_t row1_start = p.t_lo + (row0 + 1) * p.cols;     // first element of the next row
-            const uint64_t row0_start = row1_start - p.cols;
+            // A block of 8 lies in one row (row starts are multiples of 8).
+            // Each block's 8 products are summed by four dot2 steps, then
+            // added to the partial of its row.
             float acc0 = 0.0f, acc1 = 0.0f;
+            if (dr.simple) {
 #pragma unroll
-            for (uint32_t k = 0; k < kMergeSteps; ++k) {
-                const uint32_t blk = lane + k * kWaveLanes;
-                const uint64_t e = A + kMergeElems * blk;
-                if (blk < full && e >= p.t_lo && e < p.t_hi) {
-                    const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + kMergeElems * blk);
-                    uint32_t o0, o1, o2, o3;
-                    join4(smv[k].x, e2.x, o0, o1);
-                    join4(smv[k].y, e2.y, o2, o3);
-                    const bool second = e >= row1_start;
-                    const uint64_t col = e - (second ? row1_start : row0_start);
-                    const uint4 xv = *reinterpret_cast<const uint4*>(p.x + col);
-                    if (second)
-                        acc1 = dot8_bf16(o0, o1, o2, o3, xv, acc1);
-                    else
-                        acc0 = dot8_bf16(o0, o1, o2, o3, xv, acc0);
+                for (uint32_t k = 0; k < kMergeSteps; ++k) {
+                    const uint32_t blk = lane + k * kWaveLanes;
+                    if (blk < full) {
+                        const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + kMergeElems * blk);
+                        uint32_t o0, o1, o2, o3;
+                        join4(smv[k].x, e2.x, o0, o1);
+                        join4(smv[k].y, e2.y, o2, o3);
+                        acc0 += dot8_bf16(o0, o1, o2, o3, xv[k]);
+                    }
                 }
+                acc0 = wave_sum(acc0);
+            } else {
+#pragma unroll
+                for (uint32_t k = 0; k < kMergeSteps; ++k) {
+                    const uint32_t blk = lane + k * kWaveLanes;
+                    const uint32_t rel = kMergeElems * blk;
+                    if (blk < full && rel >= dr.lo_rel && rel < dr.hi_rel) {
+                        const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + rel);
+                        uint32_t o0, o1, o2, o3;
+                        join4(smv[k].x, e2.x, o0, o1);
+                        join4(smv[k].y, e2.y, o2, o3);
+                        const bool second = rel >= dr.r1_rel;
+                        const float d = dot8_bf16(o0, o1, o2, o3, xv[k]);
+                        acc0 += second ? 0.0f : d;
+                        acc1 += second ? d : 0.0f;
+                    }
+                }
+                acc0 = wave_sum(acc0);
+                acc1 = wave_sum(acc1);
             }
-            acc0 = wave_sum(acc0);
-            acc1 = wave_sum(acc1);
-            if (lane == 0) *reinterpret_cast<float2*>(p.work + 2 * (u - p.u_begin)) = make_float2(acc0, acc1);
+            if (lane == 0) {
+                const uint64_t g = u - p.u_begin;
+                *reinterpret_cast<float2*>(p.dot.part + 2 * g) = make_float2(acc0, acc1);
+                // each row's first group with that first row: the group holding
+                // the row's first element, or the next one when that group
+                // started in the row before
+                if (dr.starts_row0)
+                    p.dot.row_group[dr.row0] = (uint32_t)g;
+                else if (dr.starts_row1)
+                    p.dot.row_group[dr.row0 + 1] = (uint32_t)(g + 1);
+            }
         } else {
 #pragma unroll
         for (uint32_t k = 0; k < kMergeSteps; ++k) {
@@ -798,31 +892,27 @@ hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t de
 
 namespace {
 
-// y[r] = the partial dot products of the groups covering row r, added in
-// group order (a fixed order, so y is reproducible).  One lane per row; the
-// first group is found by binary search over the groups' first elements.
-__global__ __launch_bounds__(256) void gemv_rows_kernel(DecodeParams p, float* __restrict__ y, uint32_t rows) {
+// y of global row r = the second partial of the last group whose first row
+// is r - 1 (zero when that group ends before row r), then the first partials
+// of the groups whose first row is r, in group order: a fixed order, so y is
+// reproducible.  One lane per row.
+__global__ __launch_bounds__(256) void gemv_rows_kernel(DecodeParams p) {
+    const DotParams& q = p.dot;
     const uint32_t r = blockIdx.x * 256 + threadIdx.x;
-    if (r >= rows) return;
-    const uint64_t start = p.t_lo + (uint64_t)r * p.cols, end = start + p.cols;
-    uint64_t lo = p.u_begin, hi = p.u_end;   // the last group whose first element is <= start
-    while (hi - lo > 1) {
-        const uint64_t mid = lo + (hi - lo) / 2;
-        if (p.groups[2 * mid] <= start) lo = mid; else hi = mid;
-    }
-    float sum = 0.0f;
-    for (uint64_t g = lo; g < p.u_end && p.groups[2 * g] < end; ++g) {
-        const uint64_t first = p.groups[2 * g] > p.t_lo ? p.groups[2 * g] : p.t_lo;
-        const uint64_t row0 = (first - p.t_lo) / p.cols;
-        sum += p.work[2 * (g - p.u_begin) + (row0 == r ? 0 : 1)];
-    }
-    y[r] = sum;
+    if (r >= q.rows) return;
+    const uint32_t g0 = q.row_group[r];
+    const uint32_t g1 = r + 1 < q.rows ? q.row_group[r + 1] : (uint32_t)(p.u_end - p.u_begin);
+    float sum = r > 0 ? q.part[2 * (uint64_t)g0 - 1] : 0.0f;
+    for (uint32_t g = g0; g < g1; ++g) sum += q.part[2 * (uint64_t)g];
+    uint32_t k = 0;
+    for (uint32_t j = 1; j < q.n_mats; ++j) k = q.row_base[j] <= r ? j : k;
+    q.y[k][r - q.row_base[k]] = sum;
 }
 
 }  // namespace
 
-hipError_t launch_gemv_rows(const DecodeParams& p, float* y, uint32_t rows, hipStream_t stream) {
-    hipLaunchKernelGGL(gemv_rows_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream, p, y, rows);
+hipError_t launch_gemv_rows(const DecodeParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL(gemv_rows_kernel, dim3((p.dot.rows + 255) / 256), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

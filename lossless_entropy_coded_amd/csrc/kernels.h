@@ -58,6 +58,40 @@ struct CodeLens {
     uint8_t len[256];
 };
 
+// Fused decode -> matrix-vector products over consecutive matrices of a
+// container (one launch for all of them): the elements [bounds[0],
+// bounds[n_mats]) are the matrices back to back, matrix k in rows of cols[k]
+// starting at element bounds[k]; its rows are the global rows row_base[k] ..
+// Every cols[k] is a multiple of 8 and at least the largest group, so a group
+// touches at most two consecutive global rows: the row holding its first
+// element inside the range and the next.
+constexpr uint32_t kMaxDotMats = 16;
+
+// Division by an invariant divisor 1 < d < 2^31 through a multiply (the
+// round-up method of Granlund and Montgomery, "Division by invariant integers
+// using multiplication", PLDI 1994, section 4): with l = ceil(log2 d),
+// m = floor(2^32 (2^l - d) / d) + 1 and t = floor(m n / 2^32),
+// floor(n / d) = (t + ((n - t) >> 1)) >> (l - 1) for every n < 2^32.
+inline void div_magic_params(uint32_t d, uint32_t& magic, uint32_t& shift) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    magic = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+    shift = l - 1;
+}
+struct DotParams {
+    uint64_t bounds[kMaxDotMats + 1];
+    uint64_t row_base[kMaxDotMats + 1];   // row_base[n_mats] = total rows
+    const uint16_t* x[kMaxDotMats];       // cols[k] bf16 each, 16-byte aligned
+    float* y[kMaxDotMats];                // rows of matrix k, fp32
+    uint32_t cols[kMaxDotMats];           // < 2^31; every matrix holds < 2^32 elements
+    uint32_t magic[kMaxDotMats];          // e / cols[k] = div_magic(e, magic[k], shift[k]) for e < 2^32
+    uint32_t shift[kMaxDotMats];
+    uint32_t n_mats;
+    uint32_t rows;                        // total rows
+    float* part;        // per group g: part[2(g - u_begin)] for its first row, part[2(g - u_begin) + 1] for the next
+    uint32_t* row_group;  // per global row r: the first group (minus u_begin) whose first row is r
+};
+
 struct DecodeParams {
     const uint8_t* stream;
     const uint8_t* gap;
@@ -70,15 +104,7 @@ struct DecodeParams {
     uint64_t u_end;
     uint32_t ebuf_bytes;     // exponent staging bytes per wave
     uint32_t l2_cap;         // long-code prefixes staged in LDS (0 .. kL2Prefixes)
-    // fused decode -> matrix-vector launches: the matrix is the elements
-    // [t_lo, t_hi) seen as rows of `cols`; each group leaves in work[2g] and
-    // work[2g + 1] its partial dot products with x for the first row it
-    // touches and the next one
-    const uint16_t* x;
-    float* work;
-    uint64_t t_lo, t_hi;
-    uint32_t cols;
-    uint32_t pad;
+    DotParams dot;           // fused matrix-vector launches only
 };
 
 // Wavefronts per decode workgroup the kernels are built for.
@@ -103,8 +129,8 @@ hipError_t launch_build_tables(const CodeLens& lens, uint32_t count_bits, uint32
 hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t decode_bits, uint32_t waves,
                          uint32_t grid, bool dot, hipStream_t stream);
 
-// One launch adding the partial dot products of the groups that cover each
-// row of the matrix [p.t_lo, p.t_hi) into y, in group order.
-hipError_t launch_gemv_rows(const DecodeParams& p, float* y, uint32_t rows, hipStream_t stream);
+// One launch adding, for every global row of p.dot, the partial dot products
+// of the groups covering it, in group order, into the row's y.
+hipError_t launch_gemv_rows(const DecodeParams& p, hipStream_t stream);
 
 }  // namespace wc

@@ -358,22 +358,78 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
 }
 
-extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, uint32_t tensor, uint32_t cols,
-                                    const uint16_t* x_dev, float* y_dev, float* work_dev, void* stream) {
-    if (!p || tensor >= p->h.n_tensors || cols == 0 || cols % wc::kMergeElems) return WC_ERR_INVALID_ARG;
-    const uint64_t off = p->tensor_offsets[tensor], numel = p->tensor_numels[tensor];
-    if (numel == 0) return WC_OK;
-    if (numel % cols || off % wc::kMergeElems || cols < p->max_group_elems || numel / cols > 0xFFFFFFFFull)
-        return WC_ERR_INVALID_ARG;
-    if (!blob_dev || !x_dev || !y_dev || !work_dev) return WC_ERR_INVALID_ARG;
-    if ((reinterpret_cast<uintptr_t>(blob_dev) & 255u) || (reinterpret_cast<uintptr_t>(x_dev) & 15u) ||
-        (reinterpret_cast<uintptr_t>(y_dev) & 3u) || (reinterpret_cast<uintptr_t>(work_dev) & 7u))
+namespace {
+
+// The fused product's launch parameters for ops[0 .. n_ops): checks every
+// operand, drops empty matrices, and sizes the work buffer (the group
+// partials, then the per-row first groups, each 256-byte aligned).
+int prepare_gemv(const wc_plan_t* p, const wc_gemv_operand* ops, uint32_t n_ops, wc::DotParams& q,
+                 uint64_t& u_begin, uint64_t& u_end, uint64_t& work_bytes, uint64_t& rows_off) {
+    if (!p || !ops || n_ops == 0 || n_ops > wc::kMaxDotMats) return WC_ERR_INVALID_ARG;
+    std::memset(&q, 0, sizeof(q));
+    uint64_t rows = 0;
+    for (uint32_t i = 0; i < n_ops; ++i) {
+        const wc_gemv_operand& o = ops[i];
+        if (o.tensor >= p->h.n_tensors || o.tensor != ops[0].tensor + i) return WC_ERR_INVALID_ARG;
+        if (o.cols == 0 || o.cols % wc::kMergeElems || o.cols > 0x7FFFFFFFu) return WC_ERR_INVALID_ARG;
+        const uint64_t off = p->tensor_offsets[o.tensor], numel = p->tensor_numels[o.tensor];
+        if (numel == 0) continue;
+        if (numel % o.cols || off % wc::kMergeElems || o.cols < p->max_group_elems || numel > 0xFFFFFFFFull)
+            return WC_ERR_INVALID_ARG;
+        if (!o.x || !o.y || (reinterpret_cast<uintptr_t>(o.x) & 15u) || (reinterpret_cast<uintptr_t>(o.y) & 3u))
+            return WC_ERR_INVALID_ARG;
+        const uint32_t k = q.n_mats++;
+        if (k == 0) u_begin = p->tensor_g0[o.tensor];
+        u_end = p->tensor_g1[o.tensor];
+        q.bounds[k] = off;
+        q.bounds[k + 1] = off + numel;
+        q.row_base[k] = rows;
+        q.cols[k] = o.cols;
+        wc::div_magic_params(o.cols, q.magic[k], q.shift[k]);
+        q.x[k] = o.x;
+        q.y[k] = o.y;
+        rows += numel / o.cols;
+    }
+    q.row_base[q.n_mats] = rows;
+    if (rows > 0xFFFFFFFFull) return WC_ERR_INVALID_ARG;
+    q.rows = (uint32_t)rows;
+    if (q.n_mats == 0) {
+        u_begin = u_end = 0;
+        work_bytes = rows_off = 0;
+        return WC_OK;
+    }
+    if (u_end - u_begin > 0xFFFFFFFFull) return WC_ERR_INVALID_ARG;
+    rows_off = wc::round_up(8 * (u_end - u_begin), 256);
+    work_bytes = rows_off + 4 * rows;
+    return WC_OK;
+}
+
+}  // namespace
+
+extern "C" int wc_decode_gemv_work_bytes(const wc_plan_t* p, const wc_gemv_operand* ops, uint32_t n_ops,
+                                         uint64_t* work_bytes) {
+    if (!work_bytes) return WC_ERR_INVALID_ARG;
+    wc::DotParams q;
+    uint64_t ub = 0, ue = 0, wb = 0, ro = 0;
+    const int st = prepare_gemv(p, ops, n_ops, q, ub, ue, wb, ro);
+    if (st == WC_OK) *work_bytes = wb;
+    return st;
+}
+
+extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, const wc_gemv_operand* ops,
+                                    uint32_t n_ops, void* work_dev, uint64_t work_bytes, void* stream) {
+    wc::DecodeParams d;
+    uint64_t need = 0, rows_off = 0;
+    const int st = prepare_gemv(p, ops, n_ops, d.dot, d.u_begin, d.u_end, need, rows_off);
+    if (st != WC_OK) return st;
+    if (d.dot.n_mats == 0) return WC_OK;
+    if (!blob_dev || !work_dev || work_bytes < need || (reinterpret_cast<uintptr_t>(blob_dev) & 255u) ||
+        (reinterpret_cast<uintptr_t>(work_dev) & 255u))
         return WC_ERR_INVALID_ARG;
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) return WC_ERR_HIP;
     if (cur != p->device) return WC_ERR_INVALID_ARG;
     const uint8_t* b = static_cast<const uint8_t*>(blob_dev);
-    wc::DecodeParams d;
     d.stream = b + p->h.off_stream;
     d.gap = b + p->h.off_gap;
     d.groups = reinterpret_cast<const uint64_t*>(b + p->h.off_groups);
@@ -381,30 +437,16 @@ extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, ui
     d.out = nullptr;
     d.tables = p->d_tables;
     d.n_elems = p->h.n_elems;
-    d.u_begin = p->tensor_g0[tensor];
-    d.u_end = p->tensor_g1[tensor];
     d.ebuf_bytes = p->ebuf_bytes;
     d.l2_cap = p->l2_cap;
-    d.x = x_dev;
-    d.work = work_dev;
-    d.t_lo = off;
-    d.t_hi = off + numel;
-    d.cols = cols;
-    d.pad = 0;
-    const uint64_t need = wc::div_up(d.u_end - d.u_begin, p->waves);
-    const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(p->slots, need));
+    d.dot.part = static_cast<float*>(work_dev);
+    d.dot.row_group = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(work_dev) + rows_off);
+    const uint64_t groups = wc::div_up(d.u_end - d.u_begin, p->waves);
+    const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(p->slots, groups));
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, grid, true, s);
-    if (e == hipSuccess) e = wc::launch_gemv_rows(d, y_dev, (uint32_t)(numel / cols), s);
+    if (e == hipSuccess) e = wc::launch_gemv_rows(d, s);
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
-}
-
-extern "C" int wc_plan_tensor_groups(const wc_plan_t* p, uint32_t tensor, uint64_t* first_group,
-                                     uint64_t* n_groups) {
-    if (!p || tensor >= p->h.n_tensors) return WC_ERR_INVALID_ARG;
-    if (first_group) *first_group = p->tensor_g0[tensor];
-    if (n_groups) *n_groups = p->tensor_g1[tensor] - p->tensor_g0[tensor];
-    return WC_OK;
 }
 
 extern "C" void wc_plan_destroy(wc_plan_t* p) {

@@ -53,11 +53,18 @@ _lib.wc_decode_async.restype = ctypes.c_int
 _lib.wc_gemv_bf16_async.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p]
 _lib.wc_gemv_bf16_async.restype = ctypes.c_int
-_lib.wc_decode_gemv_async.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32,
-                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+
+
+class GemvOperand(ctypes.Structure):
+    _fields_ = [("tensor", ctypes.c_uint32), ("cols", ctypes.c_uint32), ("x", ctypes.c_void_p),
+                ("y", ctypes.c_void_p)]
+
+
+_lib.wc_decode_gemv_work_bytes.argtypes = [ctypes.c_void_p, ctypes.POINTER(GemvOperand), ctypes.c_uint32, _u64p]
+_lib.wc_decode_gemv_work_bytes.restype = ctypes.c_int
+_lib.wc_decode_gemv_async.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(GemvOperand),
+                                      ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
 _lib.wc_decode_gemv_async.restype = ctypes.c_int
-_lib.wc_plan_tensor_groups.argtypes = [ctypes.c_void_p, ctypes.c_uint32, _u64p, _u64p]
-_lib.wc_plan_tensor_groups.restype = ctypes.c_int
 _lib.wc_plan_destroy.argtypes = [ctypes.c_void_p]
 _lib.wc_plan_destroy.restype = None
 _lib.wc_status_str.argtypes = [ctypes.c_int]
@@ -89,7 +96,7 @@ GROUP_ALIGN = 128
 GROUP_MAX_ELEMS = 4096
 
 EXPORTED = ("wc_encode_host", "wc_free_host", "wc_plan", "wc_plan_info", "wc_plan_stats",
-            "wc_decode_async", "wc_gemv_bf16_async", "wc_decode_gemv_async", "wc_plan_tensor_groups",
+            "wc_decode_async", "wc_gemv_bf16_async", "wc_decode_gemv_work_bytes", "wc_decode_gemv_async",
             "wc_plan_destroy", "wc_status_str")
 
 
@@ -180,13 +187,6 @@ class Plan:
         return {"container_bytes": cb.value, "stream_bits": sb.value, "n_groups": ng.value,
                 "count_bits": kc.value, "decode_bits": kd.value, "grid": gr.value, "lds_bytes": lds.value}
 
-    def tensor_groups(self, tensor: int):
-        """wc_plan_tensor_groups: (first group, number of groups) holding tensor `tensor`."""
-        g0, ng = ctypes.c_uint64(), ctypes.c_uint64()
-        _check(_lib.wc_plan_tensor_groups(self.handle, int(tensor), ctypes.byref(g0), ctypes.byref(ng)),
-               "wc_plan_tensor_groups")
-        return g0.value, ng.value
-
     def close(self):
         if self._h is not None:
             _lib.wc_plan_destroy(self._h)
@@ -242,12 +242,29 @@ def gemv_bf16_async(W_dev, rows: int, cols: int, x_dev, y_dev, stream=None) -> N
            "wc_gemv_bf16_async")
 
 
-def decode_gemv_async(plan: Plan, blob_dev, tensor: int, cols: int, x_dev, y_dev, work_dev, stream=None) -> None:
-    """wc_decode_gemv_async: y = W x with W = tensor `tensor` of the container as rows of `cols`,
-    decoded on chip and never written out.  work_dev: 2 floats per group covering the tensor."""
-    _check(_lib.wc_decode_gemv_async(plan.handle, ctypes.c_void_p(_ptr(blob_dev)), int(tensor), int(cols),
-                                     ctypes.c_void_p(_ptr(x_dev)), ctypes.c_void_p(_ptr(y_dev)),
-                                     ctypes.c_void_p(_ptr(work_dev)), ctypes.c_void_p(_stream_handle(stream))),
+def _operands(ops):
+    """(tensor, cols, x, y) tuples -> a ctypes array of wc_gemv_operand (x, y: device tensors or pointers)."""
+    arr = (GemvOperand * max(len(ops), 1))()
+    for i, (t, c, x, y) in enumerate(ops):
+        arr[i] = GemvOperand(int(t), int(c), _ptr(x) if x is not None else 0, _ptr(y) if y is not None else 0)
+    return arr
+
+
+def decode_gemv_work_bytes(plan: Plan, ops) -> int:
+    """wc_decode_gemv_work_bytes for operands [(tensor, cols, x, y), ...]."""
+    n = ctypes.c_uint64(0)
+    _check(_lib.wc_decode_gemv_work_bytes(plan.handle, _operands(ops), len(ops), ctypes.byref(n)),
+           "wc_decode_gemv_work_bytes")
+    return n.value
+
+
+def decode_gemv_async(plan: Plan, blob_dev, ops, work_dev, work_bytes: int, stream=None) -> None:
+    """wc_decode_gemv_async: y = W x for each operand (tensor, cols, x, y) -- consecutive tensors of the
+    container, decoded on chip and never written out -- in one decode launch and one row-sum launch.
+    work_dev: device scratch of work_bytes >= decode_gemv_work_bytes(plan, ops), 256-byte aligned."""
+    _check(_lib.wc_decode_gemv_async(plan.handle, ctypes.c_void_p(_ptr(blob_dev)), _operands(ops), len(ops),
+                                     ctypes.c_void_p(_ptr(work_dev)), int(work_bytes),
+                                     ctypes.c_void_p(_stream_handle(stream))),
            "wc_decode_gemv_async")
 
 

@@ -1,14 +1,15 @@
-"""GPU tests of the fused decode -> matrix-vector product (wc_decode_gemv_async).
+"""GPU tests of the fused decode -> matrix-vector products (wc_decode_gemv_async).
 
 The fused path never writes the decoded weights: each wave decodes one group
 and multiplies it by x on chip.  Expected values come from the oracle: its
 decoder gives W (and must give back the generated weights), its float64 GEMV
-gives y.  The GPU sums in fp32 in a fixed order: a lane adds at most 64
-products in sequence (8 merge steps of 8 elements), six butterfly levels add
-the 64 lane sums, and a row adds the partials of the groups covering it (at
-most cols/A + 2 of them, A = the container's block size), so
-|y - y64| <= (64 + 6 + cols/A + 2) * 2^-24 * sum |w x|, to first order, plus
-the underflow of products of subnormal weights (at most 2^-150 each).
+gives y.  The GPU's order is fixed: each 8-element block is summed by four
+bf16 dot2 steps (each within 3 * 2^-24 of the sum of its addends'
+magnitudes, so at most 12 * 2^-24 * sum |w x| per block), a lane adds its at
+most 8 block sums, six butterfly levels add the 64 lanes, and a row adds the
+partials of the groups covering it (at most cols/A + 2, A = the container's
+block size), so |y - y64| <= (12 + 8 + 6 + cols/A + 2) * 2^-24 * sum |w x| to
+first order, plus the rounding of products below fp32's subnormal range.
 """
 import zlib
 
@@ -37,12 +38,13 @@ def _bound(W, x, align):
     wf = (W.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     xf = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     cols = W.shape[1]
-    terms = 64 + 6 + -(-cols // align) + 2
-    return 1.01 * terms * 2.0 ** -24 * (np.abs(wf) @ np.abs(xf)) + cols * 2.0 ** -149
+    terms = 12 + 8 + 6 + -(-cols // align) + 2
+    return 1.05 * terms * 2.0 ** -24 * (np.abs(wf) @ np.abs(xf)) + cols * 2.0 ** -148
 
 
 class Fused:
-    """A container on the device plus guarded y / work buffers for one tensor."""
+    """A container on the device; runs the fused product over consecutive
+    tensors with guarded y and work buffers."""
 
     GUARD = 64
 
@@ -50,18 +52,29 @@ class Fused:
         self.wc, self.plan = wc, plan
         self._own, self.dblob = to_device_aligned(blob)
 
-    def run(self, tensor, cols, x):
+    def run(self, ops):
+        """ops: [(tensor, cols, x host bf16)] -> list of host y arrays."""
         import torch
-        rows = self.plan.tensor_numels[tensor] // cols
-        _, ng = self.plan.tensor_groups(tensor)
-        y = torch.full((rows + self.GUARD,), float("nan"), dtype=torch.float32, device="cuda")
-        work = torch.full((2 * ng + self.GUARD,), float("nan"), dtype=torch.float32, device="cuda")
-        self.wc.decode_gemv_async(self.plan, self.dblob, tensor, cols, _dev_u16(x), y, work)
+        dev = []
+        for t, c, x in ops:
+            rows = self.plan.tensor_numels[t] // c
+            y = torch.full((rows + self.GUARD,), float("nan"), dtype=torch.float32, device="cuda")
+            dev.append((t, c, _dev_u16(x), y, rows))
+        cops = [(t, c, xd, y) for t, c, xd, y, _ in dev]
+        need = self.wc.decode_gemv_work_bytes(self.plan, cops)
+        work = torch.full((need // 4 + 256 + self.GUARD,), float("nan"), dtype=torch.float32, device="cuda")
+        skew = (-work.data_ptr()) % 256 // 4
+        wview = work[skew:]
+        self.wc.decode_gemv_async(self.plan, self.dblob, cops, wview, need)
         torch.cuda.synchronize()
-        yh, wh = y.cpu().numpy(), work.cpu().numpy()
-        assert np.all(np.isnan(yh[rows:])), "fused GEMV wrote past y[rows]"
-        assert np.all(np.isnan(wh[2 * ng:])), "fused GEMV wrote past its work buffer"
-        return yh[:rows]
+        tail = wview[need // 4:].cpu().numpy()
+        assert np.all(np.isnan(tail)), "fused GEMV wrote past its work buffer"
+        out = []
+        for _, _, _, y, rows in dev:
+            yh = y.cpu().numpy()
+            assert np.all(np.isnan(yh[rows:])), "fused GEMV wrote past y[rows]"
+            out.append(yh[:rows])
+        return out
 
 
 def _check_tensor(oracle_lib, got, W, x, align):
@@ -86,6 +99,9 @@ CASES = [
 
 @pytest.mark.parametrize("name,align,cap,shapes", CASES, ids=[c[0] for c in CASES])
 def test_fused_against_oracle(wc, oracle_lib, name, align, cap, shapes):
+    """Each matrix alone, then every run of consecutive matrices in one call:
+    the values agree with the oracle, the one-call results equal the
+    per-matrix ones, and a repeated call gives the same bits."""
     from lossless_entropy_coded_amd.synth import f32_to_bf16_rne, gemv_input
     rng = np.random.default_rng(zlib.crc32(name.encode()))
     tensors = []
@@ -97,92 +113,114 @@ def test_fused_against_oracle(wc, oracle_lib, name, align, cap, shapes):
     assert np.array_equal(W_all, np.concatenate(tensors))
     with wc.Plan(blob) as plan:
         f = Fused(wc, blob, plan)
-        for k, s in enumerate(shapes):
-            if len(s) != 2:
-                continue
-            rows, cols = s
+        mats = [k for k, s in enumerate(shapes) if len(s) == 2]
+        alone = {}
+        for k in mats:
+            rows, cols = shapes[k]
             off = plan.tensor_offsets[k]
             x = gemv_input(cols)
             log(f"case: fused {name} tensor {k} {rows}x{cols} A={align} M={cap}")
-            got = f.run(k, cols, x)
+            got = f.run([(k, cols, x)])[0]
             W = W_all[off:off + rows * cols].reshape(rows, cols)
             _check_tensor(oracle_lib, got, W, x, align)
-            again = f.run(k, cols, x)
+            again = f.run([(k, cols, x)])[0]
             assert np.array_equal(got.view(np.uint32), again.view(np.uint32)), "fused GEMV is not deterministic"
+            alone[k] = got
+        # consecutive runs of matrices (vectors between matrices break a run)
+        runs, cur = [], []
+        for k in range(len(shapes)):
+            if len(shapes[k]) == 2:
+                cur.append(k)
+            else:
+                runs.append(cur)
+                cur = []
+        runs.append(cur)
+        for run in runs:
+            if len(run) < 2:
+                continue
+            log(f"case: fused {name} tensors {run} in one call")
+            ys = f.run([(k, shapes[k][1], gemv_input(shapes[k][1])) for k in run])
+            for k, y in zip(run, ys):
+                assert np.array_equal(y, alone[k]), f"tensor {k}: one-call result differs from the per-matrix call"
 
 
 @pytest.mark.parametrize("name,rows", [("heavy_tail_14k", 96), ("block_8b", 40), ("block_70b", 24)])
 def test_fused_on_workload_shapes(wc, oracle_lib, name, rows):
-    """The block workloads, truncated to a few rows per matrix: every matrix
-    of the block, read through the fused path, against the oracle."""
+    """The block workloads, truncated to a few rows per matrix: all matrices
+    of the block in one fused call, against the oracle."""
     from lossless_entropy_coded_amd.synth import gemv_input, make_workload
     wl = make_workload(name, scale_rows=rows)
     blob = wc.encode_host(wl.tensors())
     with wc.Plan(blob) as plan:
         f = Fused(wc, blob, plan)
-        for k, shape in enumerate(wl.shapes):
-            if len(shape) != 2:
-                continue
-            r, c = shape
+        mats = [k for k, s in enumerate(wl.shapes) if len(s) == 2]
+        assert mats == list(range(len(mats)))
+        log(f"case: fused {name} rows={rows} tensors {mats} in one call")
+        ys = f.run([(k, wl.shapes[k][1], gemv_input(wl.shapes[k][1])) for k in mats])
+        for k, got in zip(mats, ys):
+            r, c = wl.shapes[k]
             off = plan.tensor_offsets[k]
-            x = gemv_input(c)
-            log(f"case: fused {name} rows={rows} tensor {wl.names[k]} {r}x{c}")
-            got = f.run(k, c, x)
-            _check_tensor(oracle_lib, got, wl.bits[off:off + r * c].reshape(r, c), x, wc.GROUP_ALIGN)
+            _check_tensor(oracle_lib, got, wl.bits[off:off + r * c].reshape(r, c), gemv_input(c), wc.GROUP_ALIGN)
 
 
 def test_fused_full_block_8b_sampled(wc, oracle_lib):
-    """The full 8B-shape block (the size the benchmark decodes): every matrix
-    through the fused path; 48 sampled rows per matrix (first, last and random)
-    against the oracle's GEMV of the generated weights."""
+    """The full 8B-shape block (the size the benchmark decodes): its 7
+    matrices in one fused call; 48 sampled rows per matrix (first, last and
+    random) against the oracle's GEMV of the generated weights."""
     from lossless_entropy_coded_amd.synth import gemv_input, make_workload
     wl = make_workload("block_8b")
     blob = wc.encode_host(wl.tensors())
     rng = np.random.default_rng(8)
     with wc.Plan(blob) as plan:
         f = Fused(wc, blob, plan)
-        for k, shape in enumerate(wl.shapes):
-            if len(shape) != 2:
-                continue
-            r, c = shape
+        mats = [k for k, s in enumerate(wl.shapes) if len(s) == 2]
+        log(f"case: fused block_8b full, tensors {mats} in one call")
+        ys = f.run([(k, wl.shapes[k][1], gemv_input(wl.shapes[k][1])) for k in mats])
+        for k, got in zip(mats, ys):
+            r, c = wl.shapes[k]
             off = plan.tensor_offsets[k]
-            x = gemv_input(c)
-            log(f"case: fused block_8b full tensor {wl.names[k]} {r}x{c}")
-            got = f.run(k, c, x)
             assert np.all(np.isfinite(got))
             sample = np.unique(np.concatenate([[0, r - 1], rng.integers(0, r, 46)]))
             W = wl.bits[off:off + r * c].reshape(r, c)[sample]
-            _check_tensor(oracle_lib, got[sample], W, x, wc.GROUP_ALIGN)
+            _check_tensor(oracle_lib, got[sample], W, gemv_input(c), wc.GROUP_ALIGN)
 
 
 def test_fused_argument_checks(wc):
     import torch
     from lossless_entropy_coded_amd.synth import f32_to_bf16_rne
     rng = np.random.default_rng(5)
-    # offsets: tensor 1 at 4 (not a multiple of 8), tensor 3 at 2056
+    # offsets: tensor 1 at 4 (not a multiple of 8), tensor 3 at 2056, tensor 4 empty, tensor 5 at 4104
     t = [f32_to_bf16_rne(rng.standard_normal(n, dtype=np.float32)) for n in (4, 4 * 512, 4, 4 * 512)]
-    blob = wc.encode_host(t + [np.zeros(0, np.uint16)], group_align=64, group_max_elems=512)
+    t += [np.zeros(0, np.uint16), f32_to_bf16_rne(rng.standard_normal(2 * 512, dtype=np.float32))]
+    blob = wc.encode_host(t, group_align=64, group_max_elems=512)
     with wc.Plan(blob) as plan:
         _, dblob = to_device_aligned(blob)
         x = torch.zeros(1032, dtype=torch.int16, device="cuda")
         y = torch.zeros(64, dtype=torch.float32, device="cuda")
-        work = torch.zeros(2 * plan.stats()["n_groups"], dtype=torch.float32, device="cuda")
+        work = torch.zeros(1 << 16, dtype=torch.float32, device="cuda")
+        assert work.data_ptr() % 256 == 0
 
-        def status(tensor, cols, xp=x, yp=y):
+        def status(ops, nbytes=None):
             try:
-                wc.decode_gemv_async(plan, dblob, tensor, cols, xp, yp, work)
+                need = wc.decode_gemv_work_bytes(plan, ops)
+                wc.decode_gemv_async(plan, dblob, ops, work, need if nbytes is None else nbytes)
                 torch.cuda.synchronize()
                 return wc.WC_OK
             except wc.WCError as e:
                 return e.status
 
-        assert plan.tensor_offsets[1] == 4 and plan.tensor_offsets[3] == 2056
-        assert status(3, 512) == wc.WC_OK
-        assert status(5, 512) == wc.WC_ERR_INVALID_ARG      # no such tensor
-        assert status(1, 512) == wc.WC_ERR_INVALID_ARG      # element offset 4: not a multiple of 8
-        assert status(3, 500) == wc.WC_ERR_INVALID_ARG      # not a multiple of 8
-        assert status(3, 256) == wc.WC_ERR_INVALID_ARG      # shorter than the largest group
-        assert status(3, 768) == wc.WC_ERR_INVALID_ARG      # does not divide numel
-        assert status(3, 0) == wc.WC_ERR_INVALID_ARG
-        assert status(3, 512, xp=x.data_ptr() + 2) == wc.WC_ERR_INVALID_ARG
-        assert status(4, 512) == wc.WC_OK                    # empty tensor: no-op
+        assert plan.tensor_offsets[1] == 4 and plan.tensor_offsets[3] == 2056 and plan.tensor_offsets[5] == 4104
+        assert status([(3, 512, x, y)]) == wc.WC_OK
+        assert status([(3, 512, x, y), (4, 512, None, None), (5, 512, x, y)]) == wc.WC_OK   # empty one skipped
+        assert status([(4, 512, None, None)]) == wc.WC_OK                    # only empty: no-op
+        assert status([]) == wc.WC_ERR_INVALID_ARG
+        assert status([(6, 512, x, y)]) == wc.WC_ERR_INVALID_ARG            # no such tensor
+        assert status([(3, 512, x, y), (5, 512, x, y)]) == wc.WC_ERR_INVALID_ARG   # not consecutive
+        assert status([(1, 512, x, y)]) == wc.WC_ERR_INVALID_ARG            # element offset 4
+        assert status([(3, 500, x, y)]) == wc.WC_ERR_INVALID_ARG            # not a multiple of 8
+        assert status([(3, 256, x, y)]) == wc.WC_ERR_INVALID_ARG            # shorter than the largest group
+        assert status([(3, 768, x, y)]) == wc.WC_ERR_INVALID_ARG            # does not divide numel
+        assert status([(3, 0, x, y)]) == wc.WC_ERR_INVALID_ARG
+        assert status([(3, 512, x.data_ptr() + 2, y)]) == wc.WC_ERR_INVALID_ARG   # x misaligned
+        assert status([(3, 512, x, y)], nbytes=8) == wc.WC_ERR_INVALID_ARG   # work too small
+        assert status([(3, 512, x, y)] * 17) == wc.WC_ERR_INVALID_ARG       # more than 16 operands
