@@ -51,6 +51,8 @@ class Report(ctypes.Structure):
         ("entropy_bits", ctypes.c_double),
         ("mean_code_bits", ctypes.c_double),
         ("hist", ctypes.c_uint64 * 256),
+        ("layout", ctypes.c_uint32),
+        ("seg_max_bits", ctypes.c_uint32),
     ]
 
     def as_dict(self):
@@ -92,6 +94,8 @@ def lib():
         L.orc_canonical_codes.argtypes = [u8p, u32p]
         L.orc_encode.argtypes = [u16p, ctypes.c_uint64, u64p, ctypes.c_uint32, ctypes.c_uint32,
                                  ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(u8p), u64p]
+        L.orc_encode_lanes.argtypes = [u16p, ctypes.c_uint64, u64p, ctypes.c_uint32, ctypes.c_uint32,
+                                       ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(u8p), u64p]
         L.orc_decode.argtypes = [u8p, ctypes.c_uint64, u16p, ctypes.c_uint64, ctypes.POINTER(Report)]
         L.orc_header.argtypes = [u8p, ctypes.c_uint64, ctypes.POINTER(Report)]
         L.orc_gemv_bf16.argtypes = [u16p, ctypes.c_uint64, ctypes.c_uint64, u16p,
@@ -179,6 +183,33 @@ def encode(w: np.ndarray, numels=None, max_code_len: int = 24, chunks_per_group:
                           ctypes.byref(nbytes))
     if st:
         raise OracleError(st, "encode")
+    try:
+        blob = np.ctypeslib.as_array(out, shape=(nbytes.value,)).copy() if nbytes.value else np.zeros(0, np.uint8)
+    finally:
+        lib().orc_free(out)
+    return blob
+
+
+def encode_lanes(w: np.ndarray, numels=None, max_code_len: int = 24, group_align: int = 128,
+                 group_max_elems: int = 4096, seg_max_bits: int = 15872) -> np.ndarray:
+    """Oracle's own serial writer of the interleaved-lane layout (version 3).
+
+    Segments are runs of whole group_align-element blocks of at most
+    group_max_elems elements and seg_max_bits stream bits; inside a segment,
+    lane j of 64 takes the 8-element lane blocks j, j + 64, ..., and each
+    lane's codewords are stored together, lane after lane."""
+    w = np.ascontiguousarray(w, dtype=np.uint16).reshape(-1)
+    if numels is None:
+        nump, nt = None, 1
+    else:
+        arr = np.ascontiguousarray(numels, dtype=np.uint64)
+        nump, nt = _p(arr, ctypes.c_uint64), arr.size
+    out = ctypes.POINTER(ctypes.c_uint8)()
+    nbytes = ctypes.c_uint64(0)
+    st = lib().orc_encode_lanes(_p(w, ctypes.c_uint16), w.size, nump, nt, int(max_code_len), int(group_align),
+                                int(group_max_elems), int(seg_max_bits), ctypes.byref(out), ctypes.byref(nbytes))
+    if st:
+        raise OracleError(st, "encode_lanes")
     try:
         blob = np.ctypeslib.as_array(out, shape=(nbytes.value,)).copy() if nbytes.value else np.zeros(0, np.uint8)
     finally:

@@ -41,6 +41,16 @@
  *    each entry holds the group's first element and the
  *    stream bit where that element's codeword starts, and a final entry
  *    holds {n, stream bits}.
+ *  - interleaved-lane layout (container version 3), the LazyWeights page's
+ *    "Huffman-encode ... in interleaved lanes" (analogy section): the same
+ *    code and planes; the elements are cut into segments (runs of whole
+ *    A-element blocks, at most M elements and at most B stream bits); inside
+ *    a segment, 8-element lane blocks are dealt to 64 lanes in turn (lane j
+ *    takes lane blocks j, j + 64, j + 128, ...), each lane's codewords form
+ *    one bit string (its lane blocks in order, elements in order), and the
+ *    segment's stream is lane 0's string, then lane 1's, ... up to lane 63's;
+ *    per segment the table holds its first element and first stream bit, and
+ *    64 u16 offsets give where each lane's string starts inside it.
  */
 #include "oracle.h"
 
@@ -117,6 +127,47 @@ static uint64_t orc_groups(const uint64_t* block_bit, uint64_t nb, uint64_t n, u
         bit[g] = block_bit[k];
     }
     return g;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Interleaved-lane layout [LW analogy: Huffman codes in interleaved lanes]. */
+/* ------------------------------------------------------------------------ */
+#define LANES           64u
+#define LANE_BLOCK       8u
+#define LANES_SLACK     64u   /* zero bytes after the padded stream          */
+/* header fields of version 3 that differ from version 2 */
+#define F_LANES          9   /* u8, 64 (version 2: chunk bits)              */
+#define F_LANE_BLOCK    10   /* u16, 8 (version 2: reserved)                */
+#define F_SEGBITS       12   /* u32 stream bits per segment at most B       */
+#define F_OFF_LOFF      80   /* u64: u16 lane_off[64 * n_segs]              */
+
+/* Segments: runs of whole A-blocks, as long as possible while they hold at
+ * most M elements and their codewords at most B bits (at least one block).
+ * block_bit[k] = stream bits before block k (the layout inside a segment
+ * does not change how many bits precede it). */
+static uint64_t orc_segments(const uint64_t* block_bit, uint64_t nb, uint64_t n, uint32_t A, uint32_t B,
+                             uint32_t M, uint64_t* elem, uint64_t* bit) {
+    uint64_t g = 0, k = 0;
+    elem[0] = 0;
+    bit[0] = 0;
+    while (k < nb) {
+        uint64_t first = k;
+        ++k;
+        while (k < nb && (k + 1 - first) * (uint64_t)A <= M && block_bit[k + 1] - block_bit[first] <= B)
+            ++k;
+        ++g;
+        elem[g] = k * (uint64_t)A < n ? k * (uint64_t)A : n;
+        bit[g] = block_bit[k];
+    }
+    return g;
+}
+
+/* Element index (inside a segment of m elements) of the t-th symbol of lane
+ * j, or m if lane j has fewer symbols. */
+static uint64_t lane_elem(uint64_t m, uint32_t j, uint64_t t) {
+    uint64_t blk = j + (uint64_t)LANES * (t / LANE_BLOCK);
+    uint64_t i = blk * LANE_BLOCK + t % LANE_BLOCK;
+    return i < m ? i : m;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -402,18 +453,142 @@ int orc_encode(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n
     return ORC_OK;
 }
 
+int orc_encode_lanes(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
+                     uint32_t max_code_len, uint32_t A, uint32_t M, uint32_t B, uint8_t** blob,
+                     uint64_t* blob_bytes) {
+    if (!blob || !blob_bytes || (n && !w)) return ORC_E_ARG;
+    if (max_code_len < 1 || max_code_len > MAX_LEN_LIMIT || A < 1 || M < A || M % A) return ORC_E_ARG;
+    if (M > LANES * LANE_BLOCK * 1024u || B > 65535u || (uint64_t)A * max_code_len > B) return ORC_E_ARG;
+    uint64_t one_numel = n;
+    if (!numels) { numels = &one_numel; n_tensors = 1; }
+    uint64_t sum = 0;
+    for (uint32_t t = 0; t < n_tensors; ++t) sum += numels[t];
+    if (sum != n) return ORC_E_ARG;
+
+    uint8_t* e = (uint8_t*)malloc(n ? n : 1);
+    uint8_t* sm = (uint8_t*)malloc(n ? n : 1);
+    if (!e || !sm) { free(e); free(sm); return ORC_E_NOMEM; }
+    orc_split_planes(w, n, e, sm);
+    uint64_t hist[256] = {0};
+    for (uint64_t i = 0; i < n; ++i) hist[e[i]]++;
+    uint8_t lens[256];
+    uint32_t codes[256];
+    int st = orc_package_merge(hist, max_code_len, lens);
+    if (st == ORC_OK) st = orc_canonical_codes(lens, codes);
+    if (st != ORC_OK) { free(e); free(sm); return st; }
+    uint64_t bits = 0;
+    for (int s = 0; s < 256; ++s) bits += hist[s] * lens[s];
+    uint64_t stream_bytes = round_up(ceil_div(bits, 8), 8) + LANES_SLACK;
+
+    uint64_t nb = ceil_div(n, A);
+    uint64_t* block_bit = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+    uint64_t* s_elem = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+    uint64_t* s_bit = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+    if (!block_bit || !s_elem || !s_bit) {
+        free(block_bit); free(s_elem); free(s_bit); free(e); free(sm);
+        return ORC_E_NOMEM;
+    }
+    {
+        uint64_t at = 0;
+        for (uint64_t i = 0; i < n; ++i) {
+            if (i % A == 0) block_bit[i / A] = at;
+            at += lens[e[i]];
+        }
+        block_bit[nb] = at;
+    }
+    uint64_t n_segs = orc_segments(block_bit, nb, n, A, B, M, s_elem, s_bit);
+    free(block_bit);
+
+    uint64_t off_len = HDR_BYTES;
+    uint64_t off_tens = round_up(off_len + 256, ALIGN);
+    uint64_t off_segs = round_up(off_tens + 16ull * n_tensors, ALIGN);
+    uint64_t off_loff = round_up(off_segs + 16 * (n_segs + 1), ALIGN);
+    uint64_t off_stream = round_up(off_loff + 2ull * LANES * n_segs, ALIGN);
+    uint64_t off_sm = round_up(off_stream + stream_bytes, ALIGN);
+    uint64_t total = round_up(off_sm + n, ALIGN);
+    uint8_t* b = (uint8_t*)calloc(total, 1);
+    if (!b) { free(s_elem); free(s_bit); free(e); free(sm); return ORC_E_NOMEM; }
+
+    uint8_t* stream = b + off_stream;
+    uint64_t pos = 0;
+    for (uint64_t g = 0; g < n_segs; ++g) {
+        wr(b + off_segs + 16 * g, s_elem[g], 8);
+        wr(b + off_segs + 16 * g + 8, s_bit[g], 8);
+        uint64_t e0 = s_elem[g], m = s_elem[g + 1] - e0;
+        for (uint32_t j = 0; j < LANES; ++j) {
+            wr(b + off_loff + 2 * (LANES * g + j), pos - s_bit[g], 2);
+            for (uint64_t t = 0;; ++t) {
+                uint64_t i = lane_elem(m, j, t);
+                if (i >= m) break;
+                int L = lens[e[e0 + i]];
+                uint32_t c = codes[e[e0 + i]];
+                for (int k = L - 1; k >= 0; --k) {
+                    if ((c >> k) & 1u) stream[pos >> 3] |= (uint8_t)(0x80u >> (pos & 7));
+                    ++pos;
+                }
+            }
+        }
+    }
+    wr(b + off_segs + 16 * n_segs, n, 8);
+    wr(b + off_segs + 16 * n_segs + 8, bits, 8);
+    free(s_elem); free(s_bit);
+
+    memcpy(b + off_len, lens, 256);
+    uint64_t acc = 0;
+    for (uint32_t t = 0; t < n_tensors; ++t) {
+        wr(b + off_tens + 16ull * t, acc, 8);
+        wr(b + off_tens + 16ull * t + 8, numels[t], 8);
+        acc += numels[t];
+    }
+    if (n) memcpy(b + off_sm, sm, n);
+
+    memcpy(b + F_MAGIC, "WCBF", 4);
+    wr(b + F_VERSION, 3, 2);
+    wr(b + F_FLAGS, 0, 2);
+    wr(b + F_MAXLEN, max_code_len, 1);
+    wr(b + F_LANES, LANES, 1);
+    wr(b + F_LANE_BLOCK, LANE_BLOCK, 2);
+    wr(b + F_SEGBITS, B, 4);
+    wr(b + F_NTENS, n_tensors, 4);
+    wr(b + F_ALIGN, A, 4);
+    wr(b + F_MAXG, M, 4);
+    wr(b + F_N, n, 8);
+    wr(b + F_SBITS, bits, 8);
+    wr(b + F_NGROUPS, n_segs, 8);
+    wr(b + F_OFF_LEN, off_len, 8);
+    wr(b + F_OFF_TENS, off_tens, 8);
+    wr(b + F_OFF_GS, off_segs, 8);
+    wr(b + F_OFF_LOFF, off_loff, 8);
+    wr(b + F_OFF_STREAM, off_stream, 8);
+    wr(b + F_STREAM_BYTES, stream_bytes, 8);
+    wr(b + F_OFF_SM, off_sm, 8);
+    wr(b + F_TOTAL, total, 8);
+
+    free(e);
+    free(sm);
+    *blob = b;
+    *blob_bytes = total;
+    return ORC_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Reader                                                                   */
 /* ------------------------------------------------------------------------ */
 typedef struct {
-    uint32_t max_len, G, A, M, n_tensors;
+    uint32_t version;   /* 2: per-chunk gaps; 3: interleaved lanes */
+    uint32_t max_len, G, A, M, B, n_tensors;
     uint64_t n, stream_bits, n_chunks, n_groups;
     uint64_t off_len, off_tens, off_gs, off_gap, off_stream, stream_bytes, off_sm, total;
 } hdr_t;
 
+static int parse_header_lanes(const uint8_t* blob, uint64_t bytes, hdr_t* h);
+
 static int parse_header(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
     if (!blob || bytes < HDR_BYTES) return ORC_E_TRUNC;
     if (memcmp(blob + F_MAGIC, "WCBF", 4) != 0) return ORC_E_MAGIC;
+    if (rd(blob + F_VERSION, 2) == 3) return parse_header_lanes(blob, bytes, h);
+    h->version = 2;
+    h->B = 0;
     if (rd(blob + F_VERSION, 2) != 2 || rd(blob + F_FLAGS, 2) != 0) return ORC_E_MAGIC;
     if (rd(blob + F_CHUNKBITS, 1) != CHUNK_BITS) return ORC_E_MAGIC;
     if (rd(blob + F_RES0, 2) != 0) return ORC_E_MAGIC;
@@ -456,6 +631,49 @@ static int parse_header(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
     return ORC_OK;
 }
 
+static int parse_header_lanes(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
+    h->version = 3;
+    if (rd(blob + F_FLAGS, 2) != 0 || rd(blob + F_LANES, 1) != LANES || rd(blob + F_LANE_BLOCK, 2) != LANE_BLOCK)
+        return ORC_E_MAGIC;
+    for (uint32_t k = F_TAIL; k < HDR_BYTES; ++k) if (blob[k]) return ORC_E_MAGIC;
+    if (rd(blob + F_NCHUNKS, 8) != 0) return ORC_E_MAGIC;
+    h->max_len = (uint32_t)rd(blob + F_MAXLEN, 1);
+    h->G = 0;
+    h->B = (uint32_t)rd(blob + F_SEGBITS, 4);
+    h->A = (uint32_t)rd(blob + F_ALIGN, 4);
+    h->M = (uint32_t)rd(blob + F_MAXG, 4);
+    h->n_tensors = (uint32_t)rd(blob + F_NTENS, 4);
+    h->n = rd(blob + F_N, 8);
+    h->stream_bits = rd(blob + F_SBITS, 8);
+    h->n_chunks = 0;
+    h->n_groups = rd(blob + F_NGROUPS, 8);
+    h->off_len = rd(blob + F_OFF_LEN, 8);
+    h->off_tens = rd(blob + F_OFF_TENS, 8);
+    h->off_gs = rd(blob + F_OFF_GS, 8);
+    h->off_gap = rd(blob + F_OFF_LOFF, 8);
+    h->off_stream = rd(blob + F_OFF_STREAM, 8);
+    h->stream_bytes = rd(blob + F_STREAM_BYTES, 8);
+    h->off_sm = rd(blob + F_OFF_SM, 8);
+    h->total = rd(blob + F_TOTAL, 8);
+    if (h->max_len < 1 || h->max_len > MAX_LEN_LIMIT || h->A < 1 || h->M < h->A || h->M % h->A ||
+        h->B > 65535u || (uint64_t)h->A * h->max_len > h->B)
+        return ORC_E_MAGIC;
+    if (h->n > ((uint64_t)1 << 48) || h->stream_bits > ((uint64_t)1 << 56)) return ORC_E_SIZES;
+    if (h->n_groups > h->n || (h->n_groups == 0) != (h->n == 0)) return ORC_E_SIZES;
+    if (h->stream_bytes != round_up(ceil_div(h->stream_bits, 8), 8) + LANES_SLACK) return ORC_E_SIZES;
+    if (h->stream_bits > h->n * (uint64_t)h->max_len || h->stream_bits < h->n) return ORC_E_SIZES;
+    const uint64_t offs[6] = {h->off_len, h->off_tens, h->off_gs, h->off_gap, h->off_stream, h->off_sm};
+    const uint64_t lens[6] = {256, 16ull * h->n_tensors, 16 * (h->n_groups + 1), 2ull * LANES * h->n_groups,
+                              h->stream_bytes, h->n};
+    uint64_t lo = HDR_BYTES;
+    for (int k = 0; k < 6; ++k) {
+        if (offs[k] % ALIGN || offs[k] < lo) return ORC_E_TRUNC;
+        lo = offs[k] + lens[k];
+    }
+    if (h->total < lo || h->total > bytes) return ORC_E_TRUNC;
+    return ORC_OK;
+}
+
 int orc_header(const uint8_t* blob, uint64_t blob_bytes, orc_report* rep) {
     hdr_t h;
     int st = parse_header(blob, blob_bytes, &h);
@@ -471,6 +689,8 @@ int orc_header(const uint8_t* blob, uint64_t blob_bytes, orc_report* rep) {
         rep->group_align = h.A;
         rep->group_max_elems = h.M;
         rep->max_code_len = h.max_len;
+        rep->layout = h.version == 3 ? 1u : 0u;
+        rep->seg_max_bits = h.B;
     }
     return ORC_OK;
 }
@@ -480,6 +700,143 @@ typedef struct {
     int child[2];
     int sym;      /* -1 for an inner node */
 } trie_node;
+
+/* Version 2: serial bit-by-bit decode in element order; re-derive the
+ * per-chunk gaps and the group table from the codeword starts actually
+ * observed and compare them with the stored ones. */
+static int decode_chunks(const uint8_t* blob, const hdr_t* h, const trie_node* T, uint16_t* out,
+                         uint64_t hist[256]) {
+    int st = ORC_OK;
+    const uint8_t* stream = blob + h->off_stream;
+    const uint8_t* gap = blob + h->off_gap;
+    const uint8_t* gs = blob + h->off_gs;
+    const uint8_t* sm = blob + h->off_sm;
+    uint64_t nb = ceil_div(h->n, h->A);
+    uint64_t* block_bit = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+    if (!block_bit) return ORC_E_NOMEM;
+    uint64_t pos = 0, next_chunk = 0;
+    for (uint64_t i = 0; i < h->n && st == ORC_OK; ++i) {
+        while (next_chunk < h->n_chunks && CHUNK_BITS * next_chunk <= pos) {
+            uint64_t want = pos - CHUNK_BITS * next_chunk;
+            if (want >= CHUNK_BITS || gap[next_chunk] != want) { st = ORC_E_GAP; break; }
+            ++next_chunk;
+        }
+        if (st != ORC_OK) break;
+        if (i % h->A == 0) block_bit[i / h->A] = pos;
+        int node = 0;
+        for (;;) {
+            if (pos >= h->stream_bits) { st = ORC_E_STREAM; break; }
+            int bit = (stream[pos >> 3] >> (7 - (pos & 7))) & 1;
+            ++pos;
+            node = T[node].child[bit];
+            if (node < 0) { st = ORC_E_STREAM; break; }
+            if (T[node].sym >= 0) break;
+        }
+        if (st != ORC_OK) break;
+        uint8_t e = (uint8_t)T[node].sym;
+        hist[e]++;
+        uint16_t s = sm[i];
+        out[i] = (uint16_t)(((s & 0x80) << 8) | ((uint16_t)e << 7) | (s & 0x7F));
+    }
+    if (st != ORC_OK) { free(block_bit); return st; }
+    if (pos != h->stream_bits) { free(block_bit); return ORC_E_STREAM; }
+    while (next_chunk < h->n_chunks) {
+        uint64_t want = h->stream_bits - CHUNK_BITS * next_chunk;
+        if (want >= CHUNK_BITS || gap[next_chunk] != want) { free(block_bit); return ORC_E_GAP; }
+        ++next_chunk;
+    }
+    /* the group table, re-derived from the observed block starts */
+    block_bit[nb] = pos;
+    {
+        uint64_t* g_elem = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+        uint64_t* g_bit = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+        if (!g_elem || !g_bit) { free(g_elem); free(g_bit); free(block_bit); return ORC_E_NOMEM; }
+        uint64_t ng = orc_groups(block_bit, nb, h->n, h->A, h->G, h->M, g_elem, g_bit);
+        if (ng != h->n_groups) st = ORC_E_GROUP;
+        for (uint64_t g = 0; st == ORC_OK && g <= ng; ++g)
+            if (rd(gs + 16 * g, 8) != g_elem[g] || rd(gs + 16 * g + 8, 8) != g_bit[g]) st = ORC_E_GROUP;
+        free(g_elem); free(g_bit);
+    }
+    free(block_bit);
+    return st;
+}
+
+/* Walk the trie from bit *pos; -1 if the stream ends or leaves the code. */
+static int trie_symbol(const trie_node* T, const uint8_t* stream, uint64_t limit, uint64_t* pos) {
+    int node = 0;
+    for (;;) {
+        if (*pos >= limit) return -1;
+        int bit = (stream[*pos >> 3] >> (7 - (*pos & 7))) & 1;
+        ++*pos;
+        node = T[node].child[bit];
+        if (node < 0) return -1;
+        if (T[node].sym >= 0) return T[node].sym;
+    }
+}
+
+/* Version 3 (interleaved lanes): for every stored segment, decode lane 0's
+ * symbols, then lane 1's, ... bit by bit, checking that each lane starts at
+ * its stored offset and that the segment ends where the next begins; then
+ * re-derive the segment table from the decoded code lengths. */
+static int decode_lanes(const uint8_t* blob, const hdr_t* h, const trie_node* T, const uint8_t* lens,
+                        uint16_t* out, uint64_t hist[256]) {
+    const uint8_t* stream = blob + h->off_stream;
+    const uint8_t* segs = blob + h->off_gs;
+    const uint8_t* loff = blob + h->off_gap;
+    const uint8_t* sm = blob + h->off_sm;
+    uint8_t* e = (uint8_t*)malloc(h->n ? h->n : 1);
+    if (!e) return ORC_E_NOMEM;
+    int st = ORC_OK;
+    uint64_t pos = 0;
+    if (rd(segs, 8) != 0 || rd(segs + 8, 8) != 0) st = ORC_E_GROUP;
+    for (uint64_t g = 0; g < h->n_groups && st == ORC_OK; ++g) {
+        uint64_t e0 = rd(segs + 16 * g, 8), p0 = rd(segs + 16 * g + 8, 8);
+        uint64_t e1 = rd(segs + 16 * (g + 1), 8), p1 = rd(segs + 16 * (g + 1) + 8, 8);
+        if (e1 <= e0 || e1 > h->n || p0 != pos || p1 < p0 || p1 > h->stream_bits) { st = ORC_E_GROUP; break; }
+        uint64_t m = e1 - e0;
+        for (uint32_t j = 0; j < LANES && st == ORC_OK; ++j) {
+            if (rd(loff + 2 * (LANES * g + j), 2) != pos - p0) { st = ORC_E_GROUP; break; }
+            for (uint64_t t = 0;; ++t) {
+                uint64_t i = lane_elem(m, j, t);
+                if (i >= m) break;
+                int sym = trie_symbol(T, stream, p1, &pos);
+                if (sym < 0) { st = ORC_E_STREAM; break; }
+                e[e0 + i] = (uint8_t)sym;
+            }
+        }
+        if (st == ORC_OK && pos != p1) st = ORC_E_STREAM;
+    }
+    if (st == ORC_OK && (rd(segs + 16 * h->n_groups, 8) != h->n || rd(segs + 16 * h->n_groups + 8, 8) != h->stream_bits ||
+                         pos != h->stream_bits))
+        st = ORC_E_STREAM;
+    if (st == ORC_OK) {   /* the segment table, re-derived from the decoded code lengths */
+        uint64_t nb = ceil_div(h->n, h->A);
+        uint64_t* block_bit = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+        uint64_t* s_elem = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+        uint64_t* s_bit = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+        if (!block_bit || !s_elem || !s_bit) st = ORC_E_NOMEM;
+        if (st == ORC_OK) {
+            uint64_t at = 0;
+            for (uint64_t i = 0; i < h->n; ++i) {
+                if (i % h->A == 0) block_bit[i / h->A] = at;
+                at += lens[e[i]];
+            }
+            block_bit[nb] = at;
+            uint64_t ns = orc_segments(block_bit, nb, h->n, h->A, h->B, h->M, s_elem, s_bit);
+            if (ns != h->n_groups) st = ORC_E_GROUP;
+            for (uint64_t g = 0; st == ORC_OK && g <= ns; ++g)
+                if (rd(segs + 16 * g, 8) != s_elem[g] || rd(segs + 16 * g + 8, 8) != s_bit[g]) st = ORC_E_GROUP;
+        }
+        free(block_bit); free(s_elem); free(s_bit);
+    }
+    for (uint64_t i = 0; st == ORC_OK && i < h->n; ++i) {
+        hist[e[i]]++;
+        uint16_t s = sm[i];
+        out[i] = (uint16_t)(((s & 0x80) << 8) | ((uint16_t)e[i] << 7) | (s & 0x7F));
+    }
+    free(e);
+    return st;
+}
 
 int orc_decode(const uint8_t* blob, uint64_t bytes, uint16_t* out, uint64_t out_cap, orc_report* rep) {
     hdr_t h;
@@ -551,65 +908,16 @@ int orc_decode(const uint8_t* blob, uint64_t bytes, uint16_t* out, uint64_t out_
         }
     }
     if (st != ORC_OK) { free(T); return st; }
-
-    /* serial bit-by-bit decode; re-derive the auxiliary variables from the
-     * codeword starts actually observed and compare with the stored ones */
-    const uint8_t* stream = blob + h.off_stream;
-    const uint8_t* gap = blob + h.off_gap;
-    const uint8_t* gs = blob + h.off_gs;
-    const uint8_t* sm = blob + h.off_sm;
     uint64_t hist[256] = {0};
-    uint64_t nb = ceil_div(h.n, h.A);
-    uint64_t* block_bit = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
-    if (!block_bit) { free(T); return ORC_E_NOMEM; }
-    uint64_t pos = 0, next_chunk = 0;
-    for (uint64_t i = 0; i < h.n && st == ORC_OK; ++i) {
-        while (next_chunk < h.n_chunks && CHUNK_BITS * next_chunk <= pos) {
-            uint64_t want = pos - CHUNK_BITS * next_chunk;
-            if (want >= CHUNK_BITS || gap[next_chunk] != want) { st = ORC_E_GAP; break; }
-            ++next_chunk;
-        }
-        if (st != ORC_OK) break;
-        if (i % h.A == 0) block_bit[i / h.A] = pos;
-        int node = 0;
-        for (;;) {
-            if (pos >= h.stream_bits) { st = ORC_E_STREAM; break; }
-            int bit = (stream[pos >> 3] >> (7 - (pos & 7))) & 1;
-            ++pos;
-            node = T[node].child[bit];
-            if (node < 0) { st = ORC_E_STREAM; break; }
-            if (T[node].sym >= 0) break;
-        }
-        if (st != ORC_OK) break;
-        uint8_t e = (uint8_t)T[node].sym;
-        hist[e]++;
-        uint16_t s = sm[i];
-        out[i] = (uint16_t)(((s & 0x80) << 8) | ((uint16_t)e << 7) | (s & 0x7F));
-    }
+    if (h.version == 3)
+        st = decode_lanes(blob, &h, T, lens, out, hist);
+    else
+        st = decode_chunks(blob, &h, T, out, hist);
     free(T);
-    if (st != ORC_OK) { free(block_bit); return st; }
-    if (pos != h.stream_bits) { free(block_bit); return ORC_E_STREAM; }
-    while (next_chunk < h.n_chunks) {
-        uint64_t want = h.stream_bits - CHUNK_BITS * next_chunk;
-        if (want >= CHUNK_BITS || gap[next_chunk] != want) { free(block_bit); return ORC_E_GAP; }
-        ++next_chunk;
-    }
-    /* the group table, re-derived from the observed block starts */
-    block_bit[nb] = pos;
-    {
-        uint64_t* g_elem = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
-        uint64_t* g_bit = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
-        if (!g_elem || !g_bit) { free(g_elem); free(g_bit); free(block_bit); return ORC_E_NOMEM; }
-        uint64_t ng = orc_groups(block_bit, nb, h.n, h.A, h.G, h.M, g_elem, g_bit);
-        if (ng != h.n_groups) st = ORC_E_GROUP;
-        for (uint64_t g = 0; st == ORC_OK && g <= ng; ++g)
-            if (rd(gs + 16 * g, 8) != g_elem[g] || rd(gs + 16 * g + 8, 8) != g_bit[g]) st = ORC_E_GROUP;
-        free(g_elem); free(g_bit);
-    }
-    free(block_bit);
     if (st != ORC_OK) return st;
 
     /* every bit after stream_bits, up to the end of the section, is zero */
+    const uint8_t* stream = blob + h.off_stream;
     for (uint64_t p = h.stream_bits; p < 8 * h.stream_bytes; ++p) {
         if ((p & 7) == 0 && p + 8 <= 8 * h.stream_bytes) {
             if (stream[p >> 3]) return ORC_E_PADDING;
@@ -630,6 +938,8 @@ int orc_decode(const uint8_t* blob, uint64_t bytes, uint16_t* out, uint64_t out_
         rep->group_align = h.A;
         rep->group_max_elems = h.M;
         rep->max_code_len = h.max_len;
+        rep->layout = h.version == 3 ? 1u : 0u;
+        rep->seg_max_bits = h.B;
         rep->n_symbols = m;
         rep->longest_code = longest;
         rep->kraft_num = kraft;

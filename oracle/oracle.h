@@ -67,6 +67,8 @@ typedef struct {
     double   entropy_bits;     /* H of the exponent histogram, bits/symbol   */
     double   mean_code_bits;   /* sum(count * len) / n                       */
     uint64_t hist[256];        /* exponent histogram of the decoded data     */
+    uint32_t layout;           /* 0: per-chunk gaps (version 2); 1: lanes (3) */
+    uint32_t seg_max_bits;     /* lanes layout: stream bits per segment max  */
 } orc_report;
 
 /* Split bf16 words into exponent and sign+mantissa planes (definition). */
@@ -96,7 +98,16 @@ int orc_encode(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n
                uint32_t max_code_len, uint32_t chunks_per_group, uint32_t group_align,
                uint32_t group_max_elems, uint8_t** blob, uint64_t* blob_bytes);
 
-/* Serial bit-by-bit decoder with full container checks.
+/* Independent writer of the interleaved-lane layout (container version 3):
+ * segments of whole group_align-element blocks, at most group_max_elems
+ * elements and at most seg_max_bits (< 65536, >= group_align * max_code_len)
+ * stream bits; 64 lanes per segment, lane j taking 8-element lane blocks
+ * j, j + 64, ...; each lane's codewords contiguous, lanes in order. */
+int orc_encode_lanes(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
+                     uint32_t max_code_len, uint32_t group_align, uint32_t group_max_elems,
+                     uint32_t seg_max_bits, uint8_t** blob, uint64_t* blob_bytes);
+
+/* Serial bit-by-bit decoder with full container checks (either layout).
  * out must hold out_cap >= n_elems words.  rep may be NULL. */
 int orc_decode(const uint8_t* blob, uint64_t blob_bytes, uint16_t* out, uint64_t out_cap,
                orc_report* rep);

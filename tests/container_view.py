@@ -1,8 +1,11 @@
 """Read-only numpy view of a container's sections, for tests.
 
 Restates the container v2 layout (256-byte header of little-endian fields,
-then 256-byte-aligned sections code_len, tensors, groups, gap, stream, sm) so
-that tests can inspect what an encoder wrote.  It decodes nothing.
+then 256-byte-aligned sections code_len, tensors, groups, gap, stream, sm) and
+the interleaved-lane layout v3 (the same header positions, with u8 lanes at
+9, u16 lane block at 10, u32 segment bit cap at 12, a u16 lane-offset section
+in place of the gaps and n_chunks = 0) so that tests can inspect what an
+encoder wrote.  It decodes nothing.
 """
 from __future__ import annotations
 
@@ -24,6 +27,10 @@ def header(blob: np.ndarray) -> dict:
     h = {k: struct.unpack_from(fmt, raw, off)[0] for k, (off, fmt) in HEADER_FIELDS.items()}
     h["magic"] = raw[:4]
     h["version"] = struct.unpack_from("<H", raw, 4)[0]
+    if h["version"] == 3:
+        h["lanes"] = raw[9]
+        h["lane_block"] = struct.unpack_from("<H", raw, 10)[0]
+        h["seg_max_bits"] = struct.unpack_from("<I", raw, 12)[0]
     return h
 
 
@@ -34,7 +41,10 @@ def sections(blob: np.ndarray) -> dict:
     s["code_len"] = blob[h["off_len"]:h["off_len"] + 256]
     s["tensors"] = blob[h["off_tens"]:h["off_tens"] + 16 * nt].view(np.uint64).reshape(nt, 2)
     s["groups"] = blob[h["off_gs"]:h["off_gs"] + 16 * (ng + 1)].view(np.uint64).reshape(ng + 1, 2)
-    s["gap"] = blob[h["off_gap"]:h["off_gap"] + nc]
+    if h["version"] == 3:
+        s["lane_off"] = blob[h["off_gap"]:h["off_gap"] + 2 * 64 * ng].view(np.uint16).reshape(ng, 64)
+    else:
+        s["gap"] = blob[h["off_gap"]:h["off_gap"] + nc]
     s["stream"] = blob[h["off_stream"]:h["off_stream"] + h["stream_bytes"]]
     s["sm"] = blob[h["off_sm"]:h["off_sm"] + n]
     return s
@@ -75,3 +85,37 @@ def expected_metadata(exps: np.ndarray, code_len: np.ndarray, chunks_per_group: 
         groups.append((min(end * A, n), int(block_bit[end])))
         k = end
     return total, gap, np.array(groups, dtype=np.uint64)
+
+
+def expected_segments(exps: np.ndarray, code_len: np.ndarray, group_align: int, group_max_elems: int,
+                      seg_max_bits: int) -> np.ndarray:
+    """Segment table of the interleaved-lane layout, from first principles:
+    runs of whole A-element blocks (at least one), as long as possible while
+    they hold at most M elements and their codewords at most B bits; entries
+    {first element, bits before it}, then {n, total bits}."""
+    lens = code_len.astype(np.int64)[exps.astype(np.int64)]
+    n = exps.size
+    A = int(group_align)
+    csum = np.concatenate([[0], np.cumsum(lens)])
+    block_bit = csum[np.minimum(np.arange(0, n + A, A)[: -(-n // A) + 1], n)]
+    nb = block_bit.size - 1
+    segs = [(0, 0)]
+    k = 0
+    while k < nb:
+        # last block end whose bits from block k stay within B, at least one block, at most M elements
+        end = int(np.searchsorted(block_bit, block_bit[k] + int(seg_max_bits), side="right")) - 1
+        end = min(max(end, k + 1), nb, k + int(group_max_elems) // A)
+        segs.append((min(end * A, n), int(block_bit[end])))
+        k = end
+    return np.array(segs, dtype=np.uint64)
+
+
+def lane_permutation(m: int) -> np.ndarray:
+    """Element order (inside a segment of m elements) in which the
+    interleaved-lane layout stores codewords: element i belongs to lane
+    (i // 8) % 64; a lane's elements keep their order, lanes follow each
+    other from 0 to 63."""
+    idx = np.arange(m)
+    lane = (idx // 8) % 64
+    order = np.lexsort((idx, lane))     # by lane, then by element
+    return order
