@@ -38,23 +38,25 @@ if ROOT not in sys.path:
 
 METRIC = "decompressed bf16 GB/s and % of HBM roofline (1 MI355X), bit-exact"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "lossless_entropy_coded_amd", "csrc", "decode.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_block_8b_traffic.json")
+CSRC = os.path.join(ROOT, "lossless_entropy_coded_amd", "csrc")
+KERNEL_SOURCES = {"chunks": os.path.join(CSRC, "decode.hip"), "lanes": os.path.join(CSRC, "decode_lanes.hip")}
+TRAFFIC_FILES = {"chunks": os.path.join(ROOT, "profiles", "decode_block_8b_traffic.json"),
+                 "lanes": os.path.join(ROOT, "profiles", "decode_lanes_block_8b_traffic.json")}
 
 
-def kernel_source_sha() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def kernel_source_sha(layout: str = "chunks") -> str:
+    with open(KERNEL_SOURCES[layout], "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, layout: str = "chunks"):
     """HBM bytes per launch measured with rocprofv3 counters, if still valid."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILES[layout]) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_sha() or rec.get("workload") != workload:
+    if rec.get("kernel_source_sha256") != kernel_source_sha(layout) or rec.get("workload") != workload:
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -70,6 +72,9 @@ def parse_args():
     ap.add_argument("--workload", default="block_8b",
                     help="synthetic workload (default: block_8b, the 8B-shape transformer block)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--layout", choices=["chunks", "lanes"], default="chunks",
+                    help="container layout: chunks (v2, per-chunk gaps; the default) or lanes (v3, "
+                         "interleaved lanes)")
     ap.add_argument("--e2e", action="store_true",
                     help="70B-shape block end to end: decode + batch-1 GEMVs against GEMVs on resident "
                          "uncompressed weights (prints its own JSON line)")
@@ -274,14 +279,16 @@ def main():
 
     t_gen = time.perf_counter()
     wl = make_workload(args.workload)
-    blob = wc.encode_host(wl.tensors())
+    blob = wc.encode_host(wl.tensors(), layout=args.layout)
     t_gen = time.perf_counter() - t_gen
     n = wl.n
     plan = wc.Plan(blob, device=0)
     st = plan.stats()
     stream_bits = st["stream_bits"]
-    n_chunks = -(-stream_bits // 64)
-    alg_read = n + -(-stream_bits // 8) + n_chunks + 16 * (st["n_groups"] + 1)
+    # what the kernel must read: sm plane, stream, per-chunk gaps (v2) or
+    # per-lane offsets (v3), group/segment table; then the bf16 it writes
+    aux = -(-stream_bits // 64) if args.layout == "chunks" else 2 * 64 * st["n_groups"]
+    alg_read = n + -(-stream_bits // 8) + aux + 16 * (st["n_groups"] + 1)
     alg_bytes = alg_read + 2 * n
 
     per_copy = blob.size + 2 * n
@@ -386,6 +393,7 @@ def main():
         "data": "synthetic: seeded bf16 weights, transformer-block shapes and distributions",
         "config": {
             "workload": f"{args.workload}: {desc}",
+            "layout": args.layout,
             "n_elems": n,
             "n_tensors": len(wl.numels),
             "container_bytes": int(blob.size),
@@ -407,7 +415,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic(args.workload),
+            "traffic": recorded_traffic(args.workload, args.layout),
             "algorithmic_bytes_per_launch": alg_bytes,
             "kernel_avg_ms": round(kernel_avg_ms, 5),
             "launch_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},

@@ -44,6 +44,23 @@
  * multiple of A elements, so with A = 128 every 128-byte line of the bf16
  * output and of the sm plane belongs to one group.
  *
+ * Container v3, the interleaved-lane layout (the LazyWeights page, analogy
+ * section: Huffman codes stored in interleaved lanes and decoded on demand):
+ * the same header positions, code and planes, except
+ *   header: u16 version=3; u8 lanes=64 at 9; u16 lane_block=8 at 10;
+ *     u32 seg_max_bits B at 12 (in place of G); n_chunks = 0;
+ *   groups      the segment table: segments are runs of whole A-element
+ *               blocks, as long as possible while they hold at most M
+ *               elements and their codewords at most B bits;
+ *   lane_off    u16[64 * n_segs] at the gap section's place: inside a
+ *               segment, 8-element lane blocks are dealt to 64 lanes (lane j
+ *               takes lane blocks j, j + 64, ...); lane j's codewords (its
+ *               lane blocks in order) are contiguous and start at bit
+ *               first_bit + lane_off[64 g + j]; lanes follow each other;
+ *   stream      ceil(stream_bits / 8) rounded up to 8, plus 64 zero bytes.
+ * A lane decodes a known number of symbols from its own bit string, so the
+ * decoder needs no per-chunk gaps, no counting pass and no scan.
+ *
  * Status codes: 0 on success, a negative WC_ERR_* value otherwise.  No C++
  * exception ever crosses this interface.
  */
@@ -86,7 +103,15 @@ typedef struct {
     uint32_t group_max_elems;   /* M, a multiple of A: elements per group at most; 0    */
                                 /* selects the default 4096, the most the GPU decoder   */
                                 /* accepts.                                             */
+    uint32_t layout;            /* WC_LAYOUT_CHUNKS (0, container v2) or                */
+                                /* WC_LAYOUT_LANES (1, container v3)                    */
+    uint32_t seg_max_bits;      /* v3: stream bits per segment at most, >= A *          */
+                                /* max_code_len and < 65536; 0 selects the default      */
+                                /* 15872, the most the GPU decoder accepts.             */
 } wc_encode_opts;
+
+#define WC_LAYOUT_CHUNKS 0u
+#define WC_LAYOUT_LANES  1u
 
 /*
  * wc_encode_host -- offline preparation of one container from n_tensors bf16

@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libwc.so")
-SOURCES = ["decode.hip", "gemv.hip", "plan.cpp", "encode.cpp"]
+SOURCES = ["decode.hip", "decode_lanes.hip", "gemv.hip", "plan.cpp", "encode.cpp"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",

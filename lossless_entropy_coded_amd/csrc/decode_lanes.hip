@@ -1,0 +1,292 @@
+// decode_lanes.hip -- gfx950 decode kernel of libwc for the interleaved-lane
+// container (version 3).
+//
+// The LazyWeights page (analogy section) stores Huffman codes in interleaved
+// lanes that are decoded on demand.  Here a segment (at most 4096 elements and
+// 15872 stream bits) is one wave64's unit, and lane j of the wave owns the
+// segment's 8-element lane blocks j, j + 64, ..., whose codewords are stored
+// contiguously from the lane's own offset.  So every lane knows where its bits
+// start and how many symbols it decodes: no per-chunk gaps, no counting pass
+// and no scan.  Lane j's lane blocks are exactly the blocks it writes in the
+// merge (block j + 64k in step k), so the exponent bytes go from the lane's
+// registers to its own 8-byte LDS slots and back, never across lanes.
+//
+// Per segment and wave:
+//   stage   the segment's stream bytes (at most 1984, plus the alignment and
+//           the lookahead) arrive one iteration early as two 16-byte loads per
+//           lane and are written byte-swapped to the wave's LDS words, so that
+//           word k holds stream bits 32k .. 32k + 31 MSB-first;
+//   decode  each lane keeps a 64-bit MSB-first window of its bits (refilled
+//           one LDS word at a time, at least 32 bits valid before a lookup)
+//           and looks up the multi-codeword table (up to four symbols per
+//           lookup, as the chunked kernel); symbols are appended to a 12-byte
+//           queue, and every 8 of them go to the lane's next 8-byte slot;
+//   merge   as the chunked kernel: the sign+mantissa bytes (loaded while the
+//           lanes decode) and the staged exponents become bf16 in registers,
+//           written with 16-byte non-temporal stores, whole cache lines.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "decode_common.h"
+#include "format.h"
+#include "kernels.h"
+
+namespace wc {
+namespace {
+
+constexpr uint32_t kStageWords = kLaneStageBytes / 4;
+
+// One lane's loads for one segment: its two 16-byte pieces of the segment's
+// stream window (pieces past the bytes the segment needs are not loaded) and
+// the offset of its own bits.
+struct LaneRaw {
+    uint4 q0, q1;
+    uint32_t off;
+};
+
+__device__ __forceinline__ LaneRaw load_lane_raw(const DecodeParams& p, const Meta& m, uint64_t g, uint32_t lane) {
+    LaneRaw r;
+    const uint64_t base = (m.p0 >> 7) << 4;                    // 16-byte aligned first byte
+    const uint64_t need = ((m.p1 + 7) >> 3) + 8 - base;        // bytes up to the last bit, plus the lookahead
+    const uint8_t* q = p.stream + base;
+    r.q0 = make_uint4(0, 0, 0, 0);
+    r.q1 = make_uint4(0, 0, 0, 0);
+    if (16u * lane < need) r.q0 = *reinterpret_cast<const uint4*>(q + 16u * lane);
+    if (16u * (lane + kWaveLanes) < need) r.q1 = *reinterpret_cast<const uint4*>(q + 16u * (lane + kWaveLanes));
+    r.off = reinterpret_cast<const uint16_t*>(p.gap)[kLanes * g + lane];
+    return r;
+}
+
+__device__ __forceinline__ uint4 bswap4(const uint4& v) {
+    return make_uint4(__builtin_bswap32(v.x), __builtin_bswap32(v.y), __builtin_bswap32(v.z),
+                      __builtin_bswap32(v.w));
+}
+
+template <int KD, int W>
+__global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodeParams p) {
+    constexpr uint32_t kThreads = kWaveLanes * W;
+    // multi-codeword table, then the canonical arrays for long codes (the
+    // plan's tables from the multi-codeword table on)
+    constexpr uint32_t kDecVec = (2u << KD) / 4, kLongVec = kLongWords / 4;
+    constexpr uint32_t kTabVec = kDecVec + kLongVec;
+    __shared__ __attribute__((aligned(16))) uint4 s_tab[kTabVec];
+    const uint2* const s_dec = reinterpret_cast<const uint2*>(s_tab);
+    const uint32_t* const s_long = reinterpret_cast<const uint32_t*>(s_tab + kDecVec);
+    // dynamic: per wave, kLaneStageBytes of stream words then kGroupMaxElems
+    // exponent bytes; then the second-level table (l2_cap * 2^kL2Bits u16)
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+    uint16_t* const s_l2 = reinterpret_cast<uint16_t*>(dyn + W * kLaneWaveBytes);
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint32_t* const sbuf = reinterpret_cast<uint32_t*>(dyn + wave * kLaneWaveBytes);
+    uint8_t* const ebuf = dyn + wave * kLaneWaveBytes + kLaneStageBytes;
+
+    // wave w of workgroup b takes segments b*W + w, then every (grid * W)-th
+    const uint64_t stride = (uint64_t)gridDim.x * W;
+    uint64_t u = p.u_begin + (uint64_t)blockIdx.x * W + wave;
+    const uint64_t last_u = p.u_end - 1;
+    const bool active = u < p.u_end;
+
+    // prologue: the first segment's table entries and loads are in flight
+    // while the workgroup stages the tables
+    const Meta m_first = load_meta(p, min_u64(u, last_u));
+    constexpr uint32_t kFull = kTabVec / kThreads;
+    constexpr uint32_t kTail = kTabVec - kFull * kThreads;
+    const u32x4* const tsrc = reinterpret_cast<const u32x4*>(p.tables);
+    u32x4* const tdst = reinterpret_cast<u32x4*>(s_tab);
+    u32x4 stage[kFull > 0 ? kFull : 1];
+#pragma unroll
+    for (uint32_t k = 0; k < kFull; ++k) stage[k] = tsrc[tid + k * kThreads];
+    u32x4 stage_tail = {0, 0, 0, 0};
+    if (kTail && tid < kTail) stage_tail = tsrc[kFull * kThreads + tid];
+    Meta cur_m = uniform_meta(m_first);
+    LaneRaw cur_r = load_lane_raw(p, cur_m, min_u64(u, last_u), lane);
+    Meta m_next = load_meta(p, min_u64(u + stride, last_u));
+#pragma unroll
+    for (uint32_t k = 0; k < kFull; ++k) tdst[tid + k * kThreads] = stage[k];
+    if (kTail && tid < kTail) tdst[kFull * kThreads + tid] = stage_tail;
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(p.tables) + kTabVec;
+        for (uint32_t i = tid; i < (p.l2_cap << kL2Bits) / 8; i += kThreads)
+            reinterpret_cast<uint4*>(s_l2)[i] = src[i];
+    }
+    __syncthreads();
+    if (!active) return;
+    LongTables lt;
+    lt.count = s_long;
+    lt.first = s_long + 32;
+    lt.base = s_long + 64;
+    lt.sorted = reinterpret_cast<const uint8_t*>(s_long + 96);
+    lt.l2 = s_l2;
+    lt.l2_first = __builtin_amdgcn_readfirstlane(s_long[160]);
+    lt.l2_n = min(__builtin_amdgcn_readfirstlane(s_long[161]), p.l2_cap);
+    m_next = uniform_meta(m_next);
+
+    for (;;) {
+        const uint64_t un = u + stride;
+        const bool more = un < p.u_end;
+
+        // the segment's stream words, byte-swapped (word k = bits 32k.. MSB-first)
+        reinterpret_cast<uint4*>(sbuf)[lane] = bswap4(cur_r.q0);
+        reinterpret_cast<uint4*>(sbuf)[lane + kWaveLanes] = bswap4(cur_r.q1);
+        const uint32_t off = cur_r.off;
+
+        // next segment's loads, this segment's sign+mantissa bytes, the table
+        // entries of the segment after next
+        const LaneRaw nxt = load_lane_raw(p, m_next, min_u64(un, last_u), lane);
+        const uint64_t A = cur_m.e0;
+        const uint32_t n = (uint32_t)min_u64(cur_m.e1 - cur_m.e0, kGroupMaxElems);
+        const uint32_t last_blk = (n - 1) / kMergeElems;
+        const uint8_t* const smu = p.sm + A;
+        uint16_t* const outu = p.out + A;
+        uint2 smv[kMergeSteps];
+#pragma unroll
+        for (uint32_t k = 0; k < kMergeSteps; ++k)
+            smv[k] = load_nt8(smu + kMergeElems * min(lane + k * kWaveLanes, last_blk));
+        const Meta m_after = load_meta(p, min_u64(un + stride, last_u));
+        wave_lds_order();
+
+        // decode: this lane's symbols (8 per lane block it owns; the
+        // container's last block may be shorter)
+        {
+            const uint32_t nb8 = (n + kLaneBlock - 1) / kLaneBlock;
+            const uint32_t cnt = lane < nb8 ? (nb8 - 1 - lane) / kWaveLanes + 1 : 0u;
+            uint32_t left = kLaneBlock * cnt;
+            if (cnt && lane == (nb8 - 1) % kWaveLanes) left -= kLaneBlock * nb8 - n;
+            const uint32_t pos = (uint32_t)(cur_m.p0 & 127u) + off;   // first bit in the staged words
+            uint32_t wi = pos >> 5;
+            uint64_t win = (((uint64_t)sbuf[wi] << 32) | sbuf[wi + 1]) << (pos & 31u);
+            int32_t valid = 64 - (int32_t)(pos & 31u);
+            wi += 2;
+            uint64_t q = 0;        // pending exponent bytes, first in the lowest byte
+            uint32_t q2 = 0;       // bytes 8..11 of the queue
+            uint32_t c = 0;        // bytes pending
+            uint32_t slot = lane;  // next lane block: lane + 64 k
+            while (left > 0) {
+                const uint32_t top = (uint32_t)(win >> 32);
+                uint2 e = s_dec[top >> (32 - KD)];
+                if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
+                const uint32_t nbits = (e.x >> 16) & 0xFFu;
+                const uint32_t ns = min((e.x >> 8) & 0xFFu, left);
+                // symbols past the lane's last belong to the next lane: the
+                // loop ends with them, and they never reach a full block
+                q |= (uint64_t)e.y << (8 * c);
+                q2 |= c > 4 ? e.y >> (64 - 8 * c) : 0u;
+                c += ns;
+                left -= ns;
+                win <<= nbits;
+                valid -= (int32_t)nbits;
+                if (valid < 32) {
+                    win |= (uint64_t)sbuf[min(wi, kStageWords - 1)] << (32 - valid);
+                    ++wi;
+                    valid += 32;
+                }
+                if (c >= kLaneBlock) {
+                    *reinterpret_cast<uint2*>(ebuf + kLaneBlock * slot) = make_uint2((uint32_t)q, (uint32_t)(q >> 32));
+                    slot += kWaveLanes;
+                    q = q2;
+                    q2 = 0;
+                    c -= kLaneBlock;
+                }
+            }
+            if (c) *reinterpret_cast<uint2*>(ebuf + kLaneBlock * slot) = make_uint2((uint32_t)q, (uint32_t)(q >> 32));
+        }
+
+        const LaneRaw next_r = nxt;
+        const Meta next_m = m_next;
+        m_next = uniform_meta(m_after);
+        wave_lds_order();
+
+        // merge: step k of lane i is block 64k + i, the lane's own slots
+        const uint32_t full = n / kMergeElems;
+#pragma unroll
+        for (uint32_t k = 0; k < kMergeSteps; ++k) {
+            const uint32_t blk = lane + k * kWaveLanes;
+            if (blk < full) {
+                const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + kMergeElems * blk);
+                uint32_t o0, o1, o2, o3;
+                join4(smv[k].x, e2.x, o0, o1);
+                join4(smv[k].y, e2.y, o2, o3);
+                u32x4 v;
+                v.x = o0;
+                v.y = o1;
+                v.z = o2;
+                v.w = o3;
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(outu + kMergeElems * blk));
+            }
+        }
+        // the container's last block, when it holds fewer than 8 elements
+        if (full * kMergeElems < n && lane == 0) {
+            const uint32_t rel = kMergeElems * full;
+            const uint2 s2 = load_nt8(p.sm + A + rel);
+            const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + rel);
+            uint32_t o[4];
+            join4(s2.x, e2.x, o[0], o[1]);
+            join4(s2.y, e2.y, o[2], o[3]);
+#pragma unroll
+            for (uint32_t i = 0; i < kMergeElems; ++i)
+                if (rel + i < n) p.out[A + rel + i] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
+        }
+
+        if (!more) break;
+        wave_lds_order();   // the staging is rewritten by the next segment
+        u = un;
+        cur_m = next_m;
+        cur_r = next_r;
+    }
+}
+
+template <int KD, int W>
+struct LanesVariant {
+    static hipError_t launch(const DecodeParams& p, uint32_t grid, uint32_t dyn, hipStream_t stream) {
+        hipLaunchKernelGGL((decode_lanes_kernel<KD, W>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
+        return hipGetLastError();
+    }
+    static int blocks_per_cu(uint32_t dyn) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lanes_kernel<KD, W>, kWaveLanes * W, dyn) !=
+            hipSuccess)
+            return 0;
+        return n;
+    }
+};
+
+template <typename F>
+hipError_t dispatch_lanes(uint32_t decode_bits, uint32_t waves, F&& f) {
+    if (decode_bits == 11) return waves == 8 ? f(LanesVariant<11, 8>{}) : f(LanesVariant<11, 4>{});
+    return waves == 8 ? f(LanesVariant<10, 8>{}) : f(LanesVariant<10, 4>{});
+}
+
+}  // namespace
+
+uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap) {
+    return waves * kLaneWaveBytes + (l2_cap << kL2Bits) * 2;
+}
+
+uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap) {
+    return ((2u << decode_bits) + kLongWords) * 4 + decode_lanes_dyn_lds_bytes(waves, l2_cap);
+}
+
+int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap) {
+    if ((decode_bits != 11 && decode_bits != 10) || !supported_waves(waves)) return 0;
+    const uint32_t dyn = decode_lanes_dyn_lds_bytes(waves, l2_cap);
+    int n = 0;
+    (void)dispatch_lanes(decode_bits, waves, [&](auto v) {
+        n = decltype(v)::blocks_per_cu(dyn);
+        return hipSuccess;
+    });
+    return n;
+}
+
+hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid,
+                               hipStream_t stream) {
+    if ((decode_bits != 11 && decode_bits != 10) || !supported_waves(waves) || p.l2_cap > kL2Prefixes)
+        return hipErrorInvalidValue;
+    const uint32_t dyn = decode_lanes_dyn_lds_bytes(waves, p.l2_cap);
+    return dispatch_lanes(decode_bits, waves, [&](auto v) { return decltype(v)::launch(p, grid, dyn, stream); });
+}
+
+}  // namespace wc

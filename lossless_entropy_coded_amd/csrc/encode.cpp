@@ -16,6 +16,11 @@
 //      every 64-bit chunk the offset of its first codeword (with the group
 //      table, the auxiliary variables of the DFloat11 abstract, design point
 //      (ii)).
+// The interleaved-lane layout (container v3; the LazyWeights page stores
+// Huffman codes in interleaved lanes) shares steps 1-4, cuts segments by a
+// bit cap instead of a chunk cap in step 5, and in step 6 writes each
+// segment lane by lane: lane j's lane blocks j, j + 64, ... of 8 elements,
+// with a u16 offset per lane.
 #include <algorithm>
 #include <array>
 #include <atomic>
@@ -146,6 +151,104 @@ void parallel_for(unsigned nthreads, F&& f) {
     for (auto& x : th) x.join();
 }
 
+// MSB-first bit writer over a byte range whose first and last bytes may be
+// shared with a neighbouring writer (those two are OR-ed in atomically).
+struct BitWriter {
+    uint8_t* stream;
+    uint64_t wbyte;
+    uint32_t acc = 0;
+    int nacc;
+    bool shared_head;
+    BitWriter(uint8_t* s, uint64_t pos) : stream(s), wbyte(pos >> 3), nacc((int)(pos & 7)), shared_head(nacc != 0) {}
+    void put_code(uint32_t code, int L) {   // L <= 24
+        acc = (acc << L) | code;
+        nacc += L;
+        while (nacc >= 8) {
+            nacc -= 8;
+            const uint8_t v = (uint8_t)(acc >> nacc);
+            if (shared_head) {
+                __atomic_fetch_or(stream + wbyte, v, __ATOMIC_RELAXED);
+                shared_head = false;
+            } else {
+                stream[wbyte] = v;
+            }
+            ++wbyte;
+        }
+        acc &= (1u << nacc) - 1u;
+    }
+    void finish() {
+        if (nacc) __atomic_fetch_or(stream + wbyte, (uint8_t)(acc << (8 - nacc)), __ATOMIC_RELAXED);
+    }
+};
+
+// Container v3: segments of whole blocks (at most max_elems elements and
+// seg_bits stream bits), each written lane by lane.
+int write_lanes(const Source& src, uint64_t n, uint32_t n_tensors, const uint8_t len[256], const uint32_t code[256],
+                uint32_t max_len, uint32_t align, uint32_t max_elems, uint32_t seg_bits,
+                const std::vector<uint64_t>& block_bit, uint64_t stream_bits, unsigned nthreads, uint8_t** blob,
+                uint64_t* blob_bytes) {
+    const uint64_t n_blocks = block_bit.size() - 1;
+    std::vector<uint64_t> s_elem{0}, s_bit{0};
+    for (uint64_t k0 = 0; k0 < n_blocks;) {
+        uint64_t k1 = k0 + 1;
+        const uint64_t k_cap = k0 + max_elems / align;
+        while (k1 < n_blocks && k1 < k_cap && block_bit[k1 + 1] - block_bit[k0] <= seg_bits) ++k1;
+        s_elem.push_back(std::min<uint64_t>(k1 * align, n));
+        s_bit.push_back(block_bit[k1]);
+        k0 = k1;
+    }
+    const uint64_t n_segs = s_elem.size() - 1;
+    const Header h = layout_lanes(n, stream_bits, n_tensors, max_len, align, max_elems, seg_bits, n_segs);
+    uint8_t* out = (uint8_t*)std::aligned_alloc(kAlign, h.total_bytes);
+    if (!out) return WC_ERR_NOMEM;
+    std::memset(out, 0, h.off_sm);
+    std::memset(out + h.off_sm + n, 0, h.total_bytes - h.off_sm - n);
+    write_header(out, h);
+    std::memcpy(out + h.off_code_len, len, 256);
+    for (uint32_t k = 0; k < n_tensors; ++k) {
+        store_le<uint64_t>(out + h.off_tensors + 16ull * k, src.begin[k]);
+        store_le<uint64_t>(out + h.off_tensors + 16ull * k + 8, src.size[k]);
+    }
+    for (uint64_t g = 0; g <= n_segs; ++g) {
+        store_le<uint64_t>(out + h.off_groups + kGroupEntryBytes * g, s_elem[g]);
+        store_le<uint64_t>(out + h.off_groups + kGroupEntryBytes * g + 8, s_bit[g]);
+    }
+    uint8_t* stream = out + h.off_stream;
+    uint8_t* lane_off = out + h.off_gap;
+    uint8_t* sm = out + h.off_sm;
+    const unsigned T = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(nthreads, n_segs));
+    parallel_for(T, [&](unsigned t) {
+        const uint64_t g0 = n_segs * t / T, g1 = n_segs * (t + 1) / T;
+        if (g0 == g1) return;
+        BitWriter bw(stream, s_bit[g0]);
+        uint64_t pos = s_bit[g0];
+        std::vector<uint16_t> seg(max_elems);
+        for (uint64_t g = g0; g < g1; ++g) {
+            const uint64_t e0 = s_elem[g], m = s_elem[g + 1] - e0;
+            src.for_range(e0, e0 + m, [&](uint64_t gi, const uint16_t* p, uint64_t k) {
+                std::memcpy(seg.data() + (gi - e0), p, k * sizeof(uint16_t));
+            });
+            for (uint64_t i = 0; i < m; ++i) sm[e0 + i] = sign_mantissa_of(seg[i]);
+            const uint64_t nb8 = div_up(m, kLaneBlock);
+            for (uint32_t j = 0; j < kLanes; ++j) {
+                store_le<uint16_t>(lane_off + 2 * (kLanes * g + j), (uint16_t)(pos - s_bit[g]));
+                for (uint64_t b = j; b < nb8; b += kLanes) {
+                    const uint64_t i1 = std::min<uint64_t>(m, kLaneBlock * (b + 1));
+                    for (uint64_t i = kLaneBlock * b; i < i1; ++i) {
+                        const uint8_t e = exponent_of(seg[i]);
+                        bw.put_code(code[e], len[e]);
+                        pos += len[e];
+                    }
+                }
+            }
+        }
+        bw.finish();
+    });
+    *blob = out;
+    *blob_bytes = h.total_bytes;
+    return WC_OK;
+}
+
 }  // namespace
 }  // namespace wc
 
@@ -157,7 +260,7 @@ extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* nu
     *blob_bytes = 0;
     if (n_tensors && (!tensors || !numels)) return WC_ERR_INVALID_ARG;
     uint32_t max_len = kMaxCodeLen, group = kDefaultGroup, align = kDefaultAlign, max_elems = kDefaultMaxElems;
-    uint32_t nthreads = 0;
+    uint32_t nthreads = 0, kind = WC_LAYOUT_CHUNKS, seg_bits = kDefaultSegBits;
     if (opts) {
         if (opts->max_code_len) max_len = opts->max_code_len;
         if (opts->chunk_bytes && opts->chunk_bytes != 8) return WC_ERR_INVALID_ARG;
@@ -165,13 +268,22 @@ extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* nu
         if (opts->group_align) align = opts->group_align;
         if (opts->group_max_elems) max_elems = opts->group_max_elems;
         nthreads = opts->n_threads;
+        kind = opts->layout;
+        if (opts->seg_max_bits) seg_bits = opts->seg_max_bits;
     }
     if (max_len < 1 || max_len > kMaxCodeLen || group < 1 || group > (1u << 20) || align > (1u << 20) ||
-        max_elems < align || max_elems % align)
+        max_elems < align || max_elems % align || max_elems > (1u << 26))
         return WC_ERR_INVALID_ARG;
-    // every block must fit in one group whatever its codes: align codewords of
-    // up to max_len bits, starting anywhere in a chunk, touch at most G chunks
-    if ((uint64_t)align * max_len + (kChunkBits - 1) > (uint64_t)kChunkBits * group) return WC_ERR_INVALID_ARG;
+    if (kind == WC_LAYOUT_CHUNKS) {
+        // every block must fit in one group whatever its codes: align codewords of
+        // up to max_len bits, starting anywhere in a chunk, touch at most G chunks
+        if ((uint64_t)align * max_len + (kChunkBits - 1) > (uint64_t)kChunkBits * group) return WC_ERR_INVALID_ARG;
+    } else if (kind == WC_LAYOUT_LANES) {
+        // a segment's lane offsets are u16 bit counts; one block always fits
+        if (seg_bits > 65535u || (uint64_t)align * max_len > seg_bits) return WC_ERR_INVALID_ARG;
+    } else {
+        return WC_ERR_INVALID_ARG;
+    }
 
     Source src;
     uint64_t n = 0;
@@ -233,6 +345,9 @@ extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* nu
         });
     });
     block_bit[n_blocks] = stream_bits;
+    if (kind == WC_LAYOUT_LANES)
+        return write_lanes(src, n, n_tensors, len, code, max_len, align, max_elems, seg_bits, block_bit, stream_bits,
+                           nthreads, blob, blob_bytes);
     std::vector<uint64_t> g_elem{0}, g_bit{0};
     for (uint64_t k0 = 0; k0 < n_blocks;) {
         uint64_t k1 = k0 + 1;

@@ -1,5 +1,7 @@
-// format.h -- container v1 layout shared by the host encoder, the planner and
-// the device decoder of libwc.  (The CPU oracle keeps its own restatement.)
+// format.h -- container layouts shared by the host encoder, the planner and
+// the device decoder of libwc: version 2 (per-chunk gaps and a group table)
+// and version 3 (interleaved lanes).  (The CPU oracle keeps its own
+// restatement.)
 #pragma once
 
 #include <cstdint>
@@ -18,6 +20,16 @@ constexpr uint32_t kDefaultAlign = 128;    // elements per block: groups start a
 constexpr uint32_t kDefaultMaxElems = 4096; // elements a group may hold at most
 constexpr uint32_t kStreamSlack = 16;      // zero bytes after the last chunk
 
+// Version 3, the interleaved-lane layout: per segment (a run of whole blocks),
+// 8-element lane blocks are dealt to 64 lanes (lane j: lane blocks j, j + 64,
+// ...); each lane's codewords are contiguous, lanes follow each other, and a
+// u16 per lane gives its first bit relative to the segment's.
+constexpr uint16_t kVersionLanes = 3;
+constexpr uint32_t kLanes = 64;
+constexpr uint32_t kLaneBlock = 8;
+constexpr uint32_t kLanesSlack = 64;       // zero bytes after the 8-byte-padded stream
+constexpr uint32_t kDefaultSegBits = 15872;   // stream bits per segment at most (1984 bytes)
+
 // Header field offsets (little-endian).
 struct HeaderOffsets {
     static constexpr int magic = 0, version = 4, flags = 6, max_code_len = 8, chunk_bits = 9,
@@ -26,9 +38,14 @@ struct HeaderOffsets {
                          off_code_len = 56, off_tensors = 64, off_groups = 72, off_gap = 80,
                          off_stream = 88, stream_bytes = 96, off_sm = 104, total_bytes = 112,
                          group_max_elems = 120, reserved_tail = 124;
+    // version 3 reuses the positions: lanes at 9, lane block at 10, the
+    // segment bit cap at 12, the lane offsets at off_gap; n_chunks is 0
+    static constexpr int lanes = 9, lane_block = 10, seg_max_bits = 12;
 };
 
 struct Header {
+    uint32_t version = kVersion;   // kVersion or kVersionLanes
+    uint32_t seg_max_bits = 0;     // version 3
     uint32_t max_code_len = 0, chunks_per_group = 0, n_tensors = 0, group_align = 0, group_max_elems = 0;
     uint64_t n_elems = 0, stream_bits = 0, n_chunks = 0, n_groups = 0;
     uint64_t off_code_len = 0, off_tensors = 0, off_groups = 0, off_gap = 0, off_stream = 0,
@@ -79,14 +96,46 @@ inline Header layout(uint64_t n_elems, uint64_t stream_bits, uint32_t n_tensors,
     return h;
 }
 
+// Section placement of a version-3 (interleaved-lane) container; the lane
+// offsets take the place of the gaps (off_gap).
+inline Header layout_lanes(uint64_t n_elems, uint64_t stream_bits, uint32_t n_tensors, uint32_t max_code_len,
+                           uint32_t align, uint32_t max_elems, uint32_t seg_max_bits, uint64_t n_segs) {
+    Header h;
+    h.version = kVersionLanes;
+    h.seg_max_bits = seg_max_bits;
+    h.max_code_len = max_code_len;
+    h.group_align = align;
+    h.group_max_elems = max_elems;
+    h.n_tensors = n_tensors;
+    h.n_elems = n_elems;
+    h.stream_bits = stream_bits;
+    h.n_chunks = 0;
+    h.n_groups = n_segs;
+    h.stream_bytes = round_up(div_up(stream_bits, 8), 8) + kLanesSlack;
+    h.off_code_len = kHeaderBytes;
+    h.off_tensors = round_up(h.off_code_len + 256, kAlign);
+    h.off_groups = round_up(h.off_tensors + 16ull * n_tensors, kAlign);
+    h.off_gap = round_up(h.off_groups + kGroupEntryBytes * (n_segs + 1), kAlign);
+    h.off_stream = round_up(h.off_gap + 2ull * kLanes * n_segs, kAlign);
+    h.off_sm = round_up(h.off_stream + h.stream_bytes, kAlign);
+    h.total_bytes = round_up(h.off_sm + n_elems, kAlign);
+    return h;
+}
+
 inline void write_header(uint8_t* p, const Header& h) {
     using O = HeaderOffsets;
     std::memset(p, 0, kHeaderBytes);
     store_le<uint32_t>(p + O::magic, kMagic);
-    store_le<uint16_t>(p + O::version, kVersion);
+    store_le<uint16_t>(p + O::version, (uint16_t)h.version);
     store_le<uint8_t>(p + O::max_code_len, (uint8_t)h.max_code_len);
-    store_le<uint8_t>(p + O::chunk_bits, (uint8_t)kChunkBits);
-    store_le<uint32_t>(p + O::chunks_per_group, h.chunks_per_group);
+    if (h.version == kVersionLanes) {
+        store_le<uint8_t>(p + O::lanes, (uint8_t)kLanes);
+        store_le<uint16_t>(p + O::lane_block, (uint16_t)kLaneBlock);
+        store_le<uint32_t>(p + O::seg_max_bits, h.seg_max_bits);
+    } else {
+        store_le<uint8_t>(p + O::chunk_bits, (uint8_t)kChunkBits);
+        store_le<uint32_t>(p + O::chunks_per_group, h.chunks_per_group);
+    }
     store_le<uint32_t>(p + O::n_tensors, h.n_tensors);
     store_le<uint32_t>(p + O::group_align, h.group_align);
     store_le<uint32_t>(p + O::group_max_elems, h.group_max_elems);

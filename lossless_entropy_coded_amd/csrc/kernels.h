@@ -107,6 +107,14 @@ struct DecodeParams {
     DotParams dot;           // fused matrix-vector launches only
 };
 
+// Interleaved-lane containers (version 3): each wave stages a segment's
+// stream window (its bits, the first bit's 16-byte alignment and 8 bytes of
+// lookahead) in kLaneStageBytes of LDS, then its exponent bytes; a segment
+// therefore holds at most kLanesMaxSegBits stream bits.
+constexpr uint32_t kLaneStageBytes = 2048;
+constexpr uint32_t kLaneWaveBytes = kLaneStageBytes + kGroupMaxElems;
+constexpr uint32_t kLanesMaxSegBits = 15872;
+
 // Wavefronts per decode workgroup the kernels are built for.
 inline bool supported_waves(uint32_t waves) { return waves == 4 || waves == 8; }
 
@@ -128,6 +136,16 @@ hipError_t launch_build_tables(const CodeLens& lens, uint32_t count_bits, uint32
 // the dynamic LDS): to bf16 in p.out, or (dot) to partial dot products in p.work.
 hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t decode_bits, uint32_t waves,
                          uint32_t grid, bool dot, hipStream_t stream);
+
+// Interleaved-lane decode: LDS bytes of one workgroup (decode table index
+// width decode_bits, 11 or 10), resident workgroups per CU, and one launch
+// decoding segments [p.u_begin, p.u_end) to bf16 in p.out; p.gap points at the
+// lane offsets and p.tables at the multi-codeword table of the plan's tables.
+uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap);
+uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap);
+int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap);
+hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid,
+                               hipStream_t stream);
 
 // One launch adding, for every global row of p.dot, the partial dot products
 // of the groups covering it, in group order, into the row's y.

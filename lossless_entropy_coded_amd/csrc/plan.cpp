@@ -34,6 +34,7 @@ struct wc_plan_s {
     uint32_t lds_bytes = 0;
     uint32_t ebuf_bytes = 0;
     uint32_t l2_cap = 0;         // long-code prefixes whose second-level entries are staged in LDS
+    bool lanes = false;          // container version 3 (interleaved lanes)
     uint32_t* d_tables = nullptr;
 };
 
@@ -47,14 +48,23 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
                        std::vector<uint64_t>& tnum, uint64_t& max_group_elems) {
     using O = HeaderOffsets;
     if (bytes < wc::kHeaderBytes) return WC_ERR_TRUNCATED;
-    if (load_le<uint32_t>(b + O::magic) != wc::kMagic || load_le<uint16_t>(b + O::version) != wc::kVersion ||
-        load_le<uint16_t>(b + O::flags) != 0 || b[O::chunk_bits] != wc::kChunkBits ||
-        load_le<uint16_t>(b + O::reserved0) != 0)
+    if (load_le<uint32_t>(b + O::magic) != wc::kMagic || load_le<uint16_t>(b + O::flags) != 0)
         return WC_ERR_BAD_MAGIC;
+    h.version = load_le<uint16_t>(b + O::version);
+    const bool lanes = h.version == wc::kVersionLanes;
+    if (lanes) {
+        if (b[O::lanes] != wc::kLanes || load_le<uint16_t>(b + O::lane_block) != wc::kLaneBlock ||
+            load_le<uint64_t>(b + O::n_chunks) != 0)
+            return WC_ERR_BAD_MAGIC;
+    } else if (h.version != wc::kVersion || b[O::chunk_bits] != wc::kChunkBits ||
+               load_le<uint16_t>(b + O::reserved0) != 0) {
+        return WC_ERR_BAD_MAGIC;
+    }
     for (uint32_t k = O::reserved_tail; k < wc::kHeaderBytes; ++k)
         if (b[k]) return WC_ERR_BAD_MAGIC;
     h.max_code_len = b[O::max_code_len];
-    h.chunks_per_group = load_le<uint32_t>(b + O::chunks_per_group);
+    h.chunks_per_group = lanes ? 0u : load_le<uint32_t>(b + O::chunks_per_group);
+    h.seg_max_bits = lanes ? load_le<uint32_t>(b + O::seg_max_bits) : 0u;
     h.n_tensors = load_le<uint32_t>(b + O::n_tensors);
     h.group_align = load_le<uint32_t>(b + O::group_align);
     h.group_max_elems = load_le<uint32_t>(b + O::group_max_elems);
@@ -70,23 +80,28 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
     h.stream_bytes = load_le<uint64_t>(b + O::stream_bytes);
     h.off_sm = load_le<uint64_t>(b + O::off_sm);
     h.total_bytes = load_le<uint64_t>(b + O::total_bytes);
-    if (h.max_code_len < 1 || h.max_code_len > wc::kMaxCodeLen || h.chunks_per_group < 1 || h.group_align < 1 ||
+    if (h.max_code_len < 1 || h.max_code_len > wc::kMaxCodeLen || h.group_align < 1 ||
         h.group_max_elems < h.group_align || h.group_max_elems % h.group_align)
+        return WC_ERR_BAD_MAGIC;
+    if (!lanes && h.chunks_per_group < 1) return WC_ERR_BAD_MAGIC;
+    if (lanes && (h.seg_max_bits > 65535u || (uint64_t)h.group_align * h.max_code_len > h.seg_max_bits))
         return WC_ERR_BAD_MAGIC;
     if (h.total_bytes > bytes) return WC_ERR_TRUNCATED;
 
     // size fields
     if (h.n_elems > (1ull << 40) || h.stream_bits > h.n_elems * (uint64_t)h.max_code_len ||
-        h.stream_bits < h.n_elems || h.n_chunks != wc::div_up(h.stream_bits, wc::kChunkBits) ||
-        h.n_groups > h.n_elems || (h.n_groups == 0) != (h.n_elems == 0) ||
-        h.stream_bytes != h.n_chunks * 8 + wc::kStreamSlack)
+        h.stream_bits < h.n_elems || h.n_groups > h.n_elems || (h.n_groups == 0) != (h.n_elems == 0))
+        return WC_ERR_STREAM_BITS;
+    if (lanes ? h.stream_bytes != wc::round_up(wc::div_up(h.stream_bits, 8), 8) + wc::kLanesSlack
+              : (h.n_chunks != wc::div_up(h.stream_bits, wc::kChunkBits) ||
+                 h.stream_bytes != h.n_chunks * 8 + wc::kStreamSlack))
         return WC_ERR_STREAM_BITS;
 
     // sections: 256-byte aligned, in order, non-overlapping, inside total_bytes
     if (h.n_tensors > (1u << 24)) return WC_ERR_SECTION_BOUNDS;
     const uint64_t off[6] = {h.off_code_len, h.off_tensors, h.off_groups, h.off_gap, h.off_stream, h.off_sm};
-    const uint64_t len[6] = {256, 16ull * h.n_tensors, wc::kGroupEntryBytes * (h.n_groups + 1), h.n_chunks,
-                             h.stream_bytes, h.n_elems};
+    const uint64_t len[6] = {256, 16ull * h.n_tensors, wc::kGroupEntryBytes * (h.n_groups + 1),
+                             lanes ? 2ull * wc::kLanes * h.n_groups : h.n_chunks, h.stream_bytes, h.n_elems};
     uint64_t lo = wc::kHeaderBytes;
     for (int k = 0; k < 6; ++k) {
         if (off[k] % wc::kAlign || off[k] < lo || off[k] > h.total_bytes || len[k] > h.total_bytes - off[k])
@@ -125,7 +140,7 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
 
     // gaps: a codeword reaches at most max_code_len - 1 bits into the next chunk
     const uint8_t* gap = b + h.off_gap;
-    for (uint64_t c = 0; c < h.n_chunks; ++c)
+    for (uint64_t c = 0; !lanes && c < h.n_chunks; ++c)
         if (gap[c] >= h.max_code_len || 64 * c + gap[c] > h.stream_bits) return WC_ERR_GAP;
 
     // groups: start at {0, 0}, strictly increasing, first elements on block
@@ -141,8 +156,18 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
         const uint64_t p1 = load_le<uint64_t>(gt + wc::kGroupEntryBytes * g + 8);
         if (e1 <= e0 || p1 <= p0 || e1 > h.n_elems || p1 > h.stream_bits) return WC_ERR_GROUP_START;
         if (g < h.n_groups && e1 % h.group_align) return WC_ERR_GROUP_START;
-        if (e1 - e0 > p1 - p0 || e1 - e0 > h.group_max_elems || wc::chunk_span(p0, p1) > h.chunks_per_group)
+        if (e1 - e0 > p1 - p0 || e1 - e0 > h.group_max_elems) return WC_ERR_GROUP_START;
+        if (lanes ? p1 - p0 > h.seg_max_bits : wc::chunk_span(p0, p1) > h.chunks_per_group)
             return WC_ERR_GROUP_START;
+        if (lanes) {
+            // lane offsets: lane 0 at the segment's first bit, non-decreasing,
+            // inside the segment
+            const uint8_t* lo = gap + 2ull * wc::kLanes * (g - 1);
+            if (load_le<uint16_t>(lo) != 0) return WC_ERR_GAP;
+            for (uint32_t j = 1; j < wc::kLanes; ++j)
+                if (load_le<uint16_t>(lo + 2 * j) < load_le<uint16_t>(lo + 2 * (j - 1))) return WC_ERR_GAP;
+            if (load_le<uint16_t>(lo + 2 * (wc::kLanes - 1)) > p1 - p0) return WC_ERR_GAP;
+        }
         max_group_elems = std::max(max_group_elems, e1 - e0);
     }
     if (load_le<uint64_t>(gt + wc::kGroupEntryBytes * h.n_groups) != h.n_elems ||
@@ -188,8 +213,10 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
     wc_plan_t* p = new (std::nothrow) wc_plan_t;
     if (!p) return WC_ERR_NOMEM;
     int st = parse_and_validate(blob_host, blob_bytes, p->h, p->tensor_offsets, p->tensor_numels, p->max_group_elems);
-    if (st == WC_OK && (p->h.chunks_per_group != wc::kGroupChunks || p->h.group_align % wc::kMergeElems ||
-                        p->h.group_max_elems > wc::kGroupMaxElems))
+    const bool lanes = st == WC_OK && p->h.version == wc::kVersionLanes;
+    if (st == WC_OK && (p->h.group_align % wc::kMergeElems || p->h.group_max_elems > wc::kGroupMaxElems))
+        st = WC_ERR_UNSUPPORTED;
+    if (st == WC_OK && (lanes ? p->h.seg_max_bits > wc::kLanesMaxSegBits : p->h.chunks_per_group != wc::kGroupChunks))
         st = WC_ERR_UNSUPPORTED;
     if (st != WC_OK) {
         delete p;
@@ -250,7 +277,9 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         const uint64_t span = 1ull << p->decode_bits;
         p->l2_cap = F < span ? (uint32_t)std::min<uint64_t>(span - F, wc::kL2Prefixes) : 0u;
     }
-    p->lds_bytes = wc::decode_lds_bytes(p->count_bits, p->decode_bits, p->waves, p->ebuf_bytes, p->l2_cap);
+    p->lanes = lanes;
+    p->lds_bytes = lanes ? wc::decode_lanes_lds_bytes(p->decode_bits, p->waves, p->l2_cap)
+                         : wc::decode_lds_bytes(p->count_bits, p->decode_bits, p->waves, p->ebuf_bytes, p->l2_cap);
 
     DeviceGuard guard(hip_device);
     if (!guard.ok) {
@@ -262,7 +291,8 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         delete p;
         return WC_ERR_HIP;
     }
-    int per_cu = wc::decode_blocks_per_cu(p->count_bits, p->decode_bits, p->waves, p->ebuf_bytes, p->l2_cap);
+    int per_cu = lanes ? wc::decode_lanes_blocks_per_cu(p->decode_bits, p->waves, p->l2_cap)
+                       : wc::decode_blocks_per_cu(p->count_bits, p->decode_bits, p->waves, p->ebuf_bytes, p->l2_cap);
     // The persistent grid must be co-resident.  LDS is handed out in granules of
     // 1/128 of a compute unit's LDS (1,280 bytes of 160 KiB on gfx950), which the
     // runtime's occupancy estimate does not round for: count the granules.
@@ -353,8 +383,16 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
     d.u_end = p->h.n_groups;
     d.ebuf_bytes = p->ebuf_bytes;
     d.l2_cap = p->l2_cap;
-    hipError_t e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, p->grid, false,
-                                     static_cast<hipStream_t>(stream));
+    hipError_t e;
+    if (p->lanes) {
+        // the lane offsets sit where the gaps do; the kernel stages the tables
+        // from the multi-codeword table on
+        d.tables = p->d_tables + (1u << p->count_bits);
+        e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, p->grid, static_cast<hipStream_t>(stream));
+    } else {
+        e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, p->grid, false,
+                              static_cast<hipStream_t>(stream));
+    }
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
 }
 
@@ -422,6 +460,7 @@ extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, co
     uint64_t need = 0, rows_off = 0;
     const int st = prepare_gemv(p, ops, n_ops, d.dot, d.u_begin, d.u_end, need, rows_off);
     if (st != WC_OK) return st;
+    if (p->lanes) return WC_ERR_UNSUPPORTED;   // the fused product reads version-2 containers
     if (d.dot.n_mats == 0) return WC_OK;
     if (!blob_dev || !work_dev || work_bytes < need || (reinterpret_cast<uintptr_t>(blob_dev) & 255u) ||
         (reinterpret_cast<uintptr_t>(work_dev) & 255u))

@@ -34,7 +34,8 @@ _u32p = ctypes.POINTER(ctypes.c_uint32)
 class EncodeOpts(ctypes.Structure):
     _fields_ = [("max_code_len", ctypes.c_uint32), ("chunk_bytes", ctypes.c_uint32),
                 ("chunks_per_group", ctypes.c_uint32), ("n_threads", ctypes.c_uint32),
-                ("group_align", ctypes.c_uint32), ("group_max_elems", ctypes.c_uint32)]
+                ("group_align", ctypes.c_uint32), ("group_max_elems", ctypes.c_uint32),
+                ("layout", ctypes.c_uint32), ("seg_max_bits", ctypes.c_uint32)]
 
 
 _lib.wc_encode_host.argtypes = [ctypes.POINTER(_u16p), _u64p, ctypes.c_uint32, ctypes.POINTER(EncodeOpts),
@@ -94,6 +95,10 @@ WC_ERR_TENSOR_TABLE = -18
 GROUP_CHUNKS = 128
 GROUP_ALIGN = 128
 GROUP_MAX_ELEMS = 4096
+# Interleaved-lane layout (container v3): stream bits per segment at most; the
+# GPU decoder stages a segment's stream (at most 1984 bytes) in LDS.
+SEG_MAX_BITS = 15872
+LAYOUTS = {"chunks": 0, "lanes": 1}
 
 EXPORTED = ("wc_encode_host", "wc_free_host", "wc_plan", "wc_plan_info", "wc_plan_stats",
             "wc_decode_async", "wc_gemv_bf16_async", "wc_decode_gemv_work_bytes", "wc_decode_gemv_async",
@@ -130,15 +135,19 @@ def _as_u16(t) -> np.ndarray:
 
 def encode_host(tensors, max_code_len: int = 24, chunks_per_group: int = GROUP_CHUNKS,
                 n_threads: int = 0, group_align: int = GROUP_ALIGN,
-                group_max_elems: int = GROUP_MAX_ELEMS) -> np.ndarray:
+                group_max_elems: int = GROUP_MAX_ELEMS, layout: str = "chunks",
+                seg_max_bits: int = SEG_MAX_BITS) -> np.ndarray:
     """wc_encode_host over a list of bf16 tensors (numpy uint16 or torch CPU).
 
+    layout: "chunks" (container v2, per-chunk gaps) or "lanes" (container v3,
+    interleaved lanes; seg_max_bits caps a segment's stream bits).
     Returns the container as a numpy uint8 array (a copy of the library buffer)."""
     arrs = [_as_u16(t) for t in tensors]
     nt = len(arrs)
     ptrs = (_u16p * max(nt, 1))(*[a.ctypes.data_as(_u16p) for a in arrs])
     numels = (ctypes.c_uint64 * max(nt, 1))(*[a.size for a in arrs])
-    opts = EncodeOpts(max_code_len, 8, chunks_per_group, n_threads, group_align, group_max_elems)
+    opts = EncodeOpts(max_code_len, 8, chunks_per_group, n_threads, group_align, group_max_elems,
+                      LAYOUTS[layout], seg_max_bits)
     out = _u8p()
     nbytes = ctypes.c_uint64(0)
     _check(_lib.wc_encode_host(ptrs, numels, nt, ctypes.byref(opts), ctypes.byref(out), ctypes.byref(nbytes)),

@@ -231,3 +231,68 @@ def test_gemv_argument_checks_without_device(wc):
     assert call(vp(fake), 4, 8, vp(fake + 2), vp(fake), vp(0)) == wc.WC_ERR_INVALID_ARG
     assert call(vp(fake), 4, 8, vp(fake), vp(fake + 2), vp(0)) == wc.WC_ERR_INVALID_ARG
     assert call(vp(0), 4, 8, vp(fake), vp(fake), vp(0)) == wc.WC_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("A,M,B", [(128, 4096, 15872), (64, 1024, 4096), (8, 512, 500), (8, 4096, 65535)])
+def test_lanes_encoder_matches_oracle_writer(wc, oracle_lib, A, M, B):
+    """The product's interleaved-lane writer is byte-identical to the oracle's."""
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload("block_8b", scale_rows=24)
+    a = wc.encode_host(wl.tensors(), layout="lanes", group_align=A, group_max_elems=M, seg_max_bits=B)
+    b = oracle_lib.encode_lanes(wl.bits, numels=wl.numels, group_align=A, group_max_elems=M, seg_max_bits=B)
+    assert np.array_equal(a, b)
+    for n_threads in (1, 3):
+        c = wc.encode_host(wl.tensors(), layout="lanes", group_align=A, group_max_elems=M, seg_max_bits=B,
+                           n_threads=n_threads)
+        assert np.array_equal(a, c)
+
+
+def test_lanes_encoder_rejects_bad_options(wc):
+    w = np.arange(10, dtype=np.uint16)
+    for kw in ({"seg_max_bits": 70000}, {"seg_max_bits": 128 * 24 - 1}, {"group_align": 64, "seg_max_bits": 1000}):
+        with pytest.raises(wc.WCError) as ei:
+            wc.encode_host([w], layout="lanes", **kw)
+        assert ei.value.status == wc.WC_ERR_INVALID_ARG
+
+
+def test_plan_rejects_each_lanes_fault(wc, oracle_lib):
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload("matrix_1k", scale_rows=128)
+    blob = wc.encode_host(wl.tensors(), layout="lanes")
+    s = sections(blob)
+    ok = (wc.WC_OK, wc.WC_ERR_HIP)
+    assert s["version"] == 3 and s["n_groups"] >= 3
+    assert _plan_status(wc, blob) in ok
+
+    def mutated(fn):
+        b = blob.copy()
+        fn(b)
+        return _plan_status(wc, b)
+
+    def setb(off, val):
+        return lambda b: b.__setitem__(slice(off, off + len(val)), val)
+
+    assert mutated(setb(9, np.array([32], np.uint8))) == wc.WC_ERR_BAD_MAGIC              # lanes
+    assert mutated(setb(10, np.array([4, 0], np.uint8))) == wc.WC_ERR_BAD_MAGIC           # lane block
+    assert mutated(setb(40, _u64(1))) == wc.WC_ERR_BAD_MAGIC                               # n_chunks must be 0
+    assert mutated(setb(12, np.array([100, 0, 0, 0], np.uint8))) == wc.WC_ERR_BAD_MAGIC   # B < A * max_len
+    assert mutated(setb(96, _u64(s["stream_bytes"] + 8))) == wc.WC_ERR_STREAM_BITS
+    lo = s["off_gap"]
+    assert mutated(setb(lo, np.array([1, 0], np.uint8))) == wc.WC_ERR_GAP                 # lane 0 not at 0
+    v = int(s["lane_off"][0, 10])
+    assert mutated(setb(lo + 2 * 11, np.frombuffer(np.uint16(v - 1).tobytes(), np.uint8))) == wc.WC_ERR_GAP
+    seg_bits = int(s["groups"][1, 1] - s["groups"][0, 1])
+    assert mutated(setb(lo + 2 * 63, np.frombuffer(np.uint16(seg_bits + 1).tobytes(), np.uint8))) == wc.WC_ERR_GAP
+    b1 = s["off_gs"] + 24
+    assert mutated(setb(b1, _u64(int(s["groups"][0, 1]) + s["seg_max_bits"] + 1))) == wc.WC_ERR_GROUP_START
+    # an offset that is not where the lane's bits begin: wc_plan cannot see it
+    assert mutated(setb(lo + 2 * 11, np.frombuffer(np.uint16(int(s["lane_off"][0, 11]) + 1).tobytes(),
+                                                   np.uint8))) in ok
+    # valid containers this build does not decode
+    b2 = wc.encode_host(wl.tensors(), layout="lanes", seg_max_bits=20000)
+    assert _plan_status(wc, b2) == wc.WC_ERR_UNSUPPORTED
+    b3 = wc.encode_host(wl.tensors(), layout="lanes", group_align=100, group_max_elems=4000)
+    assert _plan_status(wc, b3) == wc.WC_ERR_UNSUPPORTED
+    # containers written by the oracle pass every check
+    wl2 = make_workload("attn_4k_zeros", scale_rows=64)
+    assert _plan_status(wc, oracle_lib.encode_lanes(wl2.bits, numels=wl2.numels)) in ok
