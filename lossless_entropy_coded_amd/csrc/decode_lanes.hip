@@ -19,11 +19,12 @@
 //   decode  each lane keeps a 64-bit MSB-first window of its bits (refilled
 //           one LDS word at a time, at least 32 bits valid before a lookup)
 //           and looks up the multi-codeword table (up to four symbols per
-//           lookup, as the chunked kernel); symbols are appended to a 12-byte
-//           queue, and every 8 of them go to the lane's next 8-byte slot;
+//           lookup, as the chunked kernel); the symbols go to the lane's own
+//           LDS slot with four byte stores, at the count decoded so far;
 //   merge   as the chunked kernel: the sign+mantissa bytes (loaded while the
-//           lanes decode) and the staged exponents become bf16 in registers,
-//           written with 16-byte non-temporal stores, whole cache lines.
+//           lanes decode) and the staged exponents (lane i's k-th 8 bytes
+//           are block i + 64k) become bf16 in registers, written with
+//           16-byte non-temporal stores, whole cache lines.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -73,8 +74,9 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
     __shared__ __attribute__((aligned(16))) uint4 s_tab[kTabVec];
     const uint2* const s_dec = reinterpret_cast<const uint2*>(s_tab);
     const uint32_t* const s_long = reinterpret_cast<const uint32_t*>(s_tab + kDecVec);
-    // dynamic: per wave, kLaneStageBytes of stream words then kGroupMaxElems
-    // exponent bytes; then the second-level table (l2_cap * 2^kL2Bits u16)
+    // dynamic: per wave, kLaneStageBytes of stream words then one
+    // kLaneSlotBytes exponent slot per lane; then the second-level table
+    // (l2_cap * 2^kL2Bits u16)
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
     uint16_t* const s_l2 = reinterpret_cast<uint16_t*>(dyn + W * kLaneWaveBytes);
 
@@ -83,6 +85,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     uint32_t* const sbuf = reinterpret_cast<uint32_t*>(dyn + wave * kLaneWaveBytes);
     uint8_t* const ebuf = dyn + wave * kLaneWaveBytes + kLaneStageBytes;
+    uint8_t* const slot = ebuf + kLaneSlotBytes * lane;   // this lane's exponents, in its symbol order
 
     // wave w of workgroup b takes segments b*W + w, then every (grid * W)-th
     const uint64_t stride = (uint64_t)gridDim.x * W;
@@ -154,29 +157,29 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
         {
             const uint32_t nb8 = (n + kLaneBlock - 1) / kLaneBlock;
             const uint32_t cnt = lane < nb8 ? (nb8 - 1 - lane) / kWaveLanes + 1 : 0u;
-            uint32_t left = kLaneBlock * cnt;
-            if (cnt && lane == (nb8 - 1) % kWaveLanes) left -= kLaneBlock * nb8 - n;
+            uint32_t nsym = kLaneBlock * cnt;
+            if (cnt && lane == (nb8 - 1) % kWaveLanes) nsym -= kLaneBlock * nb8 - n;
             const uint32_t pos = (uint32_t)(cur_m.p0 & 127u) + off;   // first bit in the staged words
             uint32_t wi = pos >> 5;
             uint64_t win = (((uint64_t)sbuf[wi] << 32) | sbuf[wi + 1]) << (pos & 31u);
             int32_t valid = 64 - (int32_t)(pos & 31u);
             wi += 2;
-            uint64_t q = 0;        // pending exponent bytes, first in the lowest byte
-            uint32_t q2 = 0;       // bytes 8..11 of the queue
-            uint32_t c = 0;        // bytes pending
-            uint32_t slot = lane;  // next lane block: lane + 64 k
-            while (left > 0) {
+            // a lookup's symbols past the lane's last one (they belong to the
+            // next lane) land in the slot's spare bytes: p < nsym <= 64 before
+            // the store, so it ends by byte 67
+            uint32_t p = 0;
+            while (p < nsym) {
                 const uint32_t top = (uint32_t)(win >> 32);
                 uint2 e = s_dec[top >> (32 - KD)];
                 if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
+                uint8_t* const dst = slot + p;
+                const uint32_t odd = __builtin_amdgcn_perm(e.y, e.y, 0x0C030C01u);   // [s1, 0, s3, 0]
+                dst[0] = (uint8_t)e.y;
+                dst[1] = (uint8_t)odd;
+                dst[2] = (uint8_t)(e.y >> 16);
+                dst[3] = (uint8_t)(odd >> 16);
+                p += (e.x >> 8) & 0xFFu;
                 const uint32_t nbits = (e.x >> 16) & 0xFFu;
-                const uint32_t ns = min((e.x >> 8) & 0xFFu, left);
-                // symbols past the lane's last belong to the next lane: the
-                // loop ends with them, and they never reach a full block
-                q |= (uint64_t)e.y << (8 * c);
-                q2 |= c > 4 ? e.y >> (64 - 8 * c) : 0u;
-                c += ns;
-                left -= ns;
                 win <<= nbits;
                 valid -= (int32_t)nbits;
                 if (valid < 32) {
@@ -184,15 +187,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
                     ++wi;
                     valid += 32;
                 }
-                if (c >= kLaneBlock) {
-                    *reinterpret_cast<uint2*>(ebuf + kLaneBlock * slot) = make_uint2((uint32_t)q, (uint32_t)(q >> 32));
-                    slot += kWaveLanes;
-                    q = q2;
-                    q2 = 0;
-                    c -= kLaneBlock;
-                }
             }
-            if (c) *reinterpret_cast<uint2*>(ebuf + kLaneBlock * slot) = make_uint2((uint32_t)q, (uint32_t)(q >> 32));
         }
 
         const LaneRaw next_r = nxt;
@@ -200,13 +195,13 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
         m_next = uniform_meta(m_after);
         wave_lds_order();
 
-        // merge: step k of lane i is block 64k + i, the lane's own slots
+        // merge: step k of lane i is block 64k + i, bytes 8k.. of the lane's slot
         const uint32_t full = n / kMergeElems;
 #pragma unroll
         for (uint32_t k = 0; k < kMergeSteps; ++k) {
             const uint32_t blk = lane + k * kWaveLanes;
             if (blk < full) {
-                const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + kMergeElems * blk);
+                const uint2 e2 = *reinterpret_cast<const uint2*>(slot + kMergeElems * k);
                 uint32_t o0, o1, o2, o3;
                 join4(smv[k].x, e2.x, o0, o1);
                 join4(smv[k].y, e2.y, o2, o3);
@@ -222,7 +217,9 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
         if (full * kMergeElems < n && lane == 0) {
             const uint32_t rel = kMergeElems * full;
             const uint2 s2 = load_nt8(p.sm + A + rel);
-            const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + rel);
+            // block `full` is the (full / 64)-th of lane full % 64
+            const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + kLaneSlotBytes * (full % kWaveLanes) +
+                                                             kMergeElems * (full / kWaveLanes));
             uint32_t o[4];
             join4(s2.x, e2.x, o[0], o[1]);
             join4(s2.y, e2.y, o[2], o[3]);

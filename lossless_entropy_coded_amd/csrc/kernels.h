@@ -109,10 +109,14 @@ struct DecodeParams {
 
 // Interleaved-lane containers (version 3): each wave stages a segment's
 // stream window (its bits, the first bit's 16-byte alignment and 8 bytes of
-// lookahead) in kLaneStageBytes of LDS, then its exponent bytes; a segment
-// therefore holds at most kLanesMaxSegBits stream bits.
+// lookahead) in kLaneStageBytes of LDS, then the exponent bytes, one
+// kLaneSlotBytes slot per lane (its at most 64 symbols and the up to three
+// bytes a four-symbol lookup may write past them, 72 bytes so that the
+// lanes' 8-byte merge reads fall in different banks); a segment therefore
+// holds at most kLanesMaxSegBits stream bits.
 constexpr uint32_t kLaneStageBytes = 2048;
-constexpr uint32_t kLaneWaveBytes = kLaneStageBytes + kGroupMaxElems;
+constexpr uint32_t kLaneSlotBytes = 72;
+constexpr uint32_t kLaneWaveBytes = kLaneStageBytes + kWaveLanes * kLaneSlotBytes;
 constexpr uint32_t kLanesMaxSegBits = 15872;
 
 // Wavefronts per decode workgroup the kernels are built for.
