@@ -72,9 +72,9 @@ def parse_args():
     ap.add_argument("--workload", default="block_8b",
                     help="synthetic workload (default: block_8b, the 8B-shape transformer block)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
-    ap.add_argument("--layout", choices=["chunks", "lanes"], default="chunks",
-                    help="container layout: chunks (v2, per-chunk gaps; the default) or lanes (v3, "
-                         "interleaved lanes)")
+    ap.add_argument("--layout", choices=["lanes", "chunks"], default="lanes",
+                    help="container layout: lanes (v3, interleaved lanes; the library's default) or "
+                         "chunks (v2, per-chunk gaps)")
     ap.add_argument("--e2e", action="store_true",
                     help="70B-shape block end to end: decode + batch-1 GEMVs against GEMVs on resident "
                          "uncompressed weights (prints its own JSON line)")
@@ -166,7 +166,7 @@ def end_to_end(args):
 
     name = args.workload if args.workload != "block_8b" else "block_70b"
     wl = make_workload(name)
-    blob = wc.encode_host(wl.tensors())
+    blob = wc.encode_host(wl.tensors(), layout=args.layout)
     plan = wc.Plan(blob, device=0)
     n = wl.n
     mats = [(k, s[0], s[1]) for k, s in enumerate(wl.shapes) if len(s) == 2]
@@ -237,7 +237,8 @@ def end_to_end(args):
         "data": "synthetic: seeded bf16 weights (70B-block shapes, N(0, 0.015)), x ~ N(0, 1) in bf16",
         "config": {"workload": f"{name}: decode of the whole block, then q,k,v,o,gate,up,down GEMVs "
                                f"(x length = each matrix's in-dimension)",
-                   "n_elems": n, "container_bytes": int(blob.size), "weight_bytes": weight_bytes},
+                   "layout": args.layout, "n_elems": n, "container_bytes": int(blob.size),
+                   "weight_bytes": weight_bytes},
         "arm_a_decode_plus_gemv_ms": round(ms_a, 4),
         "arm_b_uncompressed_gemv_ms": round(ms_b, 4),
         "arm_c_fused_decode_gemv_ms": round(ms_c, 4),

@@ -103,15 +103,15 @@ typedef struct {
     uint32_t group_max_elems;   /* M, a multiple of A: elements per group at most; 0    */
                                 /* selects the default 4096, the most the GPU decoder   */
                                 /* accepts.                                             */
-    uint32_t layout;            /* WC_LAYOUT_CHUNKS (0, container v2) or                */
-                                /* WC_LAYOUT_LANES (1, container v3)                    */
+    uint32_t layout;            /* WC_LAYOUT_LANES (0, the default: container v3) or    */
+                                /* WC_LAYOUT_CHUNKS (1, container v2)                   */
     uint32_t seg_max_bits;      /* v3: stream bits per segment at most, >= A *          */
                                 /* max_code_len and < 65536; 0 selects the default      */
                                 /* 15872, the most the GPU decoder accepts.             */
 } wc_encode_opts;
 
-#define WC_LAYOUT_CHUNKS 0u
-#define WC_LAYOUT_LANES  1u
+#define WC_LAYOUT_LANES  0u
+#define WC_LAYOUT_CHUNKS 1u
 
 /*
  * wc_encode_host -- offline preparation of one container from n_tensors bf16

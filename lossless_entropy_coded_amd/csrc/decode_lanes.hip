@@ -64,7 +64,11 @@ __device__ __forceinline__ uint4 bswap4(const uint4& v) {
                       __builtin_bswap32(v.w));
 }
 
-template <int KD, int W>
+// kDot = false: decode the segments to bf16 in p.out.  kDot = true (fused
+// decode -> matrix-vector product): the decoded weights never leave the chip;
+// each wave multiplies its segment by x and leaves its partial dot products
+// in p.dot.part.
+template <int KD, int W, bool kDot>
 __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodeParams p) {
     constexpr uint32_t kThreads = kWaveLanes * W;
     // multi-codeword table, then the canonical arrays for long codes (the
@@ -127,6 +131,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
     lt.l2_first = __builtin_amdgcn_readfirstlane(s_long[160]);
     lt.l2_n = min(__builtin_amdgcn_readfirstlane(s_long[161]), p.l2_cap);
     m_next = uniform_meta(m_next);
+    uint32_t dot_mat = 0;   // fused product: matrix of the wave's current segment
 
     for (;;) {
         const uint64_t un = u + stride;
@@ -149,6 +154,14 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
 #pragma unroll
         for (uint32_t k = 0; k < kMergeSteps; ++k)
             smv[k] = load_nt8(smu + kMergeElems * min(lane + k * kWaveLanes, last_blk));
+        // fused product: the x entries of the segment's blocks, loaded with
+        // the sm bytes so that they have arrived by the merge
+        DotRows dr;
+        uint4 xv[kDot ? kMergeSteps : 1];
+        if constexpr (kDot) {
+            dr = dot_rows(p.dot, A, n, dot_mat);
+            load_dot_x(dr, n, lane, xv);
+        }
         const Meta m_after = load_meta(p, min_u64(un + stride, last_u));
         wave_lds_order();
 
@@ -197,6 +210,10 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
 
         // merge: step k of lane i is block 64k + i, bytes 8k.. of the lane's slot
         const uint32_t full = n / kMergeElems;
+        if constexpr (kDot) {
+            dot_group(p.dot, dr, full, lane, smv, xv, u - p.u_begin,
+                      [&](uint32_t k) { return *reinterpret_cast<const uint2*>(slot + kMergeElems * k); });
+        } else {
 #pragma unroll
         for (uint32_t k = 0; k < kMergeSteps; ++k) {
             const uint32_t blk = lane + k * kWaveLanes;
@@ -213,8 +230,10 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
                 __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(outu + kMergeElems * blk));
             }
         }
-        // the container's last block, when it holds fewer than 8 elements
-        if (full * kMergeElems < n && lane == 0) {
+        }
+        // the container's last block, when it holds fewer than 8 elements (a
+        // matrix for the fused product never ends in a partial block)
+        if (!kDot && full * kMergeElems < n && lane == 0) {
             const uint32_t rel = kMergeElems * full;
             const uint2 s2 = load_nt8(p.sm + A + rel);
             // block `full` is the (full / 64)-th of lane full % 64
@@ -238,16 +257,21 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
 
 template <int KD, int W>
 struct LanesVariant {
-    static hipError_t launch(const DecodeParams& p, uint32_t grid, uint32_t dyn, hipStream_t stream) {
-        hipLaunchKernelGGL((decode_lanes_kernel<KD, W>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
+    static hipError_t launch(const DecodeParams& p, uint32_t grid, uint32_t dyn, bool dot, hipStream_t stream) {
+        if (dot)
+            hipLaunchKernelGGL((decode_lanes_kernel<KD, W, true>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
+        else
+            hipLaunchKernelGGL((decode_lanes_kernel<KD, W, false>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
         return hipGetLastError();
     }
     static int blocks_per_cu(uint32_t dyn) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lanes_kernel<KD, W>, kWaveLanes * W, dyn) !=
-            hipSuccess)
+        int n = 0, m = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lanes_kernel<KD, W, false>, kWaveLanes * W, dyn) !=
+                hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, decode_lanes_kernel<KD, W, true>, kWaveLanes * W, dyn) !=
+                hipSuccess)
             return 0;
-        return n;
+        return n < m ? n : m;
     }
 };
 
@@ -278,12 +302,13 @@ int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2
     return n;
 }
 
-hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid,
+hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid, bool dot,
                                hipStream_t stream) {
     if ((decode_bits != 11 && decode_bits != 10) || !supported_waves(waves) || p.l2_cap > kL2Prefixes)
         return hipErrorInvalidValue;
     const uint32_t dyn = decode_lanes_dyn_lds_bytes(waves, p.l2_cap);
-    return dispatch_lanes(decode_bits, waves, [&](auto v) { return decltype(v)::launch(p, grid, dyn, stream); });
+    return dispatch_lanes(decode_bits, waves,
+                          [&](auto v) { return decltype(v)::launch(p, grid, dyn, dot, stream); });
 }
 
 }  // namespace wc

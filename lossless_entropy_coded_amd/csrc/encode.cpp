@@ -260,7 +260,7 @@ extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* nu
     *blob_bytes = 0;
     if (n_tensors && (!tensors || !numels)) return WC_ERR_INVALID_ARG;
     uint32_t max_len = kMaxCodeLen, group = kDefaultGroup, align = kDefaultAlign, max_elems = kDefaultMaxElems;
-    uint32_t nthreads = 0, kind = WC_LAYOUT_CHUNKS, seg_bits = kDefaultSegBits;
+    uint32_t nthreads = 0, kind = WC_LAYOUT_LANES, seg_bits = kDefaultSegBits;
     if (opts) {
         if (opts->max_code_len) max_len = opts->max_code_len;
         if (opts->chunk_bytes && opts->chunk_bytes != 8) return WC_ERR_INVALID_ARG;

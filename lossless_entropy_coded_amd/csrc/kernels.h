@@ -143,12 +143,13 @@ hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t de
 
 // Interleaved-lane decode: LDS bytes of one workgroup (decode table index
 // width decode_bits, 11 or 10), resident workgroups per CU, and one launch
-// decoding segments [p.u_begin, p.u_end) to bf16 in p.out; p.gap points at the
-// lane offsets and p.tables at the multi-codeword table of the plan's tables.
+// decoding segments [p.u_begin, p.u_end) to bf16 in p.out, or (dot) to
+// partial dot products in p.dot; p.gap points at the lane offsets and
+// p.tables at the multi-codeword table of the plan's tables.
 uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap);
 uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap);
 int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap);
-hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid,
+hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid, bool dot,
                                hipStream_t stream);
 
 // One launch adding, for every global row of p.dot, the partial dot products

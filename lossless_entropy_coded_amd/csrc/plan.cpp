@@ -388,7 +388,7 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
         // the lane offsets sit where the gaps do; the kernel stages the tables
         // from the multi-codeword table on
         d.tables = p->d_tables + (1u << p->count_bits);
-        e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, p->grid, static_cast<hipStream_t>(stream));
+        e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, p->grid, false, static_cast<hipStream_t>(stream));
     } else {
         e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, p->grid, false,
                               static_cast<hipStream_t>(stream));
@@ -460,7 +460,6 @@ extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, co
     uint64_t need = 0, rows_off = 0;
     const int st = prepare_gemv(p, ops, n_ops, d.dot, d.u_begin, d.u_end, need, rows_off);
     if (st != WC_OK) return st;
-    if (p->lanes) return WC_ERR_UNSUPPORTED;   // the fused product reads version-2 containers
     if (d.dot.n_mats == 0) return WC_OK;
     if (!blob_dev || !work_dev || work_bytes < need || (reinterpret_cast<uintptr_t>(blob_dev) & 255u) ||
         (reinterpret_cast<uintptr_t>(work_dev) & 255u))
@@ -483,7 +482,13 @@ extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, co
     const uint64_t groups = wc::div_up(d.u_end - d.u_begin, p->waves);
     const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(p->slots, groups));
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, grid, true, s);
+    hipError_t e;
+    if (p->lanes) {
+        d.tables = p->d_tables + (1u << p->count_bits);
+        e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, grid, true, s);
+    } else {
+        e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, grid, true, s);
+    }
     if (e == hipSuccess) e = wc::launch_gemv_rows(d, s);
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
 }

@@ -98,7 +98,7 @@ GROUP_MAX_ELEMS = 4096
 # Interleaved-lane layout (container v3): stream bits per segment at most; the
 # GPU decoder stages a segment's stream (at most 1984 bytes) in LDS.
 SEG_MAX_BITS = 15872
-LAYOUTS = {"chunks": 0, "lanes": 1}
+LAYOUTS = {"lanes": 0, "chunks": 1}
 
 EXPORTED = ("wc_encode_host", "wc_free_host", "wc_plan", "wc_plan_info", "wc_plan_stats",
             "wc_decode_async", "wc_gemv_bf16_async", "wc_decode_gemv_work_bytes", "wc_decode_gemv_async",
@@ -135,12 +135,13 @@ def _as_u16(t) -> np.ndarray:
 
 def encode_host(tensors, max_code_len: int = 24, chunks_per_group: int = GROUP_CHUNKS,
                 n_threads: int = 0, group_align: int = GROUP_ALIGN,
-                group_max_elems: int = GROUP_MAX_ELEMS, layout: str = "chunks",
+                group_max_elems: int = GROUP_MAX_ELEMS, layout: str = "lanes",
                 seg_max_bits: int = SEG_MAX_BITS) -> np.ndarray:
     """wc_encode_host over a list of bf16 tensors (numpy uint16 or torch CPU).
 
-    layout: "chunks" (container v2, per-chunk gaps) or "lanes" (container v3,
-    interleaved lanes; seg_max_bits caps a segment's stream bits).
+    layout: "lanes" (the default: container v3, interleaved lanes;
+    seg_max_bits caps a segment's stream bits) or "chunks" (container v2,
+    per-chunk gaps; chunks_per_group applies).
     Returns the container as a numpy uint8 array (a copy of the library buffer)."""
     arrs = [_as_u16(t) for t in tensors]
     nt = len(arrs)

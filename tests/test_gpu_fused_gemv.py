@@ -97,8 +97,9 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("layout", ["lanes", "chunks"])
 @pytest.mark.parametrize("name,align,cap,shapes", CASES, ids=[c[0] for c in CASES])
-def test_fused_against_oracle(wc, oracle_lib, name, align, cap, shapes):
+def test_fused_against_oracle(wc, oracle_lib, name, align, cap, shapes, layout):
     """Each matrix alone, then every run of consecutive matrices in one call:
     the values agree with the oracle, the one-call results equal the
     per-matrix ones, and a repeated call gives the same bits."""
@@ -108,7 +109,7 @@ def test_fused_against_oracle(wc, oracle_lib, name, align, cap, shapes):
     for s in shapes:
         n = int(np.prod(s))
         tensors.append(f32_to_bf16_rne(rng.standard_normal(n, dtype=np.float32) * np.float32(0.02)))
-    blob = wc.encode_host(tensors, group_align=align, group_max_elems=cap)
+    blob = wc.encode_host(tensors, group_align=align, group_max_elems=cap, layout=layout)
     W_all = oracle_lib.decode(blob)
     assert np.array_equal(W_all, np.concatenate(tensors))
     with wc.Plan(blob) as plan:
@@ -119,7 +120,7 @@ def test_fused_against_oracle(wc, oracle_lib, name, align, cap, shapes):
             rows, cols = shapes[k]
             off = plan.tensor_offsets[k]
             x = gemv_input(cols)
-            log(f"case: fused {name} tensor {k} {rows}x{cols} A={align} M={cap}")
+            log(f"case: fused {layout} {name} tensor {k} {rows}x{cols} A={align} M={cap}")
             got = f.run([(k, cols, x)])[0]
             W = W_all[off:off + rows * cols].reshape(rows, cols)
             _check_tensor(oracle_lib, got, W, x, align)
@@ -144,18 +145,19 @@ def test_fused_against_oracle(wc, oracle_lib, name, align, cap, shapes):
                 assert np.array_equal(y, alone[k]), f"tensor {k}: one-call result differs from the per-matrix call"
 
 
+@pytest.mark.parametrize("layout", ["lanes", "chunks"])
 @pytest.mark.parametrize("name,rows", [("heavy_tail_14k", 96), ("block_8b", 40), ("block_70b", 24)])
-def test_fused_on_workload_shapes(wc, oracle_lib, name, rows):
+def test_fused_on_workload_shapes(wc, oracle_lib, name, rows, layout):
     """The block workloads, truncated to a few rows per matrix: all matrices
     of the block in one fused call, against the oracle."""
     from lossless_entropy_coded_amd.synth import gemv_input, make_workload
     wl = make_workload(name, scale_rows=rows)
-    blob = wc.encode_host(wl.tensors())
+    blob = wc.encode_host(wl.tensors(), layout=layout)
     with wc.Plan(blob) as plan:
         f = Fused(wc, blob, plan)
         mats = [k for k, s in enumerate(wl.shapes) if len(s) == 2]
         assert mats == list(range(len(mats)))
-        log(f"case: fused {name} rows={rows} tensors {mats} in one call")
+        log(f"case: fused {layout} {name} rows={rows} tensors {mats} in one call")
         ys = f.run([(k, wl.shapes[k][1], gemv_input(wl.shapes[k][1])) for k in mats])
         for k, got in zip(mats, ys):
             r, c = wl.shapes[k]
@@ -163,18 +165,19 @@ def test_fused_on_workload_shapes(wc, oracle_lib, name, rows):
             _check_tensor(oracle_lib, got, wl.bits[off:off + r * c].reshape(r, c), gemv_input(c), wc.GROUP_ALIGN)
 
 
-def test_fused_full_block_8b_sampled(wc, oracle_lib):
+@pytest.mark.parametrize("layout", ["lanes", "chunks"])
+def test_fused_full_block_8b_sampled(wc, oracle_lib, layout):
     """The full 8B-shape block (the size the benchmark decodes): its 7
     matrices in one fused call; 48 sampled rows per matrix (first, last and
     random) against the oracle's GEMV of the generated weights."""
     from lossless_entropy_coded_amd.synth import gemv_input, make_workload
     wl = make_workload("block_8b")
-    blob = wc.encode_host(wl.tensors())
+    blob = wc.encode_host(wl.tensors(), layout=layout)
     rng = np.random.default_rng(8)
     with wc.Plan(blob) as plan:
         f = Fused(wc, blob, plan)
         mats = [k for k, s in enumerate(wl.shapes) if len(s) == 2]
-        log(f"case: fused block_8b full, tensors {mats} in one call")
+        log(f"case: fused {layout} block_8b full, tensors {mats} in one call")
         ys = f.run([(k, wl.shapes[k][1], gemv_input(wl.shapes[k][1])) for k in mats])
         for k, got in zip(mats, ys):
             r, c = wl.shapes[k]

@@ -45,7 +45,7 @@ def env_knob():
 def test_worked_example(wc):
     w = np.array([0x3C80, 0x3C00, 0x3C80, 0x3B80, 0x3C80, 0x3D00, 0x3C00, 0x3C80], np.uint16)
     log("case: worked example n=8")
-    assert np.array_equal(gpu_decode(wc, wc.encode_host([w])), w)
+    assert np.array_equal(gpu_decode(wc, wc.encode_host([w], layout="chunks")), w)
 
 
 @pytest.mark.parametrize("shuffle", [False, True])
@@ -54,7 +54,7 @@ def test_all_bf16_patterns(wc, oracle_lib, shuffle):
     if shuffle:
         w = np.random.default_rng(99).permutation(w)
     for writer in ("product", "oracle"):
-        blob = wc.encode_host([w]) if writer == "product" else oracle_lib.encode(w, chunks_per_group=wc.GROUP_CHUNKS)
+        blob = wc.encode_host([w], layout="chunks") if writer == "product" else oracle_lib.encode(w, chunks_per_group=wc.GROUP_CHUNKS)
         log(f"case: all 65536 patterns shuffle={shuffle} writer={writer}")
         assert np.array_equal(gpu_decode(wc, blob), w)
 
@@ -70,7 +70,7 @@ def test_tiny_and_special_sequences(wc, oracle_lib):
         cases.append(np.full(n, 0x3C00, np.uint16))
     for i, w in enumerate(cases):
         log(f"case: tiny #{i} n={w.size}")
-        blob = wc.encode_host([w]) if i % 2 == 0 else oracle_lib.encode(w, chunks_per_group=wc.GROUP_CHUNKS)
+        blob = wc.encode_host([w], layout="chunks") if i % 2 == 0 else oracle_lib.encode(w, chunks_per_group=wc.GROUP_CHUNKS)
         got = gpu_decode(wc, blob)
         assert np.array_equal(got, w), f"case {i} n={w.size}"
 
@@ -95,7 +95,7 @@ def test_long_codes_and_chunk_boundaries(wc, oracle_lib, prefix):
     chunk boundaries by up to 23 bits, both writers."""
     w = _fib_alphabet(prefix)
     for writer in ("product", "oracle"):
-        blob = wc.encode_host([w]) if writer == "product" else oracle_lib.encode(w, chunks_per_group=wc.GROUP_CHUNKS)
+        blob = wc.encode_host([w], layout="chunks") if writer == "product" else oracle_lib.encode(w, chunks_per_group=wc.GROUP_CHUNKS)
         log(f"case: fib alphabet prefix_len={len(prefix)} writer={writer} n={w.size}")
         assert np.array_equal(gpu_decode(wc, blob), w)
 
@@ -125,7 +125,7 @@ def test_many_long_code_prefixes(wc, oracle_lib, env_knob, bits):
     """Long codes of many distinct prefixes, at every table width: some resolve
     in one second-level lookup, others need the length-by-length search."""
     w = _many_rare_exponents()
-    blob = wc.encode_host([w])
+    blob = wc.encode_host([w], layout="chunks")
     env_knob("WC_COUNT_BITS", bits[0])
     env_knob("WC_DECODE_BITS", bits[1])
     log(f"case: many rare exponents n={w.size} table bits={bits}")
@@ -143,7 +143,7 @@ def test_table_width_and_grid_invariance(wc, env_knob, bits, grid, waves):
     of the die count) decodes the same bits."""
     from lossless_entropy_coded_amd.synth import make_workload
     wl = make_workload("heavy_tail_14k", scale_rows=512)
-    blob = wc.encode_host(wl.tensors())
+    blob = wc.encode_host(wl.tensors(), layout="chunks")
     env_knob("WC_COUNT_BITS", bits[0])
     env_knob("WC_DECODE_BITS", bits[1])
     env_knob("WC_GRID", grid or None)
@@ -163,7 +163,7 @@ def test_workload_full_size(wc, oracle_lib, name):
     import torch
     from lossless_entropy_coded_amd.synth import make_workload
     wl = make_workload(name)
-    blob = wc.encode_host(wl.tensors())
+    blob = wc.encode_host(wl.tensors(), layout="chunks")
     log(f"case: full {name} n={wl.n} container={blob.size}")
     with wc.Plan(blob) as plan:
         assert plan.n_elems == wl.n and plan.tensor_numels == wl.numels
@@ -203,7 +203,7 @@ def test_group_block_sizes(wc, oracle_lib, align, writer):
     wl = make_workload("heavy_tail_14k", scale_rows=256)
     M = wc.GROUP_MAX_ELEMS // align * align            # the largest multiple of A the decoder accepts
     if writer == "product":
-        blob = wc.encode_host(wl.tensors(), group_align=align, group_max_elems=M)
+        blob = wc.encode_host(wl.tensors(), group_align=align, group_max_elems=M, layout="chunks")
     else:
         blob = oracle_lib.encode(wl.bits, numels=wl.numels, chunks_per_group=wc.GROUP_CHUNKS, group_align=align,
                                  group_max_elems=M)
@@ -217,7 +217,7 @@ def test_corrupted_stream_stays_in_bounds(wc):
     from container_view import sections
     from lossless_entropy_coded_amd.synth import make_workload
     wl = make_workload("matrix_1k", scale_rows=256)
-    blob = wc.encode_host(wl.tensors())
+    blob = wc.encode_host(wl.tensors(), layout="chunks")
     s = sections(blob)
     rng = np.random.default_rng(3)
     nbytes = (s["stream_bits"] + 7) // 8
@@ -251,7 +251,7 @@ def test_plan_reuse_across_streams_and_repeats(wc):
     import torch
     from lossless_entropy_coded_amd.synth import make_workload
     wl = make_workload("attn_4k_zeros", scale_rows=1024)
-    blob = wc.encode_host(wl.tensors())
+    blob = wc.encode_host(wl.tensors(), layout="chunks")
     ref = torch.from_numpy(wl.bits.view(np.int16)).cuda()
     log("case: two streams, repeated decodes")
     with wc.Plan(blob) as plan:
@@ -269,7 +269,7 @@ def test_plan_reuse_across_streams_and_repeats(wc):
 def test_argument_checks(wc):
     import torch
     w = np.arange(4096, dtype=np.uint16)
-    blob = wc.encode_host([w])
+    blob = wc.encode_host([w], layout="chunks")
     with wc.Plan(blob) as plan:
         _, dblob = to_device_aligned(blob)
         out = torch.empty(w.size + 16, dtype=torch.int16, device="cuda")
@@ -282,7 +282,7 @@ def test_argument_checks(wc):
         assert ei.value.status == wc.WC_ERR_INVALID_ARG
         with pytest.raises(wc.WCError):
             wc.decode_async(plan, 0, out)
-    empty = wc.encode_host([np.zeros(0, np.uint16)])
+    empty = wc.encode_host([np.zeros(0, np.uint16)], layout="chunks")
     with wc.Plan(empty) as plan:
         assert plan.n_elems == 0
         wc.decode_async(plan, 0, 0)       # n = 0 is a no-op
