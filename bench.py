@@ -40,7 +40,7 @@ METRIC = "decompressed bf16 GB/s and % of HBM roofline (1 MI355X), bit-exact"
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "lossless_entropy_coded_amd", "csrc")
 KERNEL_SOURCES = {"chunks": os.path.join(CSRC, "decode.hip"), "lanes": os.path.join(CSRC, "decode_lanes.hip")}
-TRAFFIC_FILES = {"chunks": os.path.join(ROOT, "profiles", "decode_block_8b_traffic.json"),
+TRAFFIC_FILES = {"chunks": os.path.join(ROOT, "profiles", "decode_chunks_block_8b_traffic.json"),
                  "lanes": os.path.join(ROOT, "profiles", "decode_lanes_block_8b_traffic.json")}
 
 
