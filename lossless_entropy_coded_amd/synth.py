@@ -191,3 +191,80 @@ def make_workload(name: str, scale_rows: int | None = None) -> Workload:
         numels.append(n)
     bits = np.concatenate(parts) if len(parts) > 1 else parts[0]
     return Workload(name=name, bits=bits, names=names, shapes=shapes, numels=numels)
+
+
+# ---------------------------------------------------------------------------
+# Planes of quantized integer codes (the setting of the LazyWeights page:
+# Huffman codes for the already-quantized weights of a model).  No quantized
+# model is available, so seeded stand-ins with the 8B-shape block's matrix
+# shapes are drawn: a quantizer maps a weight to round(w / scale) and clips it
+# to the code range; with the weights roughly Gaussian, a code is
+# round(N(0, sigma)) clipped, sigma being the weights' spread in units of the
+# scale (smaller sigma: more skewed codes).  Codes are stored unsigned with a
+# zero point (code + 2^(bits - 1)); int4 codes are packed two per byte, the
+# first in the low nibble.
+# ---------------------------------------------------------------------------
+
+# name -> (description, seed, bits per code, sigma)
+CODE_WORKLOADS = {
+    "int8_codes_8b": ("8B-shape block's 7 matrices as int8 codes: round(N(0, 20)) clipped to [-128, 127], "
+                      "zero point 128, one byte per weight", 5, 8, 20.0),
+    "int4_codes_8b": ("8B-shape block's 7 matrices as int4 codes: round(N(0, 1.5)) clipped to [-8, 7], "
+                      "zero point 8, two per byte (low nibble first)", 6, 4, 1.5),
+}
+
+
+@dataclass
+class CodeWorkload:
+    """A generated plane of 8-bit symbols and its tensor partition."""
+
+    name: str
+    codes: np.ndarray                     # uint8[n], all tensors concatenated
+    bits: int                             # bits per quantized code (8, or 4 packed in pairs)
+    sigma: float
+    names: list = field(default_factory=list)
+    shapes: list = field(default_factory=list)   # byte shapes
+    numels: list = field(default_factory=list)   # bytes per tensor
+
+    @property
+    def n(self) -> int:
+        return int(self.codes.size)
+
+    def tensors(self):
+        out, off = [], 0
+        for k in self.numels:
+            out.append(self.codes[off:off + k])
+            off += k
+        return out
+
+
+def quantized_codes(rng, n: int, bits: int, sigma: float) -> np.ndarray:
+    """n codes of `bits` bits: round(N(0, sigma)) clipped to the signed range,
+    plus the zero point 2^(bits - 1), as uint8."""
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    z = rng.standard_normal(n, dtype=np.float32) * np.float32(sigma)
+    return (np.clip(np.rint(z), lo, hi).astype(np.int16) + (1 << (bits - 1))).astype(np.uint8)
+
+
+def make_code_workload(name: str, scale_rows: int | None = None) -> CodeWorkload:
+    desc, seed, bits, sigma = CODE_WORKLOADS[name]
+    rng = np.random.default_rng(seed)
+    parts, names, shapes, numels = [], [], [], []
+    for spec in _block_8b():
+        if len(spec.shape) != 2:
+            continue
+        rows, cols = spec.shape
+        if scale_rows is not None:
+            rows = min(rows, scale_rows)
+        q = quantized_codes(rng, rows * cols, bits, sigma)
+        if bits == 4:
+            q = (q[0::2] | (q[1::2] << 4)).astype(np.uint8)
+            shape = (rows, cols // 2)
+        else:
+            shape = (rows, cols)
+        parts.append(q)
+        names.append(spec.name)
+        shapes.append(shape)
+        numels.append(q.size)
+    return CodeWorkload(name=name, codes=np.concatenate(parts), bits=bits, sigma=sigma, names=names,
+                        shapes=shapes, numels=numels)

@@ -23,7 +23,7 @@ ERRORS = {
     -4: "code length out of range", -5: "Kraft sum wrong", -6: "prefix conflict",
     -7: "stream does not decode to n symbols", -8: "non-zero padding", -9: "gap mismatch",
     -10: "group table mismatch", -11: "tensor table mismatch", -12: "size fields inconsistent",
-    -13: "out of memory", -14: "output too small",
+    -13: "out of memory", -14: "output too small", -15: "element kind differs",
 }
 
 
@@ -53,6 +53,8 @@ class Report(ctypes.Structure):
         ("hist", ctypes.c_uint64 * 256),
         ("layout", ctypes.c_uint32),
         ("seg_max_bits", ctypes.c_uint32),
+        ("elem_kind", ctypes.c_uint32),
+        ("reserved2", ctypes.c_uint32),
     ]
 
     def as_dict(self):
@@ -96,6 +98,9 @@ def lib():
                                  ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(u8p), u64p]
         L.orc_encode_lanes.argtypes = [u16p, ctypes.c_uint64, u64p, ctypes.c_uint32, ctypes.c_uint32,
                                        ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(u8p), u64p]
+        L.orc_encode_lanes_u8.argtypes = [u8p, ctypes.c_uint64, u64p, ctypes.c_uint32, ctypes.c_uint32,
+                                          ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(u8p), u64p]
+        L.orc_decode_u8.argtypes = [u8p, ctypes.c_uint64, u8p, ctypes.c_uint64, ctypes.POINTER(Report)]
         L.orc_decode.argtypes = [u8p, ctypes.c_uint64, u16p, ctypes.c_uint64, ctypes.POINTER(Report)]
         L.orc_header.argtypes = [u8p, ctypes.c_uint64, ctypes.POINTER(Report)]
         L.orc_gemv_bf16.argtypes = [u16p, ctypes.c_uint64, ctypes.c_uint64, u16p,
@@ -215,6 +220,44 @@ def encode_lanes(w: np.ndarray, numels=None, max_code_len: int = 24, group_align
     finally:
         lib().orc_free(out)
     return blob
+
+
+def encode_lanes_u8(codes: np.ndarray, numels=None, max_code_len: int = 24, group_align: int = 128,
+                    group_max_elems: int = 4096, seg_max_bits: int = 15872) -> np.ndarray:
+    """Oracle's writer of a u8-kind interleaved-lane container: every byte of
+    `codes` is one symbol of the canonical code; no raw plane."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1)
+    if numels is None:
+        nump, nt = None, 1
+    else:
+        arr = np.ascontiguousarray(numels, dtype=np.uint64)
+        nump, nt = _p(arr, ctypes.c_uint64), arr.size
+    out = ctypes.POINTER(ctypes.c_uint8)()
+    nbytes = ctypes.c_uint64(0)
+    st = lib().orc_encode_lanes_u8(_p(codes, ctypes.c_uint8), codes.size, nump, nt, int(max_code_len),
+                                   int(group_align), int(group_max_elems), int(seg_max_bits), ctypes.byref(out),
+                                   ctypes.byref(nbytes))
+    if st:
+        raise OracleError(st, "encode_lanes_u8")
+    try:
+        blob = np.ctypeslib.as_array(out, shape=(nbytes.value,)).copy() if nbytes.value else np.zeros(0, np.uint8)
+    finally:
+        lib().orc_free(out)
+    return blob
+
+
+def decode_u8(blob: np.ndarray, with_report: bool = False):
+    """Serial decode of a u8-kind container: returns the bytes (uint8)."""
+    blob = np.ascontiguousarray(blob, dtype=np.uint8)
+    h = header(blob)
+    n = int(h["n_elems"])
+    out = np.empty(max(n, 1), np.uint8)
+    rep = Report()
+    st = lib().orc_decode_u8(_p(blob, ctypes.c_uint8), blob.size, _p(out, ctypes.c_uint8), n, ctypes.byref(rep))
+    if st:
+        raise OracleError(st, "decode_u8")
+    out = out[:n]
+    return (out, rep.as_dict()) if with_report else out
 
 
 def gemv_bf16(W: np.ndarray, x: np.ndarray) -> np.ndarray:

@@ -50,7 +50,12 @@
  *    one bit string (its lane blocks in order, elements in order), and the
  *    segment's stream is lane 0's string, then lane 1's, ... up to lane 63's;
  *    per segment the table holds its first element and first stream bit, and
- *    64 u16 offsets give where each lane's string starts inside it.
+ *    64 u16 offsets give where each lane's string starts inside it;
+ *  - symbol planes of 8-bit codes (version 3, element kind u8): for already
+ *    quantized weights (the LazyWeights page, analogy: Huffman codes for the
+ *    integer codes of a quantized model), every byte is one symbol of the
+ *    same canonical code, in the same lane layout, with no raw plane; the
+ *    decode gives back the bytes.
  */
 #include "oracle.h"
 
@@ -88,7 +93,10 @@
 #define F_OFF_SM       104   /* u64: u8 sm[n]                               */
 #define F_TOTAL        112   /* u64: whole container size                   */
 #define F_MAXG         120   /* u32 elements per group at most M            */
-#define F_TAIL         124   /* zero from here to the end of the header     */
+#define F_KIND         124   /* u8 element kind (version 3): 0 bf16, 1 u8   */
+#define F_TAIL         125   /* zero from here to the end of the header     */
+#define KIND_BF16        0   /* exponent coded, sign+mantissa plane raw     */
+#define KIND_U8          1   /* the whole byte coded, no raw plane          */
 
 static uint64_t rd(const uint8_t* p, int nbytes) {
     uint64_t v = 0;
@@ -453,22 +461,10 @@ int orc_encode(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n
     return ORC_OK;
 }
 
-int orc_encode_lanes(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
-                     uint32_t max_code_len, uint32_t A, uint32_t M, uint32_t B, uint8_t** blob,
-                     uint64_t* blob_bytes) {
-    if (!blob || !blob_bytes || (n && !w)) return ORC_E_ARG;
-    if (max_code_len < 1 || max_code_len > MAX_LEN_LIMIT || A < 1 || M < A || M % A) return ORC_E_ARG;
-    if (M > LANES * LANE_BLOCK * 1024u || B > 65535u || (uint64_t)A * max_code_len > B) return ORC_E_ARG;
-    uint64_t one_numel = n;
-    if (!numels) { numels = &one_numel; n_tensors = 1; }
-    uint64_t sum = 0;
-    for (uint32_t t = 0; t < n_tensors; ++t) sum += numels[t];
-    if (sum != n) return ORC_E_ARG;
-
-    uint8_t* e = (uint8_t*)malloc(n ? n : 1);
-    uint8_t* sm = (uint8_t*)malloc(n ? n : 1);
-    if (!e || !sm) { free(e); free(sm); return ORC_E_NOMEM; }
-    orc_split_planes(w, n, e, sm);
+/* Lanes writer over a symbol plane e (and, for bf16, the raw plane sm). */
+static int encode_lanes_planes(uint8_t* e, uint8_t* sm, uint32_t kind, uint64_t n, const uint64_t* numels,
+                               uint32_t n_tensors, uint32_t max_code_len, uint32_t A, uint32_t M, uint32_t B,
+                               uint8_t** blob, uint64_t* blob_bytes) {
     uint64_t hist[256] = {0};
     for (uint64_t i = 0; i < n; ++i) hist[e[i]]++;
     uint8_t lens[256];
@@ -505,7 +501,8 @@ int orc_encode_lanes(const uint16_t* w, uint64_t n, const uint64_t* numels, uint
     uint64_t off_loff = round_up(off_segs + 16 * (n_segs + 1), ALIGN);
     uint64_t off_stream = round_up(off_loff + 2ull * LANES * n_segs, ALIGN);
     uint64_t off_sm = round_up(off_stream + stream_bytes, ALIGN);
-    uint64_t total = round_up(off_sm + n, ALIGN);
+    uint64_t sm_bytes = kind == KIND_BF16 ? n : 0;
+    uint64_t total = round_up(off_sm + sm_bytes, ALIGN);
     uint8_t* b = (uint8_t*)calloc(total, 1);
     if (!b) { free(s_elem); free(s_bit); free(e); free(sm); return ORC_E_NOMEM; }
 
@@ -540,10 +537,11 @@ int orc_encode_lanes(const uint16_t* w, uint64_t n, const uint64_t* numels, uint
         wr(b + off_tens + 16ull * t + 8, numels[t], 8);
         acc += numels[t];
     }
-    if (n) memcpy(b + off_sm, sm, n);
+    if (sm_bytes) memcpy(b + off_sm, sm, sm_bytes);
 
     memcpy(b + F_MAGIC, "WCBF", 4);
     wr(b + F_VERSION, 3, 2);
+    wr(b + F_KIND, kind, 1);
     wr(b + F_FLAGS, 0, 2);
     wr(b + F_MAXLEN, max_code_len, 1);
     wr(b + F_LANES, LANES, 1);
@@ -571,11 +569,50 @@ int orc_encode_lanes(const uint16_t* w, uint64_t n, const uint64_t* numels, uint
     return ORC_OK;
 }
 
+static int lanes_args(uint64_t n, const void* src, const uint64_t** numels, uint32_t* n_tensors,
+                      uint64_t* one_numel, uint32_t max_code_len, uint32_t A, uint32_t M, uint32_t B,
+                      uint8_t** blob, uint64_t* blob_bytes) {
+    if (!blob || !blob_bytes || (n && !src)) return ORC_E_ARG;
+    if (max_code_len < 1 || max_code_len > MAX_LEN_LIMIT || A < 1 || M < A || M % A) return ORC_E_ARG;
+    if (M > LANES * LANE_BLOCK * 1024u || B > 65535u || (uint64_t)A * max_code_len > B) return ORC_E_ARG;
+    *one_numel = n;
+    if (!*numels) { *numels = one_numel; *n_tensors = 1; }
+    uint64_t sum = 0;
+    for (uint32_t t = 0; t < *n_tensors; ++t) sum += (*numels)[t];
+    return sum == n ? ORC_OK : ORC_E_ARG;
+}
+
+int orc_encode_lanes(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
+                     uint32_t max_code_len, uint32_t A, uint32_t M, uint32_t B, uint8_t** blob,
+                     uint64_t* blob_bytes) {
+    uint64_t one;
+    int st = lanes_args(n, w, &numels, &n_tensors, &one, max_code_len, A, M, B, blob, blob_bytes);
+    if (st != ORC_OK) return st;
+    uint8_t* e = (uint8_t*)malloc(n ? n : 1);
+    uint8_t* sm = (uint8_t*)malloc(n ? n : 1);
+    if (!e || !sm) { free(e); free(sm); return ORC_E_NOMEM; }
+    orc_split_planes(w, n, e, sm);
+    return encode_lanes_planes(e, sm, KIND_BF16, n, numels, n_tensors, max_code_len, A, M, B, blob, blob_bytes);
+}
+
+int orc_encode_lanes_u8(const uint8_t* codes, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
+                        uint32_t max_code_len, uint32_t A, uint32_t M, uint32_t B, uint8_t** blob,
+                        uint64_t* blob_bytes) {
+    uint64_t one;
+    int st = lanes_args(n, codes, &numels, &n_tensors, &one, max_code_len, A, M, B, blob, blob_bytes);
+    if (st != ORC_OK) return st;
+    uint8_t* e = (uint8_t*)malloc(n ? n : 1);
+    if (!e) return ORC_E_NOMEM;
+    if (n) memcpy(e, codes, n);
+    return encode_lanes_planes(e, NULL, KIND_U8, n, numels, n_tensors, max_code_len, A, M, B, blob, blob_bytes);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Reader                                                                   */
 /* ------------------------------------------------------------------------ */
 typedef struct {
     uint32_t version;   /* 2: per-chunk gaps; 3: interleaved lanes */
+    uint32_t kind;      /* KIND_BF16 or (version 3) KIND_U8 */
     uint32_t max_len, G, A, M, B, n_tensors;
     uint64_t n, stream_bits, n_chunks, n_groups;
     uint64_t off_len, off_tens, off_gs, off_gap, off_stream, stream_bytes, off_sm, total;
@@ -588,7 +625,9 @@ static int parse_header(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
     if (memcmp(blob + F_MAGIC, "WCBF", 4) != 0) return ORC_E_MAGIC;
     if (rd(blob + F_VERSION, 2) == 3) return parse_header_lanes(blob, bytes, h);
     h->version = 2;
+    h->kind = KIND_BF16;
     h->B = 0;
+    if (blob[F_KIND]) return ORC_E_MAGIC;
     if (rd(blob + F_VERSION, 2) != 2 || rd(blob + F_FLAGS, 2) != 0) return ORC_E_MAGIC;
     if (rd(blob + F_CHUNKBITS, 1) != CHUNK_BITS) return ORC_E_MAGIC;
     if (rd(blob + F_RES0, 2) != 0) return ORC_E_MAGIC;
@@ -633,6 +672,8 @@ static int parse_header(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
 
 static int parse_header_lanes(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
     h->version = 3;
+    h->kind = blob[F_KIND];
+    if (h->kind != KIND_BF16 && h->kind != KIND_U8) return ORC_E_MAGIC;
     if (rd(blob + F_FLAGS, 2) != 0 || rd(blob + F_LANES, 1) != LANES || rd(blob + F_LANE_BLOCK, 2) != LANE_BLOCK)
         return ORC_E_MAGIC;
     for (uint32_t k = F_TAIL; k < HDR_BYTES; ++k) if (blob[k]) return ORC_E_MAGIC;
@@ -664,7 +705,7 @@ static int parse_header_lanes(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
     if (h->stream_bits > h->n * (uint64_t)h->max_len || h->stream_bits < h->n) return ORC_E_SIZES;
     const uint64_t offs[6] = {h->off_len, h->off_tens, h->off_gs, h->off_gap, h->off_stream, h->off_sm};
     const uint64_t lens[6] = {256, 16ull * h->n_tensors, 16 * (h->n_groups + 1), 2ull * LANES * h->n_groups,
-                              h->stream_bytes, h->n};
+                              h->stream_bytes, h->kind == KIND_BF16 ? h->n : 0};
     uint64_t lo = HDR_BYTES;
     for (int k = 0; k < 6; ++k) {
         if (offs[k] % ALIGN || offs[k] < lo) return ORC_E_TRUNC;
@@ -691,6 +732,7 @@ int orc_header(const uint8_t* blob, uint64_t blob_bytes, orc_report* rep) {
         rep->max_code_len = h.max_len;
         rep->layout = h.version == 3 ? 1u : 0u;
         rep->seg_max_bits = h.B;
+        rep->elem_kind = h.kind;
     }
     return ORC_OK;
 }
@@ -779,7 +821,7 @@ static int trie_symbol(const trie_node* T, const uint8_t* stream, uint64_t limit
  * its stored offset and that the segment ends where the next begins; then
  * re-derive the segment table from the decoded code lengths. */
 static int decode_lanes(const uint8_t* blob, const hdr_t* h, const trie_node* T, const uint8_t* lens,
-                        uint16_t* out, uint64_t hist[256]) {
+                        uint16_t* out, uint8_t* out8, uint64_t hist[256]) {
     const uint8_t* stream = blob + h->off_stream;
     const uint8_t* segs = blob + h->off_gs;
     const uint8_t* loff = blob + h->off_gap;
@@ -831,18 +873,24 @@ static int decode_lanes(const uint8_t* blob, const hdr_t* h, const trie_node* T,
     }
     for (uint64_t i = 0; st == ORC_OK && i < h->n; ++i) {
         hist[e[i]]++;
-        uint16_t s = sm[i];
-        out[i] = (uint16_t)(((s & 0x80) << 8) | ((uint16_t)e[i] << 7) | (s & 0x7F));
+        if (h->kind == KIND_U8) {
+            out8[i] = e[i];
+        } else {
+            uint16_t s = sm[i];
+            out[i] = (uint16_t)(((s & 0x80) << 8) | ((uint16_t)e[i] << 7) | (s & 0x7F));
+        }
     }
     free(e);
     return st;
 }
 
-int orc_decode(const uint8_t* blob, uint64_t bytes, uint16_t* out, uint64_t out_cap, orc_report* rep) {
+static int decode_container(const uint8_t* blob, uint64_t bytes, uint32_t kind, uint16_t* out, uint8_t* out8,
+                            uint64_t out_cap, orc_report* rep) {
     hdr_t h;
     int st = parse_header(blob, bytes, &h);
     if (st != ORC_OK) return st;
-    if (h.n > out_cap || (h.n && !out)) return ORC_E_OUTSIZE;
+    if (h.kind != kind) return ORC_E_KIND;
+    if (h.n > out_cap || (h.n && !(kind == KIND_U8 ? (void*)out8 : (void*)out))) return ORC_E_OUTSIZE;
 
     /* tensor table must be a partition of [0, n) in order */
     {
@@ -910,7 +958,7 @@ int orc_decode(const uint8_t* blob, uint64_t bytes, uint16_t* out, uint64_t out_
     if (st != ORC_OK) { free(T); return st; }
     uint64_t hist[256] = {0};
     if (h.version == 3)
-        st = decode_lanes(blob, &h, T, lens, out, hist);
+        st = decode_lanes(blob, &h, T, lens, out, out8, hist);
     else
         st = decode_chunks(blob, &h, T, out, hist);
     free(T);
@@ -940,6 +988,7 @@ int orc_decode(const uint8_t* blob, uint64_t bytes, uint16_t* out, uint64_t out_
         rep->max_code_len = h.max_len;
         rep->layout = h.version == 3 ? 1u : 0u;
         rep->seg_max_bits = h.B;
+        rep->elem_kind = h.kind;
         rep->n_symbols = m;
         rep->longest_code = longest;
         rep->kraft_num = kraft;
@@ -955,6 +1004,14 @@ int orc_decode(const uint8_t* blob, uint64_t bytes, uint16_t* out, uint64_t out_
         rep->mean_code_bits = h.n ? Lsum / (double)h.n : 0.0;
     }
     return ORC_OK;
+}
+
+int orc_decode(const uint8_t* blob, uint64_t bytes, uint16_t* out, uint64_t out_cap, orc_report* rep) {
+    return decode_container(blob, bytes, KIND_BF16, out, NULL, out_cap, rep);
+}
+
+int orc_decode_u8(const uint8_t* blob, uint64_t bytes, uint8_t* out, uint64_t out_cap, orc_report* rep) {
+    return decode_container(blob, bytes, KIND_U8, NULL, out, out_cap, rep);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -48,6 +48,7 @@ extern "C" {
 #define ORC_E_SIZES      -12   /* n_chunks / n_groups / stream_bytes wrong   */
 #define ORC_E_NOMEM      -13
 #define ORC_E_OUTSIZE    -14   /* output buffer too small                    */
+#define ORC_E_KIND       -15   /* container holds another element kind       */
 
 /* What the decoder observed, for statistics-based pins. */
 typedef struct {
@@ -69,6 +70,8 @@ typedef struct {
     uint64_t hist[256];        /* exponent histogram of the decoded data     */
     uint32_t layout;           /* 0: per-chunk gaps (version 2); 1: lanes (3) */
     uint32_t seg_max_bits;     /* lanes layout: stream bits per segment max  */
+    uint32_t elem_kind;        /* 0: bf16 (exponent coded); 1: u8 symbols    */
+    uint32_t reserved2;
 } orc_report;
 
 /* Split bf16 words into exponent and sign+mantissa planes (definition). */
@@ -107,7 +110,18 @@ int orc_encode_lanes(const uint16_t* w, uint64_t n, const uint64_t* numels, uint
                      uint32_t max_code_len, uint32_t group_align, uint32_t group_max_elems,
                      uint32_t seg_max_bits, uint8_t** blob, uint64_t* blob_bytes);
 
-/* Serial bit-by-bit decoder with full container checks (either layout).
+/* The same layout over a plane of 8-bit codes (element kind u8): every byte
+ * is one symbol, there is no raw plane (the LazyWeights page's setting:
+ * Huffman codes for the integer codes of an already quantized model). */
+int orc_encode_lanes_u8(const uint8_t* codes, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
+                        uint32_t max_code_len, uint32_t group_align, uint32_t group_max_elems,
+                        uint32_t seg_max_bits, uint8_t** blob, uint64_t* blob_bytes);
+
+/* Serial decoder of a u8-kind container into n bytes (out_cap >= n). */
+int orc_decode_u8(const uint8_t* blob, uint64_t blob_bytes, uint8_t* out, uint64_t out_cap, orc_report* rep);
+
+/* Serial bit-by-bit decoder with full container checks (either layout,
+ * bf16 kind; ORC_E_KIND for a u8 container).
  * out must hold out_cap >= n_elems words.  rep may be NULL. */
 int orc_decode(const uint8_t* blob, uint64_t blob_bytes, uint16_t* out, uint64_t out_cap,
                orc_report* rep);

@@ -27,6 +27,7 @@ def header(blob: np.ndarray) -> dict:
     h = {k: struct.unpack_from(fmt, raw, off)[0] for k, (off, fmt) in HEADER_FIELDS.items()}
     h["magic"] = raw[:4]
     h["version"] = struct.unpack_from("<H", raw, 4)[0]
+    h["elem_kind"] = raw[124]
     if h["version"] == 3:
         h["lanes"] = raw[9]
         h["lane_block"] = struct.unpack_from("<H", raw, 10)[0]
@@ -46,7 +47,7 @@ def sections(blob: np.ndarray) -> dict:
     else:
         s["gap"] = blob[h["off_gap"]:h["off_gap"] + nc]
     s["stream"] = blob[h["off_stream"]:h["off_stream"] + h["stream_bytes"]]
-    s["sm"] = blob[h["off_sm"]:h["off_sm"] + n]
+    s["sm"] = blob[h["off_sm"]:h["off_sm"] + (n if h["elem_kind"] == 0 else 0)]
     return s
 
 
