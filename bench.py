@@ -37,6 +37,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "decompressed bf16 GB/s and % of HBM roofline (1 MI355X), bit-exact"
+METRIC_CODES = "decompressed 8-bit code GB/s and % of HBM roofline (1 MI355X), bit-exact"
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "lossless_entropy_coded_amd", "csrc")
 KERNEL_SOURCES = {"chunks": os.path.join(CSRC, "decode.hip"), "lanes": os.path.join(CSRC, "decode_lanes.hip")}
@@ -70,7 +71,8 @@ def parse_args():
                     help="untimed decode launches before the warm-up steps, for at least this much GPU time: "
                          "the GPU's clocks take about 100 back-to-back launches (~15 ms) to reach steady state")
     ap.add_argument("--workload", default="block_8b",
-                    help="synthetic workload (default: block_8b, the 8B-shape transformer block)")
+                    help="synthetic workload (default: block_8b, the 8B-shape transformer block; "
+                         "int8_codes_8b / int4_codes_8b: planes of quantized codes, decoded to bytes)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--layout", choices=["lanes", "chunks"], default="lanes",
                     help="container layout: lanes (v3, interleaved lanes; the library's default) or "
@@ -194,14 +196,14 @@ def end_to_end(args):
             wc.gemv_bf16_async(src[off:off + r * c], r, c, xs[c], ys[j], stream)
 
     def arm_a(k):
-        wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
+        decode(plan, blobs[k % copies], outs[k % copies], stream)
         gemvs(outs[k % copies], ya)
 
     def arm_b(k):
         gemvs(origs[k % copies], yb)
 
     def decode_only(k):
-        wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
+        decode(plan, blobs[k % copies], outs[k % copies], stream)
 
     def arm_c(k):
         wc.decode_gemv_async(plan, blobs[k % copies], ops, work, work_bytes, stream)
@@ -276,34 +278,46 @@ def main():
         return
 
     from lossless_entropy_coded_amd import wc
-    from lossless_entropy_coded_amd.synth import make_workload, workload_spec
+    from lossless_entropy_coded_amd.synth import CODE_WORKLOADS, make_code_workload, make_workload, workload_spec
 
+    # bf16 weights (the exponent coded, sm raw) or a plane of 8-bit quantized
+    # codes (every byte coded; lanes layout only)
+    codes = args.workload in CODE_WORKLOADS
+    if codes and args.layout != "lanes":
+        print("bench.py: code planes use the lanes layout", file=sys.stderr)
+        sys.exit(2)
     t_gen = time.perf_counter()
-    wl = make_workload(args.workload)
-    blob = wc.encode_host(wl.tensors(), layout=args.layout)
+    if codes:
+        wl = make_code_workload(args.workload)
+        blob = wc.encode_u8_host(wl.tensors())
+        raw, out_bytes, out_dtype, decode = wl.codes, 1, torch.uint8, wc.decode_u8_async
+    else:
+        wl = make_workload(args.workload)
+        blob = wc.encode_host(wl.tensors(), layout=args.layout)
+        raw, out_bytes, out_dtype, decode = wl.bits.view(np.int16), 2, torch.int16, wc.decode_async
     t_gen = time.perf_counter() - t_gen
     n = wl.n
     plan = wc.Plan(blob, device=0)
     st = plan.stats()
     stream_bits = st["stream_bits"]
-    # what the kernel must read: sm plane, stream, per-chunk gaps (v2) or
-    # per-lane offsets (v3), group/segment table; then the bf16 it writes
+    # what the kernel must read: sm plane (bf16), stream, per-chunk gaps (v2)
+    # or per-lane offsets (v3), group/segment table; then what it writes
     aux = -(-stream_bits // 64) if args.layout == "chunks" else 2 * 64 * st["n_groups"]
-    alg_read = n + -(-stream_bits // 8) + aux + 16 * (st["n_groups"] + 1)
-    alg_bytes = alg_read + 2 * n
+    alg_read = (0 if codes else n) + -(-stream_bits // 8) + aux + 16 * (st["n_groups"] + 1)
+    alg_bytes = alg_read + out_bytes * n
 
-    per_copy = blob.size + 2 * n
+    per_copy = blob.size + out_bytes * n
     copies = max(2, min(64, math.ceil((1 << 30) / per_copy)))
     blobs, outs, owners = [], [], []
     for _ in range(copies):
         own, view = aligned_device_copy(torch, blob)
         owners.append(own)
         blobs.append(view)
-        outs.append(torch.empty(n, dtype=torch.int16, device="cuda"))
-    ref = torch.from_numpy(wl.bits.view(np.int16)).cuda()
+        outs.append(torch.empty(n, dtype=out_dtype, device="cuda"))
+    ref = torch.from_numpy(raw).cuda()
 
     stream = torch.cuda.current_stream()
-    wc.decode_async(plan, blobs[0], outs[0], stream)
+    decode(plan, blobs[0], outs[0], stream)
     torch.cuda.synchronize()
     if not torch.equal(outs[0], ref):
         print("bench.py: decode is NOT bit-exact", file=sys.stderr)
@@ -316,13 +330,13 @@ def main():
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for k in range(25):
-            wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
+            decode(plan, blobs[k % copies], outs[k % copies], stream)
         b.record(stream)
         b.synchronize()
         settled_ms += a.elapsed_time(b)
         settle_launches += 25
     for k in range(args.warmup):
-        wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
+        decode(plan, blobs[k % copies], outs[k % copies], stream)
     # HIP events on the launch stream around the K back-to-back launches; a
     # step is exactly one launch of the decode kernel, so the average launch
     # duration is the timed region divided by K
@@ -331,7 +345,7 @@ def main():
     torch.cuda.synchronize()
     t0.record(stream)
     for k in range(args.steps):
-        wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
+        decode(plan, blobs[k % copies], outs[k % copies], stream)
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
@@ -342,7 +356,7 @@ def main():
         sys.exit(3)
 
     ms_per_step = total_ms / args.steps
-    value = 2.0 * n / (ms_per_step * 1e-3) / 1e9
+    value = out_bytes * n / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (kernel_avg_ms * 1e-3) / 1e9
 
     # spread of single launches (each bracketed by its own events), after the timed region
@@ -351,7 +365,7 @@ def main():
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
+        decode(plan, blobs[k % copies], outs[k % copies], stream)
         b.record(stream)
         b.synchronize()
         singles.append(a.elapsed_time(b) * 1e3)
@@ -370,17 +384,17 @@ def main():
         reps, spent = 0, 0.0
         while reps < 1 or (spent < 10.0 and reps < 8):
             t = time.perf_counter()
-            dec = oracle.decode(blob)
+            dec = oracle.decode_u8(blob) if codes else oracle.decode(blob)
             spent += time.perf_counter() - t
             reps += 1
-            assert np.array_equal(dec, wl.bits)
-        cpu = {"value": round(2.0 * n * reps / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            assert np.array_equal(dec, wl.codes if codes else wl.bits)
+        cpu = {"value": round(out_bytes * n * reps / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"the whole {args.workload} container ({n} elements) decoded {reps} times by the serial "
                          f"bit-by-bit trie decoder with every container check: {spent:.1f} s on one host core"}
 
-    desc = workload_spec(args.workload)[0]
+    desc = CODE_WORKLOADS[args.workload][0] if codes else workload_spec(args.workload)[0]
     line = {
-        "metric": METRIC,
+        "metric": METRIC_CODES if codes else METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -391,14 +405,15 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "u32",
-        "data": "synthetic: seeded bf16 weights, transformer-block shapes and distributions",
+        "data": ("synthetic: seeded quantized-code planes (rounded, clipped Gaussians), 8B-block matrix shapes"
+                 if codes else "synthetic: seeded bf16 weights, transformer-block shapes and distributions"),
         "config": {
             "workload": f"{args.workload}: {desc}",
             "layout": args.layout,
             "n_elems": n,
             "n_tensors": len(wl.numels),
             "container_bytes": int(blob.size),
-            "compression_ratio": round(2.0 * n / blob.size, 4),
+            "compression_ratio": round(out_bytes * n / blob.size, 4),
             "mean_code_bits": round(stream_bits / n, 4),
             "launches_per_step": 1,
             "count_bits": st["count_bits"],

@@ -61,6 +61,12 @@
  * A lane decodes a known number of symbols from its own bit string, so the
  * decoder needs no per-chunk gaps, no counting pass and no scan.
  *
+ * Element kind (v3, u8 at header byte 124): 0 = bf16 words as above; 1 = a
+ * plane of 8-bit codes (for instance the integer codes of a quantized model,
+ * the LazyWeights page's setting), where every byte is one symbol of the
+ * canonical code and there is no sm section (its length is 0).  Version 2
+ * containers hold bf16 only (byte 124 is 0).
+ *
  * Status codes: 0 on success, a negative WC_ERR_* value otherwise.  No C++
  * exception ever crosses this interface.
  */
@@ -130,7 +136,17 @@ typedef struct {
 int wc_encode_host(const uint16_t* const* tensors, const uint64_t* numels, uint32_t n_tensors,
                    const wc_encode_opts* opts, uint8_t** blob, uint64_t* blob_bytes);
 
-/* Release a buffer returned by wc_encode_host (NULL is ignored). */
+/*
+ * wc_encode_u8_host -- the same preparation for planes of 8-bit codes
+ * (element kind u8): each byte is a symbol of one shared canonical code; the
+ * container is the interleaved-lane layout (opts->layout must be
+ * WC_LAYOUT_LANES) with no raw plane.  tensors[k] points to numels[k] bytes.
+ * Decode with wc_decode_u8_async.
+ */
+int wc_encode_u8_host(const uint8_t* const* tensors, const uint64_t* numels, uint32_t n_tensors,
+                      const wc_encode_opts* opts, uint8_t** blob, uint64_t* blob_bytes);
+
+/* Release a buffer returned by wc_encode_host or wc_encode_u8_host (NULL is ignored). */
 void wc_free_host(uint8_t* blob);
 
 /* ---- planning ------------------------------------------------------------ */
@@ -167,6 +183,12 @@ int wc_plan_stats(const wc_plan_t* plan, uint64_t* container_bytes, uint64_t* st
                   uint32_t* lds_bytes);
 
 /*
+ * wc_plan_format -- the container's version (2: chunks, 3: lanes) and element
+ * kind (0: bf16, 1: u8).  Either output may be NULL.
+ */
+int wc_plan_format(const wc_plan_t* plan, uint32_t* version, uint32_t* elem_kind);
+
+/*
  * wc_decode_async -- decode every tensor of the container in ONE kernel launch
  * on `stream` (a hipStream_t; NULL = the device's null stream).
  *   blob_dev  device pointer to the same bytes given to wc_plan, 256-byte aligned;
@@ -179,6 +201,14 @@ int wc_plan_stats(const wc_plan_t* plan, uint64_t* container_bytes, uint64_t* st
  * The current device must be the plan's device.
  */
 int wc_decode_async(const wc_plan_t* plan, const void* blob_dev, uint16_t* out_dev, void* stream);
+
+/*
+ * wc_decode_u8_async -- the same for a u8-kind container: ONE launch decoding
+ * every byte into out_dev (n_elems bytes, 16-byte aligned, caller-owned).
+ * WC_ERR_INVALID_ARG for a bf16 container (and wc_decode_async rejects u8
+ * containers the same way).
+ */
+int wc_decode_u8_async(const wc_plan_t* plan, const void* blob_dev, uint8_t* out_dev, void* stream);
 
 /* ---- consumer of decoded weights ------------------------------------------ */
 /*

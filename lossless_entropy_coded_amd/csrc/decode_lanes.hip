@@ -27,6 +27,7 @@
 //           16-byte non-temporal stores, whole cache lines.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "decode_common.h"
@@ -64,12 +65,21 @@ __device__ __forceinline__ uint4 bswap4(const uint4& v) {
                       __builtin_bswap32(v.w));
 }
 
-// kDot = false: decode the segments to bf16 in p.out.  kDot = true (fused
+// Undo the one-bit rotation the decode tables store symbols with, in each
+// byte of a word (e = rol8(e', 1)).
+__device__ __forceinline__ uint32_t unrotate4(uint32_t x) {
+    return ((x << 1) & 0xFEFEFEFEu) | ((x >> 7) & 0x01010101u);
+}
+
+// kMode kLanesToBf16: decode bf16 segments into p.out.  kLanesToDot (fused
 // decode -> matrix-vector product): the decoded weights never leave the chip;
 // each wave multiplies its segment by x and leaves its partial dot products
-// in p.dot.part.
-template <int KD, int W, bool kDot>
+// in p.dot.part.  kLanesToU8: decode a plane of code bytes into p.out8 (no
+// sign+mantissa plane).
+template <int KD, int W, uint32_t kMode>
 __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodeParams p) {
+    constexpr bool kDot = kMode == kLanesToDot;
+    constexpr bool kU8 = kMode == kLanesToU8;
     constexpr uint32_t kThreads = kWaveLanes * W;
     // multi-codeword table, then the canonical arrays for long codes (the
     // plan's tables from the multi-codeword table on)
@@ -151,9 +161,11 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
         const uint8_t* const smu = p.sm + A;
         uint16_t* const outu = p.out + A;
         uint2 smv[kMergeSteps];
+        if constexpr (!kU8) {
 #pragma unroll
-        for (uint32_t k = 0; k < kMergeSteps; ++k)
-            smv[k] = load_nt8(smu + kMergeElems * min(lane + k * kWaveLanes, last_blk));
+            for (uint32_t k = 0; k < kMergeSteps; ++k)
+                smv[k] = load_nt8(smu + kMergeElems * min(lane + k * kWaveLanes, last_blk));
+        }
         // fused product: the x entries of the segment's blocks, loaded with
         // the sm bytes so that they have arrived by the merge
         DotRows dr;
@@ -213,6 +225,19 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
         if constexpr (kDot) {
             dot_group(p.dot, dr, full, lane, smv, xv, u - p.u_begin,
                       [&](uint32_t k) { return *reinterpret_cast<const uint2*>(slot + kMergeElems * k); });
+        } else if constexpr (kU8) {
+            uint8_t* const outb = p.out8 + A;
+#pragma unroll
+            for (uint32_t k = 0; k < kMergeSteps; ++k) {
+                const uint32_t blk = lane + k * kWaveLanes;
+                if (blk < full) {
+                    const uint2 e2 = *reinterpret_cast<const uint2*>(slot + kMergeElems * k);
+                    u32x2 v;
+                    v.x = unrotate4(e2.x);
+                    v.y = unrotate4(e2.y);
+                    __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(outb + kMergeElems * blk));
+                }
+            }
         } else {
 #pragma unroll
         for (uint32_t k = 0; k < kMergeSteps; ++k) {
@@ -232,11 +257,20 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
         }
         }
         // the container's last block, when it holds fewer than 8 elements (a
-        // matrix for the fused product never ends in a partial block)
-        if (!kDot && full * kMergeElems < n && lane == 0) {
+        // matrix for the fused product never ends in a partial block); block
+        // `full` is the (full / 64)-th of lane full % 64
+        if (kU8 && full * kMergeElems < n && lane == 0) {
+            const uint32_t rel = kMergeElems * full;
+            const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + kLaneSlotBytes * (full % kWaveLanes) +
+                                                             kMergeElems * (full / kWaveLanes));
+            const uint32_t o[2] = {unrotate4(e2.x), unrotate4(e2.y)};
+#pragma unroll
+            for (uint32_t i = 0; i < kMergeElems; ++i)
+                if (rel + i < n) p.out8[A + rel + i] = (uint8_t)(o[i >> 2] >> (8 * (i & 3)));
+        }
+        if (kMode == kLanesToBf16 && full * kMergeElems < n && lane == 0) {
             const uint32_t rel = kMergeElems * full;
             const uint2 s2 = load_nt8(p.sm + A + rel);
-            // block `full` is the (full / 64)-th of lane full % 64
             const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + kLaneSlotBytes * (full % kWaveLanes) +
                                                              kMergeElems * (full / kWaveLanes));
             uint32_t o[4];
@@ -257,21 +291,26 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
 
 template <int KD, int W>
 struct LanesVariant {
-    static hipError_t launch(const DecodeParams& p, uint32_t grid, uint32_t dyn, bool dot, hipStream_t stream) {
-        if (dot)
-            hipLaunchKernelGGL((decode_lanes_kernel<KD, W, true>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
+    static hipError_t launch(const DecodeParams& p, uint32_t grid, uint32_t dyn, LanesOut mode, hipStream_t stream) {
+        const dim3 g(grid), b(kWaveLanes * W);
+        if (mode == kLanesToDot)
+            hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToDot>), g, b, dyn, stream, p);
+        else if (mode == kLanesToU8)
+            hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToU8>), g, b, dyn, stream, p);
         else
-            hipLaunchKernelGGL((decode_lanes_kernel<KD, W, false>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
+            hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToBf16>), g, b, dyn, stream, p);
         return hipGetLastError();
     }
     static int blocks_per_cu(uint32_t dyn) {
-        int n = 0, m = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lanes_kernel<KD, W, false>, kWaveLanes * W, dyn) !=
-                hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, decode_lanes_kernel<KD, W, true>, kWaveLanes * W, dyn) !=
-                hipSuccess)
+        int n[3] = {0, 0, 0};
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[0], decode_lanes_kernel<KD, W, kLanesToBf16>,
+                                                         kWaveLanes * W, dyn) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[1], decode_lanes_kernel<KD, W, kLanesToDot>,
+                                                         kWaveLanes * W, dyn) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[2], decode_lanes_kernel<KD, W, kLanesToU8>,
+                                                         kWaveLanes * W, dyn) != hipSuccess)
             return 0;
-        return n < m ? n : m;
+        return std::min(n[0], std::min(n[1], n[2]));
     }
 };
 
@@ -302,13 +341,13 @@ int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2
     return n;
 }
 
-hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid, bool dot,
-                               hipStream_t stream) {
+hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid,
+                               LanesOut mode, hipStream_t stream) {
     if ((decode_bits != 11 && decode_bits != 10) || !supported_waves(waves) || p.l2_cap > kL2Prefixes)
         return hipErrorInvalidValue;
     const uint32_t dyn = decode_lanes_dyn_lds_bytes(waves, p.l2_cap);
     return dispatch_lanes(decode_bits, waves,
-                          [&](auto v) { return decltype(v)::launch(p, grid, dyn, dot, stream); });
+                          [&](auto v) { return decltype(v)::launch(p, grid, dyn, mode, stream); });
 }
 
 }  // namespace wc

@@ -37,6 +37,9 @@ namespace {
 
 inline uint8_t exponent_of(uint16_t b) { return (uint8_t)(b >> 7); }   // bits 14..7 (bit 15 shifted out)
 inline uint8_t sign_mantissa_of(uint16_t b) { return (uint8_t)(((b >> 8) & 0x80u) | (b & 0x7Fu)); }
+// The coded symbol of an element: a bf16 word's exponent, or a code byte itself.
+inline uint8_t symbol_of(uint16_t b) { return exponent_of(b); }
+inline uint8_t symbol_of(uint8_t b) { return b; }
 
 // ---------------------------------------------------------------------------
 // Optimal length-limited code: package-merge over a node pool.  A node is a
@@ -119,13 +122,14 @@ void canonical_codes(const uint8_t len[256], uint32_t code[256]) {
 }
 
 // Global element index space over several tensors.
-struct Source {
-    std::vector<const uint16_t*> ptr;
+template <typename T>
+struct SourceT {
+    std::vector<const T*> ptr;
     std::vector<uint64_t> begin;   // global index of each tensor's first element
     std::vector<uint64_t> size;
 
     template <typename F>
-    void for_range(uint64_t i0, uint64_t i1, F&& f) const {   // f(global_index, const uint16_t* p, count)
+    void for_range(uint64_t i0, uint64_t i1, F&& f) const {   // f(global_index, const T* p, count)
         size_t t = std::upper_bound(begin.begin(), begin.end(), i0) - begin.begin() - 1;
         uint64_t i = i0;
         while (i < i1) {
@@ -135,7 +139,7 @@ struct Source {
             i += k;
         }
     }
-    uint16_t at(uint64_t i) const {
+    T at(uint64_t i) const {
         size_t t = std::upper_bound(begin.begin(), begin.end(), i) - begin.begin() - 1;
         while (size[t] == 0 || i >= begin[t] + size[t]) ++t;
         return ptr[t][i - begin[t]];
@@ -182,8 +186,10 @@ struct BitWriter {
 };
 
 // Container v3: segments of whole blocks (at most max_elems elements and
-// seg_bits stream bits), each written lane by lane.
-int write_lanes(const Source& src, uint64_t n, uint32_t n_tensors, const uint8_t len[256], const uint32_t code[256],
+// seg_bits stream bits), each written lane by lane; bf16 elements also write
+// their sign+mantissa plane, code bytes have none.
+template <typename T>
+int write_lanes(const SourceT<T>& src, uint64_t n, uint32_t n_tensors, const uint8_t len[256], const uint32_t code[256],
                 uint32_t max_len, uint32_t align, uint32_t max_elems, uint32_t seg_bits,
                 const std::vector<uint64_t>& block_bit, uint64_t stream_bits, unsigned nthreads, uint8_t** blob,
                 uint64_t* blob_bytes) {
@@ -198,11 +204,14 @@ int write_lanes(const Source& src, uint64_t n, uint32_t n_tensors, const uint8_t
         k0 = k1;
     }
     const uint64_t n_segs = s_elem.size() - 1;
-    const Header h = layout_lanes(n, stream_bits, n_tensors, max_len, align, max_elems, seg_bits, n_segs);
+    constexpr bool kBf16 = sizeof(T) == 2;
+    const Header h = layout_lanes(n, stream_bits, n_tensors, max_len, align, max_elems, seg_bits, n_segs,
+                                  kBf16 ? kKindBf16 : kKindU8);
+    const uint64_t sm_bytes = kBf16 ? n : 0;
     uint8_t* out = (uint8_t*)std::aligned_alloc(kAlign, h.total_bytes);
     if (!out) return WC_ERR_NOMEM;
     std::memset(out, 0, h.off_sm);
-    std::memset(out + h.off_sm + n, 0, h.total_bytes - h.off_sm - n);
+    std::memset(out + h.off_sm + sm_bytes, 0, h.total_bytes - h.off_sm - sm_bytes);
     write_header(out, h);
     std::memcpy(out + h.off_code_len, len, 256);
     for (uint32_t k = 0; k < n_tensors; ++k) {
@@ -216,26 +225,27 @@ int write_lanes(const Source& src, uint64_t n, uint32_t n_tensors, const uint8_t
     uint8_t* stream = out + h.off_stream;
     uint8_t* lane_off = out + h.off_gap;
     uint8_t* sm = out + h.off_sm;
-    const unsigned T = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(nthreads, n_segs));
-    parallel_for(T, [&](unsigned t) {
-        const uint64_t g0 = n_segs * t / T, g1 = n_segs * (t + 1) / T;
+    const unsigned nt = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(nthreads, n_segs));
+    parallel_for(nt, [&](unsigned t) {
+        const uint64_t g0 = n_segs * t / nt, g1 = n_segs * (t + 1) / nt;
         if (g0 == g1) return;
         BitWriter bw(stream, s_bit[g0]);
         uint64_t pos = s_bit[g0];
-        std::vector<uint16_t> seg(max_elems);
+        std::vector<T> seg(max_elems);
         for (uint64_t g = g0; g < g1; ++g) {
             const uint64_t e0 = s_elem[g], m = s_elem[g + 1] - e0;
-            src.for_range(e0, e0 + m, [&](uint64_t gi, const uint16_t* p, uint64_t k) {
-                std::memcpy(seg.data() + (gi - e0), p, k * sizeof(uint16_t));
+            src.for_range(e0, e0 + m, [&](uint64_t gi, const T* p, uint64_t k) {
+                std::memcpy(seg.data() + (gi - e0), p, k * sizeof(T));
             });
-            for (uint64_t i = 0; i < m; ++i) sm[e0 + i] = sign_mantissa_of(seg[i]);
+            if constexpr (kBf16)
+                for (uint64_t i = 0; i < m; ++i) sm[e0 + i] = sign_mantissa_of(seg[i]);
             const uint64_t nb8 = div_up(m, kLaneBlock);
             for (uint32_t j = 0; j < kLanes; ++j) {
                 store_le<uint16_t>(lane_off + 2 * (kLanes * g + j), (uint16_t)(pos - s_bit[g]));
                 for (uint64_t b = j; b < nb8; b += kLanes) {
                     const uint64_t i1 = std::min<uint64_t>(m, kLaneBlock * (b + 1));
                     for (uint64_t i = kLaneBlock * b; i < i1; ++i) {
-                        const uint8_t e = exponent_of(seg[i]);
+                        const uint8_t e = symbol_of(seg[i]);
                         bw.put_code(code[e], len[e]);
                         pos += len[e];
                     }
@@ -249,12 +259,11 @@ int write_lanes(const Source& src, uint64_t n, uint32_t n_tensors, const uint8_t
     return WC_OK;
 }
 
-}  // namespace
-}  // namespace wc
-
-extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* numels, uint32_t n_tensors,
-                              const wc_encode_opts* opts, uint8_t** blob, uint64_t* blob_bytes) {
-    using namespace wc;
+// The whole encoder for bf16 words (T = uint16_t) or code bytes (T = uint8_t).
+template <typename T>
+int encode_impl(const T* const* tensors, const uint64_t* numels, uint32_t n_tensors, const wc_encode_opts* opts,
+                uint8_t** blob, uint64_t* blob_bytes) {
+    constexpr bool kBf16 = sizeof(T) == 2;
     if (!blob || !blob_bytes) return WC_ERR_INVALID_ARG;
     *blob = nullptr;
     *blob_bytes = 0;
@@ -284,8 +293,9 @@ extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* nu
     } else {
         return WC_ERR_INVALID_ARG;
     }
+    if (!kBf16 && kind != WC_LAYOUT_LANES) return WC_ERR_INVALID_ARG;   // code planes: lanes layout only
 
-    Source src;
+    SourceT<T> src;
     uint64_t n = 0;
     for (uint32_t k = 0; k < n_tensors; ++k) {
         if (numels[k] && !tensors[k]) return WC_ERR_INVALID_ARG;
@@ -308,8 +318,8 @@ extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* nu
     parallel_for(nthreads, [&](unsigned t) {
         auto& h = hist_t[t];
         h.fill(0);
-        src.for_range(r0[t], r0[t + 1], [&](uint64_t, const uint16_t* p, uint64_t k) {
-            for (uint64_t j = 0; j < k; ++j) ++h[exponent_of(p[j])];
+        src.for_range(r0[t], r0[t + 1], [&](uint64_t, const T* p, uint64_t k) {
+            for (uint64_t j = 0; j < k; ++j) ++h[symbol_of(p[j])];
         });
     });
     uint64_t hist[256] = {0};
@@ -337,10 +347,10 @@ extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* nu
     std::vector<uint64_t> block_bit(n_blocks + 1, 0);
     parallel_for(nthreads, [&](unsigned t) {
         uint64_t pos = tbits[t];
-        src.for_range(r0[t], r0[t + 1], [&](uint64_t gi, const uint16_t* p, uint64_t k) {
+        src.for_range(r0[t], r0[t + 1], [&](uint64_t gi, const T* p, uint64_t k) {
             for (uint64_t j = 0; j < k; ++j) {
                 if ((gi + j) % align == 0) block_bit[(gi + j) / align] = pos;
-                pos += len[exponent_of(p[j])];
+                pos += len[symbol_of(p[j])];
             }
         });
     });
@@ -404,7 +414,7 @@ extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* nu
             }
             ++wbyte;
         };
-        src.for_range(i0, i1, [&](uint64_t gi, const uint16_t* p, uint64_t k) {
+        src.for_range(i0, i1, [&](uint64_t gi, const T* p, uint64_t k) {
             for (uint64_t j = 0; j < k; ++j) {
                 const uint16_t b = p[j];
                 const uint8_t e = exponent_of(b);
@@ -433,6 +443,19 @@ extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* nu
     *blob = out;
     *blob_bytes = h.total_bytes;
     return WC_OK;
+}
+
+}  // namespace
+}  // namespace wc
+
+extern "C" int wc_encode_host(const uint16_t* const* tensors, const uint64_t* numels, uint32_t n_tensors,
+                              const wc_encode_opts* opts, uint8_t** blob, uint64_t* blob_bytes) {
+    return wc::encode_impl<uint16_t>(tensors, numels, n_tensors, opts, blob, blob_bytes);
+}
+
+extern "C" int wc_encode_u8_host(const uint8_t* const* tensors, const uint64_t* numels, uint32_t n_tensors,
+                                 const wc_encode_opts* opts, uint8_t** blob, uint64_t* blob_bytes) {
+    return wc::encode_impl<uint8_t>(tensors, numels, n_tensors, opts, blob, blob_bytes);
 }
 
 extern "C" void wc_free_host(uint8_t* blob) { std::free(blob); }

@@ -29,6 +29,11 @@ constexpr uint32_t kLanes = 64;
 constexpr uint32_t kLaneBlock = 8;
 constexpr uint32_t kLanesSlack = 64;       // zero bytes after the 8-byte-padded stream
 constexpr uint32_t kDefaultSegBits = 15872;   // stream bits per segment at most (1984 bytes)
+// Element kinds of a version-3 container: bf16 words (the exponent coded, the
+// sign+mantissa byte raw) or bytes (each byte coded, no raw plane: planes of
+// quantized integer codes).
+constexpr uint32_t kKindBf16 = 0;
+constexpr uint32_t kKindU8 = 1;
 
 // Header field offsets (little-endian).
 struct HeaderOffsets {
@@ -37,7 +42,7 @@ struct HeaderOffsets {
                          n_elems = 24, stream_bits = 32, n_chunks = 40, n_groups = 48,
                          off_code_len = 56, off_tensors = 64, off_groups = 72, off_gap = 80,
                          off_stream = 88, stream_bytes = 96, off_sm = 104, total_bytes = 112,
-                         group_max_elems = 120, reserved_tail = 124;
+                         group_max_elems = 120, elem_kind = 124, reserved_tail = 125;
     // version 3 reuses the positions: lanes at 9, lane block at 10, the
     // segment bit cap at 12, the lane offsets at off_gap; n_chunks is 0
     static constexpr int lanes = 9, lane_block = 10, seg_max_bits = 12;
@@ -46,6 +51,7 @@ struct HeaderOffsets {
 struct Header {
     uint32_t version = kVersion;   // kVersion or kVersionLanes
     uint32_t seg_max_bits = 0;     // version 3
+    uint32_t elem_kind = kKindBf16;   // version 3: kKindBf16 or kKindU8
     uint32_t max_code_len = 0, chunks_per_group = 0, n_tensors = 0, group_align = 0, group_max_elems = 0;
     uint64_t n_elems = 0, stream_bits = 0, n_chunks = 0, n_groups = 0;
     uint64_t off_code_len = 0, off_tensors = 0, off_groups = 0, off_gap = 0, off_stream = 0,
@@ -99,9 +105,11 @@ inline Header layout(uint64_t n_elems, uint64_t stream_bits, uint32_t n_tensors,
 // Section placement of a version-3 (interleaved-lane) container; the lane
 // offsets take the place of the gaps (off_gap).
 inline Header layout_lanes(uint64_t n_elems, uint64_t stream_bits, uint32_t n_tensors, uint32_t max_code_len,
-                           uint32_t align, uint32_t max_elems, uint32_t seg_max_bits, uint64_t n_segs) {
+                           uint32_t align, uint32_t max_elems, uint32_t seg_max_bits, uint64_t n_segs,
+                           uint32_t elem_kind = kKindBf16) {
     Header h;
     h.version = kVersionLanes;
+    h.elem_kind = elem_kind;
     h.seg_max_bits = seg_max_bits;
     h.max_code_len = max_code_len;
     h.group_align = align;
@@ -118,7 +126,7 @@ inline Header layout_lanes(uint64_t n_elems, uint64_t stream_bits, uint32_t n_te
     h.off_gap = round_up(h.off_groups + kGroupEntryBytes * (n_segs + 1), kAlign);
     h.off_stream = round_up(h.off_gap + 2ull * kLanes * n_segs, kAlign);
     h.off_sm = round_up(h.off_stream + h.stream_bytes, kAlign);
-    h.total_bytes = round_up(h.off_sm + n_elems, kAlign);
+    h.total_bytes = round_up(h.off_sm + (elem_kind == kKindBf16 ? n_elems : 0), kAlign);
     return h;
 }
 
@@ -132,6 +140,7 @@ inline void write_header(uint8_t* p, const Header& h) {
         store_le<uint8_t>(p + O::lanes, (uint8_t)kLanes);
         store_le<uint16_t>(p + O::lane_block, (uint16_t)kLaneBlock);
         store_le<uint32_t>(p + O::seg_max_bits, h.seg_max_bits);
+        store_le<uint8_t>(p + O::elem_kind, (uint8_t)h.elem_kind);
     } else {
         store_le<uint8_t>(p + O::chunk_bits, (uint8_t)kChunkBits);
         store_le<uint32_t>(p + O::chunks_per_group, h.chunks_per_group);

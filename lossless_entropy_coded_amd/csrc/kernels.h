@@ -98,6 +98,7 @@ struct DecodeParams {
     const uint64_t* groups;  // {first element, first bit} per group, n_groups + 1 entries
     const uint8_t* sm;
     uint16_t* out;           // decoded bf16 (decode launches)
+    uint8_t* out8;           // decoded bytes (u8-kind lanes launches)
     const uint32_t* tables;
     uint64_t n_elems;
     uint64_t u_begin;        // groups [u_begin, u_end) are decoded, one per wave
@@ -146,11 +147,15 @@ hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t de
 // decoding segments [p.u_begin, p.u_end) to bf16 in p.out, or (dot) to
 // partial dot products in p.dot; p.gap points at the lane offsets and
 // p.tables at the multi-codeword table of the plan's tables.
+// What a lanes launch produces: bf16 words in p.out (the exponent coded,
+// joined with the sign+mantissa plane), partial dot products in p.dot, or
+// the decoded bytes themselves in p.out8 (u8-kind containers).
+enum LanesOut : uint32_t { kLanesToBf16 = 0, kLanesToDot = 1, kLanesToU8 = 2 };
 uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap);
 uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap);
 int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap);
-hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid, bool dot,
-                               hipStream_t stream);
+hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid,
+                               LanesOut mode, hipStream_t stream);
 
 // One launch adding, for every global row of p.dot, the partial dot products
 // of the groups covering it, in group order, into the row's y.

@@ -62,6 +62,8 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
     }
     for (uint32_t k = O::reserved_tail; k < wc::kHeaderBytes; ++k)
         if (b[k]) return WC_ERR_BAD_MAGIC;
+    h.elem_kind = b[O::elem_kind];
+    if (h.elem_kind != wc::kKindBf16 && (!lanes || h.elem_kind != wc::kKindU8)) return WC_ERR_BAD_MAGIC;
     h.max_code_len = b[O::max_code_len];
     h.chunks_per_group = lanes ? 0u : load_le<uint32_t>(b + O::chunks_per_group);
     h.seg_max_bits = lanes ? load_le<uint32_t>(b + O::seg_max_bits) : 0u;
@@ -101,7 +103,8 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
     if (h.n_tensors > (1u << 24)) return WC_ERR_SECTION_BOUNDS;
     const uint64_t off[6] = {h.off_code_len, h.off_tensors, h.off_groups, h.off_gap, h.off_stream, h.off_sm};
     const uint64_t len[6] = {256, 16ull * h.n_tensors, wc::kGroupEntryBytes * (h.n_groups + 1),
-                             lanes ? 2ull * wc::kLanes * h.n_groups : h.n_chunks, h.stream_bytes, h.n_elems};
+                             lanes ? 2ull * wc::kLanes * h.n_groups : h.n_chunks, h.stream_bytes,
+                             h.elem_kind == wc::kKindBf16 ? h.n_elems : 0};
     uint64_t lo = wc::kHeaderBytes;
     for (int k = 0; k < 6; ++k) {
         if (off[k] % wc::kAlign || off[k] < lo || off[k] > h.total_bytes || len[k] > h.total_bytes - off[k])
@@ -109,7 +112,8 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
         lo = off[k] + len[k];
     }
     // the decoder reads the sign+mantissa plane in 16-byte blocks
-    if (wc::round_up(h.n_elems, 16) > h.total_bytes - h.off_sm) return WC_ERR_SECTION_BOUNDS;
+    if (h.elem_kind == wc::kKindBf16 && wc::round_up(h.n_elems, 16) > h.total_bytes - h.off_sm)
+        return WC_ERR_SECTION_BOUNDS;
 
     // tensor table
     toff.resize(h.n_tensors);
@@ -362,7 +366,7 @@ extern "C" int wc_plan_stats(const wc_plan_t* p, uint64_t* container_bytes, uint
 }
 
 extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_t* out_dev, void* stream) {
-    if (!p) return WC_ERR_INVALID_ARG;
+    if (!p || p->h.elem_kind != wc::kKindBf16) return WC_ERR_INVALID_ARG;
     if (p->h.n_elems == 0) return WC_OK;
     if (!blob_dev || !out_dev) return WC_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(blob_dev) & 255u) || (reinterpret_cast<uintptr_t>(out_dev) & 15u))
@@ -377,6 +381,7 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
     d.groups = reinterpret_cast<const uint64_t*>(b + p->h.off_groups);
     d.sm = b + p->h.off_sm;
     d.out = out_dev;
+    d.out8 = nullptr;
     d.tables = p->d_tables;
     d.n_elems = p->h.n_elems;
     d.u_begin = 0;
@@ -388,12 +393,48 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
         // the lane offsets sit where the gaps do; the kernel stages the tables
         // from the multi-codeword table on
         d.tables = p->d_tables + (1u << p->count_bits);
-        e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, p->grid, false, static_cast<hipStream_t>(stream));
+        e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, p->grid, wc::kLanesToBf16,
+                                    static_cast<hipStream_t>(stream));
     } else {
         e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, p->grid, false,
                               static_cast<hipStream_t>(stream));
     }
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
+}
+
+extern "C" int wc_decode_u8_async(const wc_plan_t* p, const void* blob_dev, uint8_t* out_dev, void* stream) {
+    if (!p || p->h.elem_kind != wc::kKindU8) return WC_ERR_INVALID_ARG;
+    if (p->h.n_elems == 0) return WC_OK;
+    if (!blob_dev || !out_dev) return WC_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(blob_dev) & 255u) || (reinterpret_cast<uintptr_t>(out_dev) & 15u))
+        return WC_ERR_INVALID_ARG;
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return WC_ERR_HIP;
+    if (cur != p->device) return WC_ERR_INVALID_ARG;
+    const uint8_t* b = static_cast<const uint8_t*>(blob_dev);
+    wc::DecodeParams d;
+    d.stream = b + p->h.off_stream;
+    d.gap = b + p->h.off_gap;
+    d.groups = reinterpret_cast<const uint64_t*>(b + p->h.off_groups);
+    d.sm = nullptr;
+    d.out = nullptr;
+    d.out8 = out_dev;
+    d.tables = p->d_tables + (1u << p->count_bits);
+    d.n_elems = p->h.n_elems;
+    d.u_begin = 0;
+    d.u_end = p->h.n_groups;
+    d.ebuf_bytes = p->ebuf_bytes;
+    d.l2_cap = p->l2_cap;
+    const hipError_t e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, p->grid, wc::kLanesToU8,
+                                                 static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? WC_OK : WC_ERR_HIP;
+}
+
+extern "C" int wc_plan_format(const wc_plan_t* p, uint32_t* version, uint32_t* elem_kind) {
+    if (!p) return WC_ERR_INVALID_ARG;
+    if (version) *version = p->h.version;
+    if (elem_kind) *elem_kind = p->h.elem_kind;
+    return WC_OK;
 }
 
 namespace {
@@ -403,7 +444,8 @@ namespace {
 // partials, then the per-row first groups, each 256-byte aligned).
 int prepare_gemv(const wc_plan_t* p, const wc_gemv_operand* ops, uint32_t n_ops, wc::DotParams& q,
                  uint64_t& u_begin, uint64_t& u_end, uint64_t& work_bytes, uint64_t& rows_off) {
-    if (!p || !ops || n_ops == 0 || n_ops > wc::kMaxDotMats) return WC_ERR_INVALID_ARG;
+    if (!p || !ops || n_ops == 0 || n_ops > wc::kMaxDotMats || p->h.elem_kind != wc::kKindBf16)
+        return WC_ERR_INVALID_ARG;
     std::memset(&q, 0, sizeof(q));
     uint64_t rows = 0;
     for (uint32_t i = 0; i < n_ops; ++i) {
@@ -473,6 +515,7 @@ extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, co
     d.groups = reinterpret_cast<const uint64_t*>(b + p->h.off_groups);
     d.sm = b + p->h.off_sm;
     d.out = nullptr;
+    d.out8 = nullptr;
     d.tables = p->d_tables;
     d.n_elems = p->h.n_elems;
     d.ebuf_bytes = p->ebuf_bytes;
@@ -485,7 +528,7 @@ extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, co
     hipError_t e;
     if (p->lanes) {
         d.tables = p->d_tables + (1u << p->count_bits);
-        e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, grid, true, s);
+        e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, grid, wc::kLanesToDot, s);
     } else {
         e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, grid, true, s);
     }

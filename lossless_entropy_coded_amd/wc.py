@@ -41,6 +41,9 @@ class EncodeOpts(ctypes.Structure):
 _lib.wc_encode_host.argtypes = [ctypes.POINTER(_u16p), _u64p, ctypes.c_uint32, ctypes.POINTER(EncodeOpts),
                                 ctypes.POINTER(_u8p), _u64p]
 _lib.wc_encode_host.restype = ctypes.c_int
+_lib.wc_encode_u8_host.argtypes = [ctypes.POINTER(_u8p), _u64p, ctypes.c_uint32, ctypes.POINTER(EncodeOpts),
+                                   ctypes.POINTER(_u8p), _u64p]
+_lib.wc_encode_u8_host.restype = ctypes.c_int
 _lib.wc_free_host.argtypes = [_u8p]
 _lib.wc_free_host.restype = None
 _lib.wc_plan.argtypes = [_u8p, ctypes.c_uint64, ctypes.c_int, ctypes.POINTER(ctypes.c_void_p)]
@@ -51,6 +54,10 @@ _lib.wc_plan_stats.argtypes = [ctypes.c_void_p, _u64p, _u64p, _u64p, _u32p, _u32
 _lib.wc_plan_stats.restype = ctypes.c_int
 _lib.wc_decode_async.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
 _lib.wc_decode_async.restype = ctypes.c_int
+_lib.wc_decode_u8_async.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+_lib.wc_decode_u8_async.restype = ctypes.c_int
+_lib.wc_plan_format.argtypes = [ctypes.c_void_p, _u32p, _u32p]
+_lib.wc_plan_format.restype = ctypes.c_int
 _lib.wc_gemv_bf16_async.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p]
 _lib.wc_gemv_bf16_async.restype = ctypes.c_int
@@ -100,7 +107,8 @@ GROUP_MAX_ELEMS = 4096
 SEG_MAX_BITS = 15872
 LAYOUTS = {"lanes": 0, "chunks": 1}
 
-EXPORTED = ("wc_encode_host", "wc_free_host", "wc_plan", "wc_plan_info", "wc_plan_stats",
+EXPORTED = ("wc_encode_host", "wc_encode_u8_host", "wc_free_host", "wc_plan", "wc_plan_info", "wc_plan_stats",
+            "wc_plan_format", "wc_decode_u8_async",
             "wc_decode_async", "wc_gemv_bf16_async", "wc_decode_gemv_work_bytes", "wc_decode_gemv_async",
             "wc_plan_destroy", "wc_status_str")
 
@@ -161,6 +169,28 @@ def encode_host(tensors, max_code_len: int = 24, chunks_per_group: int = GROUP_C
     return blob
 
 
+def encode_u8_host(tensors, max_code_len: int = 24, n_threads: int = 0, group_align: int = GROUP_ALIGN,
+                   group_max_elems: int = GROUP_MAX_ELEMS, seg_max_bits: int = SEG_MAX_BITS) -> np.ndarray:
+    """wc_encode_u8_host over a list of uint8 code planes (numpy or torch CPU): a u8-kind
+    interleaved-lane container (each byte one symbol, no raw plane)."""
+    arrs = [np.ascontiguousarray(t.numpy() if hasattr(t, "numpy") else t).reshape(-1).view(np.uint8)
+            for t in tensors]
+    nt = len(arrs)
+    ptrs = (_u8p * max(nt, 1))(*[a.ctypes.data_as(_u8p) for a in arrs])
+    numels = (ctypes.c_uint64 * max(nt, 1))(*[a.size for a in arrs])
+    opts = EncodeOpts(max_code_len, 8, 0, n_threads, group_align, group_max_elems, LAYOUTS["lanes"], seg_max_bits)
+    out = _u8p()
+    nbytes = ctypes.c_uint64(0)
+    _check(_lib.wc_encode_u8_host(ptrs, numels, nt, ctypes.byref(opts), ctypes.byref(out), ctypes.byref(nbytes)),
+           "wc_encode_u8_host")
+    try:
+        blob = np.empty(nbytes.value, np.uint8)
+        ctypes.memmove(blob.ctypes.data, out, nbytes.value)
+    finally:
+        _lib.wc_free_host(out)
+    return blob
+
+
 class Plan:
     """wc_plan over a host container; owns the native plan until close()."""
 
@@ -187,6 +217,12 @@ class Plan:
         if self._h is None:
             raise RuntimeError("plan is closed")
         return self._h
+
+    def format(self):
+        """wc_plan_format: (container version, element kind: 0 bf16, 1 u8)."""
+        v, k = ctypes.c_uint32(), ctypes.c_uint32()
+        _check(_lib.wc_plan_format(self.handle, ctypes.byref(v), ctypes.byref(k)), "wc_plan_format")
+        return v.value, k.value
 
     def stats(self) -> dict:
         cb, sb, ng = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
@@ -232,6 +268,12 @@ def decode_async(plan: Plan, blob_dev, out_dev, stream=None) -> None:
         stream = stream.cuda_stream
     _check(_lib.wc_decode_async(plan.handle, ctypes.c_void_p(_ptr(blob_dev)), ctypes.c_void_p(_ptr(out_dev)),
                                 ctypes.c_void_p(int(stream))), "wc_decode_async")
+
+
+def decode_u8_async(plan: Plan, blob_dev, out_dev, stream=None) -> None:
+    """wc_decode_u8_async: one launch decoding a u8-kind container into out_dev (n bytes)."""
+    _check(_lib.wc_decode_u8_async(plan.handle, ctypes.c_void_p(_ptr(blob_dev)), ctypes.c_void_p(_ptr(out_dev)),
+                                   ctypes.c_void_p(_stream_handle(stream))), "wc_decode_u8_async")
 
 
 def _stream_handle(stream) -> int:

@@ -296,3 +296,42 @@ def test_plan_rejects_each_lanes_fault(wc, oracle_lib):
     # containers written by the oracle pass every check
     wl2 = make_workload("attn_4k_zeros", scale_rows=64)
     assert _plan_status(wc, oracle_lib.encode_lanes(wl2.bits, numels=wl2.numels)) in ok
+
+
+@pytest.mark.parametrize("name,A,M,B", [("int8_codes_8b", 128, 4096, 15872), ("int4_codes_8b", 128, 4096, 15872),
+                                        ("int8_codes_8b", 8, 512, 500), ("int4_codes_8b", 64, 1024, 4096)])
+def test_u8_encoder_matches_oracle_writer(wc, oracle_lib, name, A, M, B):
+    """The product's u8-kind writer is byte-identical to the oracle's."""
+    from lossless_entropy_coded_amd.synth import make_code_workload
+    wl = make_code_workload(name, scale_rows=24)
+    a = wc.encode_u8_host(wl.tensors(), group_align=A, group_max_elems=M, seg_max_bits=B)
+    b = oracle_lib.encode_lanes_u8(wl.codes, numels=wl.numels, group_align=A, group_max_elems=M, seg_max_bits=B)
+    assert np.array_equal(a, b)
+    assert np.array_equal(oracle_lib.decode_u8(a), wl.codes)
+    assert np.array_equal(wc.encode_u8_host(wl.tensors(), group_align=A, group_max_elems=M, seg_max_bits=B,
+                                            n_threads=3), a)
+
+
+def test_plan_checks_element_kind(wc):
+    c = (np.arange(5000) % 251).astype(np.uint8)
+    blob = wc.encode_u8_host([c])
+    s = sections(blob)
+    assert s["elem_kind"] == 1 and s["sm"].size == 0
+    ok = (wc.WC_OK, wc.WC_ERR_HIP)
+    assert _plan_status(wc, blob) in ok
+    bad = blob.copy()
+    bad[124] = 2
+    assert _plan_status(wc, bad) == wc.WC_ERR_BAD_MAGIC
+    chunked = wc.encode_host([np.arange(5000, dtype=np.uint16)], layout="chunks")
+    chunked[124] = 1                               # version 2 holds bf16 only
+    assert _plan_status(wc, chunked) == wc.WC_ERR_BAD_MAGIC
+    # code planes take the lanes layout only
+    with pytest.raises(wc.WCError) as ei:
+        opts = wc.EncodeOpts(24, 8, 0, 0, 128, 4096, wc.LAYOUTS["chunks"], 0)
+        import ctypes
+        arr = (wc._u8p * 1)(c.ctypes.data_as(wc._u8p))
+        num = (ctypes.c_uint64 * 1)(c.size)
+        out, nb = wc._u8p(), ctypes.c_uint64()
+        wc._check(wc._lib.wc_encode_u8_host(arr, num, 1, ctypes.byref(opts), ctypes.byref(out), ctypes.byref(nb)),
+                  "wc_encode_u8_host")
+    assert ei.value.status == wc.WC_ERR_INVALID_ARG
