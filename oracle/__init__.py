@@ -54,7 +54,7 @@ class Report(ctypes.Structure):
         ("layout", ctypes.c_uint32),
         ("seg_max_bits", ctypes.c_uint32),
         ("elem_kind", ctypes.c_uint32),
-        ("reserved2", ctypes.c_uint32),
+        ("coder", ctypes.c_uint32),
     ]
 
     def as_dict(self):
@@ -100,6 +100,10 @@ def lib():
                                        ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(u8p), u64p]
         L.orc_encode_lanes_u8.argtypes = [u8p, ctypes.c_uint64, u64p, ctypes.c_uint32, ctypes.c_uint32,
                                           ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(u8p), u64p]
+        L.orc_encode_lanes_rans.argtypes = [u16p, ctypes.c_uint64, u64p, ctypes.c_uint32, ctypes.c_uint32,
+                                            ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(u8p), u64p]
+        L.orc_encode_lanes_rans_u8.argtypes = [u8p, ctypes.c_uint64, u64p, ctypes.c_uint32, ctypes.c_uint32,
+                                               ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(u8p), u64p]
         L.orc_decode_u8.argtypes = [u8p, ctypes.c_uint64, u8p, ctypes.c_uint64, ctypes.POINTER(Report)]
         L.orc_decode.argtypes = [u8p, ctypes.c_uint64, u16p, ctypes.c_uint64, ctypes.POINTER(Report)]
         L.orc_header.argtypes = [u8p, ctypes.c_uint64, ctypes.POINTER(Report)]
@@ -244,6 +248,40 @@ def encode_lanes_u8(codes: np.ndarray, numels=None, max_code_len: int = 24, grou
     finally:
         lib().orc_free(out)
     return blob
+
+
+def _encode_call(fn, data, ct, numels, *params):
+    data = np.ascontiguousarray(data).reshape(-1)
+    if numels is None:
+        nump, nt = None, 1
+    else:
+        arr = np.ascontiguousarray(numels, dtype=np.uint64)
+        nump, nt = _p(arr, ctypes.c_uint64), arr.size
+    out = ctypes.POINTER(ctypes.c_uint8)()
+    nbytes = ctypes.c_uint64(0)
+    st = fn(_p(data, ct), data.size, nump, nt, *[int(v) for v in params], ctypes.byref(out), ctypes.byref(nbytes))
+    if st:
+        raise OracleError(st, fn.__name__)
+    try:
+        blob = np.ctypeslib.as_array(out, shape=(nbytes.value,)).copy() if nbytes.value else np.zeros(0, np.uint8)
+    finally:
+        lib().orc_free(out)
+    return blob
+
+
+def encode_lanes_rans(w: np.ndarray, numels=None, group_align: int = 128, group_max_elems: int = 4096,
+                      seg_max_bits: int = 15872) -> np.ndarray:
+    """Oracle's writer of an rANS lane container (coder 1) over bf16 words:
+    12-bit frequencies, one rANS stream per lane."""
+    return _encode_call(lib().orc_encode_lanes_rans, np.asarray(w, dtype=np.uint16), ctypes.c_uint16, numels,
+                        group_align, group_max_elems, seg_max_bits)
+
+
+def encode_lanes_rans_u8(codes: np.ndarray, numels=None, group_align: int = 128, group_max_elems: int = 4096,
+                         seg_max_bits: int = 15872) -> np.ndarray:
+    """The same over a plane of 8-bit codes (element kind u8)."""
+    return _encode_call(lib().orc_encode_lanes_rans_u8, np.asarray(codes, dtype=np.uint8), ctypes.c_uint8, numels,
+                        group_align, group_max_elems, seg_max_bits)
 
 
 def decode_u8(blob: np.ndarray, with_report: bool = False):

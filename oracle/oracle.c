@@ -55,7 +55,14 @@
  *    quantized weights (the LazyWeights page, analogy: Huffman codes for the
  *    integer codes of a quantized model), every byte is one symbol of the
  *    same canonical code, in the same lane layout, with no raw plane; the
- *    decode gives back the bytes.
+ *    decode gives back the bytes;
+ *  - rANS in the lane layout (version 3, coder 1): the Llama2-7B page names
+ *    ANS as the hardware coder; the LazyWeights page compares a Huffman and
+ *    an rANS decoder.  Here each lane is one rANS stream: symbol frequencies
+ *    quantized to sum to 2^12 replace the code lengths, a segment is cut by
+ *    an upper bound of its encoded size (each symbol grows the state by at
+ *    most 12 - log2 f + log2(1 + 2^-4) bits, so ceil(8 (12 - log2 f)) + 1
+ *    eighths of a bit bound it; each lane adds 32 bits for its final state).
  */
 #include "oracle.h"
 
@@ -94,7 +101,17 @@
 #define F_TOTAL        112   /* u64: whole container size                   */
 #define F_MAXG         120   /* u32 elements per group at most M            */
 #define F_KIND         124   /* u8 element kind (version 3): 0 bf16, 1 u8   */
-#define F_TAIL         125   /* zero from here to the end of the header     */
+#define F_CODER        125   /* u8 coder (version 3): 0 Huffman, 1 rANS     */
+#define F_TAIL         126   /* zero from here to the end of the header     */
+#define CODER_HUFFMAN    0
+#define CODER_RANS       1
+/* rANS [L2-7B abstract: ANS]: 12-bit frequencies, a 32-bit state kept in
+ * [2^16, 2^32), 16-bit renormalisation words; a lane's string is its final
+ * state (two words, high first) and then the words its decoder reads, each
+ * big-endian; a lane with no symbols has an empty string. */
+#define RANS_P          12u
+#define RANS_L     65536ull
+#define RANS_FLUSH      32u
 #define KIND_BF16        0   /* exponent coded, sign+mantissa plane raw     */
 #define KIND_U8          1   /* the whole byte coded, no raw plane          */
 
@@ -608,11 +625,247 @@ int orc_encode_lanes_u8(const uint8_t* codes, uint64_t n, const uint64_t* numels
 }
 
 /* ------------------------------------------------------------------------ */
+/* rANS in the lane layout [L2-7B abstract: ANS; LW: Huffman vs rANS]       */
+/* ------------------------------------------------------------------------ */
+/* Frequencies summing to 2^P: f = max(1, floor(count * 2^P / n)) for present
+ * symbols, then while the sum is too large take 1 from the largest f (> 1;
+ * ties: smallest symbol), while too small give 1 to the most frequent symbol
+ * (ties: smallest symbol). */
+static void rans_freqs(const uint64_t hist[256], uint64_t n, uint32_t f[256]) {
+    uint64_t sum = 0;
+    int top = -1;
+    for (int s = 0; s < 256; ++s) {
+        f[s] = 0;
+        if (!hist[s]) continue;
+        uint64_t v = hist[s] * ((uint64_t)1 << RANS_P) / n;
+        f[s] = (uint32_t)(v ? v : 1);
+        sum += f[s];
+        if (top < 0 || hist[s] > hist[top]) top = s;
+    }
+    if (top < 0) return;
+    while (sum > ((uint64_t)1 << RANS_P)) {
+        int b = -1;
+        for (int s = 0; s < 256; ++s)
+            if (f[s] > 1 && (b < 0 || f[s] > f[b])) b = s;
+        f[b]--;
+        sum--;
+    }
+    while (sum < ((uint64_t)1 << RANS_P)) { f[top]++; sum++; }
+}
+
+/* Upper bound, in eighths of a bit, of what one symbol of frequency f adds to
+ * a lane's string: encoding x < 2^20 f gives x' < (x / f + 1) 2^P, so log2 x
+ * grows by less than P - log2 f + log2(1 + f / x) <= P - log2 f + 0.0875
+ * (x >= 2^16, f <= 2^12); the bound is ceil(8 (P - log2 f)) + 1, with the
+ * ceiling q the least q such that f^8 2^q >= 2^(8P), exact in integers. */
+static uint32_t rans_cost8(uint32_t f) {
+    unsigned __int128 f8 = 1;
+    for (int i = 0; i < 8; ++i) f8 *= f;
+    uint32_t q = 0;
+    while ((f8 << q) < ((unsigned __int128)1 << (8 * RANS_P))) ++q;
+    return q + 1;
+}
+
+/* Segments for rANS: runs of whole A-blocks, at most M elements, whose bound
+ * 64 * 32 bits + (sum of rans_cost8 over their elements) / 8 is at most B.
+ * cost_before[k] = sum of rans_cost8 over the elements before block k. */
+static uint64_t rans_segments(const uint64_t* cost_before, uint64_t nb, uint64_t n, uint32_t A, uint32_t B,
+                              uint32_t M, uint64_t* elem) {
+    uint64_t g = 0, k = 0;
+    elem[0] = 0;
+    while (k < nb) {
+        uint64_t first = k;
+        ++k;
+        while (k < nb && (k + 1 - first) * (uint64_t)A <= M &&
+               8ull * LANES * RANS_FLUSH + cost_before[k + 1] - cost_before[first] <= 8ull * B)
+            ++k;
+        ++g;
+        elem[g] = k * (uint64_t)A < n ? k * (uint64_t)A : n;
+    }
+    return g;
+}
+
+/* Encode one lane's symbols sym[0..k) (k > 0) into big-endian 16-bit words at
+ * out (capacity known sufficient); returns the number of words. */
+static uint64_t rans_encode_lane(const uint8_t* sym, uint64_t k, const uint32_t f[256], const uint32_t cum[256],
+                                 uint16_t* scratch, uint16_t* out) {
+    uint64_t x = RANS_L, nw = 0;
+    for (uint64_t t = k; t-- > 0;) {          /* last symbol first */
+        uint32_t s = sym[t];
+        uint64_t xmax = ((RANS_L >> RANS_P) << 16) * f[s];
+        while (x >= xmax) { scratch[nw++] = (uint16_t)(x & 0xFFFF); x >>= 16; }
+        x = (x / f[s] << RANS_P) + x % f[s] + cum[s];
+    }
+    out[0] = (uint16_t)(x >> 16);
+    out[1] = (uint16_t)(x & 0xFFFF);
+    for (uint64_t i = 0; i < nw; ++i) out[2 + i] = scratch[nw - 1 - i];   /* in the order the decoder reads */
+    return nw + 2;
+}
+
+static int encode_rans_planes(uint8_t* e, uint8_t* sm, uint32_t kind, uint64_t n, const uint64_t* numels,
+                              uint32_t n_tensors, uint32_t A, uint32_t M, uint32_t B, uint8_t** blob,
+                              uint64_t* blob_bytes) {
+    uint64_t hist[256] = {0};
+    for (uint64_t i = 0; i < n; ++i) hist[e[i]]++;
+    uint32_t f[256], cum[256], acc = 0;
+    rans_freqs(hist, n, f);
+    for (int s = 0; s < 256; ++s) { cum[s] = acc; acc += f[s]; }
+    uint64_t nb = ceil_div(n, A);
+    uint64_t* cost_before = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+    uint64_t* s_elem = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+    /* worst case: 2 words per symbol plus 2 per lane */
+    uint16_t* scratch = (uint16_t*)malloc((size_t)(2 * M + 8) * sizeof(uint16_t));
+    uint16_t* words = (uint16_t*)malloc((size_t)(2 * M + 2 * LANES + 8) * sizeof(uint16_t));
+    uint8_t* lane_sym = (uint8_t*)malloc((size_t)M + 8);
+    if (!cost_before || !s_elem || !scratch || !words || !lane_sym) {
+        free(cost_before); free(s_elem); free(scratch); free(words); free(lane_sym); free(e); free(sm);
+        return ORC_E_NOMEM;
+    }
+    {
+        uint64_t at = 0;
+        for (uint64_t i = 0; i < n; ++i) {
+            if (i % A == 0) cost_before[i / A] = at;
+            at += rans_cost8(f[e[i]]);
+        }
+        cost_before[nb] = at;
+    }
+    uint64_t n_segs = rans_segments(cost_before, nb, n, A, B, M, s_elem);
+    free(cost_before);
+    /* the stream is at most the bound of every segment */
+    uint64_t cap_bits = (uint64_t)LANES * RANS_FLUSH * n_segs;
+    for (uint64_t i = 0; i < n; ++i) cap_bits += rans_cost8(f[e[i]]);   /* eighths: a generous cap */
+    uint8_t* tmp = (uint8_t*)calloc(ceil_div(cap_bits, 8) + 8, 1);
+    uint16_t* loff = (uint16_t*)malloc((size_t)(LANES * n_segs + 1) * sizeof(uint16_t));
+    uint64_t* s_bit = (uint64_t*)malloc((size_t)(n_segs + 1) * sizeof(uint64_t));
+    if (!tmp || !loff || !s_bit) {
+        free(tmp); free(loff); free(s_bit); free(s_elem); free(scratch); free(words); free(lane_sym); free(e); free(sm);
+        return ORC_E_NOMEM;
+    }
+    uint64_t pos = 0;   /* bits, always a multiple of 16 */
+    for (uint64_t g = 0; g < n_segs; ++g) {
+        s_bit[g] = pos;
+        uint64_t e0 = s_elem[g], m = s_elem[g + 1] - e0;
+        for (uint32_t j = 0; j < LANES; ++j) {
+            loff[LANES * g + j] = (uint16_t)(pos - s_bit[g]);
+            uint64_t k = 0;
+            for (uint64_t t = 0;; ++t) {
+                uint64_t i = lane_elem(m, j, t);
+                if (i >= m) break;
+                lane_sym[k++] = e[e0 + i];
+            }
+            if (!k) continue;
+            uint64_t nw = rans_encode_lane(lane_sym, k, f, cum, scratch, words);
+            for (uint64_t w = 0; w < nw; ++w) {
+                tmp[pos >> 3] = (uint8_t)(words[w] >> 8);
+                tmp[(pos >> 3) + 1] = (uint8_t)(words[w] & 0xFF);
+                pos += 16;
+            }
+        }
+    }
+    s_bit[n_segs] = pos;
+    free(scratch); free(words); free(lane_sym);
+    uint64_t bits = pos;
+    uint64_t stream_bytes = round_up(ceil_div(bits, 8), 8) + LANES_SLACK;
+    uint64_t off_len = HDR_BYTES;
+    uint64_t off_tens = round_up(off_len + 512, ALIGN);
+    uint64_t off_segs = round_up(off_tens + 16ull * n_tensors, ALIGN);
+    uint64_t off_loff = round_up(off_segs + 16 * (n_segs + 1), ALIGN);
+    uint64_t off_stream = round_up(off_loff + 2ull * LANES * n_segs, ALIGN);
+    uint64_t off_sm = round_up(off_stream + stream_bytes, ALIGN);
+    uint64_t sm_bytes = kind == KIND_BF16 ? n : 0;
+    uint64_t total = round_up(off_sm + sm_bytes, ALIGN);
+    uint8_t* b = (uint8_t*)calloc(total, 1);
+    if (!b) { free(tmp); free(loff); free(s_bit); free(s_elem); free(e); free(sm); return ORC_E_NOMEM; }
+    for (int s2 = 0; s2 < 256; ++s2) wr(b + off_len + 2 * s2, f[s2], 2);
+    uint64_t at = 0;
+    for (uint32_t t = 0; t < n_tensors; ++t) {
+        wr(b + off_tens + 16ull * t, at, 8);
+        wr(b + off_tens + 16ull * t + 8, numels[t], 8);
+        at += numels[t];
+    }
+    for (uint64_t g = 0; g <= n_segs; ++g) {
+        wr(b + off_segs + 16 * g, s_elem[g], 8);
+        wr(b + off_segs + 16 * g + 8, s_bit[g], 8);
+    }
+    for (uint64_t i = 0; i < LANES * n_segs; ++i) wr(b + off_loff + 2 * i, loff[i], 2);
+    memcpy(b + off_stream, tmp, ceil_div(bits, 8));
+    if (sm_bytes) memcpy(b + off_sm, sm, sm_bytes);
+    free(tmp); free(loff); free(s_bit); free(s_elem);
+
+    memcpy(b + F_MAGIC, "WCBF", 4);
+    wr(b + F_VERSION, 3, 2);
+    wr(b + F_FLAGS, 0, 2);
+    wr(b + F_MAXLEN, RANS_P, 1);
+    wr(b + F_LANES, LANES, 1);
+    wr(b + F_LANE_BLOCK, LANE_BLOCK, 2);
+    wr(b + F_SEGBITS, B, 4);
+    wr(b + F_NTENS, n_tensors, 4);
+    wr(b + F_ALIGN, A, 4);
+    wr(b + F_MAXG, M, 4);
+    wr(b + F_N, n, 8);
+    wr(b + F_SBITS, bits, 8);
+    wr(b + F_NGROUPS, n_segs, 8);
+    wr(b + F_OFF_LEN, off_len, 8);
+    wr(b + F_OFF_TENS, off_tens, 8);
+    wr(b + F_OFF_GS, off_segs, 8);
+    wr(b + F_OFF_LOFF, off_loff, 8);
+    wr(b + F_OFF_STREAM, off_stream, 8);
+    wr(b + F_STREAM_BYTES, stream_bytes, 8);
+    wr(b + F_OFF_SM, off_sm, 8);
+    wr(b + F_TOTAL, total, 8);
+    wr(b + F_KIND, kind, 1);
+    wr(b + F_CODER, CODER_RANS, 1);
+    free(e);
+    free(sm);
+    *blob = b;
+    *blob_bytes = total;
+    return ORC_OK;
+}
+
+static int rans_args(uint64_t n, const void* src, const uint64_t** numels, uint32_t* n_tensors, uint64_t* one,
+                     uint32_t A, uint32_t M, uint32_t B, uint8_t** blob, uint64_t* blob_bytes) {
+    if (!blob || !blob_bytes || (n && !src)) return ORC_E_ARG;
+    /* one block always fits: A symbols of frequency 1 cost 97 eighths each */
+    if (A < 1 || M < A || M % A || M > LANES * LANE_BLOCK * 1024u || B > 65535u || B < LANES * RANS_FLUSH ||
+        97ull * A > 8ull * (B - LANES * RANS_FLUSH))
+        return ORC_E_ARG;
+    *one = n;
+    if (!*numels) { *numels = one; *n_tensors = 1; }
+    uint64_t sum = 0;
+    for (uint32_t t = 0; t < *n_tensors; ++t) sum += (*numels)[t];
+    return sum == n ? ORC_OK : ORC_E_ARG;
+}
+
+int orc_encode_lanes_rans(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n_tensors, uint32_t A,
+                          uint32_t M, uint32_t B, uint8_t** blob, uint64_t* blob_bytes) {
+    uint64_t one;
+    int st = rans_args(n, w, &numels, &n_tensors, &one, A, M, B, blob, blob_bytes);
+    if (st != ORC_OK) return st;
+    uint8_t* e = (uint8_t*)malloc(n ? n : 1);
+    uint8_t* sm = (uint8_t*)malloc(n ? n : 1);
+    if (!e || !sm) { free(e); free(sm); return ORC_E_NOMEM; }
+    orc_split_planes(w, n, e, sm);
+    return encode_rans_planes(e, sm, KIND_BF16, n, numels, n_tensors, A, M, B, blob, blob_bytes);
+}
+
+int orc_encode_lanes_rans_u8(const uint8_t* codes, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
+                             uint32_t A, uint32_t M, uint32_t B, uint8_t** blob, uint64_t* blob_bytes) {
+    uint64_t one;
+    int st = rans_args(n, codes, &numels, &n_tensors, &one, A, M, B, blob, blob_bytes);
+    if (st != ORC_OK) return st;
+    uint8_t* e = (uint8_t*)malloc(n ? n : 1);
+    if (!e) return ORC_E_NOMEM;
+    if (n) memcpy(e, codes, n);
+    return encode_rans_planes(e, NULL, KIND_U8, n, numels, n_tensors, A, M, B, blob, blob_bytes);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Reader                                                                   */
 /* ------------------------------------------------------------------------ */
 typedef struct {
     uint32_t version;   /* 2: per-chunk gaps; 3: interleaved lanes */
     uint32_t kind;      /* KIND_BF16 or (version 3) KIND_U8 */
+    uint32_t coder;     /* CODER_HUFFMAN or (version 3) CODER_RANS */
     uint32_t max_len, G, A, M, B, n_tensors;
     uint64_t n, stream_bits, n_chunks, n_groups;
     uint64_t off_len, off_tens, off_gs, off_gap, off_stream, stream_bytes, off_sm, total;
@@ -626,8 +879,9 @@ static int parse_header(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
     if (rd(blob + F_VERSION, 2) == 3) return parse_header_lanes(blob, bytes, h);
     h->version = 2;
     h->kind = KIND_BF16;
+    h->coder = CODER_HUFFMAN;
     h->B = 0;
-    if (blob[F_KIND]) return ORC_E_MAGIC;
+    if (blob[F_KIND] || blob[F_CODER]) return ORC_E_MAGIC;
     if (rd(blob + F_VERSION, 2) != 2 || rd(blob + F_FLAGS, 2) != 0) return ORC_E_MAGIC;
     if (rd(blob + F_CHUNKBITS, 1) != CHUNK_BITS) return ORC_E_MAGIC;
     if (rd(blob + F_RES0, 2) != 0) return ORC_E_MAGIC;
@@ -673,7 +927,9 @@ static int parse_header(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
 static int parse_header_lanes(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
     h->version = 3;
     h->kind = blob[F_KIND];
+    h->coder = blob[F_CODER];
     if (h->kind != KIND_BF16 && h->kind != KIND_U8) return ORC_E_MAGIC;
+    if (h->coder != CODER_HUFFMAN && h->coder != CODER_RANS) return ORC_E_MAGIC;
     if (rd(blob + F_FLAGS, 2) != 0 || rd(blob + F_LANES, 1) != LANES || rd(blob + F_LANE_BLOCK, 2) != LANE_BLOCK)
         return ORC_E_MAGIC;
     for (uint32_t k = F_TAIL; k < HDR_BYTES; ++k) if (blob[k]) return ORC_E_MAGIC;
@@ -696,16 +952,24 @@ static int parse_header_lanes(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
     h->stream_bytes = rd(blob + F_STREAM_BYTES, 8);
     h->off_sm = rd(blob + F_OFF_SM, 8);
     h->total = rd(blob + F_TOTAL, 8);
-    if (h->max_len < 1 || h->max_len > MAX_LEN_LIMIT || h->A < 1 || h->M < h->A || h->M % h->A ||
-        h->B > 65535u || (uint64_t)h->A * h->max_len > h->B)
+    if (h->A < 1 || h->M < h->A || h->M % h->A || h->B > 65535u) return ORC_E_MAGIC;
+    if (h->coder == CODER_HUFFMAN &&
+        (h->max_len < 1 || h->max_len > MAX_LEN_LIMIT || (uint64_t)h->A * h->max_len > h->B))
+        return ORC_E_MAGIC;
+    if (h->coder == CODER_RANS && (h->max_len != RANS_P || h->B < LANES * RANS_FLUSH ||
+                                   97ull * h->A > 8ull * (h->B - LANES * RANS_FLUSH)))
         return ORC_E_MAGIC;
     if (h->n > ((uint64_t)1 << 48) || h->stream_bits > ((uint64_t)1 << 56)) return ORC_E_SIZES;
     if (h->n_groups > h->n || (h->n_groups == 0) != (h->n == 0)) return ORC_E_SIZES;
     if (h->stream_bytes != round_up(ceil_div(h->stream_bits, 8), 8) + LANES_SLACK) return ORC_E_SIZES;
-    if (h->stream_bits > h->n * (uint64_t)h->max_len || h->stream_bits < h->n) return ORC_E_SIZES;
+    if (h->coder == CODER_HUFFMAN && (h->stream_bits > h->n * (uint64_t)h->max_len || h->stream_bits < h->n))
+        return ORC_E_SIZES;
+    if (h->coder == CODER_RANS && (h->stream_bits % 16 || h->stream_bits > h->n * (uint64_t)(RANS_P + 1) +
+                                                                           (uint64_t)LANES * RANS_FLUSH * h->n_groups))
+        return ORC_E_SIZES;
     const uint64_t offs[6] = {h->off_len, h->off_tens, h->off_gs, h->off_gap, h->off_stream, h->off_sm};
-    const uint64_t lens[6] = {256, 16ull * h->n_tensors, 16 * (h->n_groups + 1), 2ull * LANES * h->n_groups,
-                              h->stream_bytes, h->kind == KIND_BF16 ? h->n : 0};
+    const uint64_t lens[6] = {h->coder == CODER_RANS ? 512u : 256u, 16ull * h->n_tensors, 16 * (h->n_groups + 1),
+                              2ull * LANES * h->n_groups, h->stream_bytes, h->kind == KIND_BF16 ? h->n : 0};
     uint64_t lo = HDR_BYTES;
     for (int k = 0; k < 6; ++k) {
         if (offs[k] % ALIGN || offs[k] < lo) return ORC_E_TRUNC;
@@ -733,6 +997,7 @@ int orc_header(const uint8_t* blob, uint64_t blob_bytes, orc_report* rep) {
         rep->layout = h.version == 3 ? 1u : 0u;
         rep->seg_max_bits = h.B;
         rep->elem_kind = h.kind;
+        rep->coder = h.coder;
     }
     return ORC_OK;
 }
@@ -884,6 +1149,91 @@ static int decode_lanes(const uint8_t* blob, const hdr_t* h, const trie_node* T,
     return st;
 }
 
+/* rANS lanes: for every stored segment and lane, check the lane's stored
+ * offset, read its final state (two words) and decode its symbols with the
+ * frequency table (slot = x mod 2^P, the symbol whose cumulative range holds
+ * it, x = f (x >> P) + slot - cum, one more word when x < 2^16); each lane must
+ * end in the encoder's initial state 2^16 exactly where the next lane begins.
+ * Then re-derive the segment table from the frequency bound. */
+static int decode_lanes_rans(const uint8_t* blob, const hdr_t* h, const uint32_t f[256], uint16_t* out,
+                             uint8_t* out8, uint64_t hist[256]) {
+    const uint8_t* stream = blob + h->off_stream;
+    const uint8_t* segs = blob + h->off_gs;
+    const uint8_t* loff = blob + h->off_gap;
+    const uint8_t* sm = blob + h->off_sm;
+    uint32_t cum[257];
+    cum[0] = 0;
+    for (int s = 0; s < 256; ++s) cum[s + 1] = cum[s] + f[s];
+    uint8_t* e = (uint8_t*)malloc(h->n ? h->n : 1);
+    if (!e) return ORC_E_NOMEM;
+    int st = ORC_OK;
+    uint64_t pos = 0;
+    if (rd(segs, 8) != 0 || rd(segs + 8, 8) != 0) st = ORC_E_GROUP;
+    for (uint64_t g = 0; g < h->n_groups && st == ORC_OK; ++g) {
+        uint64_t e0 = rd(segs + 16 * g, 8), p0 = rd(segs + 16 * g + 8, 8);
+        uint64_t e1 = rd(segs + 16 * (g + 1), 8), p1 = rd(segs + 16 * (g + 1) + 8, 8);
+        if (e1 <= e0 || e1 > h->n || p0 != pos || p1 < p0 || p1 > h->stream_bits) { st = ORC_E_GROUP; break; }
+        uint64_t m = e1 - e0;
+        for (uint32_t j = 0; j < LANES && st == ORC_OK; ++j) {
+            if (rd(loff + 2 * (LANES * g + j), 2) != pos - p0) { st = ORC_E_GROUP; break; }
+            if (lane_elem(m, j, 0) >= m) continue;          /* an empty lane has an empty string */
+            if (pos + 32 > p1) { st = ORC_E_STREAM; break; }
+            uint64_t x = ((uint64_t)stream[pos >> 3] << 24) | ((uint64_t)stream[(pos >> 3) + 1] << 16) |
+                         ((uint64_t)stream[(pos >> 3) + 2] << 8) | stream[(pos >> 3) + 3];
+            pos += 32;
+            for (uint64_t t = 0;; ++t) {
+                uint64_t i = lane_elem(m, j, t);
+                if (i >= m) break;
+                uint32_t slot = (uint32_t)(x & (((uint64_t)1 << RANS_P) - 1));
+                uint32_t s = 0;
+                while (cum[s + 1] <= slot) ++s;
+                e[e0 + i] = (uint8_t)s;
+                x = f[s] * (x >> RANS_P) + slot - cum[s];
+                if (x < RANS_L) {
+                    if (pos + 16 > p1) { st = ORC_E_STREAM; break; }
+                    x = (x << 16) | ((uint64_t)stream[pos >> 3] << 8) | stream[(pos >> 3) + 1];
+                    pos += 16;
+                }
+            }
+            if (st == ORC_OK && x != RANS_L) st = ORC_E_STREAM;
+        }
+        if (st == ORC_OK && pos != p1) st = ORC_E_STREAM;
+    }
+    if (st == ORC_OK && (rd(segs + 16 * h->n_groups, 8) != h->n ||
+                         rd(segs + 16 * h->n_groups + 8, 8) != h->stream_bits || pos != h->stream_bits))
+        st = ORC_E_STREAM;
+    if (st == ORC_OK) {
+        uint64_t nb = ceil_div(h->n, h->A);
+        uint64_t* cost_before = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+        uint64_t* s_elem = (uint64_t*)malloc((size_t)(nb + 1) * sizeof(uint64_t));
+        if (!cost_before || !s_elem) st = ORC_E_NOMEM;
+        if (st == ORC_OK) {
+            uint64_t at = 0;
+            for (uint64_t i = 0; i < h->n; ++i) {
+                if (i % h->A == 0) cost_before[i / h->A] = at;
+                at += rans_cost8(f[e[i]]);
+            }
+            cost_before[nb] = at;
+            uint64_t ns = rans_segments(cost_before, nb, h->n, h->A, h->B, h->M, s_elem);
+            if (ns != h->n_groups) st = ORC_E_GROUP;
+            for (uint64_t g = 0; st == ORC_OK && g <= ns; ++g)
+                if (rd(segs + 16 * g, 8) != s_elem[g]) st = ORC_E_GROUP;
+        }
+        free(cost_before); free(s_elem);
+    }
+    for (uint64_t i = 0; st == ORC_OK && i < h->n; ++i) {
+        hist[e[i]]++;
+        if (h->kind == KIND_U8) {
+            out8[i] = e[i];
+        } else {
+            uint16_t s = sm[i];
+            out[i] = (uint16_t)(((s & 0x80) << 8) | ((uint16_t)e[i] << 7) | (s & 0x7F));
+        }
+    }
+    free(e);
+    return st;
+}
+
 static int decode_container(const uint8_t* blob, uint64_t bytes, uint32_t kind, uint16_t* out, uint8_t* out8,
                             uint64_t out_cap, orc_report* rep) {
     hdr_t h;
@@ -904,10 +1254,26 @@ static int decode_container(const uint8_t* blob, uint64_t bytes, uint32_t kind, 
         if (acc != h.n) return ORC_E_TENSORS;
     }
 
-    /* code lengths and Kraft's sum, exactly, in units of 2^-24 */
-    const uint8_t* lens = blob + h.off_len;
-    uint64_t kraft = 0;
+    uint64_t hist[256] = {0};
     uint32_t m = 0, longest = 0;
+    uint64_t kraft = 0;
+    const uint8_t* lens = blob + h.off_len;
+    if (h.coder == CODER_RANS) {
+        /* frequencies: at most 2^P each, summing to 2^P (or all 0 for n = 0) */
+        uint32_t f[256];
+        uint64_t sum = 0;
+        for (int s = 0; s < 256; ++s) {
+            f[s] = (uint32_t)rd(lens + 2 * s, 2);
+            if (f[s] > (1u << RANS_P)) return ORC_E_LENGTHS;
+            sum += f[s];
+            m += f[s] != 0;
+        }
+        if (h.n ? sum != (1u << RANS_P) : sum != 0) return ORC_E_KRAFT;
+        st = decode_lanes_rans(blob, &h, f, out, out8, hist);
+        if (st != ORC_OK) return st;
+        goto padding;
+    }
+    /* code lengths and Kraft's sum, exactly, in units of 2^-24 */
     for (int s = 0; s < 256; ++s) {
         if (!lens[s]) continue;
         if (lens[s] > h.max_len) return ORC_E_LENGTHS;
@@ -956,7 +1322,6 @@ static int decode_container(const uint8_t* blob, uint64_t bytes, uint32_t kind, 
         }
     }
     if (st != ORC_OK) { free(T); return st; }
-    uint64_t hist[256] = {0};
     if (h.version == 3)
         st = decode_lanes(blob, &h, T, lens, out, out8, hist);
     else
@@ -964,6 +1329,7 @@ static int decode_container(const uint8_t* blob, uint64_t bytes, uint32_t kind, 
     free(T);
     if (st != ORC_OK) return st;
 
+padding:;
     /* every bit after stream_bits, up to the end of the section, is zero */
     const uint8_t* stream = blob + h.off_stream;
     for (uint64_t p = h.stream_bits; p < 8 * h.stream_bytes; ++p) {
@@ -989,6 +1355,7 @@ static int decode_container(const uint8_t* blob, uint64_t bytes, uint32_t kind, 
         rep->layout = h.version == 3 ? 1u : 0u;
         rep->seg_max_bits = h.B;
         rep->elem_kind = h.kind;
+        rep->coder = h.coder;
         rep->n_symbols = m;
         rep->longest_code = longest;
         rep->kraft_num = kraft;
@@ -998,8 +1365,9 @@ static int decode_container(const uint8_t* blob, uint64_t bytes, uint32_t kind, 
             if (!hist[s]) continue;
             double p = (double)hist[s] / (double)h.n;
             H -= p * log2(p);
-            Lsum += (double)hist[s] * (double)lens[s];
+            if (h.coder == CODER_HUFFMAN) Lsum += (double)hist[s] * (double)lens[s];
         }
+        if (h.coder == CODER_RANS) Lsum = (double)h.stream_bits;   /* every stored bit, final states included */
         rep->entropy_bits = H;
         rep->mean_code_bits = h.n ? Lsum / (double)h.n : 0.0;
     }

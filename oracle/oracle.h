@@ -71,7 +71,7 @@ typedef struct {
     uint32_t layout;           /* 0: per-chunk gaps (version 2); 1: lanes (3) */
     uint32_t seg_max_bits;     /* lanes layout: stream bits per segment max  */
     uint32_t elem_kind;        /* 0: bf16 (exponent coded); 1: u8 symbols    */
-    uint32_t reserved2;
+    uint32_t coder;            /* 0: canonical Huffman; 1: rANS              */
 } orc_report;
 
 /* Split bf16 words into exponent and sign+mantissa planes (definition). */
@@ -116,6 +116,18 @@ int orc_encode_lanes(const uint16_t* w, uint64_t n, const uint64_t* numels, uint
 int orc_encode_lanes_u8(const uint8_t* codes, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
                         uint32_t max_code_len, uint32_t group_align, uint32_t group_max_elems,
                         uint32_t seg_max_bits, uint8_t** blob, uint64_t* blob_bytes);
+
+/* rANS in the same lane layout (coder 1): frequencies quantized to sum to
+ * 2^12 replace the code lengths (u16[256] in their section); each lane is one
+ * rANS stream (32-bit state in [2^16, 2^32), 16-bit renormalisation words);
+ * segments are cut by an upper bound of their encoded size; seg_max_bits must
+ * leave room for 64 final states and one block.  The _u8 form codes bytes. */
+int orc_encode_lanes_rans(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
+                          uint32_t group_align, uint32_t group_max_elems, uint32_t seg_max_bits, uint8_t** blob,
+                          uint64_t* blob_bytes);
+int orc_encode_lanes_rans_u8(const uint8_t* codes, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
+                             uint32_t group_align, uint32_t group_max_elems, uint32_t seg_max_bits,
+                             uint8_t** blob, uint64_t* blob_bytes);
 
 /* Serial decoder of a u8-kind container into n bytes (out_cap >= n). */
 int orc_decode_u8(const uint8_t* blob, uint64_t blob_bytes, uint8_t* out, uint64_t out_cap, orc_report* rep);

@@ -28,6 +28,7 @@ def header(blob: np.ndarray) -> dict:
     h["magic"] = raw[:4]
     h["version"] = struct.unpack_from("<H", raw, 4)[0]
     h["elem_kind"] = raw[124]
+    h["coder"] = raw[125]
     if h["version"] == 3:
         h["lanes"] = raw[9]
         h["lane_block"] = struct.unpack_from("<H", raw, 10)[0]
@@ -39,7 +40,10 @@ def sections(blob: np.ndarray) -> dict:
     h = header(blob)
     n, nc, ng, nt = h["n_elems"], h["n_chunks"], h["n_groups"], h["n_tensors"]
     s = dict(h)
-    s["code_len"] = blob[h["off_len"]:h["off_len"] + 256]
+    if h["coder"] == 1:      # rANS: u16 frequencies in the code-length section
+        s["freq"] = blob[h["off_len"]:h["off_len"] + 512].view(np.uint16)
+    else:
+        s["code_len"] = blob[h["off_len"]:h["off_len"] + 256]
     s["tensors"] = blob[h["off_tens"]:h["off_tens"] + 16 * nt].view(np.uint64).reshape(nt, 2)
     s["groups"] = blob[h["off_gs"]:h["off_gs"] + 16 * (ng + 1)].view(np.uint64).reshape(ng + 1, 2)
     if h["version"] == 3:
