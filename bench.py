@@ -41,8 +41,14 @@ METRIC_CODES = "decompressed 8-bit code GB/s and % of HBM roofline (1 MI355X), b
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "lossless_entropy_coded_amd", "csrc")
 KERNEL_SOURCES = {"chunks": os.path.join(CSRC, "decode.hip"), "lanes": os.path.join(CSRC, "decode_lanes.hip")}
+# counter records per kernel variant: layout, and the coder when not Huffman
 TRAFFIC_FILES = {"chunks": os.path.join(ROOT, "profiles", "decode_chunks_block_8b_traffic.json"),
-                 "lanes": os.path.join(ROOT, "profiles", "decode_lanes_block_8b_traffic.json")}
+                 "lanes": os.path.join(ROOT, "profiles", "decode_lanes_block_8b_traffic.json"),
+                 "lanes_rans": os.path.join(ROOT, "profiles", "decode_lanes_rans_block_8b_traffic.json")}
+
+
+def variant_of(layout: str, coder: str = "huffman") -> str:
+    return layout if coder == "huffman" else f"{layout}_{coder}"
 
 
 def kernel_source_sha(layout: str = "chunks") -> str:
@@ -50,12 +56,12 @@ def kernel_source_sha(layout: str = "chunks") -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def recorded_traffic(workload: str, layout: str = "chunks"):
+def recorded_traffic(workload: str, layout: str = "chunks", coder: str = "huffman"):
     """HBM bytes per launch measured with rocprofv3 counters, if still valid."""
     try:
-        with open(TRAFFIC_FILES[layout]) as f:
+        with open(TRAFFIC_FILES[variant_of(layout, coder)]) as f:
             rec = json.load(f)
-    except (OSError, ValueError):
+    except (OSError, ValueError, KeyError):
         return None
     if rec.get("kernel_source_sha256") != kernel_source_sha(layout) or rec.get("workload") != workload:
         return None
@@ -77,6 +83,8 @@ def parse_args():
     ap.add_argument("--layout", choices=["lanes", "chunks"], default="lanes",
                     help="container layout: lanes (v3, interleaved lanes; the library's default) or "
                          "chunks (v2, per-chunk gaps)")
+    ap.add_argument("--coder", choices=["huffman", "rans"], default="huffman",
+                    help="entropy coder of the lanes layout: huffman (the default) or rans")
     ap.add_argument("--e2e", action="store_true",
                     help="70B-shape block end to end: decode + batch-1 GEMVs against GEMVs on resident "
                          "uncompressed weights (prints its own JSON line)")
@@ -283,17 +291,17 @@ def main():
     # bf16 weights (the exponent coded, sm raw) or a plane of 8-bit quantized
     # codes (every byte coded; lanes layout only)
     codes = args.workload in CODE_WORKLOADS
-    if codes and args.layout != "lanes":
-        print("bench.py: code planes use the lanes layout", file=sys.stderr)
+    if (codes or args.coder != "huffman") and args.layout != "lanes":
+        print("bench.py: code planes and the rANS coder use the lanes layout", file=sys.stderr)
         sys.exit(2)
     t_gen = time.perf_counter()
     if codes:
         wl = make_code_workload(args.workload)
-        blob = wc.encode_u8_host(wl.tensors())
+        blob = wc.encode_u8_host(wl.tensors(), coder=args.coder)
         raw, out_bytes, out_dtype, decode = wl.codes, 1, torch.uint8, wc.decode_u8_async
     else:
         wl = make_workload(args.workload)
-        blob = wc.encode_host(wl.tensors(), layout=args.layout)
+        blob = wc.encode_host(wl.tensors(), layout=args.layout, coder=args.coder)
         raw, out_bytes, out_dtype, decode = wl.bits.view(np.int16), 2, torch.int16, wc.decode_async
     t_gen = time.perf_counter() - t_gen
     n = wl.n
@@ -390,7 +398,8 @@ def main():
             assert np.array_equal(dec, wl.codes if codes else wl.bits)
         cpu = {"value": round(out_bytes * n * reps / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"the whole {args.workload} container ({n} elements) decoded {reps} times by the serial "
-                         f"bit-by-bit trie decoder with every container check: {spent:.1f} s on one host core"}
+                         f"{'rANS decoder (linear slot search)' if args.coder == 'rans' else 'bit-by-bit trie decoder'} "
+                         f"with every container check: {spent:.1f} s on one host core"}
 
     desc = CODE_WORKLOADS[args.workload][0] if codes else workload_spec(args.workload)[0]
     line = {
@@ -410,6 +419,7 @@ def main():
         "config": {
             "workload": f"{args.workload}: {desc}",
             "layout": args.layout,
+            "coder": args.coder,
             "n_elems": n,
             "n_tensors": len(wl.numels),
             "container_bytes": int(blob.size),
@@ -431,7 +441,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic(args.workload, args.layout),
+            "traffic": recorded_traffic(args.workload, args.layout, args.coder),
             "algorithmic_bytes_per_launch": alg_bytes,
             "kernel_avg_ms": round(kernel_avg_ms, 5),
             "launch_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},

@@ -67,6 +67,32 @@
  * canonical code and there is no sm section (its length is 0).  Version 2
  * containers hold bf16 only (byte 124 is 0).
  *
+ * Coder (v3, u8 at header byte 125; version 2: 0): 0 = the canonical Huffman
+ * code above; 1 = rANS (pages: "From a Lossless (~1.5:1) Compression
+ * Algorithm for Llama2 7B Weights ...", abstract, names ANS; the LazyWeights
+ * review compares a Huffman and an rANS decoder).  An rANS container differs
+ * from a Huffman one in:
+ *   max_code_len = 12 (the frequency precision P);
+ *   code_len    replaced by u16 freq[256] (512 bytes): quantized symbol
+ *               frequencies summing to 2^12 (all 0 when n_elems = 0);
+ *               cum[s] = sum of freq[t] for t < s;
+ *   lanes       each non-empty lane is one rANS stream over its symbols in
+ *               lane order: its string is the 32-bit final state (high
+ *               16 bits first) then the 16-bit renormalisation words in the
+ *               order the decoder reads them, all big-endian.  Decoding a
+ *               symbol from state x: slot = x mod 2^12, s the symbol with
+ *               cum[s] <= slot < cum[s] + freq[s],
+ *               x = freq[s] * (x >> 12) + slot - cum[s], and while x < 2^16
+ *               x = (x << 16) | next word; the encoder starts (and so the
+ *               decoder ends) every lane at x = 2^16.  A lane with no symbols
+ *               has an empty string; every lane length, lane offset and
+ *               segment bit is a multiple of 16;
+ *   segments    as long as possible while they hold at most M elements and
+ *               64 * 32 + (sum over their elements of c(freq[s])) / 8 <= B,
+ *               with c(f) = ceil(8 (12 - log2 f)) + 1 (an upper bound, in
+ *               eighths of a bit, of what one symbol adds to a lane);
+ *               B >= 2048 and 97 A <= 8 (B - 2048), so one block always fits.
+ *
  * Status codes: 0 on success, a negative WC_ERR_* value otherwise.  No C++
  * exception ever crosses this interface.
  */
@@ -89,8 +115,10 @@ extern "C" {
 #define WC_ERR_TRUNCATED        -11  /* blob shorter than the header or total_bytes           */
 #define WC_ERR_SECTION_BOUNDS   -12  /* a section is misaligned, out of order or outside blob */
 #define WC_ERR_CODE_LENGTHS     -13  /* a code length > max_code_len, or no symbols for n > 0 */
+                                     /* (rANS: a frequency above 2^12)                        */
 #define WC_ERR_KRAFT            -14  /* code lengths do not form a complete prefix code       */
-#define WC_ERR_GAP              -15  /* a per-chunk gap is out of range                        */
+                                     /* (rANS: frequencies do not sum to 2^12)                */
+#define WC_ERR_GAP              -15  /* a per-chunk gap or a lane offset is out of range       */
 #define WC_ERR_GROUP_START      -16  /* group table not increasing, misaligned, too wide, or  */
                                      /* not ending at {n_elems, stream_bits}                  */
 #define WC_ERR_STREAM_BITS      -17  /* stream_bits / n_chunks / n_groups / stream_bytes wrong */
@@ -114,10 +142,15 @@ typedef struct {
     uint32_t seg_max_bits;      /* v3: stream bits per segment at most, >= A *          */
                                 /* max_code_len and < 65536; 0 selects the default      */
                                 /* 15872, the most the GPU decoder accepts.             */
+    uint32_t coder;             /* WC_CODER_HUFFMAN (0, the default) or WC_CODER_RANS   */
+                                /* (1: lanes layout only; max_code_len is ignored and   */
+                                /* 97 A <= 8 (seg_max_bits - 2048) is required)         */
 } wc_encode_opts;
 
 #define WC_LAYOUT_LANES  0u
 #define WC_LAYOUT_CHUNKS 1u
+#define WC_CODER_HUFFMAN 0u
+#define WC_CODER_RANS    1u
 
 /*
  * wc_encode_host -- offline preparation of one container from n_tensors bf16
@@ -183,10 +216,11 @@ int wc_plan_stats(const wc_plan_t* plan, uint64_t* container_bytes, uint64_t* st
                   uint32_t* lds_bytes);
 
 /*
- * wc_plan_format -- the container's version (2: chunks, 3: lanes) and element
- * kind (0: bf16, 1: u8).  Either output may be NULL.
+ * wc_plan_format -- the container's version (2: chunks, 3: lanes), element
+ * kind (0: bf16, 1: u8) and coder (0: Huffman, 1: rANS).  Any output may be
+ * NULL.
  */
-int wc_plan_format(const wc_plan_t* plan, uint32_t* version, uint32_t* elem_kind);
+int wc_plan_format(const wc_plan_t* plan, uint32_t* version, uint32_t* elem_kind, uint32_t* coder);
 
 /*
  * wc_decode_async -- decode every tensor of the container in ONE kernel launch

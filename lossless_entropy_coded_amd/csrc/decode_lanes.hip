@@ -25,6 +25,15 @@
 //           lanes decode) and the staged exponents (lane i's k-th 8 bytes
 //           are block i + 64k) become bf16 in registers, written with
 //           16-byte non-temporal stores, whole cache lines.
+//
+// rANS containers (the Llama2-7B page's abstract names ANS; the LazyWeights
+// review compares a Huffman and an rANS decoder) use the same segments,
+// staging and merge; a lane is then one rANS stream: the staged bytes are
+// swapped within 16-bit halves so that half-word q is the stream's q-th
+// big-endian word, and each step takes one symbol from the 2^12-slot table
+// (x = f (x >> 12) + x mod 2^12 - cum, then one word in when x < 2^16).
+// The state chain allows one symbol per table read where a Huffman lookup
+// yields up to four.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -38,6 +47,8 @@ namespace wc {
 namespace {
 
 constexpr uint32_t kStageWords = kLaneStageBytes / 4;
+constexpr uint32_t kStageHalves = kLaneStageBytes / 2;
+constexpr uint32_t kRansSlots = 1u << kRansBits;
 
 // One lane's loads for one segment: its two 16-byte pieces of the segment's
 // stream window (pieces past the bytes the segment needs are not loaded) and
@@ -65,6 +76,13 @@ __device__ __forceinline__ uint4 bswap4(const uint4& v) {
                       __builtin_bswap32(v.w));
 }
 
+// Each 16-bit half of each word byte-swapped: LDS half-word q of the staged
+// window is the stream's big-endian 16-bit word q.
+__device__ __forceinline__ uint4 swap16x8(const uint4& v) {
+    return make_uint4(__builtin_amdgcn_perm(v.x, v.x, 0x02030001u), __builtin_amdgcn_perm(v.y, v.y, 0x02030001u),
+                      __builtin_amdgcn_perm(v.z, v.z, 0x02030001u), __builtin_amdgcn_perm(v.w, v.w, 0x02030001u));
+}
+
 // Undo the one-bit rotation the decode tables store symbols with, in each
 // byte of a word (e = rol8(e', 1)).
 __device__ __forceinline__ uint32_t unrotate4(uint32_t x) {
@@ -75,9 +93,11 @@ __device__ __forceinline__ uint32_t unrotate4(uint32_t x) {
 // decode -> matrix-vector product): the decoded weights never leave the chip;
 // each wave multiplies its segment by x and leaves its partial dot products
 // in p.dot.part.  kLanesToU8: decode a plane of code bytes into p.out8 (no
-// sign+mantissa plane).
-template <int KD, int W, uint32_t kMode>
+// sign+mantissa plane).  kRans: rANS lanes (KD = 11: the slot table fills
+// the multi-codeword table's 16 KiB).
+template <int KD, int W, uint32_t kMode, bool kRans>
 __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodeParams p) {
+    static_assert(!kRans || (2u << KD) == kRansSlots, "the rANS slot table takes the multi-codeword table's place");
     constexpr bool kDot = kMode == kLanesToDot;
     constexpr bool kU8 = kMode == kLanesToU8;
     constexpr uint32_t kThreads = kWaveLanes * W;
@@ -147,9 +167,15 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
         const uint64_t un = u + stride;
         const bool more = un < p.u_end;
 
-        // the segment's stream words, byte-swapped (word k = bits 32k.. MSB-first)
-        reinterpret_cast<uint4*>(sbuf)[lane] = bswap4(cur_r.q0);
-        reinterpret_cast<uint4*>(sbuf)[lane + kWaveLanes] = bswap4(cur_r.q1);
+        // the segment's stream words, byte-swapped (word k = bits 32k.. MSB-first;
+        // rANS: half-word q = big-endian word q)
+        if constexpr (kRans) {
+            reinterpret_cast<uint4*>(sbuf)[lane] = swap16x8(cur_r.q0);
+            reinterpret_cast<uint4*>(sbuf)[lane + kWaveLanes] = swap16x8(cur_r.q1);
+        } else {
+            reinterpret_cast<uint4*>(sbuf)[lane] = bswap4(cur_r.q0);
+            reinterpret_cast<uint4*>(sbuf)[lane + kWaveLanes] = bswap4(cur_r.q1);
+        }
         const uint32_t off = cur_r.off;
 
         // next segment's loads, this segment's sign+mantissa bytes, the table
@@ -185,32 +211,59 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
             uint32_t nsym = kLaneBlock * cnt;
             if (cnt && lane == (nb8 - 1) % kWaveLanes) nsym -= kLaneBlock * nb8 - n;
             const uint32_t pos = (uint32_t)(cur_m.p0 & 127u) + off;   // first bit in the staged words
-            uint32_t wi = pos >> 5;
-            uint64_t win = (((uint64_t)sbuf[wi] << 32) | sbuf[wi + 1]) << (pos & 31u);
-            int32_t valid = 64 - (int32_t)(pos & 31u);
-            wi += 2;
-            // a lookup's symbols past the lane's last one (they belong to the
-            // next lane) land in the slot's spare bytes: p < nsym <= 64 before
-            // the store, so it ends by byte 67
-            uint32_t p = 0;
-            while (p < nsym) {
-                const uint32_t top = (uint32_t)(win >> 32);
-                uint2 e = s_dec[top >> (32 - KD)];
-                if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
-                uint8_t* const dst = slot + p;
-                const uint32_t odd = __builtin_amdgcn_perm(e.y, e.y, 0x0C030C01u);   // [s1, 0, s3, 0]
-                dst[0] = (uint8_t)e.y;
-                dst[1] = (uint8_t)odd;
-                dst[2] = (uint8_t)(e.y >> 16);
-                dst[3] = (uint8_t)(odd >> 16);
-                p += (e.x >> 8) & 0xFFu;
-                const uint32_t nbits = (e.x >> 16) & 0xFFu;
-                win <<= nbits;
-                valid -= (int32_t)nbits;
-                if (valid < 32) {
-                    win |= (uint64_t)sbuf[min(wi, kStageWords - 1)] << (32 - valid);
-                    ++wi;
-                    valid += 32;
+            if constexpr (kRans) {
+                // the final state, then one symbol per step, four per slot
+                // store; a lane whose count is not a multiple of four decodes
+                // up to three more (from whatever words follow, indexes
+                // clamped) into the slot's spare bytes
+                const uint16_t* const s16 = reinterpret_cast<const uint16_t*>(sbuf);
+                const uint32_t* const s_slot = reinterpret_cast<const uint32_t*>(s_tab);
+                uint32_t q = min(pos >> 4, kStageHalves - 2);
+                uint32_t x = (uint32_t)s16[q] << 16 | s16[q + 1];
+                q += 2;
+                for (uint32_t p = 0; p < nsym; p += 4) {
+                    uint32_t four = 0;
+#pragma unroll
+                    for (uint32_t i = 0; i < 4; ++i) {
+                        const uint32_t w = s16[min(q, kStageHalves - 1)];
+                        const uint32_t e = s_slot[x & (kRansSlots - 1)];
+                        const uint32_t hi = x >> kRansBits;
+                        x = __umul24((e >> 8) & 0xFFFu, hi) + hi + (e >> 20);   // f (x >> 12) + slot - cum
+                        const bool in = x < kRansLow;
+                        x = in ? x << 16 | w : x;
+                        q += in ? 1u : 0u;
+                        four |= (e & 0xFFu) << (8 * i);
+                    }
+                    *reinterpret_cast<uint32_t*>(slot + p) = four;
+                }
+            } else {
+                uint32_t wi = pos >> 5;
+                uint64_t win = (((uint64_t)sbuf[wi] << 32) | sbuf[wi + 1]) << (pos & 31u);
+                int32_t valid = 64 - (int32_t)(pos & 31u);
+                wi += 2;
+                // a lookup's symbols past the lane's last one (they belong to the
+                // next lane) land in the slot's spare bytes: p < nsym <= 64 before
+                // the store, so it ends by byte 67
+                uint32_t p = 0;
+                while (p < nsym) {
+                    const uint32_t top = (uint32_t)(win >> 32);
+                    uint2 e = s_dec[top >> (32 - KD)];
+                    if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
+                    uint8_t* const dst = slot + p;
+                    const uint32_t odd = __builtin_amdgcn_perm(e.y, e.y, 0x0C030C01u);   // [s1, 0, s3, 0]
+                    dst[0] = (uint8_t)e.y;
+                    dst[1] = (uint8_t)odd;
+                    dst[2] = (uint8_t)(e.y >> 16);
+                    dst[3] = (uint8_t)(odd >> 16);
+                    p += (e.x >> 8) & 0xFFu;
+                    const uint32_t nbits = (e.x >> 16) & 0xFFu;
+                    win <<= nbits;
+                    valid -= (int32_t)nbits;
+                    if (valid < 32) {
+                        win |= (uint64_t)sbuf[min(wi, kStageWords - 1)] << (32 - valid);
+                        ++wi;
+                        valid += 32;
+                    }
                 }
             }
         }
@@ -289,25 +342,25 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
     }
 }
 
-template <int KD, int W>
+template <int KD, int W, bool kRans>
 struct LanesVariant {
     static hipError_t launch(const DecodeParams& p, uint32_t grid, uint32_t dyn, LanesOut mode, hipStream_t stream) {
         const dim3 g(grid), b(kWaveLanes * W);
         if (mode == kLanesToDot)
-            hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToDot>), g, b, dyn, stream, p);
+            hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToDot, kRans>), g, b, dyn, stream, p);
         else if (mode == kLanesToU8)
-            hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToU8>), g, b, dyn, stream, p);
+            hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToU8, kRans>), g, b, dyn, stream, p);
         else
-            hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToBf16>), g, b, dyn, stream, p);
+            hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToBf16, kRans>), g, b, dyn, stream, p);
         return hipGetLastError();
     }
     static int blocks_per_cu(uint32_t dyn) {
         int n[3] = {0, 0, 0};
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[0], decode_lanes_kernel<KD, W, kLanesToBf16>,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[0], decode_lanes_kernel<KD, W, kLanesToBf16, kRans>,
                                                          kWaveLanes * W, dyn) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[1], decode_lanes_kernel<KD, W, kLanesToDot>,
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[1], decode_lanes_kernel<KD, W, kLanesToDot, kRans>,
                                                          kWaveLanes * W, dyn) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[2], decode_lanes_kernel<KD, W, kLanesToU8>,
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[2], decode_lanes_kernel<KD, W, kLanesToU8, kRans>,
                                                          kWaveLanes * W, dyn) != hipSuccess)
             return 0;
         return std::min(n[0], std::min(n[1], n[2]));
@@ -315,9 +368,10 @@ struct LanesVariant {
 };
 
 template <typename F>
-hipError_t dispatch_lanes(uint32_t decode_bits, uint32_t waves, F&& f) {
-    if (decode_bits == 11) return waves == 8 ? f(LanesVariant<11, 8>{}) : f(LanesVariant<11, 4>{});
-    return waves == 8 ? f(LanesVariant<10, 8>{}) : f(LanesVariant<10, 4>{});
+hipError_t dispatch_lanes(uint32_t decode_bits, uint32_t waves, bool rans, F&& f) {
+    if (rans) return waves == 8 ? f(LanesVariant<11, 8, true>{}) : f(LanesVariant<11, 4, true>{});
+    if (decode_bits == 11) return waves == 8 ? f(LanesVariant<11, 8, false>{}) : f(LanesVariant<11, 4, false>{});
+    return waves == 8 ? f(LanesVariant<10, 8, false>{}) : f(LanesVariant<10, 4, false>{});
 }
 
 }  // namespace
@@ -330,11 +384,11 @@ uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l
     return ((2u << decode_bits) + kLongWords) * 4 + decode_lanes_dyn_lds_bytes(waves, l2_cap);
 }
 
-int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap) {
-    if ((decode_bits != 11 && decode_bits != 10) || !supported_waves(waves)) return 0;
+int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool rans) {
+    if ((decode_bits != 11 && decode_bits != 10) || (rans && decode_bits != 11) || !supported_waves(waves)) return 0;
     const uint32_t dyn = decode_lanes_dyn_lds_bytes(waves, l2_cap);
     int n = 0;
-    (void)dispatch_lanes(decode_bits, waves, [&](auto v) {
+    (void)dispatch_lanes(decode_bits, waves, rans, [&](auto v) {
         n = decltype(v)::blocks_per_cu(dyn);
         return hipSuccess;
     });
@@ -342,11 +396,12 @@ int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2
 }
 
 hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid,
-                               LanesOut mode, hipStream_t stream) {
-    if ((decode_bits != 11 && decode_bits != 10) || !supported_waves(waves) || p.l2_cap > kL2Prefixes)
+                               LanesOut mode, bool rans, hipStream_t stream) {
+    if ((decode_bits != 11 && decode_bits != 10) || (rans && (decode_bits != 11 || p.l2_cap)) ||
+        !supported_waves(waves) || p.l2_cap > kL2Prefixes)
         return hipErrorInvalidValue;
     const uint32_t dyn = decode_lanes_dyn_lds_bytes(waves, p.l2_cap);
-    return dispatch_lanes(decode_bits, waves,
+    return dispatch_lanes(decode_bits, waves, rans,
                           [&](auto v) { return decltype(v)::launch(p, grid, dyn, mode, stream); });
 }
 

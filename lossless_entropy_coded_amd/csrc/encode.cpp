@@ -21,6 +21,9 @@
 // bit cap instead of a chunk cap in step 5, and in step 6 writes each
 // segment lane by lane: lane j's lane blocks j, j + 64, ... of 8 elements,
 // with a u16 offset per lane.
+// The rANS coder (coder 1; the Llama2-7B page's abstract names ANS) replaces
+// steps 3-4 by quantized frequencies, cuts segments by a proven upper bound
+// of their encoded size, and makes every lane one rANS stream.
 #include <algorithm>
 #include <array>
 #include <atomic>
@@ -259,6 +262,181 @@ int write_lanes(const SourceT<T>& src, uint64_t n, uint32_t n_tensors, const uin
     return WC_OK;
 }
 
+// ---------------------------------------------------------------------------
+// rANS in the lane layout.
+// ---------------------------------------------------------------------------
+// Quantized frequencies summing to 2^12: every present symbol first gets
+// max(1, floor(count * 2^12 / n)); an excess is then removed one unit at a
+// time from the largest frequency above 1 (the lowest symbol among equal
+// ones), a shortfall is added to the most frequent symbol (the lowest among
+// equal counts).
+void rans_frequencies(const uint64_t hist[256], uint64_t n, uint32_t freq[256]) {
+    constexpr uint32_t kTotal = 1u << kRansBits;
+    int top = -1;
+    uint32_t sum = 0;
+    for (int s = 0; s < 256; ++s) {
+        freq[s] = hist[s] ? (uint32_t)std::max<uint64_t>(1, (hist[s] << kRansBits) / n) : 0u;
+        sum += freq[s];
+        if (hist[s] && (top < 0 || hist[s] > hist[top])) top = s;
+    }
+    if (top < 0) return;
+    while (sum > kTotal) {
+        int big = -1;
+        for (int s = 0; s < 256; ++s)
+            if (freq[s] > 1 && (big < 0 || freq[s] > freq[big])) big = s;
+        --freq[big];
+        --sum;
+    }
+    freq[top] += kTotal - sum;
+}
+
+// Upper bound, in eighths of a bit, of the growth of a lane's string per
+// symbol of frequency f: encoding multiplies the state by at most
+// 2^12 / f * (1 + f / x) with x >= 2^16, so it adds less than 12 - log2 f +
+// 0.0875 bits, and ceil(8 (12 - log2 f)) + 1 eighths bound it.  With
+// v = f^8 <= 2^96 of bit length b, the ceiling is the least q with
+// v 2^q >= 2^96, which is 97 - b whether or not v is a power of two.
+uint32_t rans_cost8(uint32_t f) {
+    unsigned __int128 v = 1;
+    for (int i = 0; i < 8; ++i) v *= f;
+    const uint64_t hi = (uint64_t)(v >> 64), lo = (uint64_t)v;
+    const uint32_t b = hi ? 128u - (uint32_t)__builtin_clzll(hi) : 64u - (uint32_t)__builtin_clzll(lo);
+    return 97u - b + 1u;
+}
+
+// One segment of m symbols: every lane's string appended to `words` (lane
+// order), lane j's bit offset from the segment's first bit in loff[j].  A
+// lane encodes its symbols last to first from the state 2^16; a word is
+// pushed out when the state would leave [2^16, 2^32) (x >= f 2^20 before
+// the step), so one push always suffices.
+void rans_encode_segment(const uint8_t* sym, uint64_t m, const uint32_t freq[256], const uint32_t cum[256],
+                         std::vector<uint16_t>& words, std::vector<uint16_t>& pushed, uint16_t* loff) {
+    const uint64_t start = words.size();
+    const uint64_t nb8 = div_up(m, kLaneBlock);
+    for (uint32_t j = 0; j < kLanes; ++j) {
+        loff[j] = (uint16_t)(16 * (words.size() - start));
+        if (j >= nb8) continue;
+        pushed.clear();
+        uint32_t x = kRansLow;
+        const uint64_t last = j + (nb8 - 1 - j) / kLanes * kLanes;   // the lane's last lane block
+        for (uint64_t b = last + kLanes; b > j;) {
+            b -= kLanes;
+            const uint64_t i0 = kLaneBlock * b, i1 = std::min<uint64_t>(m, i0 + kLaneBlock);
+            for (uint64_t i = i1; i-- > i0;) {
+                const uint32_t f = freq[sym[i]];
+                if (x >= ((uint64_t)f << 20)) {
+                    pushed.push_back((uint16_t)x);
+                    x >>= 16;
+                }
+                x = ((x / f) << kRansBits) + x % f + cum[sym[i]];
+            }
+        }
+        words.push_back((uint16_t)(x >> 16));
+        words.push_back((uint16_t)x);
+        words.insert(words.end(), pushed.rbegin(), pushed.rend());   // the order the decoder reads them
+    }
+}
+
+template <typename T>
+int write_lanes_rans(const SourceT<T>& src, uint64_t n, uint32_t n_tensors, const uint64_t hist[256],
+                     uint32_t align, uint32_t max_elems, uint32_t seg_bits, unsigned nthreads, uint8_t** blob,
+                     uint64_t* blob_bytes) {
+    constexpr bool kBf16 = sizeof(T) == 2;
+    uint32_t freq[256], cum[256], cost8[256];
+    rans_frequencies(hist, n, freq);
+    for (uint32_t s = 0, acc = 0; s < 256; ++s) {
+        cum[s] = acc;
+        acc += freq[s];
+        cost8[s] = freq[s] ? rans_cost8(freq[s]) : 0u;
+    }
+    // segments: the longest runs of whole blocks with at most max_elems
+    // elements whose bound (64 final states plus the symbols' cost8) fits
+    const uint64_t n_blocks = div_up(n, align);
+    std::vector<uint64_t> cost_before(n_blocks + 1, 0);
+    parallel_for(nthreads, [&](unsigned t) {
+        const uint64_t k0 = n_blocks * t / nthreads, k1 = n_blocks * (t + 1) / nthreads;
+        for (uint64_t k = k0; k < k1; ++k) {
+            uint64_t c = 0;
+            src.for_range(k * align, std::min<uint64_t>(n, (k + 1) * align), [&](uint64_t, const T* p, uint64_t cnt) {
+                for (uint64_t i = 0; i < cnt; ++i) c += cost8[symbol_of(p[i])];
+            });
+            cost_before[k + 1] = c;
+        }
+    });
+    for (uint64_t k = 0; k < n_blocks; ++k) cost_before[k + 1] += cost_before[k];
+    const uint64_t fixed8 = 8ull * kLanes * kRansStateBits;
+    std::vector<uint64_t> s_elem{0};
+    for (uint64_t k0 = 0; k0 < n_blocks;) {
+        uint64_t k1 = k0 + 1;
+        const uint64_t k_cap = k0 + max_elems / align;
+        while (k1 < n_blocks && k1 < k_cap && fixed8 + cost_before[k1 + 1] - cost_before[k0] <= 8ull * seg_bits) ++k1;
+        s_elem.push_back(std::min<uint64_t>(k1 * align, n));
+        k0 = k1;
+    }
+    const uint64_t n_segs = s_elem.size() - 1;
+
+    // encode: each thread a run of segments into its own words
+    const unsigned nt = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(nthreads, n_segs));
+    std::vector<std::vector<uint16_t>> words(nt);
+    std::vector<uint64_t> seg_words(n_segs + 1, 0);
+    std::vector<uint16_t> loff(kLanes * n_segs);
+    std::atomic<bool> too_long{false};
+    parallel_for(nt, [&](unsigned t) {
+        const uint64_t g0 = n_segs * t / nt, g1 = n_segs * (t + 1) / nt;
+        std::vector<uint8_t> sym(max_elems);
+        std::vector<uint16_t> pushed;
+        for (uint64_t g = g0; g < g1; ++g) {
+            const uint64_t e0 = s_elem[g], m = s_elem[g + 1] - e0;
+            src.for_range(e0, e0 + m, [&](uint64_t gi, const T* p, uint64_t k) {
+                for (uint64_t i = 0; i < k; ++i) sym[gi - e0 + i] = symbol_of(p[i]);
+            });
+            const uint64_t before = words[t].size();
+            rans_encode_segment(sym.data(), m, freq, cum, words[t], pushed, loff.data() + kLanes * g);
+            seg_words[g + 1] = words[t].size() - before;
+            if (16 * seg_words[g + 1] > seg_bits) too_long = true;   // excluded by the bound
+        }
+    });
+    if (too_long) return WC_ERR_INVALID_ARG;
+    for (uint64_t g = 0; g < n_segs; ++g) seg_words[g + 1] += seg_words[g];
+    const uint64_t stream_bits = 16 * seg_words[n_segs];
+
+    const Header h = layout_lanes(n, stream_bits, n_tensors, kRansBits, align, max_elems, seg_bits, n_segs,
+                                  kBf16 ? kKindBf16 : kKindU8, kCoderRans);
+    const uint64_t sm_bytes = kBf16 ? n : 0;
+    uint8_t* out = (uint8_t*)std::aligned_alloc(kAlign, h.total_bytes);
+    if (!out) return WC_ERR_NOMEM;
+    std::memset(out, 0, h.off_sm);
+    std::memset(out + h.off_sm + sm_bytes, 0, h.total_bytes - h.off_sm - sm_bytes);
+    write_header(out, h);
+    for (int s = 0; s < 256; ++s) store_le<uint16_t>(out + h.off_code_len + 2 * s, (uint16_t)freq[s]);
+    for (uint32_t k = 0; k < n_tensors; ++k) {
+        store_le<uint64_t>(out + h.off_tensors + 16ull * k, src.begin[k]);
+        store_le<uint64_t>(out + h.off_tensors + 16ull * k + 8, src.size[k]);
+    }
+    for (uint64_t g = 0; g <= n_segs; ++g) {
+        store_le<uint64_t>(out + h.off_groups + kGroupEntryBytes * g, s_elem[g]);
+        store_le<uint64_t>(out + h.off_groups + kGroupEntryBytes * g + 8, 16 * seg_words[g]);
+    }
+    for (uint64_t i = 0; i < kLanes * n_segs; ++i) store_le<uint16_t>(out + h.off_gap + 2 * i, loff[i]);
+    uint8_t* stream = out + h.off_stream;
+    uint8_t* sm = out + h.off_sm;
+    parallel_for(nt, [&](unsigned t) {
+        const uint64_t g0 = n_segs * t / nt, g1 = n_segs * (t + 1) / nt;
+        uint8_t* dst = stream + 2 * seg_words[g0];
+        for (const uint16_t w : words[t]) {   // big-endian words
+            *dst++ = (uint8_t)(w >> 8);
+            *dst++ = (uint8_t)w;
+        }
+        if constexpr (kBf16)
+            src.for_range(s_elem[g0], s_elem[g1], [&](uint64_t gi, const T* p, uint64_t k) {
+                for (uint64_t i = 0; i < k; ++i) sm[gi + i] = sign_mantissa_of(p[i]);
+            });
+    });
+    *blob = out;
+    *blob_bytes = h.total_bytes;
+    return WC_OK;
+}
+
 // The whole encoder for bf16 words (T = uint16_t) or code bytes (T = uint8_t).
 template <typename T>
 int encode_impl(const T* const* tensors, const uint64_t* numels, uint32_t n_tensors, const wc_encode_opts* opts,
@@ -269,7 +447,7 @@ int encode_impl(const T* const* tensors, const uint64_t* numels, uint32_t n_tens
     *blob_bytes = 0;
     if (n_tensors && (!tensors || !numels)) return WC_ERR_INVALID_ARG;
     uint32_t max_len = kMaxCodeLen, group = kDefaultGroup, align = kDefaultAlign, max_elems = kDefaultMaxElems;
-    uint32_t nthreads = 0, kind = WC_LAYOUT_LANES, seg_bits = kDefaultSegBits;
+    uint32_t nthreads = 0, kind = WC_LAYOUT_LANES, seg_bits = kDefaultSegBits, coder = WC_CODER_HUFFMAN;
     if (opts) {
         if (opts->max_code_len) max_len = opts->max_code_len;
         if (opts->chunk_bytes && opts->chunk_bytes != 8) return WC_ERR_INVALID_ARG;
@@ -279,6 +457,7 @@ int encode_impl(const T* const* tensors, const uint64_t* numels, uint32_t n_tens
         nthreads = opts->n_threads;
         kind = opts->layout;
         if (opts->seg_max_bits) seg_bits = opts->seg_max_bits;
+        coder = opts->coder;
     }
     if (max_len < 1 || max_len > kMaxCodeLen || group < 1 || group > (1u << 20) || align > (1u << 20) ||
         max_elems < align || max_elems % align || max_elems > (1u << 26))
@@ -289,11 +468,17 @@ int encode_impl(const T* const* tensors, const uint64_t* numels, uint32_t n_tens
         if ((uint64_t)align * max_len + (kChunkBits - 1) > (uint64_t)kChunkBits * group) return WC_ERR_INVALID_ARG;
     } else if (kind == WC_LAYOUT_LANES) {
         // a segment's lane offsets are u16 bit counts; one block always fits
-        if (seg_bits > 65535u || (uint64_t)align * max_len > seg_bits) return WC_ERR_INVALID_ARG;
+        // (rANS: A symbols cost at most 97 eighths each besides the 64 final states)
+        if (seg_bits > 65535u) return WC_ERR_INVALID_ARG;
+        if (coder == WC_CODER_RANS ? seg_bits < kLanes * kRansStateBits ||
+                                         97ull * align > 8ull * (seg_bits - kLanes * kRansStateBits)
+                                   : (uint64_t)align * max_len > seg_bits)
+            return WC_ERR_INVALID_ARG;
     } else {
         return WC_ERR_INVALID_ARG;
     }
     if (!kBf16 && kind != WC_LAYOUT_LANES) return WC_ERR_INVALID_ARG;   // code planes: lanes layout only
+    if (coder != WC_CODER_HUFFMAN && (coder != WC_CODER_RANS || kind != WC_LAYOUT_LANES)) return WC_ERR_INVALID_ARG;
 
     SourceT<T> src;
     uint64_t n = 0;
@@ -325,6 +510,8 @@ int encode_impl(const T* const* tensors, const uint64_t* numels, uint32_t n_tens
     uint64_t hist[256] = {0};
     for (auto& h : hist_t)
         for (int s = 0; s < 256; ++s) hist[s] += h[s];
+    if (coder == WC_CODER_RANS)
+        return write_lanes_rans(src, n, n_tensors, hist, align, max_elems, seg_bits, nthreads, blob, blob_bytes);
 
     // 3-4. code lengths and canonical codes
     uint8_t len[256];

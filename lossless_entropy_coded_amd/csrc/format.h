@@ -34,6 +34,18 @@ constexpr uint32_t kDefaultSegBits = 15872;   // stream bits per segment at most
 // quantized integer codes).
 constexpr uint32_t kKindBf16 = 0;
 constexpr uint32_t kKindU8 = 1;
+// Coders of a version-3 container: the canonical Huffman code, or rANS
+// (Llama2-7B page, abstract: ANS; the LazyWeights page compares the two).
+// rANS: kRansBits-bit quantized frequencies (u16[256] in place of the code
+// lengths, summing to 2^kRansBits), a 32-bit state kept in [kRansLow, 2^32),
+// 16-bit renormalisation words; a lane's string is its final state (two
+// words, high first) followed by the words its decoder reads, each
+// big-endian, and is empty for a lane with no symbols.
+constexpr uint32_t kCoderHuffman = 0;
+constexpr uint32_t kCoderRans = 1;
+constexpr uint32_t kRansBits = 12;
+constexpr uint32_t kRansLow = 1u << 16;
+constexpr uint32_t kRansStateBits = 32;    // the final state every non-empty lane string starts with
 
 // Header field offsets (little-endian).
 struct HeaderOffsets {
@@ -42,7 +54,7 @@ struct HeaderOffsets {
                          n_elems = 24, stream_bits = 32, n_chunks = 40, n_groups = 48,
                          off_code_len = 56, off_tensors = 64, off_groups = 72, off_gap = 80,
                          off_stream = 88, stream_bytes = 96, off_sm = 104, total_bytes = 112,
-                         group_max_elems = 120, elem_kind = 124, reserved_tail = 125;
+                         group_max_elems = 120, elem_kind = 124, coder = 125, reserved_tail = 126;
     // version 3 reuses the positions: lanes at 9, lane block at 10, the
     // segment bit cap at 12, the lane offsets at off_gap; n_chunks is 0
     static constexpr int lanes = 9, lane_block = 10, seg_max_bits = 12;
@@ -52,6 +64,7 @@ struct Header {
     uint32_t version = kVersion;   // kVersion or kVersionLanes
     uint32_t seg_max_bits = 0;     // version 3
     uint32_t elem_kind = kKindBf16;   // version 3: kKindBf16 or kKindU8
+    uint32_t coder = kCoderHuffman;   // version 3: kCoderHuffman or kCoderRans
     uint32_t max_code_len = 0, chunks_per_group = 0, n_tensors = 0, group_align = 0, group_max_elems = 0;
     uint64_t n_elems = 0, stream_bits = 0, n_chunks = 0, n_groups = 0;
     uint64_t off_code_len = 0, off_tensors = 0, off_groups = 0, off_gap = 0, off_stream = 0,
@@ -102,14 +115,19 @@ inline Header layout(uint64_t n_elems, uint64_t stream_bits, uint32_t n_tensors,
     return h;
 }
 
+// Bytes of the code section: code lengths (u8) or rANS frequencies (u16).
+inline uint64_t code_section_bytes(uint32_t coder) { return coder == kCoderRans ? 512 : 256; }
+
 // Section placement of a version-3 (interleaved-lane) container; the lane
-// offsets take the place of the gaps (off_gap).
+// offsets take the place of the gaps (off_gap).  For rANS, max_code_len is
+// kRansBits.
 inline Header layout_lanes(uint64_t n_elems, uint64_t stream_bits, uint32_t n_tensors, uint32_t max_code_len,
                            uint32_t align, uint32_t max_elems, uint32_t seg_max_bits, uint64_t n_segs,
-                           uint32_t elem_kind = kKindBf16) {
+                           uint32_t elem_kind = kKindBf16, uint32_t coder = kCoderHuffman) {
     Header h;
     h.version = kVersionLanes;
     h.elem_kind = elem_kind;
+    h.coder = coder;
     h.seg_max_bits = seg_max_bits;
     h.max_code_len = max_code_len;
     h.group_align = align;
@@ -121,7 +139,7 @@ inline Header layout_lanes(uint64_t n_elems, uint64_t stream_bits, uint32_t n_te
     h.n_groups = n_segs;
     h.stream_bytes = round_up(div_up(stream_bits, 8), 8) + kLanesSlack;
     h.off_code_len = kHeaderBytes;
-    h.off_tensors = round_up(h.off_code_len + 256, kAlign);
+    h.off_tensors = round_up(h.off_code_len + code_section_bytes(coder), kAlign);
     h.off_groups = round_up(h.off_tensors + 16ull * n_tensors, kAlign);
     h.off_gap = round_up(h.off_groups + kGroupEntryBytes * (n_segs + 1), kAlign);
     h.off_stream = round_up(h.off_gap + 2ull * kLanes * n_segs, kAlign);
@@ -141,6 +159,7 @@ inline void write_header(uint8_t* p, const Header& h) {
         store_le<uint16_t>(p + O::lane_block, (uint16_t)kLaneBlock);
         store_le<uint32_t>(p + O::seg_max_bits, h.seg_max_bits);
         store_le<uint8_t>(p + O::elem_kind, (uint8_t)h.elem_kind);
+        store_le<uint8_t>(p + O::coder, (uint8_t)h.coder);
     } else {
         store_le<uint8_t>(p + O::chunk_bits, (uint8_t)kChunkBits);
         store_le<uint32_t>(p + O::chunks_per_group, h.chunks_per_group);

@@ -150,12 +150,15 @@ hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t de
 // What a lanes launch produces: bf16 words in p.out (the exponent coded,
 // joined with the sign+mantissa plane), partial dot products in p.dot, or
 // the decoded bytes themselves in p.out8 (u8-kind containers).
+// With rans, the lanes are rANS streams and p.tables holds the 2^12-entry
+// slot table in the multi-codeword table's place (decode_bits must be 11):
+// entry t = rotated symbol | (f - 1) << 8 | (t - cum) << 20.
 enum LanesOut : uint32_t { kLanesToBf16 = 0, kLanesToDot = 1, kLanesToU8 = 2 };
 uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap);
 uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap);
-int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap);
+int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool rans);
 hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid,
-                               LanesOut mode, hipStream_t stream);
+                               LanesOut mode, bool rans, hipStream_t stream);
 
 // One launch adding, for every global row of p.dot, the partial dot products
 // of the groups covering it, in group order, into the row's y.

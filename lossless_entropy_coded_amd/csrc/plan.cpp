@@ -7,7 +7,10 @@
 // monotone and end at n, gaps are shorter than the longest code, and the code
 // lengths form a complete prefix code.  It then builds the compact decode
 // tables on the device (design point (i)) and sizes one persistent launch
-// that covers a whole multi-tensor container (design point (iii)).
+// that covers a whole multi-tensor container (design point (iii)).  For an
+// rANS container (the Llama2-7B page's ANS) the checks are on the quantized
+// frequencies and 16-bit word alignment instead, and the decode table maps
+// each of the 2^12 slots to its symbol, frequency and offset.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -35,6 +38,7 @@ struct wc_plan_s {
     uint32_t ebuf_bytes = 0;
     uint32_t l2_cap = 0;         // long-code prefixes whose second-level entries are staged in LDS
     bool lanes = false;          // container version 3 (interleaved lanes)
+    bool rans = false;           // coder rANS (version 3)
     uint32_t* d_tables = nullptr;
 };
 
@@ -64,6 +68,9 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
         if (b[k]) return WC_ERR_BAD_MAGIC;
     h.elem_kind = b[O::elem_kind];
     if (h.elem_kind != wc::kKindBf16 && (!lanes || h.elem_kind != wc::kKindU8)) return WC_ERR_BAD_MAGIC;
+    h.coder = b[O::coder];
+    if (h.coder != wc::kCoderHuffman && (!lanes || h.coder != wc::kCoderRans)) return WC_ERR_BAD_MAGIC;
+    const bool rans = h.coder == wc::kCoderRans;
     h.max_code_len = b[O::max_code_len];
     h.chunks_per_group = lanes ? 0u : load_le<uint32_t>(b + O::chunks_per_group);
     h.seg_max_bits = lanes ? load_le<uint32_t>(b + O::seg_max_bits) : 0u;
@@ -86,13 +93,22 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
         h.group_max_elems < h.group_align || h.group_max_elems % h.group_align)
         return WC_ERR_BAD_MAGIC;
     if (!lanes && h.chunks_per_group < 1) return WC_ERR_BAD_MAGIC;
-    if (lanes && (h.seg_max_bits > 65535u || (uint64_t)h.group_align * h.max_code_len > h.seg_max_bits))
+    if (lanes && !rans && (h.seg_max_bits > 65535u || (uint64_t)h.group_align * h.max_code_len > h.seg_max_bits))
+        return WC_ERR_BAD_MAGIC;
+    // rANS: P = 12, and one block always fits a segment (at most 97 eighths
+    // of a bit per symbol besides the 64 final states)
+    constexpr uint32_t kStates = wc::kLanes * wc::kRansStateBits;
+    if (rans && (h.max_code_len != wc::kRansBits || h.seg_max_bits > 65535u || h.seg_max_bits < kStates ||
+                 97ull * h.group_align > 8ull * (h.seg_max_bits - kStates)))
         return WC_ERR_BAD_MAGIC;
     if (h.total_bytes > bytes) return WC_ERR_TRUNCATED;
 
-    // size fields
-    if (h.n_elems > (1ull << 40) || h.stream_bits > h.n_elems * (uint64_t)h.max_code_len ||
-        h.stream_bits < h.n_elems || h.n_groups > h.n_elems || (h.n_groups == 0) != (h.n_elems == 0))
+    // size fields (rANS: at most 13 bits per symbol and a final state per lane,
+    // whole 16-bit words)
+    if (h.n_elems > (1ull << 40) || h.n_groups > h.n_elems || (h.n_groups == 0) != (h.n_elems == 0))
+        return WC_ERR_STREAM_BITS;
+    if (rans ? h.stream_bits % 16 || h.stream_bits > h.n_elems * (wc::kRansBits + 1) + kStates * h.n_groups
+             : h.stream_bits > h.n_elems * (uint64_t)h.max_code_len || h.stream_bits < h.n_elems)
         return WC_ERR_STREAM_BITS;
     if (lanes ? h.stream_bytes != wc::round_up(wc::div_up(h.stream_bits, 8), 8) + wc::kLanesSlack
               : (h.n_chunks != wc::div_up(h.stream_bits, wc::kChunkBits) ||
@@ -102,7 +118,7 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
     // sections: 256-byte aligned, in order, non-overlapping, inside total_bytes
     if (h.n_tensors > (1u << 24)) return WC_ERR_SECTION_BOUNDS;
     const uint64_t off[6] = {h.off_code_len, h.off_tensors, h.off_groups, h.off_gap, h.off_stream, h.off_sm};
-    const uint64_t len[6] = {256, 16ull * h.n_tensors, wc::kGroupEntryBytes * (h.n_groups + 1),
+    const uint64_t len[6] = {wc::code_section_bytes(h.coder), 16ull * h.n_tensors, wc::kGroupEntryBytes * (h.n_groups + 1),
                              lanes ? 2ull * wc::kLanes * h.n_groups : h.n_chunks, h.stream_bytes,
                              h.elem_kind == wc::kKindBf16 ? h.n_elems : 0};
     uint64_t lo = wc::kHeaderBytes;
@@ -127,18 +143,28 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
     }
     if (acc != h.n_elems) return WC_ERR_TENSOR_TABLE;
 
+    if (rans) {
+        // frequencies: each at most 2^12, summing to 2^12 (all 0 for no elements)
+        uint32_t sum = 0;
+        for (int s = 0; s < 256; ++s) {
+            const uint32_t f = load_le<uint16_t>(b + h.off_code_len + 2 * s);
+            if (f > (1u << wc::kRansBits)) return WC_ERR_CODE_LENGTHS;
+            sum += f;
+        }
+        if (sum != (h.n_elems ? 1u << wc::kRansBits : 0u)) return WC_ERR_KRAFT;
+    }
     // code lengths: complete prefix code (Kraft sum exactly 1), or one 1-bit code
     const uint8_t* cl = b + h.off_code_len;
     uint64_t kraft = 0;
     uint32_t present = 0, longest = 0;
-    for (int s = 0; s < 256; ++s) {
+    for (int s = 0; s < 256 && !rans; ++s) {
         if (!cl[s]) continue;
         if (cl[s] > h.max_code_len) return WC_ERR_CODE_LENGTHS;
         kraft += 1ull << (wc::kMaxCodeLen - cl[s]);
         ++present;
         longest = std::max<uint32_t>(longest, cl[s]);
     }
-    if (present == 0 && h.n_elems) return WC_ERR_CODE_LENGTHS;
+    if (!rans && present == 0 && h.n_elems) return WC_ERR_CODE_LENGTHS;
     if (present >= 2 && kraft != (1ull << wc::kMaxCodeLen)) return WC_ERR_KRAFT;
     if (present == 1 && longest != 1) return WC_ERR_KRAFT;
 
@@ -160,7 +186,8 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
         const uint64_t p1 = load_le<uint64_t>(gt + wc::kGroupEntryBytes * g + 8);
         if (e1 <= e0 || p1 <= p0 || e1 > h.n_elems || p1 > h.stream_bits) return WC_ERR_GROUP_START;
         if (g < h.n_groups && e1 % h.group_align) return WC_ERR_GROUP_START;
-        if (e1 - e0 > p1 - p0 || e1 - e0 > h.group_max_elems) return WC_ERR_GROUP_START;
+        if ((!rans && e1 - e0 > p1 - p0) || e1 - e0 > h.group_max_elems) return WC_ERR_GROUP_START;
+        if (rans && p1 % 16) return WC_ERR_GROUP_START;
         if (lanes ? p1 - p0 > h.seg_max_bits : wc::chunk_span(p0, p1) > h.chunks_per_group)
             return WC_ERR_GROUP_START;
         if (lanes) {
@@ -169,7 +196,9 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
             const uint8_t* lo = gap + 2ull * wc::kLanes * (g - 1);
             if (load_le<uint16_t>(lo) != 0) return WC_ERR_GAP;
             for (uint32_t j = 1; j < wc::kLanes; ++j)
-                if (load_le<uint16_t>(lo + 2 * j) < load_le<uint16_t>(lo + 2 * (j - 1))) return WC_ERR_GAP;
+                if (load_le<uint16_t>(lo + 2 * j) < load_le<uint16_t>(lo + 2 * (j - 1)) ||
+                    (rans && load_le<uint16_t>(lo + 2 * j) % 16))
+                    return WC_ERR_GAP;
             if (load_le<uint16_t>(lo + 2 * (wc::kLanes - 1)) > p1 - p0) return WC_ERR_GAP;
         }
         max_group_elems = std::max(max_group_elems, e1 - e0);
@@ -251,10 +280,11 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
             p->tensor_g1[k] = groups_le(e - 1);
         }
     }
+    p->rans = p->h.coder == wc::kCoderRans;
     p->count_bits = env_u32("WC_COUNT_BITS", 12);
     p->decode_bits = env_u32("WC_DECODE_BITS", 11);
-    if (!wc::supported_table_bits(p->count_bits, p->decode_bits)) {
-        p->count_bits = 12;
+    if (!wc::supported_table_bits(p->count_bits, p->decode_bits) || p->rans) {
+        p->count_bits = 12;   // rANS: the 2^12-slot table takes the place of the 11-bit multi-codeword table
         p->decode_bits = 11;
     }
     p->waves = env_u32("WC_WAVES", 4);
@@ -266,7 +296,7 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
     // Long codes: canonical codes longer than the decode-table index all have
     // index-bit prefixes >= F = (first code of length decode_bits + 1) / 2; the
     // second-level table is staged for min(2^decode_bits - F, kL2Prefixes) of them.
-    {
+    if (!p->rans) {
         const uint8_t* len = blob_host + p->h.off_code_len;
         uint64_t count[33] = {0};
         for (int sym = 0; sym < 256; ++sym)
@@ -295,7 +325,7 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         delete p;
         return WC_ERR_HIP;
     }
-    int per_cu = lanes ? wc::decode_lanes_blocks_per_cu(p->decode_bits, p->waves, p->l2_cap)
+    int per_cu = lanes ? wc::decode_lanes_blocks_per_cu(p->decode_bits, p->waves, p->l2_cap, p->rans)
                        : wc::decode_blocks_per_cu(p->count_bits, p->decode_bits, p->waves, p->ebuf_bytes, p->l2_cap);
     // The persistent grid must be co-resident.  LDS is handed out in granules of
     // 1/128 of a compute unit's LDS (1,280 bytes of 160 KiB on gfx950), which the
@@ -330,10 +360,25 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         delete p;
         return WC_ERR_NOMEM;
     }
-    wc::CodeLens lens;
-    std::memcpy(lens.len, blob_host + p->h.off_code_len, 256);
-    if (wc::launch_build_tables(lens, p->count_bits, p->decode_bits, p->d_tables, nullptr) != hipSuccess ||
-        hipStreamSynchronize(nullptr) != hipSuccess) {
+    hipError_t te;
+    if (p->rans) {
+        // slot t of [0, 2^12): the symbol s with cum[s] <= t < cum[s] + f[s],
+        // stored rotated as the Huffman tables store it, | (f - 1) << 8 |
+        // (t - cum[s]) << 20; at the multi-codeword table's place
+        std::vector<uint32_t> host(tbytes / 4, 0u);
+        uint32_t* entries = host.data() + (1u << p->count_bits);
+        for (uint32_t sym = 0, t = 0; sym < 256; ++sym) {
+            const uint32_t f = load_le<uint16_t>(blob_host + p->h.off_code_len + 2 * sym);
+            const uint32_t rot = ((sym >> 1) | (sym << 7)) & 0xFFu;
+            for (uint32_t r = 0; r < f; ++r, ++t) entries[t] = rot | (f - 1) << 8 | r << 20;
+        }
+        te = hipMemcpy(p->d_tables, host.data(), tbytes, hipMemcpyHostToDevice);
+    } else {
+        wc::CodeLens lens;
+        std::memcpy(lens.len, blob_host + p->h.off_code_len, 256);
+        te = wc::launch_build_tables(lens, p->count_bits, p->decode_bits, p->d_tables, nullptr);
+    }
+    if (te != hipSuccess || hipStreamSynchronize(nullptr) != hipSuccess) {
         (void)hipFree(p->d_tables);
         delete p;
         return WC_ERR_HIP;
@@ -393,7 +438,7 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
         // the lane offsets sit where the gaps do; the kernel stages the tables
         // from the multi-codeword table on
         d.tables = p->d_tables + (1u << p->count_bits);
-        e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, p->grid, wc::kLanesToBf16,
+        e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, p->grid, wc::kLanesToBf16, p->rans,
                                     static_cast<hipStream_t>(stream));
     } else {
         e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, p->grid, false,
@@ -425,15 +470,16 @@ extern "C" int wc_decode_u8_async(const wc_plan_t* p, const void* blob_dev, uint
     d.u_end = p->h.n_groups;
     d.ebuf_bytes = p->ebuf_bytes;
     d.l2_cap = p->l2_cap;
-    const hipError_t e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, p->grid, wc::kLanesToU8,
+    const hipError_t e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, p->grid, wc::kLanesToU8, p->rans,
                                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
 }
 
-extern "C" int wc_plan_format(const wc_plan_t* p, uint32_t* version, uint32_t* elem_kind) {
+extern "C" int wc_plan_format(const wc_plan_t* p, uint32_t* version, uint32_t* elem_kind, uint32_t* coder) {
     if (!p) return WC_ERR_INVALID_ARG;
     if (version) *version = p->h.version;
     if (elem_kind) *elem_kind = p->h.elem_kind;
+    if (coder) *coder = p->h.coder;
     return WC_OK;
 }
 
@@ -528,7 +574,7 @@ extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, co
     hipError_t e;
     if (p->lanes) {
         d.tables = p->d_tables + (1u << p->count_bits);
-        e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, grid, wc::kLanesToDot, s);
+        e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, grid, wc::kLanesToDot, p->rans, s);
     } else {
         e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, grid, true, s);
     }

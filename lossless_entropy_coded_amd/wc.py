@@ -35,7 +35,7 @@ class EncodeOpts(ctypes.Structure):
     _fields_ = [("max_code_len", ctypes.c_uint32), ("chunk_bytes", ctypes.c_uint32),
                 ("chunks_per_group", ctypes.c_uint32), ("n_threads", ctypes.c_uint32),
                 ("group_align", ctypes.c_uint32), ("group_max_elems", ctypes.c_uint32),
-                ("layout", ctypes.c_uint32), ("seg_max_bits", ctypes.c_uint32)]
+                ("layout", ctypes.c_uint32), ("seg_max_bits", ctypes.c_uint32), ("coder", ctypes.c_uint32)]
 
 
 _lib.wc_encode_host.argtypes = [ctypes.POINTER(_u16p), _u64p, ctypes.c_uint32, ctypes.POINTER(EncodeOpts),
@@ -56,7 +56,7 @@ _lib.wc_decode_async.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void
 _lib.wc_decode_async.restype = ctypes.c_int
 _lib.wc_decode_u8_async.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
 _lib.wc_decode_u8_async.restype = ctypes.c_int
-_lib.wc_plan_format.argtypes = [ctypes.c_void_p, _u32p, _u32p]
+_lib.wc_plan_format.argtypes = [ctypes.c_void_p, _u32p, _u32p, _u32p]
 _lib.wc_plan_format.restype = ctypes.c_int
 _lib.wc_gemv_bf16_async.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p]
@@ -106,6 +106,9 @@ GROUP_MAX_ELEMS = 4096
 # GPU decoder stages a segment's stream (at most 1984 bytes) in LDS.
 SEG_MAX_BITS = 15872
 LAYOUTS = {"lanes": 0, "chunks": 1}
+# Entropy coders of the interleaved-lane layout: canonical Huffman, or rANS
+# (12-bit frequencies, 32-bit state, 16-bit words; lanes layout only).
+CODERS = {"huffman": 0, "rans": 1}
 
 EXPORTED = ("wc_encode_host", "wc_encode_u8_host", "wc_free_host", "wc_plan", "wc_plan_info", "wc_plan_stats",
             "wc_plan_format", "wc_decode_u8_async",
@@ -144,19 +147,20 @@ def _as_u16(t) -> np.ndarray:
 def encode_host(tensors, max_code_len: int = 24, chunks_per_group: int = GROUP_CHUNKS,
                 n_threads: int = 0, group_align: int = GROUP_ALIGN,
                 group_max_elems: int = GROUP_MAX_ELEMS, layout: str = "lanes",
-                seg_max_bits: int = SEG_MAX_BITS) -> np.ndarray:
+                seg_max_bits: int = SEG_MAX_BITS, coder: str = "huffman") -> np.ndarray:
     """wc_encode_host over a list of bf16 tensors (numpy uint16 or torch CPU).
 
     layout: "lanes" (the default: container v3, interleaved lanes;
     seg_max_bits caps a segment's stream bits) or "chunks" (container v2,
-    per-chunk gaps; chunks_per_group applies).
+    per-chunk gaps; chunks_per_group applies).  coder: "huffman" or "rans"
+    (lanes only; max_code_len is then ignored).
     Returns the container as a numpy uint8 array (a copy of the library buffer)."""
     arrs = [_as_u16(t) for t in tensors]
     nt = len(arrs)
     ptrs = (_u16p * max(nt, 1))(*[a.ctypes.data_as(_u16p) for a in arrs])
     numels = (ctypes.c_uint64 * max(nt, 1))(*[a.size for a in arrs])
     opts = EncodeOpts(max_code_len, 8, chunks_per_group, n_threads, group_align, group_max_elems,
-                      LAYOUTS[layout], seg_max_bits)
+                      LAYOUTS[layout], seg_max_bits, CODERS[coder])
     out = _u8p()
     nbytes = ctypes.c_uint64(0)
     _check(_lib.wc_encode_host(ptrs, numels, nt, ctypes.byref(opts), ctypes.byref(out), ctypes.byref(nbytes)),
@@ -170,15 +174,17 @@ def encode_host(tensors, max_code_len: int = 24, chunks_per_group: int = GROUP_C
 
 
 def encode_u8_host(tensors, max_code_len: int = 24, n_threads: int = 0, group_align: int = GROUP_ALIGN,
-                   group_max_elems: int = GROUP_MAX_ELEMS, seg_max_bits: int = SEG_MAX_BITS) -> np.ndarray:
+                   group_max_elems: int = GROUP_MAX_ELEMS, seg_max_bits: int = SEG_MAX_BITS,
+                   coder: str = "huffman") -> np.ndarray:
     """wc_encode_u8_host over a list of uint8 code planes (numpy or torch CPU): a u8-kind
-    interleaved-lane container (each byte one symbol, no raw plane)."""
+    interleaved-lane container (each byte one symbol, no raw plane), Huffman or rANS."""
     arrs = [np.ascontiguousarray(t.numpy() if hasattr(t, "numpy") else t).reshape(-1).view(np.uint8)
             for t in tensors]
     nt = len(arrs)
     ptrs = (_u8p * max(nt, 1))(*[a.ctypes.data_as(_u8p) for a in arrs])
     numels = (ctypes.c_uint64 * max(nt, 1))(*[a.size for a in arrs])
-    opts = EncodeOpts(max_code_len, 8, 0, n_threads, group_align, group_max_elems, LAYOUTS["lanes"], seg_max_bits)
+    opts = EncodeOpts(max_code_len, 8, 0, n_threads, group_align, group_max_elems, LAYOUTS["lanes"], seg_max_bits,
+                      CODERS[coder])
     out = _u8p()
     nbytes = ctypes.c_uint64(0)
     _check(_lib.wc_encode_u8_host(ptrs, numels, nt, ctypes.byref(opts), ctypes.byref(out), ctypes.byref(nbytes)),
@@ -219,10 +225,11 @@ class Plan:
         return self._h
 
     def format(self):
-        """wc_plan_format: (container version, element kind: 0 bf16, 1 u8)."""
-        v, k = ctypes.c_uint32(), ctypes.c_uint32()
-        _check(_lib.wc_plan_format(self.handle, ctypes.byref(v), ctypes.byref(k)), "wc_plan_format")
-        return v.value, k.value
+        """wc_plan_format: (container version, element kind: 0 bf16, 1 u8, coder: 0 Huffman, 1 rANS)."""
+        v, k, c = ctypes.c_uint32(), ctypes.c_uint32(), ctypes.c_uint32()
+        _check(_lib.wc_plan_format(self.handle, ctypes.byref(v), ctypes.byref(k), ctypes.byref(c)),
+               "wc_plan_format")
+        return v.value, k.value, c.value
 
     def stats(self) -> dict:
         cb, sb, ng = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()

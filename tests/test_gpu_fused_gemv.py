@@ -85,6 +85,13 @@ def _check_tensor(oracle_lib, got, W, x, align):
     assert bad.size == 0, f"rows {bad[:8]} off by {err[bad[:8]]} > {bound[bad[:8]]}"
 
 
+# the container variants the fused product runs on: Huffman in interleaved
+# lanes, Huffman in chunks, rANS in interleaved lanes (whose segments are also
+# runs of whole blocks, so the same bound holds)
+ENCODINGS = {"lanes": {"layout": "lanes"}, "chunks": {"layout": "chunks"},
+             "rans": {"layout": "lanes", "coder": "rans"}}
+
+
 # (block size A, group cap M, tensors as (rows, cols) or (n,) vectors); every
 # tensor offset is a multiple of 8 and most are not multiples of A, so groups
 # straddle tensors and rows.
@@ -97,7 +104,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("layout", ["lanes", "chunks"])
+@pytest.mark.parametrize("layout", ["lanes", "chunks", "rans"])
 @pytest.mark.parametrize("name,align,cap,shapes", CASES, ids=[c[0] for c in CASES])
 def test_fused_against_oracle(wc, oracle_lib, name, align, cap, shapes, layout):
     """Each matrix alone, then every run of consecutive matrices in one call:
@@ -109,7 +116,7 @@ def test_fused_against_oracle(wc, oracle_lib, name, align, cap, shapes, layout):
     for s in shapes:
         n = int(np.prod(s))
         tensors.append(f32_to_bf16_rne(rng.standard_normal(n, dtype=np.float32) * np.float32(0.02)))
-    blob = wc.encode_host(tensors, group_align=align, group_max_elems=cap, layout=layout)
+    blob = wc.encode_host(tensors, group_align=align, group_max_elems=cap, **ENCODINGS[layout])
     W_all = oracle_lib.decode(blob)
     assert np.array_equal(W_all, np.concatenate(tensors))
     with wc.Plan(blob) as plan:
@@ -145,14 +152,14 @@ def test_fused_against_oracle(wc, oracle_lib, name, align, cap, shapes, layout):
                 assert np.array_equal(y, alone[k]), f"tensor {k}: one-call result differs from the per-matrix call"
 
 
-@pytest.mark.parametrize("layout", ["lanes", "chunks"])
+@pytest.mark.parametrize("layout", ["lanes", "chunks", "rans"])
 @pytest.mark.parametrize("name,rows", [("heavy_tail_14k", 96), ("block_8b", 40), ("block_70b", 24)])
 def test_fused_on_workload_shapes(wc, oracle_lib, name, rows, layout):
     """The block workloads, truncated to a few rows per matrix: all matrices
     of the block in one fused call, against the oracle."""
     from lossless_entropy_coded_amd.synth import gemv_input, make_workload
     wl = make_workload(name, scale_rows=rows)
-    blob = wc.encode_host(wl.tensors(), layout=layout)
+    blob = wc.encode_host(wl.tensors(), **ENCODINGS[layout])
     with wc.Plan(blob) as plan:
         f = Fused(wc, blob, plan)
         mats = [k for k, s in enumerate(wl.shapes) if len(s) == 2]
@@ -165,14 +172,14 @@ def test_fused_on_workload_shapes(wc, oracle_lib, name, rows, layout):
             _check_tensor(oracle_lib, got, wl.bits[off:off + r * c].reshape(r, c), gemv_input(c), wc.GROUP_ALIGN)
 
 
-@pytest.mark.parametrize("layout", ["lanes", "chunks"])
+@pytest.mark.parametrize("layout", ["lanes", "chunks", "rans"])
 def test_fused_full_block_8b_sampled(wc, oracle_lib, layout):
     """The full 8B-shape block (the size the benchmark decodes): its 7
     matrices in one fused call; 48 sampled rows per matrix (first, last and
     random) against the oracle's GEMV of the generated weights."""
     from lossless_entropy_coded_amd.synth import gemv_input, make_workload
     wl = make_workload("block_8b")
-    blob = wc.encode_host(wl.tensors(), layout=layout)
+    blob = wc.encode_host(wl.tensors(), **ENCODINGS[layout])
     rng = np.random.default_rng(8)
     with wc.Plan(blob) as plan:
         f = Fused(wc, blob, plan)

@@ -24,7 +24,7 @@ def wc():
 def gpu_decode_u8(wc, blob, stream=None):
     import torch
     with wc.Plan(blob) as plan:
-        assert plan.format() == (3, 1)
+        assert plan.format()[:2] == (3, 1)
         _, dblob = to_device_aligned(blob)
         buf = torch.full((plan.n_elems + 2 * GUARD,), CANARY, dtype=torch.uint8, device="cuda")
         out = buf[GUARD:GUARD + plan.n_elems]
@@ -117,7 +117,7 @@ def test_u8_kind_checks(wc):
             wc.decode_async(plan, out, out)
         assert ei.value.status == wc.WC_ERR_INVALID_ARG
     with wc.Plan(wc.encode_host([w])) as plan:
-        assert plan.format() == (3, 0)
+        assert plan.format() == (3, 0, 0)
         out = torch.zeros(8192, dtype=torch.uint8, device="cuda")
         with pytest.raises(wc.WCError) as ei:
             wc.decode_u8_async(plan, out, out)

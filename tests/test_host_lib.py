@@ -335,3 +335,92 @@ def test_plan_checks_element_kind(wc):
         wc._check(wc._lib.wc_encode_u8_host(arr, num, 1, ctypes.byref(opts), ctypes.byref(out), ctypes.byref(nb)),
                   "wc_encode_u8_host")
     assert ei.value.status == wc.WC_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("A,M,B", [(128, 4096, 15872), (64, 1024, 4096), (8, 512, 2200), (8, 4096, 65535)])
+def test_rans_encoder_matches_oracle_writer(wc, oracle_lib, A, M, B):
+    """The product's rANS writer (bf16 and u8 kinds) is byte-identical to the
+    oracle's, for any thread count."""
+    from lossless_entropy_coded_amd.synth import make_code_workload, make_workload
+    wl = make_workload("block_8b", scale_rows=24)
+    a = wc.encode_host(wl.tensors(), group_align=A, group_max_elems=M, seg_max_bits=B, coder="rans")
+    b = oracle_lib.encode_lanes_rans(wl.bits, numels=wl.numels, group_align=A, group_max_elems=M, seg_max_bits=B)
+    assert np.array_equal(a, b)
+    for n_threads in (1, 3):
+        assert np.array_equal(wc.encode_host(wl.tensors(), group_align=A, group_max_elems=M, seg_max_bits=B,
+                                             coder="rans", n_threads=n_threads), a)
+    cw = make_code_workload("int4_codes_8b", scale_rows=24)
+    a8 = wc.encode_u8_host(cw.tensors(), group_align=A, group_max_elems=M, seg_max_bits=B, coder="rans")
+    b8 = oracle_lib.encode_lanes_rans_u8(cw.codes, numels=cw.numels, group_align=A, group_max_elems=M,
+                                         seg_max_bits=B)
+    assert np.array_equal(a8, b8)
+
+
+def test_rans_encoder_edge_inputs(wc, oracle_lib):
+    rng = np.random.default_rng(21)
+    cases = [np.zeros(0, np.uint16), np.array([0x3F80], np.uint16), np.full(5000, 0x3F80, np.uint16),
+             np.arange(65536, dtype=np.uint32).astype(np.uint16), rng.integers(0, 65536, 777).astype(np.uint16)]
+    for w in cases:
+        a = wc.encode_host([w], coder="rans")
+        assert np.array_equal(a, oracle_lib.encode_lanes_rans(w))
+        assert np.array_equal(oracle_lib.decode(a), w)
+    # several tensors, some empty, one codebook
+    parts = [rng.integers(0, 65536, n).astype(np.uint16) for n in (0, 13, 0, 4096, 1)]
+    a = wc.encode_host(parts, coder="rans")
+    assert np.array_equal(oracle_lib.decode(a), np.concatenate(parts))
+
+
+def test_rans_encoder_rejects_bad_options(wc):
+    w = np.arange(10, dtype=np.uint16)
+    for kw in ({"seg_max_bits": 2047}, {"seg_max_bits": 70000}, {"group_align": 128, "seg_max_bits": 3599},
+               {"layout": "chunks"}):
+        with pytest.raises(wc.WCError) as ei:
+            wc.encode_host([w], coder="rans", **kw)
+        assert ei.value.status == wc.WC_ERR_INVALID_ARG
+    # 97 A <= 8 (B - 2048) exactly at the limit is accepted
+    assert wc.encode_host([w], coder="rans", group_align=8, group_max_elems=512, seg_max_bits=2048 + 97).size > 0
+
+
+def test_plan_rejects_each_rans_fault(wc, oracle_lib):
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload("matrix_1k", scale_rows=128)
+    blob = wc.encode_host(wl.tensors(), coder="rans")
+    s = sections(blob)
+    ok = (wc.WC_OK, wc.WC_ERR_HIP)
+    assert s["coder"] == 1 and s["n_groups"] >= 3
+    assert _plan_status(wc, blob) in ok
+
+    def mutated(fn):
+        b = blob.copy()
+        fn(b)
+        return _plan_status(wc, b)
+
+    def setb(off, val):
+        return lambda b: b.__setitem__(slice(off, off + len(val)), val)
+
+    u16 = lambda v: np.frombuffer(np.uint16(v).tobytes(), np.uint8)
+    assert mutated(setb(125, np.array([2], np.uint8))) == wc.WC_ERR_BAD_MAGIC             # unknown coder
+    assert mutated(setb(8, np.array([11], np.uint8))) == wc.WC_ERR_BAD_MAGIC              # P must be 12
+    assert mutated(setb(12, np.array([0, 8, 0, 0], np.uint8))) == wc.WC_ERR_BAD_MAGIC     # B = 2048: no room
+    fo = s["off_len"]
+    top = int(np.argmax(s["freq"]))
+    assert mutated(setb(fo + 2 * top, u16(int(s["freq"][top]) + 1))) == wc.WC_ERR_KRAFT  # sum 4097
+    assert mutated(setb(fo + 2 * top, u16(4097))) == wc.WC_ERR_CODE_LENGTHS
+    assert mutated(setb(32, _u64(s["stream_bits"] + 8))) in (wc.WC_ERR_STREAM_BITS,)    # not whole words
+    lo = s["off_gap"]
+    v = int(s["lane_off"][0, 10])
+    assert mutated(setb(lo + 2 * 10, u16(v + 8))) == wc.WC_ERR_GAP                       # not a word boundary
+    assert mutated(setb(lo + 2 * 11, u16(v - 16))) == wc.WC_ERR_GAP                      # decreasing
+    b1 = s["off_gs"] + 24                                                                 # segment 1's first bit
+    assert mutated(setb(b1, _u64(int(s["groups"][1, 1]) + 8))) == wc.WC_ERR_GROUP_START
+    # a Huffman container with its coder byte set is not an rANS container
+    h = wc.encode_host(wl.tensors())
+    h[125] = 1
+    assert _plan_status(wc, h) != wc.WC_OK
+    v2 = wc.encode_host(wl.tensors(), layout="chunks")
+    v2[125] = 1                                                                            # version 2: Huffman only
+    assert _plan_status(wc, v2) == wc.WC_ERR_BAD_MAGIC
+    # containers written by the oracle pass every check; the u8 kind too
+    assert _plan_status(wc, oracle_lib.encode_lanes_rans(wl.bits, numels=wl.numels)) in ok
+    c = (np.arange(5000) % 7).astype(np.uint8)
+    assert _plan_status(wc, wc.encode_u8_host([c], coder="rans")) in ok
