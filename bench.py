@@ -85,12 +85,18 @@ def parse_args():
                          "chunks (v2, per-chunk gaps)")
     ap.add_argument("--coder", choices=["huffman", "rans"], default="huffman",
                     help="entropy coder of the lanes layout: huffman (the default) or rans")
+    ap.add_argument("--max-code-len", type=int, default=0,
+                    help="Huffman code length limit for the encoder (0: the library's default)")
     ap.add_argument("--e2e", action="store_true",
                     help="70B-shape block end to end: decode + batch-1 GEMVs against GEMVs on resident "
                          "uncompressed weights (prints its own JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device copy instead (for scaling HBM counters)")
     return ap.parse_args()
+
+
+def code_len_opt(args) -> dict:
+    return {"max_code_len": args.max_code_len} if args.max_code_len else {}
 
 
 def aligned_device_copy(torch, blob, align=256):
@@ -176,7 +182,7 @@ def end_to_end(args):
 
     name = args.workload if args.workload != "block_8b" else "block_70b"
     wl = make_workload(name)
-    blob = wc.encode_host(wl.tensors(), layout=args.layout)
+    blob = wc.encode_host(wl.tensors(), layout=args.layout, coder=args.coder, **code_len_opt(args))
     plan = wc.Plan(blob, device=0)
     n = wl.n
     mats = [(k, s[0], s[1]) for k, s in enumerate(wl.shapes) if len(s) == 2]
@@ -204,14 +210,14 @@ def end_to_end(args):
             wc.gemv_bf16_async(src[off:off + r * c], r, c, xs[c], ys[j], stream)
 
     def arm_a(k):
-        decode(plan, blobs[k % copies], outs[k % copies], stream)
+        wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
         gemvs(outs[k % copies], ya)
 
     def arm_b(k):
         gemvs(origs[k % copies], yb)
 
     def decode_only(k):
-        decode(plan, blobs[k % copies], outs[k % copies], stream)
+        wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
 
     def arm_c(k):
         wc.decode_gemv_async(plan, blobs[k % copies], ops, work, work_bytes, stream)
@@ -247,7 +253,7 @@ def end_to_end(args):
         "data": "synthetic: seeded bf16 weights (70B-block shapes, N(0, 0.015)), x ~ N(0, 1) in bf16",
         "config": {"workload": f"{name}: decode of the whole block, then q,k,v,o,gate,up,down GEMVs "
                                f"(x length = each matrix's in-dimension)",
-                   "layout": args.layout, "n_elems": n, "container_bytes": int(blob.size),
+                   "layout": args.layout, "coder": args.coder, "n_elems": n, "container_bytes": int(blob.size),
                    "weight_bytes": weight_bytes},
         "arm_a_decode_plus_gemv_ms": round(ms_a, 4),
         "arm_b_uncompressed_gemv_ms": round(ms_b, 4),
@@ -297,11 +303,11 @@ def main():
     t_gen = time.perf_counter()
     if codes:
         wl = make_code_workload(args.workload)
-        blob = wc.encode_u8_host(wl.tensors(), coder=args.coder)
+        blob = wc.encode_u8_host(wl.tensors(), coder=args.coder, **code_len_opt(args))
         raw, out_bytes, out_dtype, decode = wl.codes, 1, torch.uint8, wc.decode_u8_async
     else:
         wl = make_workload(args.workload)
-        blob = wc.encode_host(wl.tensors(), layout=args.layout, coder=args.coder)
+        blob = wc.encode_host(wl.tensors(), layout=args.layout, coder=args.coder, **code_len_opt(args))
         raw, out_bytes, out_dtype, decode = wl.bits.view(np.int16), 2, torch.int16, wc.decode_async
     t_gen = time.perf_counter() - t_gen
     n = wl.n
@@ -420,6 +426,7 @@ def main():
             "workload": f"{args.workload}: {desc}",
             "layout": args.layout,
             "coder": args.coder,
+            "max_code_len": args.max_code_len or None,
             "n_elems": n,
             "n_tensors": len(wl.numels),
             "container_bytes": int(blob.size),

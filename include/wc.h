@@ -126,7 +126,8 @@ extern "C" {
 
 /* ---- host encoder ------------------------------------------------------ */
 typedef struct {
-    uint32_t max_code_len;      /* 1..24; 0 selects the default 24                      */
+    uint32_t max_code_len;      /* 1..24; 0 selects the default: 24 for bf16 weights,   */
+                                /* 11 for code planes (wc_encode_u8_host)               */
     uint32_t chunk_bytes;       /* must be 8 (or 0 for the default)                     */
     uint32_t chunks_per_group;  /* G >= 1; 0 selects the default 128.  The GPU decoder  */
                                 /* of this build accepts only G = 128.                  */
@@ -174,6 +175,8 @@ int wc_encode_host(const uint16_t* const* tensors, const uint64_t* numels, uint3
  * (element kind u8): each byte is a symbol of one shared canonical code; the
  * container is the interleaved-lane layout (opts->layout must be
  * WC_LAYOUT_LANES) with no raw plane.  tensors[k] points to numels[k] bytes.
+ * Codes are limited to 11 bits unless opts->max_code_len says otherwise: the
+ * GPU decoder's table width, so that no code needs its slower long-code path.
  * Decode with wc_decode_u8_async.
  */
 int wc_encode_u8_host(const uint8_t* const* tensors, const uint64_t* numels, uint32_t n_tensors,

@@ -46,8 +46,6 @@
 namespace wc {
 namespace {
 
-constexpr uint32_t kStageWords = kLaneStageBytes / 4;
-constexpr uint32_t kStageHalves = kLaneStageBytes / 2;
 constexpr uint32_t kRansSlots = 1u << kRansBits;
 
 // One lane's loads for one segment: its two 16-byte pieces of the segment's
@@ -162,6 +160,9 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
     lt.l2_n = min(__builtin_amdgcn_readfirstlane(s_long[161]), p.l2_cap);
     m_next = uniform_meta(m_next);
     uint32_t dot_mat = 0;   // fused product: matrix of the wave's current segment
+    // rANS with one symbol: its frequency 2^12 is stored as 0
+    const bool rans_single =
+        kRans && ((__builtin_amdgcn_readfirstlane(reinterpret_cast<const uint32_t*>(s_tab)[0]) >> 8) & 0xFFFu) == 0;
 
     for (;;) {
         const uint64_t un = u + stride;
@@ -212,59 +213,91 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
             if (cnt && lane == (nb8 - 1) % kWaveLanes) nsym -= kLaneBlock * nb8 - n;
             const uint32_t pos = (uint32_t)(cur_m.p0 & 127u) + off;   // first bit in the staged words
             if constexpr (kRans) {
-                // the final state, then one symbol per step, four per slot
-                // store; a lane whose count is not a multiple of four decodes
-                // up to three more (from whatever words follow, indexes
-                // clamped) into the slot's spare bytes
+                // the final state, then one symbol per step, eight per slot
+                // store (a lane whose count is not a multiple of eight decodes
+                // up to seven more into the slot's unused bytes).  Reads stay
+                // in the wave's LDS region unclamped: the planner bounds every
+                // lane offset by the segment's bits (<= 15872), so the first
+                // half-word is at most 999, and a lane takes at most 64 steps
+                // and one word per step: at most half-word 1065, byte 2131 of
+                // the wave's 2048 staging and 4608 slot bytes.
                 const uint16_t* const s16 = reinterpret_cast<const uint16_t*>(sbuf);
                 const uint32_t* const s_slot = reinterpret_cast<const uint32_t*>(s_tab);
-                uint32_t q = min(pos >> 4, kStageHalves - 2);
-                uint32_t x = (uint32_t)s16[q] << 16 | s16[q + 1];
-                q += 2;
-                for (uint32_t p = 0; p < nsym; p += 4) {
-                    uint32_t four = 0;
+                if (rans_single) {
+                    // one symbol of frequency 2^12: the state never moves
+                    const uint32_t v = (s_slot[0] & 0xFFu) * 0x01010101u;
+                    for (uint32_t p = 0; p < nsym; p += kMergeElems)
+                        *reinterpret_cast<uint2*>(slot + p) = make_uint2(v, v);
+                } else {
+                    uint32_t q = pos >> 4;
+                    uint32_t x = (uint32_t)s16[q] << 16 | s16[q + 1];
+                    q += 2;
+                    for (uint32_t p = 0; p < nsym; p += kMergeElems) {
+                        uint32_t e[kMergeElems];
 #pragma unroll
-                    for (uint32_t i = 0; i < 4; ++i) {
-                        const uint32_t w = s16[min(q, kStageHalves - 1)];
-                        const uint32_t e = s_slot[x & (kRansSlots - 1)];
-                        const uint32_t hi = x >> kRansBits;
-                        x = __umul24((e >> 8) & 0xFFFu, hi) + hi + (e >> 20);   // f (x >> 12) + slot - cum
-                        const bool in = x < kRansLow;
-                        x = in ? x << 16 | w : x;
-                        q += in ? 1u : 0u;
-                        four |= (e & 0xFFu) << (8 * i);
+                        for (uint32_t i = 0; i < kMergeElems; ++i) {
+                            const uint32_t w = s16[q];
+                            e[i] = s_slot[x & (kRansSlots - 1)];
+                            // f (x >> 12) + slot - cum
+                            x = __umul24((e[i] >> 8) & 0xFFFu, x >> kRansBits) + (e[i] >> 20);
+                            const bool in = x < kRansLow;
+                            x = in ? x << 16 | w : x;
+                            q += in ? 1u : 0u;
+                        }
+                        // the symbols are the entries' low bytes
+                        const uint32_t s0 = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0400u) |
+                                            __builtin_amdgcn_perm(e[3], e[2], 0x04000C0Cu);
+                        const uint32_t s1 = __builtin_amdgcn_perm(e[5], e[4], 0x0C0C0400u) |
+                                            __builtin_amdgcn_perm(e[7], e[6], 0x04000C0Cu);
+                        *reinterpret_cast<uint2*>(slot + p) = make_uint2(s0, s1);
                     }
-                    *reinterpret_cast<uint32_t*>(slot + p) = four;
                 }
             } else {
-                uint32_t wi = pos >> 5;
-                uint64_t win = (((uint64_t)sbuf[wi] << 32) | sbuf[wi + 1]) << (pos & 31u);
-                int32_t valid = 64 - (int32_t)(pos & 31u);
-                wi += 2;
-                // a lookup's symbols past the lane's last one (they belong to the
-                // next lane) land in the slot's spare bytes: p < nsym <= 64 before
-                // the store, so it ends by byte 67
+                // each lookup re-reads its 32-bit window from the staged
+                // words: t = (bit position) - 1, words t >> 5 (arithmetic:
+                // -1 at position 0, the 4 bytes before the staging) and the
+                // next, shifted right by -position mod 32 (always below 32).
+                // A lookup's symbols past the lane's last one (they belong
+                // to the next lane) land in the slot's spare bytes: p < nsym
+                // <= 64 before the store, so it ends by byte 67.  The words
+                // stay in the wave's LDS region unclamped: the planner bounds
+                // every lane offset by the segment's bits (<= 15872), and a
+                // lane makes at most 64 lookups of at most 24 bits (at most
+                // word 548, byte 2195 of the wave's staging and slots).
+                int32_t t = (int32_t)pos - 1;
                 uint32_t p = 0;
+                // code planes (about one symbol per lookup): the symbols are
+                // gathered in a register and written as aligned words (the
+                // table's bytes past a lookup's symbols are 0); the last word
+                // ends by byte 67.  bf16 exponents (two to three symbols per
+                // lookup): four byte stores at the count decoded so far.
+                uint32_t acc = 0;
                 while (p < nsym) {
-                    const uint32_t top = (uint32_t)(win >> 32);
+                    const int32_t k = t >> 5;
+                    const uint32_t top = __builtin_amdgcn_alignbit(sbuf[k], sbuf[k + 1], ~(uint32_t)t);
                     uint2 e = s_dec[top >> (32 - KD)];
                     if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
-                    uint8_t* const dst = slot + p;
-                    const uint32_t odd = __builtin_amdgcn_perm(e.y, e.y, 0x0C030C01u);   // [s1, 0, s3, 0]
-                    dst[0] = (uint8_t)e.y;
-                    dst[1] = (uint8_t)odd;
-                    dst[2] = (uint8_t)(e.y >> 16);
-                    dst[3] = (uint8_t)(odd >> 16);
-                    p += (e.x >> 8) & 0xFFu;
-                    const uint32_t nbits = (e.x >> 16) & 0xFFu;
-                    win <<= nbits;
-                    valid -= (int32_t)nbits;
-                    if (valid < 32) {
-                        win |= (uint64_t)sbuf[min(wi, kStageWords - 1)] << (32 - valid);
-                        ++wi;
-                        valid += 32;
+                    const uint32_t pn = p + ((e.x >> 8) & 0xFFu);
+                    if constexpr (kU8) {
+                        const uint64_t comb = ((uint64_t)e.y << ((p & 3u) << 3)) | acc;
+                        if ((p ^ pn) >= 4u) {   // a word is complete
+                            *reinterpret_cast<uint32_t*>(slot + (p & ~3u)) = (uint32_t)comb;
+                            acc = (uint32_t)(comb >> 32);
+                        } else {
+                            acc = (uint32_t)comb;
+                        }
+                    } else {
+                        uint8_t* const dst = slot + p;
+                        const uint32_t odd = __builtin_amdgcn_perm(e.y, e.y, 0x0C030C01u);   // [s1, 0, s3, 0]
+                        dst[0] = (uint8_t)e.y;
+                        dst[1] = (uint8_t)odd;
+                        dst[2] = (uint8_t)(e.y >> 16);
+                        dst[3] = (uint8_t)(odd >> 16);
                     }
+                    p = pn;
+                    t += (int32_t)((e.x >> 16) & 0xFFu);
                 }
+                if (kU8 && (p & 3u)) *reinterpret_cast<uint32_t*>(slot + (p & ~3u)) = acc;
             }
         }
 

@@ -446,7 +446,8 @@ int encode_impl(const T* const* tensors, const uint64_t* numels, uint32_t n_tens
     *blob = nullptr;
     *blob_bytes = 0;
     if (n_tensors && (!tensors || !numels)) return WC_ERR_INVALID_ARG;
-    uint32_t max_len = kMaxCodeLen, group = kDefaultGroup, align = kDefaultAlign, max_elems = kDefaultMaxElems;
+    uint32_t max_len = kBf16 ? kMaxCodeLen : kDefaultCodeLenU8, group = kDefaultGroup, align = kDefaultAlign,
+             max_elems = kDefaultMaxElems;
     uint32_t nthreads = 0, kind = WC_LAYOUT_LANES, seg_bits = kDefaultSegBits, coder = WC_CODER_HUFFMAN;
     if (opts) {
         if (opts->max_code_len) max_len = opts->max_code_len;

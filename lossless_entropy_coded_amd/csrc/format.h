@@ -34,6 +34,12 @@ constexpr uint32_t kDefaultSegBits = 15872;   // stream bits per segment at most
 // quantized integer codes).
 constexpr uint32_t kKindBf16 = 0;
 constexpr uint32_t kKindU8 = 1;
+// Default code length limit of u8-kind (code plane) containers: the GPU
+// decoder's table index width, so that no code takes its slower long-code
+// path.  Wide alphabets of quantized codes have many long codes otherwise
+// (about 0.4% of int8 codes of spread 20 exceed 11 bits); the limit costs
+// them 0.3-0.6% in size.  bf16 exponents keep kMaxCodeLen.
+constexpr uint32_t kDefaultCodeLenU8 = 11;
 // Coders of a version-3 container: the canonical Huffman code, or rANS
 // (Llama2-7B page, abstract: ANS; the LazyWeights page compares the two).
 // rANS: kRansBits-bit quantized frequencies (u16[256] in place of the code

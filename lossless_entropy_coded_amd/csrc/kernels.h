@@ -152,7 +152,8 @@ hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t de
 // the decoded bytes themselves in p.out8 (u8-kind containers).
 // With rans, the lanes are rANS streams and p.tables holds the 2^12-entry
 // slot table in the multi-codeword table's place (decode_bits must be 11):
-// entry t = rotated symbol | (f - 1) << 8 | (t - cum) << 20.
+// entry t = rotated symbol | (f mod 2^12) << 8 | (t - cum) << 20 (f = 2^12,
+// stored as 0, only when one symbol has every slot).
 enum LanesOut : uint32_t { kLanesToBf16 = 0, kLanesToDot = 1, kLanesToU8 = 2 };
 uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap);
 uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap);

@@ -363,14 +363,14 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
     hipError_t te;
     if (p->rans) {
         // slot t of [0, 2^12): the symbol s with cum[s] <= t < cum[s] + f[s],
-        // stored rotated as the Huffman tables store it, | (f - 1) << 8 |
+        // stored rotated as the Huffman tables store it, | (f mod 2^12) << 8 |
         // (t - cum[s]) << 20; at the multi-codeword table's place
         std::vector<uint32_t> host(tbytes / 4, 0u);
         uint32_t* entries = host.data() + (1u << p->count_bits);
         for (uint32_t sym = 0, t = 0; sym < 256; ++sym) {
             const uint32_t f = load_le<uint16_t>(blob_host + p->h.off_code_len + 2 * sym);
             const uint32_t rot = ((sym >> 1) | (sym << 7)) & 0xFFu;
-            for (uint32_t r = 0; r < f; ++r, ++t) entries[t] = rot | (f - 1) << 8 | r << 20;
+            for (uint32_t r = 0; r < f; ++r, ++t) entries[t] = rot | (f & 0xFFFu) << 8 | r << 20;
         }
         te = hipMemcpy(p->d_tables, host.data(), tbytes, hipMemcpyHostToDevice);
     } else {

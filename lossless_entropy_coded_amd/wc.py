@@ -173,11 +173,12 @@ def encode_host(tensors, max_code_len: int = 24, chunks_per_group: int = GROUP_C
     return blob
 
 
-def encode_u8_host(tensors, max_code_len: int = 24, n_threads: int = 0, group_align: int = GROUP_ALIGN,
+def encode_u8_host(tensors, max_code_len: int = 0, n_threads: int = 0, group_align: int = GROUP_ALIGN,
                    group_max_elems: int = GROUP_MAX_ELEMS, seg_max_bits: int = SEG_MAX_BITS,
                    coder: str = "huffman") -> np.ndarray:
     """wc_encode_u8_host over a list of uint8 code planes (numpy or torch CPU): a u8-kind
-    interleaved-lane container (each byte one symbol, no raw plane), Huffman or rANS."""
+    interleaved-lane container (each byte one symbol, no raw plane), Huffman or rANS.
+    max_code_len 0 selects the library's default for code planes (11 bits)."""
     arrs = [np.ascontiguousarray(t.numpy() if hasattr(t, "numpy") else t).reshape(-1).view(np.uint8)
             for t in tensors]
     nt = len(arrs)

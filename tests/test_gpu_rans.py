@@ -150,7 +150,8 @@ def test_rans_u8_code_planes(wc, oracle_lib, name):
 
 def test_rans_corrupted_stream_stays_in_bounds(wc):
     """Flipped stream bits and states give wrong values but no write outside
-    the output and no fault (every index the kernel forms is clamped)."""
+    the output and no fault (the table index is 12 bits, and a lane's word
+    reads stay inside its wave's LDS region whatever the words hold)."""
     from container_view import sections
     from lossless_entropy_coded_amd.synth import make_workload
     wl = make_workload("block_8b", scale_rows=64)

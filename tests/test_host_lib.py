@@ -301,12 +301,18 @@ def test_plan_rejects_each_lanes_fault(wc, oracle_lib):
 @pytest.mark.parametrize("name,A,M,B", [("int8_codes_8b", 128, 4096, 15872), ("int4_codes_8b", 128, 4096, 15872),
                                         ("int8_codes_8b", 8, 512, 500), ("int4_codes_8b", 64, 1024, 4096)])
 def test_u8_encoder_matches_oracle_writer(wc, oracle_lib, name, A, M, B):
-    """The product's u8-kind writer is byte-identical to the oracle's."""
+    """The product's u8-kind writer is byte-identical to the oracle's, at the
+    product's default code length limit for code planes (11) and at 24."""
     from lossless_entropy_coded_amd.synth import make_code_workload
     wl = make_code_workload(name, scale_rows=24)
     a = wc.encode_u8_host(wl.tensors(), group_align=A, group_max_elems=M, seg_max_bits=B)
-    b = oracle_lib.encode_lanes_u8(wl.codes, numels=wl.numels, group_align=A, group_max_elems=M, seg_max_bits=B)
-    assert np.array_equal(a, b)
+    b = oracle_lib.encode_lanes_u8(wl.codes, numels=wl.numels, max_code_len=11, group_align=A, group_max_elems=M,
+                                   seg_max_bits=B)
+    assert np.array_equal(a, b) and sections(a)["code_len"].max() <= 11
+    a24 = wc.encode_u8_host(wl.tensors(), max_code_len=24, group_align=A, group_max_elems=M, seg_max_bits=B)
+    b24 = oracle_lib.encode_lanes_u8(wl.codes, numels=wl.numels, max_code_len=24, group_align=A, group_max_elems=M,
+                                     seg_max_bits=B)
+    assert np.array_equal(a24, b24)
     assert np.array_equal(oracle_lib.decode_u8(a), wl.codes)
     assert np.array_equal(wc.encode_u8_host(wl.tensors(), group_align=A, group_max_elems=M, seg_max_bits=B,
                                             n_threads=3), a)
