@@ -16,11 +16,14 @@
 //           the lookahead) arrive one iteration early as two 16-byte loads per
 //           lane and are written byte-swapped to the wave's LDS words, so that
 //           word k holds stream bits 32k .. 32k + 31 MSB-first;
-//   decode  each lane keeps a 64-bit MSB-first window of its bits (refilled
-//           one LDS word at a time, at least 32 bits valid before a lookup)
-//           and looks up the multi-codeword table (up to four symbols per
-//           lookup, as the chunked kernel); the symbols go to the lane's own
-//           LDS slot with four byte stores, at the count decoded so far;
+//   decode  each lane looks up the multi-codeword table (up to four symbols
+//           per lookup, as the chunked kernel) with a 32-bit window of its
+//           bits: for the plain decode from a 64-bit register window refilled
+//           one LDS word at a time; for the fused product and code planes,
+//           whose instructions bound them, re-read from the staged words at
+//           every lookup (no per-lane refill branch).  The symbols go to the
+//           lane's own LDS slot at the count decoded so far (code planes:
+//           gathered into aligned words);
 //   merge   as the chunked kernel: the sign+mantissa bytes (loaded while the
 //           lanes decode) and the staged exponents (lane i's k-th 8 bytes
 //           are block i + 64k) become bf16 in registers, written with
@@ -46,6 +49,7 @@
 namespace wc {
 namespace {
 
+constexpr uint32_t kStageWords = kLaneStageBytes / 4;
 constexpr uint32_t kRansSlots = 1u << kRansBits;
 
 // One lane's loads for one segment: its two 16-byte pieces of the segment's
@@ -252,8 +256,42 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
                         *reinterpret_cast<uint2*>(slot + p) = make_uint2(s0, s1);
                     }
                 }
+            } else if constexpr (kMode == kLanesToBf16) {
+                // plain decode (bound by HBM): a 64-bit MSB-first register
+                // window of the lane's bits, at least 32 valid before a
+                // lookup, refilled one staged word at a time (index clamped
+                // to the staging).  A lookup's symbols past the lane's last
+                // one (they belong to the next lane) land in the slot's spare
+                // bytes: p < nsym <= 64 before the store, so it ends by byte 67
+                uint32_t wi = pos >> 5;
+                uint64_t win = (((uint64_t)sbuf[wi] << 32) | sbuf[wi + 1]) << (pos & 31u);
+                int32_t valid = 64 - (int32_t)(pos & 31u);
+                wi += 2;
+                uint32_t p = 0;
+                while (p < nsym) {
+                    const uint32_t top = (uint32_t)(win >> 32);
+                    uint2 e = s_dec[top >> (32 - KD)];
+                    if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
+                    uint8_t* const dst = slot + p;
+                    const uint32_t odd = __builtin_amdgcn_perm(e.y, e.y, 0x0C030C01u);   // [s1, 0, s3, 0]
+                    dst[0] = (uint8_t)e.y;
+                    dst[1] = (uint8_t)odd;
+                    dst[2] = (uint8_t)(e.y >> 16);
+                    dst[3] = (uint8_t)(odd >> 16);
+                    p += (e.x >> 8) & 0xFFu;
+                    const uint32_t nbits = (e.x >> 16) & 0xFFu;
+                    win <<= nbits;
+                    valid -= (int32_t)nbits;
+                    if (valid < 32) {
+                        win |= (uint64_t)sbuf[min(wi, kStageWords - 1)] << (32 - valid);
+                        ++wi;
+                        valid += 32;
+                    }
+                }
             } else {
-                // each lookup re-reads its 32-bit window from the staged
+                // fused product and code planes (bound by the decode's
+                // instructions and LDS): no register window; each lookup
+                // re-reads its 32-bit window from the staged
                 // words: t = (bit position) - 1, words t >> 5 (arithmetic:
                 // -1 at position 0, the 4 bytes before the staging) and the
                 // next, shifted right by -position mod 32 (always below 32).
@@ -269,8 +307,9 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
                 // code planes (about one symbol per lookup): the symbols are
                 // gathered in a register and written as aligned words (the
                 // table's bytes past a lookup's symbols are 0); the last word
-                // ends by byte 67.  bf16 exponents (two to three symbols per
-                // lookup): four byte stores at the count decoded so far.
+                // ends by byte 67.  bf16 exponents for the fused product (two
+                // to three symbols per lookup): four byte stores at the count
+                // decoded so far.
                 uint32_t acc = 0;
                 while (p < nsym) {
                     const int32_t k = t >> 5;
