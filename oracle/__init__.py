@@ -55,6 +55,7 @@ class Report(ctypes.Structure):
         ("seg_max_bits", ctypes.c_uint32),
         ("elem_kind", ctypes.c_uint32),
         ("coder", ctypes.c_uint32),
+        ("gap_bits", ctypes.c_uint32),
     ]
 
     def as_dict(self):
@@ -96,6 +97,9 @@ def lib():
         L.orc_canonical_codes.argtypes = [u8p, u32p]
         L.orc_encode.argtypes = [u16p, ctypes.c_uint64, u64p, ctypes.c_uint32, ctypes.c_uint32,
                                  ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(u8p), u64p]
+        L.orc_encode_gaps.argtypes = [u16p, ctypes.c_uint64, u64p, ctypes.c_uint32, ctypes.c_uint32,
+                                      ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                                      ctypes.POINTER(u8p), u64p]
         L.orc_encode_lanes.argtypes = [u16p, ctypes.c_uint64, u64p, ctypes.c_uint32, ctypes.c_uint32,
                                        ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32, ctypes.POINTER(u8p), u64p]
         L.orc_encode_lanes_u8.argtypes = [u8p, ctypes.c_uint64, u64p, ctypes.c_uint32, ctypes.c_uint32,
@@ -173,12 +177,13 @@ def canonical_codes(lens) -> np.ndarray:
 
 
 def encode(w: np.ndarray, numels=None, max_code_len: int = 24, chunks_per_group: int = 128,
-           group_align: int = 128, group_max_elems: int = 4096) -> np.ndarray:
+           group_align: int = 128, group_max_elems: int = 4096, gap_bits: int = 8) -> np.ndarray:
     """Oracle's own serial container writer.  Returns the container bytes.
 
     chunks_per_group (G), group_align (A) and group_max_elems (M) set the group
     table: groups are runs of whole A-element blocks whose codewords touch at
-    most G chunks, of at most M elements."""
+    most G chunks, of at most M elements.  gap_bits: 8 (one byte per chunk) or
+    5 (packed)."""
     w = np.ascontiguousarray(w, dtype=np.uint16).reshape(-1)
     if numels is None:
         nump, nt = None, 1
@@ -187,9 +192,9 @@ def encode(w: np.ndarray, numels=None, max_code_len: int = 24, chunks_per_group:
         nump, nt = _p(arr, ctypes.c_uint64), arr.size
     out = ctypes.POINTER(ctypes.c_uint8)()
     nbytes = ctypes.c_uint64(0)
-    st = lib().orc_encode(_p(w, ctypes.c_uint16), w.size, nump, nt, int(max_code_len),
-                          int(chunks_per_group), int(group_align), int(group_max_elems), ctypes.byref(out),
-                          ctypes.byref(nbytes))
+    st = lib().orc_encode_gaps(_p(w, ctypes.c_uint16), w.size, nump, nt, int(max_code_len),
+                               int(chunks_per_group), int(group_align), int(group_max_elems), int(gap_bits),
+                               ctypes.byref(out), ctypes.byref(nbytes))
     if st:
         raise OracleError(st, "encode")
     try:

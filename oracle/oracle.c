@@ -26,13 +26,17 @@
  *    optimal length-limited code (Larmore & Hirschberg, 1990); canonical
  *    code assignment as in RFC 1951 section 3.2.2.
  *
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings where the pages are silent:
  *  - split: e = bits 14..7 of the bf16 word, sm = bit 15 then bits 6..0;
  *  - codes are canonical, at most max_code_len (<= 24) bits, written
  *    MSB-first into bytes in ascending address order;
  *  - one present symbol gets the 1-bit code "0";
  *  - the stream is cut into 64-bit chunks; gap[c] is the offset of the first
- *    codeword that starts at or after bit 64c (stream end if none);
+ *    codeword that starts at or after bit 64c (stream end if none); gaps are
+ *    stored one byte per chunk, or (header byte 10 = 5) packed in 5 bits,
+ *    gap c in bits 5c .. 5c + 4 of the section read as a little-endian bit
+ *    string (byte k holds bits 8k .. 8k + 7, lowest first): every gap is
+ *    below the longest code, at most 23;
  *  - the per-block output positions of the pages are a group table: the
  *    elements are cut into blocks of A (the last block may be shorter); a
  *    group is a run of whole blocks that is as long as possible while the
@@ -83,7 +87,8 @@
 #define F_FLAGS          6   /* u16, 0                                      */
 #define F_MAXLEN         8   /* u8                                          */
 #define F_CHUNKBITS      9   /* u8, 64                                      */
-#define F_RES0          10   /* u16, 0                                      */
+#define F_RES0          10   /* u16, 0 (low byte: gap width, see below)     */
+#define F_GAPBITS       10   /* u8 (version 2): 0 one byte per gap, 5 packed */
 #define F_G             12   /* u32 chunks per group                        */
 #define F_NTENS         16   /* u32                                         */
 #define F_ALIGN         20   /* u32 elements per block A                    */
@@ -357,10 +362,33 @@ int orc_canonical_codes(const uint8_t lens[256], uint32_t codes[256]) {
 /* ------------------------------------------------------------------------ */
 /* Writer (serial).  Container layout as in the header comment.             */
 /* ------------------------------------------------------------------------ */
+/* Bytes of the gap section: one per chunk, or 5 bits per chunk. */
+static uint64_t gap_section_bytes(uint64_t n_chunks, uint32_t gap_bits) {
+    return gap_bits == 5 ? ceil_div(5 * n_chunks, 8) : n_chunks;
+}
+
+/* Gap of chunk c from a section of the given width. */
+static uint32_t gap_at(const uint8_t* g, uint64_t c, uint32_t gap_bits) {
+    if (gap_bits != 5) return g[c];
+    uint32_t v = 0;
+    for (uint32_t j = 0; j < 5; ++j) {
+        uint64_t bit = 5 * c + j;
+        v |= (uint32_t)((g[bit >> 3] >> (bit & 7)) & 1u) << j;
+    }
+    return v;
+}
+
 int orc_encode(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
                uint32_t max_code_len, uint32_t G, uint32_t A, uint32_t M, uint8_t** blob, uint64_t* blob_bytes) {
+    return orc_encode_gaps(w, n, numels, n_tensors, max_code_len, G, A, M, 8, blob, blob_bytes);
+}
+
+int orc_encode_gaps(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
+                    uint32_t max_code_len, uint32_t G, uint32_t A, uint32_t M, uint32_t gap_bits, uint8_t** blob,
+                    uint64_t* blob_bytes) {
     if (!blob || !blob_bytes || (n && !w)) return ORC_E_ARG;
     if (max_code_len < 1 || max_code_len > MAX_LEN_LIMIT || G < 1 || A < 1 || M < A || M % A) return ORC_E_ARG;
+    if (gap_bits != 8 && gap_bits != 5) return ORC_E_ARG;
     uint64_t one_numel = n;
     if (!numels) { numels = &one_numel; n_tensors = 1; }
     uint64_t sum = 0;
@@ -408,15 +436,15 @@ int orc_encode(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n
     uint64_t off_tens = round_up(off_len + 256, ALIGN);
     uint64_t off_gs = round_up(off_tens + 16ull * n_tensors, ALIGN);
     uint64_t off_gap = round_up(off_gs + 16 * (n_groups + 1), ALIGN);
-    uint64_t off_stream = round_up(off_gap + n_chunks, ALIGN);
+    uint64_t off_stream = round_up(off_gap + gap_section_bytes(n_chunks, gap_bits), ALIGN);
     uint64_t off_sm = round_up(off_stream + stream_bytes, ALIGN);
     uint64_t total = round_up(off_sm + n, ALIGN);
 
     uint8_t* b = (uint8_t*)calloc(total, 1);
-    if (!b) { free(block_bit); free(g_elem); free(g_bit); free(e); free(sm); return ORC_E_NOMEM; }
+    uint8_t* gap = (uint8_t*)calloc(n_chunks ? n_chunks : 1, 1);   /* gap values, one per chunk */
+    if (!b || !gap) { free(b); free(gap); free(block_bit); free(g_elem); free(g_bit); free(e); free(sm); return ORC_E_NOMEM; }
 
     uint8_t* stream = b + off_stream;
-    uint8_t* gap = b + off_gap;
     uint8_t* gs = b + off_gs;
     for (uint64_t g = 0; g <= n_groups; ++g) {
         wr(gs + 16 * g, g_elem[g], 8);
@@ -439,6 +467,18 @@ int orc_encode(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n
         }
     }
     while (next_chunk < n_chunks) { gap[next_chunk] = (uint8_t)(bits - CHUNK_BITS * next_chunk); ++next_chunk; }
+    /* the gap section: one byte per chunk, or 5 bits per chunk, lowest bit first */
+    for (uint64_t c = 0; c < n_chunks; ++c) {
+        if (gap_bits == 8) {
+            b[off_gap + c] = gap[c];
+        } else {
+            for (uint32_t j = 0; j < 5; ++j) {
+                uint64_t bit = 5 * c + j;
+                if ((gap[c] >> j) & 1u) b[off_gap + (bit >> 3)] |= (uint8_t)(1u << (bit & 7));
+            }
+        }
+    }
+    free(gap);
 
     memcpy(b + off_len, lens, 256);
     uint64_t acc = 0;
@@ -454,6 +494,7 @@ int orc_encode(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n
     wr(b + F_FLAGS, 0, 2);
     wr(b + F_MAXLEN, max_code_len, 1);
     wr(b + F_CHUNKBITS, CHUNK_BITS, 1);
+    wr(b + F_GAPBITS, gap_bits == 5 ? 5 : 0, 1);
     wr(b + F_G, G, 4);
     wr(b + F_NTENS, n_tensors, 4);
     wr(b + F_ALIGN, A, 4);
@@ -866,6 +907,7 @@ typedef struct {
     uint32_t version;   /* 2: per-chunk gaps; 3: interleaved lanes */
     uint32_t kind;      /* KIND_BF16 or (version 3) KIND_U8 */
     uint32_t coder;     /* CODER_HUFFMAN or (version 3) CODER_RANS */
+    uint32_t gap_bits;  /* version 2: 8 (one byte per gap) or 5 (packed) */
     uint32_t max_len, G, A, M, B, n_tensors;
     uint64_t n, stream_bits, n_chunks, n_groups;
     uint64_t off_len, off_tens, off_gs, off_gap, off_stream, stream_bytes, off_sm, total;
@@ -884,7 +926,9 @@ static int parse_header(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
     if (blob[F_KIND] || blob[F_CODER]) return ORC_E_MAGIC;
     if (rd(blob + F_VERSION, 2) != 2 || rd(blob + F_FLAGS, 2) != 0) return ORC_E_MAGIC;
     if (rd(blob + F_CHUNKBITS, 1) != CHUNK_BITS) return ORC_E_MAGIC;
-    if (rd(blob + F_RES0, 2) != 0) return ORC_E_MAGIC;
+    if (rd(blob + F_GAPBITS, 1) != 0 && rd(blob + F_GAPBITS, 1) != 5) return ORC_E_MAGIC;
+    if (rd(blob + F_GAPBITS + 1, 1) != 0) return ORC_E_MAGIC;
+    h->gap_bits = rd(blob + F_GAPBITS, 1) == 5 ? 5u : 8u;
     for (uint32_t k = F_TAIL; k < HDR_BYTES; ++k) if (blob[k]) return ORC_E_MAGIC;
     h->max_len = (uint32_t)rd(blob + F_MAXLEN, 1);
     h->G = (uint32_t)rd(blob + F_G, 4);
@@ -913,8 +957,8 @@ static int parse_header(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
     if (h->stream_bits > h->n * (uint64_t)h->max_len || h->stream_bits < h->n) return ORC_E_SIZES;
     /* sections: aligned, in order, inside the blob */
     const uint64_t offs[6] = {h->off_len, h->off_tens, h->off_gs, h->off_gap, h->off_stream, h->off_sm};
-    const uint64_t lens[6] = {256, 16ull * h->n_tensors, 16 * (h->n_groups + 1), h->n_chunks,
-                              h->stream_bytes, h->n};
+    const uint64_t lens[6] = {256, 16ull * h->n_tensors, 16 * (h->n_groups + 1),
+                              gap_section_bytes(h->n_chunks, h->gap_bits), h->stream_bytes, h->n};
     uint64_t lo = HDR_BYTES;
     for (int k = 0; k < 6; ++k) {
         if (offs[k] % ALIGN || offs[k] < lo) return ORC_E_TRUNC;
@@ -926,6 +970,7 @@ static int parse_header(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
 
 static int parse_header_lanes(const uint8_t* blob, uint64_t bytes, hdr_t* h) {
     h->version = 3;
+    h->gap_bits = 8;   /* no gap section */
     h->kind = blob[F_KIND];
     h->coder = blob[F_CODER];
     if (h->kind != KIND_BF16 && h->kind != KIND_U8) return ORC_E_MAGIC;
@@ -998,6 +1043,7 @@ int orc_header(const uint8_t* blob, uint64_t blob_bytes, orc_report* rep) {
         rep->seg_max_bits = h.B;
         rep->elem_kind = h.kind;
         rep->coder = h.coder;
+        rep->gap_bits = h.gap_bits;
     }
     return ORC_OK;
 }
@@ -1025,7 +1071,7 @@ static int decode_chunks(const uint8_t* blob, const hdr_t* h, const trie_node* T
     for (uint64_t i = 0; i < h->n && st == ORC_OK; ++i) {
         while (next_chunk < h->n_chunks && CHUNK_BITS * next_chunk <= pos) {
             uint64_t want = pos - CHUNK_BITS * next_chunk;
-            if (want >= CHUNK_BITS || gap[next_chunk] != want) { st = ORC_E_GAP; break; }
+            if (want >= CHUNK_BITS || gap_at(gap, next_chunk, h->gap_bits) != want) { st = ORC_E_GAP; break; }
             ++next_chunk;
         }
         if (st != ORC_OK) break;
@@ -1049,7 +1095,7 @@ static int decode_chunks(const uint8_t* blob, const hdr_t* h, const trie_node* T
     if (pos != h->stream_bits) { free(block_bit); return ORC_E_STREAM; }
     while (next_chunk < h->n_chunks) {
         uint64_t want = h->stream_bits - CHUNK_BITS * next_chunk;
-        if (want >= CHUNK_BITS || gap[next_chunk] != want) { free(block_bit); return ORC_E_GAP; }
+        if (want >= CHUNK_BITS || gap_at(gap, next_chunk, h->gap_bits) != want) { free(block_bit); return ORC_E_GAP; }
         ++next_chunk;
     }
     /* the group table, re-derived from the observed block starts */
@@ -1356,6 +1402,7 @@ padding:;
         rep->seg_max_bits = h.B;
         rep->elem_kind = h.kind;
         rep->coder = h.coder;
+        rep->gap_bits = h.gap_bits;
         rep->n_symbols = m;
         rep->longest_code = longest;
         rep->kraft_num = kraft;

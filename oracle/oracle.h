@@ -72,6 +72,7 @@ typedef struct {
     uint32_t seg_max_bits;     /* lanes layout: stream bits per segment max  */
     uint32_t elem_kind;        /* 0: bf16 (exponent coded); 1: u8 symbols    */
     uint32_t coder;            /* 0: canonical Huffman; 1: rANS              */
+    uint32_t gap_bits;         /* version 2: 8 or 5 bits per stored gap      */
 } orc_report;
 
 /* Split bf16 words into exponent and sign+mantissa planes (definition). */
@@ -100,6 +101,13 @@ int orc_canonical_codes(const uint8_t lens[256], uint32_t codes[256]);
 int orc_encode(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
                uint32_t max_code_len, uint32_t chunks_per_group, uint32_t group_align,
                uint32_t group_max_elems, uint8_t** blob, uint64_t* blob_bytes);
+
+/* The same with the gap width chosen: gap_bits 8 (one byte per chunk, as
+ * orc_encode) or 5 (gap c in bits 5c .. 5c + 4 of the section, lowest bit
+ * first; header byte 10 = 5). */
+int orc_encode_gaps(const uint16_t* w, uint64_t n, const uint64_t* numels, uint32_t n_tensors,
+                    uint32_t max_code_len, uint32_t chunks_per_group, uint32_t group_align,
+                    uint32_t group_max_elems, uint32_t gap_bits, uint8_t** blob, uint64_t* blob_bytes);
 
 /* Independent writer of the interleaved-lane layout (container version 3):
  * segments of whole group_align-element blocks, at most group_max_elems

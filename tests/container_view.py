@@ -29,6 +29,7 @@ def header(blob: np.ndarray) -> dict:
     h["version"] = struct.unpack_from("<H", raw, 4)[0]
     h["elem_kind"] = raw[124]
     h["coder"] = raw[125]
+    h["gap_bits"] = 5 if (h["version"] == 2 and raw[10] == 5) else 8
     if h["version"] == 3:
         h["lanes"] = raw[9]
         h["lane_block"] = struct.unpack_from("<H", raw, 10)[0]
@@ -48,6 +49,12 @@ def sections(blob: np.ndarray) -> dict:
     s["groups"] = blob[h["off_gs"]:h["off_gs"] + 16 * (ng + 1)].view(np.uint64).reshape(ng + 1, 2)
     if h["version"] == 3:
         s["lane_off"] = blob[h["off_gap"]:h["off_gap"] + 2 * 64 * ng].view(np.uint16).reshape(ng, 64)
+    elif h["gap_bits"] == 5:
+        # packed: gap c in bits 5c .. 5c + 4 of the section, lowest bit first
+        packed = blob[h["off_gap"]:h["off_gap"] + (5 * nc + 7) // 8]
+        s["gap_packed"] = packed
+        bits = np.unpackbits(packed, bitorder="little")[:5 * nc].reshape(nc, 5)
+        s["gap"] = (bits.astype(np.uint8) << np.arange(5, dtype=np.uint8)).sum(axis=1).astype(np.uint8)
     else:
         s["gap"] = blob[h["off_gap"]:h["off_gap"] + nc]
     s["stream"] = blob[h["off_stream"]:h["off_stream"] + h["stream_bytes"]]
