@@ -85,6 +85,8 @@ def parse_args():
                          "chunks (v2, per-chunk gaps)")
     ap.add_argument("--coder", choices=["huffman", "rans"], default="huffman",
                     help="entropy coder of the lanes layout: huffman (the default) or rans")
+    ap.add_argument("--gap-bits", type=int, choices=[8, 5], default=8,
+                    help="chunks layout: bits per stored gap, 8 or 5 (packed)")
     ap.add_argument("--max-code-len", type=int, default=0,
                     help="Huffman code length limit for the encoder (0: the library's default)")
     ap.add_argument("--e2e", action="store_true",
@@ -96,7 +98,10 @@ def parse_args():
 
 
 def code_len_opt(args) -> dict:
-    return {"max_code_len": args.max_code_len} if args.max_code_len else {}
+    opt = {"max_code_len": args.max_code_len} if args.max_code_len else {}
+    if args.gap_bits != 8:
+        opt["gap_bits"] = args.gap_bits
+    return opt
 
 
 def aligned_device_copy(torch, blob, align=256):
@@ -300,6 +305,9 @@ def main():
     if (codes or args.coder != "huffman") and args.layout != "lanes":
         print("bench.py: code planes and the rANS coder use the lanes layout", file=sys.stderr)
         sys.exit(2)
+    if args.gap_bits != 8 and args.layout != "chunks":
+        print("bench.py: --gap-bits applies to the chunks layout", file=sys.stderr)
+        sys.exit(2)
     t_gen = time.perf_counter()
     if codes:
         wl = make_code_workload(args.workload)
@@ -316,7 +324,8 @@ def main():
     stream_bits = st["stream_bits"]
     # what the kernel must read: sm plane (bf16), stream, per-chunk gaps (v2)
     # or per-lane offsets (v3), group/segment table; then what it writes
-    aux = -(-stream_bits // 64) if args.layout == "chunks" else 2 * 64 * st["n_groups"]
+    n_chunks = -(-stream_bits // 64)
+    aux = (-(-args.gap_bits * n_chunks // 8) if args.layout == "chunks" else 2 * 64 * st["n_groups"])
     alg_read = (0 if codes else n) + -(-stream_bits // 8) + aux + 16 * (st["n_groups"] + 1)
     alg_bytes = alg_read + out_bytes * n
 
@@ -427,6 +436,7 @@ def main():
             "layout": args.layout,
             "coder": args.coder,
             "max_code_len": args.max_code_len or None,
+            "gap_bits": args.gap_bits if args.layout == "chunks" else None,
             "n_elems": n,
             "n_tensors": len(wl.numels),
             "container_bytes": int(blob.size),

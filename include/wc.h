@@ -18,7 +18,7 @@
  *
  * Container v2 (all fields little-endian; every section 256-byte aligned):
  *   header (256 B): "WCBF", u16 version=2, u16 flags=0, u8 max_code_len,
- *     u8 chunk_bits=64, u16 0, u32 chunks_per_group G, u32 n_tensors,
+ *     u8 chunk_bits=64, u8 gap_bits (0 or 5), u8 0, u32 chunks_per_group G, u32 n_tensors,
  *     u32 group_align A, u64 n_elems, u64 stream_bits, u64 n_chunks,
  *     u64 n_groups, u64 offsets of code_len / tensors / groups / gap / stream,
  *     u64 stream_bytes, u64 offset of sm, u64 total_bytes, u32 group_max_elems M;
@@ -37,7 +37,12 @@
  *                         last entry is {n_elems, stream_bits};
  *   gap         u8[n_chunks]: bit offset, inside 64-bit chunk c, of the first
  *                         codeword starting at or after bit 64c (or of the
- *                         stream end);
+ *                         stream end); every gap is below max_code_len.  With
+ *                         header byte 10 = 5 (it is 0 otherwise) the gaps are
+ *                         packed in 5 bits, ceil(5 n_chunks / 8) bytes: gap c
+ *                         in bits 5c .. 5c + 4 of the section read as a
+ *                         little-endian bit string (byte k holds bits 8k ..
+ *                         8k + 7, lowest first);
  *   stream      exponent codes, MSB-first, n_chunks*8 + 16 bytes, zero padded;
  *   sm          u8[n_elems]: sign bit << 7 | 7 mantissa bits.
  * Each group is one independent unit of GPU work: its output starts at a
@@ -146,6 +151,8 @@ typedef struct {
     uint32_t coder;             /* WC_CODER_HUFFMAN (0, the default) or WC_CODER_RANS   */
                                 /* (1: lanes layout only; max_code_len is ignored and   */
                                 /* 97 A <= 8 (seg_max_bits - 2048) is required)         */
+    uint32_t gap_bits;          /* v2: bits per stored gap, 8 (or 0: the default) or 5  */
+                                /* (packed; chunks layout only)                         */
 } wc_encode_opts;
 
 #define WC_LAYOUT_LANES  0u

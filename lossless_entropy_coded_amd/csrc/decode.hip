@@ -66,7 +66,7 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 
 // Raw loads of one lane for one group: the stream bytes of its two chunks
 // a = c0 + 2t and a + 1 plus the lookahead of the second (20 bytes from 8a),
-// and both gaps.  The group's chunks c0 .. c1 (c0 = p0 / 64, c1 = (p1 - 1) /
+// and both gaps (packed gaps: the three bytes holding bits 5a .. 5a + 9).  The group's chunks c0 .. c1 (c0 = p0 / 64, c1 = (p1 - 1) /
 // 64) start at any chunk, so the 20 bytes are taken from two aligned 16-byte
 // loads at 8 * (a rounded down to even) (of 16 and 12 bytes); the parity of a
 // is that of c0, the same for every lane.  Both loads stay inside the
@@ -91,8 +91,16 @@ __device__ __forceinline__ Raw load_raw(const DecodeParams& p, const Meta& m, ui
         const uint8_t* q = p.stream + 8 * (a & ~(uint64_t)1);
         r.q0 = *reinterpret_cast<const uint4*>(q);
         r.q1 = *reinterpret_cast<const uint3*>(q + 16);
-        r.ga = p.gap[a];
-        r.gb = p.gap[a + 1];   // gap[n_chunks] lies in the padding after the gap section
+        if (p.gap_packed) {
+            // at most 2 bytes past the section: the stream section follows
+            const uint8_t* g = p.gap + ((5 * a) >> 3);
+            const uint32_t v = ((uint32_t)g[0] | (uint32_t)g[1] << 8 | (uint32_t)g[2] << 16) >> ((5 * a) & 7u);
+            r.ga = v & 31u;
+            r.gb = (v >> 5) & 31u;
+        } else {
+            r.ga = p.gap[a];
+            r.gb = p.gap[a + 1];   // gap[n_chunks] lies in the padding after the gap section
+        }
     }
     return r;
 }

@@ -449,6 +449,7 @@ int encode_impl(const T* const* tensors, const uint64_t* numels, uint32_t n_tens
     uint32_t max_len = kBf16 ? kMaxCodeLen : kDefaultCodeLenU8, group = kDefaultGroup, align = kDefaultAlign,
              max_elems = kDefaultMaxElems;
     uint32_t nthreads = 0, kind = WC_LAYOUT_LANES, seg_bits = kDefaultSegBits, coder = WC_CODER_HUFFMAN;
+    uint32_t gap_bits = kGapBitsByte;
     if (opts) {
         if (opts->max_code_len) max_len = opts->max_code_len;
         if (opts->chunk_bytes && opts->chunk_bytes != 8) return WC_ERR_INVALID_ARG;
@@ -459,6 +460,7 @@ int encode_impl(const T* const* tensors, const uint64_t* numels, uint32_t n_tens
         kind = opts->layout;
         if (opts->seg_max_bits) seg_bits = opts->seg_max_bits;
         coder = opts->coder;
+        if (opts->gap_bits) gap_bits = opts->gap_bits;
     }
     if (max_len < 1 || max_len > kMaxCodeLen || group < 1 || group > (1u << 20) || align > (1u << 20) ||
         max_elems < align || max_elems % align || max_elems > (1u << 26))
@@ -480,6 +482,7 @@ int encode_impl(const T* const* tensors, const uint64_t* numels, uint32_t n_tens
     }
     if (!kBf16 && kind != WC_LAYOUT_LANES) return WC_ERR_INVALID_ARG;   // code planes: lanes layout only
     if (coder != WC_CODER_HUFFMAN && (coder != WC_CODER_RANS || kind != WC_LAYOUT_LANES)) return WC_ERR_INVALID_ARG;
+    if (gap_bits != kGapBitsByte && (gap_bits != kGapBitsPacked || kind != WC_LAYOUT_CHUNKS)) return WC_ERR_INVALID_ARG;
 
     SourceT<T> src;
     uint64_t n = 0;
@@ -556,7 +559,7 @@ int encode_impl(const T* const* tensors, const uint64_t* numels, uint32_t n_tens
         k0 = k1;
     }
     const uint64_t n_groups = g_elem.size() - 1;
-    Header h = layout(n, stream_bits, n_tensors, max_len, group, align, max_elems, n_groups);
+    Header h = layout(n, stream_bits, n_tensors, max_len, group, align, max_elems, n_groups, gap_bits);
 
     uint8_t* out = (uint8_t*)std::aligned_alloc(kAlign, h.total_bytes);
     if (!out) return WC_ERR_NOMEM;
@@ -579,7 +582,9 @@ int encode_impl(const T* const* tensors, const uint64_t* numels, uint32_t n_tens
         store_le<uint64_t>(out + h.off_groups + kGroupEntryBytes * g + 8, g_bit[g]);
     }
     uint8_t* stream = out + h.off_stream;
-    uint8_t* gap = out + h.off_gap;
+    // packed gaps are collected one byte per chunk, then packed
+    std::vector<uint8_t> gap_bytes(gap_bits == kGapBitsPacked ? h.n_chunks : 0);
+    uint8_t* gap = gap_bits == kGapBitsPacked ? gap_bytes.data() : out + h.off_gap;
     uint8_t* sm = out + h.off_sm;
 
     // 6. pack, plane split and per-chunk gaps, per element range
@@ -627,6 +632,20 @@ int encode_impl(const T* const* tensors, const uint64_t* numels, uint32_t n_tens
             for (uint64_t c = (prev >> 6) + 1; c < h.n_chunks; ++c) gap[c] = (uint8_t)(stream_bits - 64 * c);
         }
     });
+    if (gap_bits == kGapBitsPacked) {
+        // 8 gaps fill 5 bytes: threads take runs of whole 8-chunk groups
+        uint8_t* packed = out + h.off_gap;
+        const uint64_t n8 = div_up(h.n_chunks, 8);
+        parallel_for(nthreads, [&](unsigned t) {
+            for (uint64_t q = n8 * t / nthreads; q < n8 * (t + 1) / nthreads; ++q) {
+                uint64_t v = 0;
+                for (uint64_t c = 8 * q; c < std::min<uint64_t>(8 * q + 8, h.n_chunks); ++c)
+                    v |= (uint64_t)(gap_bytes[c] & 31u) << (5 * (c - 8 * q));
+                for (uint64_t k = 5 * q; k < std::min<uint64_t>(5 * q + 5, div_up(5 * h.n_chunks, 8)); ++k)
+                    packed[k] = (uint8_t)(v >> (8 * (k - 5 * q)));
+            }
+        });
+    }
 
     *blob = out;
     *blob_bytes = h.total_bytes;

@@ -19,6 +19,11 @@ constexpr uint32_t kDefaultGroup = 128;    // chunks per group: one wave64 unit,
 constexpr uint32_t kDefaultAlign = 128;    // elements per block: groups start at multiples of it
 constexpr uint32_t kDefaultMaxElems = 4096; // elements a group may hold at most
 constexpr uint32_t kStreamSlack = 16;      // zero bytes after the last chunk
+// Version 2 gap widths: one byte per chunk, or 5 bits per chunk (every gap is
+// below the longest code, at most 23): gap c in bits 5c .. 5c + 4 of the
+// section read as a little-endian bit string; header byte 10 holds 0 or 5.
+constexpr uint32_t kGapBitsByte = 8;
+constexpr uint32_t kGapBitsPacked = 5;
 
 // Version 3, the interleaved-lane layout: per segment (a run of whole blocks),
 // 8-element lane blocks are dealt to 64 lanes (lane j: lane blocks j, j + 64,
@@ -56,7 +61,7 @@ constexpr uint32_t kRansStateBits = 32;    // the final state every non-empty la
 // Header field offsets (little-endian).
 struct HeaderOffsets {
     static constexpr int magic = 0, version = 4, flags = 6, max_code_len = 8, chunk_bits = 9,
-                         reserved0 = 10, chunks_per_group = 12, n_tensors = 16, group_align = 20,
+                         gap_bits = 10, reserved0 = 11, chunks_per_group = 12, n_tensors = 16, group_align = 20,
                          n_elems = 24, stream_bits = 32, n_chunks = 40, n_groups = 48,
                          off_code_len = 56, off_tensors = 64, off_groups = 72, off_gap = 80,
                          off_stream = 88, stream_bytes = 96, off_sm = 104, total_bytes = 112,
@@ -71,6 +76,7 @@ struct Header {
     uint32_t seg_max_bits = 0;     // version 3
     uint32_t elem_kind = kKindBf16;   // version 3: kKindBf16 or kKindU8
     uint32_t coder = kCoderHuffman;   // version 3: kCoderHuffman or kCoderRans
+    uint32_t gap_bits = kGapBitsByte;  // version 2: kGapBitsByte or kGapBitsPacked
     uint32_t max_code_len = 0, chunks_per_group = 0, n_tensors = 0, group_align = 0, group_max_elems = 0;
     uint64_t n_elems = 0, stream_bits = 0, n_chunks = 0, n_groups = 0;
     uint64_t off_code_len = 0, off_tensors = 0, off_groups = 0, off_gap = 0, off_stream = 0,
@@ -94,13 +100,20 @@ inline void store_le(uint8_t* p, T v) {
 // Bytes of one entry of the groups section: u64 first element, u64 its bit.
 constexpr uint32_t kGroupEntryBytes = 16;
 
+// Bytes of a version-2 gap section.
+inline uint64_t gap_section_bytes(uint64_t n_chunks, uint32_t gap_bits) {
+    return gap_bits == kGapBitsPacked ? div_up(5 * n_chunks, 8) : n_chunks;
+}
+
 // Chunks touched by the stream bits [p, q), q > p.
 inline uint64_t chunk_span(uint64_t p, uint64_t q) { return (q - 1) / kChunkBits - p / kChunkBits + 1; }
 
 // Section placement for a container with the given sizes.
 inline Header layout(uint64_t n_elems, uint64_t stream_bits, uint32_t n_tensors, uint32_t max_code_len,
-                     uint32_t group, uint32_t align, uint32_t max_elems, uint64_t n_groups) {
+                     uint32_t group, uint32_t align, uint32_t max_elems, uint64_t n_groups,
+                     uint32_t gap_bits = kGapBitsByte) {
     Header h;
+    h.gap_bits = gap_bits;
     h.max_code_len = max_code_len;
     h.chunks_per_group = group;
     h.group_align = align;
@@ -115,7 +128,7 @@ inline Header layout(uint64_t n_elems, uint64_t stream_bits, uint32_t n_tensors,
     h.off_tensors = round_up(h.off_code_len + 256, kAlign);
     h.off_groups = round_up(h.off_tensors + 16ull * n_tensors, kAlign);
     h.off_gap = round_up(h.off_groups + kGroupEntryBytes * (h.n_groups + 1), kAlign);
-    h.off_stream = round_up(h.off_gap + h.n_chunks, kAlign);
+    h.off_stream = round_up(h.off_gap + gap_section_bytes(h.n_chunks, gap_bits), kAlign);
     h.off_sm = round_up(h.off_stream + h.stream_bytes, kAlign);
     h.total_bytes = round_up(h.off_sm + n_elems, kAlign);
     return h;
@@ -168,6 +181,7 @@ inline void write_header(uint8_t* p, const Header& h) {
         store_le<uint8_t>(p + O::coder, (uint8_t)h.coder);
     } else {
         store_le<uint8_t>(p + O::chunk_bits, (uint8_t)kChunkBits);
+        store_le<uint8_t>(p + O::gap_bits, (uint8_t)(h.gap_bits == kGapBitsPacked ? kGapBitsPacked : 0));
         store_le<uint32_t>(p + O::chunks_per_group, h.chunks_per_group);
     }
     store_le<uint32_t>(p + O::n_tensors, h.n_tensors);

@@ -105,6 +105,7 @@ struct DecodeParams {
     uint64_t u_end;
     uint32_t ebuf_bytes;     // exponent staging bytes per wave
     uint32_t l2_cap;         // long-code prefixes staged in LDS (0 .. kL2Prefixes)
+    uint32_t gap_packed;     // chunks layout: gaps stored in 5 bits (else one byte each)
     DotParams dot;           // fused matrix-vector launches only
 };
 

@@ -60,10 +60,11 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
         if (b[O::lanes] != wc::kLanes || load_le<uint16_t>(b + O::lane_block) != wc::kLaneBlock ||
             load_le<uint64_t>(b + O::n_chunks) != 0)
             return WC_ERR_BAD_MAGIC;
-    } else if (h.version != wc::kVersion || b[O::chunk_bits] != wc::kChunkBits ||
-               load_le<uint16_t>(b + O::reserved0) != 0) {
+    } else if (h.version != wc::kVersion || b[O::chunk_bits] != wc::kChunkBits || b[O::reserved0] != 0 ||
+               (b[O::gap_bits] != 0 && b[O::gap_bits] != wc::kGapBitsPacked)) {
         return WC_ERR_BAD_MAGIC;
     }
+    h.gap_bits = !lanes && b[O::gap_bits] == wc::kGapBitsPacked ? wc::kGapBitsPacked : wc::kGapBitsByte;
     for (uint32_t k = O::reserved_tail; k < wc::kHeaderBytes; ++k)
         if (b[k]) return WC_ERR_BAD_MAGIC;
     h.elem_kind = b[O::elem_kind];
@@ -119,7 +120,8 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
     if (h.n_tensors > (1u << 24)) return WC_ERR_SECTION_BOUNDS;
     const uint64_t off[6] = {h.off_code_len, h.off_tensors, h.off_groups, h.off_gap, h.off_stream, h.off_sm};
     const uint64_t len[6] = {wc::code_section_bytes(h.coder), 16ull * h.n_tensors, wc::kGroupEntryBytes * (h.n_groups + 1),
-                             lanes ? 2ull * wc::kLanes * h.n_groups : h.n_chunks, h.stream_bytes,
+                             lanes ? 2ull * wc::kLanes * h.n_groups : wc::gap_section_bytes(h.n_chunks, h.gap_bits),
+                             h.stream_bytes,
                              h.elem_kind == wc::kKindBf16 ? h.n_elems : 0};
     uint64_t lo = wc::kHeaderBytes;
     for (int k = 0; k < 6; ++k) {
@@ -170,8 +172,14 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
 
     // gaps: a codeword reaches at most max_code_len - 1 bits into the next chunk
     const uint8_t* gap = b + h.off_gap;
-    for (uint64_t c = 0; !lanes && c < h.n_chunks; ++c)
-        if (gap[c] >= h.max_code_len || 64 * c + gap[c] > h.stream_bits) return WC_ERR_GAP;
+    for (uint64_t c = 0; !lanes && c < h.n_chunks; ++c) {
+        uint32_t g = gap[c];
+        if (h.gap_bits == wc::kGapBitsPacked) {
+            const uint64_t bit = 5 * c;
+            g = (uint32_t)((gap[bit >> 3] | (uint32_t)gap[(bit >> 3) + 1] << 8) >> (bit & 7)) & 31u;
+        }
+        if (g >= h.max_code_len || 64 * c + g > h.stream_bits) return WC_ERR_GAP;
+    }
 
     // groups: start at {0, 0}, strictly increasing, first elements on block
     // boundaries, at most G chunks, at most group_max_elems elements and at
@@ -433,6 +441,7 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
     d.u_end = p->h.n_groups;
     d.ebuf_bytes = p->ebuf_bytes;
     d.l2_cap = p->l2_cap;
+    d.gap_packed = p->h.gap_bits == wc::kGapBitsPacked ? 1u : 0u;
     hipError_t e;
     if (p->lanes) {
         // the lane offsets sit where the gaps do; the kernel stages the tables
@@ -470,6 +479,7 @@ extern "C" int wc_decode_u8_async(const wc_plan_t* p, const void* blob_dev, uint
     d.u_end = p->h.n_groups;
     d.ebuf_bytes = p->ebuf_bytes;
     d.l2_cap = p->l2_cap;
+    d.gap_packed = p->h.gap_bits == wc::kGapBitsPacked ? 1u : 0u;
     const hipError_t e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, p->grid, wc::kLanesToU8, p->rans,
                                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
@@ -566,6 +576,7 @@ extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, co
     d.n_elems = p->h.n_elems;
     d.ebuf_bytes = p->ebuf_bytes;
     d.l2_cap = p->l2_cap;
+    d.gap_packed = p->h.gap_bits == wc::kGapBitsPacked ? 1u : 0u;
     d.dot.part = static_cast<float*>(work_dev);
     d.dot.row_group = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(work_dev) + rows_off);
     const uint64_t groups = wc::div_up(d.u_end - d.u_begin, p->waves);

@@ -35,7 +35,8 @@ class EncodeOpts(ctypes.Structure):
     _fields_ = [("max_code_len", ctypes.c_uint32), ("chunk_bytes", ctypes.c_uint32),
                 ("chunks_per_group", ctypes.c_uint32), ("n_threads", ctypes.c_uint32),
                 ("group_align", ctypes.c_uint32), ("group_max_elems", ctypes.c_uint32),
-                ("layout", ctypes.c_uint32), ("seg_max_bits", ctypes.c_uint32), ("coder", ctypes.c_uint32)]
+                ("layout", ctypes.c_uint32), ("seg_max_bits", ctypes.c_uint32), ("coder", ctypes.c_uint32),
+                ("gap_bits", ctypes.c_uint32)]
 
 
 _lib.wc_encode_host.argtypes = [ctypes.POINTER(_u16p), _u64p, ctypes.c_uint32, ctypes.POINTER(EncodeOpts),
@@ -147,20 +148,21 @@ def _as_u16(t) -> np.ndarray:
 def encode_host(tensors, max_code_len: int = 24, chunks_per_group: int = GROUP_CHUNKS,
                 n_threads: int = 0, group_align: int = GROUP_ALIGN,
                 group_max_elems: int = GROUP_MAX_ELEMS, layout: str = "lanes",
-                seg_max_bits: int = SEG_MAX_BITS, coder: str = "huffman") -> np.ndarray:
+                seg_max_bits: int = SEG_MAX_BITS, coder: str = "huffman", gap_bits: int = 8) -> np.ndarray:
     """wc_encode_host over a list of bf16 tensors (numpy uint16 or torch CPU).
 
     layout: "lanes" (the default: container v3, interleaved lanes;
     seg_max_bits caps a segment's stream bits) or "chunks" (container v2,
     per-chunk gaps; chunks_per_group applies).  coder: "huffman" or "rans"
-    (lanes only; max_code_len is then ignored).
+    (lanes only; max_code_len is then ignored).  gap_bits: 8, or 5 for packed
+    gaps (chunks only).
     Returns the container as a numpy uint8 array (a copy of the library buffer)."""
     arrs = [_as_u16(t) for t in tensors]
     nt = len(arrs)
     ptrs = (_u16p * max(nt, 1))(*[a.ctypes.data_as(_u16p) for a in arrs])
     numels = (ctypes.c_uint64 * max(nt, 1))(*[a.size for a in arrs])
     opts = EncodeOpts(max_code_len, 8, chunks_per_group, n_threads, group_align, group_max_elems,
-                      LAYOUTS[layout], seg_max_bits, CODERS[coder])
+                      LAYOUTS[layout], seg_max_bits, CODERS[coder], gap_bits)
     out = _u8p()
     nbytes = ctypes.c_uint64(0)
     _check(_lib.wc_encode_host(ptrs, numels, nt, ctypes.byref(opts), ctypes.byref(out), ctypes.byref(nbytes)),

@@ -86,10 +86,10 @@ def _check_tensor(oracle_lib, got, W, x, align):
 
 
 # the container variants the fused product runs on: Huffman in interleaved
-# lanes, Huffman in chunks, rANS in interleaved lanes (whose segments are also
-# runs of whole blocks, so the same bound holds)
+# lanes, Huffman in chunks (byte or packed gaps), rANS in interleaved lanes
+# (whose segments are also runs of whole blocks, so the same bound holds)
 ENCODINGS = {"lanes": {"layout": "lanes"}, "chunks": {"layout": "chunks"},
-             "rans": {"layout": "lanes", "coder": "rans"}}
+             "rans": {"layout": "lanes", "coder": "rans"}, "chunks5": {"layout": "chunks", "gap_bits": 5}}
 
 
 # (block size A, group cap M, tensors as (rows, cols) or (n,) vectors); every
@@ -104,7 +104,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("layout", ["lanes", "chunks", "rans"])
+@pytest.mark.parametrize("layout", ["lanes", "chunks", "rans", "chunks5"])
 @pytest.mark.parametrize("name,align,cap,shapes", CASES, ids=[c[0] for c in CASES])
 def test_fused_against_oracle(wc, oracle_lib, name, align, cap, shapes, layout):
     """Each matrix alone, then every run of consecutive matrices in one call:
@@ -152,7 +152,7 @@ def test_fused_against_oracle(wc, oracle_lib, name, align, cap, shapes, layout):
                 assert np.array_equal(y, alone[k]), f"tensor {k}: one-call result differs from the per-matrix call"
 
 
-@pytest.mark.parametrize("layout", ["lanes", "chunks", "rans"])
+@pytest.mark.parametrize("layout", ["lanes", "chunks", "rans", "chunks5"])
 @pytest.mark.parametrize("name,rows", [("heavy_tail_14k", 96), ("block_8b", 40), ("block_70b", 24)])
 def test_fused_on_workload_shapes(wc, oracle_lib, name, rows, layout):
     """The block workloads, truncated to a few rows per matrix: all matrices
@@ -172,7 +172,7 @@ def test_fused_on_workload_shapes(wc, oracle_lib, name, rows, layout):
             _check_tensor(oracle_lib, got, wl.bits[off:off + r * c].reshape(r, c), gemv_input(c), wc.GROUP_ALIGN)
 
 
-@pytest.mark.parametrize("layout", ["lanes", "chunks", "rans"])
+@pytest.mark.parametrize("layout", ["lanes", "chunks", "rans", "chunks5"])
 def test_fused_full_block_8b_sampled(wc, oracle_lib, layout):
     """The full 8B-shape block (the size the benchmark decodes): its 7
     matrices in one fused call; 48 sampled rows per matrix (first, last and

@@ -430,3 +430,45 @@ def test_plan_rejects_each_rans_fault(wc, oracle_lib):
     assert _plan_status(wc, oracle_lib.encode_lanes_rans(wl.bits, numels=wl.numels)) in ok
     c = (np.arange(5000) % 7).astype(np.uint8)
     assert _plan_status(wc, wc.encode_u8_host([c], coder="rans")) in ok
+
+
+@pytest.mark.parametrize("G,A,M", [(128, 128, 4096), (128, 8, 64), (128, 120, 3960), (256, 64, 1024)])
+def test_packed_gap_encoder_matches_oracle_writer(wc, oracle_lib, G, A, M):
+    """The product's packed-gap chunks writer is byte-identical to the
+    oracle's for any thread count; only the gap section differs from the
+    byte-gap container."""
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload("heavy_tail_14k", scale_rows=24)
+    kw = dict(layout="chunks", chunks_per_group=G, group_align=A, group_max_elems=M)
+    a = wc.encode_host(wl.tensors(), gap_bits=5, **kw)
+    b = oracle_lib.encode(wl.bits, numels=wl.numels, gap_bits=5, chunks_per_group=G, group_align=A, group_max_elems=M)
+    assert np.array_equal(a, b)
+    for n_threads in (1, 3):
+        assert np.array_equal(wc.encode_host(wl.tensors(), gap_bits=5, n_threads=n_threads, **kw), a)
+    s5, s8 = sections(a), sections(wc.encode_host(wl.tensors(), **kw))
+    assert np.array_equal(s5["gap"], s8["gap"]) and np.array_equal(s5["stream"], s8["stream"])
+    assert a.size <= s8["total"]
+
+
+def test_packed_gap_options_and_plan_faults(wc):
+    from lossless_entropy_coded_amd.synth import make_workload
+    w = np.arange(1000, dtype=np.uint16)
+    for kw in ({"gap_bits": 6, "layout": "chunks"}, {"gap_bits": 5, "layout": "lanes"}):
+        with pytest.raises(wc.WCError) as ei:
+            wc.encode_host([w], **kw)
+        assert ei.value.status == wc.WC_ERR_INVALID_ARG
+    wl = make_workload("matrix_1k", scale_rows=128)
+    blob = wc.encode_host(wl.tensors(), layout="chunks", gap_bits=5)
+    s = sections(blob)
+    ok = (wc.WC_OK, wc.WC_ERR_HIP)
+    assert s["gap_bits"] == 5 and _plan_status(wc, blob) in ok
+    for off, val in ((10, 6), (10, 8), (11, 1)):
+        b = blob.copy()
+        b[off] = val
+        assert _plan_status(wc, b) == wc.WC_ERR_BAD_MAGIC, (off, val)
+    # a gap of 31 (>= max_code_len) in chunk 3
+    b = blob.copy()
+    for j in range(5):
+        bit = 5 * 3 + j
+        b[s["off_gap"] + bit // 8] |= np.uint8(1 << (bit % 8))
+    assert _plan_status(wc, b) == wc.WC_ERR_GAP
