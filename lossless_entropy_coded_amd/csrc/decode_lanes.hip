@@ -85,6 +85,18 @@ __device__ __forceinline__ uint4 swap16x8(const uint4& v) {
                       __builtin_amdgcn_perm(v.z, v.z, 0x02030001u), __builtin_amdgcn_perm(v.w, v.w, 0x02030001u));
 }
 
+// Eight bytes of a lane slot (4-byte aligned: slots are 17 dwords apart) as
+// two dwords.
+__device__ __forceinline__ uint2 load_slot8(const uint8_t* q) {
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(q);
+    return make_uint2(w[0], w[1]);
+}
+__device__ __forceinline__ void store_slot8(uint8_t* q, uint2 v) {
+    uint32_t* w = reinterpret_cast<uint32_t*>(q);
+    w[0] = v.x;
+    w[1] = v.y;
+}
+
 // Undo the one-bit rotation the decode tables store symbols with, in each
 // byte of a word (e = rol8(e', 1)).
 __device__ __forceinline__ uint32_t unrotate4(uint32_t x) {
@@ -224,14 +236,14 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
                 // lane offset by the segment's bits (<= 15872), so the first
                 // half-word is at most 999, and a lane takes at most 64 steps
                 // and one word per step: at most half-word 1065, byte 2131 of
-                // the wave's 2048 staging and 4608 slot bytes.
+                // the wave's 2048 staging and 4352 slot bytes.
                 const uint16_t* const s16 = reinterpret_cast<const uint16_t*>(sbuf);
                 const uint32_t* const s_slot = reinterpret_cast<const uint32_t*>(s_tab);
                 if (rans_single) {
                     // one symbol of frequency 2^12: the state never moves
                     const uint32_t v = (s_slot[0] & 0xFFu) * 0x01010101u;
                     for (uint32_t p = 0; p < nsym; p += kMergeElems)
-                        *reinterpret_cast<uint2*>(slot + p) = make_uint2(v, v);
+                        store_slot8(slot + p, make_uint2(v, v));
                 } else {
                     uint32_t q = pos >> 4;
                     uint32_t x = (uint32_t)s16[q] << 16 | s16[q + 1];
@@ -253,7 +265,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
                                             __builtin_amdgcn_perm(e[3], e[2], 0x04000C0Cu);
                         const uint32_t s1 = __builtin_amdgcn_perm(e[5], e[4], 0x0C0C0400u) |
                                             __builtin_amdgcn_perm(e[7], e[6], 0x04000C0Cu);
-                        *reinterpret_cast<uint2*>(slot + p) = make_uint2(s0, s1);
+                        store_slot8(slot + p, make_uint2(s0, s1));
                     }
                 }
             } else if constexpr (kMode == kLanesToBf16) {
@@ -349,14 +361,14 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
         const uint32_t full = n / kMergeElems;
         if constexpr (kDot) {
             dot_group(p.dot, dr, full, lane, smv, xv, u - p.u_begin,
-                      [&](uint32_t k) { return *reinterpret_cast<const uint2*>(slot + kMergeElems * k); });
+                      [&](uint32_t k) { return load_slot8(slot + kMergeElems * k); });
         } else if constexpr (kU8) {
             uint8_t* const outb = p.out8 + A;
 #pragma unroll
             for (uint32_t k = 0; k < kMergeSteps; ++k) {
                 const uint32_t blk = lane + k * kWaveLanes;
                 if (blk < full) {
-                    const uint2 e2 = *reinterpret_cast<const uint2*>(slot + kMergeElems * k);
+                    const uint2 e2 = load_slot8(slot + kMergeElems * k);
                     u32x2 v;
                     v.x = unrotate4(e2.x);
                     v.y = unrotate4(e2.y);
@@ -368,7 +380,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
         for (uint32_t k = 0; k < kMergeSteps; ++k) {
             const uint32_t blk = lane + k * kWaveLanes;
             if (blk < full) {
-                const uint2 e2 = *reinterpret_cast<const uint2*>(slot + kMergeElems * k);
+                const uint2 e2 = load_slot8(slot + kMergeElems * k);
                 uint32_t o0, o1, o2, o3;
                 join4(smv[k].x, e2.x, o0, o1);
                 join4(smv[k].y, e2.y, o2, o3);
@@ -386,8 +398,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
         // `full` is the (full / 64)-th of lane full % 64
         if (kU8 && full * kMergeElems < n && lane == 0) {
             const uint32_t rel = kMergeElems * full;
-            const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + kLaneSlotBytes * (full % kWaveLanes) +
-                                                             kMergeElems * (full / kWaveLanes));
+            const uint2 e2 = load_slot8(ebuf + kLaneSlotBytes * (full % kWaveLanes) + kMergeElems * (full / kWaveLanes));
             const uint32_t o[2] = {unrotate4(e2.x), unrotate4(e2.y)};
 #pragma unroll
             for (uint32_t i = 0; i < kMergeElems; ++i)
@@ -396,8 +407,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
         if (kMode == kLanesToBf16 && full * kMergeElems < n && lane == 0) {
             const uint32_t rel = kMergeElems * full;
             const uint2 s2 = load_nt8(p.sm + A + rel);
-            const uint2 e2 = *reinterpret_cast<const uint2*>(ebuf + kLaneSlotBytes * (full % kWaveLanes) +
-                                                             kMergeElems * (full / kWaveLanes));
+            const uint2 e2 = load_slot8(ebuf + kLaneSlotBytes * (full % kWaveLanes) + kMergeElems * (full / kWaveLanes));
             uint32_t o[4];
             join4(s2.x, e2.x, o[0], o[1]);
             join4(s2.y, e2.y, o[2], o[3]);

@@ -113,11 +113,12 @@ struct DecodeParams {
 // stream window (its bits, the first bit's 16-byte alignment and 8 bytes of
 // lookahead) in kLaneStageBytes of LDS, then the exponent bytes, one
 // kLaneSlotBytes slot per lane (its at most 64 symbols and the up to three
-// bytes a four-symbol lookup may write past them, 72 bytes so that the
-// lanes' 8-byte merge reads fall in different banks); a segment therefore
-// holds at most kLanesMaxSegBits stream bits.
+// bytes a four-symbol lookup may write past them: 68 bytes, 17 dwords, an odd
+// stride, so that lanes at equal offsets use 64 different banks; slots are
+// accessed as bytes and dwords); a segment therefore holds at most
+// kLanesMaxSegBits stream bits.
 constexpr uint32_t kLaneStageBytes = 2048;
-constexpr uint32_t kLaneSlotBytes = 72;
+constexpr uint32_t kLaneSlotBytes = 68;
 constexpr uint32_t kLaneWaveBytes = kLaneStageBytes + kWaveLanes * kLaneSlotBytes;
 constexpr uint32_t kLanesMaxSegBits = 15872;
 
