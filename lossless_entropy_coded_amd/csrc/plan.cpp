@@ -31,9 +31,19 @@ struct wc_plan_s {
     uint64_t max_group_elems = 0;   // elements of the largest group (one wave's unit)
     uint32_t count_bits = 12;    // index width of the codeword-start table
     uint32_t decode_bits = 11;   // index width of the multi-codeword table
-    uint32_t waves = 4;          // wavefronts per workgroup
-    uint32_t grid = 0;
-    uint32_t slots = 0;          // co-resident workgroups on the device
+    // Launch shapes: the plain bf16 decode is bound by HBM and runs best with
+    // 4-wave workgroups (3 per CU); the code-plane decode and the fused
+    // product are bound by the decode's own latency and instructions and run
+    // best with more waves in flight, 8-wave workgroups (2 per CU) on the
+    // lanes layout.  WC_WAVES sets both.
+    struct Shape {
+        uint32_t waves = 4;      // wavefronts per workgroup
+        uint32_t grid = 0;       // persistent workgroups of a whole-container decode
+        uint32_t slots = 0;      // co-resident workgroups on the device
+        uint32_t lds_bytes = 0;
+    };
+    Shape plain, busy;
+    uint32_t grid = 0;           // of the container's decode entry point (stats)
     uint32_t lds_bytes = 0;
     uint32_t ebuf_bytes = 0;
     uint32_t l2_cap = 0;         // long-code prefixes whose second-level entries are staged in LDS
@@ -295,8 +305,12 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         p->count_bits = 12;   // rANS: the 2^12-slot table takes the place of the 11-bit multi-codeword table
         p->decode_bits = 11;
     }
-    p->waves = env_u32("WC_WAVES", 4);
-    if (!wc::supported_waves(p->waves)) p->waves = 4;
+    {
+        const uint32_t forced_waves = env_u32("WC_WAVES", 0);
+        const bool ok = wc::supported_waves(forced_waves);
+        p->plain.waves = ok ? forced_waves : 4u;
+        p->busy.waves = ok ? forced_waves : (lanes ? 8u : 4u);
+    }
     // each wave's staging of one group's exponents: a chain may write
     // kEbufSlack bytes past the end, and the merge reads whole blocks
     p->ebuf_bytes =
@@ -320,8 +334,6 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         p->l2_cap = F < span ? (uint32_t)std::min<uint64_t>(span - F, wc::kL2Prefixes) : 0u;
     }
     p->lanes = lanes;
-    p->lds_bytes = lanes ? wc::decode_lanes_lds_bytes(p->decode_bits, p->waves, p->l2_cap)
-                         : wc::decode_lds_bytes(p->count_bits, p->decode_bits, p->waves, p->ebuf_bytes, p->l2_cap);
 
     DeviceGuard guard(hip_device);
     if (!guard.ok) {
@@ -333,35 +345,45 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         delete p;
         return WC_ERR_HIP;
     }
-    int per_cu = lanes ? wc::decode_lanes_blocks_per_cu(p->decode_bits, p->waves, p->l2_cap, p->rans)
-                       : wc::decode_blocks_per_cu(p->count_bits, p->decode_bits, p->waves, p->ebuf_bytes, p->l2_cap);
-    // The persistent grid must be co-resident.  LDS is handed out in granules of
-    // 1/128 of a compute unit's LDS (1,280 bytes of 160 KiB on gfx950), which the
-    // runtime's occupancy estimate does not round for: count the granules.
-    {
-        int lds_cu = 0;
-        if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, hip_device) !=
-                hipSuccess ||
-            lds_cu <= 0)
-            lds_cu = 160 * 1024;
+    int lds_cu = 0;
+    if (hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, hip_device) != hipSuccess ||
+        lds_cu <= 0)
+        lds_cu = 160 * 1024;
+    const uint32_t forced_grid = env_u32("WC_GRID", 0);
+    auto size_shape = [&](wc_plan_s::Shape& sh) {
+        sh.lds_bytes = lanes ? wc::decode_lanes_lds_bytes(p->decode_bits, sh.waves, p->l2_cap)
+                             : wc::decode_lds_bytes(p->count_bits, p->decode_bits, sh.waves, p->ebuf_bytes, p->l2_cap);
+        int per_cu = lanes ? wc::decode_lanes_blocks_per_cu(p->decode_bits, sh.waves, p->l2_cap, p->rans)
+                           : wc::decode_blocks_per_cu(p->count_bits, p->decode_bits, sh.waves, p->ebuf_bytes,
+                                                      p->l2_cap);
+        // The persistent grid must be co-resident.  LDS is handed out in
+        // granules of 1/128 of a compute unit's LDS (1,280 bytes of 160 KiB on
+        // gfx950), which the runtime's occupancy estimate does not round for:
+        // count the granules.
         const uint32_t granule = std::max<uint32_t>(1, (uint32_t)lds_cu / 128);
-        const uint32_t granules = (uint32_t)wc::div_up(p->lds_bytes, granule);
+        const uint32_t granules = (uint32_t)wc::div_up(sh.lds_bytes, granule);
         per_cu = std::min<int>(per_cu, (int)(128 / std::max<uint32_t>(granules, 1)));
-    }
-    if (per_cu <= 0) {
+        if (per_cu <= 0) return false;
+        // One persistent workgroup per resident slot (all of them: every
+        // extra wave helps the decode more than an even last round of groups
+        // would), and no more workgroups than there are groups to give their
+        // waves.
+        uint64_t want = (uint64_t)n_cu * (uint64_t)per_cu;
+        sh.slots = (uint32_t)want;
+        if (forced_grid) want = forced_grid;
+        const uint64_t need = std::max<uint64_t>(1, wc::div_up(p->h.n_groups, sh.waves));
+        sh.grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(want, need));
+        return true;
+    };
+    if (!size_shape(p->plain) || !size_shape(p->busy)) {
         delete p;
         return WC_ERR_UNSUPPORTED;
     }
-    // One persistent workgroup per resident slot (all of them: the decode is
-    // bound by memory throughput, which every extra wave helps more than an
-    // even last round of groups would), and no more workgroups than there
-    // are groups to give their waves.
-    uint64_t want = (uint64_t)n_cu * (uint64_t)per_cu;
-    p->slots = (uint32_t)want;
-    uint32_t forced = env_u32("WC_GRID", 0);
-    if (forced) want = forced;
-    const uint64_t need = std::max<uint64_t>(1, wc::div_up(p->h.n_groups, p->waves));
-    p->grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(want, need));
+    {
+        const wc_plan_s::Shape& own = p->h.elem_kind == wc::kKindU8 ? p->busy : p->plain;
+        p->grid = own.grid;
+        p->lds_bytes = own.lds_bytes;
+    }
 
     const size_t tbytes = (size_t)wc::table_words(p->count_bits, p->decode_bits) * 4;
     if (hipMalloc(reinterpret_cast<void**>(&p->d_tables), tbytes) != hipSuccess) {
@@ -447,10 +469,10 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
         // the lane offsets sit where the gaps do; the kernel stages the tables
         // from the multi-codeword table on
         d.tables = p->d_tables + (1u << p->count_bits);
-        e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, p->grid, wc::kLanesToBf16, p->rans,
+        e = wc::launch_decode_lanes(d, p->decode_bits, p->plain.waves, p->plain.grid, wc::kLanesToBf16, p->rans,
                                     static_cast<hipStream_t>(stream));
     } else {
-        e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, p->grid, false,
+        e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->plain.waves, p->plain.grid, false,
                               static_cast<hipStream_t>(stream));
     }
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
@@ -480,7 +502,7 @@ extern "C" int wc_decode_u8_async(const wc_plan_t* p, const void* blob_dev, uint
     d.ebuf_bytes = p->ebuf_bytes;
     d.l2_cap = p->l2_cap;
     d.gap_packed = p->h.gap_bits == wc::kGapBitsPacked ? 1u : 0u;
-    const hipError_t e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, p->grid, wc::kLanesToU8, p->rans,
+    const hipError_t e = wc::launch_decode_lanes(d, p->decode_bits, p->busy.waves, p->busy.grid, wc::kLanesToU8, p->rans,
                                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
 }
@@ -579,15 +601,15 @@ extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, co
     d.gap_packed = p->h.gap_bits == wc::kGapBitsPacked ? 1u : 0u;
     d.dot.part = static_cast<float*>(work_dev);
     d.dot.row_group = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(work_dev) + rows_off);
-    const uint64_t groups = wc::div_up(d.u_end - d.u_begin, p->waves);
-    const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(p->slots, groups));
+    const uint64_t groups = wc::div_up(d.u_end - d.u_begin, p->busy.waves);
+    const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(p->busy.slots, groups));
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (p->lanes) {
         d.tables = p->d_tables + (1u << p->count_bits);
-        e = wc::launch_decode_lanes(d, p->decode_bits, p->waves, grid, wc::kLanesToDot, p->rans, s);
+        e = wc::launch_decode_lanes(d, p->decode_bits, p->busy.waves, grid, wc::kLanesToDot, p->rans, s);
     } else {
-        e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->waves, grid, true, s);
+        e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->busy.waves, grid, true, s);
     }
     if (e == hipSuccess) e = wc::launch_gemv_rows(d, s);
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
