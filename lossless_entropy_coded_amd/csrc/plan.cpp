@@ -34,8 +34,8 @@ struct wc_plan_s {
     // Launch shapes: the plain bf16 decode is bound by HBM and runs best with
     // 4-wave workgroups (3 per CU); the code-plane decode and the fused
     // product are bound by the decode's own latency and instructions and run
-    // best with more waves in flight, 8-wave workgroups (2 per CU) on the
-    // lanes layout.  WC_WAVES sets both.
+    // best with more waves in flight, 8-wave workgroups (2 per CU).
+    // WC_WAVES sets both.
     struct Shape {
         uint32_t waves = 4;      // wavefronts per workgroup
         uint32_t grid = 0;       // persistent workgroups of a whole-container decode
@@ -309,7 +309,7 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         const uint32_t forced_waves = env_u32("WC_WAVES", 0);
         const bool ok = wc::supported_waves(forced_waves);
         p->plain.waves = ok ? forced_waves : 4u;
-        p->busy.waves = ok ? forced_waves : (lanes ? 8u : 4u);
+        p->busy.waves = ok ? forced_waves : 8u;
     }
     // each wave's staging of one group's exponents: a chain may write
     // kEbufSlack bytes past the end, and the merge reads whole blocks
