@@ -279,7 +279,7 @@ def end_to_end(args):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (decode is per-GPU and needs no collectives); "
+        print(f"bench.py: the decode runs on one GPU only (it is per-GPU and needs no collectives); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
     import numpy as np

@@ -115,7 +115,7 @@ extern "C" {
 #define WC_ERR_INVALID_ARG      -1   /* NULL pointer, misaligned pointer, bad option          */
 #define WC_ERR_NOMEM            -2   /* host or device allocation failed                      */
 #define WC_ERR_HIP              -3   /* a HIP runtime call or kernel launch failed             */
-#define WC_ERR_UNSUPPORTED      -4   /* valid container this build cannot decode (e.g. G)     */
+#define WC_ERR_UNSUPPORTED      -4   /* valid container the GPU decoder cannot decode (e.g. G) */
 #define WC_ERR_BAD_MAGIC        -10  /* magic, version, flags or a fixed field is wrong       */
 #define WC_ERR_TRUNCATED        -11  /* blob shorter than the header or total_bytes           */
 #define WC_ERR_SECTION_BOUNDS   -12  /* a section is misaligned, out of order or outside blob */
@@ -135,7 +135,7 @@ typedef struct {
                                 /* 11 for code planes (wc_encode_u8_host)               */
     uint32_t chunk_bytes;       /* must be 8 (or 0 for the default)                     */
     uint32_t chunks_per_group;  /* G >= 1; 0 selects the default 128.  The GPU decoder  */
-                                /* of this build accepts only G = 128.                  */
+                                /* of this library accepts only G = 128.                */
     uint32_t n_threads;         /* host threads for encoding; 0 = all hardware threads  */
     uint32_t group_align;       /* A >= 1 elements per block; 0 selects the default 128. */
                                 /* A * max_code_len + 63 must not exceed 64 * G.  The   */

@@ -195,7 +195,7 @@ def test_plan_rejects_each_fault(wc):
     assert mutated(setb(pad, np.array([0x10], np.uint8))) == wc.WC_ERR_STREAM_BITS
     assert mutated(setb(s["off_tens"] + 8, _u64(s["n_elems"] + 1))) == wc.WC_ERR_TENSOR_TABLE
     assert mutated(setb(s["off_tens"], _u64(3))) == wc.WC_ERR_TENSOR_TABLE
-    # valid containers with a group size or block size this build does not decode
+    # valid containers with a group size or block size the GPU decoder does not accept
     b2 = wc.encode_host(wl.tensors(), chunks_per_group=2 * wc.GROUP_CHUNKS, layout="chunks")
     assert _plan_status(wc, b2) == wc.WC_ERR_UNSUPPORTED
     b3 = wc.encode_host(wl.tensors(), group_align=100, group_max_elems=4000, layout="chunks")
@@ -288,7 +288,7 @@ def test_plan_rejects_each_lanes_fault(wc, oracle_lib):
     # an offset that is not where the lane's bits begin: wc_plan cannot see it
     assert mutated(setb(lo + 2 * 11, np.frombuffer(np.uint16(int(s["lane_off"][0, 11]) + 1).tobytes(),
                                                    np.uint8))) in ok
-    # valid containers this build does not decode
+    # valid containers the GPU decoder does not accept
     b2 = wc.encode_host(wl.tensors(), layout="lanes", seg_max_bits=20000)
     assert _plan_status(wc, b2) == wc.WC_ERR_UNSUPPORTED
     b3 = wc.encode_host(wl.tensors(), layout="lanes", group_align=100, group_max_elems=4000)
