@@ -218,8 +218,10 @@ int wc_plan_info(const wc_plan_t* plan, uint64_t* n_elems, uint32_t* n_tensors,
  * wc_plan_stats -- container statistics and launch configuration: total
  * container bytes, stream bits, number of groups, the index widths of the
  * kernel's two LDS tables (codeword-start table, multi-codeword table), the
- * launch grid (workgroups) and the LDS bytes per workgroup.  Any output may
- * be NULL.
+ * launch grid (workgroups) and the LDS bytes per workgroup of the container's
+ * decode entry point (wc_decode_async for bf16, wc_decode_u8_async for code
+ * planes; the fused product launches 8-wave workgroups of its own).  Any
+ * output may be NULL.
  */
 int wc_plan_stats(const wc_plan_t* plan, uint64_t* container_bytes, uint64_t* stream_bits,
                   uint64_t* n_groups, uint32_t* count_bits, uint32_t* decode_bits, uint32_t* grid,
