@@ -207,6 +207,8 @@ int write_lanes(const SourceT<T>& src, uint64_t n, uint32_t n_tensors, const uin
         k0 = k1;
     }
     const uint64_t n_segs = s_elem.size() - 1;
+    uint64_t seg_max = 0;   // the largest segment: each thread's staging buffer
+    for (uint64_t g = 0; g < n_segs; ++g) seg_max = std::max<uint64_t>(seg_max, s_elem[g + 1] - s_elem[g]);
     constexpr bool kBf16 = sizeof(T) == 2;
     const Header h = layout_lanes(n, stream_bits, n_tensors, max_len, align, max_elems, seg_bits, n_segs,
                                   kBf16 ? kKindBf16 : kKindU8);
@@ -234,7 +236,7 @@ int write_lanes(const SourceT<T>& src, uint64_t n, uint32_t n_tensors, const uin
         if (g0 == g1) return;
         BitWriter bw(stream, s_bit[g0]);
         uint64_t pos = s_bit[g0];
-        std::vector<T> seg(max_elems);
+        std::vector<T> seg(seg_max);
         for (uint64_t g = g0; g < g1; ++g) {
             const uint64_t e0 = s_elem[g], m = s_elem[g + 1] - e0;
             src.for_range(e0, e0 + m, [&](uint64_t gi, const T* p, uint64_t k) {
@@ -374,6 +376,8 @@ int write_lanes_rans(const SourceT<T>& src, uint64_t n, uint32_t n_tensors, cons
         k0 = k1;
     }
     const uint64_t n_segs = s_elem.size() - 1;
+    uint64_t seg_max = 0;   // the largest segment: each thread's staging buffer
+    for (uint64_t g = 0; g < n_segs; ++g) seg_max = std::max<uint64_t>(seg_max, s_elem[g + 1] - s_elem[g]);
 
     // encode: each thread a run of segments into its own words
     const unsigned nt = (unsigned)std::max<uint64_t>(1, std::min<uint64_t>(nthreads, n_segs));
@@ -383,7 +387,7 @@ int write_lanes_rans(const SourceT<T>& src, uint64_t n, uint32_t n_tensors, cons
     std::atomic<bool> too_long{false};
     parallel_for(nt, [&](unsigned t) {
         const uint64_t g0 = n_segs * t / nt, g1 = n_segs * (t + 1) / nt;
-        std::vector<uint8_t> sym(max_elems);
+        std::vector<uint8_t> sym(seg_max);
         std::vector<uint16_t> pushed;
         for (uint64_t g = g0; g < g1; ++g) {
             const uint64_t e0 = s_elem[g], m = s_elem[g + 1] - e0;
