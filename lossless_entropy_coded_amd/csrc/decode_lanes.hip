@@ -131,8 +131,8 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    uint32_t* const sbuf = reinterpret_cast<uint32_t*>(dyn + wave * kLaneWaveBytes);
-    uint8_t* const ebuf = dyn + wave * kLaneWaveBytes + kLaneStageBytes;
+    uint32_t* const sbuf = reinterpret_cast<uint32_t*>(dyn + wave * kLaneWaveBytes + kLanePadBytes);
+    uint8_t* const ebuf = dyn + wave * kLaneWaveBytes + kLanePadBytes + kLaneStageBytes;
     uint8_t* const slot = ebuf + kLaneSlotBytes * lane;   // this lane's exponents, in its symbol order
 
     // wave w of workgroup b takes segments b*W + w, then every (grid * W)-th
@@ -305,8 +305,9 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
                 // instructions and LDS): no register window; each lookup
                 // re-reads its 32-bit window from the staged
                 // words: t = (bit position) - 1, words t >> 5 (arithmetic:
-                // -1 at position 0, the 4 bytes before the staging) and the
-                // next, shifted right by -position mod 32 (always below 32).
+                // -1 at position 0, the last word of the wave's pad, shifted
+                // out) and the next, shifted right by -position mod 32
+                // (always below 32).
                 // A lookup's symbols past the lane's last one (they belong
                 // to the next lane) land in the slot's spare bytes: p < nsym
                 // <= 64 before the store, so it ends by byte 67.  The words

@@ -119,7 +119,10 @@ struct DecodeParams {
 // kLanesMaxSegBits stream bits.
 constexpr uint32_t kLaneStageBytes = 2048;
 constexpr uint32_t kLaneSlotBytes = 68;
-constexpr uint32_t kLaneWaveBytes = kLaneStageBytes + kWaveLanes * kLaneSlotBytes;
+// Each wave's region starts with kLanePadBytes that nothing writes: a window
+// read at bit position 0 takes the word before the staging (and discards it).
+constexpr uint32_t kLanePadBytes = 16;
+constexpr uint32_t kLaneWaveBytes = kLanePadBytes + kLaneStageBytes + kWaveLanes * kLaneSlotBytes;
 constexpr uint32_t kLanesMaxSegBits = 15872;
 
 // Wavefronts per decode workgroup the kernels are built for.
