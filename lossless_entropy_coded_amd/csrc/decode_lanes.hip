@@ -179,6 +179,8 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
     // rANS with one symbol: its frequency 2^12 is stored as 0
     const bool rans_single =
         kRans && ((__builtin_amdgcn_readfirstlane(reinterpret_cast<const uint32_t*>(s_tab)[0]) >> 8) & 0xFFFu) == 0;
+    // code planes: each multi-codeword table entry holds one code at most
+    const bool one_code = kU8 && !kRans && p.one_code != 0;
 
     for (;;) {
         const uint64_t un = u + stride;
@@ -316,40 +318,63 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
                 // lane makes at most 64 lookups of at most 24 bits (at most
                 // word 548, byte 2195 of the wave's staging and slots).
                 int32_t t = (int32_t)pos - 1;
-                uint32_t p = 0;
-                // code planes (about one symbol per lookup): the symbols are
-                // gathered in a register and written as aligned words (the
-                // table's bytes past a lookup's symbols are 0); the last word
-                // ends by byte 67.  bf16 exponents for the fused product (two
-                // to three symbols per lookup): four byte stores at the count
-                // decoded so far.
-                uint32_t acc = 0;
-                while (p < nsym) {
-                    const int32_t k = t >> 5;
-                    const uint32_t top = __builtin_amdgcn_alignbit(sbuf[k], sbuf[k + 1], ~(uint32_t)t);
-                    uint2 e = s_dec[top >> (32 - KD)];
-                    if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
-                    const uint32_t pn = p + ((e.x >> 8) & 0xFFu);
-                    if constexpr (kU8) {
-                        const uint64_t comb = ((uint64_t)e.y << ((p & 3u) << 3)) | acc;
-                        if ((p ^ pn) >= 4u) {   // a word is complete
-                            *reinterpret_cast<uint32_t*>(slot + (p & ~3u)) = (uint32_t)comb;
-                            acc = (uint32_t)(comb >> 32);
-                        } else {
-                            acc = (uint32_t)comb;
+                if (one_code) {
+                    // code planes whose shortest code is longer than half the
+                    // table index: every lookup yields exactly one code (the
+                    // entry's other symbol bytes are 0), so four lookups fill
+                    // one aligned word.  A lane whose count is not a multiple
+                    // of four decodes up to three more, into the slot's
+                    // unused bytes; it still makes at most 64 lookups and
+                    // stores below byte 64.
+                    for (uint32_t q = 0; q < nsym; q += 4) {
+                        uint32_t w = 0;
+#pragma unroll
+                        for (uint32_t i = 0; i < 4; ++i) {
+                            const int32_t k = t >> 5;
+                            const uint32_t top = __builtin_amdgcn_alignbit(sbuf[k], sbuf[k + 1], ~(uint32_t)t);
+                            uint2 e = s_dec[top >> (32 - KD)];
+                            if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
+                            w |= e.y << (8 * i);
+                            t += (int32_t)((e.x >> 16) & 0xFFu);
                         }
-                    } else {
-                        uint8_t* const dst = slot + p;
-                        const uint32_t odd = __builtin_amdgcn_perm(e.y, e.y, 0x0C030C01u);   // [s1, 0, s3, 0]
-                        dst[0] = (uint8_t)e.y;
-                        dst[1] = (uint8_t)odd;
-                        dst[2] = (uint8_t)(e.y >> 16);
-                        dst[3] = (uint8_t)(odd >> 16);
+                        *reinterpret_cast<uint32_t*>(slot + q) = w;
                     }
-                    p = pn;
-                    t += (int32_t)((e.x >> 16) & 0xFFu);
+                } else {
+                    uint32_t p = 0;
+                    // code planes (about one symbol per lookup): the symbols are
+                    // gathered in a register and written as aligned words (the
+                    // table's bytes past a lookup's symbols are 0); the last word
+                    // ends by byte 67.  bf16 exponents for the fused product (two
+                    // to three symbols per lookup): four byte stores at the count
+                    // decoded so far.
+                    uint32_t acc = 0;
+                    while (p < nsym) {
+                        const int32_t k = t >> 5;
+                        const uint32_t top = __builtin_amdgcn_alignbit(sbuf[k], sbuf[k + 1], ~(uint32_t)t);
+                        uint2 e = s_dec[top >> (32 - KD)];
+                        if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
+                        const uint32_t pn = p + ((e.x >> 8) & 0xFFu);
+                        if constexpr (kU8) {
+                            const uint64_t comb = ((uint64_t)e.y << ((p & 3u) << 3)) | acc;
+                            if ((p ^ pn) >= 4u) {   // a word is complete
+                                *reinterpret_cast<uint32_t*>(slot + (p & ~3u)) = (uint32_t)comb;
+                                acc = (uint32_t)(comb >> 32);
+                            } else {
+                                acc = (uint32_t)comb;
+                            }
+                        } else {
+                            uint8_t* const dst = slot + p;
+                            const uint32_t odd = __builtin_amdgcn_perm(e.y, e.y, 0x0C030C01u);   // [s1, 0, s3, 0]
+                            dst[0] = (uint8_t)e.y;
+                            dst[1] = (uint8_t)odd;
+                            dst[2] = (uint8_t)(e.y >> 16);
+                            dst[3] = (uint8_t)(odd >> 16);
+                        }
+                        p = pn;
+                        t += (int32_t)((e.x >> 16) & 0xFFu);
+                    }
+                    if (kU8 && (p & 3u)) *reinterpret_cast<uint32_t*>(slot + (p & ~3u)) = acc;
                 }
-                if (kU8 && (p & 3u)) *reinterpret_cast<uint32_t*>(slot + (p & ~3u)) = acc;
             }
         }
 

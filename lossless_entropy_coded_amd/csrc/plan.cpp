@@ -49,6 +49,7 @@ struct wc_plan_s {
     uint32_t l2_cap = 0;         // long-code prefixes whose second-level entries are staged in LDS
     bool lanes = false;          // container version 3 (interleaved lanes)
     bool rans = false;           // coder rANS (version 3)
+    bool one_code = false;       // Huffman: each multi-codeword table entry holds one code at most
     uint32_t* d_tables = nullptr;
 };
 
@@ -305,6 +306,16 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         p->count_bits = 12;   // rANS: the 2^12-slot table takes the place of the 11-bit multi-codeword table
         p->decode_bits = 11;
     }
+    if (!p->rans) {
+        // no multi-codeword table entry holds two whole codes when the
+        // shortest code is longer than half the table index
+        uint32_t shortest = 0;
+        for (int s = 0; s < 256; ++s) {
+            const uint32_t L = blob_host[p->h.off_code_len + s];
+            if (L && (!shortest || L < shortest)) shortest = L;
+        }
+        p->one_code = shortest && 2 * shortest > p->decode_bits;
+    }
     {
         const uint32_t forced_waves = env_u32("WC_WAVES", 0);
         const bool ok = wc::supported_waves(forced_waves);
@@ -464,6 +475,7 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
     d.ebuf_bytes = p->ebuf_bytes;
     d.l2_cap = p->l2_cap;
     d.gap_packed = p->h.gap_bits == wc::kGapBitsPacked ? 1u : 0u;
+    d.one_code = p->one_code ? 1u : 0u;
     hipError_t e;
     if (p->lanes) {
         // the lane offsets sit where the gaps do; the kernel stages the tables
@@ -502,6 +514,7 @@ extern "C" int wc_decode_u8_async(const wc_plan_t* p, const void* blob_dev, uint
     d.ebuf_bytes = p->ebuf_bytes;
     d.l2_cap = p->l2_cap;
     d.gap_packed = p->h.gap_bits == wc::kGapBitsPacked ? 1u : 0u;
+    d.one_code = p->one_code ? 1u : 0u;
     const hipError_t e = wc::launch_decode_lanes(d, p->decode_bits, p->busy.waves, p->busy.grid, wc::kLanesToU8, p->rans,
                                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
@@ -599,6 +612,7 @@ extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, co
     d.ebuf_bytes = p->ebuf_bytes;
     d.l2_cap = p->l2_cap;
     d.gap_packed = p->h.gap_bits == wc::kGapBitsPacked ? 1u : 0u;
+    d.one_code = p->one_code ? 1u : 0u;
     d.dot.part = static_cast<float*>(work_dev);
     d.dot.row_group = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(work_dev) + rows_off);
     const uint64_t groups = wc::div_up(d.u_end - d.u_begin, p->busy.waves);

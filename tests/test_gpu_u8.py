@@ -92,10 +92,38 @@ def test_u8_workload_full_size(wc, oracle_lib, name):
     assert np.array_equal(got, oracle_lib.decode_u8(blob))
 
 
-def test_u8_corrupted_stream_stays_in_bounds(wc):
+@pytest.mark.parametrize("sigma,max_len,one_code,longest_over", [
+    (20.0, 0, True, False),     # shortest code 6 bits, none longer than the 11-bit index
+    (30.0, 24, True, True),     # shortest 6, longest 18: the long-code path inside one-code lookups
+    (20.0, 24, False, True),    # shortest 5: two codes can share a lookup
+    (3.0, 0, False, False),     # shortest 3: up to three codes per lookup
+])
+def test_u8_one_code_lookups(wc, oracle_lib, sigma, max_len, one_code, longest_over):
+    """Code planes whose shortest code is longer than half the 11-bit table
+    index never see two codes in one table entry, and the decoder takes one
+    code per lookup, four per aligned word; the others take the multi-code
+    loop.  Both are bit-exact against the input and the oracle."""
+    from container_view import sections
+    from lossless_entropy_coded_amd.synth import quantized_codes
+    rng = np.random.default_rng(int(sigma * 10) + max_len)
+    c = quantized_codes(rng, 300_000, 8, sigma)
+    blob = wc.encode_u8_host([c], max_code_len=max_len)
+    lens = sections(blob)["code_len"]
+    with wc.Plan(blob) as plan:
+        kd = plan.stats()["decode_bits"]
+    assert (2 * int(lens[lens > 0].min()) > kd) == one_code
+    assert (int(lens.max()) > kd) == longest_over
+    log(f"case: u8 one-code sigma={sigma} max_len={max_len} one_code={one_code}")
+    got = gpu_decode_u8(wc, blob)
+    assert np.array_equal(got, c)
+    assert np.array_equal(got, oracle_lib.decode_u8(blob))
+
+
+@pytest.mark.parametrize("name", ["int8_codes_8b", "int4_codes_8b"])
+def test_u8_corrupted_stream_stays_in_bounds(wc, name):
     from container_view import sections
     from lossless_entropy_coded_amd.synth import make_code_workload
-    wl = make_code_workload("int4_codes_8b", scale_rows=128)
+    wl = make_code_workload(name, scale_rows=128)
     blob = wc.encode_u8_host(wl.tensors())
     s = sections(blob)
     rng = np.random.default_rng(9)
