@@ -320,23 +320,32 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
                 int32_t t = (int32_t)pos - 1;
                 if (one_code) {
                     // code planes whose shortest code is longer than half the
-                    // table index: every lookup yields exactly one code (the
-                    // entry's other symbol bytes are 0), so four lookups fill
-                    // one aligned word.  A lane whose count is not a multiple
-                    // of four decodes up to three more, into the slot's
-                    // unused bytes; it still makes at most 64 lookups and
-                    // stores below byte 64.
+                    // table index and whose codes are at most 16 bits: every
+                    // lookup yields exactly one code (the entry's other
+                    // symbol bytes are 0), and four of them fit one 64-bit
+                    // window, read from three staged words.  Four lookups
+                    // fill one aligned word.  A lane whose count is not a
+                    // multiple of four decodes up to three more, into the
+                    // slot's unused bytes; it still makes at most 64 lookups
+                    // of at most 16 bits (at most word 530 of the wave's
+                    // staging and slots) and stores below byte 64.
                     for (uint32_t q = 0; q < nsym; q += 4) {
-                        uint32_t w = 0;
+                        const int32_t k = t >> 5;
+                        const uint32_t w1 = sbuf[k + 1];
+                        uint64_t win = (uint64_t)__builtin_amdgcn_alignbit(sbuf[k], w1, ~(uint32_t)t) << 32 |
+                                       __builtin_amdgcn_alignbit(w1, sbuf[k + 2], ~(uint32_t)t);
+                        uint32_t w = 0, used = 0;
 #pragma unroll
                         for (uint32_t i = 0; i < 4; ++i) {
-                            const int32_t k = t >> 5;
-                            const uint32_t top = __builtin_amdgcn_alignbit(sbuf[k], sbuf[k + 1], ~(uint32_t)t);
+                            const uint32_t top = (uint32_t)(win >> 32);
                             uint2 e = s_dec[top >> (32 - KD)];
                             if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
                             w |= e.y << (8 * i);
-                            t += (int32_t)((e.x >> 16) & 0xFFu);
+                            const uint32_t len = (e.x >> 16) & 0xFFu;
+                            win <<= len;
+                            used += len;
                         }
+                        t += (int32_t)used;
                         *reinterpret_cast<uint32_t*>(slot + q) = w;
                     }
                 } else {

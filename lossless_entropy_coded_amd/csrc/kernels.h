@@ -106,7 +106,7 @@ struct DecodeParams {
     uint32_t ebuf_bytes;     // exponent staging bytes per wave
     uint32_t l2_cap;         // long-code prefixes staged in LDS (0 .. kL2Prefixes)
     uint32_t gap_packed;     // chunks layout: gaps stored in 5 bits (else one byte each)
-    uint32_t one_code;       // lanes layout, Huffman: no multi-codeword table entry holds two codes
+    uint32_t one_code;       // lanes layout, Huffman: one code per table entry at most, all <= 16 bits
     DotParams dot;           // fused matrix-vector launches only
 };
 

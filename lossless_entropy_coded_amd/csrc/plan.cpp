@@ -49,7 +49,7 @@ struct wc_plan_s {
     uint32_t l2_cap = 0;         // long-code prefixes whose second-level entries are staged in LDS
     bool lanes = false;          // container version 3 (interleaved lanes)
     bool rans = false;           // coder rANS (version 3)
-    bool one_code = false;       // Huffman: each multi-codeword table entry holds one code at most
+    bool one_code = false;       // Huffman: one code per table entry at most, none longer than 16 bits
     uint32_t* d_tables = nullptr;
 };
 
@@ -308,13 +308,15 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
     }
     if (!p->rans) {
         // no multi-codeword table entry holds two whole codes when the
-        // shortest code is longer than half the table index
-        uint32_t shortest = 0;
+        // shortest code is longer than half the table index; four codes of at
+        // most 16 bits fit one 64-bit window
+        uint32_t shortest = 0, longest = 0;
         for (int s = 0; s < 256; ++s) {
             const uint32_t L = blob_host[p->h.off_code_len + s];
             if (L && (!shortest || L < shortest)) shortest = L;
+            longest = std::max(longest, L);
         }
-        p->one_code = shortest && 2 * shortest > p->decode_bits;
+        p->one_code = shortest && 2 * shortest > p->decode_bits && longest <= 16;
     }
     {
         const uint32_t forced_waves = env_u32("WC_WAVES", 0);

@@ -94,15 +94,17 @@ def test_u8_workload_full_size(wc, oracle_lib, name):
 
 @pytest.mark.parametrize("sigma,max_len,one_code,longest_over", [
     (20.0, 0, True, False),     # shortest code 6 bits, none longer than the 11-bit index
-    (30.0, 24, True, True),     # shortest 6, longest 18: the long-code path inside one-code lookups
+    (40.0, 24, True, True),     # shortest 6, longest 14: the long-code path inside one-code lookups
+    (30.0, 24, False, True),    # shortest 6, longest 18: four codes may not fit 64 bits
     (20.0, 24, False, True),    # shortest 5: two codes can share a lookup
     (3.0, 0, False, False),     # shortest 3: up to three codes per lookup
 ])
 def test_u8_one_code_lookups(wc, oracle_lib, sigma, max_len, one_code, longest_over):
     """Code planes whose shortest code is longer than half the 11-bit table
-    index never see two codes in one table entry, and the decoder takes one
-    code per lookup, four per aligned word; the others take the multi-code
-    loop.  Both are bit-exact against the input and the oracle."""
+    index never see two codes in one table entry; when no code is longer than
+    16 bits the decoder takes one code per lookup, four per 64-bit window and
+    per aligned word.  The others take the multi-code loop.  Both are
+    bit-exact against the input and the oracle."""
     from container_view import sections
     from lossless_entropy_coded_amd.synth import quantized_codes
     rng = np.random.default_rng(int(sigma * 10) + max_len)
@@ -111,7 +113,7 @@ def test_u8_one_code_lookups(wc, oracle_lib, sigma, max_len, one_code, longest_o
     lens = sections(blob)["code_len"]
     with wc.Plan(blob) as plan:
         kd = plan.stats()["decode_bits"]
-    assert (2 * int(lens[lens > 0].min()) > kd) == one_code
+    assert (2 * int(lens[lens > 0].min()) > kd and int(lens.max()) <= 16) == one_code
     assert (int(lens.max()) > kd) == longest_over
     log(f"case: u8 one-code sigma={sigma} max_len={max_len} one_code={one_code}")
     got = gpu_decode_u8(wc, blob)
