@@ -20,7 +20,19 @@ Prints one JSON line:
             `launch_us`: p10 / p50 / p90 of individually timed launches
   cpu_baseline  the CPU oracle's serial decode of the same container on one
             host core, repeated until about 10 s have elapsed (reported
-            baseline, not a target)
+            baseline, not a target), with the host CPU's model name
+  layouts   (default run) the same block in the chunks layout, the two-phase
+            count / scan / decode kernel: ms per launch and its fraction of
+            8 TB/s on its own algorithmic bytes
+  e2e       (default run) the 70B-shape block end to end: decode + 7 batch-1
+            GEMVs (arm A), the GEMVs on resident uncompressed bf16 (arm B),
+            the fused decode -> GEMV (arm C), and the decode alone
+
+Evidence rules: every launch of a run takes the next (container, output) copy
+in one rotation whose copies together exceed 1 GiB (four times the 256 MiB
+Infinity Cache), so a copy's previous use is at least that much traffic back;
+every output the timed launches write is first filled with a canary (or NaN)
+and compared with the expected bits after the timed region.
 """
 from __future__ import annotations
 
@@ -39,6 +51,9 @@ if ROOT not in sys.path:
 METRIC = "decompressed bf16 GB/s and % of HBM roofline (1 MI355X), bit-exact"
 METRIC_CODES = "decompressed 8-bit code GB/s and % of HBM roofline (1 MI355X), bit-exact"
 HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 1 << 30          # rotated (container, output) bytes: 4 x the 256 MiB Infinity Cache
+CANARY16 = 0x5A5A               # fills timed bf16 outputs before the timed region
+CANARY8 = 0xA5
 CSRC = os.path.join(ROOT, "lossless_entropy_coded_amd", "csrc")
 KERNEL_SOURCES = {"chunks": os.path.join(CSRC, "decode.hip"), "lanes": os.path.join(CSRC, "decode_lanes.hip")}
 # counter records per kernel variant: layout, and the coder when not Huffman
@@ -68,6 +83,41 @@ def recorded_traffic(workload: str, layout: str = "chunks", coder: str = "huffma
     return rec.get("traffic_bytes_per_launch")
 
 
+def progress(msg: str) -> None:
+    """One line on stderr per phase of a run (stdout carries only the JSON line)."""
+    print(f"bench.py: {msg}", file=sys.stderr, flush=True)
+
+
+def rotation_copies(per_copy_bytes: int) -> int:
+    """(container, output) copies to rotate through: together at least
+    ROTATE_BYTES, so that the copy a launch reads was last touched at least
+    ROTATE_BYTES - per_copy bytes of other traffic earlier."""
+    return max(2, math.ceil(ROTATE_BYTES / max(1, per_copy_bytes)))
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (the first 'model name' of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def algorithmic_bytes(n: int, stream_bits: int, n_groups: int, layout: str, gap_bits: int, codes: bool) -> int:
+    """Bytes the decode must move: the sm plane (bf16 kinds), the stream, the
+    per-chunk gaps (chunks layout) or per-lane offsets (lanes layout), the
+    group or segment table, and the decoded output."""
+    n_chunks = -(-stream_bits // 64)
+    aux = -(-gap_bits * n_chunks // 8) if layout == "chunks" else 2 * 64 * n_groups
+    read = (0 if codes else n) + -(-stream_bits // 8) + aux + 16 * (n_groups + 1)
+    return read + (1 if codes else 2) * n
+
+
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +144,9 @@ def parse_args():
                          "uncompressed weights (prints its own JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain 1 GiB device copy instead (for scaling HBM counters)")
+    ap.add_argument("--extras", choices=["on", "off"], default="on",
+                    help="with the default workload and layout, also time the chunks layout and the 70B-block "
+                         "end-to-end arms and add them to the JSON line (layouts, e2e)")
     return ap.parse_args()
 
 
@@ -172,108 +225,269 @@ def _timed(torch, stream, fn, steps):
     return a.elapsed_time(b) / steps
 
 
-def end_to_end(args):
+class Rotation:
+    """Device copies of one container and of its output, used in turn by every
+    launch of a run (one counter across settle, warm-up and timed launches)."""
+
+    def __init__(self, torch, blob, n, out_dtype, copies):
+        self.copies = copies
+        self.owners, self.blobs, self.outs = [], [], []
+        for _ in range(copies):
+            own, view = aligned_device_copy(torch, blob)
+            self.owners.append(own)
+            self.blobs.append(view)
+            self.outs.append(torch.empty(n, dtype=out_dtype, device="cuda"))
+        self.it = 0
+
+    def next(self):
+        k = self.it % self.copies
+        self.it += 1
+        return k
+
+
+def time_decode(torch, wc, plan, blob, raw, out_bytes, codes, args, stream):
+    """Time `args.steps` back-to-back whole-container decode launches.
+
+    Every launch takes the next copy of the rotation.  Before the timed
+    launches every output copy is filled with a canary; after them each copy a
+    timed launch wrote must equal the expected bits.  Returns the timing dict."""
+    import numpy as np
+    n = plan.n_elems
+    decode = wc.decode_u8_async if codes else wc.decode_async
+    out_dtype = torch.uint8 if codes else torch.int16
+    copies = rotation_copies(blob.size + out_bytes * n)
+    rot = Rotation(torch, blob, n, out_dtype, copies)
+    ref = torch.from_numpy(np.ascontiguousarray(raw)).cuda()
+
+    def launch():
+        k = rot.next()
+        decode(plan, rot.blobs[k], rot.outs[k], stream)
+        return k
+
+    k = launch()
+    torch.cuda.synchronize()
+    if not torch.equal(rot.outs[k], ref):
+        print("bench.py: decode is NOT bit-exact", file=sys.stderr)
+        sys.exit(3)
+    # settle: untimed launches until the GPU has run the decode for settle_ms
+    settle_launches, settled_ms = 0, 0.0
+    while settled_ms < args.settle_ms and settle_launches < 5000:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(25):
+            launch()
+        b.record(stream)
+        b.synchronize()
+        settled_ms += a.elapsed_time(b)
+        settle_launches += 25
+    for _ in range(args.warmup):
+        launch()
+    # canary in every output copy, then the timed launches: HIP events on the
+    # launch stream around K back-to-back launches (a step is one launch)
+    canary = CANARY8 if codes else CANARY16
+    with torch.cuda.stream(stream):
+        for o in rot.outs:
+            o.fill_(canary)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    written = set()
+    for _ in range(args.steps):
+        written.add(launch())
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    bit_exact = all(torch.equal(rot.outs[k], ref) for k in sorted(written))
+    if not bit_exact:
+        print("bench.py: timed outputs are NOT bit-exact", file=sys.stderr)
+        sys.exit(3)
+    # spread of single launches (each bracketed by its own events), after the timed region
+    singles = []
+    for _ in range(min(args.steps, 50)):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        launch()
+        b.record(stream)
+        b.synchronize()
+        singles.append(a.elapsed_time(b) * 1e3)
+    singles.sort()
+
+    def pct(q):
+        return round(singles[min(len(singles) - 1, int(q * len(singles)))], 1)
+
+    del rot, ref
+    torch.cuda.empty_cache()
+    return {"total_ms": total_ms, "kernel_avg_ms": total_ms / args.steps, "copies": copies,
+            "rotated_bytes": copies * (blob.size + out_bytes * n), "settle_launches": settle_launches,
+            "timed_outputs_checked": len(written), "bit_exact": bit_exact,
+            "launch_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)}}
+
+
+def e2e_measure(torch, wc, name, layout, coder, steps, warmup, opts, stream):
     """The 70B-shape block: decode the whole block and run a batch-1 bf16 GEMV
     over each of its 7 matrices (arm A), against the same 7 GEMVs on resident
-    uncompressed weights (arm B), and the fused decode -> GEMV of all 7 matrices
-    in one call, which never writes the decoded weights (arm C).  Arms A and B run the same
-    GEMV kernel, so their outputs must be bit-identical; arm C sums in another
-    fixed order and must agree with B within both kernels' fp32 rounding
-    bounds.  Both are checked on the timed outputs."""
+    uncompressed weights (arm B), and the fused decode -> GEMV of all 7
+    matrices in one call, which never writes the decoded weights (arm C).
+    Arms A and B run the same GEMV kernel, so their outputs must be
+    bit-identical; arm C sums in another fixed order and must agree with B
+    within both kernels' fp32 rounding bounds.  Every output of a timed arm is
+    filled with NaN (the decoded weights with a canary) before it and checked
+    after it.  Returns (record, ok)."""
     import numpy as np
-    import torch
-    from lossless_entropy_coded_amd import wc
     from lossless_entropy_coded_amd.synth import gemv_input, make_workload
 
-    name = args.workload if args.workload != "block_8b" else "block_70b"
+    progress(f"{name}: generating and encoding ({layout}, {coder})")
+    t_gen = time.perf_counter()
     wl = make_workload(name)
-    blob = wc.encode_host(wl.tensors(), layout=args.layout, coder=args.coder, **code_len_opt(args))
+    blob = wc.encode_host(wl.tensors(), layout=layout, coder=coder, **opts)
+    t_gen = time.perf_counter() - t_gen
+    progress(f"{name}: timing arms A, B, C and the decode alone")
     plan = wc.Plan(blob, device=0)
     n = wl.n
     mats = [(k, s[0], s[1]) for k, s in enumerate(wl.shapes) if len(s) == 2]
-    copies = 2
-    owners, blobs, outs, origs = [], [], [], []
-    for _ in range(copies):
-        own, view = aligned_device_copy(torch, blob)
-        owners.append(own)
-        blobs.append(view)
-        outs.append(torch.empty(n, dtype=torch.int16, device="cuda"))
-        origs.append(torch.from_numpy(wl.bits.view(np.int16)).cuda())
+    copies = rotation_copies(blob.size + 2 * n)
+    rot = Rotation(torch, blob, n, torch.int16, copies)
+    origs = [torch.from_numpy(wl.bits.view(np.int16)).cuda() for _ in range(copies)]
     xs = {c: torch.from_numpy(gemv_input(c).view(np.int16)).cuda() for _, _, c in mats}
     ya = [torch.empty(r, dtype=torch.float32, device="cuda") for _, r, _ in mats]
     yb = [torch.empty(r, dtype=torch.float32, device="cuda") for _, r, _ in mats]
     yc = [torch.empty(r, dtype=torch.float32, device="cuda") for _, r, _ in mats]
     ops = [(k, c, xs[c], yc[j]) for j, (k, r, c) in enumerate(mats)]
     work_bytes = wc.decode_gemv_work_bytes(plan, ops)
-    work = torch.empty(work_bytes // 4 + 64, dtype=torch.float32, device="cuda")
-    work = work[(-work.data_ptr()) % 256 // 4:]
-    stream = torch.cuda.current_stream()
+    work_own = torch.empty(work_bytes // 4 + 64, dtype=torch.float32, device="cuda")
+    work = work_own[(-work_own.data_ptr()) % 256 // 4:]
 
     def gemvs(src, ys):
         for j, (k, r, c) in enumerate(mats):
             off = plan.tensor_offsets[k]
             wc.gemv_bf16_async(src[off:off + r * c], r, c, xs[c], ys[j], stream)
 
-    def arm_a(k):
-        wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
-        gemvs(outs[k % copies], ya)
+    touched = set()
 
-    def arm_b(k):
-        gemvs(origs[k % copies], yb)
+    def arm_a(_):
+        k = rot.next()
+        touched.add(k)
+        wc.decode_async(plan, rot.blobs[k], rot.outs[k], stream)
+        gemvs(rot.outs[k], ya)
 
-    def decode_only(k):
-        wc.decode_async(plan, blobs[k % copies], outs[k % copies], stream)
+    def arm_b(i):
+        gemvs(origs[i % copies], yb)
 
-    def arm_c(k):
-        wc.decode_gemv_async(plan, blobs[k % copies], ops, work, work_bytes, stream)
+    def decode_only(_):
+        k = rot.next()
+        touched.add(k)
+        wc.decode_async(plan, rot.blobs[k], rot.outs[k], stream)
 
-    _timed(torch, stream, arm_a, max(40, args.warmup))          # settle clocks, warm up both arms
-    _timed(torch, stream, arm_b, max(40, args.warmup))
-    _timed(torch, stream, arm_c, max(40, args.warmup))
-    steps = args.steps
+    def arm_c(_):
+        wc.decode_gemv_async(plan, rot.blobs[rot.next()], ops, work, work_bytes, stream)
+
+    def fill(tensors, value):
+        with torch.cuda.stream(stream):
+            for t in tensors:
+                t.fill_(value)
+
+    def outs_exact():
+        ok = all(torch.equal(rot.outs[k], origs[0]) for k in sorted(touched))
+        touched.clear()
+        return ok
+
+    warm = max(40, warmup)
+    for arm in (arm_a, arm_b, arm_c):                  # settle clocks, warm up every arm
+        _timed(torch, stream, arm, warm)
+    fill(rot.outs, CANARY16)
+    fill(ya, float("nan"))
+    touched.clear()
     ms_a = _timed(torch, stream, arm_a, steps)
+    exact_a = outs_exact()
+    fill(yb, float("nan"))
     ms_b = _timed(torch, stream, arm_b, steps)
+    fill(yc, float("nan"))
     ms_c = _timed(torch, stream, arm_c, steps)
+    fill(rot.outs, CANARY16)
     ms_dec = _timed(torch, stream, decode_only, steps)
+    exact_dec = outs_exact()
     identical = all(torch.equal(a.view(torch.int32), b.view(torch.int32)) for a, b in zip(ya, yb))
-    exact = torch.equal(outs[(steps - 1) % copies], origs[0])
+    finite = all(bool(torch.isfinite(y).all()) for y in ya + yb + yc)
     # arm C against arm B: |yc - yb| <= (fused bound + GEMV bound) * 2^-24 * sum |w x|,
     # with sum |w x| from the GEMV kernel on the magnitudes (sign bits cleared)
     fused_ok = True
     for j, (t, r, c) in enumerate(mats):
         off = plan.tensor_offsets[t]
         mag = torch.empty(r, dtype=torch.float32, device="cuda")
-        wc.gemv_bf16_async(origs[0][off:off + r * c] & 0x7FFF, r, c, xs[c] & 0x7FFF, mag, stream)
+        wc.gemv_bf16_async((origs[0][off:off + r * c] & 0x7FFF).contiguous(), r, c, (xs[c] & 0x7FFF).contiguous(),
+                           mag, stream)
         terms = (12 + 8 + 6 + c // wc.GROUP_ALIGN + 2) + (c // 64 + 14)
         fused_ok &= bool(((yc[j] - yb[j]).abs() <= 1.05 * terms * 2.0 ** -24 * mag).all().item())
-    if not (identical and exact and fused_ok):
-        print(f"bench.py --e2e: outputs disagree (A==B {identical}, decode exact {exact}, "
-              f"C~B {fused_ok})", file=sys.stderr)
-        sys.exit(3)
+    ok = identical and exact_a and exact_dec and finite and fused_ok
     weight_bytes = 2 * sum(r * c for _, r, c in mats)
-    line = {
-        "metric": "end-to-end batch-1 bf16 GEMV over a 70B-shape block: decode + GEMV vs GEMV on uncompressed weights",
-        "value": round(ms_a, 4), "unit": "ms", "n_gpus": 1, "steps": steps, "warmup": max(40, args.warmup),
-        "higher_is_better": False, "vs_baseline": None, "dtype": "bf16 in, fp32 accumulate",
-        "data": "synthetic: seeded bf16 weights (70B-block shapes, N(0, 0.015)), x ~ N(0, 1) in bf16",
-        "config": {"workload": f"{name}: decode of the whole block, then q,k,v,o,gate,up,down GEMVs "
-                               f"(x length = each matrix's in-dimension)",
-                   "layout": args.layout, "coder": args.coder, "n_elems": n, "container_bytes": int(blob.size),
-                   "weight_bytes": weight_bytes},
+    rec = {
+        "workload": f"{name}: decode of the whole block, then q,k,v,o,gate,up,down batch-1 GEMVs "
+                    f"(x length = each matrix's in-dimension)",
+        "layout": layout, "coder": coder, "n_elems": n, "container_bytes": int(blob.size),
+        "weight_bytes": weight_bytes, "steps": steps, "warmup": warm, "rotating_copies": copies,
         "arm_a_decode_plus_gemv_ms": round(ms_a, 4),
         "arm_b_uncompressed_gemv_ms": round(ms_b, 4),
         "arm_c_fused_decode_gemv_ms": round(ms_c, 4),
         "decode_only_ms": round(ms_dec, 4),
         "ratio_a_over_b": round(ms_a / ms_b, 3),
         "ratio_c_over_b": round(ms_c / ms_b, 3),
-        "fused_GBps": round((blob.size) / (ms_c * 1e-3) / 1e9, 1),
+        "fused_container_GBps": round(blob.size / (ms_c * 1e-3) / 1e9, 1),
+        "fused_frac_of_hbm_peak": round(blob.size / (ms_c * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "gemv_weight_GBps": round(weight_bytes / (ms_b * 1e-3) / 1e9, 1),
         "decode_roofline_frac": round((blob.size + 2 * n) / (ms_dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "outputs_bit_identical": identical,
+        "outputs_bit_identical_a_b": identical,
+        "decoded_weights_bit_exact": exact_a and exact_dec,
         "fused_within_bound": fused_ok,
+        "host_prep_s": round(t_gen, 2),
+    }
+    plan.close()
+    del rot, origs, work_own
+    torch.cuda.empty_cache()
+    return rec, ok
+
+
+def end_to_end(args):
+    """--e2e: the 70B-block arms as a JSON line of their own."""
+    import torch
+    from lossless_entropy_coded_amd import wc
+    name = args.workload if args.workload != "block_8b" else "block_70b"
+    rec, ok = e2e_measure(torch, wc, name, args.layout, args.coder, args.steps, args.warmup, code_len_opt(args),
+                          torch.cuda.current_stream())
+    if not ok:
+        print(f"bench.py --e2e: outputs disagree: {json.dumps(rec)}", file=sys.stderr)
+        sys.exit(3)
+    line = {
+        "metric": "end-to-end batch-1 bf16 GEMV over a 70B-shape block: decode + GEMV vs GEMV on uncompressed weights",
+        "value": rec["arm_a_decode_plus_gemv_ms"], "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": rec["warmup"], "higher_is_better": False, "vs_baseline": None, "dtype": "bf16 in, fp32 accumulate",
+        "data": "synthetic: seeded bf16 weights (70B-block shapes, N(0, 0.015)), x ~ N(0, 1) in bf16",
+        "config": {"workload": rec["workload"], "layout": args.layout, "coder": args.coder},
+        **{k: v for k, v in rec.items() if k not in ("workload", "layout", "coder")},
     }
     print(json.dumps(line), flush=True)
+
+
+def layout_record(torch, wc, wl, layout, args, stream):
+    """The same workload in another layout, timed like the headline."""
+    t = time.perf_counter()
+    blob = wc.encode_host(wl.tensors(), layout=layout)
+    t = time.perf_counter() - t
+    plan = wc.Plan(blob, device=0)
+    st = plan.stats()
+    alg = algorithmic_bytes(wl.n, st["stream_bits"], st["n_groups"], layout, 8, False)
+    tm = time_decode(torch, wc, plan, blob, wl.bits.view("int16"), 2, False, args, stream)
     plan.close()
+    frac = alg / (tm["kernel_avg_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS
+    return {"kernel": "decode_kernel (per-chunk gaps; count, DPP scan, decode)" if layout == "chunks" else
+            "decode_lanes_kernel", "container_bytes": int(blob.size), "algorithmic_bytes_per_launch": alg,
+            "ms": round(tm["kernel_avg_ms"], 5), "decompressed_GBps": round(2 * wl.n / (tm["kernel_avg_ms"] * 1e-3)
+                                                                            / 1e9, 1),
+            "frac": round(frac, 4), "bit_exact": tm["bit_exact"], "launch_us": tm["launch_us"],
+            "rotating_copies": tm["copies"], "traffic": recorded_traffic(args.workload, layout),
+            "host_prep_s": round(t, 2)}
 
 
 def main():
@@ -308,101 +522,47 @@ def main():
     if args.gap_bits != 8 and args.layout != "chunks":
         print("bench.py: --gap-bits applies to the chunks layout", file=sys.stderr)
         sys.exit(2)
+    progress(f"{args.workload}: generating and encoding ({args.layout}, {args.coder})")
     t_gen = time.perf_counter()
     if codes:
         wl = make_code_workload(args.workload)
         blob = wc.encode_u8_host(wl.tensors(), coder=args.coder, **code_len_opt(args))
-        raw, out_bytes, out_dtype, decode = wl.codes, 1, torch.uint8, wc.decode_u8_async
+        raw, out_bytes = wl.codes, 1
     else:
         wl = make_workload(args.workload)
         blob = wc.encode_host(wl.tensors(), layout=args.layout, coder=args.coder, **code_len_opt(args))
-        raw, out_bytes, out_dtype, decode = wl.bits.view(np.int16), 2, torch.int16, wc.decode_async
+        raw, out_bytes = wl.bits.view(np.int16), 2
     t_gen = time.perf_counter() - t_gen
     n = wl.n
     plan = wc.Plan(blob, device=0)
     st = plan.stats()
     stream_bits = st["stream_bits"]
-    # what the kernel must read: sm plane (bf16), stream, per-chunk gaps (v2)
-    # or per-lane offsets (v3), group/segment table; then what it writes
-    n_chunks = -(-stream_bits // 64)
-    aux = (-(-args.gap_bits * n_chunks // 8) if args.layout == "chunks" else 2 * 64 * st["n_groups"])
-    alg_read = (0 if codes else n) + -(-stream_bits // 8) + aux + 16 * (st["n_groups"] + 1)
-    alg_bytes = alg_read + out_bytes * n
-
-    per_copy = blob.size + out_bytes * n
-    copies = max(2, min(64, math.ceil((1 << 30) / per_copy)))
-    blobs, outs, owners = [], [], []
-    for _ in range(copies):
-        own, view = aligned_device_copy(torch, blob)
-        owners.append(own)
-        blobs.append(view)
-        outs.append(torch.empty(n, dtype=out_dtype, device="cuda"))
-    ref = torch.from_numpy(raw).cuda()
-
+    alg_bytes = algorithmic_bytes(n, stream_bits, st["n_groups"], args.layout, args.gap_bits, codes)
     stream = torch.cuda.current_stream()
-    decode(plan, blobs[0], outs[0], stream)
-    torch.cuda.synchronize()
-    if not torch.equal(outs[0], ref):
-        print("bench.py: decode is NOT bit-exact", file=sys.stderr)
-        sys.exit(3)
-
-    # settle: untimed launches until the GPU has run the decode for settle_ms
-    settle_launches, settled_ms = 0, 0.0
-    while settled_ms < args.settle_ms and settle_launches < 5000:
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for k in range(25):
-            decode(plan, blobs[k % copies], outs[k % copies], stream)
-        b.record(stream)
-        b.synchronize()
-        settled_ms += a.elapsed_time(b)
-        settle_launches += 25
-    for k in range(args.warmup):
-        decode(plan, blobs[k % copies], outs[k % copies], stream)
-    # HIP events on the launch stream around the K back-to-back launches; a
-    # step is exactly one launch of the decode kernel, so the average launch
-    # duration is the timed region divided by K
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for k in range(args.steps):
-        decode(plan, blobs[k % copies], outs[k % copies], stream)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    kernel_avg_ms = total_ms / args.steps
-    bit_exact = all(torch.equal(outs[k % copies], ref) for k in range(min(copies, args.steps)))
-    if not bit_exact:
-        print("bench.py: timed outputs are NOT bit-exact", file=sys.stderr)
-        sys.exit(3)
-
+    progress(f"{args.workload}: timing {args.steps} decode launches")
+    tm = time_decode(torch, wc, plan, blob, raw, out_bytes, codes, args, stream)
+    total_ms = tm["total_ms"]
+    kernel_avg_ms = tm["kernel_avg_ms"]
     ms_per_step = total_ms / args.steps
     value = out_bytes * n / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (kernel_avg_ms * 1e-3) / 1e9
-
-    # spread of single launches (each bracketed by its own events), after the timed region
-    singles = []
-    for k in range(min(args.steps, 50)):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        decode(plan, blobs[k % copies], outs[k % copies], stream)
-        b.record(stream)
-        b.synchronize()
-        singles.append(a.elapsed_time(b) * 1e3)
-    singles.sort()
-
-    def pct(q):
-        return round(singles[min(len(singles) - 1, int(q * len(singles)))], 1)
-
-    del blobs, outs, owners, ref
-    torch.cuda.empty_cache()
     copy_gbps = copy_rate(torch, alg_bytes)
+
+    extras = (args.extras == "on" and args.workload == "block_8b" and args.layout == "lanes"
+              and args.coder == "huffman" and not args.max_code_len)
+    layouts = e2e = None
+    if extras:
+        progress(f"{args.workload}: timing the chunks layout")
+        layouts = {"chunks": layout_record(torch, wc, wl, "chunks", args, stream)}
+        rec, ok = e2e_measure(torch, wc, "block_70b", "lanes", "huffman", args.steps, args.warmup, {}, stream)
+        if not ok:
+            print(f"bench.py: 70B-block arms disagree: {json.dumps(rec)}", file=sys.stderr)
+            sys.exit(3)
+        e2e = rec
 
     cpu = None
     if args.cpu_baseline == "on":
+        progress(f"{args.workload}: timing the CPU oracle")
         import oracle
         reps, spent = 0, 0.0
         while reps < 1 or (spent < 10.0 and reps < 8):
@@ -411,7 +571,8 @@ def main():
             spent += time.perf_counter() - t
             reps += 1
             assert np.array_equal(dec, wl.codes if codes else wl.bits)
-        cpu = {"value": round(out_bytes * n * reps / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": round(out_bytes * n * reps / spent / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "cpu_model": cpu_model(), "kind": "oracle",
                "sample": f"the whole {args.workload} container ({n} elements) decoded {reps} times by the serial "
                          f"{'rANS decoder (linear slot search)' if args.coder == 'rans' else 'bit-by-bit trie decoder'} "
                          f"with every container check: {spent:.1f} s on one host core"}
@@ -447,9 +608,11 @@ def main():
             "decode_bits": st["decode_bits"],
             "grid": st["grid"],
             "lds_bytes": st["lds_bytes"],
-            "rotating_copies": copies,
-            "settle_launches": settle_launches,
-            "bit_exact": bit_exact,
+            "rotating_copies": tm["copies"],
+            "rotated_bytes": tm["rotated_bytes"],
+            "settle_launches": tm["settle_launches"],
+            "timed_outputs_checked": tm["timed_outputs_checked"],
+            "bit_exact": tm["bit_exact"],
             "host_prep_s": round(t_gen, 2),
         },
         "roofline": {
@@ -461,12 +624,16 @@ def main():
             "traffic": recorded_traffic(args.workload, args.layout, args.coder),
             "algorithmic_bytes_per_launch": alg_bytes,
             "kernel_avg_ms": round(kernel_avg_ms, 5),
-            "launch_us": {"p10": pct(0.1), "p50": pct(0.5), "p90": pct(0.9)},
+            "launch_us": tm["launch_us"],
             "copy_GBps": round(copy_gbps, 1),
             "frac_of_copy": round(achieved / copy_gbps, 4),
         },
         "cpu_baseline": cpu,
     }
+    if layouts is not None:
+        line["layouts"] = layouts
+    if e2e is not None:
+        line["e2e"] = e2e
     print(json.dumps(line), flush=True)
     plan.close()
 

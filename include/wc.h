@@ -197,12 +197,24 @@ typedef struct wc_plan_s wc_plan_t;   /* opaque, immutable after creation */
 
 /*
  * wc_plan -- validate a container held in host memory and prepare decoding on
- * HIP device hip_device: parses and checks every section (each failure has
- * its own WC_ERR_* code), builds the decode tables for the container's
- * codebook on that device (a small plan-owned device buffer, freed by
- * wc_plan_destroy) and chooses the launch configuration.  The host blob is
- * read only during this call.  The device copy of the same bytes that is
- * later passed to wc_decode_async is owned by the caller.
+ * HIP device hip_device (DFloat11 page, abstract, design point (ii): the
+ * kernel places every thread's reads and writes through small auxiliary
+ * variables, so those variables -- per-chunk gaps or lane offsets, the group
+ * table -- are checked here, once, before any kernel trusts them; point (i):
+ * the compact decode tables that fit in on-chip memory are built here).
+ * Parses and checks every section (each failure has its own WC_ERR_* code:
+ * a wrong magic or fixed field, a truncated blob, a section out of bounds, a
+ * code length above the limit, an incomplete prefix code, a gap or lane
+ * offset out of range, a group table that is not increasing or not closed by
+ * {n, stream_bits}, inconsistent stream sizes, a tensor table that is not a
+ * partition; WC_ERR_UNSUPPORTED for a valid container the GPU decoder cannot
+ * decode), builds the decode tables for the container's codebook on that
+ * device (a small plan-owned device buffer, freed by wc_plan_destroy) and
+ * chooses the launch configuration.  The host blob is read only during this
+ * call; nothing is kept from it.  The device copy of the same bytes that is
+ * later passed to wc_decode_async is owned by the caller.  Returns
+ * WC_ERR_HIP if the device cannot be used, WC_ERR_NOMEM if the table buffer
+ * cannot be allocated; *plan is NULL on any failure.
  */
 int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_device, wc_plan_t** plan);
 
@@ -236,7 +248,10 @@ int wc_plan_format(const wc_plan_t* plan, uint32_t* version, uint32_t* elem_kind
 
 /*
  * wc_decode_async -- decode every tensor of the container in ONE kernel launch
- * on `stream` (a hipStream_t; NULL = the device's null stream).
+ * on `stream` (a hipStream_t; NULL = the device's null stream): DFloat11
+ * page, abstract, design point (iii), decompresses a whole transformer block
+ * at once to cut latency; the output is bit-for-bit the original bf16 words
+ * (the same abstract; the Llama2-7B page's abstract: lossless).
  *   blob_dev  device pointer to the same bytes given to wc_plan, 256-byte aligned;
  *   out_dev   device pointer to n_elems bf16 words (caller-owned), 16-byte
  *             aligned; tensor k is out_dev[tensor_offsets[k] ...].

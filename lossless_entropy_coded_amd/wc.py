@@ -9,6 +9,13 @@ no Python or CPU fallback for any entry point.
 PyTorch is used only as the owner of device memory and streams: callers pass
 tensors (or raw integer device pointers) and the binding forwards
 ``data_ptr()`` and ``torch.cuda.current_stream().cuda_stream``.
+
+The C entry points receive bare pointers without sizes, so before forwarding
+a tensor the binding checks what the kernels will touch: the tensor must be a
+CUDA tensor on the plan's device, contiguous, and at least as large as the
+bytes the call reads or writes.  A failed check raises ``WCError`` with
+``WC_ERR_INVALID_ARG`` and nothing is launched.  Raw integer pointers are
+forwarded unchecked (the C side checks their alignment only).
 """
 from __future__ import annotations
 
@@ -118,9 +125,9 @@ EXPORTED = ("wc_encode_host", "wc_encode_u8_host", "wc_free_host", "wc_plan", "w
 
 
 class WCError(RuntimeError):
-    def __init__(self, status: int, call: str):
+    def __init__(self, status: int, call: str, detail: str = ""):
         self.status = status
-        super().__init__(f"{call} failed: {status_str(status)} ({status})")
+        super().__init__(f"{call} failed: {status_str(status)} ({status})" + (f": {detail}" if detail else ""))
 
 
 def status_str(status: int) -> str:
@@ -218,6 +225,7 @@ class Plan:
         _check(_lib.wc_plan_info(self._h, None, None, offs, nums), "wc_plan_info")
         self.n_elems = n.value
         self.n_tensors = nt.value
+        self.container_bytes = self.stats()["container_bytes"]
         self.tensor_offsets = [offs[i] for i in range(nt.value)]
         self.tensor_numels = [nums[i] for i in range(nt.value)]
 
@@ -265,23 +273,41 @@ def _ptr(x) -> int:
     return int(x.data_ptr()) if hasattr(x, "data_ptr") else int(x)
 
 
+def _require(t, nbytes: int, device, what: str, call: str) -> None:
+    """Check a tensor argument before its pointer goes to C: a CUDA tensor on
+    `device` (None: any), contiguous, holding at least `nbytes` bytes.  Raw
+    integer pointers are not checked."""
+    if not hasattr(t, "data_ptr"):
+        return
+    problem = None
+    if not getattr(t, "is_cuda", False):
+        problem = "is not a CUDA tensor"
+    elif device is not None and t.device.index is not None and t.device.index != device:
+        problem = f"is on cuda:{t.device.index}, not on cuda:{device}"
+    elif not t.is_contiguous():
+        problem = "is not contiguous"
+    elif t.numel() * t.element_size() < nbytes:
+        problem = f"holds {t.numel() * t.element_size()} bytes, fewer than the {nbytes} the call touches"
+    if problem:
+        raise WCError(WC_ERR_INVALID_ARG, call, f"{what} {problem}")
+
+
 def decode_async(plan: Plan, blob_dev, out_dev, stream=None) -> None:
     """wc_decode_async: one launch decoding the whole container into out_dev.
 
     blob_dev / out_dev: torch device tensors (or raw device pointers).  stream:
     a torch.cuda.Stream, a raw hipStream_t integer, or None for torch's current
     stream."""
-    if stream is None:
-        import torch
-        stream = torch.cuda.current_stream().cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
+    _require(blob_dev, plan.container_bytes, plan.device, "blob_dev", "wc_decode_async")
+    _require(out_dev, 2 * plan.n_elems, plan.device, "out_dev", "wc_decode_async")
     _check(_lib.wc_decode_async(plan.handle, ctypes.c_void_p(_ptr(blob_dev)), ctypes.c_void_p(_ptr(out_dev)),
-                                ctypes.c_void_p(int(stream))), "wc_decode_async")
+                                ctypes.c_void_p(_stream_handle(stream))), "wc_decode_async")
 
 
 def decode_u8_async(plan: Plan, blob_dev, out_dev, stream=None) -> None:
     """wc_decode_u8_async: one launch decoding a u8-kind container into out_dev (n bytes)."""
+    _require(blob_dev, plan.container_bytes, plan.device, "blob_dev", "wc_decode_u8_async")
+    _require(out_dev, plan.n_elems, plan.device, "out_dev", "wc_decode_u8_async")
     _check(_lib.wc_decode_u8_async(plan.handle, ctypes.c_void_p(_ptr(blob_dev)), ctypes.c_void_p(_ptr(out_dev)),
                                    ctypes.c_void_p(_stream_handle(stream))), "wc_decode_u8_async")
 
@@ -299,9 +325,30 @@ def gemv_bf16_async(W_dev, rows: int, cols: int, x_dev, y_dev, stream=None) -> N
     """wc_gemv_bf16_async: y = W x (bf16 W rows x cols row-major, bf16 x, fp32 y), one launch.
 
     W_dev / x_dev / y_dev: torch device tensors (or raw device pointers)."""
+    if rows > 0:
+        dev = _current_device()
+        _require(W_dev, 2 * int(rows) * int(cols), dev, "W", "wc_gemv_bf16_async")
+        _require(x_dev, 2 * int(cols), dev, "x", "wc_gemv_bf16_async")
+        _require(y_dev, 4 * int(rows), dev, "y", "wc_gemv_bf16_async")
     _check(_lib.wc_gemv_bf16_async(ctypes.c_void_p(_ptr(W_dev)), int(rows), int(cols), ctypes.c_void_p(_ptr(x_dev)),
                                    ctypes.c_void_p(_ptr(y_dev)), ctypes.c_void_p(_stream_handle(stream))),
            "wc_gemv_bf16_async")
+
+
+def _current_device():
+    import torch
+    return torch.cuda.current_device() if torch.cuda.is_available() else None
+
+
+def _require_operands(plan: Plan, ops, call: str) -> None:
+    """x and y of every operand over a non-empty tensor: cols bf16 and
+    numel / cols float32 (bad tensor indexes and shapes are left to C)."""
+    for i, (t, c, x, y) in enumerate(ops):
+        t, c = int(t), int(c)
+        if not (0 <= t < plan.n_tensors) or c <= 0 or plan.tensor_numels[t] == 0:
+            continue
+        _require(x, 2 * c, plan.device, f"ops[{i}].x", call)
+        _require(y, 4 * (plan.tensor_numels[t] // c), plan.device, f"ops[{i}].y", call)
 
 
 def _operands(ops):
@@ -314,6 +361,7 @@ def _operands(ops):
 
 def decode_gemv_work_bytes(plan: Plan, ops) -> int:
     """wc_decode_gemv_work_bytes for operands [(tensor, cols, x, y), ...]."""
+    _require_operands(plan, ops, "wc_decode_gemv_work_bytes")
     n = ctypes.c_uint64(0)
     _check(_lib.wc_decode_gemv_work_bytes(plan.handle, _operands(ops), len(ops), ctypes.byref(n)),
            "wc_decode_gemv_work_bytes")
@@ -324,6 +372,9 @@ def decode_gemv_async(plan: Plan, blob_dev, ops, work_dev, work_bytes: int, stre
     """wc_decode_gemv_async: y = W x for each operand (tensor, cols, x, y) -- consecutive tensors of the
     container, decoded on chip and never written out -- in one decode launch and one row-sum launch.
     work_dev: device scratch of work_bytes >= decode_gemv_work_bytes(plan, ops), 256-byte aligned."""
+    _require(blob_dev, plan.container_bytes, plan.device, "blob_dev", "wc_decode_gemv_async")
+    _require_operands(plan, ops, "wc_decode_gemv_async")
+    _require(work_dev, int(work_bytes), plan.device, "work_dev", "wc_decode_gemv_async")
     _check(_lib.wc_decode_gemv_async(plan.handle, ctypes.c_void_p(_ptr(blob_dev)), _operands(ops), len(ops),
                                      ctypes.c_void_p(_ptr(work_dev)), int(work_bytes),
                                      ctypes.c_void_p(_stream_handle(stream))),

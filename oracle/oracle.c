@@ -45,8 +45,8 @@
  *    each entry holds the group's first element and the
  *    stream bit where that element's codeword starts, and a final entry
  *    holds {n, stream bits}.
- *  - interleaved-lane layout (container version 3), the LazyWeights page's
- *    "Huffman-encode ... in interleaved lanes" (analogy section): the same
+ *  - interleaved-lane layout (container version 3): the LazyWeights page,
+ *    analogy section, stores the Huffman codes in interleaved lanes; the same
  *    code and planes; the elements are cut into segments (runs of whole
  *    A-element blocks, at most M elements and at most B stream bits); inside
  *    a segment, 8-element lane blocks are dealt to 64 lanes in turn (lane j

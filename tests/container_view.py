@@ -131,3 +131,61 @@ def lane_permutation(m: int) -> np.ndarray:
     lane = (idx // 8) % 64
     order = np.lexsort((idx, lane))     # by lane, then by element
     return order
+
+
+RANS_P = 12          # frequency precision: frequencies sum to 2^12
+RANS_STATE_BITS = 32  # every non-empty lane string starts with its 32-bit final state
+
+
+def expected_rans_freqs(hist: np.ndarray) -> np.ndarray:
+    """Quantized rANS frequencies from a symbol histogram, restated from the
+    rule: f = max(1, floor(count * 2^12 / n)) for present symbols, 0 for the
+    others; while the sum exceeds 2^12, take one unit from the largest
+    frequency above 1 (the lowest symbol among equals); a shortfall goes to
+    the most frequent symbol (the lowest among equal counts)."""
+    hist = np.asarray(hist, dtype=np.int64)
+    n = int(hist.sum())
+    f = np.zeros(256, np.int64)
+    if n == 0:
+        return f
+    present = hist > 0
+    f[present] = np.maximum(1, (hist[present] << RANS_P) // n)
+    total = int(f.sum())
+    while total > (1 << RANS_P):
+        k = int(np.argmax(np.where(f > 1, f, -1)))     # argmax takes the lowest index among equals
+        f[k] -= 1
+        total -= 1
+    if total < (1 << RANS_P):
+        f[int(np.argmax(hist))] += (1 << RANS_P) - total
+    return f
+
+
+def rans_cost_eighths(f: int) -> int:
+    """ceil(8 (12 - log2 f)) + 1 eighths of a bit, exactly: 8 log2 f has floor
+    k = bit_length(f^8) - 1, and ceil(96 - y) = 96 - floor(y) for any real y,
+    so the cost is 97 - k."""
+    return 97 - ((int(f) ** 8).bit_length() - 1)
+
+
+def expected_rans_segment_elems(exps: np.ndarray, freq: np.ndarray, group_align: int, group_max_elems: int,
+                                seg_max_bits: int) -> np.ndarray:
+    """First elements of the rANS segments (then n), restated from the rule:
+    runs of whole A-element blocks (at least one), as long as possible while
+    they hold at most M elements and 64 * 32 + (sum of the per-symbol costs of
+    their elements, in eighths) / 8 <= B."""
+    table = np.array([rans_cost_eighths(f) if f else 0 for f in range(4097)], np.int64)
+    cost = table[np.asarray(freq, np.int64)[exps.astype(np.int64)]]
+    n = exps.size
+    A = int(group_align)
+    csum = np.concatenate([[0], np.cumsum(cost)])
+    block_cost = csum[np.minimum(np.arange(0, n + A, A)[: -(-n // A) + 1], n)]   # eighths before each block
+    nb = block_cost.size - 1
+    budget = 8 * (int(seg_max_bits) - 64 * RANS_STATE_BITS)
+    elems = [0]
+    k = 0
+    while k < nb:
+        end = int(np.searchsorted(block_cost, block_cost[k] + budget, side="right")) - 1
+        end = min(max(end, k + 1), nb, k + int(group_max_elems) // A)
+        elems.append(min(end * A, n))
+        k = end
+    return np.array(elems, dtype=np.uint64)

@@ -40,3 +40,41 @@ def test_traffic_records_name_their_workload_and_source():
         assert rec["workload"] == "block_8b" and rec["traffic_bytes_per_launch"] > 0
         assert len(rec["kernel_source_sha256"]) == 64
         assert os.path.exists(os.path.join(ROOT, rec["source"])), variant
+
+
+def test_rotation_exceeds_twice_the_infinity_cache():
+    """Every workload rotates at least 2 x 256 MiB of (container, output)
+    copies, the small matrices included, so that a timed launch never reads a
+    copy that an earlier launch left in the Infinity Cache."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from lossless_entropy_coded_amd import wc
+    from lossless_entropy_coded_amd.synth import make_workload
+    mall = 256 << 20
+    for name in ("matrix_1k", "attn_4k_zeros"):
+        wl = make_workload(name)
+        per_copy = wc.encode_host(wl.tensors()).size + 2 * wl.n
+        copies = bench.rotation_copies(per_copy)
+        assert copies * per_copy >= 2 * mall and copies >= 2, name
+    for per_copy in (1, 3_530_000, 733_000_000, 2_870_000_000):
+        assert bench.rotation_copies(per_copy) * per_copy >= 2 * mall
+
+
+def test_cpu_model_is_named():
+    sys.path.insert(0, ROOT)
+    import bench
+    name = bench.cpu_model()
+    assert isinstance(name, str) and name and name != "unknown"
+
+
+def test_algorithmic_bytes():
+    """3.36 B per element on the 8B block's shape (1 sm + L/8 stream + metadata + 2 written)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    n, bits, segs = 218_112_000, 565_226_392, 53_250
+    lanes = bench.algorithmic_bytes(n, bits, segs, "lanes", 8, False)
+    assert lanes == n + bits // 8 + 128 * segs + 16 * (segs + 1) + 2 * n
+    chunks = bench.algorithmic_bytes(n, bits, 69_000, "chunks", 8, False)
+    assert chunks == n + bits // 8 + -(-bits // 64) + 16 * 69_001 + 2 * n
+    assert bench.algorithmic_bytes(n, bits, segs, "chunks", 5, False) < chunks
+    assert bench.algorithmic_bytes(1000, 6000, 1, "lanes", 8, True) == 750 + 128 + 32 + 1000

@@ -234,3 +234,62 @@ def test_fused_argument_checks(wc):
         assert status([(3, 512, x.data_ptr() + 2, y)]) == wc.WC_ERR_INVALID_ARG   # x misaligned
         assert status([(3, 512, x, y)], nbytes=8) == wc.WC_ERR_INVALID_ARG   # work too small
         assert status([(3, 512, x, y)] * 17) == wc.WC_ERR_INVALID_ARG       # more than 16 operands
+
+
+@pytest.fixture(scope="module")
+def block_70b():
+    from lossless_entropy_coded_amd.synth import make_workload
+    log("case: generating the full 70B-shape block (855,638,016 bf16)")
+    return make_workload("block_70b")
+
+
+@pytest.mark.parametrize("layout", ["lanes", "chunks"])
+def test_block_70b_full_size_arms(wc, oracle_lib, block_70b, layout):
+    """The full 70B-shape block at the size the benchmark times: the whole
+    block decoded in one launch equals the generated weights; the GEMV on the
+    decoded buffer (arm A) equals the GEMV on the uncompressed weights (arm B)
+    bit for bit for all 7 matrices (28672 x 8192 gate/up, 8192 x 28672 down);
+    the fused decode -> GEMV of the 7 matrices in one call (arm C) agrees with
+    the oracle's float64 GEMV within the derived bound on 48 sampled rows of
+    each matrix (first, last and random), and wrote nothing past y or its
+    work buffer."""
+    import torch
+    from gpu_util import GuardedOutput
+    from lossless_entropy_coded_amd.synth import gemv_input
+    wl = block_70b
+    blob = wc.encode_host(wl.tensors(), layout=layout)
+    mats = [(k, s[0], s[1]) for k, s in enumerate(wl.shapes) if len(s) == 2]
+    assert [(r, c) for _, r, c in mats] == [(8192, 8192), (1024, 8192), (1024, 8192), (8192, 8192),
+                                           (28672, 8192), (28672, 8192), (8192, 28672)]
+    rng = np.random.default_rng(70)
+    with wc.Plan(blob) as plan:
+        f = Fused(wc, blob, plan)
+        log(f"case: block_70b full, {layout}: whole-block decode")
+        out = GuardedOutput(plan.n_elems)
+        wc.decode_async(plan, f.dblob, out.out)
+        orig = torch.from_numpy(wl.bits.view(np.int16)).cuda()
+        torch.cuda.synchronize()
+        assert out.guards_intact()
+        assert torch.equal(out.out, orig), "decoded block differs from the generated weights"
+        xs = {c: gemv_input(c) for _, _, c in mats}
+        xd = {c: _dev_u16(x) for c, x in xs.items()}
+        for k, r, c in mats:
+            log(f"case: block_70b full, {layout}: arms A and B, tensor {k} {r}x{c}")
+            off = plan.tensor_offsets[k]
+            ya = torch.full((r,), float("nan"), dtype=torch.float32, device="cuda")
+            yb = torch.full((r,), float("nan"), dtype=torch.float32, device="cuda")
+            wc.gemv_bf16_async(out.out[off:off + r * c], r, c, xd[c], ya)
+            wc.gemv_bf16_async(orig[off:off + r * c], r, c, xd[c], yb)
+            torch.cuda.synchronize()
+            assert bool(torch.isfinite(yb).all())
+            assert torch.equal(ya.view(torch.int32), yb.view(torch.int32)), f"tensor {k}: arm A != arm B"
+        del out, orig
+        torch.cuda.empty_cache()
+        log(f"case: block_70b full, {layout}: arm C, 7 matrices in one fused call")
+        ys = f.run([(k, c, xs[c]) for k, _, c in mats])
+        for (k, r, c), got in zip(mats, ys):
+            assert np.all(np.isfinite(got))
+            sample = np.unique(np.concatenate([[0, r - 1], rng.integers(0, r, 46)]))
+            off = plan.tensor_offsets[k]
+            W = wl.bits[off:off + r * c].reshape(r, c)[sample]
+            _check_tensor(oracle_lib, got[sample], W, xs[c], wc.GROUP_ALIGN)
