@@ -116,6 +116,7 @@ extern "C" {
 #define WC_ERR_NOMEM            -2   /* host or device allocation failed                      */
 #define WC_ERR_HIP              -3   /* a HIP runtime call or kernel launch failed             */
 #define WC_ERR_UNSUPPORTED      -4   /* valid container the GPU decoder cannot decode (e.g. G) */
+#define WC_ERR_SCRATCH          -5   /* work larger than WC_NOALLOC_SCRATCH_BYTES              */
 #define WC_ERR_BAD_MAGIC        -10  /* magic, version, flags or a fixed field is wrong       */
 #define WC_ERR_TRUNCATED        -11  /* blob shorter than the header or total_bytes           */
 #define WC_ERR_SECTION_BOUNDS   -12  /* a section is misaligned, out of order or outside blob */
@@ -337,6 +338,25 @@ int wc_decode_gemv_work_bytes(const wc_plan_t* plan, const wc_gemv_operand* ops,
  */
 int wc_decode_gemv_async(const wc_plan_t* plan, const void* blob_dev, const wc_gemv_operand* ops, uint32_t n_ops,
                          void* work_dev, uint64_t work_bytes, void* stream);
+
+/*
+ * wc_decode_gemv_noalloc_async -- wc_decode_gemv_async for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same launches and results,
+ * with the work buffer taken from the library's own static device array of
+ * WC_NOALLOC_SCRATCH_BYTES (8 MiB: 8 bytes per group plus 4 per row, enough
+ * for a transformer block of about 2.5 G weights, e.g. the 70B shape's
+ * 855.6 M in 2 MB).  The caller still owns blob_dev, every x and y.
+ * The array lives on every GPU the library runs on until the process ends;
+ * its address is looked up on the first call on each device.  The call
+ * allocates nothing.  Calls on one GPU share the array: calls that overlap
+ * on one GPU (e.g. on two streams) race, so the caller must order them.
+ * Returns WC_ERR_SCRATCH when wc_decode_gemv_work_bytes for these operands
+ * exceeds WC_NOALLOC_SCRATCH_BYTES, otherwise as wc_decode_gemv_async.
+ */
+#define WC_NOALLOC_SCRATCH_BYTES (8ull << 20)
+int wc_decode_gemv_noalloc_async(const wc_plan_t* plan, const void* blob_dev, const wc_gemv_operand* ops,
+                                 uint32_t n_ops, void* stream);
 
 /* Destroy a plan and its device tables (NULL is ignored).  Pending decodes
  * that use the plan must have completed. */

@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+struct wc_plan_s;
+
 namespace wc {
 
 constexpr uint32_t kWaveLanes = 64;        // lanes of a wavefront
@@ -166,6 +168,9 @@ uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l
 int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool rans);
 hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid,
                                LanesOut mode, bool rans, hipStream_t stream);
+
+// The HIP device a plan was made for.
+int plan_device(const wc_plan_s* plan);
 
 // One launch adding, for every global row of p.dot, the partial dot products
 // of the groups covering it, in group order, into the row's y.

@@ -631,6 +631,8 @@ extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, co
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
 }
 
+int wc::plan_device(const wc_plan_s* p) { return p->device; }
+
 extern "C" void wc_plan_destroy(wc_plan_t* p) {
     if (!p) return;
     if (p->d_tables) {
@@ -647,6 +649,7 @@ extern "C" const char* wc_status_str(int s) {
         case WC_ERR_NOMEM: return "out of memory";
         case WC_ERR_HIP: return "HIP runtime error";
         case WC_ERR_UNSUPPORTED: return "unsupported container parameters";
+        case WC_ERR_SCRATCH: return "work exceeds the static scratch of the no-allocation entry point";
         case WC_ERR_BAD_MAGIC: return "bad magic, version or fixed header field";
         case WC_ERR_TRUNCATED: return "container truncated";
         case WC_ERR_SECTION_BOUNDS: return "section misaligned, out of order or out of bounds";

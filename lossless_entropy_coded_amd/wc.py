@@ -81,6 +81,9 @@ _lib.wc_decode_gemv_work_bytes.restype = ctypes.c_int
 _lib.wc_decode_gemv_async.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(GemvOperand),
                                       ctypes.c_uint32, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
 _lib.wc_decode_gemv_async.restype = ctypes.c_int
+_lib.wc_decode_gemv_noalloc_async.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(GemvOperand),
+                                              ctypes.c_uint32, ctypes.c_void_p]
+_lib.wc_decode_gemv_noalloc_async.restype = ctypes.c_int
 _lib.wc_plan_destroy.argtypes = [ctypes.c_void_p]
 _lib.wc_plan_destroy.restype = None
 _lib.wc_status_str.argtypes = [ctypes.c_int]
@@ -92,6 +95,9 @@ WC_ERR_INVALID_ARG = -1
 WC_ERR_NOMEM = -2
 WC_ERR_HIP = -3
 WC_ERR_UNSUPPORTED = -4
+WC_ERR_SCRATCH = -5
+# the no-allocation fused product's static work array (include/wc.h)
+NOALLOC_SCRATCH_BYTES = 8 << 20
 WC_ERR_BAD_MAGIC = -10
 WC_ERR_TRUNCATED = -11
 WC_ERR_SECTION_BOUNDS = -12
@@ -121,6 +127,7 @@ CODERS = {"huffman": 0, "rans": 1}
 EXPORTED = ("wc_encode_host", "wc_encode_u8_host", "wc_free_host", "wc_plan", "wc_plan_info", "wc_plan_stats",
             "wc_plan_format", "wc_decode_u8_async",
             "wc_decode_async", "wc_gemv_bf16_async", "wc_decode_gemv_work_bytes", "wc_decode_gemv_async",
+            "wc_decode_gemv_noalloc_async",
             "wc_plan_destroy", "wc_status_str")
 
 
@@ -379,6 +386,17 @@ def decode_gemv_async(plan: Plan, blob_dev, ops, work_dev, work_bytes: int, stre
                                      ctypes.c_void_p(_ptr(work_dev)), int(work_bytes),
                                      ctypes.c_void_p(_stream_handle(stream))),
            "wc_decode_gemv_async")
+
+
+def decode_gemv_noalloc_async(plan: Plan, blob_dev, ops, stream=None) -> None:
+    """wc_decode_gemv_noalloc_async: decode_gemv_async with the library's static device work
+    array (NOALLOC_SCRATCH_BYTES) instead of a caller's buffer; allocates nothing.  Calls that
+    overlap on one GPU race on that array."""
+    _require(blob_dev, plan.container_bytes, plan.device, "blob_dev", "wc_decode_gemv_noalloc_async")
+    _require_operands(plan, ops, "wc_decode_gemv_noalloc_async")
+    _check(_lib.wc_decode_gemv_noalloc_async(plan.handle, ctypes.c_void_p(_ptr(blob_dev)), _operands(ops), len(ops),
+                                             ctypes.c_void_p(_stream_handle(stream))),
+           "wc_decode_gemv_noalloc_async")
 
 
 def exported_symbols():

@@ -129,3 +129,13 @@ def test_raw_pointers_pass_through(wc):
     """Integer pointers carry no size: they go to C, which checks alignment."""
     p = StandInPlan()
     assert _status(lambda: wc.decode_async(p, 1 << 24, 1 << 24, 0)) == "reached C"
+
+
+def test_decode_gemv_noalloc_checks(wc):
+    p = StandInPlan()
+    blob, x, y = DevTensor(4096), DevTensor(1024), DevTensor(32)
+    assert _status(lambda: wc.decode_gemv_noalloc_async(p, blob, [(1, 512, x, y)], 0)) == "reached C"
+    assert _status(lambda: wc.decode_gemv_noalloc_async(p, blob, [(1, 512, DevTensor(1000), y)], 0)) == \
+        wc.WC_ERR_INVALID_ARG
+    assert _status(lambda: wc.decode_gemv_noalloc_async(p, DevTensor(64), [(1, 512, x, y)], 0)) == \
+        wc.WC_ERR_INVALID_ARG

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(wc):
 
 
 def test_status_strings(wc):
-    codes = [wc.WC_OK, wc.WC_ERR_INVALID_ARG, wc.WC_ERR_NOMEM, wc.WC_ERR_HIP, wc.WC_ERR_UNSUPPORTED,
+    codes = [wc.WC_OK, wc.WC_ERR_INVALID_ARG, wc.WC_ERR_NOMEM, wc.WC_ERR_HIP, wc.WC_ERR_UNSUPPORTED, wc.WC_ERR_SCRATCH,
              wc.WC_ERR_BAD_MAGIC, wc.WC_ERR_TRUNCATED, wc.WC_ERR_SECTION_BOUNDS, wc.WC_ERR_CODE_LENGTHS,
              wc.WC_ERR_KRAFT, wc.WC_ERR_GAP, wc.WC_ERR_GROUP_START, wc.WC_ERR_STREAM_BITS,
              wc.WC_ERR_TENSOR_TABLE]
