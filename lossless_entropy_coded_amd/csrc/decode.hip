@@ -295,7 +295,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) 
         uint4 xv[kDot ? kMergeSteps : 1];
         if constexpr (kDot) {
             dr = dot_rows(p.dot, A, n_unit, dot_mat);
-            load_dot_x(dr, n_unit, lane, xv);
+            load_dot_x(dr, n_unit, lane, 0, xv);
         }
 
         const Meta m_after = load_meta(p, min_u64(un + stride, last_u));
@@ -427,7 +427,8 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) 
         const uint32_t full = n_unit / kMergeElems;
         if constexpr (kDot) {
             dot_group(p.dot, dr, full, lane, smv, xv, u - p.u_begin, [&](uint32_t k) {
-                return *reinterpret_cast<const uint2*>(ebuf + kMergeElems * (lane + k * kWaveLanes));
+                // blocks past the group read its last block: inside the staging
+                return *reinterpret_cast<const uint2*>(ebuf + kMergeElems * min(lane + k * kWaveLanes, last_blk));
             });
         } else {
 #pragma unroll

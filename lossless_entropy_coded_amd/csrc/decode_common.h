@@ -156,9 +156,21 @@ __device__ __forceinline__ float dot8_bf16(uint32_t o0, uint32_t o1, uint32_t o2
     return d;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (uint32_t m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, (int)m, 64);
+// Sum of v over the wave's 64 lanes with DPP, in a fixed order of six levels:
+// partners within quads (lane xor 1, xor 2), mirrored halves of each 8 and
+// each 16 lanes, then rows of 16 added by the row broadcasts (row 1 += row 0,
+// row 3 += row 2, then rows 2 and 3 += row 1).  Lane 63 ends with the total.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, kRowMask, 0xF, false));
+}
+__device__ __forceinline__ float wave_total(float v) {
+    v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1, 0, 3, 2]
+    v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2, 3, 0, 1]
+    v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
+    v = dpp_add<0x140, 0xF>(v);   // row_mirror
+    v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+    v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
     return v;
 }
 
@@ -208,29 +220,94 @@ __device__ __forceinline__ DotRows dot_rows(const DotParams& q, uint64_t A, uint
     return d;
 }
 
-// The x entries that step k of this lane multiplies: block lane + 64k of a
-// group of n elements whose rows dr describes.  Blocks outside the multiplied
-// range load x0[0..7], never used.
-__device__ __forceinline__ void load_dot_x(const DotRows& dr, uint32_t n, uint32_t lane, uint4 (&xv)[kMergeSteps]) {
+// The x entries that steps k0 .. k0 + kN - 1 of this lane multiply: block
+// lane + 64k of a group of n elements whose rows dr describes.  In a group
+// that lies in one row (most groups) block b takes x0[off0 + 8b ..] from one
+// uniform base, blocks past the group's last block repeating it; otherwise
+// each block takes its own row's x, and blocks outside the multiplied range
+// load x0[0..7].  Those are never used.
+template <uint32_t kN>
+__device__ __forceinline__ void load_dot_x(const DotRows& dr, uint32_t n, uint32_t lane, uint32_t k0,
+                                           uint4 (&xv)[kN]) {
     const uint32_t nblk = n / kMergeElems;
-    if (dr.simple) {   // most groups: one row, all multiplied
+    if (dr.simple) {   // every element multiplied: n is a positive multiple of 8
+        const uint8_t* const base = reinterpret_cast<const uint8_t*>(dr.x0 + dr.off0);
+        const uint32_t last = __builtin_amdgcn_readfirstlane(nblk - 1);
 #pragma unroll
-        for (uint32_t k = 0; k < kMergeSteps; ++k) {
-            const uint32_t rel = kMergeElems * (lane + k * kWaveLanes);
-            const int32_t col = lane + k * kWaveLanes < nblk ? (int32_t)rel + dr.off0 : 0;
-            xv[k] = *reinterpret_cast<const uint4*>(dr.x0 + col);
-        }
+        for (uint32_t i = 0; i < kN; ++i)
+            xv[i] = *reinterpret_cast<const uint4*>(base + 16u * min(lane + (k0 + i) * kWaveLanes, last));
     } else {
+        // a real branch: an empty volatile asm keeps the compiler from
+        // computing these addresses for every group and selecting
+        asm volatile("");
 #pragma unroll
-        for (uint32_t k = 0; k < kMergeSteps; ++k) {
-            const uint32_t blk = lane + k * kWaveLanes;
+        for (uint32_t i = 0; i < kN; ++i) {
+            const uint32_t blk = lane + (k0 + i) * kWaveLanes;
             const uint32_t rel = kMergeElems * blk;
             const bool ok = blk < nblk && rel >= dr.lo_rel && rel < dr.hi_rel;
             const bool second = rel >= dr.r1_rel;
             const uint16_t* const xp = second ? dr.x1 : dr.x0;
             const int32_t col = ok ? (int32_t)rel + (second ? dr.off1 : dr.off0) : 0;
-            xv[k] = *reinterpret_cast<const uint4*>(xp + col);
+            xv[i] = *reinterpret_cast<const uint4*>(xp + col);
         }
+    }
+}
+
+// Adds the block sums d[i] of steps k0 + i (in step order) to this lane's
+// partials of the group's first row (acc0) and the next (acc1).  Blocks past
+// the group's whole blocks (`full`) or outside the multiplied range are
+// dropped by a select, whatever was computed for them.
+template <uint32_t kN>
+__device__ __forceinline__ void add_dot_steps(const DotRows& dr, uint32_t full, uint32_t lane, uint32_t k0,
+                                              const float (&d)[kN], float& acc0, float& acc1) {
+    if (dr.simple && full == kWaveLanes * kMergeSteps) {   // most groups: every block, one row
+#pragma unroll
+        for (uint32_t i = 0; i < kN; ++i) acc0 += d[i];
+    } else if (dr.simple) {
+#pragma unroll
+        for (uint32_t i = 0; i < kN; ++i) acc0 += lane + (k0 + i) * kWaveLanes < full ? d[i] : 0.0f;
+    } else {
+        asm volatile("");   // a real branch (see load_dot_x)
+#pragma unroll
+        for (uint32_t i = 0; i < kN; ++i) {
+            const uint32_t blk = lane + (k0 + i) * kWaveLanes;
+            const uint32_t rel = kMergeElems * blk;
+            const bool ok = blk < full && rel >= dr.lo_rel && rel < dr.hi_rel;
+            const bool second = rel >= dr.r1_rel;
+            acc0 += ok && !second ? d[i] : 0.0f;
+            acc1 += ok && second ? d[i] : 0.0f;
+        }
+    }
+}
+
+// Block sums of steps k0 + i: sign+mantissa bytes sm[i] joined with the
+// exponent bytes e[i], times the x entries xv[i], four dot2 steps each.
+template <uint32_t kN>
+__device__ __forceinline__ void dot_steps(const uint2* sm, const uint2 (&e)[kN], const uint4 (&xv)[kN],
+                                          float (&d)[kN]) {
+#pragma unroll
+    for (uint32_t i = 0; i < kN; ++i) {
+        uint32_t o0, o1, o2, o3;
+        join4(sm[i].x, e[i].x, o0, o1);
+        join4(sm[i].y, e[i].y, o2, o3);
+        d[i] = dot8_bf16(o0, o1, o2, o3, xv[i]);
+    }
+}
+
+// The wave's totals of the two row partials; lane 63 writes them for group g
+// (g = group - u_begin) and, for a row that starts in the group, that row's
+// first group: the group holding the row's first element, or the next one
+// when that group started in the row before.
+__device__ __forceinline__ void finish_dot(const DotParams& q, const DotRows& dr, uint32_t lane, uint64_t g,
+                                           float acc0, float acc1) {
+    acc0 = wave_total(acc0);
+    if (!dr.simple) acc1 = wave_total(acc1);
+    if (lane == kWaveLanes - 1) {
+        *reinterpret_cast<float2*>(q.part + 2 * g) = make_float2(acc0, dr.simple ? 0.0f : acc1);
+        if (dr.starts_row0)
+            q.row_group[dr.row0] = (uint32_t)g;
+        else if (dr.starts_row1)
+            q.row_group[dr.row0 + 1] = (uint32_t)(g + 1);
     }
 }
 
@@ -238,53 +315,20 @@ __device__ __forceinline__ void load_dot_x(const DotRows& dr, uint32_t n, uint32
 // sign+mantissa bytes smv[k] with the exponent bytes exp_at(k) of block
 // lane + 64k (a block of 8 lies in one row: row starts are multiples of 8),
 // sums the block with four dot2 steps and adds it to the partial of its row.
-// Lane 0 writes the group's two partials (g = group - u_begin) and, for a row
-// that starts in the group, that row's first group: the group holding the
-// row's first element, or the next one when that group started in the row
-// before.
+// All eight exponent reads are issued first (exp_at must stay inside the
+// wave's own LDS for every k).
 template <typename ExpAt>
 __device__ __forceinline__ void dot_group(const DotParams& q, const DotRows& dr, uint32_t full, uint32_t lane,
                                           const uint2 (&smv)[kMergeSteps], const uint4 (&xv)[kMergeSteps],
                                           uint64_t g, ExpAt exp_at) {
+    uint2 e2[kMergeSteps];
+#pragma unroll
+    for (uint32_t k = 0; k < kMergeSteps; ++k) e2[k] = exp_at(k);
+    float d[kMergeSteps];
+    dot_steps(smv, e2, xv, d);
     float acc0 = 0.0f, acc1 = 0.0f;
-    if (dr.simple) {
-#pragma unroll
-        for (uint32_t k = 0; k < kMergeSteps; ++k) {
-            if (lane + k * kWaveLanes < full) {
-                const uint2 e2 = exp_at(k);
-                uint32_t o0, o1, o2, o3;
-                join4(smv[k].x, e2.x, o0, o1);
-                join4(smv[k].y, e2.y, o2, o3);
-                acc0 += dot8_bf16(o0, o1, o2, o3, xv[k]);
-            }
-        }
-        acc0 = wave_sum(acc0);
-    } else {
-#pragma unroll
-        for (uint32_t k = 0; k < kMergeSteps; ++k) {
-            const uint32_t blk = lane + k * kWaveLanes;
-            const uint32_t rel = kMergeElems * blk;
-            if (blk < full && rel >= dr.lo_rel && rel < dr.hi_rel) {
-                const uint2 e2 = exp_at(k);
-                uint32_t o0, o1, o2, o3;
-                join4(smv[k].x, e2.x, o0, o1);
-                join4(smv[k].y, e2.y, o2, o3);
-                const bool second = rel >= dr.r1_rel;
-                const float d = dot8_bf16(o0, o1, o2, o3, xv[k]);
-                acc0 += second ? 0.0f : d;
-                acc1 += second ? d : 0.0f;
-            }
-        }
-        acc0 = wave_sum(acc0);
-        acc1 = wave_sum(acc1);
-    }
-    if (lane == 0) {
-        *reinterpret_cast<float2*>(q.part + 2 * g) = make_float2(acc0, acc1);
-        if (dr.starts_row0)
-            q.row_group[dr.row0] = (uint32_t)g;
-        else if (dr.starts_row1)
-            q.row_group[dr.row0 + 1] = (uint32_t)(g + 1);
-    }
+    add_dot_steps(dr, full, lane, 0, d, acc0, acc1);
+    finish_dot(q, dr, lane, g, acc0, acc1);
 }
 
 }  // namespace

@@ -63,7 +63,9 @@ struct LaneRaw {
 __device__ __forceinline__ LaneRaw load_lane_raw(const DecodeParams& p, const Meta& m, uint64_t g, uint32_t lane) {
     LaneRaw r;
     const uint64_t base = (m.p0 >> 7) << 4;                    // 16-byte aligned first byte
-    const uint64_t need = ((m.p1 + 7) >> 3) + 8 - base;        // bytes up to the last bit, plus the lookahead
+    // bytes up to the last bit, plus the lookahead (at most 2,008: the
+    // planner bounds a segment's bits)
+    const uint32_t need = (uint32_t)(((m.p1 + 7) >> 3) + 8 - base);
     const uint8_t* q = p.stream + base;
     r.q0 = make_uint4(0, 0, 0, 0);
     r.q1 = make_uint4(0, 0, 0, 0);
@@ -112,6 +114,7 @@ __device__ __forceinline__ uint32_t unrotate4(uint32_t x) {
 template <int KD, int W, uint32_t kMode, bool kRans>
 __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodeParams p) {
     static_assert(!kRans || (2u << KD) == kRansSlots, "the rANS slot table takes the multi-codeword table's place");
+    static_assert(kMode != kLanesToDot || kRans, "the fused product of Huffman lanes is decode_lanes_dot_kernel");
     constexpr bool kDot = kMode == kLanesToDot;
     constexpr bool kU8 = kMode == kLanesToU8;
     constexpr uint32_t kThreads = kWaveLanes * W;
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
         uint4 xv[kDot ? kMergeSteps : 1];
         if constexpr (kDot) {
             dr = dot_rows(p.dot, A, n, dot_mat);
-            load_dot_x(dr, n, lane, xv);
+            load_dot_x(dr, n, lane, 0, xv);
         }
         const Meta m_after = load_meta(p, min_u64(un + stride, last_u));
         wave_lds_order();
@@ -349,40 +352,28 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
                         *reinterpret_cast<uint32_t*>(slot + q) = w;
                     }
                 } else {
-                    uint32_t p = 0;
-                    // code planes (about one symbol per lookup): the symbols are
-                    // gathered in a register and written as aligned words (the
-                    // table's bytes past a lookup's symbols are 0); the last word
-                    // ends by byte 67.  bf16 exponents for the fused product (two
-                    // to three symbols per lookup): four byte stores at the count
-                    // decoded so far.
-                    uint32_t acc = 0;
+                    // code planes (about one symbol per lookup): the symbols
+                    // are gathered in a register and written as aligned words
+                    // (the table's bytes past a lookup's symbols are 0); the
+                    // last word ends by byte 67.
+                    uint32_t p = 0, acc = 0;
                     while (p < nsym) {
                         const int32_t k = t >> 5;
                         const uint32_t top = __builtin_amdgcn_alignbit(sbuf[k], sbuf[k + 1], ~(uint32_t)t);
                         uint2 e = s_dec[top >> (32 - KD)];
                         if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
                         const uint32_t pn = p + ((e.x >> 8) & 0xFFu);
-                        if constexpr (kU8) {
-                            const uint64_t comb = ((uint64_t)e.y << ((p & 3u) << 3)) | acc;
-                            if ((p ^ pn) >= 4u) {   // a word is complete
-                                *reinterpret_cast<uint32_t*>(slot + (p & ~3u)) = (uint32_t)comb;
-                                acc = (uint32_t)(comb >> 32);
-                            } else {
-                                acc = (uint32_t)comb;
-                            }
+                        const uint64_t comb = ((uint64_t)e.y << ((p & 3u) << 3)) | acc;
+                        if ((p ^ pn) >= 4u) {   // a word is complete
+                            *reinterpret_cast<uint32_t*>(slot + (p & ~3u)) = (uint32_t)comb;
+                            acc = (uint32_t)(comb >> 32);
                         } else {
-                            uint8_t* const dst = slot + p;
-                            const uint32_t odd = __builtin_amdgcn_perm(e.y, e.y, 0x0C030C01u);   // [s1, 0, s3, 0]
-                            dst[0] = (uint8_t)e.y;
-                            dst[1] = (uint8_t)odd;
-                            dst[2] = (uint8_t)(e.y >> 16);
-                            dst[3] = (uint8_t)(odd >> 16);
+                            acc = (uint32_t)comb;
                         }
                         p = pn;
                         t += (int32_t)((e.x >> 16) & 0xFFu);
                     }
-                    if (kU8 && (p & 3u)) *reinterpret_cast<uint32_t*>(slot + (p & ~3u)) = acc;
+                    if (p & 3u) *reinterpret_cast<uint32_t*>(slot + (p & ~3u)) = acc;
                 }
             }
         }
@@ -459,13 +450,227 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
     }
 }
 
+// ---- fused decode -> matrix-vector product of Huffman lanes -----------------
+//
+// The fused product reads only the container, so the decode's own latency and
+// instructions bound it, not HBM: it runs with as many waves in flight as the
+// LDS and the register file allow.  Each lane decodes its (at most 64)
+// symbols in two phases of 32, its lane blocks 0..3 and then 4..7, into a
+// 36-byte slot, and the wave multiplies the phase's four blocks right after
+// it.  A wave's LDS region is 4,368 bytes instead of 6,416, so three 8-wave
+// workgroups fit a compute unit (24 waves instead of 16), and only one
+// phase's x entries are held in registers at a time.
+// The symbols go to the slot as aligned dwords, one store per lookup: `acc`
+// holds the bytes [c & ~3, c) decoded but not yet stored (its other bytes are
+// 0); a lookup's up to four symbols, shifted to c & 3, join it, the dword at
+// c & ~3 is stored and the part past that dword carries over, also from one
+// phase into the next (the second phase stores symbol c at slot byte c - 32).
+// Every byte a merge reads lies below the phase's end, in a dword that the
+// last lookup reaching it stored whole; bytes past the lane's symbols are
+// never multiplied.
+// A segment's entry pair read through the scalar data cache (the table is
+// read-only while the kernel runs, and the segment index is uniform): the
+// entries land in scalar registers, not in every lane's vector registers.
+__device__ __forceinline__ Meta load_meta_scalar(const DecodeParams& p, uint64_t u) {
+    typedef __attribute__((address_space(4))) const uint32_t* ConstU32;
+    const ConstU32 g = (ConstU32)(uintptr_t)(p.groups + 2 * u);
+    Meta m;
+    m.e0 = ((uint64_t)g[1] << 32) | g[0];
+    m.p0 = ((uint64_t)g[3] << 32) | g[2];
+    m.e1 = ((uint64_t)g[5] << 32) | g[4];
+    m.p1 = ((uint64_t)g[7] << 32) | g[6];
+    return m;
+}
+
+constexpr uint32_t kDotHalf = 32;                 // symbols per lane and phase
+constexpr uint32_t kDotSlotBytes = kDotHalf + 4;  // 9 dwords: an odd stride across the LDS banks
+constexpr uint32_t kDotSteps = kMergeSteps / 2;   // merge steps per phase
+constexpr uint32_t kDotWaveBytes = kLanePadBytes + kLaneStageBytes + kWaveLanes * kDotSlotBytes;
+
+template <int KD, int W>
+__global__ __launch_bounds__(kWaveLanes * W, 6) void decode_lanes_dot_kernel(DecodeParams p) {
+    constexpr uint32_t kThreads = kWaveLanes * W;
+    constexpr uint32_t kDecVec = (2u << KD) / 4, kLongVec = kLongWords / 4;
+    constexpr uint32_t kTabVec = kDecVec + kLongVec;
+    __shared__ __attribute__((aligned(16))) uint4 s_tab[kTabVec];
+    const uint2* const s_dec = reinterpret_cast<const uint2*>(s_tab);
+    const uint32_t* const s_long = reinterpret_cast<const uint32_t*>(s_tab + kDecVec);
+    // dynamic: per wave the 16-byte pad, kLaneStageBytes of stream words and
+    // one kDotSlotBytes slot per lane; then the second-level table
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
+    uint16_t* const s_l2 = reinterpret_cast<uint16_t*>(dyn + W * kDotWaveBytes);
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & 63u;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    uint32_t* const sbuf = reinterpret_cast<uint32_t*>(dyn + wave * kDotWaveBytes + kLanePadBytes);
+    uint8_t* const slot = dyn + wave * kDotWaveBytes + kLanePadBytes + kLaneStageBytes + kDotSlotBytes * lane;
+
+    const uint64_t stride = (uint64_t)gridDim.x * W;
+    uint64_t u = p.u_begin + (uint64_t)blockIdx.x * W + wave;
+    const uint64_t last_u = p.u_end - 1;
+    const bool active = u < p.u_end;
+
+    // prologue: the first segment's entries and loads are in flight while the
+    // workgroup stages the tables
+    const Meta m_first = load_meta_scalar(p, min_u64(u, last_u));
+    constexpr uint32_t kFull = kTabVec / kThreads;
+    constexpr uint32_t kTail = kTabVec - kFull * kThreads;
+    const u32x4* const tsrc = reinterpret_cast<const u32x4*>(p.tables);
+    u32x4* const tdst = reinterpret_cast<u32x4*>(s_tab);
+    u32x4 stage[kFull > 0 ? kFull : 1];
+#pragma unroll
+    for (uint32_t k = 0; k < kFull; ++k) stage[k] = tsrc[tid + k * kThreads];
+    u32x4 stage_tail = {0, 0, 0, 0};
+    if (kTail && tid < kTail) stage_tail = tsrc[kFull * kThreads + tid];
+    Meta cur_m = m_first;
+    LaneRaw cur_r = load_lane_raw(p, cur_m, min_u64(u, last_u), lane);
+    Meta m_next = load_meta_scalar(p, min_u64(u + stride, last_u));
+#pragma unroll
+    for (uint32_t k = 0; k < kFull; ++k) tdst[tid + k * kThreads] = stage[k];
+    if (kTail && tid < kTail) tdst[kFull * kThreads + tid] = stage_tail;
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(p.tables) + kTabVec;
+        for (uint32_t i = tid; i < (p.l2_cap << kL2Bits) / 8; i += kThreads)
+            reinterpret_cast<uint4*>(s_l2)[i] = src[i];
+    }
+    __syncthreads();
+    if (!active) return;
+    LongTables lt;
+    lt.count = s_long;
+    lt.first = s_long + 32;
+    lt.base = s_long + 64;
+    lt.sorted = reinterpret_cast<const uint8_t*>(s_long + 96);
+    lt.l2 = s_l2;
+    lt.l2_first = __builtin_amdgcn_readfirstlane(s_long[160]);
+    lt.l2_n = min(__builtin_amdgcn_readfirstlane(s_long[161]), p.l2_cap);
+    uint32_t dot_mat = 0;   // matrix of the wave's current segment
+
+    for (;;) {
+        const uint64_t un = u + stride;
+        const bool more = un < p.u_end;
+        reinterpret_cast<uint4*>(sbuf)[lane] = bswap4(cur_r.q0);
+        reinterpret_cast<uint4*>(sbuf)[lane + kWaveLanes] = bswap4(cur_r.q1);
+        const uint32_t off = cur_r.off;
+
+        // the next segment's stream and lane offset, this segment's first
+        // phase of sign and mantissa bytes and x entries, the table entries
+        // of the segment after next
+        const LaneRaw nxt = load_lane_raw(p, m_next, min_u64(un, last_u), lane);
+        const uint64_t A = cur_m.e0;
+        // the planner bounds every segment by the element cap (at most 4096)
+        const uint32_t n = min((uint32_t)cur_m.e1 - (uint32_t)cur_m.e0, kGroupMaxElems);
+        const uint32_t last_blk = (n - 1) / kMergeElems;
+        uint2 smv[kDotSteps];
+        auto load_sm = [&](uint32_t k0) {
+#pragma unroll
+            for (uint32_t i = 0; i < kDotSteps; ++i)
+                smv[i] = load_nt8(p.sm + A + kMergeElems * min(lane + (k0 + i) * kWaveLanes, last_blk));
+        };
+        load_sm(0);
+        const DotRows dr = dot_rows(p.dot, A, n, dot_mat);
+        uint4 xv[kDotSteps];
+        load_dot_x(dr, n, lane, 0, xv);
+        const Meta m_after = load_meta_scalar(p, min_u64(un + stride, last_u));
+        wave_lds_order();
+
+        const uint32_t nb8 = (n + kLaneBlock - 1) / kLaneBlock;
+        const uint32_t cnt = lane < nb8 ? (nb8 - 1 - lane) / kWaveLanes + 1 : 0u;
+        uint32_t nsym = kLaneBlock * cnt;
+        if (cnt && lane == (nb8 - 1) % kWaveLanes) nsym -= kLaneBlock * nb8 - n;
+        // the window of bit position t + 1: staged words t >> 5 (arithmetic:
+        // -1 at position 0, the pad's last word, shifted out) and the next,
+        // shifted right by -(t + 1) mod 32.  A lane's first bit is at most
+        // 15,999 (the planner bounds lane offsets by the segment's bits) and
+        // it makes at most 64 lookups of at most 24 bits, so its last window
+        // word is at most 548: inside the wave's staging and slots.
+        int32_t t = (int32_t)((uint32_t)(cur_m.p0 & 127u) + off) - 1;
+        // the symbol count is kept as the LDS byte address of the next symbol
+        // (a local-address-space offset; slots are 4-byte aligned, so its low
+        // two bits are the count's)
+        typedef __attribute__((address_space(3))) uint8_t LdsByte;
+        typedef __attribute__((address_space(3))) uint32_t LdsWord;
+        const uint32_t slot_addr = (uint32_t)(uintptr_t)(LdsByte*)slot;
+        uint32_t a = slot_addr;
+        uint32_t acc = 0;
+        const uint32_t full = n / kMergeElems;
+        float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+        for (uint32_t h = 0; h < 2; ++h) {
+            // symbol c of this phase goes to slot byte c - 32h
+            const uint32_t end = slot_addr + min(nsym, kDotHalf * (h + 1)) - kDotHalf * h;
+            while (a < end) {
+                const int32_t k = t >> 5;
+                const uint32_t top = __builtin_amdgcn_alignbit(sbuf[k], sbuf[k + 1], ~(uint32_t)t);
+                uint2 e = s_dec[top >> (32 - KD)];
+                if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
+                const uint32_t q = a & 3u;
+                const uint64_t w = (uint64_t)e.y << (q << 3);
+                const uint32_t lo = (uint32_t)w | acc;
+                *(LdsWord*)(uintptr_t)(a - q) = lo;
+                acc = q + ((e.x >> 8) & 0xFFu) >= 4u ? (uint32_t)(w >> 32) : lo;
+                a += (e.x >> 8) & 0xFFu;
+                t += (int32_t)((e.x >> 16) & 0xFFu);
+            }
+            a -= kDotHalf * (h == 0);
+            wave_lds_order();
+            // merge steps 4h .. 4h + 3: slot bytes 8i of block lane + 64(4h + i)
+            uint2 e2[kDotSteps];
+#pragma unroll
+            for (uint32_t i = 0; i < kDotSteps; ++i) e2[i] = load_slot8(slot + kMergeElems * i);
+            float d[kDotSteps];
+            dot_steps(smv, e2, xv, d);
+            add_dot_steps(dr, full, lane, kDotSteps * h, d, acc0, acc1);
+            if (h == 0) {   // the second phase's operands, in flight while it decodes
+                load_sm(kDotSteps);
+                load_dot_x(dr, n, lane, kDotSteps, xv);
+            }
+            wave_lds_order();   // the second phase rewrites the slot
+        }
+        finish_dot(p.dot, dr, lane, u - p.u_begin, acc0, acc1);
+
+        const LaneRaw next_r = nxt;
+        const Meta next_m = m_next;
+        m_next = m_after;
+        if (!more) break;
+        wave_lds_order();   // the staging is rewritten by the next segment
+        u = un;
+        cur_m = next_m;
+        cur_r = next_r;
+    }
+}
+
+template <int KD, int W>
+struct LanesDotVariant {
+    static hipError_t launch(const DecodeParams& p, uint32_t grid, uint32_t dyn, hipStream_t stream) {
+        hipLaunchKernelGGL((decode_lanes_dot_kernel<KD, W>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
+        return hipGetLastError();
+    }
+    static int blocks_per_cu(uint32_t dyn) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lanes_dot_kernel<KD, W>, kWaveLanes * W, dyn) !=
+            hipSuccess)
+            return 0;
+        return n;
+    }
+};
+
+template <typename F>
+hipError_t dispatch_lanes_dot(uint32_t decode_bits, uint32_t waves, F&& f) {
+    if (decode_bits == 11) return waves == 8 ? f(LanesDotVariant<11, 8>{}) : f(LanesDotVariant<11, 4>{});
+    return waves == 8 ? f(LanesDotVariant<10, 8>{}) : f(LanesDotVariant<10, 4>{});
+}
+
 template <int KD, int W, bool kRans>
 struct LanesVariant {
     static hipError_t launch(const DecodeParams& p, uint32_t grid, uint32_t dyn, LanesOut mode, hipStream_t stream) {
         const dim3 g(grid), b(kWaveLanes * W);
-        if (mode == kLanesToDot)
-            hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToDot, kRans>), g, b, dyn, stream, p);
-        else if (mode == kLanesToU8)
+        if (mode == kLanesToDot) {
+            if constexpr (kRans)
+                hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToDot, kRans>), g, b, dyn, stream, p);
+            else
+                return hipErrorInvalidValue;   // Huffman lanes: launch_decode_lanes_dot
+        } else if (mode == kLanesToU8)
             hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToU8, kRans>), g, b, dyn, stream, p);
         else
             hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToBf16, kRans>), g, b, dyn, stream, p);
@@ -475,11 +680,15 @@ struct LanesVariant {
         int n[3] = {0, 0, 0};
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[0], decode_lanes_kernel<KD, W, kLanesToBf16, kRans>,
                                                          kWaveLanes * W, dyn) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[1], decode_lanes_kernel<KD, W, kLanesToDot, kRans>,
-                                                         kWaveLanes * W, dyn) != hipSuccess ||
             hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[2], decode_lanes_kernel<KD, W, kLanesToU8, kRans>,
                                                          kWaveLanes * W, dyn) != hipSuccess)
             return 0;
+        n[1] = n[0];
+        if constexpr (kRans) {
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n[1], decode_lanes_kernel<KD, W, kLanesToDot, kRans>,
+                                                             kWaveLanes * W, dyn) != hipSuccess)
+                return 0;
+        }
         return std::min(n[0], std::min(n[1], n[2]));
     }
 };
@@ -510,6 +719,29 @@ int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2
         return hipSuccess;
     });
     return n;
+}
+
+uint32_t decode_lanes_dot_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap) {
+    return ((2u << decode_bits) + kLongWords) * 4 + waves * kDotWaveBytes + (l2_cap << kL2Bits) * 2;
+}
+
+int decode_lanes_dot_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap) {
+    if ((decode_bits != 11 && decode_bits != 10) || !supported_waves(waves)) return 0;
+    const uint32_t dyn = waves * kDotWaveBytes + (l2_cap << kL2Bits) * 2;
+    int n = 0;
+    (void)dispatch_lanes_dot(decode_bits, waves, [&](auto v) {
+        n = decltype(v)::blocks_per_cu(dyn);
+        return hipSuccess;
+    });
+    return n;
+}
+
+hipError_t launch_decode_lanes_dot(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid,
+                                   hipStream_t stream) {
+    if ((decode_bits != 11 && decode_bits != 10) || !supported_waves(waves) || p.l2_cap > kL2Prefixes)
+        return hipErrorInvalidValue;
+    const uint32_t dyn = waves * kDotWaveBytes + (p.l2_cap << kL2Bits) * 2;
+    return dispatch_lanes_dot(decode_bits, waves, [&](auto v) { return decltype(v)::launch(p, grid, dyn, stream); });
 }
 
 hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid,

@@ -172,6 +172,15 @@ hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint
 // The HIP device a plan was made for.
 int plan_device(const wc_plan_s* plan);
 
+// The fused product of a Huffman lanes container: LDS bytes of one workgroup,
+// resident workgroups per CU, and one launch over segments [p.u_begin,
+// p.u_end) leaving partial dot products in p.dot (p.gap at the lane offsets,
+// p.tables at the multi-codeword table, as for launch_decode_lanes).
+uint32_t decode_lanes_dot_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap);
+int decode_lanes_dot_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap);
+hipError_t launch_decode_lanes_dot(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid,
+                                   hipStream_t stream);
+
 // One launch adding, for every global row of p.dot, the partial dot products
 // of the groups covering it, in group order, into the row's y.
 hipError_t launch_gemv_rows(const DecodeParams& p, hipStream_t stream);

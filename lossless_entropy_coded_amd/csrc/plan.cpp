@@ -43,6 +43,7 @@ struct wc_plan_s {
         uint32_t lds_bytes = 0;
     };
     Shape plain, busy;
+    Shape dot;                   // fused product of a Huffman lanes container (its own kernel)
     uint32_t grid = 0;           // of the container's decode entry point (stats)
     uint32_t lds_bytes = 0;
     uint32_t ebuf_bytes = 0;
@@ -363,12 +364,15 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         lds_cu <= 0)
         lds_cu = 160 * 1024;
     const uint32_t forced_grid = env_u32("WC_GRID", 0);
-    auto size_shape = [&](wc_plan_s::Shape& sh) {
-        sh.lds_bytes = lanes ? wc::decode_lanes_lds_bytes(p->decode_bits, sh.waves, p->l2_cap)
-                             : wc::decode_lds_bytes(p->count_bits, p->decode_bits, sh.waves, p->ebuf_bytes, p->l2_cap);
-        int per_cu = lanes ? wc::decode_lanes_blocks_per_cu(p->decode_bits, sh.waves, p->l2_cap, p->rans)
-                           : wc::decode_blocks_per_cu(p->count_bits, p->decode_bits, sh.waves, p->ebuf_bytes,
-                                                      p->l2_cap);
+    auto size_shape = [&](wc_plan_s::Shape& sh, bool fused_lanes) {
+        sh.lds_bytes = fused_lanes ? wc::decode_lanes_dot_lds_bytes(p->decode_bits, sh.waves, p->l2_cap)
+                       : lanes     ? wc::decode_lanes_lds_bytes(p->decode_bits, sh.waves, p->l2_cap)
+                                   : wc::decode_lds_bytes(p->count_bits, p->decode_bits, sh.waves, p->ebuf_bytes,
+                                                          p->l2_cap);
+        int per_cu = fused_lanes ? wc::decode_lanes_dot_blocks_per_cu(p->decode_bits, sh.waves, p->l2_cap)
+                     : lanes     ? wc::decode_lanes_blocks_per_cu(p->decode_bits, sh.waves, p->l2_cap, p->rans)
+                                 : wc::decode_blocks_per_cu(p->count_bits, p->decode_bits, sh.waves, p->ebuf_bytes,
+                                                            p->l2_cap);
         // The persistent grid must be co-resident.  LDS is handed out in
         // granules of 1/128 of a compute unit's LDS (1,280 bytes of 160 KiB on
         // gfx950), which the runtime's occupancy estimate does not round for:
@@ -388,7 +392,9 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         sh.grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(want, need));
         return true;
     };
-    if (!size_shape(p->plain) || !size_shape(p->busy)) {
+    p->dot.waves = p->busy.waves;
+    const bool fused_lanes = lanes && !p->rans && p->h.elem_kind == wc::kKindBf16;
+    if (!size_shape(p->plain, false) || !size_shape(p->busy, false) || (fused_lanes && !size_shape(p->dot, true))) {
         delete p;
         return WC_ERR_UNSUPPORTED;
     }
@@ -617,13 +623,21 @@ extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, co
     d.one_code = p->one_code ? 1u : 0u;
     d.dot.part = static_cast<float*>(work_dev);
     d.dot.row_group = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(work_dev) + rows_off);
-    const uint64_t groups = wc::div_up(d.u_end - d.u_begin, p->busy.waves);
-    const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(p->busy.slots, groups));
+    // Huffman lanes containers have a fused kernel of their own (its own
+    // launch shape); rANS lanes and chunks containers use their decode
+    // kernel's fused mode
+    const bool own = p->lanes && !p->rans;
+    const wc_plan_s::Shape& sh = own ? p->dot : p->busy;
+    const uint64_t groups = wc::div_up(d.u_end - d.u_begin, sh.waves);
+    const uint32_t grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(sh.slots, groups));
     const hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
-    if (p->lanes) {
+    if (own) {
         d.tables = p->d_tables + (1u << p->count_bits);
-        e = wc::launch_decode_lanes(d, p->decode_bits, p->busy.waves, grid, wc::kLanesToDot, p->rans, s);
+        e = wc::launch_decode_lanes_dot(d, p->decode_bits, sh.waves, grid, s);
+    } else if (p->lanes) {
+        d.tables = p->d_tables + (1u << p->count_bits);
+        e = wc::launch_decode_lanes(d, p->decode_bits, sh.waves, grid, wc::kLanesToDot, p->rans, s);
     } else {
         e = wc::launch_decode(d, p->count_bits, p->decode_bits, p->busy.waves, grid, true, s);
     }
