@@ -115,7 +115,7 @@ extern "C" {
 #define WC_ERR_INVALID_ARG      -1   /* NULL pointer, misaligned pointer, bad option          */
 #define WC_ERR_NOMEM            -2   /* host or device allocation failed                      */
 #define WC_ERR_HIP              -3   /* a HIP runtime call or kernel launch failed             */
-#define WC_ERR_UNSUPPORTED      -4   /* valid container the GPU decoder cannot decode (e.g. G) */
+#define WC_ERR_UNSUPPORTED      -4   /* valid container the GPU decoder cannot decode (A, M, B) */
 #define WC_ERR_SCRATCH          -5   /* work larger than WC_NOALLOC_SCRATCH_BYTES              */
 #define WC_ERR_BAD_MAGIC        -10  /* magic, version, flags or a fixed field is wrong       */
 #define WC_ERR_TRUNCATED        -11  /* blob shorter than the header or total_bytes           */
@@ -135,20 +135,18 @@ typedef struct {
     uint32_t max_code_len;      /* 1..24; 0 selects the default: 24 for bf16 weights,   */
                                 /* 11 for code planes (wc_encode_u8_host)               */
     uint32_t chunk_bytes;       /* must be 8 (or 0 for the default)                     */
-    uint32_t chunks_per_group;  /* G >= 1; 0 selects the default 128.  The GPU decoder  */
-                                /* of this library accepts only G = 128.                */
+    uint32_t chunks_per_group;  /* G >= 1; 0 selects the default 128.  Any G decodes:   */
+                                /* a group wider than 128 chunks takes several passes.  */
     uint32_t n_threads;         /* host threads for encoding; 0 = all hardware threads  */
-    uint32_t group_align;       /* A >= 1 elements per block; 0 selects the default 128. */
-                                /* A * max_code_len + 63 must not exceed 64 * G.  The   */
-                                /* GPU decoder accepts multiples of 8.                  */
-    uint32_t group_max_elems;   /* M, a multiple of A: elements per group at most; 0    */
-                                /* selects the default 4096, the most the GPU decoder   */
-                                /* accepts.                                             */
+    uint32_t group_align;       /* A, elements per block: a positive multiple of 8; 0   */
+                                /* selects the default 128.  Chunks layout:             */
+                                /* A * max_code_len + 63 must not exceed 64 * G.        */
+    uint32_t group_max_elems;   /* M, a multiple of A: elements per group at most,      */
+                                /* <= 4096; 0 selects the default 4096.                 */
     uint32_t layout;            /* WC_LAYOUT_LANES (0, the default: container v3) or    */
                                 /* WC_LAYOUT_CHUNKS (1, container v2)                   */
     uint32_t seg_max_bits;      /* v3: stream bits per segment at most, >= A *          */
-                                /* max_code_len and < 65536; 0 selects the default      */
-                                /* 15872, the most the GPU decoder accepts.             */
+                                /* max_code_len and <= 15872 (0: that default).         */
     uint32_t coder;             /* WC_CODER_HUFFMAN (0, the default) or WC_CODER_RANS   */
                                 /* (1: lanes layout only; max_code_len is ignored and   */
                                 /* 97 A <= 8 (seg_max_bits - 2048) is required)         */

@@ -80,9 +80,9 @@ struct Raw {
     uint32_t ga, gb;
 };
 
-__device__ __forceinline__ Raw load_raw(const DecodeParams& p, const Meta& m, uint32_t lane) {
+__device__ __forceinline__ Raw load_raw(const DecodeParams& p, const Meta& m, uint32_t lane, uint32_t pass = 0) {
     Raw r;
-    const uint64_t a = (m.p0 >> 6) + kChunksPerLane * lane;
+    const uint64_t a = (m.p0 >> 6) + kGroupChunks * pass + kChunksPerLane * lane;
     const uint64_t c1 = (m.p1 - 1) >> 6;
     r.q0 = make_uint4(0, 0, 0, 0);
     r.q1 = make_uint3(0, 0, 0);
@@ -144,21 +144,27 @@ __device__ __forceinline__ Chain make_chain(uint64_t c, uint64_t p0, uint64_t p1
 
 struct Unit {
     Chain a, b;
-    uint64_t A;    // first element of the group
-    uint32_t n;    // its elements (at most kGroupMaxElems)
+    uint64_t A;       // first element of the group
+    uint32_t n;       // its elements (at most kGroupMaxElems)
+    uint32_t passes;  // passes of 128 chunks its codewords span (1 unless chunks_per_group > 128)
 };
 
-__device__ __forceinline__ Unit make_unit(const Raw& r, const Meta& m, uint32_t lane) {
+// The chains of pass `pass` of a group: lane t takes its chunks
+// c0 + 128 pass + 2t and the next (the pass's first chunk has the parity of
+// c0, so the same window cut serves every pass).
+__device__ __forceinline__ Unit make_unit(const Raw& r, const Meta& m, uint32_t lane, uint32_t pass = 0) {
     Unit x;
     const bool odd = (m.p0 >> 6) & 1;
     const uint32_t d0 = odd ? r.q0.z : r.q0.x, d1 = odd ? r.q0.w : r.q0.y;
     const uint32_t d2 = odd ? r.q1.x : r.q0.z, d3 = odd ? r.q1.y : r.q0.w;
     const uint32_t d4 = odd ? r.q1.z : r.q1.x;
-    const uint64_t c = (m.p0 >> 6) + kChunksPerLane * lane;
+    const uint64_t c = (m.p0 >> 6) + kGroupChunks * pass + kChunksPerLane * lane;
     x.a = make_chain(c, m.p0, m.p1, d0, d1, d2, r.ga);
     x.b = make_chain(c + 1, m.p0, m.p1, d2, d3, d4, r.gb);
     x.A = m.e0;
     x.n = (uint32_t)min_u64(m.e1 - m.e0, kGroupMaxElems);   // kept 64-bit: every loaded word is used
+    const uint64_t span = ((m.p1 - 1) >> 6) - (m.p0 >> 6) + 1;   // chunks the group's codewords touch
+    x.passes = (uint32_t)((span + kGroupChunks - 1) / kGroupChunks);
     return x;
 }
 
@@ -267,6 +273,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) 
     lt.l2_n = min(__builtin_amdgcn_readfirstlane(s_long[161]), p.l2_cap);
 
     Unit cur = make_unit(r0, m0, lane);
+    Meta cur_meta = m0;
     m_next = uniform_meta(m_next);
     uint32_t dot_mat = 0;   // fused product: matrix of the wave's current group
 
@@ -300,119 +307,136 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) 
 
         const Meta m_after = load_meta(p, min_u64(un + stride, last_u));
 
-        // phase 1: count the codewords starting in each chunk
-        uint32_t ca = 0, cb = 0;
-        {
-            uint32_t a0 = cur.a.w0, a1 = cur.a.w1, a2 = cur.a.w2;
-            uint32_t b0 = cur.b.w0, b1 = cur.b.w1, b2 = cur.b.w2;
-            int32_t ra = cur.a.bits, rb = cur.b.bits;
-            while (ra > 0 || rb > 0) {
-                // both lookups are issued before the (rare) long-code branch
-                uint32_t ea = s_cnt[a0 >> (32 - KC)];
-                uint32_t eb = s_cnt[b0 >> (32 - KC)];
-                if ((ea == 0) | (eb == 0)) {
-                    if (ea == 0) ea = long_count_entry<KD>(a0, KC + 1, lt);
-                    if (eb == 0) eb = long_count_entry<KD>(b0, KC + 1, lt);
-                }
-                ca += __popc(__builtin_amdgcn_ubfe(ea, 16, (uint32_t)min(max(ra, 0), 16)));
-                cb += __popc(__builtin_amdgcn_ubfe(eb, 16, (uint32_t)min(max(rb, 0), 16)));
-                ra -= (int32_t)((ea >> 8) & 0xFFu);
-                rb -= (int32_t)((eb >> 8) & 0xFFu);
-                consume(a0, a1, a2, ea);
-                consume(b0, b1, b2, eb);
-            }
-        }
-
-        // wave-wide exclusive scan of the lane counts: each chain's first
-        // output index inside the unit
-        const uint32_t count = ca + cb;
-        const uint32_t pos_a = wave_inclusive_scan(count) - count;
-        const uint32_t pos_b = pos_a + ca;
-
-        // phase 2: decode again and stage the exponent bytes; a chain never
-        // writes past the group's element range, even for a corrupted stream
-        const uint32_t todo_a = min(ca, pos_a < n_unit ? n_unit - pos_a : 0u);
-        const uint32_t todo_b = min(cb, pos_b < n_unit ? n_unit - pos_b : 0u);
-        uint8_t* qa = ebuf + pos_a;
-        uint8_t* qb = ebuf + pos_b;
-        uint8_t* const qa_end = qa + todo_a;
-        uint8_t* const qb_end = qb + todo_b;
-        {
-            uint32_t a0 = cur.a.w0, a1 = cur.a.w1, a2 = cur.a.w2;
-            uint32_t b0 = cur.b.w0, b1 = cur.b.w1, b2 = cur.b.w2;
-            auto step_a = [&]() {
-                uint2 e = s_dec[a0 >> (32 - KD)];
-                if (e.x == 0) e = long_decode_entry<KD>(a0, KD + 1, lt);
-                put4(qa, qa_end, dummy, e);
-                consume(a0, a1, a2, e.x);
-                return e;
-            };
-            auto step_b = [&]() {
-                uint2 e = s_dec[b0 >> (32 - KD)];
-                if (e.x == 0) e = long_decode_entry<KD>(b0, KD + 1, lt);
-                put4(qb, qb_end, dummy, e);
-                consume(b0, b1, b2, e.x);
-                return e;
-            };
-            // first lookups: each chain keeps its first three symbols aside
-            uint32_t head_a, head_b, na, nb;
+        // The phases over one pass of chains: lane t's chains are the pass's
+        // chunks 2t and 2t + 1; their output starts at `base` inside the
+        // group.  Returns the pass's codeword count (the same for every lane).
+        auto run_pass = [&](const Chain& ch_a, const Chain& ch_b, uint32_t base) -> uint32_t {
+            // phase 1: count the codewords starting in each chunk
+            uint32_t ca = 0, cb = 0;
             {
-                uint2 ea = s_dec[a0 >> (32 - KD)];
-                uint2 eb = s_dec[b0 >> (32 - KD)];
-                if ((ea.x == 0) | (eb.x == 0)) {
-                    if (ea.x == 0) ea = long_decode_entry<KD>(a0, KD + 1, lt);
-                    if (eb.x == 0) eb = long_decode_entry<KD>(b0, KD + 1, lt);
+                uint32_t a0 = ch_a.w0, a1 = ch_a.w1, a2 = ch_a.w2;
+                uint32_t b0 = ch_b.w0, b1 = ch_b.w1, b2 = ch_b.w2;
+                int32_t ra = ch_a.bits, rb = ch_b.bits;
+                while (ra > 0 || rb > 0) {
+                    // both lookups are issued before the (rare) long-code branch
+                    uint32_t ea = s_cnt[a0 >> (32 - KC)];
+                    uint32_t eb = s_cnt[b0 >> (32 - KC)];
+                    if ((ea == 0) | (eb == 0)) {
+                        if (ea == 0) ea = long_count_entry<KD>(a0, KC + 1, lt);
+                        if (eb == 0) eb = long_count_entry<KD>(b0, KC + 1, lt);
+                    }
+                    ca += __popc(__builtin_amdgcn_ubfe(ea, 16, (uint32_t)min(max(ra, 0), 16)));
+                    cb += __popc(__builtin_amdgcn_ubfe(eb, 16, (uint32_t)min(max(rb, 0), 16)));
+                    ra -= (int32_t)((ea >> 8) & 0xFFu);
+                    rb -= (int32_t)((eb >> 8) & 0xFFu);
+                    consume(a0, a1, a2, ea);
+                    consume(b0, b1, b2, eb);
                 }
-                put4(qa, qa_end, dummy, ea);
-                put4(qb, qb_end, dummy, eb);
-                consume(a0, a1, a2, ea.x);
-                consume(b0, b1, b2, eb.x);
-                head_a = ea.y;
-                head_b = eb.y;
-                na = (ea.x >> 8) & 0xFFu;
-                nb = (eb.x >> 8) & 0xFFu;
             }
-            while (na < kHeadBytes && qa < qa_end) {   // rare: the first lookup held fewer symbols
-                const uint2 e = step_a();
-                head_a = (head_a & ((1u << (8 * na)) - 1u)) | (e.y << (8 * na));
-                na += (e.x >> 8) & 0xFFu;
-            }
-            while (nb < kHeadBytes && qb < qb_end) {
-                const uint2 e = step_b();
-                head_b = (head_b & ((1u << (8 * nb)) - 1u)) | (e.y << (8 * nb));
-                nb += (e.x >> 8) & 0xFFu;
-            }
-            while (qa < qa_end || qb < qb_end) {
-                // both lookups are issued before the (rare) long-code branch
-                uint2 ea = s_dec[a0 >> (32 - KD)];
-                uint2 eb = s_dec[b0 >> (32 - KD)];
-                if ((ea.x == 0) | (eb.x == 0)) {
-                    if (ea.x == 0) ea = long_decode_entry<KD>(a0, KD + 1, lt);
-                    if (eb.x == 0) eb = long_decode_entry<KD>(b0, KD + 1, lt);
+
+            // wave-wide exclusive scan of the lane counts: each chain's first
+            // output index inside the unit
+            const uint32_t count = ca + cb;
+            const uint32_t incl = wave_inclusive_scan(count);
+            const uint32_t pos_a = base + incl - count;
+            const uint32_t pos_b = pos_a + ca;
+
+            // phase 2: decode again and stage the exponent bytes; a chain never
+            // writes past the group's element range, even for a corrupted stream
+            const uint32_t todo_a = min(ca, pos_a < n_unit ? n_unit - pos_a : 0u);
+            const uint32_t todo_b = min(cb, pos_b < n_unit ? n_unit - pos_b : 0u);
+            uint8_t* qa = ebuf + pos_a;
+            uint8_t* qb = ebuf + pos_b;
+            uint8_t* const qa_end = qa + todo_a;
+            uint8_t* const qb_end = qb + todo_b;
+            {
+                uint32_t a0 = ch_a.w0, a1 = ch_a.w1, a2 = ch_a.w2;
+                uint32_t b0 = ch_b.w0, b1 = ch_b.w1, b2 = ch_b.w2;
+                auto step_a = [&]() {
+                    uint2 e = s_dec[a0 >> (32 - KD)];
+                    if (e.x == 0) e = long_decode_entry<KD>(a0, KD + 1, lt);
+                    put4(qa, qa_end, dummy, e);
+                    consume(a0, a1, a2, e.x);
+                    return e;
+                };
+                auto step_b = [&]() {
+                    uint2 e = s_dec[b0 >> (32 - KD)];
+                    if (e.x == 0) e = long_decode_entry<KD>(b0, KD + 1, lt);
+                    put4(qb, qb_end, dummy, e);
+                    consume(b0, b1, b2, e.x);
+                    return e;
+                };
+                // first lookups: each chain keeps its first three symbols aside
+                uint32_t head_a, head_b, na, nb;
+                {
+                    uint2 ea = s_dec[a0 >> (32 - KD)];
+                    uint2 eb = s_dec[b0 >> (32 - KD)];
+                    if ((ea.x == 0) | (eb.x == 0)) {
+                        if (ea.x == 0) ea = long_decode_entry<KD>(a0, KD + 1, lt);
+                        if (eb.x == 0) eb = long_decode_entry<KD>(b0, KD + 1, lt);
+                    }
+                    put4(qa, qa_end, dummy, ea);
+                    put4(qb, qb_end, dummy, eb);
+                    consume(a0, a1, a2, ea.x);
+                    consume(b0, b1, b2, eb.x);
+                    head_a = ea.y;
+                    head_b = eb.y;
+                    na = (ea.x >> 8) & 0xFFu;
+                    nb = (eb.x >> 8) & 0xFFu;
                 }
-                put4(qa, qa_end, dummy, ea);
-                put4(qb, qb_end, dummy, eb);
-                consume(a0, a1, a2, ea.x);
-                consume(b0, b1, b2, eb.x);
+                while (na < kHeadBytes && qa < qa_end) {   // rare: the first lookup held fewer symbols
+                    const uint2 e = step_a();
+                    head_a = (head_a & ((1u << (8 * na)) - 1u)) | (e.y << (8 * na));
+                    na += (e.x >> 8) & 0xFFu;
+                }
+                while (nb < kHeadBytes && qb < qb_end) {
+                    const uint2 e = step_b();
+                    head_b = (head_b & ((1u << (8 * nb)) - 1u)) | (e.y << (8 * nb));
+                    nb += (e.x >> 8) & 0xFFu;
+                }
+                while (qa < qa_end || qb < qb_end) {
+                    // both lookups are issued before the (rare) long-code branch
+                    uint2 ea = s_dec[a0 >> (32 - KD)];
+                    uint2 eb = s_dec[b0 >> (32 - KD)];
+                    if ((ea.x == 0) | (eb.x == 0)) {
+                        if (ea.x == 0) ea = long_decode_entry<KD>(a0, KD + 1, lt);
+                        if (eb.x == 0) eb = long_decode_entry<KD>(b0, KD + 1, lt);
+                    }
+                    put4(qa, qa_end, dummy, ea);
+                    put4(qb, qb_end, dummy, eb);
+                    consume(a0, a1, a2, ea.x);
+                    consume(b0, b1, b2, eb.x);
+                }
+                // The staging belongs to this wave alone, and the LDS executes a
+                // wave's accesses in issue order: once every lane has left the
+                // loop, the head bytes overwrite whatever a left neighbour's last
+                // four-byte store put there.
+                wave_lds_order();
+                uint8_t* ha = ebuf + pos_a;
+                uint8_t* hb = ebuf + pos_b;
+    #pragma unroll
+                for (uint32_t k = 0; k < kHeadBytes; ++k) {
+                    if (todo_a > k) ha[k] = (uint8_t)(head_a >> (8 * k));
+                    if (todo_b > k) hb[k] = (uint8_t)(head_b >> (8 * k));
+                }
             }
-            // The staging belongs to this wave alone, and the LDS executes a
-            // wave's accesses in issue order: once every lane has left the
-            // loop, the head bytes overwrite whatever a left neighbour's last
-            // four-byte store put there.
-            wave_lds_order();
-            uint8_t* ha = ebuf + pos_a;
-            uint8_t* hb = ebuf + pos_b;
-#pragma unroll
-            for (uint32_t k = 0; k < kHeadBytes; ++k) {
-                if (todo_a > k) ha[k] = (uint8_t)(head_a >> (8 * k));
-                if (todo_b > k) hb[k] = (uint8_t)(head_b >> (8 * k));
-            }
+            return (uint32_t)__builtin_amdgcn_readlane((int)incl, kWaveLanes - 1);
+        };
+        uint32_t done = run_pass(cur.a, cur.b, 0);
+        // a group whose codewords span more than one pass of 128 chunks
+        // (chunks_per_group above 128): the further passes load their chunks
+        // here and continue at the count decoded so far
+        for (uint32_t pass = 1; pass < cur.passes; ++pass) {
+            const Unit w = make_unit(load_raw(p, cur_meta, lane, pass), cur_meta, lane, pass);
+            done += run_pass(w.a, w.b, done);
         }
+
         // consume every load of this iteration now, before the merge issues
         // its stores: the next group's chains and table entries, and the sm
         // bytes (a load still pending at the next iteration's top would make
         // the wait there cover the merge stores as well)
         const Unit next = make_unit(nxt, m_next, lane);
+        const Meta next_meta = m_next;
         m_next = uniform_meta(m_after);
         wave_lds_order();
 #pragma unroll
@@ -453,6 +477,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) 
         wave_lds_order();   // the staging is rewritten by the next group
         u = un;
         cur = next;
+        cur_meta = next_meta;
     }
 
     // the container's last block, when it holds fewer than 8 elements (a

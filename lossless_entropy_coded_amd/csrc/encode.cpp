@@ -466,8 +466,15 @@ int encode_impl(const T* const* tensors, const uint64_t* numels, uint32_t n_tens
         coder = opts->coder;
         if (opts->gap_bits) gap_bits = opts->gap_bits;
     }
-    if (max_len < 1 || max_len > kMaxCodeLen || group < 1 || group > (1u << 20) || align > (1u << 20) ||
-        max_elems < align || max_elems % align || max_elems > (1u << 26))
+    // The containers this library writes are the ones its GPU decoder takes:
+    // blocks of a positive multiple of 8 elements (each lane writes whole
+    // 8-element blocks), at most 4096 elements per group or segment (one
+    // wave's eight merge steps), and for the lanes layout at most 15872 bits
+    // per segment (one wave's 2 KB staging window).  The oracle's writer also
+    // accepts other values of these fields; the GPU decoder refuses those
+    // containers with WC_ERR_UNSUPPORTED.
+    if (max_len < 1 || max_len > kMaxCodeLen || group < 1 || group > (1u << 20) || align < 8 || align % 8 ||
+        max_elems < align || max_elems % align || max_elems > kDefaultMaxElems)
         return WC_ERR_INVALID_ARG;
     if (kind == WC_LAYOUT_CHUNKS) {
         // every block must fit in one group whatever its codes: align codewords of
@@ -476,7 +483,7 @@ int encode_impl(const T* const* tensors, const uint64_t* numels, uint32_t n_tens
     } else if (kind == WC_LAYOUT_LANES) {
         // a segment's lane offsets are u16 bit counts; one block always fits
         // (rANS: A symbols cost at most 97 eighths each besides the 64 final states)
-        if (seg_bits > 65535u) return WC_ERR_INVALID_ARG;
+        if (seg_bits > kDefaultSegBits) return WC_ERR_INVALID_ARG;
         if (coder == WC_CODER_RANS ? seg_bits < kLanes * kRansStateBits ||
                                          97ull * align > 8ull * (seg_bits - kLanes * kRansStateBits)
                                    : (uint64_t)align * max_len > seg_bits)

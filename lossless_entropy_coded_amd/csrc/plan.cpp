@@ -269,8 +269,9 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
     const bool lanes = st == WC_OK && p->h.version == wc::kVersionLanes;
     if (st == WC_OK && (p->h.group_align % wc::kMergeElems || p->h.group_max_elems > wc::kGroupMaxElems))
         st = WC_ERR_UNSUPPORTED;
-    if (st == WC_OK && (lanes ? p->h.seg_max_bits > wc::kLanesMaxSegBits : p->h.chunks_per_group != wc::kGroupChunks))
-        st = WC_ERR_UNSUPPORTED;
+    // (any chunks_per_group: a group spanning more than 128 chunks is decoded
+    // in passes of 128)
+    if (st == WC_OK && lanes && p->h.seg_max_bits > wc::kLanesMaxSegBits) st = WC_ERR_UNSUPPORTED;
     if (st != WC_OK) {
         delete p;
         return st;

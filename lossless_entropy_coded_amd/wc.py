@@ -108,11 +108,12 @@ WC_ERR_GROUP_START = -16
 WC_ERR_STREAM_BITS = -17
 WC_ERR_TENSOR_TABLE = -18
 
-# Group table defaults (wc_encode_opts): G = chunks per group, the most one
-# wave64 decodes (two 64-bit chunks per lane); A = elements per block, so that
-# every group's output starts on a 256-byte boundary; M = elements per group at
-# most (eight 8-element merge steps per lane).  The GPU decoder accepts G = 128,
-# any A that is a multiple of 8 and M <= 4096.
+# Group table defaults (wc_encode_opts): G = chunks per group, what one wave64
+# decodes in one pass (two 64-bit chunks per lane; wider groups take several
+# passes); A = elements per block, so that every group's output starts on a
+# 256-byte boundary; M = elements per group at most (eight 8-element merge
+# steps per lane).  The writer takes any G, A a positive multiple of 8 and
+# M <= 4096, the range the GPU decoder takes.
 GROUP_CHUNKS = 128
 GROUP_ALIGN = 128
 GROUP_MAX_ELEMS = 4096

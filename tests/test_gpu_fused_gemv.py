@@ -89,7 +89,10 @@ def _check_tensor(oracle_lib, got, W, x, align):
 # lanes, Huffman in chunks (byte or packed gaps), rANS in interleaved lanes
 # (whose segments are also runs of whole blocks, so the same bound holds)
 ENCODINGS = {"lanes": {"layout": "lanes"}, "chunks": {"layout": "chunks"},
-             "rans": {"layout": "lanes", "coder": "rans"}, "chunks5": {"layout": "chunks", "gap_bits": 5}}
+             "rans": {"layout": "lanes", "coder": "rans"}, "chunks5": {"layout": "chunks", "gap_bits": 5},
+             # groups of 64 chunks, and of 1000 chunks (decoded in passes of 128)
+             "chunks_g64": {"layout": "chunks", "chunks_per_group": 64},
+             "chunks5_g1000": {"layout": "chunks", "gap_bits": 5, "chunks_per_group": 1000}}
 
 
 # (block size A, group cap M, tensors as (rows, cols) or (n,) vectors); every
@@ -104,7 +107,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("layout", ["lanes", "chunks", "rans", "chunks5"])
+@pytest.mark.parametrize("layout", ["lanes", "chunks", "rans", "chunks5", "chunks_g64", "chunks5_g1000"])
 @pytest.mark.parametrize("name,align,cap,shapes", CASES, ids=[c[0] for c in CASES])
 def test_fused_against_oracle(wc, oracle_lib, name, align, cap, shapes, layout):
     """Each matrix alone, then every run of consecutive matrices in one call:

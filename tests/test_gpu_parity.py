@@ -211,6 +211,29 @@ def test_group_block_sizes(wc, oracle_lib, align, writer):
     assert np.array_equal(gpu_decode(wc, blob), wl.bits)
 
 
+@pytest.mark.parametrize("G", [49, 64, 256, 1000])
+@pytest.mark.parametrize("writer", ["product", "oracle"])
+@pytest.mark.parametrize("gap_bits", [8, 5])
+def test_chunks_per_group(wc, oracle_lib, G, writer, gap_bits):
+    """Any group width in chunks decodes exactly: a group whose codewords span
+    more than 128 chunks is decoded in passes of 128 chunks.  High-entropy
+    values (about 16-bit codes) make groups of 4096 elements span up to 1024
+    chunks, i.e. up to eight passes; the low-entropy block keeps groups
+    within one pass."""
+    from lossless_entropy_coded_amd.synth import make_workload
+    rng = np.random.default_rng(G)
+    wide = rng.permutation(np.arange(65536, dtype=np.uint32).astype(np.uint16))[:50_000]
+    wl = make_workload("heavy_tail_14k", scale_rows=128)
+    for label, w, numels in (("all patterns", wide, None), ("heavy_tail_14k", wl.bits, wl.numels)):
+        if writer == "product":
+            parts = [w] if numels is None else wl.tensors()
+            blob = wc.encode_host(parts, layout="chunks", chunks_per_group=G, gap_bits=gap_bits)
+        else:
+            blob = oracle_lib.encode(w, numels=numels, chunks_per_group=G, gap_bits=gap_bits)
+        log(f"case: chunks_per_group={G} writer={writer} gap={gap_bits} {label}")
+        assert np.array_equal(gpu_decode(wc, blob), w)
+
+
 def test_corrupted_stream_stays_in_bounds(wc):
     """Valid metadata, garbage bit stream: output may be wrong, but nothing is
     written outside [out, out + n)."""

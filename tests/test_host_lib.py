@@ -139,7 +139,7 @@ def _u64(v):
     return np.frombuffer(np.uint64(v).tobytes(), np.uint8)
 
 
-def test_plan_rejects_each_fault(wc):
+def test_plan_rejects_each_fault(wc, oracle_lib):
     from lossless_entropy_coded_amd.synth import make_workload
     wl = make_workload("matrix_1k", scale_rows=128)
     blob = wc.encode_host(wl.tensors(), layout="chunks")
@@ -195,13 +195,19 @@ def test_plan_rejects_each_fault(wc):
     assert mutated(setb(pad, np.array([0x10], np.uint8))) == wc.WC_ERR_STREAM_BITS
     assert mutated(setb(s["off_tens"] + 8, _u64(s["n_elems"] + 1))) == wc.WC_ERR_TENSOR_TABLE
     assert mutated(setb(s["off_tens"], _u64(3))) == wc.WC_ERR_TENSOR_TABLE
-    # valid containers with a group size or block size the GPU decoder does not accept
-    b2 = wc.encode_host(wl.tensors(), chunks_per_group=2 * wc.GROUP_CHUNKS, layout="chunks")
-    assert _plan_status(wc, b2) == wc.WC_ERR_UNSUPPORTED
-    b3 = wc.encode_host(wl.tensors(), group_align=100, group_max_elems=4000, layout="chunks")
-    assert _plan_status(wc, b3) == wc.WC_ERR_UNSUPPORTED
-    b4 = wc.encode_host(wl.tensors(), group_max_elems=2 * wc.GROUP_MAX_ELEMS, layout="chunks")
-    assert _plan_status(wc, b4) == wc.WC_ERR_UNSUPPORTED
+    # any chunks-per-group is decoded (a group wider than 128 chunks in passes)
+    for g in (49, 64, 2 * wc.GROUP_CHUNKS, 1000):
+        assert _plan_status(wc, wc.encode_host(wl.tensors(), chunks_per_group=g, layout="chunks")) in ok
+    # valid containers with a block size or group size the GPU decoder does not
+    # take: only the oracle writes them, the product's writer refuses them
+    for kw in ({"group_align": 100, "group_max_elems": 4000}, {"group_max_elems": 2 * wc.GROUP_MAX_ELEMS},
+               {"group_align": 4, "group_max_elems": 4096}):
+        with pytest.raises(wc.WCError) as ei:
+            wc.encode_host(wl.tensors(), layout="chunks", **kw)
+        assert ei.value.status == wc.WC_ERR_INVALID_ARG
+        blob_o = oracle_lib.encode(wl.bits, numels=wl.numels, chunks_per_group=wc.GROUP_CHUNKS, **kw)
+        assert _plan_status(wc, blob_o) == wc.WC_ERR_UNSUPPORTED
+        assert np.array_equal(oracle_lib.decode(blob_o), wl.bits)
 
 
 def test_plan_rejects_random_corruption_without_crashing(wc):
@@ -233,7 +239,7 @@ def test_gemv_argument_checks_without_device(wc):
     assert call(vp(0), 4, 8, vp(fake), vp(fake), vp(0)) == wc.WC_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("A,M,B", [(128, 4096, 15872), (64, 1024, 4096), (8, 512, 500), (8, 4096, 65535)])
+@pytest.mark.parametrize("A,M,B", [(128, 4096, 15872), (64, 1024, 4096), (8, 512, 500), (8, 4096, 15872)])
 def test_lanes_encoder_matches_oracle_writer(wc, oracle_lib, A, M, B):
     """The product's interleaved-lane writer is byte-identical to the oracle's."""
     from lossless_entropy_coded_amd.synth import make_workload
@@ -249,7 +255,9 @@ def test_lanes_encoder_matches_oracle_writer(wc, oracle_lib, A, M, B):
 
 def test_lanes_encoder_rejects_bad_options(wc):
     w = np.arange(10, dtype=np.uint16)
-    for kw in ({"seg_max_bits": 70000}, {"seg_max_bits": 128 * 24 - 1}, {"group_align": 64, "seg_max_bits": 1000}):
+    for kw in ({"seg_max_bits": 70000}, {"seg_max_bits": 15873}, {"seg_max_bits": 128 * 24 - 1},
+               {"group_align": 64, "seg_max_bits": 1000}, {"group_align": 12, "group_max_elems": 48},
+               {"group_max_elems": 4104, "group_align": 8}):
         with pytest.raises(wc.WCError) as ei:
             wc.encode_host([w], layout="lanes", **kw)
         assert ei.value.status == wc.WC_ERR_INVALID_ARG
@@ -288,11 +296,16 @@ def test_plan_rejects_each_lanes_fault(wc, oracle_lib):
     # an offset that is not where the lane's bits begin: wc_plan cannot see it
     assert mutated(setb(lo + 2 * 11, np.frombuffer(np.uint16(int(s["lane_off"][0, 11]) + 1).tobytes(),
                                                    np.uint8))) in ok
-    # valid containers the GPU decoder does not accept
-    b2 = wc.encode_host(wl.tensors(), layout="lanes", seg_max_bits=20000)
-    assert _plan_status(wc, b2) == wc.WC_ERR_UNSUPPORTED
-    b3 = wc.encode_host(wl.tensors(), layout="lanes", group_align=100, group_max_elems=4000)
-    assert _plan_status(wc, b3) == wc.WC_ERR_UNSUPPORTED
+    # valid containers the GPU decoder does not accept: only the oracle writes
+    # them, the product's writer refuses them
+    for kw in ({"seg_max_bits": 20000}, {"group_align": 100, "group_max_elems": 4000},
+               {"group_max_elems": 8192}):
+        with pytest.raises(wc.WCError) as ei:
+            wc.encode_host(wl.tensors(), layout="lanes", **kw)
+        assert ei.value.status == wc.WC_ERR_INVALID_ARG
+        blob_o = oracle_lib.encode_lanes(wl.bits, numels=wl.numels, **kw)
+        assert _plan_status(wc, blob_o) == wc.WC_ERR_UNSUPPORTED
+        assert np.array_equal(oracle_lib.decode(blob_o), wl.bits)
     # containers written by the oracle pass every check
     wl2 = make_workload("attn_4k_zeros", scale_rows=64)
     assert _plan_status(wc, oracle_lib.encode_lanes(wl2.bits, numels=wl2.numels)) in ok
@@ -343,7 +356,7 @@ def test_plan_checks_element_kind(wc):
     assert ei.value.status == wc.WC_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("A,M,B", [(128, 4096, 15872), (64, 1024, 4096), (8, 512, 2200), (8, 4096, 65535)])
+@pytest.mark.parametrize("A,M,B", [(128, 4096, 15872), (64, 1024, 4096), (8, 512, 2200), (8, 4096, 2560)])
 def test_rans_encoder_matches_oracle_writer(wc, oracle_lib, A, M, B):
     """The product's rANS writer (bf16 and u8 kinds) is byte-identical to the
     oracle's, for any thread count."""
@@ -378,8 +391,8 @@ def test_rans_encoder_edge_inputs(wc, oracle_lib):
 
 def test_rans_encoder_rejects_bad_options(wc):
     w = np.arange(10, dtype=np.uint16)
-    for kw in ({"seg_max_bits": 2047}, {"seg_max_bits": 70000}, {"group_align": 128, "seg_max_bits": 3599},
-               {"layout": "chunks"}):
+    for kw in ({"seg_max_bits": 2047}, {"seg_max_bits": 70000}, {"seg_max_bits": 15873},
+               {"group_align": 128, "seg_max_bits": 3599}, {"layout": "chunks"}):
         with pytest.raises(wc.WCError) as ei:
             wc.encode_host([w], coder="rans", **kw)
         assert ei.value.status == wc.WC_ERR_INVALID_ARG

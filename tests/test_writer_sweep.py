@@ -1,8 +1,11 @@
 """A seeded sweep over encoder options: for random combinations of layout,
 coder, element kind, gap width, block size A, element cap M, segment bit cap
-B, thread count and input (length, distribution), the product's writer and
-the oracle's writer give the same container byte for byte, and the oracle
-decodes it to the input."""
+B, chunks per group G, thread count and input (length, distribution), the
+product's writer and the oracle's writer give the same container byte for
+byte, and the oracle decodes it to the input.  Where the options leave the
+range the GPU decoder takes (A not a positive multiple of 8, M above 4096, a
+lanes segment above 15872 bits) the product's writer refuses them with
+WC_ERR_INVALID_ARG, and the oracle's container still decodes on the CPU."""
 import numpy as np
 import pytest
 
@@ -39,8 +42,26 @@ def wc_lib():
     return wc
 
 
+def product_range(A, M, B=None):
+    """Whether the product's writer takes these options (the GPU decoder's range)."""
+    return A >= 8 and A % 8 == 0 and M <= 4096 and (B is None or B <= 15872)
+
+
+def _product(wc, in_range, write):
+    """The product writer's container, or None after checking that it refuses
+    options outside its range."""
+    if in_range:
+        return write()
+    with pytest.raises(wc.WCError) as ei:
+        write()
+    assert ei.value.status == wc.WC_ERR_INVALID_ARG
+    return None
+
+
 def build_case(wc, oracle_lib, case):
-    """Case `case` of the sweep: (product container, oracle container, input, element kind, description)."""
+    """Case `case` of the sweep: (product container or None when the product's
+    writer refuses the options, oracle container, input, element kind,
+    description)."""
     rng = np.random.default_rng(1000 + case)
     variant = ["lanes-huffman", "lanes-rans", "chunks", "chunks-gap5"][case % 4]
     kind = "u8" if (variant.startswith("lanes") and rng.integers(0, 3) == 0) else "bf16"
@@ -55,37 +76,38 @@ def build_case(wc, oracle_lib, case):
     desc = f"{variant} {kind} n={n} A={A} M={M}"
     if variant.startswith("chunks"):
         L = int(rng.choice([12, 16, 24]))
-        G = int(rng.choice([64, 128, 256]))
+        G = int(rng.choice([64, 128, 256, 1000]))
         if A * L + 63 > 64 * G:
             G = -(-(A * L + 63) // 64)
         gap = 5 if variant.endswith("gap5") else 8
-        a = wc.encode_host(tensors, layout="chunks", max_code_len=L, chunks_per_group=G, group_align=A,
-                           group_max_elems=M, gap_bits=gap, n_threads=threads)
+        a = _product(wc, product_range(A, M), lambda: wc.encode_host(
+            tensors, layout="chunks", max_code_len=L, chunks_per_group=G, group_align=A, group_max_elems=M,
+            gap_bits=gap, n_threads=threads))
         b = oracle_lib.encode(data, numels=numels, max_code_len=L, chunks_per_group=G, group_align=A,
                               group_max_elems=M, gap_bits=gap)
         desc += f" L={L} G={G} gap={gap}"
     elif variant == "lanes-rans":
         B = max(int(rng.choice([2048, 4096, 15872, 65535])), 2048 + (97 * A + 7) // 8)
         if kind == "u8":
-            a = wc.encode_u8_host(tensors, coder="rans", group_align=A, group_max_elems=M, seg_max_bits=B,
-                                  n_threads=threads)
+            a = _product(wc, product_range(A, M, B), lambda: wc.encode_u8_host(
+                tensors, coder="rans", group_align=A, group_max_elems=M, seg_max_bits=B, n_threads=threads))
             b = oracle_lib.encode_lanes_rans_u8(data, numels=numels, group_align=A, group_max_elems=M, seg_max_bits=B)
         else:
-            a = wc.encode_host(tensors, coder="rans", group_align=A, group_max_elems=M, seg_max_bits=B,
-                               n_threads=threads)
+            a = _product(wc, product_range(A, M, B), lambda: wc.encode_host(
+                tensors, coder="rans", group_align=A, group_max_elems=M, seg_max_bits=B, n_threads=threads))
             b = oracle_lib.encode_lanes_rans(data, numels=numels, group_align=A, group_max_elems=M, seg_max_bits=B)
         desc += f" B={B}"
     else:
         L = int(rng.choice([11, 16, 24]))
         B = max(int(rng.choice([500, 4096, 15872, 65535])), A * L)
         if kind == "u8":
-            a = wc.encode_u8_host(tensors, max_code_len=L, group_align=A, group_max_elems=M, seg_max_bits=B,
-                                  n_threads=threads)
+            a = _product(wc, product_range(A, M, B), lambda: wc.encode_u8_host(
+                tensors, max_code_len=L, group_align=A, group_max_elems=M, seg_max_bits=B, n_threads=threads))
             b = oracle_lib.encode_lanes_u8(data, numels=numels, max_code_len=L, group_align=A, group_max_elems=M,
                                            seg_max_bits=B)
         else:
-            a = wc.encode_host(tensors, max_code_len=L, group_align=A, group_max_elems=M, seg_max_bits=B,
-                               n_threads=threads)
+            a = _product(wc, product_range(A, M, B), lambda: wc.encode_host(
+                tensors, max_code_len=L, group_align=A, group_max_elems=M, seg_max_bits=B, n_threads=threads))
             b = oracle_lib.encode_lanes(data, numels=numels, max_code_len=L, group_align=A, group_max_elems=M,
                                         seg_max_bits=B)
         desc += f" L={L} B={B}"
@@ -95,6 +117,12 @@ def build_case(wc, oracle_lib, case):
 @pytest.mark.parametrize("case", CASES)
 def test_product_writer_equals_oracle_writer(wc_lib, oracle_lib, case):
     a, b, data, kind, desc = build_case(wc_lib, oracle_lib, case)
-    assert np.array_equal(a, b), desc
-    out = oracle_lib.decode_u8(a) if kind == "u8" else oracle_lib.decode(a)
+    assert a is None or np.array_equal(a, b), desc
+    out = oracle_lib.decode_u8(b) if kind == "u8" else oracle_lib.decode(b)
     assert np.array_equal(out, data), desc
+
+
+def test_sweep_covers_both_sides_of_the_range(wc_lib, oracle_lib):
+    """The sweep holds options the product writes and options it refuses."""
+    written = sum(build_case(wc_lib, oracle_lib, c)[0] is not None for c in CASES[:48])
+    assert 0 < written < 48
