@@ -15,8 +15,11 @@ Prints one JSON line:
             (HIP events on the launch stream), against 8 TB/s HBM3E peak;
             `traffic` = HBM bytes from rocprofv3 FETCH_SIZE/WRITE_SIZE runs
             recorded under profiles/ (null if the kernel source changed since);
-            `copy_GBps` / `frac_of_copy`: the same traffic against a plain
-            copy-shaped kernel moving as many bytes, timed in the same process;
+            `stream_ref`: the library's streaming yardstick
+            (wc_stream_reference_async: one load and one store per 16 bytes,
+            workgroups in address order) reading as many bytes as the decode
+            reads and writing as many as it writes, timed the same way in
+            the same process; `frac_of_stream_ref` = achieved / its GB/s;
             `launch_us`: p10 / p50 / p90 of individually timed launches
   cpu_baseline  the CPU oracle's serial decode of the same container on one
             host core, repeated until about 10 s have elapsed (reported
@@ -190,26 +193,38 @@ def copy_calibration(args):
                       "GBps_read_plus_write": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
 
 
-def copy_rate(torch, nbytes, reps=20):
-    """GB/s (read + write) of a copy-shaped elementwise kernel that reads and
-    writes nbytes / 2 each, median of `reps` launches."""
-    half = max(4, (nbytes // 2) // 4 * 4)
-    src = torch.randint(-2**31, 2**31 - 1, (half // 4,), dtype=torch.int32, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        torch.bitwise_not(src, out=dst)
-    ts = []
-    for _ in range(reps):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        torch.bitwise_not(src, out=dst)
-        b.record()
-        b.synchronize()
-        ts.append(a.elapsed_time(b))
-    ts.sort()
-    del src, dst
-    return 2 * half / (ts[len(ts) // 2] * 1e-3) / 1e9
+def stream_reference(torch, wc, read_bytes, write_bytes, steps, stream):
+    """The streaming yardstick over the decode's traffic: wc_stream_reference_async
+    reading `read_bytes` and writing `write_bytes` (rounded down to 16), in a
+    rotation of copies exceeding 1 GiB like the decode's, settled for 60 ms,
+    then `steps` back-to-back launches timed with HIP events on `stream`."""
+    r16, w16 = read_bytes // 16 * 16, write_bytes // 16 * 16
+    if not 0 < r16 <= w16:              # the yardstick reads at most what it writes
+        return None
+    copies = rotation_copies(r16 + w16)
+    srcs = [torch.randint(-2**31, 2**31 - 1, (r16 // 4,), dtype=torch.int32, device="cuda") for _ in range(copies)]
+    dsts = [torch.empty(w16 // 4, dtype=torch.int32, device="cuda") for _ in range(copies)]
+
+    def launch(k):
+        wc.stream_reference_async(srcs[k % copies], r16, dsts[k % copies], w16, stream)
+
+    settle(torch, stream, launch, 60.0)
+    ms = _timed(torch, stream, launch, steps)
+    # spot check: the first and last output items of the last launch
+    k = (steps - 1) % copies
+    ns, nd = r16 // 16, w16 // 16
+    rr = -(-(ns << 32) // nd)
+    for j in (0, nd - 1):
+        i = min((j * rr) >> 32, ns - 1)
+        if not torch.equal(dsts[k][4 * j:4 * j + 4], ~srcs[k][4 * i:4 * i + 4]):
+            print("bench.py: the streaming reference wrote wrong bytes", file=sys.stderr)
+            sys.exit(3)
+    del srcs, dsts
+    torch.cuda.empty_cache()
+    return {"kernel": "wc_stream_reference_async (one 16-byte load + store per lane, a workgroup per 4 KiB "
+                      "of output in address order)",
+            "read_bytes": r16, "write_bytes": w16, "ms": round(ms, 5),
+            "GBps": round((r16 + w16) / (ms * 1e-3) / 1e9, 1), "rotating_copies": copies}
 
 
 def _timed(torch, stream, fn, steps):
@@ -223,6 +238,36 @@ def _timed(torch, stream, fn, steps):
     b.record(stream)
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps
+
+
+def settle(torch, stream, fn, ms):
+    """Untimed calls of fn until the GPU has run it for at least `ms`."""
+    spent, k = 0.0, 0
+    while spent < ms and k < 5000:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(10):
+            fn(k)
+            k += 1
+        b.record(stream)
+        b.synchronize()
+        spent += a.elapsed_time(b)
+    return k
+
+
+class Scrub:
+    """A 1 GiB buffer read (never written) right before a timed region: the
+    canary fills leave dirty lines in the 256 MiB Infinity Cache, and reading
+    4x its size writes them back before the timed launches start, not during
+    them."""
+
+    def __init__(self, torch):
+        self.buf = torch.zeros(ROTATE_BYTES // 4, dtype=torch.int32, device="cuda")
+
+    def __call__(self, torch, stream):
+        with torch.cuda.stream(stream):
+            self.buf.amax()
 
 
 class Rotation:
@@ -289,6 +334,8 @@ def time_decode(torch, wc, plan, blob, raw, out_bytes, codes, args, stream):
     with torch.cuda.stream(stream):
         for o in rot.outs:
             o.fill_(canary)
+    scrub = Scrub(torch)
+    scrub(torch, stream)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -318,7 +365,7 @@ def time_decode(torch, wc, plan, blob, raw, out_bytes, codes, args, stream):
     def pct(q):
         return round(singles[min(len(singles) - 1, int(q * len(singles)))], 1)
 
-    del rot, ref
+    del rot, ref, scrub
     torch.cuda.empty_cache()
     return {"total_ms": total_ms, "kernel_avg_ms": total_ms / args.steps, "copies": copies,
             "rotated_bytes": copies * (blob.size + out_bytes * n), "settle_launches": settle_launches,
@@ -394,20 +441,25 @@ def e2e_measure(torch, wc, name, layout, coder, steps, warmup, opts, stream):
         touched.clear()
         return ok
 
-    warm = max(40, warmup)
-    for arm in (arm_a, arm_b, arm_c):                  # settle clocks, warm up every arm
-        _timed(torch, stream, arm, warm)
-    fill(rot.outs, CANARY16)
-    fill(ya, float("nan"))
-    touched.clear()
-    ms_a = _timed(torch, stream, arm_a, steps)
+    # each arm: settled for at least 60 ms of its own launches (the GPU's
+    # clocks follow the load), then its outputs filled with canaries, the
+    # cache scrubbed, and `steps` launches timed
+    scrub = Scrub(torch)
+    warm = {}
+
+    def timed_arm(name, fn, fills):
+        warm[name] = settle(torch, stream, fn, 60.0)
+        for tensors, value in fills:
+            fill(tensors, value)
+        touched.clear()
+        scrub(torch, stream)
+        return _timed(torch, stream, fn, steps)
+
+    ms_a = timed_arm("a", arm_a, [(rot.outs, CANARY16), (ya, float("nan"))])
     exact_a = outs_exact()
-    fill(yb, float("nan"))
-    ms_b = _timed(torch, stream, arm_b, steps)
-    fill(yc, float("nan"))
-    ms_c = _timed(torch, stream, arm_c, steps)
-    fill(rot.outs, CANARY16)
-    ms_dec = _timed(torch, stream, decode_only, steps)
+    ms_b = timed_arm("b", arm_b, [(yb, float("nan"))])
+    ms_c = timed_arm("c", arm_c, [(yc, float("nan"))])
+    ms_dec = timed_arm("decode", decode_only, [(rot.outs, CANARY16)])
     exact_dec = outs_exact()
     identical = all(torch.equal(a.view(torch.int32), b.view(torch.int32)) for a, b in zip(ya, yb))
     finite = all(bool(torch.isfinite(y).all()) for y in ya + yb + yc)
@@ -427,7 +479,7 @@ def e2e_measure(torch, wc, name, layout, coder, steps, warmup, opts, stream):
         "workload": f"{name}: decode of the whole block, then q,k,v,o,gate,up,down batch-1 GEMVs "
                     f"(x length = each matrix's in-dimension)",
         "layout": layout, "coder": coder, "n_elems": n, "container_bytes": int(blob.size),
-        "weight_bytes": weight_bytes, "steps": steps, "warmup": warm, "rotating_copies": copies,
+        "weight_bytes": weight_bytes, "steps": steps, "settle_launches": warm, "rotating_copies": copies,
         "arm_a_decode_plus_gemv_ms": round(ms_a, 4),
         "arm_b_uncompressed_gemv_ms": round(ms_b, 4),
         "arm_c_fused_decode_gemv_ms": round(ms_c, 4),
@@ -444,7 +496,7 @@ def e2e_measure(torch, wc, name, layout, coder, steps, warmup, opts, stream):
         "host_prep_s": round(t_gen, 2),
     }
     plan.close()
-    del rot, origs, work_own
+    del rot, origs, work_own, scrub
     torch.cuda.empty_cache()
     return rec, ok
 
@@ -462,7 +514,7 @@ def end_to_end(args):
     line = {
         "metric": "end-to-end batch-1 bf16 GEMV over a 70B-shape block: decode + GEMV vs GEMV on uncompressed weights",
         "value": rec["arm_a_decode_plus_gemv_ms"], "unit": "ms", "n_gpus": 1, "steps": args.steps,
-        "warmup": rec["warmup"], "higher_is_better": False, "vs_baseline": None, "dtype": "bf16 in, fp32 accumulate",
+        "warmup": args.warmup, "higher_is_better": False, "vs_baseline": None, "dtype": "bf16 in, fp32 accumulate",
         "data": "synthetic: seeded bf16 weights (70B-block shapes, N(0, 0.015)), x ~ N(0, 1) in bf16",
         "config": {"workload": rec["workload"], "layout": args.layout, "coder": args.coder},
         **{k: v for k, v in rec.items() if k not in ("workload", "layout", "coder")},
@@ -546,7 +598,8 @@ def main():
     ms_per_step = total_ms / args.steps
     value = out_bytes * n / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (kernel_avg_ms * 1e-3) / 1e9
-    copy_gbps = copy_rate(torch, alg_bytes)
+    progress(f"{args.workload}: timing the streaming reference")
+    sref = stream_reference(torch, wc, alg_bytes - out_bytes * n, out_bytes * n, args.steps, stream)
 
     extras = (args.extras == "on" and args.workload == "block_8b" and args.layout == "lanes"
               and args.coder == "huffman" and not args.max_code_len)
@@ -625,12 +678,16 @@ def main():
             "algorithmic_bytes_per_launch": alg_bytes,
             "kernel_avg_ms": round(kernel_avg_ms, 5),
             "launch_us": tm["launch_us"],
-            "copy_GBps": round(copy_gbps, 1),
-            "frac_of_copy": round(achieved / copy_gbps, 4),
+            "stream_ref": sref,
+            "frac_of_stream_ref": round(achieved / sref["GBps"], 4) if sref else None,
         },
         "cpu_baseline": cpu,
     }
     if layouts is not None:
+        if sref:
+            for rec in layouts.values():
+                rec["frac_of_stream_ref"] = round(rec["algorithmic_bytes_per_launch"] / (rec["ms"] * 1e-3) / 1e9
+                                                  / sref["GBps"], 4)
         line["layouts"] = layouts
     if e2e is not None:
         line["e2e"] = e2e

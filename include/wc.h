@@ -289,6 +289,25 @@ int wc_decode_u8_async(const wc_plan_t* plan, const void* blob_dev, uint8_t* out
 int wc_gemv_bf16_async(const uint16_t* W, uint32_t rows, uint32_t cols, const uint16_t* x, float* y,
                        void* stream);
 
+/* ---- measurement ----------------------------------------------------------- */
+/*
+ * wc_stream_reference_async -- the streaming yardstick for the decode kernels'
+ * bandwidth (not a step of the method): reads src_bytes from src once and
+ * writes dst_bytes to dst, as a decode of a container of src_bytes into
+ * dst_bytes of weights does, with the simplest kernel that does so (one
+ * workgroup per 4 KiB of output in index order, one non-temporal 16-byte load
+ * and store per lane).  With ns = src_bytes / 16 and nd = dst_bytes / 16,
+ * 16-byte output item j is the bitwise NOT of input item
+ * min(floor(j * r / 2^32), ns - 1), r = ceil(ns * 2^32 / nd); every input item
+ * is read.  One launch on `stream`.
+ *   src, dst   device pointers, 16-byte aligned; the caller owns both;
+ *   src_bytes  a positive multiple of 16, at most dst_bytes;
+ *   dst_bytes  a multiple of 16, below 2^43.
+ * Both sizes 0 is a no-op.  Returns WC_ERR_INVALID_ARG for bad sizes or
+ * alignment, WC_ERR_HIP if the launch fails.
+ */
+int wc_stream_reference_async(const void* src, uint64_t src_bytes, void* dst, uint64_t dst_bytes, void* stream);
+
 /*
  * Fused decode -> matrix-vector products: y_k = W_k x_k for consecutive
  * tensors W_k of the container, each seen as a row-major matrix, without

@@ -84,6 +84,9 @@ _lib.wc_decode_gemv_async.restype = ctypes.c_int
 _lib.wc_decode_gemv_noalloc_async.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(GemvOperand),
                                               ctypes.c_uint32, ctypes.c_void_p]
 _lib.wc_decode_gemv_noalloc_async.restype = ctypes.c_int
+_lib.wc_stream_reference_async.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
+                                           ctypes.c_void_p]
+_lib.wc_stream_reference_async.restype = ctypes.c_int
 _lib.wc_plan_destroy.argtypes = [ctypes.c_void_p]
 _lib.wc_plan_destroy.restype = None
 _lib.wc_status_str.argtypes = [ctypes.c_int]
@@ -128,7 +131,7 @@ CODERS = {"huffman": 0, "rans": 1}
 EXPORTED = ("wc_encode_host", "wc_encode_u8_host", "wc_free_host", "wc_plan", "wc_plan_info", "wc_plan_stats",
             "wc_plan_format", "wc_decode_u8_async",
             "wc_decode_async", "wc_gemv_bf16_async", "wc_decode_gemv_work_bytes", "wc_decode_gemv_async",
-            "wc_decode_gemv_noalloc_async",
+            "wc_decode_gemv_noalloc_async", "wc_stream_reference_async",
             "wc_plan_destroy", "wc_status_str")
 
 
@@ -341,6 +344,19 @@ def gemv_bf16_async(W_dev, rows: int, cols: int, x_dev, y_dev, stream=None) -> N
     _check(_lib.wc_gemv_bf16_async(ctypes.c_void_p(_ptr(W_dev)), int(rows), int(cols), ctypes.c_void_p(_ptr(x_dev)),
                                    ctypes.c_void_p(_ptr(y_dev)), ctypes.c_void_p(_stream_handle(stream))),
            "wc_gemv_bf16_async")
+
+
+def stream_reference_async(src_dev, src_bytes: int, dst_dev, dst_bytes: int, stream=None) -> None:
+    """wc_stream_reference_async: the streaming yardstick (reads src_bytes once,
+    writes dst_bytes; 16-byte output item j = NOT input item
+    min(floor(j r / 2^32), ns - 1), r = ceil(ns 2^32 / nd)), one launch."""
+    if src_bytes or dst_bytes:
+        dev = _current_device()
+        _require(src_dev, int(src_bytes), dev, "src", "wc_stream_reference_async")
+        _require(dst_dev, int(dst_bytes), dev, "dst", "wc_stream_reference_async")
+    _check(_lib.wc_stream_reference_async(ctypes.c_void_p(_ptr(src_dev)), int(src_bytes), ctypes.c_void_p(_ptr(dst_dev)),
+                                          int(dst_bytes), ctypes.c_void_p(_stream_handle(stream))),
+           "wc_stream_reference_async")
 
 
 def _current_device():

@@ -224,6 +224,19 @@ def test_plan_rejects_random_corruption_without_crashing(wc):
         assert st <= 0
 
 
+def test_stream_reference_argument_checks_without_device(wc):
+    """Size and alignment checks of wc_stream_reference_async return before any HIP call."""
+    import ctypes
+    fake, vp = 1 << 20, ctypes.c_void_p
+    call = wc._lib.wc_stream_reference_async
+    assert call(vp(fake), 0, vp(fake), 0, vp(0)) == wc.WC_OK                          # no-op
+    for sb, db in ((32, 16), (16, 24), (8, 16), (0, 16), (16, 1 << 43)):
+        assert call(vp(fake), sb, vp(fake), db, vp(0)) == wc.WC_ERR_INVALID_ARG
+    assert call(vp(fake + 8), 16, vp(fake), 16, vp(0)) == wc.WC_ERR_INVALID_ARG
+    assert call(vp(fake), 16, vp(fake + 4), 16, vp(0)) == wc.WC_ERR_INVALID_ARG
+    assert call(vp(0), 16, vp(fake), 16, vp(0)) == wc.WC_ERR_INVALID_ARG
+
+
 def test_gemv_argument_checks_without_device(wc):
     """Size and alignment checks of wc_gemv_bf16_async return before any HIP call."""
     import ctypes
