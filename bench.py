@@ -35,7 +35,10 @@ Evidence rules: every launch of a run takes the next (container, output) copy
 in one rotation whose copies together exceed 1 GiB (four times the 256 MiB
 Infinity Cache), so a copy's previous use is at least that much traffic back;
 every output the timed launches write is first filled with a canary (or NaN)
-and compared with the expected bits after the timed region.
+and compared with the expected bits after the timed region.  Untimed launches
+(settle, warm-up) read the same containers but write separate burn outputs,
+and run both before the canary fill and for at least 10 ms after it, so the
+timed launches start from the decode's own steady state.
 """
 from __future__ import annotations
 
@@ -303,10 +306,13 @@ def time_decode(torch, wc, plan, blob, raw, out_bytes, codes, args, stream):
     copies = rotation_copies(blob.size + out_bytes * n)
     rot = Rotation(torch, blob, n, out_dtype, copies)
     ref = torch.from_numpy(np.ascontiguousarray(raw)).cuda()
+    # untimed launches (settle, warm-up) read the rotation's containers but
+    # write this output, so that only timed launches write the canaried copies
+    burn_out = torch.empty(n, dtype=out_dtype, device="cuda")
 
-    def launch():
+    def launch(burn=False):
         k = rot.next()
-        decode(plan, rot.blobs[k], rot.outs[k], stream)
+        decode(plan, rot.blobs[k], burn_out if burn else rot.outs[k], stream)
         return k
 
     k = launch()
@@ -315,27 +321,21 @@ def time_decode(torch, wc, plan, blob, raw, out_bytes, codes, args, stream):
         print("bench.py: decode is NOT bit-exact", file=sys.stderr)
         sys.exit(3)
     # settle: untimed launches until the GPU has run the decode for settle_ms
-    settle_launches, settled_ms = 0, 0.0
-    while settled_ms < args.settle_ms and settle_launches < 5000:
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(25):
-            launch()
-        b.record(stream)
-        b.synchronize()
-        settled_ms += a.elapsed_time(b)
-        settle_launches += 25
-    for _ in range(args.warmup):
-        launch()
-    # canary in every output copy, then the timed launches: HIP events on the
-    # launch stream around K back-to-back launches (a step is one launch)
+    settle_launches = settle(torch, stream, lambda _: launch(True), args.settle_ms)
+    # canary in every output copy, the cache scrubbed, then the warm-up: W
+    # launches and at least 10 ms more of them (the canary fills and the scrub
+    # leave the memory system in another state than the decode's own), then
+    # the timed launches: HIP events on the launch stream around K
+    # back-to-back launches (a step is one launch)
     canary = CANARY8 if codes else CANARY16
     with torch.cuda.stream(stream):
         for o in rot.outs:
             o.fill_(canary)
     scrub = Scrub(torch)
     scrub(torch, stream)
+    for _ in range(args.warmup):
+        launch(True)
+    settle_launches += args.warmup + settle(torch, stream, lambda _: launch(True), 10.0)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -365,7 +365,7 @@ def time_decode(torch, wc, plan, blob, raw, out_bytes, codes, args, stream):
     def pct(q):
         return round(singles[min(len(singles) - 1, int(q * len(singles)))], 1)
 
-    del rot, ref, scrub
+    del rot, ref, scrub, burn_out
     torch.cuda.empty_cache()
     return {"total_ms": total_ms, "kernel_avg_ms": total_ms / args.steps, "copies": copies,
             "rotated_bytes": copies * (blob.size + out_bytes * n), "settle_launches": settle_launches,
@@ -403,6 +403,11 @@ def e2e_measure(torch, wc, name, layout, coder, steps, warmup, opts, stream):
     yb = [torch.empty(r, dtype=torch.float32, device="cuda") for _, r, _ in mats]
     yc = [torch.empty(r, dtype=torch.float32, device="cuda") for _, r, _ in mats]
     ops = [(k, c, xs[c], yc[j]) for j, (k, r, c) in enumerate(mats)]
+    # untimed launches write these instead, so that only timed launches
+    # write the canaried (or NaN-filled) outputs
+    burn_out = torch.empty(n, dtype=torch.int16, device="cuda")
+    y_burn = [torch.empty(r, dtype=torch.float32, device="cuda") for _, r, _ in mats]
+    ops_burn = [(k, c, xs[c], y_burn[j]) for j, (k, r, c) in enumerate(mats)]
     work_bytes = wc.decode_gemv_work_bytes(plan, ops)
     work_own = torch.empty(work_bytes // 4 + 64, dtype=torch.float32, device="cuda")
     work = work_own[(-work_own.data_ptr()) % 256 // 4:]
@@ -414,22 +419,25 @@ def e2e_measure(torch, wc, name, layout, coder, steps, warmup, opts, stream):
 
     touched = set()
 
-    def arm_a(_):
+    def arm_a(_, burn=False):
         k = rot.next()
-        touched.add(k)
-        wc.decode_async(plan, rot.blobs[k], rot.outs[k], stream)
-        gemvs(rot.outs[k], ya)
+        out = burn_out if burn else rot.outs[k]
+        if not burn:
+            touched.add(k)
+        wc.decode_async(plan, rot.blobs[k], out, stream)
+        gemvs(out, y_burn if burn else ya)
 
-    def arm_b(i):
-        gemvs(origs[i % copies], yb)
+    def arm_b(i, burn=False):
+        gemvs(origs[i % copies], y_burn if burn else yb)
 
-    def decode_only(_):
+    def decode_only(_, burn=False):
         k = rot.next()
-        touched.add(k)
-        wc.decode_async(plan, rot.blobs[k], rot.outs[k], stream)
+        if not burn:
+            touched.add(k)
+        wc.decode_async(plan, rot.blobs[k], burn_out if burn else rot.outs[k], stream)
 
-    def arm_c(_):
-        wc.decode_gemv_async(plan, rot.blobs[rot.next()], ops, work, work_bytes, stream)
+    def arm_c(_, burn=False):
+        wc.decode_gemv_async(plan, rot.blobs[rot.next()], ops_burn if burn else ops, work, work_bytes, stream)
 
     def fill(tensors, value):
         with torch.cuda.stream(stream):
@@ -442,17 +450,19 @@ def e2e_measure(torch, wc, name, layout, coder, steps, warmup, opts, stream):
         return ok
 
     # each arm: settled for at least 60 ms of its own launches (the GPU's
-    # clocks follow the load), then its outputs filled with canaries, the
-    # cache scrubbed, and `steps` launches timed
+    # clocks follow the load), its outputs filled with canaries, the cache
+    # scrubbed, 10 ms more of its launches, and `steps` launches timed; the
+    # untimed launches write the burn outputs
     scrub = Scrub(torch)
     warm = {}
 
     def timed_arm(name, fn, fills):
-        warm[name] = settle(torch, stream, fn, 60.0)
+        warm[name] = settle(torch, stream, lambda i: fn(i, True), 60.0)
         for tensors, value in fills:
             fill(tensors, value)
-        touched.clear()
         scrub(torch, stream)
+        warm[name] += settle(torch, stream, lambda i: fn(i, True), 10.0)
+        touched.clear()
         return _timed(torch, stream, fn, steps)
 
     ms_a = timed_arm("a", arm_a, [(rot.outs, CANARY16), (ya, float("nan"))])
@@ -496,7 +506,7 @@ def e2e_measure(torch, wc, name, layout, coder, steps, warmup, opts, stream):
         "host_prep_s": round(t_gen, 2),
     }
     plan.close()
-    del rot, origs, work_own, scrub
+    del rot, origs, work_own, scrub, burn_out
     torch.cuda.empty_cache()
     return rec, ok
 
