@@ -41,6 +41,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <type_traits>
 
 #include "decode_common.h"
 #include "format.h"
@@ -125,6 +126,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
     __shared__ __attribute__((aligned(16))) uint4 s_tab[kTabVec];
     const uint2* const s_dec = reinterpret_cast<const uint2*>(s_tab);
     const uint32_t* const s_long = reinterpret_cast<const uint32_t*>(s_tab + kDecVec);
+    const uint16_t* const s_c16 = reinterpret_cast<const uint16_t*>(s_tab);   // code planes, one code per entry
     // dynamic: per wave, kLaneStageBytes of stream words then one
     // kLaneSlotBytes exponent slot per lane; then the second-level table
     // (l2_cap * 2^kL2Bits u16)
@@ -159,9 +161,35 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
     Meta cur_m = uniform_meta(m_first);
     LaneRaw cur_r = load_lane_raw(p, cur_m, min_u64(u, last_u), lane);
     Meta m_next = load_meta(p, min_u64(u + stride, last_u));
+    // code planes (Huffman): the multi-codeword table is staged with its
+    // symbols un-rotated, so that the merge stores the slot bytes as they
+    // are; with one code per entry, as 16-bit entries (symbol | length << 8,
+    // 0 for a code longer than the index) packed into the first 2^KD / 2
+    // words of the table's place, a quarter of the LDS bytes per lookup
+    if constexpr (kU8 && !kRans) {
+        const bool compact = p.one_code != 0;
+        auto put = [&](uint32_t i, u32x4 v) {
+            if (i < kDecVec) {
+                if (compact) {
+                    auto c16 = [](uint32_t x, uint32_t y) {
+                        return x == 0 ? 0u : (unrotate4(y) & 0xFFu) | (((x >> 16) & 0xFFu) << 8);
+                    };
+                    reinterpret_cast<uint32_t*>(s_tab)[i] = c16(v.x, v.y) | c16(v.z, v.w) << 16;
+                    return;
+                }
+                v.y = unrotate4(v.y);
+                v.w = unrotate4(v.w);
+            }
+            tdst[i] = v;
+        };
 #pragma unroll
-    for (uint32_t k = 0; k < kFull; ++k) tdst[tid + k * kThreads] = stage[k];
-    if (kTail && tid < kTail) tdst[kFull * kThreads + tid] = stage_tail;
+        for (uint32_t k = 0; k < kFull; ++k) put(tid + k * kThreads, stage[k]);
+        if (kTail && tid < kTail) put(kFull * kThreads + tid, stage_tail);
+    } else {
+#pragma unroll
+        for (uint32_t k = 0; k < kFull; ++k) tdst[tid + k * kThreads] = stage[k];
+        if (kTail && tid < kTail) tdst[kFull * kThreads + tid] = stage_tail;
+    }
     {
         const uint4* src = reinterpret_cast<const uint4*>(p.tables) + kTabVec;
         for (uint32_t i = tid; i < (p.l2_cap << kL2Bits) / 8; i += kThreads)
@@ -306,75 +334,95 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
                     }
                 }
             } else {
-                // fused product and code planes (bound by the decode's
-                // instructions and LDS): no register window; each lookup
+                // code planes (bound by the decode's instructions and LDS):
+                // no register window; each lookup
                 // re-reads its 32-bit window from the staged
                 // words: t = (bit position) - 1, words t >> 5 (arithmetic:
                 // -1 at position 0, the last word of the wave's pad, shifted
                 // out) and the next, shifted right by -position mod 32
                 // (always below 32).
                 // A lookup's symbols past the lane's last one (they belong
-                // to the next lane) land in the slot's spare bytes: p < nsym
+                // to the next lane) land in the slot's spare bytes: c < nsym
                 // <= 64 before the store, so it ends by byte 67.  The words
                 // stay in the wave's LDS region unclamped: the planner bounds
                 // every lane offset by the segment's bits (<= 15872), and a
                 // lane makes at most 64 lookups of at most 24 bits (at most
                 // word 548, byte 2195 of the wave's staging and slots).
+                // The long-code lookup is compiled in only for codebooks with
+                // codes longer than the table index.
                 int32_t t = (int32_t)pos - 1;
-                if (one_code) {
-                    // code planes whose shortest code is longer than half the
-                    // table index and whose codes are at most 16 bits: every
-                    // lookup yields exactly one code (the entry's other
-                    // symbol bytes are 0), and four of them fit one 64-bit
-                    // window, read from three staged words.  Four lookups
-                    // fill one aligned word.  A lane whose count is not a
-                    // multiple of four decodes up to three more, into the
-                    // slot's unused bytes; it still makes at most 64 lookups
-                    // of at most 16 bits (at most word 530 of the wave's
-                    // staging and slots) and stores below byte 64.
-                    for (uint32_t q = 0; q < nsym; q += 4) {
-                        const int32_t k = t >> 5;
-                        const uint32_t w1 = sbuf[k + 1];
-                        uint64_t win = (uint64_t)__builtin_amdgcn_alignbit(sbuf[k], w1, ~(uint32_t)t) << 32 |
-                                       __builtin_amdgcn_alignbit(w1, sbuf[k + 2], ~(uint32_t)t);
-                        uint32_t w = 0, used = 0;
+                auto run = [&](auto has_long) {
+                    constexpr bool kLong = decltype(has_long)::value;
+                    if (one_code) {
+                        // the shortest code is longer than half the table
+                        // index and no code exceeds 16 bits: every lookup
+                        // yields exactly one code, and four of them fit one
+                        // 64-bit window, read from three staged words.  Four
+                        // lookups fill one aligned word.  A lane whose count
+                        // is not a multiple of four decodes up to three more,
+                        // into the slot's unused bytes; it still makes at
+                        // most 64 lookups of at most 16 bits (at most word
+                        // 530 of the wave's staging and slots) and stores
+                        // below byte 64.
+                        for (uint32_t q = 0; q < nsym; q += 4) {
+                            const int32_t k = t >> 5;
+                            const uint32_t w1 = sbuf[k + 1];
+                            uint64_t win = (uint64_t)__builtin_amdgcn_alignbit(sbuf[k], w1, ~(uint32_t)t) << 32 |
+                                           __builtin_amdgcn_alignbit(w1, sbuf[k + 2], ~(uint32_t)t);
+                            uint32_t w = 0, used = 0;
 #pragma unroll
-                        for (uint32_t i = 0; i < 4; ++i) {
-                            const uint32_t top = (uint32_t)(win >> 32);
+                            for (uint32_t i = 0; i < 4; ++i) {
+                                const uint32_t top = (uint32_t)(win >> 32);
+                                uint32_t e = s_c16[top >> (32 - KD)];
+                                if constexpr (kLong) {
+                                    if (e == 0) {
+                                        const uint2 l = long_decode_entry<KD>(top, KD + 1, lt);
+                                        e = (unrotate4(l.y) & 0xFFu) | (((l.x >> 16) & 0xFFu) << 8);
+                                    }
+                                }
+                                w |= (e & 0xFFu) << (8 * i);
+                                const uint32_t len = e >> 8;
+                                win <<= len;
+                                used += len;
+                            }
+                            t += (int32_t)used;
+                            *reinterpret_cast<uint32_t*>(slot + q) = w;
+                        }
+                    } else {
+                        // up to four symbols per lookup, stored as aligned
+                        // words, one store per lookup: `acc` holds the bytes
+                        // [c & ~3, c) decoded so far (its other bytes 0; the
+                        // table's bytes past a lookup's symbols are 0); a
+                        // lookup's symbols, shifted to c & 3, join it, the
+                        // word at c & ~3 is stored and the part past that
+                        // word carries over.  The last word ends by byte 67.
+                        uint32_t c = 0, acc = 0;
+                        while (c < nsym) {
+                            const int32_t k = t >> 5;
+                            const uint32_t top = __builtin_amdgcn_alignbit(sbuf[k], sbuf[k + 1], ~(uint32_t)t);
                             uint2 e = s_dec[top >> (32 - KD)];
-                            if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
-                            w |= e.y << (8 * i);
-                            const uint32_t len = (e.x >> 16) & 0xFFu;
-                            win <<= len;
-                            used += len;
+                            if constexpr (kLong) {
+                                if (e.x == 0) {
+                                    e = long_decode_entry<KD>(top, KD + 1, lt);
+                                    e.y = unrotate4(e.y);
+                                }
+                            }
+                            const uint32_t q = c & 3u;
+                            const uint32_t ns = (e.x >> 8) & 0xFFu;
+                            const uint64_t w = (uint64_t)e.y << (q << 3);
+                            const uint32_t lo = (uint32_t)w | acc;
+                            *reinterpret_cast<uint32_t*>(slot + (c - q)) = lo;
+                            acc = q + ns >= 4u ? (uint32_t)(w >> 32) : lo;
+                            c += ns;
+                            t += (int32_t)((e.x >> 16) & 0xFFu);
                         }
-                        t += (int32_t)used;
-                        *reinterpret_cast<uint32_t*>(slot + q) = w;
+                        if (c & 3u) *reinterpret_cast<uint32_t*>(slot + (c & ~3u)) = acc;
                     }
-                } else {
-                    // code planes (about one symbol per lookup): the symbols
-                    // are gathered in a register and written as aligned words
-                    // (the table's bytes past a lookup's symbols are 0); the
-                    // last word ends by byte 67.
-                    uint32_t p = 0, acc = 0;
-                    while (p < nsym) {
-                        const int32_t k = t >> 5;
-                        const uint32_t top = __builtin_amdgcn_alignbit(sbuf[k], sbuf[k + 1], ~(uint32_t)t);
-                        uint2 e = s_dec[top >> (32 - KD)];
-                        if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
-                        const uint32_t pn = p + ((e.x >> 8) & 0xFFu);
-                        const uint64_t comb = ((uint64_t)e.y << ((p & 3u) << 3)) | acc;
-                        if ((p ^ pn) >= 4u) {   // a word is complete
-                            *reinterpret_cast<uint32_t*>(slot + (p & ~3u)) = (uint32_t)comb;
-                            acc = (uint32_t)(comb >> 32);
-                        } else {
-                            acc = (uint32_t)comb;
-                        }
-                        p = pn;
-                        t += (int32_t)((e.x >> 16) & 0xFFu);
-                    }
-                    if (p & 3u) *reinterpret_cast<uint32_t*>(slot + (p & ~3u)) = acc;
-                }
+                };
+                if (p.no_long)
+                    run(std::false_type{});
+                else
+                    run(std::true_type{});
             }
         }
 
@@ -396,8 +444,8 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
                 if (blk < full) {
                     const uint2 e2 = load_slot8(slot + kMergeElems * k);
                     u32x2 v;
-                    v.x = unrotate4(e2.x);
-                    v.y = unrotate4(e2.y);
+                    v.x = kRans ? unrotate4(e2.x) : e2.x;
+                    v.y = kRans ? unrotate4(e2.y) : e2.y;
                     __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(outb + kMergeElems * blk));
                 }
             }
@@ -425,7 +473,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
         if (kU8 && full * kMergeElems < n && lane == 0) {
             const uint32_t rel = kMergeElems * full;
             const uint2 e2 = load_slot8(ebuf + kLaneSlotBytes * (full % kWaveLanes) + kMergeElems * (full / kWaveLanes));
-            const uint32_t o[2] = {unrotate4(e2.x), unrotate4(e2.y)};
+            const uint32_t o[2] = {kRans ? unrotate4(e2.x) : e2.x, kRans ? unrotate4(e2.y) : e2.y};
 #pragma unroll
             for (uint32_t i = 0; i < kMergeElems; ++i)
                 if (rel + i < n) p.out8[A + rel + i] = (uint8_t)(o[i >> 2] >> (8 * (i & 3)));

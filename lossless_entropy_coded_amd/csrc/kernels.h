@@ -109,6 +109,7 @@ struct DecodeParams {
     uint32_t l2_cap;         // long-code prefixes staged in LDS (0 .. kL2Prefixes)
     uint32_t gap_packed;     // chunks layout: gaps stored in 5 bits (else one byte each)
     uint32_t one_code;       // lanes layout, Huffman: one code per table entry at most, all <= 16 bits
+    uint32_t no_long;        // Huffman: no code is longer than the multi-codeword table's index
     DotParams dot;           // fused matrix-vector launches only
 };
 

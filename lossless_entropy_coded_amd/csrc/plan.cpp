@@ -51,6 +51,7 @@ struct wc_plan_s {
     bool lanes = false;          // container version 3 (interleaved lanes)
     bool rans = false;           // coder rANS (version 3)
     bool one_code = false;       // Huffman: one code per table entry at most, none longer than 16 bits
+    bool no_long = false;        // Huffman: no code longer than decode_bits
     uint32_t* d_tables = nullptr;
 };
 
@@ -319,6 +320,7 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
             longest = std::max(longest, L);
         }
         p->one_code = shortest && 2 * shortest > p->decode_bits && longest <= 16;
+        p->no_long = longest <= p->decode_bits;
     }
     {
         const uint32_t forced_waves = env_u32("WC_WAVES", 0);
@@ -485,6 +487,7 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
     d.l2_cap = p->l2_cap;
     d.gap_packed = p->h.gap_bits == wc::kGapBitsPacked ? 1u : 0u;
     d.one_code = p->one_code ? 1u : 0u;
+    d.no_long = p->no_long ? 1u : 0u;
     hipError_t e;
     if (p->lanes) {
         // the lane offsets sit where the gaps do; the kernel stages the tables
@@ -524,6 +527,7 @@ extern "C" int wc_decode_u8_async(const wc_plan_t* p, const void* blob_dev, uint
     d.l2_cap = p->l2_cap;
     d.gap_packed = p->h.gap_bits == wc::kGapBitsPacked ? 1u : 0u;
     d.one_code = p->one_code ? 1u : 0u;
+    d.no_long = p->no_long ? 1u : 0u;
     const hipError_t e = wc::launch_decode_lanes(d, p->decode_bits, p->busy.waves, p->busy.grid, wc::kLanesToU8, p->rans,
                                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
@@ -622,6 +626,7 @@ extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, co
     d.l2_cap = p->l2_cap;
     d.gap_packed = p->h.gap_bits == wc::kGapBitsPacked ? 1u : 0u;
     d.one_code = p->one_code ? 1u : 0u;
+    d.no_long = p->no_long ? 1u : 0u;
     d.dot.part = static_cast<float*>(work_dev);
     d.dot.row_group = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(work_dev) + rows_off);
     // Huffman lanes containers have a fused kernel of their own (its own
