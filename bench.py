@@ -508,6 +508,11 @@ def e2e_measure(torch, wc, name, layout, coder, steps, warmup, opts, stream):
     plan.close()
     del rot, origs, work_own, scrub, burn_out
     torch.cuda.empty_cache()
+    # the streaming yardstick over the whole-block decode's traffic
+    sref = stream_reference(torch, wc, int(blob.size), 2 * n, steps, stream)
+    if sref:
+        rec["decode_stream_ref"] = sref
+        rec["decode_frac_of_stream_ref"] = round((blob.size + 2 * n) / (ms_dec * 1e-3) / 1e9 / sref["GBps"], 4)
     return rec, ok
 
 
@@ -666,7 +671,9 @@ def main():
             "container_bytes": int(blob.size),
             "compression_ratio": round(out_bytes * n / blob.size, 4),
             "mean_code_bits": round(stream_bits / n, 4),
-            "launches_per_step": 1,
+            # wc_decode_async: one launch per at most 40 rounds of the
+            # persistent grid (4 waves per workgroup); code planes: one launch
+            "launches_per_step": 1 if codes else max(1, -(-(-(-st["n_groups"] // (4 * st["grid"]))) // 40)),
             "count_bits": st["count_bits"],
             "decode_bits": st["decode_bits"],
             "grid": st["grid"],

@@ -246,11 +246,15 @@ int wc_plan_stats(const wc_plan_t* plan, uint64_t* container_bytes, uint64_t* st
 int wc_plan_format(const wc_plan_t* plan, uint32_t* version, uint32_t* elem_kind, uint32_t* coder);
 
 /*
- * wc_decode_async -- decode every tensor of the container in ONE kernel launch
- * on `stream` (a hipStream_t; NULL = the device's null stream): DFloat11
- * page, abstract, design point (iii), decompresses a whole transformer block
- * at once to cut latency; the output is bit-for-bit the original bf16 words
- * (the same abstract; the Llama2-7B page's abstract: lossless).
+ * wc_decode_async -- decode every tensor of the container with one kernel
+ * launch on `stream` (a hipStream_t; NULL = the device's null stream):
+ * DFloat11 page, abstract, design point (iii), decompresses a whole
+ * transformer block at once to cut latency; the output is bit-for-bit the
+ * original bf16 words (the same abstract; the Llama2-7B page's abstract:
+ * lossless).  A container of more than 40 rounds of the persistent grid's
+ * segments (on MI355X about 5 x 10^8 elements; an 8B-shape block is 17
+ * rounds) is decoded by consecutive launches of at most 40 rounds each on
+ * the same stream (a 70B-shape block: two).
  *   blob_dev  device pointer to the same bytes given to wc_plan, 256-byte aligned;
  *   out_dev   device pointer to n_elems bf16 words (caller-owned), 16-byte
  *             aligned; tensor k is out_dev[tensor_offsets[k] ...].

@@ -310,3 +310,18 @@ def test_argument_checks(wc):
         assert plan.n_elems == 0
         wc.decode_async(plan, 0, 0)       # n = 0 is a no-op
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("rounds", [1, 2])
+@pytest.mark.parametrize("layout,coder", [("lanes", "huffman"), ("lanes", "rans"), ("chunks", "huffman")])
+def test_decode_in_several_launches(wc, env_knob, rounds, layout, coder):
+    """A decode split into consecutive launches of `rounds` rounds of the
+    persistent grid each (WC_LAUNCH_ROUNDS, read by wc_plan; large
+    containers are split this way by default) is bit-exact: every launch
+    starts at its own first segment."""
+    from lossless_entropy_coded_amd.synth import make_workload
+    wl = make_workload("heavy_tail_14k")              # 58.7 M elements: about 4.7 rounds
+    blob = wc.encode_host(wl.tensors(), layout=layout, coder=coder)
+    env_knob("WC_LAUNCH_ROUNDS", rounds)
+    log(f"case: {layout} {coder} decode in launches of {rounds} rounds, n={wl.n}")
+    assert np.array_equal(gpu_decode(wc, blob), wl.bits)
