@@ -113,7 +113,7 @@ __device__ __forceinline__ uint32_t unrotate4(uint32_t x) {
 // sign+mantissa plane).  kRans: rANS lanes (KD = 11: the slot table fills
 // the multi-codeword table's 16 KiB).
 template <int KD, int W, uint32_t kMode, bool kRans>
-__global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void decode_lanes_kernel(DecodeParams p) {
     static_assert(!kRans || (2u << KD) == kRansSlots, "the rANS slot table takes the multi-codeword table's place");
     static_assert(kMode != kLanesToDot || kRans, "the fused product of Huffman lanes is decode_lanes_dot_kernel");
     constexpr bool kDot = kMode == kLanesToDot;
@@ -128,16 +128,19 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
     const uint32_t* const s_long = reinterpret_cast<const uint32_t*>(s_tab + kDecVec);
     const uint16_t* const s_c16 = reinterpret_cast<const uint16_t*>(s_tab);   // code planes, one code per entry
     // dynamic: per wave, kLaneStageBytes of stream words then one
-    // kLaneSlotBytes exponent slot per lane; then the second-level table
-    // (l2_cap * 2^kL2Bits u16)
+    // kLaneSlotBytes exponent slot per lane (code planes with one code per
+    // table entry: no slots, kLaneCompactWaveBytes per wave); then the
+    // second-level table (l2_cap * 2^kL2Bits u16)
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
-    uint16_t* const s_l2 = reinterpret_cast<uint16_t*>(dyn + W * kLaneWaveBytes);
+    const bool one_code = kU8 && !kRans && p.one_code != 0;
+    const uint32_t wave_bytes = one_code ? kLaneCompactWaveBytes : kLaneWaveBytes;
+    uint16_t* const s_l2 = reinterpret_cast<uint16_t*>(dyn + W * wave_bytes);
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & 63u;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    uint32_t* const sbuf = reinterpret_cast<uint32_t*>(dyn + wave * kLaneWaveBytes + kLanePadBytes);
-    uint8_t* const ebuf = dyn + wave * kLaneWaveBytes + kLanePadBytes + kLaneStageBytes;
+    uint32_t* const sbuf = reinterpret_cast<uint32_t*>(dyn + wave * wave_bytes + kLanePadBytes);
+    uint8_t* const ebuf = dyn + wave * wave_bytes + kLanePadBytes + kLaneStageBytes;
     uint8_t* const slot = ebuf + kLaneSlotBytes * lane;   // this lane's exponents, in its symbol order
 
     // wave w of workgroup b takes segments b*W + w, then every (grid * W)-th
@@ -210,8 +213,6 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
     // rANS with one symbol: its frequency 2^12 is stored as 0
     const bool rans_single =
         kRans && ((__builtin_amdgcn_readfirstlane(reinterpret_cast<const uint32_t*>(s_tab)[0]) >> 8) & 0xFFFu) == 0;
-    // code planes: each multi-codeword table entry holds one code at most
-    const bool one_code = kU8 && !kRans && p.one_code != 0;
 
     for (;;) {
         const uint64_t un = u + stride;
@@ -357,36 +358,58 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
                         // the shortest code is longer than half the table
                         // index and no code exceeds 16 bits: every lookup
                         // yields exactly one code, and four of them fit one
-                        // 64-bit window, read from three staged words.  Four
-                        // lookups fill one aligned word.  A lane whose count
-                        // is not a multiple of four decodes up to three more,
-                        // into the slot's unused bytes; it still makes at
-                        // most 64 lookups of at most 16 bits (at most word
-                        // 530 of the wave's staging and slots) and stores
-                        // below byte 64.
-                        for (uint32_t q = 0; q < nsym; q += 4) {
-                            const int32_t k = t >> 5;
-                            const uint32_t w1 = sbuf[k + 1];
-                            uint64_t win = (uint64_t)__builtin_amdgcn_alignbit(sbuf[k], w1, ~(uint32_t)t) << 32 |
-                                           __builtin_amdgcn_alignbit(w1, sbuf[k + 2], ~(uint32_t)t);
-                            uint32_t w = 0, used = 0;
+                        // 64-bit window, read from three staged words.
+                        // Eight lookups make one lane block, stored straight
+                        // to memory (block 64k + lane is the lane's k-th: a
+                        // wave's store covers 512 contiguous bytes); the
+                        // container's last, partial block byte by byte.  A
+                        // lane whose count is not a multiple of eight
+                        // decodes up to seven more symbols, never stored; it
+                        // still makes at most 64 lookups of at most 16 bits,
+                        // so it reads at most word 533 past the pad (byte
+                        // 2136 of the wave's region of 2192).
+                        uint8_t* const outb = p.out8 + A;
+                        const uint32_t full = n / kMergeElems;
+                        for (uint32_t q = 0; q < nsym; q += 8) {
+                            uint32_t w[2];
 #pragma unroll
-                            for (uint32_t i = 0; i < 4; ++i) {
-                                const uint32_t top = (uint32_t)(win >> 32);
-                                uint32_t e = s_c16[top >> (32 - KD)];
-                                if constexpr (kLong) {
-                                    if (e == 0) {
-                                        const uint2 l = long_decode_entry<KD>(top, KD + 1, lt);
-                                        e = (unrotate4(l.y) & 0xFFu) | (((l.x >> 16) & 0xFFu) << 8);
+                            for (uint32_t h = 0; h < 2; ++h) {
+                                const int32_t k = t >> 5;
+                                const uint32_t w1 = sbuf[k + 1];
+                                uint64_t win =
+                                    (uint64_t)__builtin_amdgcn_alignbit(sbuf[k], w1, ~(uint32_t)t) << 32 |
+                                    __builtin_amdgcn_alignbit(w1, sbuf[k + 2], ~(uint32_t)t);
+                                uint32_t acc = 0, used = 0;
+#pragma unroll
+                                for (uint32_t i = 0; i < 4; ++i) {
+                                    const uint32_t top = (uint32_t)(win >> 32);
+                                    uint32_t e = s_c16[top >> (32 - KD)];
+                                    if constexpr (kLong) {
+                                        if (e == 0) {
+                                            const uint2 l = long_decode_entry<KD>(top, KD + 1, lt);
+                                            e = (unrotate4(l.y) & 0xFFu) | (((l.x >> 16) & 0xFFu) << 8);
+                                        }
                                     }
+                                    acc |= (e & 0xFFu) << (8 * i);
+                                    const uint32_t len = e >> 8;
+                                    win <<= len;
+                                    used += len;
                                 }
-                                w |= (e & 0xFFu) << (8 * i);
-                                const uint32_t len = e >> 8;
-                                win <<= len;
-                                used += len;
+                                t += (int32_t)used;
+                                w[h] = acc;
                             }
-                            t += (int32_t)used;
-                            *reinterpret_cast<uint32_t*>(slot + q) = w;
+                            const uint32_t blk = lane + kWaveLanes * (q / kMergeElems);
+                            if (blk < full) {
+                                u32x2 v;
+                                v.x = w[0];
+                                v.y = w[1];
+                                __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(outb + kMergeElems * blk));
+                            } else if (blk == full) {
+#pragma unroll
+                                for (uint32_t i = 0; i < kMergeElems; ++i)
+                                    if (kMergeElems * full + i < n)
+                                        outb[kMergeElems * full + i] = (uint8_t)(w[i >> 2] >> (8 * (i & 3)));
+                            }
                         }
                     } else {
                         // up to four symbols per lookup, stored as aligned
@@ -441,7 +464,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
 #pragma unroll
             for (uint32_t k = 0; k < kMergeSteps; ++k) {
                 const uint32_t blk = lane + k * kWaveLanes;
-                if (blk < full) {
+                if (!one_code && blk < full) {   // one code per entry: stored by the decode
                     const uint2 e2 = load_slot8(slot + kMergeElems * k);
                     u32x2 v;
                     v.x = kRans ? unrotate4(e2.x) : e2.x;
@@ -470,7 +493,7 @@ __global__ __launch_bounds__(kWaveLanes * W) void decode_lanes_kernel(DecodePara
         // the container's last block, when it holds fewer than 8 elements (a
         // matrix for the fused product never ends in a partial block); block
         // `full` is the (full / 64)-th of lane full % 64
-        if (kU8 && full * kMergeElems < n && lane == 0) {
+        if (kU8 && !one_code && full * kMergeElems < n && lane == 0) {
             const uint32_t rel = kMergeElems * full;
             const uint2 e2 = load_slot8(ebuf + kLaneSlotBytes * (full % kWaveLanes) + kMergeElems * (full / kWaveLanes));
             const uint32_t o[2] = {kRans ? unrotate4(e2.x) : e2.x, kRans ? unrotate4(e2.y) : e2.y};
@@ -750,17 +773,17 @@ hipError_t dispatch_lanes(uint32_t decode_bits, uint32_t waves, bool rans, F&& f
 
 }  // namespace
 
-uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap) {
-    return waves * kLaneWaveBytes + (l2_cap << kL2Bits) * 2;
+uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap, bool compact) {
+    return waves * (compact ? kLaneCompactWaveBytes : kLaneWaveBytes) + (l2_cap << kL2Bits) * 2;
 }
 
-uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap) {
-    return ((2u << decode_bits) + kLongWords) * 4 + decode_lanes_dyn_lds_bytes(waves, l2_cap);
+uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool compact) {
+    return ((2u << decode_bits) + kLongWords) * 4 + decode_lanes_dyn_lds_bytes(waves, l2_cap, compact);
 }
 
-int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool rans) {
+int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool rans, bool compact) {
     if ((decode_bits != 11 && decode_bits != 10) || (rans && decode_bits != 11) || !supported_waves(waves)) return 0;
-    const uint32_t dyn = decode_lanes_dyn_lds_bytes(waves, l2_cap);
+    const uint32_t dyn = decode_lanes_dyn_lds_bytes(waves, l2_cap, compact);
     int n = 0;
     (void)dispatch_lanes(decode_bits, waves, rans, [&](auto v) {
         n = decltype(v)::blocks_per_cu(dyn);
@@ -797,7 +820,7 @@ hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint
     if ((decode_bits != 11 && decode_bits != 10) || (rans && (decode_bits != 11 || p.l2_cap)) ||
         !supported_waves(waves) || p.l2_cap > kL2Prefixes)
         return hipErrorInvalidValue;
-    const uint32_t dyn = decode_lanes_dyn_lds_bytes(waves, p.l2_cap);
+    const uint32_t dyn = decode_lanes_dyn_lds_bytes(waves, p.l2_cap, mode == kLanesToU8 && !rans && p.one_code);
     return dispatch_lanes(decode_bits, waves, rans,
                           [&](auto v) { return decltype(v)::launch(p, grid, dyn, mode, stream); });
 }

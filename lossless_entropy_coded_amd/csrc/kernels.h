@@ -127,6 +127,10 @@ constexpr uint32_t kLaneSlotBytes = 68;
 // read at bit position 0 takes the word before the staging (and discards it).
 constexpr uint32_t kLanePadBytes = 16;
 constexpr uint32_t kLaneWaveBytes = kLanePadBytes + kLaneStageBytes + kWaveLanes * kLaneSlotBytes;
+// Code planes with one code per table entry write their bytes straight to
+// memory and need no slots: a wave's region is the pad, the staging and 128
+// bytes a lane's last 64-bit windows may read past the staging.
+constexpr uint32_t kLaneCompactWaveBytes = kLanePadBytes + kLaneStageBytes + 128;
 constexpr uint32_t kLanesMaxSegBits = 15872;
 
 // Wavefronts per decode workgroup the kernels are built for.
@@ -164,9 +168,11 @@ hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t de
 // entry t = rotated symbol | (f mod 2^12) << 8 | (t - cum) << 20 (f = 2^12,
 // stored as 0, only when one symbol has every slot).
 enum LanesOut : uint32_t { kLanesToBf16 = 0, kLanesToDot = 1, kLanesToU8 = 2 };
-uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap);
-uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap);
-int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool rans);
+// compact: the layout of one-code code planes (kLaneCompactWaveBytes per wave).
+uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap, bool compact = false);
+uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool compact = false);
+int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool rans,
+                               bool compact = false);
 hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid,
                                LanesOut mode, bool rans, hipStream_t stream);
 

@@ -375,13 +375,15 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
     // 1.8% faster for the 70B-shape block; for the 8B-shape block's 17 rounds
     // splitting only costs).  WC_LAUNCH_ROUNDS overrides it (0: one launch).
     p->launch_rounds = env_u32("WC_LAUNCH_ROUNDS", 40);
+    // code planes with one code per table entry: no exponent slots
+    const bool compact = lanes && !p->rans && p->h.elem_kind == wc::kKindU8 && p->one_code;
     auto size_shape = [&](wc_plan_s::Shape& sh, bool fused_lanes) {
         sh.lds_bytes = fused_lanes ? wc::decode_lanes_dot_lds_bytes(p->decode_bits, sh.waves, p->l2_cap)
-                       : lanes     ? wc::decode_lanes_lds_bytes(p->decode_bits, sh.waves, p->l2_cap)
+                       : lanes     ? wc::decode_lanes_lds_bytes(p->decode_bits, sh.waves, p->l2_cap, compact)
                                    : wc::decode_lds_bytes(p->count_bits, p->decode_bits, sh.waves, p->ebuf_bytes,
                                                           p->l2_cap);
         int per_cu = fused_lanes ? wc::decode_lanes_dot_blocks_per_cu(p->decode_bits, sh.waves, p->l2_cap)
-                     : lanes     ? wc::decode_lanes_blocks_per_cu(p->decode_bits, sh.waves, p->l2_cap, p->rans)
+                     : lanes     ? wc::decode_lanes_blocks_per_cu(p->decode_bits, sh.waves, p->l2_cap, p->rans, compact)
                                  : wc::decode_blocks_per_cu(p->count_bits, p->decode_bits, sh.waves, p->ebuf_bytes,
                                                             p->l2_cap);
         // The persistent grid must be co-resident.  LDS is handed out in

@@ -92,13 +92,13 @@ hipError_t launch_decode(const DecodeParams& p, uint32_t, uint32_t, uint32_t wav
     g_stub.dot_launches += dot;
     return hipSuccess;
 }
-uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap) {
-    return waves * kLaneWaveBytes + (l2_cap << kL2Bits) * 2;
+uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap, bool compact) {
+    return waves * (compact ? kLaneCompactWaveBytes : kLaneWaveBytes) + (l2_cap << kL2Bits) * 2;
 }
-uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap) {
-    return ((2u << decode_bits) + kLongWords) * 4 + decode_lanes_dyn_lds_bytes(waves, l2_cap);
+uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool compact) {
+    return ((2u << decode_bits) + kLongWords) * 4 + decode_lanes_dyn_lds_bytes(waves, l2_cap, compact);
 }
-int decode_lanes_blocks_per_cu(uint32_t, uint32_t waves, uint32_t, bool) { return waves == 4 ? 3 : 2; }
+int decode_lanes_blocks_per_cu(uint32_t, uint32_t waves, uint32_t, bool, bool) { return waves == 4 ? 3 : 2; }
 hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t, uint32_t waves, uint32_t grid, LanesOut mode,
                                bool, hipStream_t) {
     check_common(p, waves, grid);
@@ -107,7 +107,7 @@ hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t, uint32_t waves, 
     return hipSuccess;
 }
 uint32_t decode_lanes_dot_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap) {
-    return decode_lanes_lds_bytes(decode_bits, waves, l2_cap);
+    return decode_lanes_lds_bytes(decode_bits, waves, l2_cap, false);
 }
 int decode_lanes_dot_blocks_per_cu(uint32_t, uint32_t, uint32_t) { return 3; }
 hipError_t launch_decode_lanes_dot(const DecodeParams& p, uint32_t, uint32_t waves, uint32_t grid, hipStream_t) {
