@@ -78,3 +78,61 @@ def test_algorithmic_bytes():
     assert chunks == n + bits // 8 + -(-bits // 64) + 16 * 69_001 + 2 * n
     assert bench.algorithmic_bytes(n, bits, segs, "chunks", 5, False) < chunks
     assert bench.algorithmic_bytes(1000, 6000, 1, "lanes", 8, True) == 750 + 128 + 32 + 1000
+
+
+def _sample_line():
+    import json
+    path = os.path.join(ROOT, "profiles", "bench_block_8b_default.md")
+    text = open(path).read()
+    return json.loads(text.split("```json\n", 1)[1].split("\n```", 1)[0])
+
+
+def test_committed_bench_line_has_the_contract_fields():
+    """The committed sample of the default run's line carries every field of
+    the contract and of this benchmark's records."""
+    d = _sample_line()
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+              "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline", "layouts", "e2e"):
+        assert k in d, k
+    assert d["n_gpus"] == 1 and d["higher_is_better"] is True and d["scaling"] == "weak" and d["unit"] == "GB/s"
+    assert d["vs_baseline"] is None and d["data"].startswith("synthetic")
+    assert d["config"]["workload"].startswith("block_8b") and d["config"]["bit_exact"] is True
+    assert d["config"]["timed_outputs_checked"] >= 2 and d["config"]["rotated_bytes"] >= 1 << 30
+    r = d["roofline"]
+    for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "algorithmic_bytes_per_launch", "kernel_avg_ms",
+              "launch_us", "stream_ref", "frac_of_stream_ref"):
+        assert k in r, k
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
+    c = d["cpu_baseline"]
+    assert c["kind"] == "oracle" and c["cores"] >= 1 and c["cpu_model"] and c["sample"] and c["value"] > 0
+    for k in ("ms", "frac", "bit_exact", "frac_of_stream_ref", "traffic"):
+        assert k in d["layouts"]["chunks"], k
+    for k in ("arm_a_decode_plus_gemv_ms", "arm_b_uncompressed_gemv_ms", "arm_c_fused_decode_gemv_ms",
+              "decode_only_ms", "ratio_c_over_b", "decode_frac_of_stream_ref"):
+        assert k in d["e2e"], k
+    assert d["e2e"]["outputs_bit_identical_a_b"] and d["e2e"]["decoded_weights_bit_exact"]
+    assert d["e2e"]["fused_within_bound"]
+
+
+def test_committed_bench_line_arithmetic():
+    """value, roofline and ratios in the committed sample follow from its own
+    timings and byte counts."""
+    d = _sample_line()
+    r, cfg = d["roofline"], d["config"]
+    n = cfg["n_elems"]
+    assert abs(d["value"] - 2 * n / (d["ms_per_step"] * 1e-3) / 1e9) <= 0.01 * d["value"]
+    achieved = r["algorithmic_bytes_per_launch"] / (r["kernel_avg_ms"] * 1e-3) / 1e9
+    assert abs(r["achieved"] - achieved) <= 0.5
+    assert abs(r["frac"] - r["achieved"] / r["peak"]) <= 1e-4
+    assert abs(r["frac_of_stream_ref"] - r["achieved"] / r["stream_ref"]["GBps"]) <= 1e-3
+    sref = r["stream_ref"]
+    assert abs(sref["GBps"] - (sref["read_bytes"] + sref["write_bytes"]) / (sref["ms"] * 1e-3) / 1e9) <= 0.01 * sref["GBps"]
+    # measured HBM traffic within 5% above the algorithmic bytes
+    assert 1.0 <= r["traffic"] / r["algorithmic_bytes_per_launch"] <= 1.05
+    # the algorithmic reads are the container's sections the decode needs:
+    # all of it but the header, code lengths, tensor table and padding
+    reads = r["algorithmic_bytes_per_launch"] - 2 * n
+    assert 0.99 * cfg["container_bytes"] <= reads <= cfg["container_bytes"]
+    e = d["e2e"]
+    assert abs(e["ratio_c_over_b"] - e["arm_c_fused_decode_gemv_ms"] / e["arm_b_uncompressed_gemv_ms"]) <= 2e-3
+    assert abs(e["ratio_a_over_b"] - e["arm_a_decode_plus_gemv_ms"] / e["arm_b_uncompressed_gemv_ms"]) <= 2e-3
