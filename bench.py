@@ -68,8 +68,9 @@ TRAFFIC_FILES = {"chunks": os.path.join(ROOT, "profiles", "decode_chunks_block_8
                  "lanes_rans": os.path.join(ROOT, "profiles", "decode_lanes_rans_block_8b_traffic.json")}
 
 
-def variant_of(layout: str, coder: str = "huffman") -> str:
-    return layout if coder == "huffman" else f"{layout}_{coder}"
+def variant_of(layout: str, coder: str = "huffman", gap_bits: int = 8) -> str:
+    v = layout if coder == "huffman" else f"{layout}_{coder}"
+    return v + "_gap5" if layout == "chunks" and gap_bits == 5 else v
 
 
 def kernel_source_sha(layout: str = "chunks") -> str:
@@ -77,10 +78,11 @@ def kernel_source_sha(layout: str = "chunks") -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def recorded_traffic(workload: str, layout: str = "chunks", coder: str = "huffman"):
-    """HBM bytes per launch measured with rocprofv3 counters, if still valid."""
+def recorded_traffic(workload: str, layout: str = "chunks", coder: str = "huffman", gap_bits: int = 8):
+    """HBM bytes per launch measured with rocprofv3 counters, if still valid
+    (None for a variant with no record, such as packed gaps)."""
     try:
-        with open(TRAFFIC_FILES[variant_of(layout, coder)]) as f:
+        with open(TRAFFIC_FILES[variant_of(layout, coder, gap_bits)]) as f:
             rec = json.load(f)
     except (OSError, ValueError, KeyError):
         return None
@@ -691,7 +693,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic(args.workload, args.layout, args.coder),
+            "traffic": recorded_traffic(args.workload, args.layout, args.coder, args.gap_bits),
             "algorithmic_bytes_per_launch": alg_bytes,
             "kernel_avg_ms": round(kernel_avg_ms, 5),
             "launch_us": tm["launch_us"],

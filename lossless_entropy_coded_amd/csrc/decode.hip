@@ -194,8 +194,10 @@ __device__ __forceinline__ void put4(uint8_t*& q, const uint8_t* q_end, uint8_t*
 // decode -> matrix-vector product): the decoded weights of each group never
 // leave the chip; the wave multiplies them by x and leaves its partial dot
 // products in p.work.
+// The fused product runs 8-wave workgroups, two per CU: at most 128 VGPRs (4
+// waves per SIMD).
 template <int KC, int KD, int W, bool kDot>
-__global__ __launch_bounds__(kWaveLanes * W) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kWaveLanes * W, kDot ? 4 : 1) void decode_kernel(DecodeParams p) {
     constexpr uint32_t kThreads = kWaveLanes * W;
     // decode tables, in the order of the plan's device buffer: codeword-start
     // table, multi-codeword table, the canonical arrays for long codes

@@ -136,3 +136,13 @@ def test_committed_bench_line_arithmetic():
     e = d["e2e"]
     assert abs(e["ratio_c_over_b"] - e["arm_c_fused_decode_gemv_ms"] / e["arm_b_uncompressed_gemv_ms"]) <= 2e-3
     assert abs(e["ratio_a_over_b"] - e["arm_a_decode_plus_gemv_ms"] / e["arm_b_uncompressed_gemv_ms"]) <= 2e-3
+
+
+def test_packed_gaps_have_no_traffic_record():
+    """The chunks layout's record is for byte gaps; packed gaps change the
+    bytes moved, so no recorded traffic applies to them."""
+    sys.path.insert(0, ROOT)
+    import bench
+    assert bench.variant_of("chunks", "huffman", 5) == "chunks_gap5"
+    assert bench.recorded_traffic("block_8b", "chunks", "huffman", 5) is None
+    assert bench.variant_of("lanes", "rans", 8) == "lanes_rans"
