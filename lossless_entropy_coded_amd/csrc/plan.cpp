@@ -314,14 +314,19 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         // no multi-codeword table entry holds two whole codes when the
         // shortest code is longer than half the table index; four codes of at
         // most 16 bits fit one 64-bit window
-        uint32_t shortest = 0, longest = 0;
+        uint32_t shortest = 0, longest = 0, present = 0;
         for (int s = 0; s < 256; ++s) {
             const uint32_t L = blob_host[p->h.off_code_len + s];
             if (L && (!shortest || L < shortest)) shortest = L;
             longest = std::max(longest, L);
+            present += L != 0;
         }
         p->one_code = shortest && 2 * shortest > p->decode_bits && longest <= 16;
-        p->no_long = longest <= p->decode_bits;
+        // Without the long-code lookup every table entry must decode at least
+        // one code, i.e. the code must be complete: a single symbol's code
+        // "0" leaves the windows that start with 1 undecodable, and a lookup
+        // there would not advance (the long-code lookup always does).
+        p->no_long = present >= 2 && longest <= p->decode_bits;
     }
     {
         const uint32_t forced_waves = env_u32("WC_WAVES", 0);

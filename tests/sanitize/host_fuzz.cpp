@@ -246,6 +246,29 @@ int main(int argc, char** argv) {
             }
         }
     }
+    // one-symbol codes are incomplete ("0" only): the planner must keep the
+    // long-code lookup (which always advances) in the decode loops
+    for (int kind = 0; kind < 2; ++kind) {
+        const uint64_t n = 5000;
+        const uint64_t numels[1] = {n};
+        uint8_t* blob = nullptr;
+        uint64_t bytes = 0;
+        int st;
+        if (kind == 0) {
+            const std::vector<uint16_t> w(n, 0x3F80);
+            const uint16_t* ts[1] = {w.data()};
+            st = wc_encode_host(ts, numels, 1, nullptr, &blob, &bytes);
+        } else {
+            const std::vector<uint8_t> c(n, 77);
+            const uint8_t* ts[1] = {c.data()};
+            st = wc_encode_u8_host(ts, numels, 1, nullptr, &blob, &bytes);
+        }
+        EXPECT(st == WC_OK, "one-symbol encode kind %d: %d", kind, st);
+        if (st != WC_OK) continue;
+        plan_and_decode(blob, bytes, true);
+        EXPECT(g_stub.last_no_long == 0, "one-symbol kind %d planned without the long-code lookup", kind);
+        wc_free_host(blob);
+    }
     // blocks of matrices (row lengths 4096 and 8192) for the fused product,
     // in every bf16 layout and coder
     for (int v = 0; v < 4; ++v) {

@@ -28,6 +28,8 @@ void fail(const char* what) {
 }
 
 void check_common(const wc::DecodeParams& p, uint32_t waves, uint32_t grid) {
+    g_stub.last_no_long = p.no_long;
+    g_stub.last_one_code = p.one_code;
     if (!wc::supported_waves(waves)) fail("waves");
     if (grid == 0) fail("empty grid");
     if (p.u_begin >= p.u_end) fail("empty group range");

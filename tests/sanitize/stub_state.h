@@ -8,5 +8,7 @@ struct StubState {
     uint64_t launches = 0;
     uint64_t dot_launches = 0;
     int64_t live_allocs = 0;       // "device" allocations not yet freed
+    uint32_t last_no_long = 0;     // the last launch's no_long and one_code flags
+    uint32_t last_one_code = 0;
 };
 extern StubState g_stub;

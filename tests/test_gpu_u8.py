@@ -137,6 +137,26 @@ def test_u8_corrupted_stream_stays_in_bounds(wc, name):
         assert gpu_decode_u8(wc, b).size == wl.n
 
 
+def test_u8_single_symbol_corrupted_stream_ends(wc):
+    """A one-symbol code plane has the incomplete code "0": windows that start
+    with a 1 bit match no code, so the planner keeps the long-code lookup
+    (which always advances) in its loop.  A stream corrupted to 1 bits still
+    ends and writes nothing outside the output; the valid stream decodes
+    exactly."""
+    from container_view import sections
+    c = np.full(100_003, 77, np.uint8)
+    blob = wc.encode_u8_host([c])
+    log("case: u8 one symbol, valid")
+    assert np.array_equal(gpu_decode_u8(wc, blob), c)
+    s = sections(blob)
+    nbytes = (s["stream_bits"] + 7) // 8
+    for fill in (0xFF, 0xA5):
+        b = blob.copy()
+        b[s["off_stream"]:s["off_stream"] + nbytes - 1] = fill
+        log(f"case: u8 one symbol, stream bytes set to {fill:#x}")
+        assert gpu_decode_u8(wc, b).size == c.size
+
+
 def test_u8_kind_checks(wc):
     import torch
     c = np.arange(4096).astype(np.uint8)
