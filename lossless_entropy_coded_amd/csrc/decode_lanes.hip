@@ -133,7 +133,9 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
     // second-level table (l2_cap * 2^kL2Bits u16)
     extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
     const bool one_code = kU8 && !kRans && p.one_code != 0;
-    const uint32_t wave_bytes = one_code ? kLaneCompactWaveBytes : kLaneWaveBytes;
+    const bool wide = kU8 && !kRans && !one_code;   // code planes with the wide table
+    const uint32_t slot_bytes = wide ? kLaneWideSlotBytes : kLaneSlotBytes;
+    const uint32_t wave_bytes = one_code ? kLaneCompactWaveBytes : wide ? kLaneWideWaveBytes : kLaneWaveBytes;
     uint16_t* const s_l2 = reinterpret_cast<uint16_t*>(dyn + W * wave_bytes);
 
     const uint32_t tid = threadIdx.x;
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     uint32_t* const sbuf = reinterpret_cast<uint32_t*>(dyn + wave * wave_bytes + kLanePadBytes);
     uint8_t* const ebuf = dyn + wave * wave_bytes + kLanePadBytes + kLaneStageBytes;
-    uint8_t* const slot = ebuf + kLaneSlotBytes * lane;   // this lane's exponents, in its symbol order
+    uint8_t* const slot = ebuf + slot_bytes * lane;   // this lane's symbols, in its symbol order
 
     // wave w of workgroup b takes segments b*W + w, then every (grid * W)-th
     const uint64_t stride = (uint64_t)gridDim.x * W;
@@ -164,24 +166,21 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
     Meta cur_m = uniform_meta(m_first);
     LaneRaw cur_r = load_lane_raw(p, cur_m, min_u64(u, last_u), lane);
     Meta m_next = load_meta(p, min_u64(u + stride, last_u));
-    // code planes (Huffman): the multi-codeword table is staged with its
-    // symbols un-rotated, so that the merge stores the slot bytes as they
-    // are; with one code per entry, as 16-bit entries (symbol | length << 8,
-    // 0 for a code longer than the index) packed into the first 2^KD / 2
-    // words of the table's place, a quarter of the LDS bytes per lookup
+    // code planes (Huffman) with one code per entry: the multi-codeword
+    // table is staged as 16-bit entries (un-rotated symbol | length << 8, 0
+    // for a code longer than the index) packed into the first 2^KD / 2 words
+    // of the table's place, a quarter of the LDS bytes per lookup.  (Other
+    // Huffman code planes find the wide table, built by the planner, in the
+    // multi-codeword table's place and stage it as it is.)
     if constexpr (kU8 && !kRans) {
         const bool compact = p.one_code != 0;
         auto put = [&](uint32_t i, u32x4 v) {
-            if (i < kDecVec) {
-                if (compact) {
-                    auto c16 = [](uint32_t x, uint32_t y) {
-                        return x == 0 ? 0u : (unrotate4(y) & 0xFFu) | (((x >> 16) & 0xFFu) << 8);
-                    };
-                    reinterpret_cast<uint32_t*>(s_tab)[i] = c16(v.x, v.y) | c16(v.z, v.w) << 16;
-                    return;
-                }
-                v.y = unrotate4(v.y);
-                v.w = unrotate4(v.w);
+            if (compact && i < kDecVec) {
+                auto c16 = [](uint32_t x, uint32_t y) {
+                    return x == 0 ? 0u : (unrotate4(y) & 0xFFu) | (((x >> 16) & 0xFFu) << 8);
+                };
+                reinterpret_cast<uint32_t*>(s_tab)[i] = c16(v.x, v.y) | c16(v.z, v.w) << 16;
+                return;
             }
             tdst[i] = v;
         };
@@ -412,32 +411,70 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                             }
                         }
                     } else {
-                        // up to four symbols per lookup, stored as aligned
-                        // words, one store per lookup: `acc` holds the bytes
-                        // [c & ~3, c) decoded so far (its other bytes 0; the
-                        // table's bytes past a lookup's symbols are 0); a
-                        // lookup's symbols, shifted to c & 3, join it, the
-                        // word at c & ~3 is stored and the part past that
-                        // word carries over.  The last word ends by byte 67.
+                        // the wide table: a (KD + 1)-bit index, 4-byte entries
+                        // of up to three whole codes (total bits | count << 5
+                        // | symbols << 8, first in the low byte; 0 when the
+                        // first code is longer than the index).  Symbols go
+                        // to the slot as aligned words, one store per
+                        // lookup: `acc` holds the bytes [c & ~3, c) decoded
+                        // so far (its other bytes 0); a lookup's symbols,
+                        // shifted to c & 3, join it, the word at c & ~3 is
+                        // stored and the part past that word carries over.
+                        const uint32_t* const s_wide = reinterpret_cast<const uint32_t*>(s_tab);
+                        constexpr uint32_t KW = KD + 1;
                         uint32_t c = 0, acc = 0;
-                        while (c < nsym) {
-                            const int32_t k = t >> 5;
-                            const uint32_t top = __builtin_amdgcn_alignbit(sbuf[k], sbuf[k + 1], ~(uint32_t)t);
-                            uint2 e = s_dec[top >> (32 - KD)];
-                            if constexpr (kLong) {
-                                if (e.x == 0) {
-                                    e = long_decode_entry<KD>(top, KD + 1, lt);
-                                    e.y = unrotate4(e.y);
-                                }
-                            }
+                        auto put = [&](uint32_t e) {
                             const uint32_t q = c & 3u;
-                            const uint32_t ns = (e.x >> 8) & 0xFFu;
-                            const uint64_t w = (uint64_t)e.y << (q << 3);
+                            const uint32_t ns = (e >> 5) & 3u;
+                            const uint64_t w = (uint64_t)(e >> 8) << (q << 3);
                             const uint32_t lo = (uint32_t)w | acc;
                             *reinterpret_cast<uint32_t*>(slot + (c - q)) = lo;
                             acc = q + ns >= 4u ? (uint32_t)(w >> 32) : lo;
                             c += ns;
-                            t += (int32_t)((e.x >> 16) & 0xFFu);
+                        };
+                        if constexpr (!kLong) {
+                            // every code fits the index (and the code is
+                            // complete, so every entry holds one at least):
+                            // four lookups of at most KW bits per 64-bit
+                            // window, read from three staged words.  A lane
+                            // enters with c <= 63 and four lookups add at
+                            // most 12 symbols, so its stores end by byte 75
+                            // of its 76-byte slot; it makes at most 64
+                            // lookups of at most 12 bits (at most word 524
+                            // of the wave's staging and slots).
+                            while (c < nsym) {
+                                const int32_t k = t >> 5;
+                                const uint32_t w1 = sbuf[k + 1];
+                                uint64_t win =
+                                    (uint64_t)__builtin_amdgcn_alignbit(sbuf[k], w1, ~(uint32_t)t) << 32 |
+                                    __builtin_amdgcn_alignbit(w1, sbuf[k + 2], ~(uint32_t)t);
+                                uint32_t used = 0;
+#pragma unroll
+                                for (uint32_t i = 0; i < 4; ++i) {
+                                    const uint32_t e = s_wide[(uint32_t)(win >> 32) >> (32 - KW)];
+                                    put(e);
+                                    const uint32_t nb = e & 31u;
+                                    win <<= nb;
+                                    used += nb;
+                                }
+                                t += (int32_t)used;
+                            }
+                        } else {
+                            // codes longer than the index: one lookup per
+                            // window, re-read at every lookup (a long code
+                            // takes up to 24 bits); the last word ends by
+                            // byte 67.
+                            while (c < nsym) {
+                                const int32_t k = t >> 5;
+                                const uint32_t top = __builtin_amdgcn_alignbit(sbuf[k], sbuf[k + 1], ~(uint32_t)t);
+                                uint32_t e = s_wide[top >> (32 - KW)];
+                                if (e == 0) {
+                                    const uint2 l = long_decode_entry<KD>(top, KD + 1, lt);
+                                    e = ((l.x >> 16) & 31u) | 1u << 5 | (unrotate4(l.y) & 0xFFu) << 8;
+                                }
+                                put(e);
+                                t += (int32_t)(e & 31u);
+                            }
                         }
                         if (c & 3u) *reinterpret_cast<uint32_t*>(slot + (c & ~3u)) = acc;
                     }
@@ -495,7 +532,7 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
         // `full` is the (full / 64)-th of lane full % 64
         if (kU8 && !one_code && full * kMergeElems < n && lane == 0) {
             const uint32_t rel = kMergeElems * full;
-            const uint2 e2 = load_slot8(ebuf + kLaneSlotBytes * (full % kWaveLanes) + kMergeElems * (full / kWaveLanes));
+            const uint2 e2 = load_slot8(ebuf + slot_bytes * (full % kWaveLanes) + kMergeElems * (full / kWaveLanes));
             const uint32_t o[2] = {kRans ? unrotate4(e2.x) : e2.x, kRans ? unrotate4(e2.y) : e2.y};
 #pragma unroll
             for (uint32_t i = 0; i < kMergeElems; ++i)
@@ -773,17 +810,17 @@ hipError_t dispatch_lanes(uint32_t decode_bits, uint32_t waves, bool rans, F&& f
 
 }  // namespace
 
-uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap, bool compact) {
-    return waves * (compact ? kLaneCompactWaveBytes : kLaneWaveBytes) + (l2_cap << kL2Bits) * 2;
+uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap, LaneLds layout) {
+    return waves * lane_wave_bytes(layout) + (l2_cap << kL2Bits) * 2;
 }
 
-uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool compact) {
-    return ((2u << decode_bits) + kLongWords) * 4 + decode_lanes_dyn_lds_bytes(waves, l2_cap, compact);
+uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, LaneLds layout) {
+    return ((2u << decode_bits) + kLongWords) * 4 + decode_lanes_dyn_lds_bytes(waves, l2_cap, layout);
 }
 
-int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool rans, bool compact) {
+int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool rans, LaneLds layout) {
     if ((decode_bits != 11 && decode_bits != 10) || (rans && decode_bits != 11) || !supported_waves(waves)) return 0;
-    const uint32_t dyn = decode_lanes_dyn_lds_bytes(waves, l2_cap, compact);
+    const uint32_t dyn = decode_lanes_dyn_lds_bytes(waves, l2_cap, layout);
     int n = 0;
     (void)dispatch_lanes(decode_bits, waves, rans, [&](auto v) {
         n = decltype(v)::blocks_per_cu(dyn);
@@ -820,7 +857,8 @@ hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint
     if ((decode_bits != 11 && decode_bits != 10) || (rans && (decode_bits != 11 || p.l2_cap)) ||
         !supported_waves(waves) || p.l2_cap > kL2Prefixes)
         return hipErrorInvalidValue;
-    const uint32_t dyn = decode_lanes_dyn_lds_bytes(waves, p.l2_cap, mode == kLanesToU8 && !rans && p.one_code);
+    const LaneLds layout = mode != kLanesToU8 || rans ? kLdsSlots : p.one_code ? kLdsCompact : kLdsWide;
+    const uint32_t dyn = decode_lanes_dyn_lds_bytes(waves, p.l2_cap, layout);
     return dispatch_lanes(decode_bits, waves, rans,
                           [&](auto v) { return decltype(v)::launch(p, grid, dyn, mode, stream); });
 }

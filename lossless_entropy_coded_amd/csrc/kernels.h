@@ -129,8 +129,17 @@ constexpr uint32_t kLanePadBytes = 16;
 constexpr uint32_t kLaneWaveBytes = kLanePadBytes + kLaneStageBytes + kWaveLanes * kLaneSlotBytes;
 // Code planes with one code per table entry write their bytes straight to
 // memory and need no slots: a wave's region is the pad, the staging and 128
-// bytes a lane's last 64-bit windows may read past the staging.
+// bytes a lane's last 64-bit windows may read past the staging.  Other code
+// planes take the wide table (up to three codes per lookup, four lookups per
+// window) and 76-byte slots (19 dwords, odd): four lookups from a lane's 63rd
+// symbol may store up to byte 75.
 constexpr uint32_t kLaneCompactWaveBytes = kLanePadBytes + kLaneStageBytes + 128;
+constexpr uint32_t kLaneWideSlotBytes = 76;
+constexpr uint32_t kLaneWideWaveBytes = kLanePadBytes + kLaneStageBytes + kWaveLanes * kLaneWideSlotBytes;
+enum LaneLds : uint32_t { kLdsSlots = 0, kLdsCompact = 1, kLdsWide = 2 };
+inline uint32_t lane_wave_bytes(LaneLds layout) {
+    return layout == kLdsCompact ? kLaneCompactWaveBytes : layout == kLdsWide ? kLaneWideWaveBytes : kLaneWaveBytes;
+}
 constexpr uint32_t kLanesMaxSegBits = 15872;
 
 // Wavefronts per decode workgroup the kernels are built for.
@@ -168,11 +177,12 @@ hipError_t launch_decode(const DecodeParams& p, uint32_t count_bits, uint32_t de
 // entry t = rotated symbol | (f mod 2^12) << 8 | (t - cum) << 20 (f = 2^12,
 // stored as 0, only when one symbol has every slot).
 enum LanesOut : uint32_t { kLanesToBf16 = 0, kLanesToDot = 1, kLanesToU8 = 2 };
-// compact: the layout of one-code code planes (kLaneCompactWaveBytes per wave).
-uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap, bool compact = false);
-uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool compact = false);
+// layout: the per-wave LDS region (kLdsSlots for bf16, rANS and the fused
+// product; kLdsCompact or kLdsWide for Huffman code planes).
+uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap, LaneLds layout = kLdsSlots);
+uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, LaneLds layout = kLdsSlots);
 int decode_lanes_blocks_per_cu(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool rans,
-                               bool compact = false);
+                               LaneLds layout = kLdsSlots);
 hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t decode_bits, uint32_t waves, uint32_t grid,
                                LanesOut mode, bool rans, hipStream_t stream);
 

@@ -261,6 +261,43 @@ struct DeviceGuard {
 
 }  // namespace
 
+// The wide decode table of Huffman code planes: for each `bits`-bit window,
+// up to three whole codes from its start, as total bits | count << 5 |
+// symbols << 8 (first code in the low byte), or 0 when the window's first
+// code is longer than the window.  Codes are canonical (shorter codes
+// numerically smaller, equal lengths in symbol order).
+static void build_wide_table(const uint8_t* lens, uint32_t bits, uint32_t* out) {
+    const uint32_t size = 1u << bits;
+    // first[w]: the window's first code, symbol | length << 8 (0: longer than the window)
+    std::vector<uint32_t> first(size, 0u);
+    uint32_t count[wc::kMaxCodeLen + 2] = {0};
+    for (int s = 0; s < 256; ++s) count[lens[s]] += lens[s] != 0;
+    uint32_t next[wc::kMaxCodeLen + 2] = {0};
+    for (uint32_t L = 1, code = 0; L <= wc::kMaxCodeLen; ++L) {
+        code = (code + count[L - 1] * (L > 1)) << 1;
+        next[L] = code;
+    }
+    for (uint32_t L = 1; L <= std::min<uint32_t>(bits, wc::kMaxCodeLen); ++L)
+        for (int s = 0; s < 256; ++s) {
+            if (lens[s] != L) continue;
+            const uint32_t code = next[L]++;
+            const uint32_t lo = code << (bits - L), hi = (code + 1) << (bits - L);
+            for (uint32_t w = lo; w < hi; ++w) first[w] = (uint32_t)s | L << 8;
+        }
+    for (uint32_t w = 0; w < size; ++w) {
+        uint32_t pos = 0, n = 0, syms = 0;
+        while (n < 3 && pos < bits) {
+            const uint32_t f = first[(w << pos) & (size - 1)];
+            const uint32_t L = f >> 8;
+            if (f == 0 || L > bits - pos) break;
+            syms |= (f & 0xFFu) << (8 * n);
+            ++n;
+            pos += L;
+        }
+        out[w] = n ? pos | n << 5 | syms << 8 : 0u;
+    }
+}
+
 extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_device, wc_plan_t** out) {
     if (!out) return WC_ERR_INVALID_ARG;
     *out = nullptr;
@@ -380,15 +417,17 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
     // 1.8% faster for the 70B-shape block; for the 8B-shape block's 17 rounds
     // splitting only costs).  WC_LAUNCH_ROUNDS overrides it (0: one launch).
     p->launch_rounds = env_u32("WC_LAUNCH_ROUNDS", 40);
-    // code planes with one code per table entry: no exponent slots
-    const bool compact = lanes && !p->rans && p->h.elem_kind == wc::kKindU8 && p->one_code;
+    // Huffman code planes: no slots with one code per table entry, else the
+    // wide table's larger slots
+    const bool u8_huffman = lanes && !p->rans && p->h.elem_kind == wc::kKindU8;
+    const wc::LaneLds layout = !u8_huffman ? wc::kLdsSlots : p->one_code ? wc::kLdsCompact : wc::kLdsWide;
     auto size_shape = [&](wc_plan_s::Shape& sh, bool fused_lanes) {
         sh.lds_bytes = fused_lanes ? wc::decode_lanes_dot_lds_bytes(p->decode_bits, sh.waves, p->l2_cap)
-                       : lanes     ? wc::decode_lanes_lds_bytes(p->decode_bits, sh.waves, p->l2_cap, compact)
+                       : lanes     ? wc::decode_lanes_lds_bytes(p->decode_bits, sh.waves, p->l2_cap, layout)
                                    : wc::decode_lds_bytes(p->count_bits, p->decode_bits, sh.waves, p->ebuf_bytes,
                                                           p->l2_cap);
         int per_cu = fused_lanes ? wc::decode_lanes_dot_blocks_per_cu(p->decode_bits, sh.waves, p->l2_cap)
-                     : lanes     ? wc::decode_lanes_blocks_per_cu(p->decode_bits, sh.waves, p->l2_cap, p->rans, compact)
+                     : lanes     ? wc::decode_lanes_blocks_per_cu(p->decode_bits, sh.waves, p->l2_cap, p->rans, layout)
                                  : wc::decode_blocks_per_cu(p->count_bits, p->decode_bits, sh.waves, p->ebuf_bytes,
                                                             p->l2_cap);
         // The persistent grid must be co-resident.  LDS is handed out in
@@ -444,6 +483,16 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         wc::CodeLens lens;
         std::memcpy(lens.len, blob_host + p->h.off_code_len, 256);
         te = wc::launch_build_tables(lens, p->count_bits, p->decode_bits, p->d_tables, nullptr);
+        if (te == hipSuccess && layout == wc::kLdsWide) {
+            // the wide table of code planes, at the multi-codeword table's
+            // place (2^(decode_bits + 1) 4-byte entries: the same bytes)
+            std::vector<uint32_t> wide(2u << p->decode_bits);
+            build_wide_table(lens.len, p->decode_bits + 1, wide.data());
+            te = hipStreamSynchronize(nullptr);
+            if (te == hipSuccess)
+                te = hipMemcpy(p->d_tables + (1u << p->count_bits), wide.data(), wide.size() * 4,
+                               hipMemcpyHostToDevice);
+        }
     }
     if (te != hipSuccess || hipStreamSynchronize(nullptr) != hipSuccess) {
         (void)hipFree(p->d_tables);

@@ -94,13 +94,13 @@ hipError_t launch_decode(const DecodeParams& p, uint32_t, uint32_t, uint32_t wav
     g_stub.dot_launches += dot;
     return hipSuccess;
 }
-uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap, bool compact) {
-    return waves * (compact ? kLaneCompactWaveBytes : kLaneWaveBytes) + (l2_cap << kL2Bits) * 2;
+uint32_t decode_lanes_dyn_lds_bytes(uint32_t waves, uint32_t l2_cap, LaneLds layout) {
+    return waves * lane_wave_bytes(layout) + (l2_cap << kL2Bits) * 2;
 }
-uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, bool compact) {
-    return ((2u << decode_bits) + kLongWords) * 4 + decode_lanes_dyn_lds_bytes(waves, l2_cap, compact);
+uint32_t decode_lanes_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap, LaneLds layout) {
+    return ((2u << decode_bits) + kLongWords) * 4 + decode_lanes_dyn_lds_bytes(waves, l2_cap, layout);
 }
-int decode_lanes_blocks_per_cu(uint32_t, uint32_t waves, uint32_t, bool, bool) { return waves == 4 ? 3 : 2; }
+int decode_lanes_blocks_per_cu(uint32_t, uint32_t waves, uint32_t, bool, LaneLds) { return waves == 4 ? 3 : 2; }
 hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t, uint32_t waves, uint32_t grid, LanesOut mode,
                                bool, hipStream_t) {
     check_common(p, waves, grid);
@@ -109,7 +109,7 @@ hipError_t launch_decode_lanes(const DecodeParams& p, uint32_t, uint32_t waves, 
     return hipSuccess;
 }
 uint32_t decode_lanes_dot_lds_bytes(uint32_t decode_bits, uint32_t waves, uint32_t l2_cap) {
-    return decode_lanes_lds_bytes(decode_bits, waves, l2_cap, false);
+    return decode_lanes_lds_bytes(decode_bits, waves, l2_cap, kLdsSlots);
 }
 int decode_lanes_dot_blocks_per_cu(uint32_t, uint32_t, uint32_t) { return 3; }
 hipError_t launch_decode_lanes_dot(const DecodeParams& p, uint32_t, uint32_t waves, uint32_t grid, hipStream_t) {
