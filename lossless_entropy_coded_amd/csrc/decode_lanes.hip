@@ -686,19 +686,22 @@ __global__ __launch_bounds__(kWaveLanes * W, 6) void decode_lanes_dot_kernel(Dec
         const uint32_t cnt = lane < nb8 ? (nb8 - 1 - lane) / kWaveLanes + 1 : 0u;
         uint32_t nsym = kLaneBlock * cnt;
         if (cnt && lane == (nb8 - 1) % kWaveLanes) nsym -= kLaneBlock * nb8 - n;
-        // the window of bit position t + 1: staged words t >> 5 (arithmetic:
-        // -1 at position 0, the pad's last word, shifted out) and the next,
-        // shifted right by -(t + 1) mod 32.  A lane's first bit is at most
-        // 15,999 (the planner bounds lane offsets by the segment's bits) and
-        // it makes at most 64 lookups of at most 24 bits, so its last window
-        // word is at most 548: inside the wave's staging and slots.
-        int32_t t = (int32_t)((uint32_t)(cur_m.p0 & 127u) + off) - 1;
+        // the window of bit position b is kept as nb = -b: staged words
+        // (b - 1) >> 5 = -1 - (nb >> 5) (arithmetic: -1 at position 0, the
+        // pad's last word, shifted out) and the next, shifted right by
+        // nb mod 32 (one instruction fewer per lookup than keeping b - 1).  A
+        // lane's first bit is at most 15,999 (the planner bounds lane offsets
+        // by the segment's bits) and it makes at most 64 lookups of at most 24
+        // bits, so its last window word is at most 548: inside the wave's
+        // staging and slots.
+        int32_t nb = -(int32_t)((uint32_t)(cur_m.p0 & 127u) + off);
         // the symbol count is kept as the LDS byte address of the next symbol
         // (a local-address-space offset; slots are 4-byte aligned, so its low
         // two bits are the count's)
         typedef __attribute__((address_space(3))) uint8_t LdsByte;
         typedef __attribute__((address_space(3))) uint32_t LdsWord;
         const uint32_t slot_addr = (uint32_t)(uintptr_t)(LdsByte*)slot;
+        const uint32_t sbuf_addr = (uint32_t)(uintptr_t)(LdsByte*)(sbuf - 1);   // word -1: the pad's last
         uint32_t a = slot_addr;
         uint32_t acc = 0;
         const uint32_t full = n / kMergeElems;
@@ -708,8 +711,12 @@ __global__ __launch_bounds__(kWaveLanes * W, 6) void decode_lanes_dot_kernel(Dec
             // symbol c of this phase goes to slot byte c - 32h
             const uint32_t end = slot_addr + min(nsym, kDotHalf * (h + 1)) - kDotHalf * h;
             while (a < end) {
-                const int32_t k = t >> 5;
-                const uint32_t top = __builtin_amdgcn_alignbit(sbuf[k], sbuf[k + 1], ~(uint32_t)t);
+                // word -1 - (nb >> 5) of the staging: one v_mad_i32_i24
+                // (the compiler otherwise splits the multiply-add in two)
+                uint32_t waddr;
+                asm("v_mad_i32_i24 %0, %1, -4, %2" : "=v"(waddr) : "v"(nb >> 5), "s"(sbuf_addr));
+                const LdsWord* const wp = (const LdsWord*)(uintptr_t)waddr;
+                const uint32_t top = __builtin_amdgcn_alignbit(wp[0], wp[1], (uint32_t)nb);
                 uint2 e = s_dec[top >> (32 - KD)];
                 if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
                 const uint32_t q = a & 3u;
@@ -718,7 +725,7 @@ __global__ __launch_bounds__(kWaveLanes * W, 6) void decode_lanes_dot_kernel(Dec
                 *(LdsWord*)(uintptr_t)(a - q) = lo;
                 acc = q + ((e.x >> 8) & 0xFFu) >= 4u ? (uint32_t)(w >> 32) : lo;
                 a += (e.x >> 8) & 0xFFu;
-                t += (int32_t)((e.x >> 16) & 0xFFu);
+                nb -= (int32_t)((e.x >> 16) & 0xFFu);
             }
             a -= kDotHalf * (h == 0);
             wave_lds_order();
