@@ -293,6 +293,27 @@ int wc_decode_u8_async(const wc_plan_t* plan, const void* blob_dev, uint8_t* out
 int wc_gemv_bf16_async(const uint16_t* W, uint32_t rows, uint32_t cols, const uint16_t* x, float* y,
                        void* stream);
 
+/* ---- debug status ---------------------------------------------------------- */
+/*
+ * wc_plan_debug_status -- a plan made with WC_DEBUG=1 in the environment
+ * carries a device status word: the chunks-layout decode kernels (the plain
+ * decode and the fused product) check that the codewords starting in each
+ * group's bits number exactly its elements (phase 1's count; DFloat11 page,
+ * abstract, design point (ii): the auxiliary variables that place each
+ * block's output) and OR WC_DEBUG_GROUP_COUNT into the word when they do
+ * not: a corrupted stream or group bit offset, which wc_plan's host checks
+ * cannot see.  Other layouts leave the word alone.  Plans made without
+ * WC_DEBUG launch kernels compiled without the check.
+ *   plan    a plan made with WC_DEBUG=1;
+ *   status  receives the word (host pointer);
+ *   reset   nonzero: the word is cleared after it is read.
+ * Synchronises the plan's device first (every launch that uses the plan has
+ * finished).  Returns WC_ERR_INVALID_ARG for a NULL argument or a plan made
+ * without WC_DEBUG, WC_ERR_HIP if a HIP call fails.
+ */
+#define WC_DEBUG_GROUP_COUNT 1u
+int wc_plan_debug_status(const wc_plan_t* plan, uint32_t* status, int reset);
+
 /* ---- measurement ----------------------------------------------------------- */
 /*
  * wc_stream_reference_async -- the streaming yardstick for the decode kernels'

@@ -38,7 +38,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <initializer_list>
 
+#include "../../include/wc.h"
 #include "decode_common.h"
 #include "kernels.h"
 
@@ -196,7 +198,7 @@ __device__ __forceinline__ void put4(uint8_t*& q, const uint8_t* q_end, uint8_t*
 // products in p.work.
 // The fused product runs 8-wave workgroups, two per CU: at most 128 VGPRs (4
 // waves per SIMD).
-template <int KC, int KD, int W, bool kDot>
+template <int KC, int KD, int W, bool kDot, bool kCheck>
 __global__ __launch_bounds__(kWaveLanes * W, kDot ? 4 : 1) void decode_kernel(DecodeParams p) {
     constexpr uint32_t kThreads = kWaveLanes * W;
     // decode tables, in the order of the plan's device buffer: codeword-start
@@ -432,6 +434,13 @@ __global__ __launch_bounds__(kWaveLanes * W, kDot ? 4 : 1) void decode_kernel(De
             const Unit w = make_unit(load_raw(p, cur_meta, lane, pass), cur_meta, lane, pass);
             done += run_pass(w.a, w.b, done);
         }
+        // debug plans (kernels compiled with the check): the codewords that
+        // start in the group's bits are its elements, one each (a corrupted
+        // stream or group bit offset, which the host checks cannot see,
+        // breaks this); a vector-memory atomic OR into the status word
+        if constexpr (kCheck) {
+            if (done != n_unit && lane == 0) atomicOr(p.status, WC_DEBUG_GROUP_COUNT);
+        }
 
         // consume every load of this iteration now, before the merge issues
         // its stores: the next group's chains and table entries, and the sm
@@ -601,21 +610,32 @@ __global__ __launch_bounds__(1024) void build_tables_kernel(CodeLens lens, uint3
 
 template <int KC, int KD, int W>
 struct Variant {
+    // plans with a status word run the kernels compiled with the per-group
+    // check; the others pay nothing for it
+    template <bool kDot, bool kCheck>
+    static void go(const DecodeParams& p, uint32_t grid, uint32_t dyn, hipStream_t stream) {
+        hipLaunchKernelGGL((decode_kernel<KC, KD, W, kDot, kCheck>), dim3(grid), dim3(kWaveLanes * W), dyn, stream,
+                           p);
+    }
     static hipError_t launch(const DecodeParams& p, uint32_t grid, uint32_t dyn, bool dot, hipStream_t stream) {
+        const bool check = p.status != nullptr;
         if (dot)
-            hipLaunchKernelGGL((decode_kernel<KC, KD, W, true>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
+            check ? go<true, true>(p, grid, dyn, stream) : go<true, false>(p, grid, dyn, stream);
         else
-            hipLaunchKernelGGL((decode_kernel<KC, KD, W, false>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
+            check ? go<false, true>(p, grid, dyn, stream) : go<false, false>(p, grid, dyn, stream);
         return hipGetLastError();
     }
     static int blocks_per_cu(uint32_t dyn) {
-        int n = 0, m = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<KC, KD, W, false>, kWaveLanes * W, dyn) !=
-                hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, decode_kernel<KC, KD, W, true>, kWaveLanes * W, dyn) !=
-                hipSuccess)
-            return 0;
-        return n < m ? n : m;
+        int least = 1 << 30;
+        for (const void* k : {reinterpret_cast<const void*>(decode_kernel<KC, KD, W, false, false>),
+                              reinterpret_cast<const void*>(decode_kernel<KC, KD, W, true, false>),
+                              reinterpret_cast<const void*>(decode_kernel<KC, KD, W, false, true>),
+                              reinterpret_cast<const void*>(decode_kernel<KC, KD, W, true, true>)}) {
+            int n = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, kWaveLanes * W, dyn) != hipSuccess) return 0;
+            least = n < least ? n : least;
+        }
+        return least;
     }
     static hipError_t build(const CodeLens& lens, uint32_t* d_tables, hipStream_t stream) {
         hipLaunchKernelGGL((build_tables_kernel<KC, KD>), dim3(1), dim3(1024), 0, stream, lens, d_tables);

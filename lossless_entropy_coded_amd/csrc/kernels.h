@@ -110,6 +110,7 @@ struct DecodeParams {
     uint32_t gap_packed;     // chunks layout: gaps stored in 5 bits (else one byte each)
     uint32_t one_code;       // lanes layout, Huffman: one code per table entry at most, all <= 16 bits
     uint32_t no_long;        // Huffman: no code is longer than the multi-codeword table's index
+    uint32_t* status;        // debug plans: invariant failures are OR-ed in here (else null)
     DotParams dot;           // fused matrix-vector launches only
 };
 

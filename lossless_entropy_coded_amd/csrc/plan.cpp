@@ -54,6 +54,7 @@ struct wc_plan_s {
     bool no_long = false;        // Huffman: no code longer than decode_bits
     uint32_t launch_rounds = 0;  // plain decode: segment rounds per launch at most (0: one launch)
     uint32_t* d_tables = nullptr;
+    uint32_t* d_status = nullptr;   // WC_DEBUG plans: the debug status word
 };
 
 namespace {
@@ -494,8 +495,13 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
                                hipMemcpyHostToDevice);
         }
     }
+    if (te == hipSuccess && env_u32("WC_DEBUG", 0)) {
+        te = hipMalloc(reinterpret_cast<void**>(&p->d_status), 4);
+        if (te == hipSuccess) te = hipMemset(p->d_status, 0, 4);
+    }
     if (te != hipSuccess || hipStreamSynchronize(nullptr) != hipSuccess) {
         (void)hipFree(p->d_tables);
+        if (p->d_status) (void)hipFree(p->d_status);
         delete p;
         return WC_ERR_HIP;
     }
@@ -552,6 +558,7 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
     d.gap_packed = p->h.gap_bits == wc::kGapBitsPacked ? 1u : 0u;
     d.one_code = p->one_code ? 1u : 0u;
     d.no_long = p->no_long ? 1u : 0u;
+    d.status = p->d_status;
     hipError_t e = hipSuccess;
     // launches of at most launch_rounds rounds of the persistent grid each
     const uint64_t per_round = (uint64_t)p->plain.grid * p->plain.waves;
@@ -600,6 +607,7 @@ extern "C" int wc_decode_u8_async(const wc_plan_t* p, const void* blob_dev, uint
     d.gap_packed = p->h.gap_bits == wc::kGapBitsPacked ? 1u : 0u;
     d.one_code = p->one_code ? 1u : 0u;
     d.no_long = p->no_long ? 1u : 0u;
+    d.status = p->d_status;
     const hipError_t e = wc::launch_decode_lanes(d, p->decode_bits, p->busy.waves, p->busy.grid, wc::kLanesToU8, p->rans,
                                                  static_cast<hipStream_t>(stream));
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
@@ -699,6 +707,7 @@ extern "C" int wc_decode_gemv_async(const wc_plan_t* p, const void* blob_dev, co
     d.gap_packed = p->h.gap_bits == wc::kGapBitsPacked ? 1u : 0u;
     d.one_code = p->one_code ? 1u : 0u;
     d.no_long = p->no_long ? 1u : 0u;
+    d.status = p->d_status;
     d.dot.part = static_cast<float*>(work_dev);
     d.dot.row_group = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(work_dev) + rows_off);
     // Huffman lanes containers have a fused kernel of their own (its own
@@ -727,11 +736,23 @@ int wc::plan_device(const wc_plan_s* p) { return p->device; }
 
 extern "C" void wc_plan_destroy(wc_plan_t* p) {
     if (!p) return;
-    if (p->d_tables) {
+    if (p->d_tables || p->d_status) {
         DeviceGuard guard(p->device);
-        (void)hipFree(p->d_tables);
+        if (p->d_tables) (void)hipFree(p->d_tables);
+        if (p->d_status) (void)hipFree(p->d_status);
     }
     delete p;
+}
+
+extern "C" int wc_plan_debug_status(const wc_plan_t* p, uint32_t* status, int reset) {
+    if (!p || !status || !p->d_status) return WC_ERR_INVALID_ARG;
+    DeviceGuard guard(p->device);
+    if (!guard.ok || hipDeviceSynchronize() != hipSuccess ||
+        hipMemcpy(status, p->d_status, 4, hipMemcpyDeviceToHost) != hipSuccess)
+        return WC_ERR_HIP;
+    if (reset && (hipMemset(p->d_status, 0, 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess))
+        return WC_ERR_HIP;
+    return WC_OK;
 }
 
 extern "C" const char* wc_status_str(int s) {

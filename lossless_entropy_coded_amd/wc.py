@@ -87,6 +87,8 @@ _lib.wc_decode_gemv_noalloc_async.restype = ctypes.c_int
 _lib.wc_stream_reference_async.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_uint64,
                                            ctypes.c_void_p]
 _lib.wc_stream_reference_async.restype = ctypes.c_int
+_lib.wc_plan_debug_status.argtypes = [ctypes.c_void_p, _u32p, ctypes.c_int]
+_lib.wc_plan_debug_status.restype = ctypes.c_int
 _lib.wc_plan_destroy.argtypes = [ctypes.c_void_p]
 _lib.wc_plan_destroy.restype = None
 _lib.wc_status_str.argtypes = [ctypes.c_int]
@@ -110,6 +112,8 @@ WC_ERR_GAP = -15
 WC_ERR_GROUP_START = -16
 WC_ERR_STREAM_BITS = -17
 WC_ERR_TENSOR_TABLE = -18
+# bits of a debug plan's status word (plans made with WC_DEBUG=1)
+WC_DEBUG_GROUP_COUNT = 1
 
 # Group table defaults (wc_encode_opts): G = chunks per group, what one wave64
 # decodes in one pass (two 64-bit chunks per lane; wider groups take several
@@ -131,7 +135,7 @@ CODERS = {"huffman": 0, "rans": 1}
 EXPORTED = ("wc_encode_host", "wc_encode_u8_host", "wc_free_host", "wc_plan", "wc_plan_info", "wc_plan_stats",
             "wc_plan_format", "wc_decode_u8_async",
             "wc_decode_async", "wc_gemv_bf16_async", "wc_decode_gemv_work_bytes", "wc_decode_gemv_async",
-            "wc_decode_gemv_noalloc_async", "wc_stream_reference_async",
+            "wc_decode_gemv_noalloc_async", "wc_stream_reference_async", "wc_plan_debug_status",
             "wc_plan_destroy", "wc_status_str")
 
 
@@ -278,6 +282,16 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+def plan_debug_status(plan: Plan, reset: bool = False) -> int:
+    """wc_plan_debug_status: the status word of a plan made with WC_DEBUG=1 in
+    the environment (0: no invariant failed; WC_DEBUG_GROUP_COUNT: a group of
+    the chunks layout decoded a codeword count other than its element count).
+    Waits for the plan's device; reset clears the word after reading it."""
+    word = ctypes.c_uint32(0)
+    _check(_lib.wc_plan_debug_status(plan.handle, ctypes.byref(word), 1 if reset else 0), "wc_plan_debug_status")
+    return word.value
 
 
 def _ptr(x) -> int:

@@ -150,6 +150,18 @@ int plan_and_decode(const uint8_t* blob, uint64_t bytes, bool expect_ok) {
         EXPECT(wc_decode_async(plan, blob, reinterpret_cast<uint16_t*>(out_al), nullptr) == WC_ERR_INVALID_ARG,
                "bf16 entry on u8");
     }
+    // the debug status word: present (and clear) only when the plan was made
+    // with WC_DEBUG=1, and handed to the launches
+    {
+        const char* dbg = std::getenv("WC_DEBUG");
+        const bool debug = dbg && std::strcmp(dbg, "1") == 0;
+        uint32_t word = 7;
+        const int ds = wc_plan_debug_status(plan, &word, 1);
+        EXPECT(ds == (debug ? WC_OK : WC_ERR_INVALID_ARG), "wc_plan_debug_status with WC_DEBUG=%d: %d", debug, ds);
+        if (debug) EXPECT(word == 0, "a fresh debug status word reads %u", word);
+        EXPECT(n == 0 || (g_stub.last_status != nullptr) == debug, "the launches' status pointer");
+        EXPECT(wc_plan_debug_status(plan, nullptr, 0) == WC_ERR_INVALID_ARG, "null status");
+    }
     // misaligned and null device pointers are refused
     if (n) {
         EXPECT(wc_decode_async(plan, blob + 1, reinterpret_cast<uint16_t*>(out_al), nullptr) == WC_ERR_INVALID_ARG,
@@ -239,8 +251,10 @@ int main(int argc, char** argv) {
                            kind, (unsigned long long)n, o.group_align, o.group_max_elems, st);
                     if (st != WC_OK) continue;
                     ++containers;
+                    setenv("WC_DEBUG", n % 2 ? "1" : "0", 1);   // debug plans for the odd sizes
                     plan_and_decode(blob, bytes, true);
                     corrupt(r, blob, bytes, metadata_end(blob, bytes), rounds);
+                    unsetenv("WC_DEBUG");
                     wc_free_host(blob);
                 }
             }

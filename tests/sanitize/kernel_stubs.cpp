@@ -30,6 +30,7 @@ void fail(const char* what) {
 void check_common(const wc::DecodeParams& p, uint32_t waves, uint32_t grid) {
     g_stub.last_no_long = p.no_long;
     g_stub.last_one_code = p.one_code;
+    g_stub.last_status = p.status;
     if (!wc::supported_waves(waves)) fail("waves");
     if (grid == 0) fail("empty grid");
     if (p.u_begin >= p.u_end) fail("empty group range");
@@ -69,7 +70,12 @@ hipError_t hipMemcpy(void* dst, const void* src, size_t n, hipMemcpyKind) {
     std::memcpy(dst, src, n);
     return hipSuccess;
 }
+hipError_t hipMemset(void* dst, int v, size_t n) {
+    std::memset(dst, v, n);
+    return hipSuccess;
+}
 hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
+hipError_t hipDeviceSynchronize() { return hipSuccess; }
 }
 
 namespace wc {

@@ -10,5 +10,6 @@ struct StubState {
     int64_t live_allocs = 0;       // "device" allocations not yet freed
     uint32_t last_no_long = 0;     // the last launch's no_long and one_code flags
     uint32_t last_one_code = 0;
+    const uint32_t* last_status = nullptr;   // the last launch's debug status word
 };
 extern StubState g_stub;
