@@ -61,7 +61,10 @@ ROTATE_BYTES = 1 << 30          # rotated (container, output) bytes: 4 x the 256
 CANARY16 = 0x5A5A               # fills timed bf16 outputs before the timed region
 CANARY8 = 0xA5
 CSRC = os.path.join(ROOT, "lossless_entropy_coded_amd", "csrc")
-KERNEL_SOURCES = {"chunks": os.path.join(CSRC, "decode.hip"), "lanes": os.path.join(CSRC, "decode_lanes.hip")}
+# the files each decode kernel is compiled from (a counter record holds while
+# none of them has changed)
+KERNEL_SOURCES = {layout: [os.path.join(CSRC, f) for f in (src, "decode_common.h", "kernels.h")]
+                  for layout, src in (("chunks", "decode.hip"), ("lanes", "decode_lanes.hip"))}
 # counter records per kernel variant: layout, and the coder when not Huffman
 TRAFFIC_FILES = {"chunks": os.path.join(ROOT, "profiles", "decode_chunks_block_8b_traffic.json"),
                  "lanes": os.path.join(ROOT, "profiles", "decode_lanes_block_8b_traffic.json"),
@@ -74,8 +77,12 @@ def variant_of(layout: str, coder: str = "huffman", gap_bits: int = 8) -> str:
 
 
 def kernel_source_sha(layout: str = "chunks") -> str:
-    with open(KERNEL_SOURCES[layout], "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the kernel's source files, in order."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES[layout]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def recorded_traffic(workload: str, layout: str = "chunks", coder: str = "huffman", gap_bits: int = 8):

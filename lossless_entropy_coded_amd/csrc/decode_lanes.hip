@@ -167,9 +167,10 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
     LaneRaw cur_r = load_lane_raw(p, cur_m, min_u64(u, last_u), lane);
     Meta m_next = load_meta(p, min_u64(u + stride, last_u));
     // code planes (Huffman) with one code per entry: the multi-codeword
-    // table is staged as 16-bit entries (un-rotated symbol | length << 8, 0
-    // for a code longer than the index) packed into the first 2^KD / 2 words
-    // of the table's place, a quarter of the LDS bytes per lookup.  (Other
+    // table is staged as 16-bit entries ((32 - length) | un-rotated symbol <<
+    // 8, 0 for a code longer than the index) packed into the first 2^KD / 2
+    // words of the table's place, a quarter of the LDS bytes per lookup.  The
+    // low bits are the alignbit shift that drops the code from a window.  (Other
     // Huffman code planes find the wide table, built by the planner, in the
     // multi-codeword table's place and stage it as it is.)
     if constexpr (kU8 && !kRans) {
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
         auto put = [&](uint32_t i, u32x4 v) {
             if (compact && i < kDecVec) {
                 auto c16 = [](uint32_t x, uint32_t y) {
-                    return x == 0 ? 0u : (unrotate4(y) & 0xFFu) | (((x >> 16) & 0xFFu) << 8);
+                    return x == 0 ? 0u : ((32u - ((x >> 16) & 0xFFu)) & 31u) | (unrotate4(y) & 0xFFu) << 8;
                 };
                 reinterpret_cast<uint32_t*>(s_tab)[i] = c16(v.x, v.y) | c16(v.z, v.w) << 16;
                 return;
@@ -356,8 +357,10 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                     if (one_code) {
                         // the shortest code is longer than half the table
                         // index and no code exceeds 16 bits: every lookup
-                        // yields exactly one code, and four of them fit one
-                        // 64-bit window, read from three staged words.
+                        // yields exactly one code; eight of them fit one
+                        // 96-bit window of four staged words when no code
+                        // exceeds the index, else four fit one 64-bit
+                        // window of three.
                         // Eight lookups make one lane block, stored straight
                         // to memory (block 64k + lane is the lane's k-th: a
                         // wave's store covers 512 contiguous bytes); the
@@ -366,11 +369,43 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                         // decodes up to seven more symbols, never stored; it
                         // still makes at most 64 lookups of at most 16 bits,
                         // so it reads at most word 533 past the pad (byte
-                        // 2136 of the wave's region of 2192).
+                        // 2136 of the wave's region of 2192; with codes of
+                        // at most 11 bits, the 96-bit windows end by word
+                        // 522).
                         uint8_t* const outb = p.out8 + A;
                         const uint32_t full = n / kMergeElems;
                         for (uint32_t q = 0; q < nsym; q += 8) {
                             uint32_t w[2];
+                            if constexpr (!kLong) {
+                                // no code exceeds the 11-bit index: the
+                                // eight codes (at most 88 bits) come from
+                                // one 96-bit window of four staged words,
+                                // held in three registers; each lookup's
+                                // entry shifts them by its code (its low
+                                // bits are 32 - length, alignbit's shift).
+                                // The sum of the eight entries' low bytes is
+                                // that of their 32 - length (at most 208).
+                                const int32_t k = t >> 5;
+                                const uint32_t s1 = sbuf[k + 1], s2 = sbuf[k + 2];
+                                uint32_t hi = __builtin_amdgcn_alignbit(sbuf[k], s1, ~(uint32_t)t);
+                                uint32_t mid = __builtin_amdgcn_alignbit(s1, s2, ~(uint32_t)t);
+                                uint32_t lo = __builtin_amdgcn_alignbit(s2, sbuf[k + 3], ~(uint32_t)t);
+                                uint32_t e[8];
+#pragma unroll
+                                for (uint32_t i = 0; i < 8; ++i) {
+                                    e[i] = s_c16[hi >> (32 - KD)];
+                                    hi = __builtin_amdgcn_alignbit(hi, mid, e[i]);
+                                    mid = __builtin_amdgcn_alignbit(mid, lo, e[i]);
+                                    lo = __builtin_amdgcn_alignbit(lo, 0u, e[i]);
+                                }
+                                // the symbols are the entries' second bytes
+                                w[0] = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0501u) |
+                                       __builtin_amdgcn_perm(e[3], e[2], 0x05010C0Cu);
+                                w[1] = __builtin_amdgcn_perm(e[5], e[4], 0x0C0C0501u) |
+                                       __builtin_amdgcn_perm(e[7], e[6], 0x05010C0Cu);
+                                const uint32_t sum = e[0] + e[1] + e[2] + e[3] + e[4] + e[5] + e[6] + e[7];
+                                t += (int32_t)(256u - (sum & 0xFFu));
+                            } else {
 #pragma unroll
                             for (uint32_t h = 0; h < 2; ++h) {
                                 const int32_t k = t >> 5;
@@ -383,19 +418,18 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                                 for (uint32_t i = 0; i < 4; ++i) {
                                     const uint32_t top = (uint32_t)(win >> 32);
                                     uint32_t e = s_c16[top >> (32 - KD)];
-                                    if constexpr (kLong) {
-                                        if (e == 0) {
-                                            const uint2 l = long_decode_entry<KD>(top, KD + 1, lt);
-                                            e = (unrotate4(l.y) & 0xFFu) | (((l.x >> 16) & 0xFFu) << 8);
-                                        }
+                                    if (e == 0) {
+                                        const uint2 l = long_decode_entry<KD>(top, KD + 1, lt);
+                                        e = ((32u - ((l.x >> 16) & 0xFFu)) & 31u) | (unrotate4(l.y) & 0xFFu) << 8;
                                     }
-                                    acc |= (e & 0xFFu) << (8 * i);
-                                    const uint32_t len = e >> 8;
+                                    acc |= (e >> 8) << (8 * i);
+                                    const uint32_t len = 32u - (e & 31u);
                                     win <<= len;
                                     used += len;
                                 }
                                 t += (int32_t)used;
                                 w[h] = acc;
+                            }
                             }
                             const uint32_t blk = lane + kWaveLanes * (q / kMergeElems);
                             if (blk < full) {
@@ -573,6 +607,9 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
 // 0); a lookup's up to four symbols, shifted to c & 3, join it, the dword at
 // c & ~3 is stored and the part past that dword carries over, also from one
 // phase into the next (the second phase stores symbol c at slot byte c - 32).
+// The shift 8 (c & 3) is kept in a register of its own and advanced by the
+// entry's 8 * (symbol count), which the staging adds to each multi-codeword
+// entry's top byte: that sum, past 31, is also the carry test.
 // Every byte a merge reads lies below the phase's end, in a dword that the
 // last lookup reaching it stored whole; bytes past the lane's symbols are
 // never multiplied.
@@ -634,9 +671,18 @@ __global__ __launch_bounds__(kWaveLanes * W, 6) void decode_lanes_dot_kernel(Dec
     Meta cur_m = m_first;
     LaneRaw cur_r = load_lane_raw(p, cur_m, min_u64(u, last_u), lane);
     Meta m_next = load_meta_scalar(p, min_u64(u + stride, last_u));
+    // multi-codeword entries gain 8 * (symbol count) in their top byte (the
+    // table's own top byte is 0; the rest of the tables are copied as they are)
+    auto put = [&](uint32_t i, u32x4 v) {
+        if (i < kDecVec) {
+            v.x |= (v.x & 0xFF00u) << 19;
+            v.z |= (v.z & 0xFF00u) << 19;
+        }
+        tdst[i] = v;
+    };
 #pragma unroll
-    for (uint32_t k = 0; k < kFull; ++k) tdst[tid + k * kThreads] = stage[k];
-    if (kTail && tid < kTail) tdst[kFull * kThreads + tid] = stage_tail;
+    for (uint32_t k = 0; k < kFull; ++k) put(tid + k * kThreads, stage[k]);
+    if (kTail && tid < kTail) put(kFull * kThreads + tid, stage_tail);
     {
         const uint4* src = reinterpret_cast<const uint4*>(p.tables) + kTabVec;
         for (uint32_t i = tid; i < (p.l2_cap << kL2Bits) / 8; i += kThreads)
@@ -704,6 +750,7 @@ __global__ __launch_bounds__(kWaveLanes * W, 6) void decode_lanes_dot_kernel(Dec
         const uint32_t sbuf_addr = (uint32_t)(uintptr_t)(LdsByte*)(sbuf - 1);   // word -1: the pad's last
         uint32_t a = slot_addr;
         uint32_t acc = 0;
+        uint32_t sh = 0;   // 8 * (a & 3) (the phase change moves a by 32, which keeps it)
         const uint32_t full = n / kMergeElems;
         float acc0 = 0.0f, acc1 = 0.0f;
 #pragma unroll
@@ -718,12 +765,16 @@ __global__ __launch_bounds__(kWaveLanes * W, 6) void decode_lanes_dot_kernel(Dec
                 const LdsWord* const wp = (const LdsWord*)(uintptr_t)waddr;
                 const uint32_t top = __builtin_amdgcn_alignbit(wp[0], wp[1], (uint32_t)nb);
                 uint2 e = s_dec[top >> (32 - KD)];
-                if (e.x == 0) e = long_decode_entry<KD>(top, KD + 1, lt);
-                const uint32_t q = a & 3u;
-                const uint64_t w = (uint64_t)e.y << (q << 3);
+                if (e.x == 0) {
+                    e = long_decode_entry<KD>(top, KD + 1, lt);
+                    e.x |= 8u << 24;
+                }
+                const uint64_t w = (uint64_t)e.y << sh;
                 const uint32_t lo = (uint32_t)w | acc;
-                *(LdsWord*)(uintptr_t)(a - q) = lo;
-                acc = q + ((e.x >> 8) & 0xFFu) >= 4u ? (uint32_t)(w >> 32) : lo;
+                *(LdsWord*)(uintptr_t)(a & ~3u) = lo;
+                const uint32_t s2 = sh + (e.x >> 24);
+                acc = s2 >= 32u ? (uint32_t)(w >> 32) : lo;
+                sh = s2 & 24u;
                 a += (e.x >> 8) & 0xFFu;
                 nb -= (int32_t)((e.x >> 16) & 0xFFu);
             }

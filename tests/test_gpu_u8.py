@@ -102,9 +102,10 @@ def test_u8_workload_full_size(wc, oracle_lib, name):
 def test_u8_one_code_lookups(wc, oracle_lib, sigma, max_len, one_code, longest_over):
     """Code planes whose shortest code is longer than half the 11-bit table
     index never see two codes in one table entry; when no code is longer than
-    16 bits the decoder takes one code per lookup, four per 64-bit window and
-    per aligned word.  The others take the multi-code loop.  Both are
-    bit-exact against the input and the oracle."""
+    16 bits the decoder takes one code per lookup: eight per 96-bit window
+    when none is longer than the index, else four per 64-bit window.  The
+    others take the multi-code loop.  All are bit-exact against the input and
+    the oracle."""
     from container_view import sections
     from lossless_entropy_coded_amd.synth import quantized_codes
     rng = np.random.default_rng(int(sigma * 10) + max_len)
