@@ -454,63 +454,98 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                         // so far (its other bytes 0); a lookup's symbols,
                         // shifted to c & 3, join it, the word at c & ~3 is
                         // stored and the part past that word carries over.
+                        // Two phases of 32 symbols (the lane's blocks 0..3,
+                        // then 4..7), each stored to memory right after it,
+                        // share a 36-byte slot (symbol c of phase h at byte
+                        // c - 32h), so that three 8-wave workgroups fit a
+                        // compute unit.  A lookup starts only below its
+                        // phase's end and adds at most three symbols, so a
+                        // phase's stores end by byte 35; the bytes it carries
+                        // past 32 go on in `acc` (32 is a multiple of 4).
+                        // With the phase's end a multiple of 4, every symbol
+                        // below it is stored once the phase ends.
                         const uint32_t* const s_wide = reinterpret_cast<const uint32_t*>(s_tab);
                         constexpr uint32_t KW = KD + 1;
-                        uint32_t c = 0, acc = 0;
+                        int32_t c = 0;
+                        uint32_t acc = 0;
                         auto put = [&](uint32_t e) {
-                            const uint32_t q = c & 3u;
+                            const uint32_t q = (uint32_t)c & 3u;
                             const uint32_t ns = (e >> 5) & 3u;
                             const uint64_t w = (uint64_t)(e >> 8) << (q << 3);
                             const uint32_t lo = (uint32_t)w | acc;
-                            *reinterpret_cast<uint32_t*>(slot + (c - q)) = lo;
+                            *reinterpret_cast<uint32_t*>(slot + (c - (int32_t)q)) = lo;
                             acc = q + ns >= 4u ? (uint32_t)(w >> 32) : lo;
-                            c += ns;
+                            c += (int32_t)ns;
                         };
-                        if constexpr (!kLong) {
-                            // every code fits the index (and the code is
-                            // complete, so every entry holds one at least):
-                            // four lookups of at most KW bits per 64-bit
-                            // window, read from three staged words.  A lane
-                            // enters with c <= 63 and four lookups add at
-                            // most 12 symbols, so its stores end by byte 75
-                            // of its 76-byte slot; it makes at most 64
-                            // lookups of at most 12 bits (at most word 524
-                            // of the wave's staging and slots).
-                            while (c < nsym) {
-                                const int32_t k = t >> 5;
-                                const uint32_t w1 = sbuf[k + 1];
-                                uint64_t win =
-                                    (uint64_t)__builtin_amdgcn_alignbit(sbuf[k], w1, ~(uint32_t)t) << 32 |
-                                    __builtin_amdgcn_alignbit(w1, sbuf[k + 2], ~(uint32_t)t);
-                                uint32_t used = 0;
+                        uint8_t* const outb = p.out8 + A;
+                        const uint32_t full = n / kMergeElems;
 #pragma unroll
-                                for (uint32_t i = 0; i < 4; ++i) {
-                                    const uint32_t e = s_wide[(uint32_t)(win >> 32) >> (32 - KW)];
+                        for (uint32_t h = 0; h < 2; ++h) {
+                            const int32_t end = (int32_t)min(nsym, kWidePhase * (h + 1)) - (int32_t)(kWidePhase * h);
+                            if constexpr (!kLong) {
+                                // every code fits the index (and the code is
+                                // complete, so every entry holds one at
+                                // least): up to four lookups of at most KW
+                                // bits per 64-bit window, read from three
+                                // staged words.  A lane makes at most 64
+                                // lookups of at most 12 bits (at most word
+                                // 524 of the wave's staging and slots).
+                                while (c < end) {
+                                    const int32_t k = t >> 5;
+                                    const uint32_t w1 = sbuf[k + 1];
+                                    uint64_t win =
+                                        (uint64_t)__builtin_amdgcn_alignbit(sbuf[k], w1, ~(uint32_t)t) << 32 |
+                                        __builtin_amdgcn_alignbit(w1, sbuf[k + 2], ~(uint32_t)t);
+                                    uint32_t used = 0;
+#pragma unroll
+                                    for (uint32_t i = 0; i < 4; ++i) {
+                                        if (i == 0 || c < end) {
+                                            const uint32_t e = s_wide[(uint32_t)(win >> 32) >> (32 - KW)];
+                                            put(e);
+                                            const uint32_t nb = e & 31u;
+                                            win <<= nb;
+                                            used += nb;
+                                        }
+                                    }
+                                    t += (int32_t)used;
+                                }
+                            } else {
+                                // codes longer than the index: one lookup
+                                // per window, re-read at every lookup (a
+                                // long code takes up to 24 bits).
+                                while (c < end) {
+                                    const int32_t k = t >> 5;
+                                    const uint32_t top =
+                                        __builtin_amdgcn_alignbit(sbuf[k], sbuf[k + 1], ~(uint32_t)t);
+                                    uint32_t e = s_wide[top >> (32 - KW)];
+                                    if (e == 0) {
+                                        const uint2 l = long_decode_entry<KD>(top, KD + 1, lt);
+                                        e = ((l.x >> 16) & 31u) | 1u << 5 | (unrotate4(l.y) & 0xFFu) << 8;
+                                    }
                                     put(e);
-                                    const uint32_t nb = e & 31u;
-                                    win <<= nb;
-                                    used += nb;
+                                    t += (int32_t)(e & 31u);
                                 }
-                                t += (int32_t)used;
                             }
-                        } else {
-                            // codes longer than the index: one lookup per
-                            // window, re-read at every lookup (a long code
-                            // takes up to 24 bits); the last word ends by
-                            // byte 67.
-                            while (c < nsym) {
-                                const int32_t k = t >> 5;
-                                const uint32_t top = __builtin_amdgcn_alignbit(sbuf[k], sbuf[k + 1], ~(uint32_t)t);
-                                uint32_t e = s_wide[top >> (32 - KW)];
-                                if (e == 0) {
-                                    const uint2 l = long_decode_entry<KD>(top, KD + 1, lt);
-                                    e = ((l.x >> 16) & 31u) | 1u << 5 | (unrotate4(l.y) & 0xFFu) << 8;
+                            // the container's last, partial block may end
+                            // inside a word still held in acc
+                            if (c & 3) *reinterpret_cast<uint32_t*>(slot + (c & ~3)) = acc;
+                            wave_lds_order();
+#pragma unroll
+                            for (uint32_t i = 0; i < kMergeSteps / 2; ++i) {
+                                const uint32_t blk = lane + kWaveLanes * (kMergeSteps / 2 * h + i);
+                                if (blk < full) {
+                                    const uint2 e2 = load_slot8(slot + kMergeElems * i);
+                                    u32x2 v;
+                                    v.x = e2.x;
+                                    v.y = e2.y;
+                                    __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(outb + kMergeElems * blk));
                                 }
-                                put(e);
-                                t += (int32_t)(e & 31u);
+                            }
+                            if (h == 0) {
+                                c -= (int32_t)kWidePhase;
+                                wave_lds_order();   // the second phase rewrites the slot
                             }
                         }
-                        if (c & 3u) *reinterpret_cast<uint32_t*>(slot + (c & ~3u)) = acc;
                     }
                 };
                 if (p.no_long)
@@ -535,7 +570,7 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
 #pragma unroll
             for (uint32_t k = 0; k < kMergeSteps; ++k) {
                 const uint32_t blk = lane + k * kWaveLanes;
-                if (!one_code && blk < full) {   // one code per entry: stored by the decode
+                if (kRans && blk < full) {   // Huffman code planes: stored by the decode
                     const uint2 e2 = load_slot8(slot + kMergeElems * k);
                     u32x2 v;
                     v.x = kRans ? unrotate4(e2.x) : e2.x;
@@ -566,7 +601,9 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
         // `full` is the (full / 64)-th of lane full % 64
         if (kU8 && !one_code && full * kMergeElems < n && lane == 0) {
             const uint32_t rel = kMergeElems * full;
-            const uint2 e2 = load_slot8(ebuf + slot_bytes * (full % kWaveLanes) + kMergeElems * (full / kWaveLanes));
+            // (the wide table's slots hold one phase of four blocks)
+            const uint32_t at = wide ? (full / kWaveLanes) % (kMergeSteps / 2) : full / kWaveLanes;
+            const uint2 e2 = load_slot8(ebuf + slot_bytes * (full % kWaveLanes) + kMergeElems * at);
             const uint32_t o[2] = {kRans ? unrotate4(e2.x) : e2.x, kRans ? unrotate4(e2.y) : e2.y};
 #pragma unroll
             for (uint32_t i = 0; i < kMergeElems; ++i)

@@ -131,11 +131,13 @@ constexpr uint32_t kLaneWaveBytes = kLanePadBytes + kLaneStageBytes + kWaveLanes
 // Code planes with one code per table entry write their bytes straight to
 // memory and need no slots: a wave's region is the pad, the staging and 128
 // bytes a lane's last 64-bit windows may read past the staging.  Other code
-// planes take the wide table (up to three codes per lookup, four lookups per
-// window) and 76-byte slots (19 dwords, odd): four lookups from a lane's 63rd
-// symbol may store up to byte 75.
+// planes take the wide table (up to three codes per lookup, up to four
+// lookups per window) in two phases of 32 symbols sharing a 36-byte slot (9
+// dwords, odd): a lookup starts below its phase's 32nd symbol, so it stores
+// up to byte 35.
 constexpr uint32_t kLaneCompactWaveBytes = kLanePadBytes + kLaneStageBytes + 128;
-constexpr uint32_t kLaneWideSlotBytes = 76;
+constexpr uint32_t kWidePhase = 32;                 // symbols per lane and phase on the wide table
+constexpr uint32_t kLaneWideSlotBytes = kWidePhase + 4;
 constexpr uint32_t kLaneWideWaveBytes = kLanePadBytes + kLaneStageBytes + kWaveLanes * kLaneWideSlotBytes;
 enum LaneLds : uint32_t { kLdsSlots = 0, kLdsCompact = 1, kLdsWide = 2 };
 inline uint32_t lane_wave_bytes(LaneLds layout) {
