@@ -466,15 +466,17 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                         // below it is stored once the phase ends.
                         const uint32_t* const s_wide = reinterpret_cast<const uint32_t*>(s_tab);
                         constexpr uint32_t KW = KD + 1;
+                        // (sh = 8 (c & 3), kept in a register of its own)
                         int32_t c = 0;
-                        uint32_t acc = 0;
+                        uint32_t acc = 0, sh = 0;
                         auto put = [&](uint32_t e) {
-                            const uint32_t q = (uint32_t)c & 3u;
                             const uint32_t ns = (e >> 5) & 3u;
-                            const uint64_t w = (uint64_t)(e >> 8) << (q << 3);
+                            const uint64_t w = (uint64_t)(e >> 8) << sh;
                             const uint32_t lo = (uint32_t)w | acc;
-                            *reinterpret_cast<uint32_t*>(slot + (c - (int32_t)q)) = lo;
-                            acc = q + ns >= 4u ? (uint32_t)(w >> 32) : lo;
+                            *reinterpret_cast<uint32_t*>(slot + (c & ~3)) = lo;
+                            const uint32_t s2 = sh + 8u * ns;
+                            acc = s2 >= 32u ? (uint32_t)(w >> 32) : lo;
+                            sh = s2 & 24u;
                             c += (int32_t)ns;
                         };
                         uint8_t* const outb = p.out8 + A;
