@@ -122,6 +122,28 @@ def test_u8_one_code_lookups(wc, oracle_lib, sigma, max_len, one_code, longest_o
     assert np.array_equal(got, oracle_lib.decode_u8(blob))
 
 
+@pytest.mark.parametrize("sigma,max_len,one_code", [(20.0, 10, True), (3.0, 10, False)])
+def test_u8_ten_bit_index(wc, oracle_lib, monkeypatch, sigma, max_len, one_code):
+    """With a 10-bit table index (WC_DECODE_BITS=10) and no code longer than
+    it: int8-like planes take the one-code path with eight codes (at most 80
+    bits) per 96-bit window, int4-like planes the wide table (11-bit index)
+    in two phases.  Bit-exact against the input and the oracle."""
+    from container_view import sections
+    from lossless_entropy_coded_amd.synth import quantized_codes
+    monkeypatch.setenv("WC_DECODE_BITS", "10")
+    rng = np.random.default_rng(int(sigma * 100) + max_len)
+    c = quantized_codes(rng, 250_000, 8, sigma)
+    blob = wc.encode_u8_host([c], max_code_len=max_len)
+    lens = sections(blob)["code_len"]
+    with wc.Plan(blob) as plan:
+        assert plan.stats()["decode_bits"] == 10
+    assert int(lens.max()) <= 10 and (2 * int(lens[lens > 0].min()) > 10) == one_code
+    log(f"case: u8 ten-bit index sigma={sigma} one_code={one_code}")
+    got = gpu_decode_u8(wc, blob)
+    assert np.array_equal(got, c)
+    assert np.array_equal(got, oracle_lib.decode_u8(blob))
+
+
 @pytest.mark.parametrize("name", ["int8_codes_8b", "int4_codes_8b"])
 def test_u8_corrupted_stream_stays_in_bounds(wc, name):
     from container_view import sections
