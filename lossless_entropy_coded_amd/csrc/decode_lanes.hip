@@ -529,8 +529,11 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                                 }
                             }
                             // the container's last, partial block may end
-                            // inside a word still held in acc
-                            if (c & 3) *reinterpret_cast<uint32_t*>(slot + (c & ~3)) = acc;
+                            // inside a word still held in acc (a lane with
+                            // no symbols in this phase has c <= 0 and
+                            // nothing to add: its slot offset would be
+                            // negative)
+                            if (c > 0 && (c & 3)) *reinterpret_cast<uint32_t*>(slot + (c & ~3)) = acc;
                             wave_lds_order();
 #pragma unroll
                             for (uint32_t i = 0; i < kMergeSteps / 2; ++i) {

@@ -144,6 +144,29 @@ def test_u8_ten_bit_index(wc, oracle_lib, monkeypatch, sigma, max_len, one_code)
     assert np.array_equal(got, oracle_lib.decode_u8(blob))
 
 
+@pytest.mark.parametrize("sigma", [3.0, 20.0])
+def test_u8_small_segments_every_tail(wc, oracle_lib, sigma):
+    """Single-segment containers of 8 * full + r codes for every tail length
+    r and full blocks on either side of each lane and phase boundary: the
+    lanes after the one holding the partial last block have fewer symbols
+    (none in the second phase), and nothing they do may touch the partial
+    block's bytes."""
+    from lossless_entropy_coded_amd.synth import quantized_codes
+    rng = np.random.default_rng(int(sigma) + 77)
+    fulls = [0, 1, 5, 36, 63, 64, 65, 100, 127, 200, 255, 256, 257, 300, 447, 510]
+    log(f"case: u8 small segments sigma={sigma}: n = 8 * full + r, full in {fulls}, r in 0..7")
+    for full in fulls:
+        for r in range(8):
+            n = 8 * full + r
+            if n == 0:
+                continue
+            c = quantized_codes(rng, n, 8, sigma)
+            blob = wc.encode_u8_host([c])
+            got = gpu_decode_u8(wc, blob)
+            assert np.array_equal(got, c), f"n = {n} (full {full}, tail {r}), sigma {sigma}"
+    assert np.array_equal(oracle_lib.decode_u8(blob), c)
+
+
 @pytest.mark.parametrize("name", ["int8_codes_8b", "int4_codes_8b"])
 def test_u8_corrupted_stream_stays_in_bounds(wc, name):
     from container_view import sections
