@@ -237,6 +237,16 @@ def test_stream_reference_argument_checks_without_device(wc):
     assert call(vp(0), 16, vp(fake), 16, vp(0)) == wc.WC_ERR_INVALID_ARG
 
 
+def test_debug_status_argument_checks_without_device(wc):
+    """wc_plan_debug_status refuses a NULL plan or status pointer before any
+    HIP call (a plan made without WC_DEBUG is refused too: GPU tests)."""
+    import ctypes
+    word = ctypes.c_uint32(7)
+    assert wc._lib.wc_plan_debug_status(None, ctypes.byref(word), 0) == wc.WC_ERR_INVALID_ARG
+    assert wc._lib.wc_plan_debug_status(None, None, 1) == wc.WC_ERR_INVALID_ARG
+    assert word.value == 7
+
+
 def test_gemv_argument_checks_without_device(wc):
     """Size and alignment checks of wc_gemv_bf16_async return before any HIP call."""
     import ctypes
