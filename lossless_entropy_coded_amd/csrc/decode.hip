@@ -68,8 +68,9 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 
 // Raw loads of one lane for one group: the stream bytes of its two chunks
 // a = c0 + 2t and a + 1 plus the lookahead of the second (20 bytes from 8a),
-// and both gaps (packed gaps: the three bytes holding bits 5a .. 5a + 9).  The group's chunks c0 .. c1 (c0 = p0 / 64, c1 = (p1 - 1) /
-// 64) start at any chunk, so the 20 bytes are taken from two aligned 16-byte
+// and both gaps (packed gaps: the three bytes holding bits 5a .. 5a + 9).
+// The group's chunks c0 .. c1 (c0 = p0 / 64, c1 = (p1 - 1) / 64) start at
+// any chunk, so the 20 bytes are taken from two aligned 16-byte
 // loads at 8 * (a rounded down to even) (of 16 and 12 bytes); the parity of a
 // is that of c0, the same for every lane.  Both loads stay inside the
 // container: they end at most 4 bytes past the stream section, which is

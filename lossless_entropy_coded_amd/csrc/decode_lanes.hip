@@ -377,14 +377,15 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                         for (uint32_t q = 0; q < nsym; q += 8) {
                             uint32_t w[2];
                             if constexpr (!kLong) {
-                                // no code exceeds the 11-bit index: the
-                                // eight codes (at most 88 bits) come from
-                                // one 96-bit window of four staged words,
-                                // held in three registers; each lookup's
-                                // entry shifts them by its code (its low
-                                // bits are 32 - length, alignbit's shift).
-                                // The sum of the eight entries' low bytes is
-                                // that of their 32 - length (at most 208).
+                                // no code exceeds the table index (KD <=
+                                // 11 bits): the eight codes (at most 88
+                                // bits) come from one 96-bit window of four
+                                // staged words, held in three registers;
+                                // each lookup's entry shifts them by its
+                                // code (its low bits are 32 - length,
+                                // alignbit's shift).  The sum of the eight
+                                // entries' low bytes is that of their
+                                // 32 - length (each at most 26: at most 208).
                                 const int32_t k = t >> 5;
                                 const uint32_t s1 = sbuf[k + 1], s2 = sbuf[k + 2];
                                 uint32_t hi = __builtin_amdgcn_alignbit(sbuf[k], s1, ~(uint32_t)t);
@@ -407,29 +408,29 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                                 t += (int32_t)(256u - (sum & 0xFFu));
                             } else {
 #pragma unroll
-                            for (uint32_t h = 0; h < 2; ++h) {
-                                const int32_t k = t >> 5;
-                                const uint32_t w1 = sbuf[k + 1];
-                                uint64_t win =
-                                    (uint64_t)__builtin_amdgcn_alignbit(sbuf[k], w1, ~(uint32_t)t) << 32 |
-                                    __builtin_amdgcn_alignbit(w1, sbuf[k + 2], ~(uint32_t)t);
-                                uint32_t acc = 0, used = 0;
+                                for (uint32_t h = 0; h < 2; ++h) {
+                                    const int32_t k = t >> 5;
+                                    const uint32_t w1 = sbuf[k + 1];
+                                    uint64_t win =
+                                        (uint64_t)__builtin_amdgcn_alignbit(sbuf[k], w1, ~(uint32_t)t) << 32 |
+                                        __builtin_amdgcn_alignbit(w1, sbuf[k + 2], ~(uint32_t)t);
+                                    uint32_t acc = 0, used = 0;
 #pragma unroll
-                                for (uint32_t i = 0; i < 4; ++i) {
-                                    const uint32_t top = (uint32_t)(win >> 32);
-                                    uint32_t e = s_c16[top >> (32 - KD)];
-                                    if (e == 0) {
-                                        const uint2 l = long_decode_entry<KD>(top, KD + 1, lt);
-                                        e = ((32u - ((l.x >> 16) & 0xFFu)) & 31u) | (unrotate4(l.y) & 0xFFu) << 8;
+                                    for (uint32_t i = 0; i < 4; ++i) {
+                                        const uint32_t top = (uint32_t)(win >> 32);
+                                        uint32_t e = s_c16[top >> (32 - KD)];
+                                        if (e == 0) {
+                                            const uint2 l = long_decode_entry<KD>(top, KD + 1, lt);
+                                            e = ((32u - ((l.x >> 16) & 0xFFu)) & 31u) | (unrotate4(l.y) & 0xFFu) << 8;
+                                        }
+                                        acc |= (e >> 8) << (8 * i);
+                                        const uint32_t len = 32u - (e & 31u);
+                                        win <<= len;
+                                        used += len;
                                     }
-                                    acc |= (e >> 8) << (8 * i);
-                                    const uint32_t len = 32u - (e & 31u);
-                                    win <<= len;
-                                    used += len;
+                                    t += (int32_t)used;
+                                    w[h] = acc;
                                 }
-                                t += (int32_t)used;
-                                w[h] = acc;
-                            }
                             }
                             const uint32_t blk = lane + kWaveLanes * (q / kMergeElems);
                             if (blk < full) {
@@ -617,7 +618,8 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
         if (kMode == kLanesToBf16 && full * kMergeElems < n && lane == 0) {
             const uint32_t rel = kMergeElems * full;
             const uint2 s2 = load_nt8(p.sm + A + rel);
-            const uint2 e2 = load_slot8(ebuf + kLaneSlotBytes * (full % kWaveLanes) + kMergeElems * (full / kWaveLanes));
+            const uint2 e2 =
+                load_slot8(ebuf + kLaneSlotBytes * (full % kWaveLanes) + kMergeElems * (full / kWaveLanes));
             uint32_t o[4];
             join4(s2.x, e2.x, o[0], o[1]);
             join4(s2.y, e2.y, o[2], o[3]);

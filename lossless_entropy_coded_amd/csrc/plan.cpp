@@ -134,7 +134,8 @@ int parse_and_validate(const uint8_t* b, uint64_t bytes, Header& h, std::vector<
     // sections: 256-byte aligned, in order, non-overlapping, inside total_bytes
     if (h.n_tensors > (1u << 24)) return WC_ERR_SECTION_BOUNDS;
     const uint64_t off[6] = {h.off_code_len, h.off_tensors, h.off_groups, h.off_gap, h.off_stream, h.off_sm};
-    const uint64_t len[6] = {wc::code_section_bytes(h.coder), 16ull * h.n_tensors, wc::kGroupEntryBytes * (h.n_groups + 1),
+    const uint64_t len[6] = {wc::code_section_bytes(h.coder), 16ull * h.n_tensors,
+                             wc::kGroupEntryBytes * (h.n_groups + 1),
                              lanes ? 2ull * wc::kLanes * h.n_groups : wc::gap_section_bytes(h.n_chunks, h.gap_bits),
                              h.stream_bytes,
                              h.elem_kind == wc::kKindBf16 ? h.n_elems : 0};
@@ -608,8 +609,8 @@ extern "C" int wc_decode_u8_async(const wc_plan_t* p, const void* blob_dev, uint
     d.one_code = p->one_code ? 1u : 0u;
     d.no_long = p->no_long ? 1u : 0u;
     d.status = p->d_status;
-    const hipError_t e = wc::launch_decode_lanes(d, p->decode_bits, p->busy.waves, p->busy.grid, wc::kLanesToU8, p->rans,
-                                                 static_cast<hipStream_t>(stream));
+    const hipError_t e = wc::launch_decode_lanes(d, p->decode_bits, p->busy.waves, p->busy.grid, wc::kLanesToU8,
+                                                 p->rans, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? WC_OK : WC_ERR_HIP;
 }
 
