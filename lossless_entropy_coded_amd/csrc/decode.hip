@@ -244,8 +244,10 @@ __global__ __launch_bounds__(kWaveLanes * W, kDot ? 4 : 1) void decode_kernel(De
     // workgroup's staging, are in flight together; the first group's stream
     // loads are issued before the tables are written to LDS.  The barrier
     // after the staging is the only point where the waves of a workgroup wait
-    // for each other.
-    const Meta m_first = load_meta(p, min_u64(u, last_u));
+    // for each other.  Group table entries come through the scalar data
+    // cache (measured faster here than vector loads that every lane takes;
+    // the lanes kernel's plain decode measured the other way).
+    const Meta m_first = load_meta_scalar(p, min_u64(u, last_u));
     constexpr uint32_t kFull = kTabVec / kThreads;          // staging rounds every lane takes part in
     constexpr uint32_t kTail = kTabVec - kFull * kThreads;  // pieces of the last, partial round
     const u32x4* const tsrc = reinterpret_cast<const u32x4*>(p.tables);
@@ -255,9 +257,9 @@ __global__ __launch_bounds__(kWaveLanes * W, kDot ? 4 : 1) void decode_kernel(De
     for (uint32_t k = 0; k < kFull; ++k) stage[k] = tsrc[tid + k * kThreads];
     u32x4 stage_tail = {0, 0, 0, 0};
     if (kTail && tid < kTail) stage_tail = tsrc[kFull * kThreads + tid];
-    const Meta m0 = uniform_meta(m_first);
+    const Meta& m0 = m_first;
     const Raw r0 = load_raw(p, m0, lane);
-    Meta m_next = load_meta(p, min_u64(u + stride, last_u));
+    Meta m_next = load_meta_scalar(p, min_u64(u + stride, last_u));
 #pragma unroll
     for (uint32_t k = 0; k < kFull; ++k) tdst[tid + k * kThreads] = stage[k];
     if (kTail && tid < kTail) tdst[kFull * kThreads + tid] = stage_tail;
@@ -279,7 +281,6 @@ __global__ __launch_bounds__(kWaveLanes * W, kDot ? 4 : 1) void decode_kernel(De
 
     Unit cur = make_unit(r0, m0, lane);
     Meta cur_meta = m0;
-    m_next = uniform_meta(m_next);
     uint32_t dot_mat = 0;   // fused product: matrix of the wave's current group
 
     for (;;) {
@@ -310,7 +311,7 @@ __global__ __launch_bounds__(kWaveLanes * W, kDot ? 4 : 1) void decode_kernel(De
             load_dot_x(dr, n_unit, lane, 0, xv);
         }
 
-        const Meta m_after = load_meta(p, min_u64(un + stride, last_u));
+        const Meta m_after = load_meta_scalar(p, min_u64(un + stride, last_u));
 
         // The phases over one pass of chains: lane t's chains are the pass's
         // chunks 2t and 2t + 1; their output starts at `base` inside the
@@ -449,7 +450,7 @@ __global__ __launch_bounds__(kWaveLanes * W, kDot ? 4 : 1) void decode_kernel(De
         // the wait there cover the merge stores as well)
         const Unit next = make_unit(nxt, m_next, lane);
         const Meta next_meta = m_next;
-        m_next = uniform_meta(m_after);
+        m_next = m_after;
         wave_lds_order();
 #pragma unroll
         for (uint32_t k = 0; k < kMergeSteps; ++k)

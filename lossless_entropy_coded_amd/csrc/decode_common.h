@@ -103,6 +103,20 @@ __device__ __forceinline__ Meta load_meta(const DecodeParams& p, uint64_t u) {
     return m;
 }
 
+// A group's or segment's entry pair read through the scalar data cache (the
+// table is read-only while a kernel runs, and the index is uniform): the
+// entries land in scalar registers, not in every lane's vector registers.
+__device__ __forceinline__ Meta load_meta_scalar(const DecodeParams& p, uint64_t u) {
+    typedef __attribute__((address_space(4))) const uint32_t* ConstU32;
+    const ConstU32 g = (ConstU32)(uintptr_t)(p.groups + 2 * u);
+    Meta m;
+    m.e0 = ((uint64_t)g[1] << 32) | g[0];
+    m.p0 = ((uint64_t)g[3] << 32) | g[2];
+    m.e1 = ((uint64_t)g[5] << 32) | g[4];
+    m.p1 = ((uint64_t)g[7] << 32) | g[6];
+    return m;
+}
+
 __device__ __forceinline__ Meta uniform_meta(const Meta& m) {
     Meta r;
     r.e0 = uniform64(m.e0);

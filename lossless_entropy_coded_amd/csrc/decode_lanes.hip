@@ -657,20 +657,6 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
 // Every byte a merge reads lies below the phase's end, in a dword that the
 // last lookup reaching it stored whole; bytes past the lane's symbols are
 // never multiplied.
-// A segment's entry pair read through the scalar data cache (the table is
-// read-only while the kernel runs, and the segment index is uniform): the
-// entries land in scalar registers, not in every lane's vector registers.
-__device__ __forceinline__ Meta load_meta_scalar(const DecodeParams& p, uint64_t u) {
-    typedef __attribute__((address_space(4))) const uint32_t* ConstU32;
-    const ConstU32 g = (ConstU32)(uintptr_t)(p.groups + 2 * u);
-    Meta m;
-    m.e0 = ((uint64_t)g[1] << 32) | g[0];
-    m.p0 = ((uint64_t)g[3] << 32) | g[2];
-    m.e1 = ((uint64_t)g[5] << 32) | g[4];
-    m.p1 = ((uint64_t)g[7] << 32) | g[6];
-    return m;
-}
-
 constexpr uint32_t kDotHalf = 32;                 // symbols per lane and phase
 constexpr uint32_t kDotSlotBytes = kDotHalf + 4;  // 9 dwords: an odd stride across the LDS banks
 constexpr uint32_t kDotSteps = kMergeSteps / 2;   // merge steps per phase
