@@ -51,6 +51,7 @@ struct wc_plan_s {
     bool lanes = false;          // container version 3 (interleaved lanes)
     bool rans = false;           // coder rANS (version 3)
     bool one_code = false;       // Huffman: one code per table entry at most, none longer than 16 bits
+    bool single_table = false;   // code planes: the first-code table in the multi-codeword table's place
     bool no_long = false;        // Huffman: no code longer than decode_bits
     uint32_t launch_rounds = 0;  // plain decode: segment rounds per launch at most (0: one launch)
     uint32_t* d_tables = nullptr;
@@ -263,15 +264,11 @@ struct DeviceGuard {
 
 }  // namespace
 
-// The wide decode table of Huffman code planes: for each `bits`-bit window,
-// up to three whole codes from its start, as total bits | count << 5 |
-// symbols << 8 (first code in the low byte), or 0 when the window's first
-// code is longer than the window.  Codes are canonical (shorter codes
-// numerically smaller, equal lengths in symbol order).
-static void build_wide_table(const uint8_t* lens, uint32_t bits, uint32_t* out) {
-    const uint32_t size = 1u << bits;
-    // first[w]: the window's first code, symbol | length << 8 (0: longer than the window)
-    std::vector<uint32_t> first(size, 0u);
+// For each `bits`-bit window, the code it starts with, as symbol | length
+// << 8, or 0 when that code is longer than the window.  Codes are canonical
+// (shorter codes numerically smaller, equal lengths in symbol order).
+static std::vector<uint32_t> first_codes(const uint8_t* lens, uint32_t bits) {
+    std::vector<uint32_t> first(1u << bits, 0u);
     uint32_t count[wc::kMaxCodeLen + 2] = {0};
     for (int s = 0; s < 256; ++s) count[lens[s]] += lens[s] != 0;
     uint32_t next[wc::kMaxCodeLen + 2] = {0};
@@ -286,6 +283,16 @@ static void build_wide_table(const uint8_t* lens, uint32_t bits, uint32_t* out) 
             const uint32_t lo = code << (bits - L), hi = (code + 1) << (bits - L);
             for (uint32_t w = lo; w < hi; ++w) first[w] = (uint32_t)s | L << 8;
         }
+    return first;
+}
+
+// The wide decode table of Huffman code planes: for each `bits`-bit window,
+// up to three whole codes from its start, as total bits | count << 5 |
+// symbols << 8 (first code in the low byte), or 0 when the window's first
+// code is longer than the window.
+static void build_wide_table(const uint8_t* lens, uint32_t bits, uint32_t* out) {
+    const uint32_t size = 1u << bits;
+    const std::vector<uint32_t> first = first_codes(lens, bits);
     for (uint32_t w = 0; w < size; ++w) {
         uint32_t pos = 0, n = 0, syms = 0;
         while (n < 3 && pos < bits) {
@@ -297,6 +304,19 @@ static void build_wide_table(const uint8_t* lens, uint32_t bits, uint32_t* out) 
             pos += L;
         }
         out[w] = n ? pos | n << 5 | syms << 8 : 0u;
+    }
+}
+
+// The first-code table: the multi-codeword table's entry format (two words
+// per `bits`-bit window: (32 - length) | count << 8 | length << 16, then the
+// symbols rotated right by one bit) with each window's first code alone, or
+// 0 when it is longer than the window.
+static void build_single_table(const uint8_t* lens, uint32_t bits, uint32_t* out) {
+    const std::vector<uint32_t> first = first_codes(lens, bits);
+    for (uint32_t w = 0; w < first.size(); ++w) {
+        const uint32_t L = first[w] >> 8, sym = first[w] & 0xFFu;
+        out[2 * w] = first[w] ? ((32u - L) & 31u) | 1u << 8 | L << 16 : 0u;
+        out[2 * w + 1] = first[w] ? ((sym >> 1) | (sym & 1u) << 7) : 0u;
     }
 }
 
@@ -350,9 +370,6 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         p->decode_bits = 11;
     }
     if (!p->rans) {
-        // no multi-codeword table entry holds two whole codes when the
-        // shortest code is longer than half the table index; four codes of at
-        // most 16 bits fit one 64-bit window
         uint32_t shortest = 0, longest = 0, present = 0;
         for (int s = 0; s < 256; ++s) {
             const uint32_t L = blob_host[p->h.off_code_len + s];
@@ -360,12 +377,22 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
             longest = std::max(longest, L);
             present += L != 0;
         }
-        p->one_code = shortest && 2 * shortest > p->decode_bits && longest <= 16;
         // Without the long-code lookup every table entry must decode at least
         // one code, i.e. the code must be complete: a single symbol's code
         // "0" leaves the windows that start with 1 undecodable, and a lookup
         // there would not advance (the long-code lookup always does).
         p->no_long = present >= 2 && longest <= p->decode_bits;
+        // One code per lookup: no multi-codeword table entry holds two whole
+        // codes when the shortest code is longer than half the table index
+        // (four codes of at most 16 bits fit one 64-bit window).  Code planes
+        // whose codes all fit the index take one code per lookup whatever
+        // their shortest code, from the first-code table: on int4 pairs
+        // (shortest codes of 4 bits) eight codes per 96-bit window decode
+        // faster than the wide table's up to three per lookup.
+        // WC_FIRST_CODE_TABLE=0 keeps the wide table for them.
+        const bool single = p->h.elem_kind == wc::kKindU8 && p->no_long && env_u32("WC_FIRST_CODE_TABLE", 1) != 0;
+        p->one_code = shortest && longest <= 16 && (2 * shortest > p->decode_bits || single);
+        p->single_table = p->one_code && 2 * shortest <= p->decode_bits;
     }
     {
         const uint32_t forced_waves = env_u32("WC_WAVES", 0);
@@ -485,6 +512,15 @@ extern "C" int wc_plan(const uint8_t* blob_host, uint64_t blob_bytes, int hip_de
         wc::CodeLens lens;
         std::memcpy(lens.len, blob_host + p->h.off_code_len, 256);
         te = wc::launch_build_tables(lens, p->count_bits, p->decode_bits, p->d_tables, nullptr);
+        if (te == hipSuccess && p->single_table) {
+            // in the multi-codeword table's place, after its build
+            std::vector<uint32_t> single(2u << p->decode_bits);
+            build_single_table(lens.len, p->decode_bits, single.data());
+            te = hipStreamSynchronize(nullptr);
+            if (te == hipSuccess)
+                te = hipMemcpy(p->d_tables + (1u << p->count_bits), single.data(), single.size() * 4,
+                               hipMemcpyHostToDevice);
+        }
         if (te == hipSuccess && layout == wc::kLdsWide) {
             // the wide table of code planes, at the multi-codeword table's
             // place (2^(decode_bits + 1) 4-byte entries: the same bytes)

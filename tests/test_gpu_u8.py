@@ -78,34 +78,48 @@ def test_u8_segment_shapes(wc, oracle_lib, A, M, B):
         assert np.array_equal(gpu_decode_u8(wc, blob), wl.codes)
 
 
-@pytest.mark.parametrize("name", ["int8_codes_8b", "int4_codes_8b"])
-def test_u8_workload_full_size(wc, oracle_lib, name):
+@pytest.mark.parametrize("name,first_code_table", [
+    ("int8_codes_8b", "1"), ("int4_codes_8b", "1"), ("int4_codes_8b", "0")])
+def test_u8_workload_full_size(wc, oracle_lib, monkeypatch, name, first_code_table):
     """The full 8B-shape code planes (218 M int8 codes; 109 M bytes of int4
-    pairs), one launch each, against the input and the oracle."""
+    pairs), one launch each, against the input and the oracle; int4 pairs
+    also on the wide table (WC_FIRST_CODE_TABLE=0)."""
     from lossless_entropy_coded_amd.synth import make_code_workload
+    monkeypatch.setenv("WC_FIRST_CODE_TABLE", first_code_table)
     wl = make_code_workload(name)
     blob = wc.encode_u8_host(wl.tensors())
-    log(f"case: u8 full {name} n={wl.n} container={blob.size}")
+    log(f"case: u8 full {name} first_code_table={first_code_table} n={wl.n} container={blob.size}")
     got = gpu_decode_u8(wc, blob)
     assert np.array_equal(got, wl.codes)
-    log(f"case: u8 full {name} oracle decode")
-    assert np.array_equal(got, oracle_lib.decode_u8(blob))
+    if first_code_table == "1":
+        log(f"case: u8 full {name} oracle decode")
+        assert np.array_equal(got, oracle_lib.decode_u8(blob))
+
+
+def one_code_expected(lens, kd):
+    """The planner's rule for code planes: one code per lookup when no code
+    exceeds 16 bits and either the shortest is longer than half the table
+    index (no table entry holds two) or every code fits the index (the
+    first-code table replaces the multi-codeword table)."""
+    present = lens[lens > 0]
+    shortest, longest = int(present.min()), int(present.max())
+    return longest <= 16 and (2 * shortest > kd or (present.size >= 2 and longest <= kd))
 
 
 @pytest.mark.parametrize("sigma,max_len,one_code,longest_over", [
     (20.0, 0, True, False),     # shortest code 6 bits, none longer than the 11-bit index
     (40.0, 24, True, True),     # shortest 6, longest 14: the long-code path inside one-code lookups
     (30.0, 24, False, True),    # shortest 6, longest 18: four codes may not fit 64 bits
-    (20.0, 24, False, True),    # shortest 5: two codes can share a lookup
-    (3.0, 0, False, False),     # shortest 3: up to three codes per lookup
+    (20.0, 24, False, True),    # shortest 5 and codes past the index: the wide table
+    (3.0, 0, True, False),      # shortest 3, none past the index: the first-code table
 ])
 def test_u8_one_code_lookups(wc, oracle_lib, sigma, max_len, one_code, longest_over):
-    """Code planes whose shortest code is longer than half the 11-bit table
-    index never see two codes in one table entry; when no code is longer than
-    16 bits the decoder takes one code per lookup: eight per 96-bit window
-    when none is longer than the index, else four per 64-bit window.  The
-    others take the multi-code loop.  All are bit-exact against the input and
-    the oracle."""
+    """Code planes take one code per lookup when no code is longer than 16
+    bits and either no table entry can hold two codes (shortest code longer
+    than half the 11-bit index) or every code fits the index (a table of
+    each window's first code): eight codes per 96-bit window when none is
+    longer than the index, else four per 64-bit window.  The others take
+    the wide table.  All are bit-exact against the input and the oracle."""
     from container_view import sections
     from lossless_entropy_coded_amd.synth import quantized_codes
     rng = np.random.default_rng(int(sigma * 10) + max_len)
@@ -114,7 +128,7 @@ def test_u8_one_code_lookups(wc, oracle_lib, sigma, max_len, one_code, longest_o
     lens = sections(blob)["code_len"]
     with wc.Plan(blob) as plan:
         kd = plan.stats()["decode_bits"]
-    assert (2 * int(lens[lens > 0].min()) > kd and int(lens.max()) <= 16) == one_code
+    assert one_code_expected(lens, kd) == one_code
     assert (int(lens.max()) > kd) == longest_over
     log(f"case: u8 one-code sigma={sigma} max_len={max_len} one_code={one_code}")
     got = gpu_decode_u8(wc, blob)
@@ -122,39 +136,48 @@ def test_u8_one_code_lookups(wc, oracle_lib, sigma, max_len, one_code, longest_o
     assert np.array_equal(got, oracle_lib.decode_u8(blob))
 
 
-@pytest.mark.parametrize("sigma,max_len,one_code", [(20.0, 10, True), (3.0, 10, False)])
-def test_u8_ten_bit_index(wc, oracle_lib, monkeypatch, sigma, max_len, one_code):
+@pytest.mark.parametrize("sigma,max_len,first_code_table,one_code", [
+    (20.0, 10, "1", True),      # shortest code longer than 5 bits
+    (3.0, 10, "1", True),       # shortest 3: the first-code table
+    (3.0, 10, "0", False),      # the same plane on the wide table (11-bit index)
+])
+def test_u8_ten_bit_index(wc, oracle_lib, monkeypatch, sigma, max_len, first_code_table, one_code):
     """With a 10-bit table index (WC_DECODE_BITS=10) and no code longer than
-    it: int8-like planes take the one-code path with eight codes (at most 80
-    bits) per 96-bit window, int4-like planes the wide table (11-bit index)
-    in two phases.  Bit-exact against the input and the oracle."""
+    it: int8-like and int4-like planes take the one-code path with eight codes
+    (at most 80 bits) per 96-bit window; with WC_FIRST_CODE_TABLE=0 int4-like
+    planes take the wide table (11-bit index) in two phases.  Bit-exact
+    against the input and the oracle."""
     from container_view import sections
     from lossless_entropy_coded_amd.synth import quantized_codes
     monkeypatch.setenv("WC_DECODE_BITS", "10")
+    monkeypatch.setenv("WC_FIRST_CODE_TABLE", first_code_table)
     rng = np.random.default_rng(int(sigma * 100) + max_len)
     c = quantized_codes(rng, 250_000, 8, sigma)
     blob = wc.encode_u8_host([c], max_code_len=max_len)
     lens = sections(blob)["code_len"]
     with wc.Plan(blob) as plan:
         assert plan.stats()["decode_bits"] == 10
-    assert int(lens.max()) <= 10 and (2 * int(lens[lens > 0].min()) > 10) == one_code
-    log(f"case: u8 ten-bit index sigma={sigma} one_code={one_code}")
+    assert int(lens.max()) <= 10 and (2 * int(lens[lens > 0].min()) > 10 or first_code_table == "1") == one_code
+    log(f"case: u8 ten-bit index sigma={sigma} first_code_table={first_code_table} one_code={one_code}")
     got = gpu_decode_u8(wc, blob)
     assert np.array_equal(got, c)
     assert np.array_equal(got, oracle_lib.decode_u8(blob))
 
 
-@pytest.mark.parametrize("sigma", [3.0, 20.0])
-def test_u8_small_segments_every_tail(wc, oracle_lib, sigma):
+@pytest.mark.parametrize("sigma,first_code_table", [(3.0, "1"), (3.0, "0"), (20.0, "1")])
+def test_u8_small_segments_every_tail(wc, oracle_lib, monkeypatch, sigma, first_code_table):
     """Single-segment containers of 8 * full + r codes for every tail length
     r and full blocks on either side of each lane and phase boundary: the
     lanes after the one holding the partial last block have fewer symbols
-    (none in the second phase), and nothing they do may touch the partial
-    block's bytes."""
+    (none in the wide table's second phase), and nothing they do may touch
+    the partial block's bytes.  int4-like planes run on the first-code table
+    and, with WC_FIRST_CODE_TABLE=0, on the wide table."""
     from lossless_entropy_coded_amd.synth import quantized_codes
+    monkeypatch.setenv("WC_FIRST_CODE_TABLE", first_code_table)
     rng = np.random.default_rng(int(sigma) + 77)
     fulls = [0, 1, 5, 36, 63, 64, 65, 100, 127, 200, 255, 256, 257, 300, 447, 510]
-    log(f"case: u8 small segments sigma={sigma}: n = 8 * full + r, full in {fulls}, r in 0..7")
+    log(f"case: u8 small segments sigma={sigma} first_code_table={first_code_table}: "
+        f"n = 8 * full + r, full in {fulls}, r in 0..7")
     for full in fulls:
         for r in range(8):
             n = 8 * full + r
