@@ -239,6 +239,20 @@ int wc_plan_stats(const wc_plan_t* plan, uint64_t* container_bytes, uint64_t* st
                   uint32_t* lds_bytes);
 
 /*
+ * wc_plan_decode_shape -- how the container's decode entry point
+ * (wc_decode_async for bf16, wc_decode_u8_async for code planes) launches:
+ * the wavefronts per workgroup, the persistent grid (workgroups) and the
+ * kernel launches one call makes.  One call decodes the whole container (the
+ * DFloat11 page, abstract, design point (iii)); the plain bf16 decode of a
+ * container of more than 40 rounds of its grid (WC_LAUNCH_ROUNDS in the
+ * environment of wc_plan overrides the bound; 0: no bound) runs as that many
+ * consecutive launches on the same stream, each a span of whole rounds, and
+ * code planes always take one.  0 launches for an empty container.  Any
+ * output may be NULL; WC_ERR_INVALID_ARG for a NULL plan.
+ */
+int wc_plan_decode_shape(const wc_plan_t* plan, uint32_t* waves_per_group, uint32_t* grid, uint32_t* launches);
+
+/*
  * wc_plan_format -- the container's version (2: chunks, 3: lanes), element
  * kind (0: bf16, 1: u8) and coder (0: Huffman, 1: rANS).  Any output may be
  * NULL.

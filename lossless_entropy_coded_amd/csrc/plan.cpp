@@ -569,6 +569,28 @@ extern "C" int wc_plan_stats(const wc_plan_t* p, uint64_t* container_bytes, uint
     return WC_OK;
 }
 
+// The plain decode's split: launches of at most launch_rounds rounds of the
+// persistent grid each, cut into equal spans of whole rounds; the segments per
+// launch (the last launch takes what is left).
+static uint64_t plain_span(const wc_plan_t* p) {
+    const uint64_t per_round = (uint64_t)p->plain.grid * p->plain.waves;
+    const uint64_t rounds = wc::div_up(p->h.n_groups, per_round);
+    const uint64_t n_launch = p->launch_rounds ? wc::div_up(rounds, p->launch_rounds) : 1;
+    return std::max<uint64_t>(1, wc::div_up(rounds, n_launch) * per_round);
+}
+
+extern "C" int wc_plan_decode_shape(const wc_plan_t* p, uint32_t* waves_per_group, uint32_t* grid,
+                                    uint32_t* launches) {
+    if (!p) return WC_ERR_INVALID_ARG;
+    const bool u8 = p->h.elem_kind == wc::kKindU8;
+    const wc_plan_s::Shape& own = u8 ? p->busy : p->plain;
+    if (waves_per_group) *waves_per_group = own.waves;
+    if (grid) *grid = own.grid;
+    if (launches)
+        *launches = p->h.n_groups == 0 ? 0u : u8 ? 1u : (uint32_t)wc::div_up(p->h.n_groups, plain_span(p));
+    return WC_OK;
+}
+
 extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_t* out_dev, void* stream) {
     if (!p || p->h.elem_kind != wc::kKindBf16) return WC_ERR_INVALID_ARG;
     if (p->h.n_elems == 0) return WC_OK;
@@ -597,11 +619,7 @@ extern "C" int wc_decode_async(const wc_plan_t* p, const void* blob_dev, uint16_
     d.no_long = p->no_long ? 1u : 0u;
     d.status = p->d_status;
     hipError_t e = hipSuccess;
-    // launches of at most launch_rounds rounds of the persistent grid each
-    const uint64_t per_round = (uint64_t)p->plain.grid * p->plain.waves;
-    const uint64_t rounds = wc::div_up(p->h.n_groups, per_round);
-    const uint64_t n_launch = p->launch_rounds ? wc::div_up(rounds, p->launch_rounds) : 1;
-    const uint64_t span = wc::div_up(rounds, n_launch) * per_round;
+    const uint64_t span = plain_span(p);
     if (p->lanes) d.tables = p->d_tables + (1u << p->count_bits);   // from the multi-codeword table on
     for (uint64_t u0 = 0; u0 < p->h.n_groups && e == hipSuccess; u0 += span) {
         d.u_begin = u0;

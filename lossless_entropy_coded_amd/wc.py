@@ -66,6 +66,8 @@ _lib.wc_decode_u8_async.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_v
 _lib.wc_decode_u8_async.restype = ctypes.c_int
 _lib.wc_plan_format.argtypes = [ctypes.c_void_p, _u32p, _u32p, _u32p]
 _lib.wc_plan_format.restype = ctypes.c_int
+_lib.wc_plan_decode_shape.argtypes = [ctypes.c_void_p, _u32p, _u32p, _u32p]
+_lib.wc_plan_decode_shape.restype = ctypes.c_int
 _lib.wc_gemv_bf16_async.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p]
 _lib.wc_gemv_bf16_async.restype = ctypes.c_int
@@ -133,7 +135,7 @@ LAYOUTS = {"lanes": 0, "chunks": 1}
 CODERS = {"huffman": 0, "rans": 1}
 
 EXPORTED = ("wc_encode_host", "wc_encode_u8_host", "wc_free_host", "wc_plan", "wc_plan_info", "wc_plan_stats",
-            "wc_plan_format", "wc_decode_u8_async",
+            "wc_plan_format", "wc_plan_decode_shape", "wc_decode_u8_async",
             "wc_decode_async", "wc_gemv_bf16_async", "wc_decode_gemv_work_bytes", "wc_decode_gemv_async",
             "wc_decode_gemv_noalloc_async", "wc_stream_reference_async", "wc_plan_debug_status",
             "wc_plan_destroy", "wc_status_str")
@@ -256,6 +258,13 @@ class Plan:
         _check(_lib.wc_plan_format(self.handle, ctypes.byref(v), ctypes.byref(k), ctypes.byref(c)),
                "wc_plan_format")
         return v.value, k.value, c.value
+
+    def decode_shape(self) -> dict:
+        """wc_plan_decode_shape: waves per workgroup, grid and launches per call of the decode entry point."""
+        w, g, n = ctypes.c_uint32(), ctypes.c_uint32(), ctypes.c_uint32()
+        _check(_lib.wc_plan_decode_shape(self.handle, ctypes.byref(w), ctypes.byref(g), ctypes.byref(n)),
+               "wc_plan_decode_shape")
+        return {"waves_per_group": w.value, "grid": g.value, "launches": n.value}
 
     def stats(self) -> dict:
         cb, sb, ng = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()

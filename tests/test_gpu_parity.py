@@ -308,6 +308,7 @@ def test_argument_checks(wc):
     empty = wc.encode_host([np.zeros(0, np.uint16)], layout="chunks")
     with wc.Plan(empty) as plan:
         assert plan.n_elems == 0
+        assert plan.decode_shape()["launches"] == 0
         wc.decode_async(plan, 0, 0)       # n = 0 is a no-op
         torch.cuda.synchronize()
 
@@ -324,4 +325,11 @@ def test_decode_in_several_launches(wc, env_knob, rounds, layout, coder):
     blob = wc.encode_host(wl.tensors(), layout=layout, coder=coder)
     env_knob("WC_LAUNCH_ROUNDS", rounds)
     log(f"case: {layout} {coder} decode in launches of {rounds} rounds, n={wl.n}")
+    with wc.Plan(blob) as plan:
+        # wc_plan_decode_shape reports the split: ceil(rounds of the grid /
+        # rounds per launch) launches of the plain decode's own shape
+        shape, st = plan.decode_shape(), plan.stats()
+        total = -(-st["n_groups"] // (shape["waves_per_group"] * shape["grid"]))
+        assert shape["grid"] == st["grid"] and shape["waves_per_group"] == 4
+        assert total >= 4 and shape["launches"] == -(-total // rounds), (shape, st)
     assert np.array_equal(gpu_decode(wc, blob), wl.bits)

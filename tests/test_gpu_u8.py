@@ -89,6 +89,11 @@ def test_u8_workload_full_size(wc, oracle_lib, monkeypatch, name, first_code_tab
     wl = make_code_workload(name)
     blob = wc.encode_u8_host(wl.tensors())
     log(f"case: u8 full {name} first_code_table={first_code_table} n={wl.n} container={blob.size}")
+    with wc.Plan(blob) as plan:
+        # code planes: one launch of 8-wave workgroups, whatever the size
+        shape = plan.decode_shape()
+        assert shape["launches"] == 1 and shape["waves_per_group"] == 8
+        assert shape["grid"] == plan.stats()["grid"]
     got = gpu_decode_u8(wc, blob)
     assert np.array_equal(got, wl.codes)
     if first_code_table == "1":
