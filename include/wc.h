@@ -316,8 +316,15 @@ int wc_gemv_bf16_async(const uint16_t* W, uint32_t rows, uint32_t cols, const ui
  * abstract, design point (ii): the auxiliary variables that place each
  * block's output) and OR WC_DEBUG_GROUP_COUNT into the word when they do
  * not: a corrupted stream or group bit offset, which wc_plan's host checks
- * cannot see.  Other layouts leave the word alone.  Plans made without
- * WC_DEBUG launch kernels compiled without the check.
+ * cannot see.  The lanes layout's plain bf16 decode (wc_decode_async) checks
+ * that every lane's decode ends its string where the next lane's begins (the
+ * lane offsets are its auxiliary variables; the last lane's string ends with
+ * the segment's bits) and ORs WC_DEBUG_LANE_BITS into the word when one does
+ * not: with Huffman codes the lane's last table lookup must contain that
+ * point (its further symbols belong to the next lane), with rANS the lane
+ * must be back in the encoder's initial state 2^16 exactly there.  Code
+ * planes and the lanes layout's fused product leave the word alone.  Plans
+ * made without WC_DEBUG launch kernels compiled without the checks.
  *   plan    a plan made with WC_DEBUG=1;
  *   status  receives the word (host pointer);
  *   reset   nonzero: the word is cleared after it is read.
@@ -326,6 +333,7 @@ int wc_gemv_bf16_async(const uint16_t* W, uint32_t rows, uint32_t cols, const ui
  * without WC_DEBUG, WC_ERR_HIP if a HIP call fails.
  */
 #define WC_DEBUG_GROUP_COUNT 1u
+#define WC_DEBUG_LANE_BITS 2u
 int wc_plan_debug_status(const wc_plan_t* plan, uint32_t* status, int reset);
 
 /* ---- measurement ----------------------------------------------------------- */

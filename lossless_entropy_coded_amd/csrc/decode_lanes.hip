@@ -43,6 +43,7 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "../../include/wc.h"
 #include "decode_common.h"
 #include "format.h"
 #include "kernels.h"
@@ -111,9 +112,12 @@ __device__ __forceinline__ uint32_t unrotate4(uint32_t x) {
 // each wave multiplies its segment by x and leaves its partial dot products
 // in p.dot.part.  kLanesToU8: decode a plane of code bytes into p.out8 (no
 // sign+mantissa plane).  kRans: rANS lanes (KD = 11: the slot table fills
-// the multi-codeword table's 16 KiB).
-template <int KD, int W, uint32_t kMode, bool kRans>
+// the multi-codeword table's 16 KiB).  kCheck (debug plans, kLanesToBf16
+// only): every lane checks that its decode ends its own string where the next
+// lane's begins, and a failure ORs WC_DEBUG_LANE_BITS into p.status.
+template <int KD, int W, uint32_t kMode, bool kRans, bool kCheck = false>
 __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void decode_lanes_kernel(DecodeParams p) {
+    static_assert(!kCheck || kMode == kLanesToBf16, "the lane-end check is compiled into the plain bf16 decode only");
     static_assert(!kRans || (2u << KD) == kRansSlots, "the rANS slot table takes the multi-codeword table's place");
     static_assert(kMode != kLanesToDot || kRans, "the fused product of Huffman lanes is decode_lanes_dot_kernel");
     constexpr bool kDot = kMode == kLanesToDot;
@@ -262,6 +266,16 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
             uint32_t nsym = kLaneBlock * cnt;
             if (cnt && lane == (nb8 - 1) % kWaveLanes) nsym -= kLaneBlock * nb8 - n;
             const uint32_t pos = (uint32_t)(cur_m.p0 & 127u) + off;   // first bit in the staged words
+            // debug plans: where this lane's string ends in the staged words,
+            // the next lane's first bit (the last lane's: the segment's end)
+            uint32_t lane_end = 0;
+            bool lane_bad = false;
+            if constexpr (kCheck) {
+                const uint32_t off_next = (uint32_t)__shfl_down((int)off, 1);
+                lane_end = (uint32_t)(cur_m.p0 & 127u) +
+                           (lane == kWaveLanes - 1 ? (uint32_t)(cur_m.p1 - cur_m.p0) : off_next);
+                lane_bad = nsym == 0 && lane_end != pos;   // an empty lane has an empty string
+            }
             if constexpr (kRans) {
                 // the final state, then one symbol per step, eight per slot
                 // store (a lane whose count is not a multiple of eight decodes
@@ -278,10 +292,15 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                     const uint32_t v = (s_slot[0] & 0xFFu) * 0x01010101u;
                     for (uint32_t p = 0; p < nsym; p += kMergeElems)
                         store_slot8(slot + p, make_uint2(v, v));
+                    // (debug: the lane's string is its final state alone)
+                    if constexpr (kCheck) lane_bad |= nsym != 0 && lane_end != pos + 32u;
                 } else {
                     uint32_t q = pos >> 4;
                     uint32_t x = (uint32_t)s16[q] << 16 | s16[q + 1];
                     q += 2;
+                    // debug: the state and next half-word after the lane's
+                    // last symbol (the loop decodes up to seven more)
+                    uint32_t x_end = kRansLow, q_end = q;
                     for (uint32_t p = 0; p < nsym; p += kMergeElems) {
                         uint32_t e[kMergeElems];
 #pragma unroll
@@ -293,6 +312,12 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                             const bool in = x < kRansLow;
                             x = in ? x << 16 | w : x;
                             q += in ? 1u : 0u;
+                            if constexpr (kCheck) {
+                                if (p + i + 1 == nsym) {
+                                    x_end = x;
+                                    q_end = q;
+                                }
+                            }
                         }
                         // the symbols are the entries' low bytes
                         const uint32_t s0 = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0400u) |
@@ -301,6 +326,9 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                                             __builtin_amdgcn_perm(e[7], e[6], 0x04000C0Cu);
                         store_slot8(slot + p, make_uint2(s0, s1));
                     }
+                    // debug: a lane ends in the encoder's initial state,
+                    // exactly where the next lane's string begins
+                    if constexpr (kCheck) lane_bad |= nsym != 0 && (x_end != kRansLow || 16u * q_end != lane_end);
                 }
             } else if constexpr (kMode == kLanesToBf16) {
                 // plain decode (bound by HBM): a 64-bit MSB-first register
@@ -314,6 +342,7 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                 int32_t valid = 64 - (int32_t)(pos & 31u);
                 wi += 2;
                 uint32_t p = 0;
+                uint32_t last_bits = 0;   // debug: the bits of the lane's last lookup
                 while (p < nsym) {
                     const uint32_t top = (uint32_t)(win >> 32);
                     uint2 e = s_dec[top >> (32 - KD)];
@@ -326,6 +355,7 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                     dst[3] = (uint8_t)(odd >> 16);
                     p += (e.x >> 8) & 0xFFu;
                     const uint32_t nbits = (e.x >> 16) & 0xFFu;
+                    if constexpr (kCheck) last_bits = nbits;
                     win <<= nbits;
                     valid -= (int32_t)nbits;
                     if (valid < 32) {
@@ -333,6 +363,13 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                         ++wi;
                         valid += 32;
                     }
+                }
+                // debug: the window starts at staged bit 32 wi - valid; the
+                // lane's last symbol ends inside its last lookup (whose
+                // further symbols, if any, belong to the next lane)
+                if constexpr (kCheck) {
+                    const uint32_t at = 32u * wi - (uint32_t)valid;
+                    lane_bad |= nsym != 0 && !(at - last_bits < lane_end && lane_end <= at);
                 }
             } else {
                 // code planes (bound by the decode's instructions and LDS):
@@ -558,6 +595,12 @@ __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void d
                     run(std::false_type{});
                 else
                     run(std::true_type{});
+            }
+            // debug plans: one vector-memory atomic OR per wave whose lanes
+            // found a string that does not end where the next one begins (a
+            // corrupted stream or lane offset, which wc_plan cannot see)
+            if constexpr (kCheck) {
+                if (__ballot(lane_bad) != 0 && lane == 0) atomicOr(p.status, WC_DEBUG_LANE_BITS);
             }
         }
 
@@ -868,6 +911,8 @@ struct LanesVariant {
                 return hipErrorInvalidValue;   // Huffman lanes: launch_decode_lanes_dot
         } else if (mode == kLanesToU8)
             hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToU8, kRans>), g, b, dyn, stream, p);
+        else if (p.status)   // debug plans: the kernel compiled with the lane-end check
+            hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToBf16, kRans, true>), g, b, dyn, stream, p);
         else
             hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToBf16, kRans>), g, b, dyn, stream, p);
         return hipGetLastError();

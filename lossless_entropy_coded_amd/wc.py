@@ -116,6 +116,7 @@ WC_ERR_STREAM_BITS = -17
 WC_ERR_TENSOR_TABLE = -18
 # bits of a debug plan's status word (plans made with WC_DEBUG=1)
 WC_DEBUG_GROUP_COUNT = 1
+WC_DEBUG_LANE_BITS = 2
 
 # Group table defaults (wc_encode_opts): G = chunks per group, what one wave64
 # decodes in one pass (two 64-bit chunks per lane; wider groups take several
@@ -296,8 +297,10 @@ class Plan:
 def plan_debug_status(plan: Plan, reset: bool = False) -> int:
     """wc_plan_debug_status: the status word of a plan made with WC_DEBUG=1 in
     the environment (0: no invariant failed; WC_DEBUG_GROUP_COUNT: a group of
-    the chunks layout decoded a codeword count other than its element count).
-    Waits for the plan's device; reset clears the word after reading it."""
+    the chunks layout decoded a codeword count other than its element count;
+    WC_DEBUG_LANE_BITS: a lane of the lanes layout's plain decode did not end
+    its string where the next lane's begins).  Waits for the plan's device;
+    reset clears the word after reading it."""
     word = ctypes.c_uint32(0)
     _check(_lib.wc_plan_debug_status(plan.handle, ctypes.byref(word), 1 if reset else 0), "wc_plan_debug_status")
     return word.value

@@ -112,3 +112,84 @@ def test_zero_stream_sets_group_count(wc, monkeypatch, path):
             _fused(wc, plan, dblob, wl.shapes)
         assert wc.plan_debug_status(plan, reset=True) & wc.WC_DEBUG_GROUP_COUNT
         assert wc.plan_debug_status(plan) == 0
+
+
+def _lane_symbols(m: int) -> np.ndarray:
+    """Symbols of each of the 64 lanes of a segment of m elements: lane j takes
+    the 8-element lane blocks j, j + 64, ... (the segment's last block may be
+    shorter)."""
+    nb8 = -(-m // 8)
+    nsym = np.array([8 * ((nb8 - 1 - j) // 64 + 1) if j < nb8 else 0 for j in range(64)], dtype=np.int64)
+    if nb8:
+        nsym[(nb8 - 1) % 64] -= 8 * nb8 - m
+    return nsym
+
+
+def _zero_lanes_stream(blob):
+    """A lanes container with every stream byte zero, and the number of lanes
+    that provably cannot end their strings where the next ones begin.  Huffman:
+    over zero bits every code is the first canonical one (all zeros, the
+    shortest length L), and a lane's last table lookup adds at most three
+    symbols past its own, so a lane of nsym symbols whose string is longer
+    than L (nsym + 3) bits stops short of its end.  rANS: the final state
+    read is 0, and from state 0 every step stays at 0 (the first present
+    symbol owns slot 0 with cumulative frequency 0, and renormalising shifts
+    in zero words), never the initial state 2^16 a lane must end in."""
+    from container_view import sections
+    s = sections(blob)
+    b = blob.copy()
+    b[s["off_stream"]:s["off_stream"] + s["stream_bytes"]] = 0
+    g = s["groups"].astype(np.int64)
+    off = s["lane_off"].astype(np.int64)
+    L = None if s["coder"] == 1 else int(s["code_len"][s["code_len"] > 0].min())
+    caught = 0
+    for k in range(int(s["n_groups"])):
+        m, seg_bits = g[k + 1, 0] - g[k, 0], g[k + 1, 1] - g[k, 1]
+        lens = np.append(off[k, 1:], seg_bits) - off[k]
+        nsym = _lane_symbols(int(m))
+        if L is None:
+            caught += int(np.sum(nsym > 0))
+        else:
+            caught += int(np.sum((nsym > 0) & (lens > L * (nsym + 3))))
+    return b, caught
+
+
+@pytest.mark.parametrize("coder", ["huffman", "rans"])
+@pytest.mark.parametrize("A,M,B,n", [(8, 4096, 15872, None), (64, 1024, 4096, None), (120, 3960, 15872, None),
+                                     (8, 512, 500, None), (8, 4096, 15872, 1), (8, 4096, 15872, 9),
+                                     (8, 4096, 15872, 521), (128, 4096, 15872, 70_001)])
+def test_lanes_valid_shapes_leave_word_clear(wc, monkeypatch, coder, A, M, B, n):
+    """The lane-end check of the lanes layout's plain decode on valid
+    containers of every segment shape (empty lanes, a short last block, the
+    last lane's end at the segment's end, bit caps down to 500): bit-exact,
+    and the status word stays 0."""
+    from lossless_entropy_coded_amd.synth import make_workload
+    monkeypatch.setenv("WC_DEBUG", "1")
+    wl = make_workload("heavy_tail_14k", scale_rows=64)
+    data = wl.bits if n is None else wl.bits[:n]
+    tensors = wl.tensors() if n is None else [data]
+    if coder == "rans":
+        B = max(B, 2048 + (97 * A + 7) // 8)       # the rANS writer's least segment bit cap
+    blob = wc.encode_host(tensors, coder=coder, group_align=A, group_max_elems=M, seg_max_bits=B)
+    with wc.Plan(blob) as plan:
+        log(f"case: debug plan, lanes {coder} A={A} M={M} B={B} n={data.size}")
+        assert np.array_equal(gpu_decode(wc, blob, plan=plan), data)
+        assert wc.plan_debug_status(plan) == 0
+
+
+@pytest.mark.parametrize("coder", ["huffman", "rans"])
+def test_lanes_zero_stream_sets_lane_bits(wc, monkeypatch, coder):
+    """A lanes container whose stream is all zero bits passes wc_plan (its
+    checks cover the metadata), stays inside its output, and sets
+    WC_DEBUG_LANE_BITS (and nothing else); reset clears the word."""
+    from lossless_entropy_coded_amd.synth import make_workload
+    monkeypatch.setenv("WC_DEBUG", "1")
+    wl = make_workload("heavy_tail_14k", scale_rows=96)
+    blob = wc.encode_host(wl.tensors(), coder=coder)
+    bad, caught = _zero_lanes_stream(blob)
+    assert caught, "no lane provably misses its end: the zero stream proves nothing here"
+    with wc.Plan(bad) as plan:
+        log(f"case: debug plan, lanes {coder} zero stream ({caught} lanes must miss their ends)")
+        gpu_decode(wc, bad, plan=plan)          # asserts the guard bands
+        assert wc.plan_debug_status(plan, reset=True) == wc.WC_DEBUG_LANE_BITS
+        assert wc.plan_debug_status(plan) == 0
