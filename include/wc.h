@@ -316,14 +316,15 @@ int wc_gemv_bf16_async(const uint16_t* W, uint32_t rows, uint32_t cols, const ui
  * abstract, design point (ii): the auxiliary variables that place each
  * block's output) and OR WC_DEBUG_GROUP_COUNT into the word when they do
  * not: a corrupted stream or group bit offset, which wc_plan's host checks
- * cannot see.  The lanes layout's plain bf16 decode (wc_decode_async) checks
+ * cannot see.  The lanes layout's plain bf16 decode (wc_decode_async) and
+ * fused product (wc_decode_gemv_async and its no-allocation variant) check
  * that every lane's decode ends its string where the next lane's begins (the
  * lane offsets are its auxiliary variables; the last lane's string ends with
  * the segment's bits) and ORs WC_DEBUG_LANE_BITS into the word when one does
  * not: with Huffman codes the lane's last table lookup must contain that
  * point (its further symbols belong to the next lane), with rANS the lane
  * must be back in the encoder's initial state 2^16 exactly there.  Code
- * planes and the lanes layout's fused product leave the word alone.  Plans
+ * planes leave the word alone.  Plans
  * made without WC_DEBUG launch kernels compiled without the checks.
  *   plan    a plan made with WC_DEBUG=1;
  *   status  receives the word (host pointer);

@@ -112,12 +112,14 @@ __device__ __forceinline__ uint32_t unrotate4(uint32_t x) {
 // each wave multiplies its segment by x and leaves its partial dot products
 // in p.dot.part.  kLanesToU8: decode a plane of code bytes into p.out8 (no
 // sign+mantissa plane).  kRans: rANS lanes (KD = 11: the slot table fills
-// the multi-codeword table's 16 KiB).  kCheck (debug plans, kLanesToBf16
-// only): every lane checks that its decode ends its own string where the next
-// lane's begins, and a failure ORs WC_DEBUG_LANE_BITS into p.status.
+// the multi-codeword table's 16 KiB).  kCheck (debug plans; the plain bf16
+// decode, and the fused product of rANS lanes): every lane checks that its
+// decode ends its own string where the next lane's begins, and a failure ORs
+// WC_DEBUG_LANE_BITS into p.status.
 template <int KD, int W, uint32_t kMode, bool kRans, bool kCheck = false>
 __global__ __launch_bounds__(kWaveLanes * W, kMode == kLanesToU8 ? 6 : 1) void decode_lanes_kernel(DecodeParams p) {
-    static_assert(!kCheck || kMode == kLanesToBf16, "the lane-end check is compiled into the plain bf16 decode only");
+    static_assert(!kCheck || kMode == kLanesToBf16 || (kMode == kLanesToDot && kRans),
+                  "the lane-end check is compiled into the plain bf16 decode and the rANS fused product only");
     static_assert(!kRans || (2u << KD) == kRansSlots, "the rANS slot table takes the multi-codeword table's place");
     static_assert(kMode != kLanesToDot || kRans, "the fused product of Huffman lanes is decode_lanes_dot_kernel");
     constexpr bool kDot = kMode == kLanesToDot;
@@ -705,7 +707,9 @@ constexpr uint32_t kDotSlotBytes = kDotHalf + 4;  // 9 dwords: an odd stride acr
 constexpr uint32_t kDotSteps = kMergeSteps / 2;   // merge steps per phase
 constexpr uint32_t kDotWaveBytes = kLanePadBytes + kLaneStageBytes + kWaveLanes * kDotSlotBytes;
 
-template <int KD, int W>
+// kCheck (debug plans): the lane-end check of the plain decode, with a failure
+// ORed into p.status as WC_DEBUG_LANE_BITS.
+template <int KD, int W, bool kCheck = false>
 __global__ __launch_bounds__(kWaveLanes * W, 6) void decode_lanes_dot_kernel(DecodeParams p) {
     constexpr uint32_t kThreads = kWaveLanes * W;
     constexpr uint32_t kDecVec = (2u << KD) / 4, kLongVec = kLongWords / 4;
@@ -814,6 +818,14 @@ __global__ __launch_bounds__(kWaveLanes * W, 6) void decode_lanes_dot_kernel(Dec
         // bits, so its last window word is at most 548: inside the wave's
         // staging and slots.
         int32_t nb = -(int32_t)((uint32_t)(cur_m.p0 & 127u) + off);
+        // debug plans: this lane's string ends at the next lane's first bit
+        // (the last lane's: the segment's end); the bits of its last lookup
+        uint32_t lane_end = 0, last_bits = 0;
+        if constexpr (kCheck) {
+            const uint32_t off_next = (uint32_t)__shfl_down((int)off, 1);
+            lane_end = (uint32_t)(cur_m.p0 & 127u) +
+                       (lane == kWaveLanes - 1 ? (uint32_t)(cur_m.p1 - cur_m.p0) : off_next);
+        }
         // the symbol count is kept as the LDS byte address of the next symbol
         // (a local-address-space offset; slots are 4-byte aligned, so its low
         // two bits are the count's)
@@ -850,6 +862,7 @@ __global__ __launch_bounds__(kWaveLanes * W, 6) void decode_lanes_dot_kernel(Dec
                 sh = s2 & 24u;
                 a += (e.x >> 8) & 0xFFu;
                 nb -= (int32_t)((e.x >> 16) & 0xFFu);
+                if constexpr (kCheck) last_bits = (e.x >> 16) & 0xFFu;
             }
             a -= kDotHalf * (h == 0);
             wave_lds_order();
@@ -867,6 +880,13 @@ __global__ __launch_bounds__(kWaveLanes * W, 6) void decode_lanes_dot_kernel(Dec
             wave_lds_order();   // the second phase rewrites the slot
         }
         finish_dot(p.dot, dr, lane, u - p.u_begin, acc0, acc1);
+        if constexpr (kCheck) {
+            // the window's bit is -nb: the lane's last lookup must span its
+            // string's end (an empty lane's string is empty)
+            const uint32_t at = (uint32_t)(-nb), start = (uint32_t)(cur_m.p0 & 127u) + off;
+            const bool bad = nsym == 0 ? lane_end != start : !(at - last_bits < lane_end && lane_end <= at);
+            if (__ballot(bad) != 0 && lane == 0) atomicOr(p.status, WC_DEBUG_LANE_BITS);
+        }
 
         const LaneRaw next_r = nxt;
         const Meta next_m = m_next;
@@ -882,7 +902,10 @@ __global__ __launch_bounds__(kWaveLanes * W, 6) void decode_lanes_dot_kernel(Dec
 template <int KD, int W>
 struct LanesDotVariant {
     static hipError_t launch(const DecodeParams& p, uint32_t grid, uint32_t dyn, hipStream_t stream) {
-        hipLaunchKernelGGL((decode_lanes_dot_kernel<KD, W>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
+        if (p.status)   // debug plans: the kernel compiled with the lane-end check
+            hipLaunchKernelGGL((decode_lanes_dot_kernel<KD, W, true>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
+        else
+            hipLaunchKernelGGL((decode_lanes_dot_kernel<KD, W>), dim3(grid), dim3(kWaveLanes * W), dyn, stream, p);
         return hipGetLastError();
     }
     static int blocks_per_cu(uint32_t dyn) {
@@ -905,9 +928,12 @@ struct LanesVariant {
     static hipError_t launch(const DecodeParams& p, uint32_t grid, uint32_t dyn, LanesOut mode, hipStream_t stream) {
         const dim3 g(grid), b(kWaveLanes * W);
         if (mode == kLanesToDot) {
-            if constexpr (kRans)
-                hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToDot, kRans>), g, b, dyn, stream, p);
-            else
+            if constexpr (kRans) {
+                if (p.status)   // debug plans: the kernel compiled with the lane-end check
+                    hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToDot, kRans, true>), g, b, dyn, stream, p);
+                else
+                    hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToDot, kRans>), g, b, dyn, stream, p);
+            } else
                 return hipErrorInvalidValue;   // Huffman lanes: launch_decode_lanes_dot
         } else if (mode == kLanesToU8)
             hipLaunchKernelGGL((decode_lanes_kernel<KD, W, kLanesToU8, kRans>), g, b, dyn, stream, p);

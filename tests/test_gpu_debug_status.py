@@ -159,10 +159,11 @@ def _zero_lanes_stream(blob):
                                      (8, 512, 500, None), (8, 4096, 15872, 1), (8, 4096, 15872, 9),
                                      (8, 4096, 15872, 521), (128, 4096, 15872, 70_001)])
 def test_lanes_valid_shapes_leave_word_clear(wc, monkeypatch, coder, A, M, B, n):
-    """The lane-end check of the lanes layout's plain decode on valid
-    containers of every segment shape (empty lanes, a short last block, the
-    last lane's end at the segment's end, bit caps down to 500): bit-exact,
-    and the status word stays 0."""
+    """The lane-end check of the lanes layout's plain decode (and, for whole
+    matrices, of its fused product) on valid containers of every segment
+    shape (empty lanes, a short last block, the last lane's end at the
+    segment's end, bit caps down to 500): bit-exact, and the status word
+    stays 0."""
     from lossless_entropy_coded_amd.synth import make_workload
     monkeypatch.setenv("WC_DEBUG", "1")
     wl = make_workload("heavy_tail_14k", scale_rows=64)
@@ -175,13 +176,21 @@ def test_lanes_valid_shapes_leave_word_clear(wc, monkeypatch, coder, A, M, B, n)
         log(f"case: debug plan, lanes {coder} A={A} M={M} B={B} n={data.size}")
         assert np.array_equal(gpu_decode(wc, blob, plan=plan), data)
         assert wc.plan_debug_status(plan) == 0
+        if n is None:
+            log(f"case: debug plan, lanes {coder} A={A} M={M} B={B}: fused product")
+            _, dblob = to_device_aligned(blob)
+            ys = _fused(wc, plan, dblob, wl.shapes)
+            assert all(np.all(np.isfinite(y)) for y in ys)
+            assert wc.plan_debug_status(plan) == 0
 
 
+@pytest.mark.parametrize("path", ["decode", "fused"])
 @pytest.mark.parametrize("coder", ["huffman", "rans"])
-def test_lanes_zero_stream_sets_lane_bits(wc, monkeypatch, coder):
+def test_lanes_zero_stream_sets_lane_bits(wc, monkeypatch, coder, path):
     """A lanes container whose stream is all zero bits passes wc_plan (its
     checks cover the metadata), stays inside its output, and sets
-    WC_DEBUG_LANE_BITS (and nothing else); reset clears the word."""
+    WC_DEBUG_LANE_BITS (and nothing else) in the plain decode and in the
+    fused product; reset clears the word."""
     from lossless_entropy_coded_amd.synth import make_workload
     monkeypatch.setenv("WC_DEBUG", "1")
     wl = make_workload("heavy_tail_14k", scale_rows=96)
@@ -189,7 +198,11 @@ def test_lanes_zero_stream_sets_lane_bits(wc, monkeypatch, coder):
     bad, caught = _zero_lanes_stream(blob)
     assert caught, "no lane provably misses its end: the zero stream proves nothing here"
     with wc.Plan(bad) as plan:
-        log(f"case: debug plan, lanes {coder} zero stream ({caught} lanes must miss their ends)")
-        gpu_decode(wc, bad, plan=plan)          # asserts the guard bands
+        log(f"case: debug plan, lanes {coder} zero stream, {path} ({caught} lanes must miss their ends)")
+        if path == "decode":
+            gpu_decode(wc, bad, plan=plan)      # asserts the guard bands
+        else:
+            _, dblob = to_device_aligned(bad)
+            _fused(wc, plan, dblob, wl.shapes)
         assert wc.plan_debug_status(plan, reset=True) == wc.WC_DEBUG_LANE_BITS
         assert wc.plan_debug_status(plan) == 0
