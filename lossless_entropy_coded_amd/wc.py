@@ -298,9 +298,9 @@ def plan_debug_status(plan: Plan, reset: bool = False) -> int:
     """wc_plan_debug_status: the status word of a plan made with WC_DEBUG=1 in
     the environment (0: no invariant failed; WC_DEBUG_GROUP_COUNT: a group of
     the chunks layout decoded a codeword count other than its element count;
-    WC_DEBUG_LANE_BITS: a lane of the lanes layout's decode or fused product did not end
-    its string where the next lane's begins).  Waits for the plan's device;
-    reset clears the word after reading it."""
+    WC_DEBUG_LANE_BITS: a lane of the lanes layout's decode or fused product
+    did not end its string where the next lane's begins).  Waits for the
+    plan's device; reset clears the word after reading it."""
     word = ctypes.c_uint32(0)
     _check(_lib.wc_plan_debug_status(plan.handle, ctypes.byref(word), 1 if reset else 0), "wc_plan_debug_status")
     return word.value

@@ -247,6 +247,17 @@ def test_debug_status_argument_checks_without_device(wc):
     assert word.value == 7
 
 
+def test_decode_shape_refuses_null_plan(wc):
+    """wc_plan_decode_shape refuses a NULL plan and leaves its outputs alone
+    (the shape of a real plan: GPU tests)."""
+    import ctypes
+    w, g, n = ctypes.c_uint32(7), ctypes.c_uint32(7), ctypes.c_uint32(7)
+    assert wc._lib.wc_plan_decode_shape(None, ctypes.byref(w), ctypes.byref(g), ctypes.byref(n)) == \
+        wc.WC_ERR_INVALID_ARG
+    assert wc._lib.wc_plan_decode_shape(None, None, None, None) == wc.WC_ERR_INVALID_ARG
+    assert (w.value, g.value, n.value) == (7, 7, 7)
+
+
 def test_gemv_argument_checks_without_device(wc):
     """Size and alignment checks of wc_gemv_bf16_async return before any HIP call."""
     import ctypes
